@@ -1,0 +1,360 @@
+"""Plain, slow fp64 oracle of the Block Cache + State Cache decode path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the GPU path.
+
+Page keys used in the citations below:
+  [Q&A]    "V4 为何要分池？块对齐与尾缓冲怎么配合？" (deepseek-tech-notes Q&A on the
+           two pools, block alignment and the tail buffer)
+  [Layout] "V4 KV Layout：Classical + State 双池" (deepseek-tech-notes)
+  [Ch12]   "Ch 12 · 推理框架 — KV 的异构调度" (DeepSeek-V4-book)
+  [Disk]   "V4 磁盘 Prefix Cache" (deepseek-tech-notes)
+
+Arithmetic is float64. Values that the layout stores as bf16 (compressed CSA and
+HCA entries) are rounded to bf16, nearest-even, when stored, and kept in
+float32 arrays that hold those bf16 values exactly; raw K/V/Q arrive as bf16
+values and indexer keys/queries as float32 values, both exact in float64.
+
+Readings taken where the pages leave a step open (each also in the design notes):
+  R1  compressor: per head h, gate logits g_t = <W[h], K_t[h]>, alpha =
+      softmax over the m tokens, entry = sum_t alpha_t (K_t, V_t); separate W
+      for CSA (m = 4) and HCA (m' = 128). The pages never define it.
+  R2  C4 and HCA entries are written together when a 128-token block fills
+      ([Q&A] §2.2, §2.3; [Ch12] Demo); csa_tail = L mod 4, hca_tail = L mod 128
+      count tokens of the one raw tail.
+  R3  indexer keys: 128 per block, one per token, 4 heads x 64 ([Ch12] §2.2).
+  R4  indexer score of token t: sum over heads and dims of qI * kI_t; score of
+      C4 entry j of a block = mean of its 4 tokens' scores. No ReLU, no head
+      weights (not on the pages).
+  R5  no de-duplication: one softmax over SWA + HCA + selected C4 even where a
+      token is also inside a sealed block ([Q&A] §2.3 leaves it to the kernel).
+  R6  the tail is read through the SWA (tail is a subset of SWA since
+      n_win >= 128 > L mod 128).
+  R8  top-k candidates are the sealed C4 entries only; kk = min(k, N_c); the
+      rest of the row is padded with -1.
+  R9  top-k order: score descending, ties to the lowest C4 ordinal.
+  R10 block ids: lowest free id first, requests in call order, blocks in token
+      order; state slots: lowest free first.
+  R11 share(src, dst): dst (fresh) references every sealed block of src
+      (refcount + 1 each) and gets a copy of src's State (SWA, tail, L).
+  R12 softmax scale 1/sqrt(128); no positional encoding, no mask.
+"""
+
+from __future__ import annotations
+
+import heapq
+import math
+from collections import deque
+
+import numpy as np
+
+BLOCK = 128          # lcm(m, m') tokens per block ([Q&A] §2.2; [Ch12] 公式白话翻译)
+M_CSA = 4            # CSA: 4 tokens -> 1 entry ([Q&A] §1.2)
+M_HCA = 128          # HCA: 128 tokens -> 1 entry ([Q&A] §1.2)
+C4_PER_BLOCK = BLOCK // M_CSA   # 32 ([Ch12] §2.2)
+N_HEADS = 16
+HEAD_DIM = 128
+IDX_HEADS = 4
+IDX_DIM = 64
+
+
+class OracleError(Exception):
+    """kind in {'invalid', 'oom_blocks', 'oom_states', 'state'}; raised before any change."""
+
+    def __init__(self, kind: str, msg: str = ""):
+        super().__init__(f"{kind}: {msg}")
+        self.kind = kind
+
+
+# ---------------------------------------------------------------- arithmetic
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bf16 value of float64 x, ties to even (8 significant bits).
+
+    Written from the definition: x = m * 2**e with 0.5 <= |m| < 1, keep 8
+    significant bits of m with round-half-to-even. Finite normal range only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def length_split(L: int) -> dict:
+    """L = 128 q + r: q sealed blocks hold 32q C4 + q HCA entries, r tokens stay
+    in the tail ([Q&A] §2.2, §3.1; [Ch12] Demo)."""
+    q, r = divmod(int(L), BLOCK)
+    return {"blocks": q, "c4": C4_PER_BLOCK * q, "hca": q, "tail": r,
+            "csa_tail": int(L) % M_CSA, "hca_tail": int(L) % M_HCA}
+
+
+def gated_pool(Kg: np.ndarray, Vg: np.ndarray, W: np.ndarray):
+    """Compress m consecutive tokens into one entry (reading R1).
+
+    Kg, Vg: [m][H][D] token K/V; W: [H][D] gate weights. Per head h:
+    g_t = <W[h], K_t[h]>, alpha = softmax_t(g), entry = sum_t alpha_t K_t[h]
+    (and the same alpha for V). Returns bf16-rounded (K, V) [H][D] as float32.
+    The m -> 1 compression and its alignment to the block: [Q&A] §2.1.
+    """
+    Kg = np.asarray(Kg, dtype=np.float64)
+    Vg = np.asarray(Vg, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    g = np.einsum("thd,hd->th", Kg, W)                  # [m][H]
+    g = g - g.max(axis=0, keepdims=True)
+    a = np.exp(g)
+    a = a / a.sum(axis=0, keepdims=True)                # softmax over the m tokens
+    Kh = np.einsum("th,thd->hd", a, Kg)
+    Vh = np.einsum("th,thd->hd", a, Vg)
+    return bf16_round(Kh).astype(np.float32), bf16_round(Vh).astype(np.float32)
+
+
+def token_scores(idx_keys: np.ndarray, q_idx: np.ndarray) -> np.ndarray:
+    """Indexer score per token (reading R4): sum over 4 heads x 64 dims of qI * kI_t.
+    idx_keys: [n][4][64]; q_idx: [4][64] -> [n] float64."""
+    k = np.asarray(idx_keys, dtype=np.float64).reshape(len(idx_keys), -1)
+    return k @ np.asarray(q_idx, dtype=np.float64).reshape(-1)
+
+
+def c4_scores(idx_keys: np.ndarray, q_idx: np.ndarray) -> np.ndarray:
+    """C4 entry scores of one block: entry j covers tokens 4j..4j+3; score = mean
+    of their token scores (reading R4). idx_keys: [128][4][64] -> [32]."""
+    s = token_scores(idx_keys, q_idx)
+    return s.reshape(C4_PER_BLOCK, M_CSA).sum(axis=1) / 4.0
+
+
+def select_topk(scores: np.ndarray, k: int):
+    """kk = min(k, N) largest scores, ordered by (score desc, ordinal asc); padded
+    to k with -1 (readings R8, R9). Returns (idx int32 [k], score float64 [k],
+    -inf padded)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.size
+    kk = min(int(k), n)
+    order = np.lexsort((np.arange(n), -scores))[:kk]    # primary: -score, then ordinal
+    idx = np.full(k, -1, np.int32)
+    val = np.full(k, -np.inf, np.float64)
+    idx[:kk] = order
+    val[:kk] = scores[order]
+    return idx, val
+
+
+def attention(q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray) -> np.ndarray:
+    """One softmax over all N cached keys, per head (reading R12).
+    q: [H][D]; Kc, Vc: [N][H][D] -> out [H][D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    Kc = np.asarray(Kc, dtype=np.float64)
+    Vc = np.asarray(Vc, dtype=np.float64)
+    s = np.einsum("nhd,hd->hn", Kc, q) / math.sqrt(q.shape[-1])
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return np.einsum("hn,nhd->hd", p, Vc)
+
+
+# ---------------------------------------------------------------- cache state
+
+class _Block:
+    """One sealed, immutable Block Cache block: 32 C4 + 1 HCA + 128 indexer keys
+    ([Ch12] §2.2; [Q&A] §2.2)."""
+    __slots__ = ("csa_k", "csa_v", "hca_k", "hca_v", "idx")
+
+
+class _State:
+    """Per-request State block: SWA window of exact K/V (oldest first) and the
+    in-flight tail of fewer than 128 tokens ([Q&A] §1.1, §3.3; [Ch12] §2.1)."""
+
+    def __init__(self, n_win: int):
+        self.L = 0
+        self.swa = deque(maxlen=n_win)     # (K, V) per token; drops the oldest ([Q&A] §4)
+        self.tail = []                     # (K, V, kI) per token of the open block
+        self.blocks = []                   # physical block ids, logical order
+
+
+class Oracle:
+    """The cache, driven call by call like the C ABI."""
+
+    def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int):
+        if n_win < BLOCK or n_win % BLOCK:
+            raise OracleError("invalid", "n_win must be a positive multiple of 128")
+        self.n_win = int(n_win)
+        self.W_csa = np.asarray(gate_csa, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
+        self.W_hca = np.asarray(gate_hca, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
+        self.max_states = int(max_states)
+        self.max_blocks = int(max_blocks)
+        self.free_states = list(range(self.max_states))
+        self.free_blocks = list(range(self.max_blocks))
+        heapq.heapify(self.free_states)
+        heapq.heapify(self.free_blocks)
+        self.refcount = np.zeros(self.max_blocks, np.int64)
+        self.store: dict[int, _Block] = {}
+        self.states: dict[int, _State] = {}
+
+    # -- State pool --------------------------------------------------------
+    def state_alloc(self) -> int:
+        """Lowest free State slot, L = 0 ([Ch12] §2.1: one State block per request)."""
+        if not self.free_states:
+            raise OracleError("oom_states")
+        s = heapq.heappop(self.free_states)
+        self.states[s] = _State(self.n_win)
+        return s
+
+    def _get(self, s) -> _State:
+        st = self.states.get(int(s))
+        if st is None:
+            raise OracleError("invalid", f"state {s} not allocated")
+        return st
+
+    def state_free(self, s: int):
+        """Release the whole State block; drop one reference of each block
+        ([Ch12] §2.1 release on request end; §2.2 refcount)."""
+        st = self._get(s)
+        for b in st.blocks:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                del self.store[b]
+                heapq.heappush(self.free_blocks, b)
+        del self.states[int(s)]
+        heapq.heappush(self.free_states, int(s))
+
+    # -- append / seal ---------------------------------------------------------
+    def append(self, states, tokens, defer_seal: bool = False):
+        """Append tokens to each listed state, in list order.
+
+        tokens[i] = (K [n][H][D], V [n][H][D], kI [n][4][64]). Per token
+        ([Q&A] §4): K/V into the tail and SWA (SWA drops its oldest token),
+        L += 1; when the tail holds 128 tokens the block is sealed ([Q&A] §3.1).
+        With defer_seal the full tail waits for compress_flush; appending to a
+        state whose tail is full is an error.
+        """
+        states = [int(s) for s in states]
+        if len(set(states)) != len(states) or len(tokens) != len(states):
+            raise OracleError("invalid", "duplicate or mismatched states")
+        need = 0
+        for s, (K, V, KI) in zip(states, tokens):
+            st = self._get(s)
+            n = len(K)
+            if len(V) != n or len(KI) != n:
+                raise OracleError("invalid", "ragged K/V/kI")
+            if n == 0:
+                continue
+            if len(st.tail) == BLOCK:
+                raise OracleError("state", "tail full: flush before appending")
+            if defer_seal:
+                if len(st.tail) + n > BLOCK:
+                    raise OracleError("state", "deferred append past one block")
+            else:
+                need += (len(st.tail) + n) // BLOCK
+        if need > len(self.free_blocks):
+            raise OracleError("oom_blocks")
+        for s, (K, V, KI) in zip(states, tokens):
+            st = self.states[s]
+            for t in range(len(K)):
+                k = np.asarray(K[t], dtype=np.float32)
+                v = np.asarray(V[t], dtype=np.float32)
+                ki = np.asarray(KI[t], dtype=np.float32)
+                st.swa.append((k, v))
+                st.tail.append((k, v, ki))
+                st.L += 1
+                if len(st.tail) == BLOCK and not defer_seal:
+                    self._seal(st)
+
+    def compress_flush(self, states):
+        """Seal every listed state whose tail holds a full block (deferred seals)."""
+        states = [int(s) for s in states]
+        if len(set(states)) != len(states):
+            raise OracleError("invalid", "duplicate states")
+        need = sum(1 for s in states if len(self._get(s).tail) == BLOCK)
+        if need > len(self.free_blocks):
+            raise OracleError("oom_blocks")
+        for s in states:
+            st = self.states[s]
+            if len(st.tail) == BLOCK:
+                self._seal(st)
+
+    def _seal(self, st: _State):
+        """Compress the 128-token tail into 32 C4 + 1 HCA entries and keep its 128
+        indexer keys, in a new immutable block ([Q&A] §2.2, §3.1; [Ch12] §2.2)."""
+        b = heapq.heappop(self.free_blocks)
+        Kt = np.stack([t[0] for t in st.tail]).astype(np.float64)   # [128][H][D]
+        Vt = np.stack([t[1] for t in st.tail]).astype(np.float64)
+        blk = _Block()
+        blk.csa_k = np.empty((C4_PER_BLOCK, N_HEADS, HEAD_DIM), np.float32)
+        blk.csa_v = np.empty_like(blk.csa_k)
+        for j in range(C4_PER_BLOCK):                 # C4 entry j: tokens 4j .. 4j+3
+            g = slice(M_CSA * j, M_CSA * (j + 1))
+            blk.csa_k[j], blk.csa_v[j] = gated_pool(Kt[g], Vt[g], self.W_csa)
+        blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)     # all 128 tokens
+        blk.idx = np.stack([t[2] for t in st.tail]).astype(np.float32)
+        self.store[b] = blk
+        self.refcount[b] = 1
+        st.blocks.append(b)
+        st.tail = []                                  # tail cleared ([Q&A] §3.1)
+
+    # -- prefix sharing --------------------------------------------------------
+    def share(self, src: int, dst: int):
+        """dst becomes a fork of src (reading R11; [Ch12] §2.2 refcount sharing)."""
+        a, d = self._get(src), self._get(dst)
+        if int(src) == int(dst):
+            raise OracleError("invalid", "src == dst")
+        if d.L != 0 or d.blocks:
+            raise OracleError("state", "dst not fresh")
+        if len(a.tail) == BLOCK:
+            raise OracleError("state", "src has a pending seal")
+        for b in a.blocks:
+            self.refcount[b] += 1
+        d.blocks = list(a.blocks)
+        d.L = a.L
+        d.swa = deque(a.swa, maxlen=self.n_win)
+        d.tail = list(a.tail)
+
+    # -- indexer top-k -----------------------------------------------------------
+    def scores(self, s: int, q_idx) -> np.ndarray:
+        """Scores of the request's sealed C4 entries, ordinal j = 32 * block + slot."""
+        st = self._get(s)
+        out = [c4_scores(self.store[b].idx, q_idx) for b in st.blocks]
+        return np.concatenate(out) if out else np.zeros(0)
+
+    def topk(self, s: int, q_idx, k: int):
+        if k < 1:
+            raise OracleError("invalid", "k must be >= 1")
+        return select_topk(self.scores(s, q_idx), k)
+
+    # -- heterogeneous attention -------------------------------------------------
+    def keys(self, s: int, sel, k: int | None = None):
+        """Materialise the key/value list: SWA (oldest -> newest), HCA of every
+        sealed block, then C4 entries named by `sel` ([Q&A] §4; [Layout]
+        Classical KV cache read modes). Only the first min(k, N_c) entries of sel
+        are read; -1 and out-of-range ordinals are skipped."""
+        st = self._get(s)
+        K = [t[0] for t in st.swa]
+        V = [t[1] for t in st.swa]
+        for b in st.blocks:
+            K.append(self.store[b].hca_k)
+            V.append(self.store[b].hca_v)
+        nc = C4_PER_BLOCK * len(st.blocks)
+        sel = np.asarray(sel if sel is not None else [], dtype=np.int64).reshape(-1)
+        kk = min(len(sel) if k is None else int(k), nc)
+        for j in sel[:kk]:
+            if 0 <= j < nc:
+                blk = self.store[st.blocks[j // C4_PER_BLOCK]]
+                K.append(blk.csa_k[j % C4_PER_BLOCK])
+                V.append(blk.csa_v[j % C4_PER_BLOCK])
+        return np.stack(K), np.stack(V)
+
+    def attend(self, s: int, q, sel, k: int | None = None) -> np.ndarray:
+        st = self._get(s)
+        if st.L == 0:
+            raise OracleError("invalid", "empty state")
+        K, V = self.keys(s, sel, k)
+        return attention(q, K, V)
+
+    # -- introspection -------------------------------------------------------------
+    def info(self, s: int) -> dict:
+        st = self._get(s)
+        d = length_split(st.L)
+        return {"len": st.L, "n_blocks": len(st.blocks), "csa_tail": st.L % M_CSA,
+                "hca_tail": len(st.tail), "swa_len": len(st.swa), "split": d}
+
+    def table(self, s: int) -> list:
+        return list(self._get(s).blocks)
+
+    def block(self, b: int) -> _Block:
+        return self.store[int(b)]

@@ -1,0 +1,430 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test ties one oracle function to something other than itself: the pages'
+worked example (tests/golden/l130_example.json), closed forms, invariants,
+exact integer arithmetic, library routines (torch bf16 conversion, torch SDPA,
+Python's sort) or brute force on small inputs.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import (BLOCK, C4_PER_BLOCK, HEAD_DIM, N_HEADS, Oracle, OracleError,
+                    attention, bf16_round, c4_scores, gated_pool, length_split,
+                    select_topk, token_scores)
+
+SEED = 0x1234
+
+
+def toks(key, p0, n, seed=SEED):
+    """Raw inputs of n tokens at positions p0.. as float64 (exact bf16 / fp32 values)."""
+    pos = np.arange(p0, p0 + n)
+    K = synth.bf16_bits_to_f32(synth.tokens_bf16(seed, synth.STREAM_K, key, pos)).astype(np.float64)
+    V = synth.bf16_bits_to_f32(synth.tokens_bf16(seed, synth.STREAM_V, key, pos)).astype(np.float64)
+    KI = synth.tokens_f32(seed, synth.STREAM_IDXK, key, pos).astype(np.float64)
+    return K, V, KI
+
+
+def make_oracle(n_win=128, max_states=8, max_blocks=64, gates=None):
+    Wc, Wh = gates if gates is not None else synth.gate_weights(SEED)
+    return Oracle(n_win, Wc, Wh, max_states, max_blocks)
+
+
+# ------------------------------------------------------------------ the pages' example
+
+def test_l130_worked_example(root):
+    g = json.load(open(os.path.join(root, "tests", "golden", "l130_example.json")))
+    o = make_oracle()
+    s = o.state_alloc()
+    K, V, KI = toks(0, 0, g["L"])
+    o.append([s], [(K, V, KI)])
+    info = o.info(s)
+    assert info["len"] == g["L"]
+    assert info["n_blocks"] == g["blocks"]
+    assert info["split"]["c4"] == g["c4_entries"] and info["split"]["hca"] == g["hca_entries"]
+    assert info["hca_tail"] == g["tail_tokens"] and info["csa_tail"] == g["csa_tail"]
+    # Classical holds exactly tokens [0, 128): rebuild the block from them
+    a, b = g["classical_positions"]
+    blk = o.block(o.table(s)[0])
+    for j in range(C4_PER_BLOCK):
+        ck, cv = gated_pool(K[a + 4 * j:a + 4 * j + 4], V[a + 4 * j:a + 4 * j + 4], o.W_csa)
+        assert np.array_equal(ck, blk.csa_k[j]) and np.array_equal(cv, blk.csa_v[j])
+    hk, hv = gated_pool(K[a:b], V[a:b], o.W_hca)
+    assert np.array_equal(hk, blk.hca_k) and np.array_equal(hv, blk.hca_v)
+    assert np.array_equal(blk.idx, KI[a:b].astype(np.float32))
+    # tokens 128, 129 stay in the tail (State pool), not in Classical
+    t0, t1 = g["tail_positions"]
+    st = o.states[s]
+    assert len(st.tail) == t1 - t0
+    for i, p in enumerate(range(t0, t1)):
+        assert np.array_equal(st.tail[i][0], K[p].astype(np.float32))
+
+
+@pytest.mark.parametrize("L", [0, 1, 3, 4, 127, 128, 129, 130, 255, 256, 257, 383, 640, 1000])
+def test_length_decomposition(L):
+    """L = 128 q + r -> 32q C4 + q HCA, tail r; CSA tail <= 3, HCA tail <= 127."""
+    o = make_oracle(max_blocks=16)
+    s = o.state_alloc()
+    K, V, KI = toks(1, 0, L)
+    o.append([s], [(K, V, KI)])
+    info = o.info(s)
+    q, r = L // 128, L % 128
+    assert info["n_blocks"] == q and len(o.table(s)) == q
+    assert info["split"] == length_split(L)
+    assert info["split"]["c4"] == 32 * q and info["hca_tail"] == r
+    assert 0 <= info["csa_tail"] <= 3 and 0 <= info["hca_tail"] <= 127
+    assert info["csa_tail"] == L % 4
+
+
+def test_length_split_closed_form():
+    for L in range(0, 5000, 7):
+        d = length_split(L)
+        assert 128 * d["blocks"] + d["tail"] == L and 0 <= d["tail"] < 128
+        assert d["c4"] == 32 * d["blocks"] and d["hca"] == d["blocks"]
+
+
+@pytest.mark.parametrize("n_win,L", [(128, 5), (128, 128), (128, 300), (256, 255), (256, 700)])
+def test_swa_is_last_window(n_win, L):
+    """The SWA holds exactly the last min(L, n_win) tokens, oldest first."""
+    o = make_oracle(n_win=n_win, max_blocks=16)
+    s = o.state_alloc()
+    K, V, KI = toks(2, 0, L)
+    # append in uneven pieces
+    cuts = [0, 1, 7, 100, 129, L]
+    cuts = sorted(set(min(c, L) for c in cuts))
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o.append([s], [(K[a:b], V[a:b], KI[a:b])])
+    w = min(L, n_win)
+    swa = o.states[s].swa
+    assert len(swa) == w
+    for i, (k, v) in enumerate(swa):
+        assert np.array_equal(k, K[L - w + i].astype(np.float32))
+        assert np.array_equal(v, V[L - w + i].astype(np.float32))
+
+
+def test_sealed_blocks_immutable():
+    o = make_oracle(max_blocks=16)
+    s = o.state_alloc()
+    K, V, KI = toks(3, 0, 700)
+    o.append([s], [(K[:300], V[:300], KI[:300])])
+    b0 = o.table(s)[0]
+    snap = {a: getattr(o.block(b0), a).copy() for a in ("csa_k", "csa_v", "hca_k", "hca_v", "idx")}
+    o.append([s], [(K[300:], V[300:], KI[300:])])
+    for a, v in snap.items():
+        assert np.array_equal(getattr(o.block(b0), a), v)
+
+
+# ------------------------------------------------------------------ bf16 rounding
+
+def test_bf16_round_matches_torch_on_float32():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(200000) * 10.0 ** rng.integers(-6, 6, 200000),
+                        synth.bf16_bits_to_f32(np.arange(0x0080, 0x7F00, 7, dtype=np.uint16))
+                        * (1 + 2.0 ** -8)]).astype(np.float32)   # exact ties
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(bf16_round(x.astype(np.float64)), ref)
+
+
+def test_bf16_round_exact_nearest_float64():
+    """Brute force with exact rationals: the nearest of the two bf16 neighbours."""
+    rng = np.random.default_rng(6)
+    xs = rng.standard_normal(3000) * 3.0
+    for x in xs:
+        y = float(bf16_round(x))
+        e = math.frexp(x)[1]
+        ulp = Fraction(2) ** (e - 8)
+        lo = Fraction(math.floor(Fraction(x) / ulp)) * ulp
+        hi = lo + ulp
+        dx = Fraction(x)
+        if dx - lo < hi - dx:
+            exp = lo
+        elif dx - lo > hi - dx:
+            exp = hi
+        else:
+            exp = lo if (lo / ulp) % 2 == 0 else hi
+        assert Fraction(y) == exp
+
+
+# ------------------------------------------------------------------ compressor (reading R1)
+
+def test_pool_zero_gates_is_mean():
+    K, V, _ = toks(4, 0, 128)
+    Z = np.zeros((N_HEADS, HEAD_DIM))
+    for m in (4, 128):
+        ck, cv = gated_pool(K[:m], V[:m], Z)
+        assert np.array_equal(ck, bf16_round(np.mean(K[:m], axis=0)).astype(np.float32))
+        assert np.array_equal(cv, bf16_round(np.mean(V[:m], axis=0)).astype(np.float32))
+
+
+def test_pool_two_tokens_logistic():
+    """m = 2: alpha_0 = 1 / (1 + exp(g1 - g0)), alpha_1 = 1 - alpha_0."""
+    K, V, _ = toks(5, 0, 2)
+    W = synth.gate_weights(99)[0].astype(np.float64) * 10
+    ck, cv = gated_pool(K, V, W)
+    for h in range(N_HEADS):
+        g0 = float(np.dot(W[h], K[0, h]))
+        g1 = float(np.dot(W[h], K[1, h]))
+        a0 = 1.0 / (1.0 + math.exp(g1 - g0))
+        exp_k = bf16_round(a0 * K[0, h] + (1 - a0) * K[1, h])
+        exp_v = bf16_round(a0 * V[0, h] + (1 - a0) * V[1, h])
+        # one bf16 ulp of slack for fp64 rounding order at exact ties
+        assert np.allclose(ck[h], exp_k, rtol=2 ** -7, atol=0)
+        assert np.allclose(cv[h], exp_v, rtol=2 ** -7, atol=0)
+        assert np.mean(ck[h] == exp_k) > 0.98
+
+
+def test_pool_permutation_invariant_and_convex():
+    K, V, _ = toks(6, 0, 128)
+    W = synth.gate_weights(7)[1]
+    rng = np.random.default_rng(0)
+    for m in (4, 128):
+        perm = rng.permutation(m)
+        a = gated_pool(K[:m], V[:m], W)
+        b = gated_pool(K[:m][perm], V[:m][perm], W)
+        assert np.allclose(a[0], b[0], rtol=2 ** -7, atol=0) and np.allclose(a[1], b[1], rtol=2 ** -7, atol=0)
+        for ent, src in ((a[0], K[:m]), (a[1], V[:m])):
+            assert np.all(ent >= src.min(axis=0)) and np.all(ent <= src.max(axis=0))
+
+
+def test_pool_dominant_gate_selects_token():
+    K, V, _ = toks(8, 0, 4)
+    W = 1000.0 * K[2]          # gate of token 2 dominates in every head
+    ck, cv = gated_pool(K, V, W)
+    assert np.array_equal(ck, K[2].astype(np.float32)) and np.array_equal(cv, V[2].astype(np.float32))
+
+
+def test_seal_uses_csa_gates_for_c4_and_hca_gates_for_hca():
+    K, V, KI = toks(9, 0, 128)
+    Wr = synth.gate_weights(11)[0] * 50
+    Z = np.zeros((N_HEADS, HEAD_DIM), np.float32)
+    for Wc, Wh in ((Z, Wr), (Wr, Z)):
+        o = make_oracle(gates=(Wc, Wh))
+        s = o.state_alloc()
+        o.append([s], [(K, V, KI)])
+        blk = o.block(o.table(s)[0])
+        mean_c = np.array([bf16_round(K[4 * j:4 * j + 4].mean(axis=0)) for j in range(32)])
+        mean_h = bf16_round(K.mean(axis=0))
+        if Wc is Z:
+            assert np.array_equal(blk.csa_k, mean_c.astype(np.float32))
+            assert not np.array_equal(blk.hca_k, mean_h.astype(np.float32))
+        else:
+            assert np.array_equal(blk.hca_k, mean_h.astype(np.float32))
+            assert not np.array_equal(blk.csa_k, mean_c.astype(np.float32))
+
+
+# ------------------------------------------------------------------ indexer (reading R4)
+
+def test_indexer_scores_exact_integer():
+    """Inputs are odd multiples of 2**-8: scores * 2**18 are exact integers; compare
+    with integer arithmetic on the generator's integers."""
+    pos = np.arange(0, 128)
+    zi = synth.z_ints(SEED, synth.STREAM_IDXK, 3, (pos[:, None] * 256 + np.arange(256)).astype(np.uint64))
+    qi = synth.z_ints(SEED, synth.STREAM_QI, 3, np.arange(256, dtype=np.uint64))
+    KI = zi.reshape(128, 4, 64) / 256.0
+    q = qi.reshape(4, 64) / 256.0
+    S = c4_scores(KI, q)
+    for j in range(32):
+        exact = sum(int(qi[e]) * int(zi[4 * j + u, e]) for u in range(4) for e in range(256))
+        assert Fraction(float(S[j])) == Fraction(exact, 4 * 65536)
+
+
+def test_indexer_one_hot_query_picks_coordinate():
+    _, _, KI = toks(10, 0, 128)
+    for h, d in ((0, 0), (3, 63), (1, 17)):
+        q = np.zeros((4, 64))
+        q[h, d] = 1.0
+        S = c4_scores(KI, q)
+        for j in range(32):
+            assert S[j] == np.mean([KI[4 * j + u, h, d] for u in range(4)])
+        assert np.array_equal(token_scores(KI, q), KI[:, h, d])
+
+
+# ------------------------------------------------------------------ top-k (readings R8, R9)
+
+def test_topk_full_sort_when_k_covers_all():
+    rng = np.random.default_rng(1)
+    s = np.round(rng.standard_normal(100) * 4) / 4      # many ties
+    idx, val = select_topk(s, 128)
+    ref = sorted(range(100), key=lambda j: (-s[j], j))
+    assert list(idx[:100]) == ref and np.all(idx[100:] == -1)
+    assert np.all(np.isneginf(val[100:]))
+
+
+def test_topk_brute_force_small():
+    rng = np.random.default_rng(2)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        k = int(rng.integers(1, 50))
+        s = rng.integers(-3, 4, n).astype(np.float64)
+        idx, _ = select_topk(s, k)
+        kk = min(k, n)
+        chosen = idx[:kk]
+        # brute force: j is chosen iff fewer than kk entries beat it under (score desc, ordinal asc)
+        beats = lambda a, b: s[a] > s[b] or (s[a] == s[b] and a < b)
+        exp = [j for j in range(n) if sum(beats(i, j) for i in range(n)) < kk]
+        assert sorted(chosen.tolist()) == exp
+        for a, b in zip(chosen[:-1], chosen[1:]):
+            assert beats(a, b)
+        assert np.all(idx[kk:] == -1)
+
+
+def test_topk_ties_lowest_index_and_negzero():
+    s = np.array([1.0, 0.0, -0.0, 1.0, 0.0, 2.0])
+    idx, _ = select_topk(s, 4)
+    assert list(idx) == [5, 0, 3, 1]
+
+
+# ------------------------------------------------------------------ attention
+
+def sdpa64(q, Kc, Vc):
+    qt = torch.from_numpy(np.asarray(q, np.float64))[:, None, :]            # [H][1][D]
+    kt = torch.from_numpy(np.asarray(Kc, np.float64)).permute(1, 0, 2).contiguous()
+    vt = torch.from_numpy(np.asarray(Vc, np.float64)).permute(1, 0, 2).contiguous()
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0, :].numpy()
+
+
+def test_attention_matches_sdpa():
+    K, V, _ = toks(11, 0, 50)
+    q = toks(12, 0, 1)[0][0]
+    assert np.allclose(attention(q, K, V), sdpa64(q, K, V), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_uniform_keys_is_mean_of_values():
+    K, V, _ = toks(13, 0, 9)
+    q = toks(14, 0, 1)[0][0]
+    Ku = np.repeat(K[:1], 9, axis=0)
+    assert np.allclose(attention(q, Ku, V), V.mean(axis=0), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("L", [1, 37, 127])
+def test_decode_without_blocks_is_plain_mha(L):
+    """L < 128: no blocks, the SWA holds every token: plain MHA decode."""
+    o = make_oracle()
+    s = o.state_alloc()
+    K, V, KI = toks(15, 0, L)
+    o.append([s], [(K, V, KI)])
+    q = toks(16, 0, 1)[0][0]
+    out = o.attend(s, q, [], k=16)
+    assert np.allclose(out, sdpa64(q, K, V), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_win,L,k", [(128, 130, 16), (128, 256, 64), (256, 777, 40), (128, 1000, 1000)])
+def test_attention_brute_force_concatenated_cache(n_win, L, k):
+    """Brute force from the raw tokens: SWA = last min(L, n_win) tokens, HCA = pool of
+    each 128-token group, C4 = pool of each selected 4-token group; one softmax."""
+    o = make_oracle(n_win=n_win, max_blocks=16)
+    s = o.state_alloc()
+    K, V, KI = toks(17, 0, L)
+    o.append([s], [(K, V, KI)])
+    qi = synth.tokens_f32(SEED, synth.STREAM_QI, 17, [L - 1])[0]
+    q = toks(18, 0, 1)[0][0]
+    sel, _ = o.topk(s, qi, k)
+    w = min(L, n_win)
+    nb = L // 128
+    Kc = [K[L - w:]]
+    Vc = [V[L - w:]]
+    for b in range(nb):
+        hk, hv = gated_pool(K[128 * b:128 * b + 128], V[128 * b:128 * b + 128], o.W_hca)
+        Kc.append(hk[None]); Vc.append(hv[None])
+    # the selection, checked by brute force on the raw indexer keys
+    allS = np.concatenate([c4_scores(KI[128 * b:128 * b + 128], qi) for b in range(nb)])
+    assert list(sel[:min(k, 32 * nb)]) == sorted(range(32 * nb), key=lambda j: (-allS[j], j))[:min(k, 32 * nb)]
+    for j in sel:
+        if j >= 0:
+            ck, cv = gated_pool(K[4 * j:4 * j + 4], V[4 * j:4 * j + 4], o.W_csa)
+            Kc.append(ck[None]); Vc.append(cv[None])
+    Kc = np.concatenate(Kc)
+    Vc = np.concatenate(Vc)
+    assert len(Kc) == w + nb + min(k, 32 * nb)
+    ref = sdpa64(q, Kc, Vc)
+    assert np.allclose(o.attend(s, q, sel, k), ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ sharing, refcounts, ids
+
+def test_share_bit_identical_to_independent_rebuild():
+    o = make_oracle(n_win=256, max_states=8, max_blocks=32)
+    K, V, KI = toks(19, 0, 900)
+    p = o.state_alloc()
+    o.append([p], [(K[:384], V[:384], KI[:384])])
+    c1, c2 = o.state_alloc(), o.state_alloc()
+    o.share(p, c1)
+    o.share(p, c2)
+    for b in o.table(p):
+        assert o.refcount[b] == 3
+    o.append([c1, c2], [(K[384:900], V[384:900], KI[384:900]), (K[384:500], V[384:500], KI[384:500])])
+    o.state_free(p)
+    for b in o.table(c1)[:3]:
+        assert o.refcount[b] == 2
+    r = o.state_alloc()
+    o.append([r], [(K, V, KI)])
+    assert o.table(c1)[:3] == o.table(c2)[:3]
+    for a, b in zip(o.table(c1), o.table(r)):
+        A, B = o.block(a), o.block(b)
+        for f in ("csa_k", "csa_v", "hca_k", "hca_v", "idx"):
+            assert np.array_equal(getattr(A, f), getattr(B, f))
+    for (k1, v1), (k2, v2) in zip(o.states[c1].swa, o.states[r].swa):
+        assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_free_returns_blocks_only_at_zero_refcount_and_lowest_id_first():
+    o = make_oracle(max_states=4, max_blocks=8)
+    K, V, KI = toks(20, 0, 512)
+    a = o.state_alloc()
+    o.append([a], [(K[:256], V[:256], KI[:256])])          # blocks 0, 1
+    b = o.state_alloc()
+    o.share(a, b)
+    o.append([b], [(K[256:512], V[256:512], KI[256:512])])  # blocks 2, 3
+    assert o.table(a) == [0, 1] and o.table(b) == [0, 1, 2, 3]
+    o.state_free(a)
+    assert sorted(o.free_blocks) == [4, 5, 6, 7]
+    o.state_free(b)
+    assert sorted(o.free_blocks) == list(range(8))
+    c = o.state_alloc()
+    assert c == 0
+    o.append([c], [(K[:128], V[:128], KI[:128])])
+    assert o.table(c) == [0]
+
+
+def test_deferred_seal_equals_default():
+    K, V, KI = toks(21, 0, 256)
+    o1, o2 = make_oracle(), make_oracle()
+    s1, s2 = o1.state_alloc(), o2.state_alloc()
+    o1.append([s1], [(K, V, KI)])
+    o2.append([s2], [(K[:128], V[:128], KI[:128])], defer_seal=True)
+    assert o2.info(s2)["n_blocks"] == 0 and o2.info(s2)["hca_tail"] == 128
+    with pytest.raises(OracleError) as e:
+        o2.append([s2], [(K[128:129], V[128:129], KI[128:129])])
+    assert e.value.kind == "state"
+    o2.compress_flush([s2])
+    o2.append([s2], [(K[128:], V[128:], KI[128:])])
+    for a, b in zip(o1.table(s1), o2.table(s2)):
+        for f in ("csa_k", "csa_v", "hca_k", "hca_v", "idx"):
+            assert np.array_equal(getattr(o1.block(a), f), getattr(o2.block(b), f))
+
+
+def test_errors_leave_state_unchanged():
+    o = make_oracle(max_states=2, max_blocks=2)
+    K, V, KI = toks(22, 0, 400)
+    a, b = o.state_alloc(), o.state_alloc()
+    with pytest.raises(OracleError) as e:
+        o.state_alloc()
+    assert e.value.kind == "oom_states"
+    o.append([a], [(K[:200], V[:200], KI[:200])])
+    with pytest.raises(OracleError) as e:       # needs 2 more blocks, 1 free
+        o.append([a, b], [(K[200:300], V[200:300], KI[200:300]), (K[:128], V[:128], KI[:128])])
+    assert e.value.kind == "oom_blocks"
+    assert o.info(a)["len"] == 200 and o.info(b)["len"] == 0
+    o.append([b], [(K[:5], V[:5], KI[:5])])
+    with pytest.raises(OracleError) as e:
+        o.share(a, b)
+    assert e.value.kind == "state"
+    with pytest.raises(OracleError):
+        o.append([a, a], [(K[:1], V[:1], KI[:1])] * 2)
