@@ -1,0 +1,315 @@
+"""Heterogeneous sparse-attention KV cache for MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/hsa.h: it checks tensor dtypes and
+shapes and passes device pointers and the current HIP stream; every step of the
+decode path runs in the library's HIP kernels. There is no Python or CPU
+fallback: without the built library every call raises.
+
+PyTorch supplies device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhsa.so")
+
+H, D, HI, DI = 16, 128, 4, 64
+MAX_TOPK = 4096
+APPEND_DEFER_SEAL = 1
+
+KERNELS = ("append", "seal", "write", "score", "select", "attend", "combine")
+KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "Block Cache full", -3: "no free State slot",
+           -4: "lifecycle error", -5: "HIP runtime error"}
+
+
+class HsaError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__(f"{where}: {_STATUS.get(code, code)} ({code}): {detail}")
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("m_csa", ctypes.c_int32), ("m_hca", ctypes.c_int32),
+                ("n_win", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
+                ("idx_dim", ctypes.c_int32), ("max_states", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int64), ("max_blocks_per_state", ctypes.c_int64),
+                ("gate_csa", ctypes.POINTER(ctypes.c_float)),
+                ("gate_hca", ctypes.POINTER(ctypes.c_float))]
+
+
+class _StateInfo(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_int64), ("n_blocks", ctypes.c_int64),
+                ("csa_tail", ctypes.c_int32), ("hca_tail", ctypes.c_int32),
+                ("swa_len", ctypes.c_int32), ("pending_seal", ctypes.c_int32)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U32 = ctypes.c_uint32
+
+# name -> argument types (all return int32 status)
+SIGNATURES = {
+    "hsa_create": [ctypes.POINTER(_Config), ctypes.c_int, ctypes.POINTER(_P)],
+    "hsa_destroy": [_P],
+    "hsa_state_alloc": [_P, ctypes.POINTER(_I32)],
+    "hsa_state_free": [_P, _I32],
+    "hsa_append_kv": [_P, _I32, _P, _P, _P, _P, _P, _U32, _P],
+    "hsa_compress_flush": [_P, _I32, _P, _P],
+    "hsa_block_table_share": [_P, _I32, _I32, _P],
+    "hsa_indexer_topk": [_P, _I32, _P, _P, _I32, _P, _P, _P],
+    "hsa_decode_attend": [_P, _I32, _P, _P, _P, _I32, _P, _P],
+    "hsa_decode_step": [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P],
+    "hsa_state_query": [_P, _I32, ctypes.POINTER(_StateInfo)],
+    "hsa_block_table_get": [_P, _I32, _P, _I64, ctypes.POINTER(_I64)],
+    "hsa_block_refcount": [_P, _I32, ctypes.POINTER(_I32)],
+    "hsa_export_block": [_P, _I32, _P, _P, _P, _P, _P, _P],
+    "hsa_export_state": [_P, _I32, _P, _P, _P, _P],
+    "hsa_timing_enable": [_P, _U32],
+    "hsa_timing_read": [_P, _P, _P],
+}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m heterogeneous_sparse_attention_amd.build` "
+                           "(there is no fallback)")
+    lib = ctypes.CDLL(path)
+    for name, argt in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argt
+        fn.restype = _I32
+    lib.hsa_status_str.restype = ctypes.c_char_p
+    lib.hsa_status_str.argtypes = [_I32]
+    lib.hsa_last_error.restype = ctypes.c_char_p
+    lib.hsa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise HsaError(code, where, _lib.hsa_last_error().decode(errors="replace"))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _host_i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_i64(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int64).reshape(-1))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev(t, dtype, shape, name):
+    """Device pointer of a contiguous CUDA tensor of the given dtype and shape."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+
+
+class Cache:
+    """One Block Cache + State Cache on one GPU (an hsa_ctx)."""
+
+    def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
+                 max_blocks_per_state: int = 0, device: int = 0):
+        lib = load()
+        self._gc = np.ascontiguousarray(np.asarray(gate_csa, np.float32).reshape(H * D))
+        self._gh = np.ascontiguousarray(np.asarray(gate_hca, np.float32).reshape(H * D))
+        cfg = _Config(H, D, 4, 128, n_win, HI, DI, max_states, max_blocks, max_blocks_per_state,
+                      self._gc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                      self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        ctx = ctypes.c_void_p()
+        _check(lib.hsa_create(ctypes.byref(cfg), device, ctypes.byref(ctx)), "hsa_create")
+        self._ctx = ctx
+        self.n_win = n_win
+        self.max_states = max_states
+        self.max_blocks = max_blocks
+        self.device = device
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            _lib.hsa_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    # -- State pool -------------------------------------------------------------
+    def state_alloc(self) -> int:
+        s = _I32()
+        _check(_lib.hsa_state_alloc(self._ctx, ctypes.byref(s)), "hsa_state_alloc")
+        return s.value
+
+    def state_free(self, s: int):
+        _check(_lib.hsa_state_free(self._ctx, int(s)), "hsa_state_free")
+
+    # -- append / seal ------------------------------------------------------------
+    def append_kv(self, states, cu_tokens, k, v, idx_k, defer: bool = False, stream=None):
+        import torch
+        st, stp = _host_i32(states)
+        cu, cup = _host_i64(cu_tokens)
+        if cu.size != st.size + 1:
+            raise ValueError("cu_tokens must have len(states) + 1 entries")
+        T = int(cu[-1]) if cu.size else 0
+        kp = _dev(k, torch.bfloat16, (T, H, D), "k")
+        vp = _dev(v, torch.bfloat16, (T, H, D), "v")
+        ip = _dev(idx_k, torch.float32, (T, HI, DI), "idx_k")
+        _check(_lib.hsa_append_kv(self._ctx, st.size, stp, cup, kp, vp, ip,
+                                  APPEND_DEFER_SEAL if defer else 0, _stream(stream)),
+               "hsa_append_kv")
+
+    def compress_flush(self, states, stream=None):
+        st, stp = _host_i32(states)
+        _check(_lib.hsa_compress_flush(self._ctx, st.size, stp, _stream(stream)), "hsa_compress_flush")
+
+    def block_table_share(self, src: int, dst: int, stream=None):
+        _check(_lib.hsa_block_table_share(self._ctx, int(src), int(dst), _stream(stream)),
+               "hsa_block_table_share")
+
+    # -- indexer top-k --------------------------------------------------------------
+    def indexer_topk(self, states, q_idx, k: int, idx_out=None, score_out=None, stream=None):
+        import torch
+        st, stp = _host_i32(states)
+        n = st.size
+        qp = _dev(q_idx, torch.float32, (n, HI, DI), "q_idx")
+        if idx_out is None:
+            idx_out = torch.empty((n, k), dtype=torch.int32, device=q_idx.device)
+        op = _dev(idx_out, torch.int32, (n, k), "idx_out")
+        sp = ctypes.c_void_p(0)
+        if score_out is not None:
+            sp = _dev(score_out, torch.float32, (n, k), "score_out")
+        _check(_lib.hsa_indexer_topk(self._ctx, n, stp, qp, int(k), op, sp, _stream(stream)),
+               "hsa_indexer_topk")
+        return idx_out, score_out
+
+    # -- attention -----------------------------------------------------------------
+    def decode_attend(self, states, q, topk, k: int, out=None, stream=None):
+        import torch
+        st, stp = _host_i32(states)
+        n = st.size
+        qp = _dev(q, torch.bfloat16, (n, H, D), "q")
+        tp = ctypes.c_void_p(0)
+        if k > 0:
+            tp = _dev(topk, torch.int32, (n, k), "topk")
+        if out is None:
+            out = torch.empty((n, H, D), dtype=torch.float32, device=q.device)
+        op = _dev(out, torch.float32, (n, H, D), "out")
+        _check(_lib.hsa_decode_attend(self._ctx, n, stp, qp, tp, int(k), op, _stream(stream)),
+               "hsa_decode_attend")
+        return out
+
+    def decode_step(self, states, k_new, v_new, idx_new, q, q_idx, k: int,
+                    topk_out=None, score_out=None, out=None, stream=None):
+        import torch
+        st, stp = _host_i32(states)
+        n = st.size
+        dev = q.device
+        if topk_out is None:
+            topk_out = torch.empty((n, k), dtype=torch.int32, device=dev)
+        if out is None:
+            out = torch.empty((n, H, D), dtype=torch.float32, device=dev)
+        sp = ctypes.c_void_p(0)
+        if score_out is not None:
+            sp = _dev(score_out, torch.float32, (n, k), "score_out")
+        _check(_lib.hsa_decode_step(
+            self._ctx, n, stp,
+            _dev(k_new, torch.bfloat16, (n, H, D), "k_new"),
+            _dev(v_new, torch.bfloat16, (n, H, D), "v_new"),
+            _dev(idx_new, torch.float32, (n, HI, DI), "idx_new"),
+            _dev(q, torch.bfloat16, (n, H, D), "q"),
+            _dev(q_idx, torch.float32, (n, HI, DI), "q_idx"),
+            int(k), _dev(topk_out, torch.int32, (n, k), "topk_out"), sp,
+            _dev(out, torch.float32, (n, H, D), "out"), _stream(stream)), "hsa_decode_step")
+        return topk_out, score_out, out
+
+    # -- introspection -----------------------------------------------------------------
+    def state_query(self, s: int) -> dict:
+        info = _StateInfo()
+        _check(_lib.hsa_state_query(self._ctx, int(s), ctypes.byref(info)), "hsa_state_query")
+        return {f: getattr(info, f) for f, _ in _StateInfo._fields_}
+
+    def block_table(self, s: int) -> list:
+        n = _I64()
+        _check(_lib.hsa_block_table_get(self._ctx, int(s), None, 0, ctypes.byref(n)), "hsa_block_table_get")
+        ids = np.zeros(max(n.value, 1), np.int32)
+        _check(_lib.hsa_block_table_get(self._ctx, int(s), ids.ctypes.data_as(ctypes.c_void_p),
+                                        ids.size, ctypes.byref(n)), "hsa_block_table_get")
+        return ids[:n.value].tolist()
+
+    def refcount(self, b: int) -> int:
+        rc = _I32()
+        _check(_lib.hsa_block_refcount(self._ctx, int(b), ctypes.byref(rc)), "hsa_block_refcount")
+        return rc.value
+
+    def export_block(self, b: int, stream=None) -> dict:
+        """bf16 arrays as uint16 bits; indexer keys as float32."""
+        out = {"csa_k": np.zeros((32, H, D), np.uint16), "csa_v": np.zeros((32, H, D), np.uint16),
+               "hca_k": np.zeros((H, D), np.uint16), "hca_v": np.zeros((H, D), np.uint16),
+               "idx": np.zeros((128, HI, DI), np.float32)}
+        p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
+        _check(_lib.hsa_export_block(self._ctx, int(b), p["csa_k"], p["csa_v"], p["hca_k"],
+                                     p["hca_v"], p["idx"], _stream(stream)), "hsa_export_block")
+        return out
+
+    def export_state(self, s: int, stream=None) -> dict:
+        out = {"swa_k": np.zeros((self.n_win, H, D), np.uint16),
+               "swa_v": np.zeros((self.n_win, H, D), np.uint16),
+               "idx_tail": np.zeros((128, HI, DI), np.float32)}
+        p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
+        _check(_lib.hsa_export_state(self._ctx, int(s), p["swa_k"], p["swa_v"], p["idx_tail"],
+                                     _stream(stream)), "hsa_export_state")
+        return out
+
+    # -- timing -----------------------------------------------------------------------
+    def timing_enable(self, kernels=()):
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNEL_ID[k]
+        _check(_lib.hsa_timing_enable(self._ctx, mask), "hsa_timing_enable")
+
+    def timing_read(self) -> dict:
+        ms = np.zeros(len(KERNELS), np.float64)
+        n = np.zeros(len(KERNELS), np.int64)
+        _check(_lib.hsa_timing_read(self._ctx, ms.ctypes.data_as(ctypes.c_void_p),
+                                    n.ctypes.data_as(ctypes.c_void_p)), "hsa_timing_read")
+        return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(KERNELS)}

@@ -1,0 +1,140 @@
+// device.h - layout constants, launch descriptors and wavefront helpers shared by
+// the gfx950 kernels of the heterogeneous KV cache.
+//
+// HBM layout (structure of arrays, indexed by physical id):
+//   swa_k, swa_v  [max_states][n_win][16][128] bf16   token p of state s in slot p mod n_win
+//   idx_tail      [max_states][128][4][64]   fp32     token p in slot p mod 128
+//   csa_k, csa_v  [max_blocks][32][16][128]  bf16     C4 entry j of a block = tokens 4j..4j+3
+//   hca_k, hca_v  [max_blocks][16][128]      bf16
+//   idx_k         [max_blocks][128][4][64]   fp32
+//   table         [max_states][table_stride] int32    logical block -> physical id
+// One K or V row (a token or an entry) is 16 x 128 bf16 = 4 KiB contiguous, so every
+// row read is a fully coalesced 4 KiB burst; one indexer row is 1 KiB.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hsa {
+
+constexpr int kH = 16;
+constexpr int kD = 128;
+constexpr int kRow = kH * kD;      // 2048 bf16 per K or V row
+constexpr int kHi = 4;
+constexpr int kDi = 64;
+constexpr int kIRow = kHi * kDi;   // 256 fp32 per indexer row
+constexpr int kBlk = 128;          // tokens per block = lcm(4, 128)
+constexpr int kC4 = 32;            // C4 entries per block
+constexpr int kMaxReq = 64;        // requests per launch descriptor
+constexpr int kSealSplit = 8;      // workgroups per decode-time seal (16 tokens each)
+constexpr int kPartFloats = 2 * kH + 2 * kRow;  // one HCA seal partial: m, l, acc K, acc V
+constexpr int kMaxTopk = 4096;
+
+struct Pools {
+  uint16_t* swa_k;
+  uint16_t* swa_v;
+  float* idx_tail;
+  uint16_t* csa_k;
+  uint16_t* csa_v;
+  uint16_t* hca_k;
+  uint16_t* hca_v;
+  float* idx_k;
+  int32_t* table;
+  int64_t table_stride;
+  const float* gate_csa;
+  const float* gate_hca;
+  int32_t n_win;
+  int32_t max_blocks;   // physical ids are in [0, max_blocks)
+};
+
+// One request of a launch: its state, its length and sealed-block count after the
+// call, and a kernel-specific field (decode append: id of the block this token
+// seals, or -1).
+struct Req {
+  int32_t state;
+  int32_t len;
+  int32_t nb;
+  int32_t aux;
+};
+
+struct ReqBatch {
+  int32_t n;
+  int32_t n_seal;              // decode append: how many requests seal
+  int32_t pad_[2];
+  Req r[kMaxReq];
+  int8_t seal_req[kMaxReq];    // decode append: batch index of each sealing request
+};
+
+// A block to seal, read from device memory by the bulk seal kernel.
+struct SealDesc {
+  int32_t state;
+  int32_t id;
+  int64_t pos0;      // position of the block's first token (128 * logical block)
+  int64_t len_old;   // tokens < len_old are resident in the state; others come from the input
+  int64_t row0;      // packed input row of position len_old
+};
+
+// A request of a bulk append, for the ring / indexer-tail write kernel.
+struct WriteDesc {
+  int32_t state;
+  int32_t nb_new;
+  int64_t len_old;
+  int64_t len_new;
+  int64_t w0;        // first position written: max(len_old, len_new - n_win)
+  int64_t row0;      // packed input row of position len_old
+  int64_t cum;       // tokens written by earlier requests of the call
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+
+__device__ __forceinline__ void unpack8(const uint4& w, float* f) {
+  f[0] = bf_lo(w.x); f[1] = bf_hi(w.x);
+  f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
+  f[4] = bf_lo(w.z); f[5] = bf_hi(w.z);
+  f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the sum.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace hsa

@@ -1,0 +1,604 @@
+// hsa.cpp - the C ABI (include/hsa.h): validation, host control plane, pool and
+// scratch management, and kernel launches on the caller's stream.
+#include "../../include/hsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "control.h"
+#include "device.h"
+#include "kernels.h"
+
+using namespace hsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& why) {
+  g_err = why;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                               \
+  do {                                                                              \
+    hipError_t e_ = (expr);                                                         \
+    if (e_ != hipSuccess) return fail(kDevice, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+}  // namespace
+
+struct hsa_ctx {
+  int device = 0;
+  Control ctl;
+  Pools P{};
+  std::vector<void*> allocs;
+
+  // scratch (device, grown on demand)
+  float* scores = nullptr;
+  size_t scores_cap = 0;
+  float* part_acc = nullptr;   // [chunks][16][128] unnormalised attention partials
+  size_t part_acc_cap = 0;     // in chunks
+  float* part_ml = nullptr;    // [chunks][2][16] running max and sum
+  size_t part_ml_cap = 0;
+  float* seal_part = nullptr;  // kMaxReq * kSealSplit HCA partials
+  int32_t* tickets = nullptr;  // kMaxReq, zero between launches
+
+  // bulk-plan staging: pinned host -> device
+  void* plan_host = nullptr;
+  void* plan_dev = nullptr;
+  size_t plan_cap = 0;
+  hipEvent_t plan_ev = nullptr;
+  bool plan_busy = false;
+
+  // timing
+  uint32_t tmask = 0;
+  std::vector<hipEvent_t> ev_free;
+  struct Rec {
+    int kid;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+
+  int32_t attend_chunk = 32;
+
+  hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {}
+};
+
+namespace {
+
+int dev_alloc(hsa_ctx* c, void** p, size_t bytes) {
+  HIP_TRY(hipMalloc(p, bytes ? bytes : 16));
+  c->allocs.push_back(*p);
+  return kOk;
+}
+
+int grow(hsa_ctx* c, void** p, size_t* cap, size_t need, size_t elem) {
+  if (need <= *cap) return kOk;
+  size_t n = std::max(need, *cap + *cap / 2);
+  HIP_TRY(hipDeviceSynchronize());
+  if (*p) {
+    c->allocs.erase(std::remove(c->allocs.begin(), c->allocs.end(), *p), c->allocs.end());
+    HIP_TRY(hipFree(*p));
+    *p = nullptr;
+  }
+  int st = dev_alloc(c, p, n * elem);
+  if (st) return st;
+  *cap = n;
+  return kOk;
+}
+
+// Timing around one launch of kernel `kid`.
+struct Timed {
+  hsa_ctx* c;
+  int kid;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(hsa_ctx* c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
+    if (!(c->tmask & (1u << kid))) return;
+    for (hipEvent_t* e : {&a, &b}) {
+      if (!c->ev_free.empty()) {
+        *e = c->ev_free.back();
+        c->ev_free.pop_back();
+      } else if (hipEventCreate(e) != hipSuccess) {
+        *e = nullptr;
+      }
+    }
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~Timed() {
+    if (a && b) {
+      hipEventRecord(b, st);
+      c->recs.push_back({kid, a, b});
+    } else {
+      if (a) c->ev_free.push_back(a);
+      if (b) c->ev_free.push_back(b);
+    }
+  }
+};
+
+int set_device(hsa_ctx* c) {
+  HIP_TRY(hipSetDevice(c->device));
+  return kOk;
+}
+
+// Stage a bulk plan (seal and write descriptors) and copy it to the device.
+int upload_plan(hsa_ctx* c, const void* data, size_t bytes, hipStream_t st) {
+  if (c->plan_busy) {
+    HIP_TRY(hipEventSynchronize(c->plan_ev));
+    c->plan_busy = false;
+  }
+  if (bytes > c->plan_cap) {
+    size_t n = std::max(bytes, c->plan_cap * 2);
+    HIP_TRY(hipDeviceSynchronize());
+    if (c->plan_host) HIP_TRY(hipHostFree(c->plan_host));
+    if (c->plan_dev) {
+      c->allocs.erase(std::remove(c->allocs.begin(), c->allocs.end(), c->plan_dev), c->allocs.end());
+      HIP_TRY(hipFree(c->plan_dev));
+    }
+    c->plan_host = nullptr;
+    c->plan_dev = nullptr;
+    c->plan_cap = 0;
+    HIP_TRY(hipHostMalloc(&c->plan_host, n, hipHostMallocDefault));
+    int s = dev_alloc(c, &c->plan_dev, n);
+    if (s) return s;
+    c->plan_cap = n;
+  }
+  std::memcpy(c->plan_host, data, bytes);
+  HIP_TRY(hipMemcpyAsync(c->plan_dev, c->plan_host, bytes, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(c->plan_ev, st));
+  c->plan_busy = true;
+  return kOk;
+}
+
+// Enqueue the seals and ring/tail writes of a committed bulk plan.
+int run_bulk(hsa_ctx* c, const AppendPlan& plan, const void* k, const void* v, const float* ik,
+             hipStream_t st) {
+  std::vector<SealDesc> seals;
+  seals.reserve(plan.seals.size());
+  for (const SealItem& s : plan.seals)
+    seals.push_back(SealDesc{s.state, s.id, s.lblock * kBlk, s.len_old, s.row0});
+  std::vector<WriteDesc> writes;
+  int64_t total = 0;
+  for (const AppendReq& r : plan.reqs) {
+    if (r.len_new == r.len_old) continue;
+    const int64_t w0 = std::max(r.len_old, r.len_new - (int64_t)c->P.n_win);
+    writes.push_back(WriteDesc{r.state, (int32_t)r.nb_new, r.len_old, r.len_new, w0, r.row0, total});
+    total += r.len_new - w0;
+  }
+  if (seals.empty() && writes.empty()) return kOk;
+  const size_t sb = seals.size() * sizeof(SealDesc), wb = writes.size() * sizeof(WriteDesc);
+  std::vector<char> buf(sb + wb);
+  if (sb) std::memcpy(buf.data(), seals.data(), sb);
+  if (wb) std::memcpy(buf.data() + sb, writes.data(), wb);
+  int s = upload_plan(c, buf.data(), buf.size(), st);
+  if (s) return s;
+  const SealDesc* dseal = reinterpret_cast<const SealDesc*>(c->plan_dev);
+  const WriteDesc* dwrite = reinterpret_cast<const WriteDesc*>(static_cast<char*>(c->plan_dev) + sb);
+  {
+    Timed t(c, HSA_KERNEL_SEAL, st);
+    HIP_TRY(launch_bulk_seal(c->P, dseal, (int64_t)seals.size(), k, v, ik, st));
+  }
+  {
+    Timed t(c, HSA_KERNEL_WRITE, st);
+    HIP_TRY(launch_bulk_write(c->P, dwrite, (int32_t)writes.size(), total, k, v, ik, st));
+  }
+  return kOk;
+}
+
+// Enqueue a committed one-token-per-request append (decode), in batches of kMaxReq.
+int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const void* v,
+                      const float* ik, hipStream_t st) {
+  std::vector<int32_t> new_id(plan.reqs.size(), -1);
+  for (const SealItem& s : plan.seals) new_id[s.req] = s.id;
+  const size_t n = plan.reqs.size();
+  for (size_t b0 = 0; b0 < n; b0 += kMaxReq) {
+    ReqBatch B{};
+    B.n = (int32_t)std::min<size_t>(kMaxReq, n - b0);
+    for (int i = 0; i < B.n; ++i) {
+      const AppendReq& r = plan.reqs[b0 + i];
+      B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, new_id[b0 + i]};
+      if (new_id[b0 + i] >= 0) B.seal_req[B.n_seal++] = (int8_t)i;
+    }
+    Timed t(c, HSA_KERNEL_APPEND, st);
+    HIP_TRY(launch_decode_append(c->P, B, static_cast<const uint16_t*>(k) + b0 * kRow,
+                                 static_cast<const uint16_t*>(v) + b0 * kRow, ik + b0 * kIRow,
+                                 c->seal_part, c->tickets, st));
+  }
+  return kOk;
+}
+
+ReqBatch read_batch(hsa_ctx* c, const int32_t* states, int32_t b0, int32_t n) {
+  ReqBatch B{};
+  B.n = n;
+  for (int i = 0; i < n; ++i) {
+    const int32_t s = states[b0 + i];
+    B.r[i] = Req{s, (int32_t)c->ctl.len(s), (int32_t)c->ctl.n_blocks(s), 0};
+  }
+  return B;
+}
+
+int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx, int32_t k,
+             int32_t* idx_out, float* score_out, hipStream_t st) {
+  for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
+    const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
+    ReqBatch B = read_batch(c, states, b0, n);
+    int64_t total = 0, maxnb = 0;
+    for (int i = 0; i < n; ++i) {
+      total += B.r[i].nb;
+      maxnb = std::max<int64_t>(maxnb, B.r[i].nb);
+    }
+    const int64_t ld = std::max<int64_t>(kC4 * maxnb, 1);
+    int s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(ld * n), sizeof(float));
+    if (s) return s;
+    {
+      Timed t(c, HSA_KERNEL_SCORE, st);
+      HIP_TRY(launch_score(c->P, B, total, q_idx + (int64_t)b0 * kIRow, c->scores, ld, st));
+    }
+    {
+      Timed t(c, HSA_KERNEL_SELECT, st);
+      HIP_TRY(launch_select(B, k, c->scores, ld, idx_out + (int64_t)b0 * k,
+                            score_out ? score_out + (int64_t)b0 * k : nullptr, st));
+    }
+  }
+  return kOk;
+}
+
+int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
+               const int32_t* topk, int32_t k, float* out, hipStream_t st) {
+  const int32_t chunk = c->attend_chunk;
+  for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
+    const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
+    ReqBatch B = read_batch(c, states, b0, n);
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) {
+      const int64_t swa = std::min<int64_t>(B.r[i].len, c->P.n_win);
+      const int64_t nk = swa + B.r[i].nb + std::min<int64_t>(k, (int64_t)kC4 * B.r[i].nb);
+      total += (nk + chunk - 1) / chunk;
+    }
+    int s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)total,
+                 kRow * sizeof(float));
+    if (s) return s;
+    s = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, (size_t)total,
+             2 * kH * sizeof(float));
+    if (s) return s;
+    const void* qb = static_cast<const uint16_t*>(q) + (int64_t)b0 * kRow;
+    const int32_t* tk = topk ? topk + (int64_t)b0 * k : nullptr;
+    {
+      Timed t(c, HSA_KERNEL_ATTEND, st);
+      HIP_TRY(launch_attend(c->P, B, total, chunk, qb, tk, k, c->part_acc, c->part_ml, st));
+    }
+    {
+      Timed t(c, HSA_KERNEL_COMBINE, st);
+      HIP_TRY(launch_combine(c->P, B, chunk, k, c->part_acc, c->part_ml, out + (int64_t)b0 * kRow, st));
+    }
+  }
+  return kOk;
+}
+
+int check_config(const hsa_config* cfg) {
+  if (!cfg) return fail(kInvalid, "config is NULL");
+  if (cfg->n_heads != kH || cfg->head_dim != kD)
+    return fail(kInvalid, "only 16 heads x 128 dims are supported");
+  if (cfg->m_csa != 4 || cfg->m_hca != kBlk) return fail(kInvalid, "m_csa must be 4 and m_hca 128");
+  if (cfg->idx_heads != kHi || cfg->idx_dim != kDi)
+    return fail(kInvalid, "indexer must be 4 heads x 64 dims");
+  if (cfg->n_win < kBlk || cfg->n_win % kBlk) return fail(kInvalid, "n_win must be a positive multiple of 128");
+  if (cfg->max_states < 1 || cfg->max_blocks < 1) return fail(kInvalid, "pool sizes must be positive");
+  if (cfg->max_blocks > INT32_MAX) return fail(kInvalid, "max_blocks must fit int32 ids");
+  const int64_t bps = cfg->max_blocks_per_state ? cfg->max_blocks_per_state : cfg->max_blocks;
+  if (bps < 1 || bps > (int64_t(1) << 24)) return fail(kInvalid, "max_blocks_per_state out of range");
+  if (!cfg->gate_csa || !cfg->gate_hca) return fail(kInvalid, "gate weights are NULL");
+  return kOk;
+}
+
+}  // namespace
+
+extern "C" {
+
+hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
+  if (!out) return fail(kInvalid, "out is NULL");
+  *out = nullptr;
+  int st = check_config(cfg);
+  if (st) return st;
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return fail(kInvalid, "no such device");
+  HIP_TRY(hipSetDevice(device));
+  const int64_t bps = cfg->max_blocks_per_state ? cfg->max_blocks_per_state : cfg->max_blocks;
+  hsa_ctx* c = new hsa_ctx(cfg->n_win, cfg->max_states, cfg->max_blocks, bps);
+  c->device = device;
+  const size_t S = (size_t)cfg->max_states, NB = (size_t)cfg->max_blocks, W = (size_t)cfg->n_win;
+  void* p[12] = {};
+  const size_t bytes[12] = {
+      S * W * kRow * 2, S * W * kRow * 2, S * kBlk * kIRow * 4,            // swa_k, swa_v, idx_tail
+      NB * kC4 * kRow * 2, NB * kC4 * kRow * 2, NB * kRow * 2, NB * kRow * 2,  // csa, hca
+      NB * kBlk * kIRow * 4,                                              // idx_k
+      S * (size_t)bps * 4,                                                // table
+      2 * kRow * 4,                                                       // gates
+      (size_t)kMaxReq * kSealSplit * kPartFloats * 4,                     // seal partials
+      (size_t)kMaxReq * 4};                                               // tickets
+  for (int i = 0; i < 12; ++i) {
+    st = dev_alloc(c, &p[i], bytes[i]);
+    if (st) {
+      hsa_destroy(c);
+      return st;
+    }
+  }
+  c->P.swa_k = static_cast<uint16_t*>(p[0]);
+  c->P.swa_v = static_cast<uint16_t*>(p[1]);
+  c->P.idx_tail = static_cast<float*>(p[2]);
+  c->P.csa_k = static_cast<uint16_t*>(p[3]);
+  c->P.csa_v = static_cast<uint16_t*>(p[4]);
+  c->P.hca_k = static_cast<uint16_t*>(p[5]);
+  c->P.hca_v = static_cast<uint16_t*>(p[6]);
+  c->P.idx_k = static_cast<float*>(p[7]);
+  c->P.table = static_cast<int32_t*>(p[8]);
+  c->P.table_stride = bps;
+  float* gates = static_cast<float*>(p[9]);
+  c->P.gate_csa = gates;
+  c->P.gate_hca = gates + kRow;
+  c->P.n_win = cfg->n_win;
+  c->P.max_blocks = (int32_t)cfg->max_blocks;
+  c->seal_part = static_cast<float*>(p[10]);
+  c->tickets = static_cast<int32_t*>(p[11]);
+  hipError_t e = hipMemcpy(gates, cfg->gate_csa, kRow * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(gates + kRow, cfg->gate_hca, kRow * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(c->tickets, 0, kMaxReq * 4);
+  if (e == hipSuccess) e = hipMemset(c->P.table, 0xff, bytes[8]);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    hsa_destroy(c);
+    return fail(kDevice, std::string("hsa_create: ") + hipGetErrorString(e));
+  }
+  *out = c;
+  return kOk;
+}
+
+hsa_status hsa_destroy(hsa_ctx* c) {
+  if (!c) return kOk;
+  hipSetDevice(c->device);
+  hipDeviceSynchronize();
+  for (void* p : c->allocs) hipFree(p);
+  if (c->plan_host) hipHostFree(c->plan_host);
+  if (c->plan_ev) hipEventDestroy(c->plan_ev);
+  for (auto& r : c->recs) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : c->ev_free) hipEventDestroy(e);
+  delete c;
+  return kOk;
+}
+
+hsa_status hsa_state_alloc(hsa_ctx* c, int32_t* out) {
+  if (!c || !out) return fail(kInvalid, "NULL argument");
+  int st = c->ctl.state_alloc(out);
+  return st ? fail(st, "no free State slot") : kOk;
+}
+
+hsa_status hsa_state_free(hsa_ctx* c, int32_t s) {
+  if (!c) return fail(kInvalid, "NULL context");
+  int st = c->ctl.state_free(s);
+  return st ? fail(st, "state " + std::to_string(s) + " is not allocated") : kOk;
+}
+
+hsa_status hsa_append_kv(hsa_ctx* c, int32_t n_req, const int32_t* states, const int64_t* cu,
+                         const void* k, const void* v, const float* idx_k, uint32_t flags,
+                         void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (flags & ~HSA_APPEND_DEFER_SEAL) return fail(kInvalid, "unknown flags");
+  std::string why;
+  AppendPlan plan;
+  int st = c->ctl.plan_append(n_req, states, cu, (flags & HSA_APPEND_DEFER_SEAL) != 0, &plan, &why);
+  if (st) return fail(st, why);
+  const int64_t T = n_req > 0 ? cu[n_req] : 0;
+  if (T > 0 && (!k || !v || !idx_k)) return fail(kInvalid, "input pointer is NULL");
+  if ((st = set_device(c))) return st;
+  bool one_each = n_req > 0;
+  for (const AppendReq& r : plan.reqs) one_each = one_each && (r.len_new - r.len_old == 1);
+  c->ctl.commit(&plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return one_each ? run_decode_append(c, plan, k, v, idx_k, s) : run_bulk(c, plan, k, v, idx_k, s);
+}
+
+hsa_status hsa_compress_flush(hsa_ctx* c, int32_t n_req, const int32_t* states, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  AppendPlan plan;
+  int st = c->ctl.plan_flush(n_req, states, &plan, &why);
+  if (st) return fail(st, why);
+  if (plan.new_blocks == 0) return kOk;
+  if ((st = set_device(c))) return st;
+  c->ctl.commit(&plan);
+  return run_bulk(c, plan, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  int st = c->ctl.check_share(src, dst, &why);
+  if (st) return fail(st, why);
+  if ((st = set_device(c))) return st;
+  c->ctl.commit_share(src, dst);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t L = c->ctl.len(dst), nb = c->ctl.n_blocks(dst), W = c->P.n_win;
+  const size_t stride = (size_t)c->P.table_stride;
+  if (nb > 0)
+    HIP_TRY(hipMemcpyAsync(c->P.table + dst * stride, c->P.table + src * stride, nb * 4,
+                           hipMemcpyDeviceToDevice, s));
+  const int64_t slots = std::min(L, W);
+  if (slots > 0) {
+    const size_t bytes = (size_t)slots * kRow * 2;
+    HIP_TRY(hipMemcpyAsync(c->P.swa_k + (size_t)dst * W * kRow, c->P.swa_k + (size_t)src * W * kRow,
+                           bytes, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(hipMemcpyAsync(c->P.swa_v + (size_t)dst * W * kRow, c->P.swa_v + (size_t)src * W * kRow,
+                           bytes, hipMemcpyDeviceToDevice, s));
+  }
+  const int64_t tail = L - kBlk * nb;
+  if (tail > 0)
+    HIP_TRY(hipMemcpyAsync(c->P.idx_tail + (size_t)dst * kBlk * kIRow,
+                           c->P.idx_tail + (size_t)src * kBlk * kIRow, (size_t)tail * kIRow * 4,
+                           hipMemcpyDeviceToDevice, s));
+  return kOk;
+}
+
+hsa_status hsa_indexer_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx,
+                            int32_t k, int32_t* idx_out, float* score_out, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  int st = c->ctl.check_states(n_req, states, false, false, &why);
+  if (st) return fail(st, why);
+  if (k < 1 || k > HSA_MAX_TOPK) return fail(kInvalid, "k must be in [1, 4096]");
+  if (n_req > 0 && (!q_idx || !idx_out)) return fail(kInvalid, "NULL device pointer");
+  if (n_req == 0) return kOk;
+  if ((st = set_device(c))) return st;
+  return run_topk(c, n_req, states, q_idx, k, idx_out, score_out, static_cast<hipStream_t>(stream));
+}
+
+hsa_status hsa_decode_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
+                             const int32_t* topk, int32_t k, float* out, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  int st = c->ctl.check_states(n_req, states, false, true, &why);
+  if (st) return fail(st, why);
+  if (k < 0 || k > HSA_MAX_TOPK) return fail(kInvalid, "k must be in [0, 4096]");
+  if (k > 0 && !topk) return fail(kInvalid, "topk is NULL with k > 0");
+  if (n_req > 0 && (!q || !out)) return fail(kInvalid, "NULL device pointer");
+  if (n_req == 0) return kOk;
+  if ((st = set_device(c))) return st;
+  return run_attend(c, n_req, states, q, k > 0 ? topk : nullptr, k, out,
+                    static_cast<hipStream_t>(stream));
+}
+
+hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* k_new,
+                           const void* v_new, const float* idx_new, const void* q,
+                           const float* q_idx, int32_t k, int32_t* topk_out, float* score_out,
+                           float* out, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (n_req < 0) return fail(kInvalid, "n_req < 0");
+  if (n_req == 0) return kOk;
+  if (k < 1 || k > HSA_MAX_TOPK) return fail(kInvalid, "k must be in [1, 4096]");
+  if (!k_new || !v_new || !idx_new || !q || !q_idx || !topk_out || !out)
+    return fail(kInvalid, "NULL device pointer");
+  std::vector<int64_t> cu(n_req + 1);
+  for (int32_t i = 0; i <= n_req; ++i) cu[i] = i;
+  std::string why;
+  AppendPlan plan;
+  int st = c->ctl.plan_append(n_req, states, cu.data(), false, &plan, &why);
+  if (st) return fail(st, why);
+  if ((st = set_device(c))) return st;
+  c->ctl.commit(&plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = run_decode_append(c, plan, k_new, v_new, idx_new, s))) return st;
+  if ((st = run_topk(c, n_req, states, q_idx, k, topk_out, score_out, s))) return st;
+  return run_attend(c, n_req, states, q, topk_out, k, out, s);
+}
+
+hsa_status hsa_state_query(hsa_ctx* c, int32_t s, hsa_state_info* out) {
+  if (!c || !out) return fail(kInvalid, "NULL argument");
+  if (!c->ctl.valid_state(s)) return fail(kInvalid, "state not allocated");
+  const int64_t L = c->ctl.len(s), nb = c->ctl.n_blocks(s);
+  out->len = L;
+  out->n_blocks = nb;
+  out->csa_tail = (int32_t)(L % 4);
+  out->hca_tail = (int32_t)(L - kBlk * nb);
+  out->swa_len = (int32_t)std::min<int64_t>(L, c->P.n_win);
+  out->pending_seal = c->ctl.pending(s) ? 1 : 0;
+  return kOk;
+}
+
+hsa_status hsa_block_table_get(hsa_ctx* c, int32_t s, int32_t* ids, int64_t cap, int64_t* n) {
+  if (!c || !n) return fail(kInvalid, "NULL argument");
+  if (!c->ctl.valid_state(s)) return fail(kInvalid, "state not allocated");
+  const auto& t = c->ctl.table(s);
+  *n = (int64_t)t.size();
+  if (ids) std::copy(t.begin(), t.begin() + std::min<int64_t>(cap, *n), ids);
+  return kOk;
+}
+
+hsa_status hsa_block_refcount(hsa_ctx* c, int32_t b, int32_t* rc) {
+  if (!c || !rc) return fail(kInvalid, "NULL argument");
+  if (!c->ctl.valid_block(b)) return fail(kInvalid, "no such block");
+  *rc = c->ctl.refcount(b);
+  return kOk;
+}
+
+hsa_status hsa_export_block(hsa_ctx* c, int32_t b, void* csa_k, void* csa_v, void* hca_k,
+                            void* hca_v, float* idx_k, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t B = (size_t)b;
+  if (csa_k) HIP_TRY(hipMemcpyAsync(csa_k, c->P.csa_k + B * kC4 * kRow, kC4 * kRow * 2, hipMemcpyDeviceToHost, s));
+  if (csa_v) HIP_TRY(hipMemcpyAsync(csa_v, c->P.csa_v + B * kC4 * kRow, kC4 * kRow * 2, hipMemcpyDeviceToHost, s));
+  if (hca_k) HIP_TRY(hipMemcpyAsync(hca_k, c->P.hca_k + B * kRow, kRow * 2, hipMemcpyDeviceToHost, s));
+  if (hca_v) HIP_TRY(hipMemcpyAsync(hca_v, c->P.hca_v + B * kRow, kRow * 2, hipMemcpyDeviceToHost, s));
+  if (idx_k) HIP_TRY(hipMemcpyAsync(idx_k, c->P.idx_k + B * kBlk * kIRow, kBlk * kIRow * 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return kOk;
+}
+
+hsa_status hsa_export_state(hsa_ctx* c, int32_t s_, void* swa_k, void* swa_v, float* idx_tail,
+                            void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->ctl.valid_state(s_)) return fail(kInvalid, "state not allocated");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t W = (size_t)c->P.n_win, S = (size_t)s_;
+  if (swa_k) HIP_TRY(hipMemcpyAsync(swa_k, c->P.swa_k + S * W * kRow, W * kRow * 2, hipMemcpyDeviceToHost, s));
+  if (swa_v) HIP_TRY(hipMemcpyAsync(swa_v, c->P.swa_v + S * W * kRow, W * kRow * 2, hipMemcpyDeviceToHost, s));
+  if (idx_tail)
+    HIP_TRY(hipMemcpyAsync(idx_tail, c->P.idx_tail + S * kBlk * kIRow, kBlk * kIRow * 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return kOk;
+}
+
+hsa_status hsa_timing_enable(hsa_ctx* c, uint32_t mask) {
+  if (!c) return fail(kInvalid, "NULL context");
+  c->tmask = mask;
+  return kOk;
+}
+
+hsa_status hsa_timing_read(hsa_ctx* c, double* ms, int64_t* launches) {
+  if (!c) return fail(kInvalid, "NULL context");
+  for (int i = 0; i < HSA_KERNEL_COUNT; ++i) {
+    if (ms) ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (auto& r : c->recs) {
+    HIP_TRY(hipEventSynchronize(r.b));
+    float t = 0.f;
+    HIP_TRY(hipEventElapsedTime(&t, r.a, r.b));
+    if (ms) ms[r.kid] += t;
+    if (launches) launches[r.kid] += 1;
+    c->ev_free.push_back(r.a);
+    c->ev_free.push_back(r.b);
+  }
+  c->recs.clear();
+  return kOk;
+}
+
+const char* hsa_status_str(hsa_status s) {
+  switch (s) {
+    case HSA_OK: return "ok";
+    case HSA_ERR_INVALID: return "invalid argument";
+    case HSA_ERR_OOM_BLOCKS: return "Block Cache full";
+    case HSA_ERR_OOM_STATES: return "no free State slot";
+    case HSA_ERR_STATE: return "lifecycle error";
+    case HSA_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* hsa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

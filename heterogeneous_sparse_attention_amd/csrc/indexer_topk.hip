@@ -1,0 +1,229 @@
+// indexer_topk.hip - indexer scores over sealed blocks and top-k selection.
+//
+// Pages: [Ch12] "Ch 12 · 推理框架 — KV 的异构调度" 名词速通 (the indexer holds tiny
+// K-only keys used for top-k selection) and §2.2 (each block keeps its 128
+// tokens' indexer keys); [Layout] "V4 KV Layout：Classical + State 双池", Classical KV
+// cache (CSA entries are read sparsely through top-k).
+//
+// The score is not defined on the pages. Reading used: score of token t = sum over
+// 4 heads x 64 dims of q_idx * k_idx_t; score of C4 entry j = mean of the scores
+// of its tokens 4j..4j+3. Top-k keeps kk = min(k, N_c) entries ordered by score
+// descending, ties to the lowest C4 ordinal.
+#include "device.h"
+#include "kernels.h"
+
+namespace hsa {
+
+namespace {
+
+// One workgroup per sealed block (128 KiB of indexer keys): wave w scores C4
+// entries 8w .. 8w+7. Lane l owns dims 4l..4l+3 of every token row, so each
+// token row is one coalesced 1 KiB read per wave; the 4 tokens of an entry are
+// summed per lane before one wave reduction.
+__global__ __launch_bounds__(256) void k_score(Pools P, ReqBatch B, const float* q_idx,
+                                               float* scores, int64_t ld) {
+  int w = blockIdx.x, r = 0;
+  for (; r < B.n - 1; ++r) {
+    if (w < B.r[r].nb) break;
+    w -= B.r[r].nb;
+  }
+  const Req R = B.r[r];
+  const int32_t id = P.table[(int64_t)R.state * P.table_stride + w];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  float* out = scores + (int64_t)r * ld + (int64_t)kC4 * w + 8 * wave;
+  if (id < 0 || id >= P.max_blocks) {          // never taken: tables are written before use
+    if (lane < 8) out[lane] = -INFINITY;
+    return;
+  }
+  const float* blk = P.idx_k + (int64_t)id * kBlk * kIRow;
+  const float4 q = reinterpret_cast<const float4*>(q_idx + (int64_t)r * kIRow)[lane];
+  float4 kv[8][4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      kv[e][u] = reinterpret_cast<const float4*>(blk + ((8 * wave + e) * 4 + u) * kIRow)[lane];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a = fmaf(q.x, kv[e][u].x, a);
+      a = fmaf(q.y, kv[e][u].y, a);
+      a = fmaf(q.z, kv[e][u].z, a);
+      a = fmaf(q.w, kv[e][u].w, a);
+    }
+    a = wave_sum(a);
+    if (lane == e) out[e] = a * 0.25f;
+  }
+}
+
+// Order-preserving map of a float score to uint32 (larger score -> larger key);
+// -0 is folded onto +0 so equal scores compare equal.
+__device__ __forceinline__ uint32_t okey(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float okey_inv(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+constexpr int kSelThreads = 1024;
+constexpr int kCacheN = 4096;
+
+// One workgroup per request. Radix select (4 passes of 8 bits, most significant
+// first) finds tau, the key of the kk-th best score, and how many entries equal
+// to tau make the cut; entries above tau and the first such entries equal to tau
+// (in ordinal order, ballot + prefix count) are gathered and sorted by (key desc,
+// ordinal asc) with a bitonic sort in LDS.
+__global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, const float* scores,
+                                                        int64_t ld, int32_t* idx_out,
+                                                        float* score_out) {
+  __shared__ uint32_t cache[kCacheN];
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long cand[kMaxTopk];
+  __shared__ int sh[4];
+  __shared__ int wave_cnt[kSelThreads / 64];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = kC4 * B.r[r].nb;
+  const int kk = min(k, N);
+  const float* S = scores + (int64_t)r * ld;
+  int32_t* io = idx_out + (int64_t)r * k;
+  float* so = score_out ? score_out + (int64_t)r * k : nullptr;
+  const bool cached = N <= kCacheN;
+
+  if (kk > 0) {
+    if (cached)
+      for (int i = tid; i < N; i += kSelThreads) cache[i] = okey(S[i]);
+    auto key = [&](int i) -> uint32_t { return cached ? cache[i] : okey(S[i]); };
+
+    uint32_t prefix = 0u, mask = 0u;
+    int rem = kk;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < N; i += kSelThreads) {
+        const uint32_t u = key(i);
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds digits 255-4l .. 252-4l (descending)
+        uint32_t c[4], tot = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * tid - q];
+          tot += c[q];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(incl, o);
+          if (tid >= o) incl += y;
+        }
+        const unsigned long long bal = __ballot(incl >= (uint32_t)rem);
+        const int first = __ffsll(bal) - 1;
+        if (tid == first) {
+          uint32_t cum = incl - tot;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (cum + c[q] >= (uint32_t)rem) {
+              sh[0] = 255 - 4 * tid - q;
+              sh[1] = (int)cum;
+              break;
+            }
+            cum += c[q];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sh[0] << shift;
+      mask |= 255u << shift;
+      rem -= sh[1];
+      __syncthreads();
+    }
+    const uint32_t tau = prefix;
+    const int n_gt = kk - rem;
+    if (tid == 0) sh[2] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += kSelThreads) {
+      const uint32_t u = key(i);
+      if (u > tau) {
+        const int pos = atomicAdd(&sh[2], 1);
+        if (pos < n_gt) cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
+      }
+    }
+    // entries equal to tau, lowest ordinals first
+    const int lane = tid & 63, wv = tid >> 6;
+    int base = 0;
+    for (int c0 = 0; c0 < N && base < rem; c0 += kSelThreads) {
+      const int i = c0 + tid;
+      const bool eq = i < N && key(i) == tau;
+      const unsigned long long bal = __ballot(eq);
+      if (lane == 0) wave_cnt[wv] = __popcll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+      for (int w = 0; w < kSelThreads / 64; ++w) {
+        before += (w < wv) ? wave_cnt[w] : 0;
+        total += wave_cnt[w];
+      }
+      const int rank = base + before + __popcll(bal & ((1ull << lane) - 1ull));
+      if (eq && rank < rem) cand[n_gt + rank] = ((unsigned long long)(~tau) << 32) | (uint32_t)i;
+      base += total;
+      __syncthreads();
+    }
+    // bitonic sort of cand[0 .. n2) ascending; padding sorts last
+    int n2 = 1;
+    while (n2 < kk) n2 <<= 1;
+    for (int i = kk + tid; i < n2; i += kSelThreads) cand[i] = ~0ull;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int t = tid; t < n2 / 2; t += kSelThreads) {
+          const int i = 2 * t - (t & (stride - 1));
+          const int j = i + stride;
+          const bool asc = (i & size) == 0;
+          const unsigned long long a = cand[i], b = cand[j];
+          if ((a > b) == asc) {
+            cand[i] = b;
+            cand[j] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  for (int i = tid; i < k; i += kSelThreads) {
+    if (i < kk) {
+      const unsigned long long c = cand[i];
+      io[i] = (int32_t)(c & 0xffffffffull);
+      if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
+    } else {
+      io[i] = -1;
+      if (so) so[i] = -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks, const float* q_idx,
+                        float* scores, int64_t ld, hipStream_t st) {
+  if (total_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_score, dim3((unsigned)total_blocks), dim3(256), 0, st, P, B, q_idx, scores, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const ReqBatch& B, int32_t k, const float* scores, int64_t ld,
+                         int32_t* idx_out, float* score_out, hipStream_t st) {
+  if (B.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_select, dim3(B.n), dim3(kSelThreads), 0, st, B, k, scores, ld, idx_out,
+                     score_out);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

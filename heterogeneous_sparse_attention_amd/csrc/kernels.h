@@ -1,0 +1,35 @@
+// kernels.h - host-side launchers of the gfx950 kernels (one per .hip file group).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device.h"
+
+namespace hsa {
+
+// append_seal.hip
+hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* kin, const void* vin,
+                                const float* iin, float* part, int32_t* tickets, hipStream_t st);
+hipError_t launch_bulk_seal(const Pools& P, const SealDesc* seals, int64_t n_seals, const void* kin,
+                            const void* vin, const float* iin, hipStream_t st);
+hipError_t launch_bulk_write(const Pools& P, const WriteDesc* w, int32_t n_req, int64_t total,
+                             const void* kin, const void* vin, const float* iin, hipStream_t st);
+
+// indexer_topk.hip
+// Scores of every sealed C4 entry of the batch's requests: scores[i * ld + j].
+hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks, const float* q_idx,
+                        float* scores, int64_t ld, hipStream_t st);
+// Top-k of each request's scores (one workgroup per request).
+hipError_t launch_select(const ReqBatch& B, int32_t k, const float* scores, int64_t ld,
+                         int32_t* idx_out, float* score_out, hipStream_t st);
+
+// attend.hip
+// Keys of request i: min(len, n_win) SWA + nb HCA + min(k, 32 nb) C4 slots, cut in
+// chunks of `chunk` keys; one workgroup per chunk writes an unnormalised partial.
+hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks, int32_t chunk,
+                         const void* q, const int32_t* topk, int32_t k, float* part_acc,
+                         float* part_ml, hipStream_t st);
+hipError_t launch_combine(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,
+                          const float* part_acc, const float* part_ml, float* out, hipStream_t st);
+
+}  // namespace hsa

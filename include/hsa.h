@@ -1,0 +1,214 @@
+/*
+ * hsa.h - C ABI of the heterogeneous sparse-attention KV cache (MI355X, gfx950).
+ *
+ * The library keeps the two pools of the DeepSeek-V4 heterogeneous KV layout on
+ * one GPU and runs the decode step over them:
+ *
+ *   State Cache  one fixed-size block per request: the SWA ring of the last
+ *                n_win tokens' exact K/V and the in-flight tail of the open
+ *                128-token block (its indexer keys; its K/V are the newest
+ *                ring slots).
+ *   Block Cache  sealed, immutable, refcounted blocks of lcm(4, 128) = 128
+ *                tokens, each holding 32 CSA (C4) entries, 1 HCA entry and the
+ *                128 tokens' indexer keys.
+ *
+ * Pages cited (by title and section):
+ *   [Q&A]    "V4 为何要分池？块对齐与尾缓冲怎么配合？" (deepseek-tech-notes)
+ *   [Layout] "V4 KV Layout：Classical + State 双池" (deepseek-tech-notes)
+ *   [Ch12]   "Ch 12 · 推理框架 — KV 的异构调度" (DeepSeek-V4-book)
+ *
+ * Conventions for every call:
+ *   - Shapes are fixed: 16 heads x 128 bf16 for K/V/Q, 4 heads x 64 fp32 for
+ *     indexer keys/queries, m = 4, m' = 128 (other values: HSA_ERR_INVALID).
+ *   - "dev" pointers are device memory owned by the caller, alive until the
+ *     work enqueued on `stream` has run; "host" arrays are read during the
+ *     call only. `stream` is a hipStream_t passed as void* (NULL = default).
+ *   - Host metadata (lengths, block tables, refcounts) changes at call time;
+ *     device work is enqueued on `stream` and never waited for, except by the
+ *     introspection calls, which synchronise `stream`.
+ *   - Every argument and capacity check runs before any metadata changes or
+ *     any work is enqueued: a call that returns an error changed nothing.
+ *     HSA_ERR_DEVICE (a HIP runtime failure) leaves the context unusable
+ *     except for hsa_destroy.
+ *   - A context is not thread safe, and its calls must be issued on one stream
+ *     at a time (calls share scratch memory).
+ */
+#ifndef HSA_H
+#define HSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hsa_status;
+#define HSA_OK 0
+#define HSA_ERR_INVALID (-1)     /* bad argument, shape, id or unallocated state   */
+#define HSA_ERR_OOM_BLOCKS (-2)  /* Block Cache or a state's block table is full   */
+#define HSA_ERR_OOM_STATES (-3)  /* no free State slot                             */
+#define HSA_ERR_STATE (-4)       /* lifecycle: share into a non-empty state, append
+                                    to a full deferred tail, deferred append past
+                                    one block                                      */
+#define HSA_ERR_DEVICE (-5)      /* HIP runtime error                              */
+
+#define HSA_APPEND_DEFER_SEAL 1u
+
+#define HSA_MAX_TOPK 4096        /* largest k accepted by indexer_topk / attend     */
+
+typedef struct hsa_ctx hsa_ctx;
+
+typedef struct hsa_config {
+  int32_t n_heads;              /* 16                                               */
+  int32_t head_dim;             /* 128                                              */
+  int32_t m_csa;                /* 4   ([Q&A] §1.2: CSA compresses 4 tokens)        */
+  int32_t m_hca;                /* 128 ([Q&A] §1.2: HCA compresses 128 tokens)      */
+  int32_t n_win;                /* SWA tokens; multiple of 128 ([Ch12] 公式白话翻译:
+                                   the window is an integer number of blocks)       */
+  int32_t idx_heads;            /* 4                                                */
+  int32_t idx_dim;              /* 64                                               */
+  int32_t max_states;           /* State slots                                      */
+  int64_t max_blocks;           /* physical blocks in the Block Cache               */
+  int64_t max_blocks_per_state; /* block-table row length; 0 = max_blocks           */
+  const float* gate_csa;        /* host [n_heads][head_dim] compressor gate, copied */
+  const float* gate_hca;        /* host [n_heads][head_dim] compressor gate, copied */
+} hsa_config;
+
+typedef struct hsa_state_info {
+  int64_t len;          /* L, tokens appended so far                                 */
+  int64_t n_blocks;     /* sealed blocks in the state's block table                  */
+  int32_t csa_tail;     /* L mod 4                                                   */
+  int32_t hca_tail;     /* tokens in the open block: L - 128 * n_blocks (<= 128)     */
+  int32_t swa_len;      /* min(L, n_win)                                             */
+  int32_t pending_seal; /* 1 if a deferred full tail awaits hsa_compress_flush       */
+} hsa_state_info;
+
+/* Create a context on `device`: validates `cfg`, allocates every pool in device
+ * memory (owned by the context until hsa_destroy) and copies the gates.
+ * Pools: SWA ring K and V [max_states][n_win][16][128] bf16, indexer tail
+ * [max_states][128][4][64] fp32, C4 K and V [max_blocks][32][16][128] bf16,
+ * HCA K and V [max_blocks][16][128] bf16, indexer keys [max_blocks][128][4][64]
+ * fp32, block table [max_states][max_blocks_per_state] int32.
+ * ([Q&A] §1.1: two pools with different lifetimes; [Ch12] §2.1, §2.2.) */
+hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out);
+hsa_status hsa_destroy(hsa_ctx* ctx);
+
+/* Take the lowest free State slot; its length is 0 and its table empty.
+ * ([Ch12] §2.1: one State block per request for its whole life.) */
+hsa_status hsa_state_alloc(hsa_ctx* ctx, int32_t* state_out);
+
+/* Release a State slot: drop one reference from each of its blocks; a block
+ * whose count reaches 0 returns to the free list. No device work.
+ * ([Ch12] §2.1: the block is freed whole at request end; §2.2: refcounts.) */
+hsa_status hsa_state_free(hsa_ctx* ctx, int32_t state);
+
+/* Append tokens to n_req distinct states ([Q&A] §4 steps 1-3; §3.1).
+ *   states    host [n_req]
+ *   cu_tokens host [n_req+1], cu_tokens[0] = 0, nondecreasing: request i owns
+ *             rows cu_tokens[i] .. cu_tokens[i+1]-1 of the packed inputs
+ *   k, v      dev bf16 [T][16][128], T = cu_tokens[n_req]
+ *   idx_k     dev fp32 [T][4][64] (indexer keys)
+ * Token at position p goes to SWA ring slot p mod n_win and indexer-tail slot
+ * p mod 128. Without flags, each time a state's open block reaches 128 tokens
+ * it is sealed: a block id is taken (lowest free id; requests in call order,
+ * blocks in token order), its 32 C4 entries (tokens 4j..4j+3) and its HCA
+ * entry (all 128 tokens) are computed by gated pooling and stored as bf16,
+ * and the 128 indexer keys are copied in. With HSA_APPEND_DEFER_SEAL the open
+ * block may fill to exactly 128 tokens and waits for hsa_compress_flush;
+ * going past 128 is HSA_ERR_STATE, as is any append to a state whose full
+ * tail awaits a flush. Errors: INVALID, OOM_BLOCKS, STATE. */
+hsa_status hsa_append_kv(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                         const int64_t* cu_tokens, const void* k, const void* v,
+                         const float* idx_k, uint32_t flags, void* stream);
+
+/* Seal every listed state whose open block holds 128 tokens (deferred seals);
+ * others are left as they are. ([Q&A] §3.1: full block -> compress -> append
+ * to the Classical pool.) Errors: INVALID, OOM_BLOCKS. */
+hsa_status hsa_compress_flush(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                              void* stream);
+
+/* Make `dst` (allocated, L = 0) a fork of `src`: dst's table references every
+ * sealed block of src (refcount + 1 each) and src's State (SWA ring, indexer
+ * tail, L) is copied into dst's slot on `stream`. ([Ch12] §2.2: requests with
+ * the same prefix reference the same block, refcounted.) Errors: INVALID
+ * (bad ids, src == dst), STATE (dst not empty, src has a pending seal). */
+hsa_status hsa_block_table_share(hsa_ctx* ctx, int32_t src, int32_t dst, void* stream);
+
+/* Indexer top-k over each state's sealed C4 entries ([Ch12] 名词速通: the
+ * indexer's K-only keys serve top-k selection; [Layout] Classical KV cache:
+ * CSA entries are read sparsely through top-k).
+ *   q_idx     dev fp32 [n_req][4][64]
+ *   idx_out   dev int32 [n_req][k]: C4 ordinals j (block j/32, slot j%32 of
+ *             the state's table), the kk = min(k, 32 * n_blocks) best scores,
+ *             ordered by score descending then ordinal ascending, then -1
+ *   score_out dev fp32 [n_req][k] or NULL: the scores, -inf after kk
+ * Score of token t: sum over 4 heads x 64 dims of q_idx * idx_key_t; score of
+ * C4 entry j = mean of its 4 tokens' scores. 1 <= k <= HSA_MAX_TOPK. */
+hsa_status hsa_indexer_topk(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                            const float* q_idx, int32_t k, int32_t* idx_out,
+                            float* score_out, void* stream);
+
+/* Heterogeneous decode attention ([Q&A] §4 step 4: sparse/dense reads of the
+ * compressed entries plus exact reads of the State): per request and head, one
+ * softmax over the SWA tokens (min(L, n_win), the open tail included), the HCA
+ * entries of every sealed block and the C4 entries named in the first
+ * min(k, 32 * n_blocks) slots of its topk row (-1 and ordinals outside
+ * [0, 32 * n_blocks) are skipped); scores are q.k / sqrt(128).
+ *   q    dev bf16 [n_req][16][128]
+ *   topk dev int32 [n_req][k] (NULL when k == 0)
+ *   out  dev fp32 [n_req][16][128]
+ * Every state must hold at least one token. 0 <= k <= HSA_MAX_TOPK. */
+hsa_status hsa_decode_attend(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                             const void* q, const int32_t* topk, int32_t k,
+                             float* out, void* stream);
+
+/* One decode step ([Q&A] §4): append one token per request (k_new, v_new dev
+ * bf16 [n_req][16][128], idx_new dev fp32 [n_req][4][64]) sealing full blocks,
+ * then hsa_indexer_topk(q_idx, k, topk_out, score_out), then
+ * hsa_decode_attend(q, topk_out, k, out). Same argument rules as those calls;
+ * k >= 1. */
+hsa_status hsa_decode_step(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                           const void* k_new, const void* v_new, const float* idx_new,
+                           const void* q, const float* q_idx, int32_t k,
+                           int32_t* topk_out, float* score_out, float* out, void* stream);
+
+/* ---- introspection (host side; the export calls synchronise `stream`) ---- */
+hsa_status hsa_state_query(hsa_ctx* ctx, int32_t state, hsa_state_info* out);
+/* Copy up to `cap` ids of the state's block table to host `ids`; *n = count. */
+hsa_status hsa_block_table_get(hsa_ctx* ctx, int32_t state, int32_t* ids, int64_t cap,
+                               int64_t* n);
+hsa_status hsa_block_refcount(hsa_ctx* ctx, int32_t block, int32_t* rc);
+/* Copy one block to host buffers (any may be NULL): csa_k, csa_v bf16
+ * [32][16][128]; hca_k, hca_v bf16 [16][128]; idx_k fp32 [128][4][64]. */
+hsa_status hsa_export_block(hsa_ctx* ctx, int32_t block, void* csa_k, void* csa_v,
+                            void* hca_k, void* hca_v, float* idx_k, void* stream);
+/* Copy one State block to host buffers (any may be NULL): swa_k, swa_v bf16
+ * [n_win][16][128] in ring-slot order (token p sits in slot p mod n_win);
+ * idx_tail fp32 [128][4][64] (token p in slot p mod 128). */
+hsa_status hsa_export_state(hsa_ctx* ctx, int32_t state, void* swa_k, void* swa_v,
+                            float* idx_tail, void* stream);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around each
+ * launch of the kernels in `mask` (bit i = kernel id i below); 0 disables.
+ * hsa_timing_read waits for the recorded events, returns total milliseconds
+ * and launch counts per kernel id (arrays of HSA_KERNEL_COUNT) and clears. */
+#define HSA_KERNEL_APPEND 0   /* decode append + fused seal            */
+#define HSA_KERNEL_SEAL 1     /* bulk seal                             */
+#define HSA_KERNEL_WRITE 2    /* bulk ring / indexer-tail write        */
+#define HSA_KERNEL_SCORE 3    /* indexer scores                        */
+#define HSA_KERNEL_SELECT 4   /* top-k select                          */
+#define HSA_KERNEL_ATTEND 5   /* split-KV attention partials           */
+#define HSA_KERNEL_COMBINE 6  /* partial merge                         */
+#define HSA_KERNEL_COUNT 7
+hsa_status hsa_timing_enable(hsa_ctx* ctx, uint32_t mask);
+hsa_status hsa_timing_read(hsa_ctx* ctx, double* ms, int64_t* launches);
+
+const char* hsa_status_str(hsa_status s);
+/* Text of the last error raised in this thread (argument or HIP failure). */
+const char* hsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_H */
