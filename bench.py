@@ -1,0 +1,401 @@
+"""Decode-step benchmark of the heterogeneous KV cache on one MI355X.
+
+A step is one pass of the whole hot path over the batch: append one token per
+request into its State (sealing full blocks into the Block Cache), indexer
+scores + top-k over every sealed C4 entry, and heterogeneous attention over
+SWA + HCA + selected C4 entries (hsa_decode_step). Inputs are synthetic and
+resident in HBM before timing starts.
+
+  python bench.py [--steps K] [--warmup W] [--workload 2]
+prints one JSON line. Other modes (for the profiles):
+  python bench.py --copy-calibration      a plain copy kernel of known size
+  python bench.py --counters DIR          summarise rocprofv3 --pmc output
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from synth import workloads  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+ROW = 8192                     # K + V bytes of one token or entry (2 x 16 x 128 bf16)
+IDX_BLOCK = 131072             # indexer keys of one block (128 x 4 x 64 fp32)
+SEAL_BYTES = 1581056           # per seal: read 128 tokens K/V + 128 indexer keys, write 32 C4 + 1 HCA + 128 keys
+KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
+                 "attend": "k_attend", "combine": "k_combine", "seal": "k_bulk_seal",
+                 "write": "k_bulk_write"}
+KERNEL_SOURCES = {"attend": ["attend.hip", "device.h"], "score": ["indexer_topk.hip", "device.h"],
+                  "select": ["indexer_topk.hip", "device.h"], "append": ["append_seal.hip", "device.h"],
+                  "combine": ["attend.hip", "device.h"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+
+def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray) -> dict:
+    """Bytes the method must move in one decode step, per kernel (scratch excluded).
+
+    L_after: lengths after the append; nb: sealed blocks after it; sealed: 1 where
+    the step sealed a block."""
+    swa = np.minimum(L_after, n_win)
+    kk = np.minimum(k, 32 * nb)
+    B = len(L_after)
+    out = {
+        # token K, V, indexer key in; ring slot + tail slot out; seals
+        "append": int(B * 2 * (ROW + 1024) + sealed.sum() * SEAL_BYTES),
+        # indexer keys of every sealed block + the indexer query
+        "score": int((nb * IDX_BLOCK).sum() + B * 1024),
+        # top-k ordinals and scores out
+        "select": int((kk * 8).sum()),
+        # K and V rows of every attended key, the query, the top-k ordinals
+        "attend": int(((swa + nb + kk) * ROW).sum() + B * 4096 + (kk * 4).sum()),
+        # fp32 output
+        "combine": int(B * 8192),
+    }
+    out["step"] = sum(out.values())
+    return out
+
+
+def src_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "heterogeneous_sparse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ the b32 decode workload
+
+def setup_decode(wl, extra_steps: int):
+    """Cache with every request prefilled to L0 (bulk append of device-generated tokens)."""
+    import torch
+    import heterogeneous_sparse_attention_amd as hsa
+    from synth.device import fill_rows
+
+    Wc, Wh = synth.gate_weights(wl.seed)
+    L0 = wl.prefill.astype(np.int64)
+    B = wl.batch
+    max_len = int(L0.max()) + extra_steps + 1
+    max_blocks = int(((L0 + extra_steps) // 128).sum()) + B + 8
+    cache = hsa.Cache(wl.n_win, B, max_blocks, Wc, Wh, max_blocks_per_state=max_len // 128 + 2)
+    states = [cache.state_alloc() for _ in range(B)]
+    # prefill in pieces of at most 64K tokens
+    chunk = 65536
+    order = list(range(B))
+    i = 0
+    while i < B:
+        grp, tot = [], 0
+        while i < B and (tot + int(L0[order[i]]) <= chunk or not grp):
+            grp.append(order[i])
+            tot += int(L0[order[i]])
+            i += 1
+        cu = np.concatenate([[0], np.cumsum(L0[grp])]).astype(np.int64)
+        T = int(cu[-1])
+        keys = torch.from_numpy(np.repeat(np.array(grp, np.int64), L0[grp]).astype(np.int32)).cuda()
+        pos = torch.from_numpy(np.concatenate([np.arange(L0[b]) for b in grp]).astype(np.int64)).cuda()
+        K = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
+        V = torch.empty_like(K)
+        KI = torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")
+        fill_rows(K, wl.seed, synth.STREAM_K, keys=keys, pos=pos)
+        fill_rows(V, wl.seed, synth.STREAM_V, keys=keys, pos=pos)
+        fill_rows(KI, wl.seed, synth.STREAM_IDXK, keys=keys, pos=pos)
+        cache.append_kv([states[b] for b in grp], cu, K, V, KI)
+        del K, V, KI
+    torch.cuda.synchronize()
+    return cache, states
+
+
+def decode_inputs(wl, L0: np.ndarray, n_steps: int):
+    """Per-step device inputs: the token at position L0 + t for each request."""
+    import torch
+    from synth.device import fill_rows
+    B = wl.batch
+    pos = (L0[None, :] + np.arange(n_steps)[:, None]).reshape(-1).astype(np.int64)
+    keys = np.tile(np.arange(B), n_steps).astype(np.int32)
+    kt = torch.from_numpy(keys).cuda()
+    pt = torch.from_numpy(pos).cuda()
+    n = n_steps * B
+    t = {
+        "k": torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda"),
+        "v": torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda"),
+        "ki": torch.empty((n, 4, 64), dtype=torch.float32, device="cuda"),
+        "q": torch.empty((n, 16, 128), dtype=torch.bfloat16, device="cuda"),
+        "qi": torch.empty((n, 4, 64), dtype=torch.float32, device="cuda"),
+    }
+    for name, sid in (("k", synth.STREAM_K), ("v", synth.STREAM_V), ("ki", synth.STREAM_IDXK),
+                      ("q", synth.STREAM_Q), ("qi", synth.STREAM_QI)):
+        fill_rows(t[name], wl.seed, sid, keys=kt, pos=pt)
+    return {n_: x.view(n_steps, B, *x.shape[1:]) for n_, x in t.items()}
+
+
+def run_decode(args) -> dict:
+    import torch
+    wl = workloads.make(args.workload)
+    B, k = wl.batch, wl.topk
+    W, K = args.warmup, args.steps
+    cache, states = setup_decode(wl, W + K)
+    L0 = wl.prefill.astype(np.int64)
+    inp = decode_inputs(wl, L0, W + K)
+    topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+
+    def step(t):
+        cache.decode_step(states, inp["k"][t], inp["v"][t], inp["ki"][t], inp["q"][t], inp["qi"][t],
+                          k, topk_out=topk, out=out)
+
+    # warmup; its second half also times every kernel to find the dominant one
+    half = W // 2
+    for t in range(half):
+        step(t)
+    torch.cuda.synchronize()
+    cache.timing_enable(list(KERNEL_SYMBOL))
+    for t in range(half, W):
+        step(t)
+    torch.cuda.synchronize()
+    warm = cache.timing_read()
+    dominant = max(("append", "score", "select", "attend", "combine"), key=lambda n: warm[n][0])
+    if args.kernel:
+        dominant = args.kernel
+
+    # timed region: HIP events (inside the library, on the launch stream) around the
+    # dominant kernel only
+    cache.timing_enable([dominant])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for t in range(W, W + K):
+        step(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    kt = cache.timing_read()
+    cache.timing_enable([])
+
+    # algorithmic bytes of the timed steps (host knows every length)
+    bytes_k = {n: 0 for n in ("append", "score", "select", "attend", "combine", "step")}
+    for t in range(W, W + K):
+        L_after = L0 + t + 1
+        nb = L_after // 128
+        sealed = (L_after % 128 == 0).astype(np.int64)
+        sb = step_bytes(L_after, nb, wl.n_win, k, sealed)
+        for n in bytes_k:
+            bytes_k[n] += sb[n]
+    ms_per_step = ms_total / K
+    dom_ms, dom_n = kt[dominant]
+    achieved = (bytes_k[dominant] / dom_n) / (dom_ms / dom_n * 1e-3) / 1e9 if dom_n else None
+    step_gbs = bytes_k["step"] / (ms_total * 1e-3) / 1e9
+
+    traffic = None
+    try:
+        tr = json.load(open(TRAFFIC_FILE))
+        ent = tr.get(KERNEL_SYMBOL[dominant])
+        if ent and ent.get("src_sha") == src_hash(dominant) and ent.get("workload") == wl.name:
+            traffic = ent.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    res = {
+        "metric": "decode tokens/s + achieved HBM GB/s (% of peak), append+attend, B=32 L<=8K",
+        "value": B * K / (ms_total * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {B} requests, L0 ~ U{{1..8192}} (seed {wl.seed:#x}), "
+                               f"decode steps, n_win {wl.n_win}, top-k {k}, 16x128 bf16 K/V/Q, "
+                               f"indexer 4x64 fp32, m=4, m'=128, 1 layer",
+                   "batch": B, "n_win": wl.n_win, "topk": k, "kv_dtype": "bf16",
+                   "L0_mean": float(L0.mean()), "parallelism": "single GPU"},
+        "hbm_gbps": step_gbs,
+        "hbm_frac_of_peak": step_gbs / PEAK_HBM_GBS,
+        "bytes_per_step": bytes_k["step"] / K,
+        "wall_s": wall,
+        "roofline": {"bound": "hbm", "kernel": KERNEL_SYMBOL[dominant],
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": (achieved / PEAK_HBM_GBS) if achieved else None,
+                     "traffic": traffic,
+                     "avg_launch_us": (dom_ms / dom_n * 1e3) if dom_n else None,
+                     "algorithmic_bytes_per_launch": (bytes_k[dominant] / dom_n) if dom_n else None},
+        "kernels_us_per_step": {n: warm[n][0] / max(1, W - half) * 1e3 for n in
+                                ("append", "score", "select", "attend", "combine")},
+    }
+    cache.close()
+    return res
+
+
+# ------------------------------------------------------------------ CPU baseline (the oracle)
+
+def cpu_baseline(args, budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on the host: decode steps of a sample of requests."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import Oracle
+
+    wl = workloads.make(args.workload)
+    Wc, Wh = synth.gate_weights(wl.seed)
+    sample = list(range(0, wl.batch, 4))           # every 4th request
+    L0 = wl.prefill.astype(np.int64)
+    max_steps = 160
+    with threadpool_limits(1):
+        o = Oracle(wl.n_win, Wc, Wh, wl.batch, int((L0 // 128).sum()) + 64)
+        st = {}
+        for b in sample:                              # untimed: build the prefill state
+            st[b] = o.state_alloc()
+            pos = np.arange(L0[b])
+            key = np.full(pos.shape, b, np.uint64)
+            K = synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_K, key, pos))
+            V = synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_V, key, pos))
+            KI = synth.tokens_f32(wl.seed, synth.STREAM_IDXK, key, pos)
+            o.append([st[b]], [(K, V, KI)])
+        inputs = []
+        for t in range(max_steps):                    # untimed: the decode inputs
+            row = []
+            for b in sample:
+                p = np.array([L0[b] + t])
+                key = np.array([b], np.uint64)
+                row.append((synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_K, key, p)),
+                            synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_V, key, p)),
+                            synth.tokens_f32(wl.seed, synth.STREAM_IDXK, key, p),
+                            synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_Q, key, p))[0],
+                            synth.tokens_f32(wl.seed, synth.STREAM_QI, key, p)[0]))
+            inputs.append(row)
+        t0 = time.perf_counter()
+        steps = 0
+        for t in range(max_steps):
+            for b, (K, V, KI, q, qi) in zip(sample, inputs[t]):
+                o.append([st[b]], [(K, V, KI)])
+                idx, _ = o.topk(st[b], qi, wl.topk)
+                o.attend(st[b], q, idx, wl.topk)
+            steps += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": len(sample) * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sample)} of {wl.batch} requests (every 4th), {steps} decode steps each "
+                      f"(append with seals, indexer top-k, attention; fp64 NumPy, 1 thread), "
+                      f"{dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ counters
+
+def copy_calibration(args):
+    """A plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}))
+
+
+def summarize_counters(args):
+    """Read rocprofv3 --pmc counter_collection CSVs (FETCH_SIZE, WRITE_SIZE, in KiB per
+    dispatch) for the copy calibration and the bench, and write profiles/traffic.json."""
+    import csv
+    d = args.counters
+    rows = []
+    dirs = d.split(",")
+    for p in [q for dd in dirs for q in glob.glob(os.path.join(dd, "**", "*counter_collection.csv"),
+                                                  recursive=True)]:
+        with open(p) as fh:
+            for r in csv.DictReader(fh):
+                r["_file"] = p
+                rows.append(r)
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+
+    def per_kernel(counter, match):
+        vals = [float(r["Counter_Value"]) for r in rows
+                if r.get("Counter_Name") == counter and match(r.get("Kernel_Name", ""))]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    copy_bytes = 256 << 20
+    # the calibration copy (torch copy_ of 256 MiB on the device) runs as the runtime's
+    # copyBuffer kernel; the bench's own setup copies are excluded by the file name
+    is_copy = lambda n: "copyBuffer" in n
+    def per_copy(counter):
+        vals = [float(r["Counter_Value"]) for r in rows if r.get("Counter_Name") == counter
+                and is_copy(r.get("Kernel_Name", "")) and "copy_counter" in os.path.basename(r["_file"])]
+        return sum(vals) / len(vals) if vals else None
+    cf, cw = per_copy("FETCH_SIZE"), per_copy("WRITE_SIZE")
+    out = {"copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes}
+    sf = copy_bytes / (cf * 1024) if cf else None
+    sw = copy_bytes / (cw * 1024) if cw else None
+    out["fetch_scale"], out["write_scale"] = sf, sw
+    for name, sym in KERNEL_SYMBOL.items():
+        f, nf = per_kernel("FETCH_SIZE", lambda n, s=sym: s + "(" in n)
+        w, nw = per_kernel("WRITE_SIZE", lambda n, s=sym: s + "(" in n)
+        if not nf:
+            continue
+        ent = {"fetch_kib": f, "write_kib": w, "dispatches": nf, "src_sha": src_hash(name),
+               "workload": args.counters_workload}
+        if sf and sw and f is not None and w is not None:
+            ent["traffic_bytes_per_launch"] = f * 1024 * sf + w * 1024 * sw
+        out[sym] = ent
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", type=int, default=2, choices=[2])
+    ap.add_argument("--kernel", default=None, help="time this kernel in the timed region")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--counters", default=None, help="comma-separated rocprofv3 --pmc output dirs")
+    ap.add_argument("--counters-workload", default="b32")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU "
+              "path: the cache shards by request, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    if args.counters:
+        summarize_counters(args)
+        return
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
+    args.warmup = max(args.warmup, 2)
+    res = run_decode(args)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
