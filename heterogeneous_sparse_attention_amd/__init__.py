@@ -22,7 +22,8 @@ H, D, HI, DI = 16, 128, 4, 64
 MAX_TOPK = 4096
 APPEND_DEFER_SEAL = 1
 
-KERNELS = ("append", "seal", "write", "score", "select", "attend", "combine")
+KERNELS = ("append", "seal", "write", "score", "select", "attend")
+TOPK_SORTED = 1
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "Block Cache full", -3: "no free State slot",
@@ -67,9 +68,9 @@ SIGNATURES = {
     "hsa_append_kv": [_P, _I32, _P, _P, _P, _P, _P, _U32, _P],
     "hsa_compress_flush": [_P, _I32, _P, _P],
     "hsa_block_table_share": [_P, _I32, _I32, _P],
-    "hsa_indexer_topk": [_P, _I32, _P, _P, _I32, _P, _P, _P],
+    "hsa_indexer_topk": [_P, _I32, _P, _P, _I32, _U32, _P, _P, _P],
     "hsa_decode_attend": [_P, _I32, _P, _P, _P, _I32, _P, _P],
-    "hsa_decode_step": [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P],
+    "hsa_decode_step": [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _U32, _P, _P, _P, _P],
     "hsa_state_query": [_P, _I32, ctypes.POINTER(_StateInfo)],
     "hsa_block_table_get": [_P, _I32, _P, _I64, ctypes.POINTER(_I64)],
     "hsa_block_refcount": [_P, _I32, ctypes.POINTER(_I32)],
@@ -207,7 +208,8 @@ class Cache:
                "hsa_block_table_share")
 
     # -- indexer top-k --------------------------------------------------------------
-    def indexer_topk(self, states, q_idx, k: int, idx_out=None, score_out=None, stream=None):
+    def indexer_topk(self, states, q_idx, k: int, idx_out=None, score_out=None, sorted=False,
+                     stream=None):
         import torch
         st, stp = _host_i32(states)
         n = st.size
@@ -218,8 +220,8 @@ class Cache:
         sp = ctypes.c_void_p(0)
         if score_out is not None:
             sp = _dev(score_out, torch.float32, (n, k), "score_out")
-        _check(_lib.hsa_indexer_topk(self._ctx, n, stp, qp, int(k), op, sp, _stream(stream)),
-               "hsa_indexer_topk")
+        _check(_lib.hsa_indexer_topk(self._ctx, n, stp, qp, int(k), TOPK_SORTED if sorted else 0,
+                                     op, sp, _stream(stream)), "hsa_indexer_topk")
         return idx_out, score_out
 
     # -- attention -----------------------------------------------------------------
@@ -239,7 +241,7 @@ class Cache:
         return out
 
     def decode_step(self, states, k_new, v_new, idx_new, q, q_idx, k: int,
-                    topk_out=None, score_out=None, out=None, stream=None):
+                    topk_out=None, score_out=None, out=None, sorted=False, stream=None):
         import torch
         st, stp = _host_i32(states)
         n = st.size
@@ -258,7 +260,7 @@ class Cache:
             _dev(idx_new, torch.float32, (n, HI, DI), "idx_new"),
             _dev(q, torch.bfloat16, (n, H, D), "q"),
             _dev(q_idx, torch.float32, (n, HI, DI), "q_idx"),
-            int(k), _dev(topk_out, torch.int32, (n, k), "topk_out"), sp,
+            int(k), TOPK_SORTED if sorted else 0, _dev(topk_out, torch.int32, (n, k), "topk_out"), sp,
             _dev(out, torch.float32, (n, H, D), "out"), _stream(stream)), "hsa_decode_step")
         return topk_out, score_out, out
 

@@ -46,7 +46,7 @@ struct hsa_ctx {
   float* part_ml = nullptr;    // [chunks][2][16] running max and sum
   size_t part_ml_cap = 0;
   float* seal_part = nullptr;  // kMaxReq * kSealSplit HCA partials
-  int32_t* tickets = nullptr;  // kMaxReq, zero between launches
+  int32_t* tickets = nullptr;  // [2][kMaxReq]: seal merge, attention merge; zero between launches
 
   // bulk-plan staging: pinned host -> device
   void* plan_host = nullptr;
@@ -64,7 +64,7 @@ struct hsa_ctx {
   };
   std::vector<Rec> recs;
 
-  int32_t attend_chunk = 32;
+  int32_t attend_wgs = 512;   // attention workgroups per launch to aim for (one round)
 
   hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {}
 };
@@ -223,7 +223,7 @@ ReqBatch read_batch(hsa_ctx* c, const int32_t* states, int32_t b0, int32_t n) {
 }
 
 int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx, int32_t k,
-             int32_t* idx_out, float* score_out, hipStream_t st) {
+             uint32_t flags, int32_t* idx_out, float* score_out, hipStream_t st) {
   for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
     const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
     ReqBatch B = read_batch(c, states, b0, n);
@@ -241,25 +241,38 @@ int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_id
     }
     {
       Timed t(c, HSA_KERNEL_SELECT, st);
-      HIP_TRY(launch_select(B, k, c->scores, ld, idx_out + (int64_t)b0 * k,
-                            score_out ? score_out + (int64_t)b0 * k : nullptr, st));
+      HIP_TRY(launch_select(B, k, (flags & HSA_TOPK_SORTED) ? 1 : 0, c->scores, ld,
+                            idx_out + (int64_t)b0 * k, score_out ? score_out + (int64_t)b0 * k : nullptr,
+                            st));
     }
   }
   return kOk;
 }
 
+// Keys per attention chunk: a multiple of 16 such that the launch has about
+// attend_wgs workgroups, i.e. fills the GPU once.
+int32_t attend_chunk(int64_t total_keys, int32_t n, int32_t target) {
+  const int64_t slots = std::max<int64_t>(64, target - n);
+  int64_t chunk = (total_keys + slots - 1) / slots;
+  chunk = std::max<int64_t>(16, (chunk + 15) / 16 * 16);
+  return (int32_t)std::min<int64_t>(chunk, 1 << 20);
+}
+
 int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
                const int32_t* topk, int32_t k, float* out, hipStream_t st) {
-  const int32_t chunk = c->attend_chunk;
   for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
     const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
     ReqBatch B = read_batch(c, states, b0, n);
-    int64_t total = 0;
+    std::vector<int64_t> nk(n);
+    int64_t keys = 0;
     for (int i = 0; i < n; ++i) {
       const int64_t swa = std::min<int64_t>(B.r[i].len, c->P.n_win);
-      const int64_t nk = swa + B.r[i].nb + std::min<int64_t>(k, (int64_t)kC4 * B.r[i].nb);
-      total += (nk + chunk - 1) / chunk;
+      nk[i] = swa + B.r[i].nb + std::min<int64_t>(k, (int64_t)kC4 * B.r[i].nb);
+      keys += nk[i];
     }
+    const int32_t chunk = attend_chunk(keys, n, c->attend_wgs);
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) total += (nk[i] + chunk - 1) / chunk;
     int s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)total,
                  kRow * sizeof(float));
     if (s) return s;
@@ -268,14 +281,9 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
     if (s) return s;
     const void* qb = static_cast<const uint16_t*>(q) + (int64_t)b0 * kRow;
     const int32_t* tk = topk ? topk + (int64_t)b0 * k : nullptr;
-    {
-      Timed t(c, HSA_KERNEL_ATTEND, st);
-      HIP_TRY(launch_attend(c->P, B, total, chunk, qb, tk, k, c->part_acc, c->part_ml, st));
-    }
-    {
-      Timed t(c, HSA_KERNEL_COMBINE, st);
-      HIP_TRY(launch_combine(c->P, B, chunk, k, c->part_acc, c->part_ml, out + (int64_t)b0 * kRow, st));
-    }
+    Timed t(c, HSA_KERNEL_ATTEND, st);
+    HIP_TRY(launch_attend(c->P, B, total, chunk, qb, tk, k, c->part_acc, c->part_ml,
+                          c->tickets + kMaxReq, out + (int64_t)b0 * kRow, st));
   }
   return kOk;
 }
@@ -321,7 +329,7 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
       S * (size_t)bps * 4,                                                // table
       2 * kRow * 4,                                                       // gates
       (size_t)kMaxReq * kSealSplit * kPartFloats * 4,                     // seal partials
-      (size_t)kMaxReq * 4};                                               // tickets
+      (size_t)2 * kMaxReq * 4};                                           // tickets
   for (int i = 0; i < 12; ++i) {
     st = dev_alloc(c, &p[i], bytes[i]);
     if (st) {
@@ -348,7 +356,7 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   c->tickets = static_cast<int32_t*>(p[11]);
   hipError_t e = hipMemcpy(gates, cfg->gate_csa, kRow * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(gates + kRow, cfg->gate_hca, kRow * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(c->tickets, 0, kMaxReq * 4);
+  if (e == hipSuccess) e = hipMemset(c->tickets, 0, 2 * kMaxReq * 4);
   if (e == hipSuccess) e = hipMemset(c->P.table, 0xff, bytes[8]);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -449,16 +457,19 @@ hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* str
 }
 
 hsa_status hsa_indexer_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx,
-                            int32_t k, int32_t* idx_out, float* score_out, void* stream) {
+                            int32_t k, uint32_t flags, int32_t* idx_out, float* score_out,
+                            void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   std::string why;
   int st = c->ctl.check_states(n_req, states, false, false, &why);
   if (st) return fail(st, why);
   if (k < 1 || k > HSA_MAX_TOPK) return fail(kInvalid, "k must be in [1, 4096]");
+  if (flags & ~HSA_TOPK_SORTED) return fail(kInvalid, "unknown flags");
   if (n_req > 0 && (!q_idx || !idx_out)) return fail(kInvalid, "NULL device pointer");
   if (n_req == 0) return kOk;
   if ((st = set_device(c))) return st;
-  return run_topk(c, n_req, states, q_idx, k, idx_out, score_out, static_cast<hipStream_t>(stream));
+  return run_topk(c, n_req, states, q_idx, k, flags, idx_out, score_out,
+                  static_cast<hipStream_t>(stream));
 }
 
 hsa_status hsa_decode_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
@@ -478,12 +489,13 @@ hsa_status hsa_decode_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, c
 
 hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* k_new,
                            const void* v_new, const float* idx_new, const void* q,
-                           const float* q_idx, int32_t k, int32_t* topk_out, float* score_out,
-                           float* out, void* stream) {
+                           const float* q_idx, int32_t k, uint32_t flags, int32_t* topk_out,
+                           float* score_out, float* out, void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   if (n_req < 0) return fail(kInvalid, "n_req < 0");
   if (n_req == 0) return kOk;
   if (k < 1 || k > HSA_MAX_TOPK) return fail(kInvalid, "k must be in [1, 4096]");
+  if (flags & ~HSA_TOPK_SORTED) return fail(kInvalid, "unknown flags");
   if (!k_new || !v_new || !idx_new || !q || !q_idx || !topk_out || !out)
     return fail(kInvalid, "NULL device pointer");
   std::vector<int64_t> cu(n_req + 1);
@@ -496,7 +508,7 @@ hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, con
   c->ctl.commit(&plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = run_decode_append(c, plan, k_new, v_new, idx_new, s))) return st;
-  if ((st = run_topk(c, n_req, states, q_idx, k, topk_out, score_out, s))) return st;
+  if ((st = run_topk(c, n_req, states, q_idx, k, flags, topk_out, score_out, s))) return st;
   return run_attend(c, n_req, states, q, topk_out, k, out, s);
 }
 

@@ -8,7 +8,8 @@
 // The score is not defined on the pages. Reading used: score of token t = sum over
 // 4 heads x 64 dims of q_idx * k_idx_t; score of C4 entry j = mean of the scores
 // of its tokens 4j..4j+3. Top-k keeps kk = min(k, N_c) entries ordered by score
-// descending, ties to the lowest C4 ordinal.
+// descending, ties to the lowest C4 ordinal, written in ascending ordinal order
+// (or in that selection order on request).
 #include "device.h"
 #include "kernels.h"
 
@@ -20,7 +21,7 @@ namespace {
 // entries 8w .. 8w+7. Lane l owns dims 4l..4l+3 of every token row, so each
 // token row is one coalesced 1 KiB read per wave; the 4 tokens of an entry are
 // summed per lane before one wave reduction.
-__global__ __launch_bounds__(256) void k_score(Pools P, ReqBatch B, const float* q_idx,
+__global__ __launch_bounds__(256, 4) void k_score(Pools P, ReqBatch B, const float* q_idx,
                                                float* scores, int64_t ld) {
   int w = blockIdx.x, r = 0;
   for (; r < B.n - 1; ++r) {
@@ -71,21 +72,44 @@ __device__ __forceinline__ float okey_inv(uint32_t u) {
 }
 
 constexpr int kSelThreads = 1024;
-constexpr int kCacheN = 4096;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kCacheN = 16384;     // scores kept in LDS (64 KiB)
+constexpr int kBins = 2048;        // radix digits of 11, 11 and 10 bits
 
-// One workgroup per request. Radix select (4 passes of 8 bits, most significant
-// first) finds tau, the key of the kk-th best score, and how many entries equal
-// to tau make the cut; entries above tau and the first such entries equal to tau
-// (in ordinal order, ballot + prefix count) are gathered and sorted by (key desc,
-// ordinal asc) with a bitonic sort in LDS.
-__global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, const float* scores,
-                                                        int64_t ld, int32_t* idx_out,
-                                                        float* score_out) {
-  __shared__ uint32_t cache[kCacheN];
-  __shared__ uint32_t hist[256];
+// Ordered count: for a flag per thread, the number of set flags in lower threads of
+// the workgroup, and the workgroup total. Two barriers; `cnt` is LDS scratch.
+__device__ __forceinline__ int ordered_rank(bool f, int* cnt, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const unsigned long long bal = __ballot(f);
+  if (lane == 0) cnt[wv] = __popcll(bal);
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int c = cnt[w];
+    before += (w < wv) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + __popcll(bal & ((1ull << lane) - 1ull));
+}
+
+// One workgroup per request. Radix select over the order-preserving keys finds
+// tau, the key of the kk-th entry under (score desc, ordinal asc), and `rem`,
+// how many entries equal to tau make the cut. One ordered pass then takes every
+// entry above tau and the first `rem` entries equal to tau, writing them in
+// ascending ordinal order (ballot + prefix counts). With `sorted`, the taken
+// entries are instead ordered by (score desc, ordinal asc) with a bitonic sort in
+// LDS.
+__global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, int32_t sorted,
+                                                        const float* scores, int64_t ld,
+                                                        int32_t* idx_out, float* score_out) {
+  __shared__ uint32_t keys[kCacheN];
+  __shared__ uint32_t hist[kBins];
   __shared__ unsigned long long cand[kMaxTopk];
-  __shared__ int sh[4];
-  __shared__ int wave_cnt[kSelThreads / 64];
+  __shared__ int sh[2];
+  __shared__ int cnt[kSelWaves];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int N = kC4 * B.r[r].nb;
@@ -96,28 +120,38 @@ __global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, c
   const bool cached = N <= kCacheN;
 
   if (kk > 0) {
-    if (cached)
-      for (int i = tid; i < N; i += kSelThreads) cache[i] = okey(S[i]);
-    auto key = [&](int i) -> uint32_t { return cached ? cache[i] : okey(S[i]); };
+    if (cached) {   // N is a multiple of 32: float4 loads
+      for (int i = tid; i < N / 4; i += kSelThreads) {
+        const float4 v = reinterpret_cast<const float4*>(S)[i];
+        keys[4 * i] = okey(v.x);
+        keys[4 * i + 1] = okey(v.y);
+        keys[4 * i + 2] = okey(v.z);
+        keys[4 * i + 3] = okey(v.w);
+      }
+    }
+    auto key = [&](int i) -> uint32_t { return cached ? keys[i] : okey(S[i]); };
 
-    uint32_t prefix = 0u, mask = 0u;
+    uint32_t prefix = 0u, pmask = 0u;
     int rem = kk;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0u;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+      for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0u;
       __syncthreads();
       for (int i = tid; i < N; i += kSelThreads) {
         const uint32_t u = key(i);
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
       __syncthreads();
       if (tid < 64) {
-        // lane l holds digits 255-4l .. 252-4l (descending)
-        uint32_t c[4], tot = 0u;
+        // lane l holds digits 2047-32l down to 2016-32l
+        const uint4* h4 = reinterpret_cast<const uint4*>(hist + kBins - 32 * (tid + 1));
+        uint32_t tot = 0u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          c[q] = hist[255 - 4 * tid - q];
-          tot += c[q];
+        for (int q = 0; q < 8; ++q) {
+          const uint4 v = h4[q];
+          tot += v.x + v.y + v.z + v.w;
         }
         uint32_t incl = tot;
 #pragma unroll
@@ -126,86 +160,80 @@ __global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, c
           if (tid >= o) incl += y;
         }
         const unsigned long long bal = __ballot(incl >= (uint32_t)rem);
-        const int first = __ffsll(bal) - 1;
+        const int first = (int)__ffsll((long long)bal) - 1;
         if (tid == first) {
           uint32_t cum = incl - tot;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (cum + c[q] >= (uint32_t)rem) {
-              sh[0] = 255 - 4 * tid - q;
+          for (int q = 0; q < 32; ++q) {
+            const int d = kBins - 1 - 32 * tid - q;
+            const uint32_t c = hist[d];
+            if (cum + c >= (uint32_t)rem) {
+              sh[0] = d;
               sh[1] = (int)cum;
               break;
             }
-            cum += c[q];
+            cum += c;
           }
         }
       }
       __syncthreads();
       prefix |= (uint32_t)sh[0] << shift;
-      mask |= 255u << shift;
+      pmask |= dmask << shift;
       rem -= sh[1];
       __syncthreads();
     }
     const uint32_t tau = prefix;
-    const int n_gt = kk - rem;
-    if (tid == 0) sh[2] = 0;
-    __syncthreads();
-    for (int i = tid; i < N; i += kSelThreads) {
-      const uint32_t u = key(i);
-      if (u > tau) {
-        const int pos = atomicAdd(&sh[2], 1);
-        if (pos < n_gt) cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
-      }
-    }
-    // entries equal to tau, lowest ordinals first
-    const int lane = tid & 63, wv = tid >> 6;
-    int base = 0;
-    for (int c0 = 0; c0 < N && base < rem; c0 += kSelThreads) {
+    // ordered pass: take entries above tau and the first `rem` equal to tau
+    int base_eq = 0, base_take = 0;
+    for (int c0 = 0; c0 < N && base_take < kk; c0 += kSelThreads) {
       const int i = c0 + tid;
-      const bool eq = i < N && key(i) == tau;
-      const unsigned long long bal = __ballot(eq);
-      if (lane == 0) wave_cnt[wv] = __popcll(bal);
-      __syncthreads();
-      int before = 0, total = 0;
-      for (int w = 0; w < kSelThreads / 64; ++w) {
-        before += (w < wv) ? wave_cnt[w] : 0;
-        total += wave_cnt[w];
-      }
-      const int rank = base + before + __popcll(bal & ((1ull << lane) - 1ull));
-      if (eq && rank < rem) cand[n_gt + rank] = ((unsigned long long)(~tau) << 32) | (uint32_t)i;
-      base += total;
-      __syncthreads();
-    }
-    // bitonic sort of cand[0 .. n2) ascending; padding sorts last
-    int n2 = 1;
-    while (n2 < kk) n2 <<= 1;
-    for (int i = kk + tid; i < n2; i += kSelThreads) cand[i] = ~0ull;
-    __syncthreads();
-    for (int size = 2; size <= n2; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int t = tid; t < n2 / 2; t += kSelThreads) {
-          const int i = 2 * t - (t & (stride - 1));
-          const int j = i + stride;
-          const bool asc = (i & size) == 0;
-          const unsigned long long a = cand[i], b = cand[j];
-          if ((a > b) == asc) {
-            cand[i] = b;
-            cand[j] = a;
-          }
+      const uint32_t u = i < N ? key(i) : 0u;
+      const bool eq = i < N && u == tau;
+      int n_eq;
+      const int req = base_eq + ordered_rank(eq, cnt, &n_eq);
+      const bool take = i < N && (u > tau || (eq && req < rem));
+      int n_take;
+      const int pos = base_take + ordered_rank(take, cnt, &n_take);
+      if (take) {
+        if (sorted) {
+          cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
+        } else {
+          io[pos] = i;
+          if (so) so[pos] = okey_inv(u);
         }
-        __syncthreads();
+      }
+      base_eq += n_eq;
+      base_take += n_take;
+    }
+    if (sorted) {
+      int n2 = 1;
+      while (n2 < kk) n2 <<= 1;
+      for (int i = kk + tid; i < n2; i += kSelThreads) cand[i] = ~0ull;
+      __syncthreads();
+      for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int t = tid; t < n2 / 2; t += kSelThreads) {
+            const int i = 2 * t - (t & (stride - 1));
+            const int j = i + stride;
+            const bool asc = (i & size) == 0;
+            const unsigned long long a = cand[i], b = cand[j];
+            if ((a > b) == asc) {
+              cand[i] = b;
+              cand[j] = a;
+            }
+          }
+          __syncthreads();
+        }
+      }
+      for (int i = tid; i < kk; i += kSelThreads) {
+        const unsigned long long c = cand[i];
+        io[i] = (int32_t)(c & 0xffffffffull);
+        if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
       }
     }
   }
-  for (int i = tid; i < k; i += kSelThreads) {
-    if (i < kk) {
-      const unsigned long long c = cand[i];
-      io[i] = (int32_t)(c & 0xffffffffull);
-      if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
-    } else {
-      io[i] = -1;
-      if (so) so[i] = -INFINITY;
-    }
+  for (int i = kk + tid; i < k; i += kSelThreads) {
+    io[i] = -1;
+    if (so) so[i] = -INFINITY;
   }
 }
 
@@ -218,11 +246,11 @@ hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks,
   return hipGetLastError();
 }
 
-hipError_t launch_select(const ReqBatch& B, int32_t k, const float* scores, int64_t ld,
-                         int32_t* idx_out, float* score_out, hipStream_t st) {
+hipError_t launch_select(const ReqBatch& B, int32_t k, int32_t sorted, const float* scores,
+                         int64_t ld, int32_t* idx_out, float* score_out, hipStream_t st) {
   if (B.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_select, dim3(B.n), dim3(kSelThreads), 0, st, B, k, scores, ld, idx_out,
-                     score_out);
+  hipLaunchKernelGGL(k_select, dim3(B.n), dim3(kSelThreads), 0, st, B, k, sorted, scores, ld,
+                     idx_out, score_out);
   return hipGetLastError();
 }
 

@@ -19,17 +19,18 @@ hipError_t launch_bulk_write(const Pools& P, const WriteDesc* w, int32_t n_req, 
 // Scores of every sealed C4 entry of the batch's requests: scores[i * ld + j].
 hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks, const float* q_idx,
                         float* scores, int64_t ld, hipStream_t st);
-// Top-k of each request's scores (one workgroup per request).
-hipError_t launch_select(const ReqBatch& B, int32_t k, const float* scores, int64_t ld,
-                         int32_t* idx_out, float* score_out, hipStream_t st);
+// Top-k of each request's scores (one workgroup per request), in ascending ordinal
+// order, or by (score desc, ordinal asc) when `sorted`.
+hipError_t launch_select(const ReqBatch& B, int32_t k, int32_t sorted, const float* scores,
+                         int64_t ld, int32_t* idx_out, float* score_out, hipStream_t st);
 
 // attend.hip
 // Keys of request i: min(len, n_win) SWA + nb HCA + min(k, 32 nb) C4 slots, cut in
-// chunks of `chunk` keys; one workgroup per chunk writes an unnormalised partial.
+// chunks of `chunk` keys (a multiple of 16); one workgroup per chunk. The last chunk
+// of each request merges the request's partials into out[i]; tickets[i] counts
+// finished chunks and is back at zero when the launch ends.
 hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks, int32_t chunk,
                          const void* q, const int32_t* topk, int32_t k, float* part_acc,
-                         float* part_ml, hipStream_t st);
-hipError_t launch_combine(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,
-                          const float* part_acc, const float* part_ml, float* out, hipStream_t st);
+                         float* part_ml, int32_t* tickets, float* out, hipStream_t st);
 
 }  // namespace hsa

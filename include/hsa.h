@@ -56,6 +56,8 @@ typedef int32_t hsa_status;
 
 #define HSA_MAX_TOPK 4096        /* largest k accepted by indexer_topk / attend     */
 
+#define HSA_TOPK_SORTED 1u       /* top-k rows by (score desc, ordinal asc)         */
+
 typedef struct hsa_ctx hsa_ctx;
 
 typedef struct hsa_config {
@@ -139,13 +141,15 @@ hsa_status hsa_block_table_share(hsa_ctx* ctx, int32_t src, int32_t dst, void* s
  * CSA entries are read sparsely through top-k).
  *   q_idx     dev fp32 [n_req][4][64]
  *   idx_out   dev int32 [n_req][k]: C4 ordinals j (block j/32, slot j%32 of
- *             the state's table), the kk = min(k, 32 * n_blocks) best scores,
- *             ordered by score descending then ordinal ascending, then -1
- *   score_out dev fp32 [n_req][k] or NULL: the scores, -inf after kk
+ *             the state's table) of the kk = min(k, 32 * n_blocks) entries that
+ *             come first by score descending, ties to the lowest ordinal; they
+ *             are written in ascending ordinal order, or in that selection order
+ *             with HSA_TOPK_SORTED; -1 after kk
+ *   score_out dev fp32 [n_req][k] or NULL: their scores, -inf after kk
  * Score of token t: sum over 4 heads x 64 dims of q_idx * idx_key_t; score of
  * C4 entry j = mean of its 4 tokens' scores. 1 <= k <= HSA_MAX_TOPK. */
 hsa_status hsa_indexer_topk(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
-                            const float* q_idx, int32_t k, int32_t* idx_out,
+                            const float* q_idx, int32_t k, uint32_t flags, int32_t* idx_out,
                             float* score_out, void* stream);
 
 /* Heterogeneous decode attention ([Q&A] §4 step 4: sparse/dense reads of the
@@ -164,12 +168,12 @@ hsa_status hsa_decode_attend(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
 
 /* One decode step ([Q&A] §4): append one token per request (k_new, v_new dev
  * bf16 [n_req][16][128], idx_new dev fp32 [n_req][4][64]) sealing full blocks,
- * then hsa_indexer_topk(q_idx, k, topk_out, score_out), then
+ * then hsa_indexer_topk(q_idx, k, flags, topk_out, score_out), then
  * hsa_decode_attend(q, topk_out, k, out). Same argument rules as those calls;
  * k >= 1. */
 hsa_status hsa_decode_step(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
                            const void* k_new, const void* v_new, const float* idx_new,
-                           const void* q, const float* q_idx, int32_t k,
+                           const void* q, const float* q_idx, int32_t k, uint32_t flags,
                            int32_t* topk_out, float* score_out, float* out, void* stream);
 
 /* ---- introspection (host side; the export calls synchronise `stream`) ---- */
@@ -197,9 +201,8 @@ hsa_status hsa_export_state(hsa_ctx* ctx, int32_t state, void* swa_k, void* swa_
 #define HSA_KERNEL_WRITE 2    /* bulk ring / indexer-tail write        */
 #define HSA_KERNEL_SCORE 3    /* indexer scores                        */
 #define HSA_KERNEL_SELECT 4   /* top-k select                          */
-#define HSA_KERNEL_ATTEND 5   /* split-KV attention partials           */
-#define HSA_KERNEL_COMBINE 6  /* partial merge                         */
-#define HSA_KERNEL_COUNT 7
+#define HSA_KERNEL_ATTEND 5   /* split-KV attention + merge            */
+#define HSA_KERNEL_COUNT 6
 hsa_status hsa_timing_enable(hsa_ctx* ctx, uint32_t mask);
 hsa_status hsa_timing_read(hsa_ctx* ctx, double* ms, int64_t* launches);
 

@@ -32,7 +32,10 @@ Readings taken where the pages leave a step open (each also in the design notes)
       n_win >= 128 > L mod 128).
   R8  top-k candidates are the sealed C4 entries only; kk = min(k, N_c); the
       rest of the row is padded with -1.
-  R9  top-k order: score descending, ties to the lowest C4 ordinal.
+  R9  top-k selection: the kk entries that come first under (score descending,
+      ordinal ascending), i.e. ties go to the lowest C4 ordinal. The pages fix no
+      output order; the entries are returned in ascending ordinal order, or in
+      selection order (score descending, ordinal ascending) when sorted=True.
   R10 block ids: lowest free id first, requests in call order, blocks in token
       order; state slots: lowest free first.
   R11 share(src, dst): dst (fresh) references every sealed block of src
@@ -121,14 +124,16 @@ def c4_scores(idx_keys: np.ndarray, q_idx: np.ndarray) -> np.ndarray:
     return s.reshape(C4_PER_BLOCK, M_CSA).sum(axis=1) / 4.0
 
 
-def select_topk(scores: np.ndarray, k: int):
-    """kk = min(k, N) largest scores, ordered by (score desc, ordinal asc); padded
-    to k with -1 (readings R8, R9). Returns (idx int32 [k], score float64 [k],
-    -inf padded)."""
+def select_topk(scores: np.ndarray, k: int, sorted: bool = False):
+    """The kk = min(k, N) entries first under (score desc, ordinal asc), padded to k
+    with -1 (readings R8, R9): in ascending ordinal order, or in that selection
+    order when sorted. Returns (idx int32 [k], score float64 [k], -inf padded)."""
     scores = np.asarray(scores, dtype=np.float64)
     n = scores.size
     kk = min(int(k), n)
     order = np.lexsort((np.arange(n), -scores))[:kk]    # primary: -score, then ordinal
+    if not sorted:
+        order = np.sort(order)
     idx = np.full(k, -1, np.int32)
     val = np.full(k, -np.inf, np.float64)
     idx[:kk] = order
@@ -312,10 +317,10 @@ class Oracle:
         out = [c4_scores(self.store[b].idx, q_idx) for b in st.blocks]
         return np.concatenate(out) if out else np.zeros(0)
 
-    def topk(self, s: int, q_idx, k: int):
+    def topk(self, s: int, q_idx, k: int, sorted: bool = False):
         if k < 1:
             raise OracleError("invalid", "k must be >= 1")
-        return select_topk(self.scores(s, q_idx), k)
+        return select_topk(self.scores(s, q_idx), k, sorted)
 
     # -- heterogeneous attention -------------------------------------------------
     def keys(self, s: int, sel, k: int | None = None):

@@ -73,15 +73,16 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
-def topk_accept(gpu_idx, gpu_val, ref_scores, k, eps_rel=1e-4):
+def topk_accept(gpu_idx, gpu_val, ref_scores, k, eps_rel=1e-4, sorted=False):
     """True if the GPU's top-k row is an acceptable answer for the oracle scores:
-    kk = min(k, N) valid entries, -1 after, and every index outside the oracle's
-    set (or missing from it) has an oracle score within eps of the oracle's kk-th
-    score tau; order by score descending."""
+    kk = min(k, N) distinct valid entries, -1 after, and every index outside the
+    oracle's set (or missing from it) has an oracle score within eps of the
+    oracle's kk-th score tau; ascending ordinals, or scores non-increasing (within
+    eps) when sorted."""
     from oracle import select_topk
     N = len(ref_scores)
     kk = min(k, N)
-    ref_idx, ref_val = select_topk(ref_scores, k)
+    ref_idx, ref_val = select_topk(ref_scores, k, sorted=True)
     g = np.asarray(gpu_idx)
     if np.any(g[kk:] != -1) or np.any(g[:kk] < 0) or np.any(g[:kk] >= N):
         return False
@@ -94,5 +95,7 @@ def topk_accept(gpu_idx, gpu_val, ref_scores, k, eps_rel=1e-4):
     diff = set(g[:kk].tolist()) ^ set(ref_idx[:kk].tolist())
     if any(abs(ref_scores[j] - tau) > eps for j in diff):
         return False
+    if not sorted:
+        return bool(np.all(np.diff(g[:kk]) > 0))
     s = ref_scores[g[:kk]]
     return bool(np.all(np.diff(s) <= eps))

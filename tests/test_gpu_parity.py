@@ -105,10 +105,11 @@ def test_l130_example_then_decode_to_256():
         Kn, Vn, KIn = dev_tokens(seed, 0, [p])
         Q, QI = dev_queries(seed, 0, [p])
         sc = torch.empty((1, k), dtype=torch.float32, device="cuda")
-        idx, _, out = cache.decode_step([s], Kn, Vn, KIn, Q, QI, k, score_out=sc)
+        srt = p % 2 == 1          # odd steps ask for score-ordered rows
+        idx, _, out = cache.decode_step([s], Kn, Vn, KIn, Q, QI, k, score_out=sc, sorted=srt)
         o.append([s], [host_tokens(seed, 0, [p])])
         q, qi = host_queries(seed, 0, [p])
-        ridx, rval = o.topk(s, qi[0], k)
+        ridx, rval = o.topk(s, qi[0], k, sorted=srt)
         gidx = idx.cpu().numpy()[0]
         assert np.array_equal(gidx, ridx), p
         g = sc.cpu().numpy()[0]
@@ -170,14 +171,14 @@ def test_deferred_seal_flush_equals_default():
             assert np.array_equal(ea[f], eb[f])
 
 
-def _decode_batch(cache, o, states, keys, seed, k, check_scores=True):
+def _decode_batch(cache, o, states, keys, seed, k, check_scores=True, sorted=False):
     """One decode step for `states` (token position = current length), GPU vs oracle."""
     import torch
     pos = np.array([o.info(s)["len"] for s in states])
     Kn, Vn, KIn = dev_tokens(seed, keys, pos)
     Q, QI = dev_queries(seed, keys, pos)
     sc = torch.empty((len(states), k), dtype=torch.float32, device="cuda")
-    idx, _, out = cache.decode_step(states, Kn, Vn, KIn, Q, QI, k, score_out=sc)
+    idx, _, out = cache.decode_step(states, Kn, Vn, KIn, Q, QI, k, score_out=sc, sorted=sorted)
     Kh, Vh, KIh = host_tokens(seed, keys, pos)
     o.append(states, [(Kh[i:i + 1], Vh[i:i + 1], KIh[i:i + 1]) for i in range(len(states))])
     q, qi = host_queries(seed, keys, pos)
@@ -186,8 +187,8 @@ def _decode_batch(cache, o, states, keys, seed, k, check_scores=True):
     gout = out.cpu().numpy()
     for i, s in enumerate(states):
         ref_scores = o.scores(s, qi[i])
-        ridx, rval = o.topk(s, qi[i], k)
-        assert topk_accept(gidx[i], gsc[i], ref_scores, k)
+        ridx, rval = o.topk(s, qi[i], k, sorted=sorted)
+        assert topk_accept(gidx[i], gsc[i], ref_scores, k, sorted=sorted)
         if check_scores:
             assert np.array_equal(gidx[i], ridx)
             m = ridx >= 0
@@ -221,7 +222,7 @@ def test_ragged_batch_over_64_requests():
         for b in o.table(s)[:2]:
             check_block(cache, o, b, b)
     for step in range(4):
-        _decode_batch(cache, o, states, keys, seed, 96)
+        _decode_batch(cache, o, states, keys, seed, 96, sorted=step == 3)
 
 
 def test_prefix_share_fork_and_free():
@@ -300,6 +301,7 @@ def test_edge_cases_short_states_and_k_bounds():
     o.append(st, [(Kh[a:b], Vh[a:b], KIh[a:b]) for a, b in zip(cu[:-1], cu[1:])])
     for k in (1, 31, 32, 33, 4096):
         _decode_batch(cache, o, st, np.arange(5), seed, k)
+    _decode_batch(cache, o, st, np.arange(5), seed, 4096, sorted=True)
     # attention without CSA (k = 0) and with user top-k rows holding -1 / out of range
     pos = np.array([o.info(s)["len"] for s in st]) - 1
     Q, _ = dev_queries(seed, np.arange(5), pos)
@@ -348,3 +350,9 @@ def test_errors_change_nothing_on_device():
         cache.decode_attend([b], *dev_queries(seed, 0, [0])[:1], None, 0)   # empty state
     with pytest.raises(hsa.HsaError):
         cache.indexer_topk([a], dev_queries(seed, 0, [0])[1], 0)            # k < 1
+    _, qi = dev_queries(seed, 0, [0])
+    idx, _ = cache.indexer_topk([a], qi, 40)                                   # standalone call
+    _, hqi = host_queries(seed, 0, [0])
+    o.state_alloc()
+    o.append([0], [host_tokens(seed, 0, np.arange(200))])
+    assert np.array_equal(idx.cpu().numpy()[0], o.topk(0, hqi[0], 40)[0])

@@ -251,9 +251,11 @@ def test_indexer_one_hot_query_picks_coordinate():
 def test_topk_full_sort_when_k_covers_all():
     rng = np.random.default_rng(1)
     s = np.round(rng.standard_normal(100) * 4) / 4      # many ties
-    idx, val = select_topk(s, 128)
+    idx, val = select_topk(s, 128, sorted=True)
     ref = sorted(range(100), key=lambda j: (-s[j], j))
     assert list(idx[:100]) == ref and np.all(idx[100:] == -1)
+    idx, val = select_topk(s, 128)
+    assert list(idx[:100]) == list(range(100)) and np.array_equal(val[:100], s)
     assert np.all(np.isneginf(val[100:]))
 
 
@@ -263,12 +265,15 @@ def test_topk_brute_force_small():
         n = int(rng.integers(1, 40))
         k = int(rng.integers(1, 50))
         s = rng.integers(-3, 4, n).astype(np.float64)
-        idx, _ = select_topk(s, k)
         kk = min(k, n)
-        chosen = idx[:kk]
         # brute force: j is chosen iff fewer than kk entries beat it under (score desc, ordinal asc)
         beats = lambda a, b: s[a] > s[b] or (s[a] == s[b] and a < b)
         exp = [j for j in range(n) if sum(beats(i, j) for i in range(n)) < kk]
+        idx, val = select_topk(s, k)
+        assert idx[:kk].tolist() == exp and np.all(idx[kk:] == -1)
+        assert np.array_equal(val[:kk], s[exp])
+        idx, _ = select_topk(s, k, sorted=True)
+        chosen = idx[:kk]
         assert sorted(chosen.tolist()) == exp
         for a, b in zip(chosen[:-1], chosen[1:]):
             assert beats(a, b)
@@ -277,8 +282,10 @@ def test_topk_brute_force_small():
 
 def test_topk_ties_lowest_index_and_negzero():
     s = np.array([1.0, 0.0, -0.0, 1.0, 0.0, 2.0])
-    idx, _ = select_topk(s, 4)
+    idx, _ = select_topk(s, 4, sorted=True)
     assert list(idx) == [5, 0, 3, 1]
+    idx, _ = select_topk(s, 4)
+    assert list(idx) == [0, 1, 3, 5]
 
 
 # ------------------------------------------------------------------ attention
@@ -335,7 +342,7 @@ def test_attention_brute_force_concatenated_cache(n_win, L, k):
         Kc.append(hk[None]); Vc.append(hv[None])
     # the selection, checked by brute force on the raw indexer keys
     allS = np.concatenate([c4_scores(KI[128 * b:128 * b + 128], qi) for b in range(nb)])
-    assert list(sel[:min(k, 32 * nb)]) == sorted(range(32 * nb), key=lambda j: (-allS[j], j))[:min(k, 32 * nb)]
+    assert list(sel[:min(k, 32 * nb)]) == sorted(sorted(range(32 * nb), key=lambda j: (-allS[j], j))[:min(k, 32 * nb)])
     for j in sel:
         if j >= 0:
             ck, cv = gated_pool(K[4 * j:4 * j + 4], V[4 * j:4 * j + 4], o.W_csa)
