@@ -36,9 +36,11 @@ ROW = 8192                     # K + V bytes of one token or entry (2 x 16 x 128
 IDX_BLOCK = 131072             # indexer keys of one block (128 x 4 x 64 fp32)
 SEAL_BYTES = 1581056           # per seal: read 128 tokens K/V + 128 indexer keys, write 32 C4 + 1 HCA + 128 keys
 KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
-                 "attend": "k_attend", "seal": "k_bulk_seal", "write": "k_bulk_write"}
+                 "attend": "k_attend", "merge": "k_merge", "seal": "k_seal_merge",
+                 "write": "k_bulk_write"}
 KERNEL_SOURCES = {"attend": ["attend.hip", "device.h"], "score": ["indexer_topk.hip", "device.h"],
-                  "select": ["indexer_topk.hip", "device.h"], "append": ["append_seal.hip", "device.h"]}
+                  "select": ["indexer_topk.hip", "device.h"], "append": ["append_seal.hip", "device.h"],
+                  "merge": ["attend.hip", "device.h"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -59,8 +61,10 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
         "score": int((nb * IDX_BLOCK).sum() + B * 1024),
         # top-k ordinals and scores out
         "select": int((kk * 8).sum()),
-        # K and V rows of every attended key, the query, the top-k ordinals, fp32 output
-        "attend": int(((swa + nb + kk) * ROW).sum() + B * 4096 + (kk * 4).sum() + B * 8192),
+        # K and V rows of every attended key, the query, the top-k ordinals
+        "attend": int(((swa + nb + kk) * ROW).sum() + B * 4096 + (kk * 4).sum()),
+        # fp32 output
+        "merge": int(B * 8192),
     }
     out["step"] = sum(out.values())
     return out
@@ -163,7 +167,7 @@ def run_decode(args) -> dict:
         step(t)
     torch.cuda.synchronize()
     warm = cache.timing_read()
-    dominant = max(("append", "score", "select", "attend"), key=lambda n: warm[n][0])
+    dominant = max(("append", "score", "select", "attend", "merge"), key=lambda n: warm[n][0])
     if args.kernel:
         dominant = args.kernel
 
@@ -184,7 +188,7 @@ def run_decode(args) -> dict:
     cache.timing_enable([])
 
     # algorithmic bytes of the timed steps (host knows every length)
-    bytes_k = {n: 0 for n in ("append", "score", "select", "attend", "step")}
+    bytes_k = {n: 0 for n in ("append", "score", "select", "attend", "merge", "step")}
     for t in range(W, W + K):
         L_after = L0 + t + 1
         nb = L_after // 128
@@ -235,7 +239,7 @@ def run_decode(args) -> dict:
                      "avg_launch_us": (dom_ms / dom_n * 1e3) if dom_n else None,
                      "algorithmic_bytes_per_launch": (bytes_k[dominant] / dom_n) if dom_n else None},
         "kernels_us_per_step": {n: warm[n][0] / max(1, W - half) * 1e3 for n in
-                                ("append", "score", "select", "attend")},
+                                ("append", "seal", "score", "select", "attend", "merge")},
     }
     cache.close()
     return res

@@ -22,7 +22,7 @@ H, D, HI, DI = 16, 128, 4, 64
 MAX_TOPK = 4096
 APPEND_DEFER_SEAL = 1
 
-KERNELS = ("append", "seal", "write", "score", "select", "attend")
+KERNELS = ("append", "seal", "write", "score", "select", "attend", "merge")
 TOPK_SORTED = 1
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 
@@ -82,10 +82,15 @@ SIGNATURES = {
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libhsa.so (raises if it has not been built)."""
+    """Load libhsa.so (raises if it has not been built).
+
+    torch is imported first so that the library binds to the HIP runtime torch
+    already loaded (one runtime per process: the library shares torch's device
+    memory and streams)."""
     global _lib
     if _lib is not None:
         return _lib
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m heterogeneous_sparse_attention_amd.build` "

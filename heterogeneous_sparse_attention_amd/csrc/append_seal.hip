@@ -193,13 +193,13 @@ __device__ __forceinline__ void store_hca(const Pools& P, int32_t id, float l, c
 // Workgroups [0, n): write request i's token into ring slot p mod n_win and
 // indexer-tail slot p mod 128 (p = len - 1), and record a new block id in the
 // device block table. Workgroups [n, n + 8 * n_seal): seal one eighth of a
-// sealing request's block; the last eighth to finish (ticket) merges the eight
-// HCA partials. No slot written by the first group is read by the second: the
-// new token's ring slot differs from the 127 older ones (n_win >= 128), and its
-// tail slot is 127, which the seal reads from the input instead.
+// sealing request's block (4 C4 entries, 16 indexer keys, one HCA partial).
+// No slot written by the first group is read by the second: the new token's
+// ring slot differs from the 127 older ones (n_win >= 128), and its tail slot is
+// 127, which the seal reads from the input instead.
 __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, const uint16_t* kin,
                                                        const uint16_t* vin, const float* iin,
-                                                       float* part, int32_t* tickets) {
+                                                       float* part) {
   const int tid = threadIdx.x;
   const int bid = blockIdx.x;
   if (bid < B.n) {
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, cons
   float m, l, acck[8], accv[8];
   seal_part(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
 
-  // HCA partial of this eighth -> scratch; the last eighth merges all eight.
+  // HCA partial of this eighth -> scratch; k_seal_merge folds the eight together
   float* mine = part + (int64_t)(item * kSealSplit + sub) * kPartFloats;
   const int h = tid >> 4;
   if ((tid & 15) == 0) {
@@ -249,13 +249,16 @@ __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, cons
   pk[1] = make_float4(acck[4], acck[5], acck[6], acck[7]);
   pv[0] = make_float4(accv[0], accv[1], accv[2], accv[3]);
   pv[1] = make_float4(accv[4], accv[5], accv[6], accv[7]);
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (tid == 0) last = (atomicAdd(&tickets[item], 1) == kSealSplit - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+}
+
+// One workgroup per block sealed by k_decode_append (next launch, so the partials
+// are visible without a device-scope fence): fold its eight partials in order, the
+// same arithmetic as the bulk seal, and store the HCA entry.
+__global__ __launch_bounds__(256) void k_seal_merge(Pools P, ReqBatch B, const float* part) {
+  const int item = blockIdx.x;
+  const Req r = B.r[B.seal_req[item]];
+  const int tid = threadIdx.x;
+  const int h = tid >> 4;
   const float* base = part + (int64_t)item * kSealSplit * kPartFloats;
   float M = -INFINITY, L = 0.f, K8[8] = {}, V8[8] = {};
   for (int s = 0; s < kSealSplit; ++s) {
@@ -269,7 +272,6 @@ __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, cons
     merge_part(M, L, K8, V8, q[h], q[kH + h], pk, pv);
   }
   store_hca(P, r.aux, L, K8, V8);
-  if (tid == 0) atomicExch(&tickets[item], 0);   // ready for the next launch
 }
 
 // Bulk seal: one workgroup per block, its eight 16-token partials merged in
@@ -326,12 +328,17 @@ __global__ __launch_bounds__(256) void k_bulk_write(Pools P, const WriteDesc* w,
 }  // namespace
 
 hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* kin, const void* vin,
-                                const float* iin, float* part, int32_t* tickets, hipStream_t st) {
+                                const float* iin, float* part, hipStream_t st) {
   const int grid = B.n + kSealSplit * B.n_seal;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(k_decode_append, dim3(grid), dim3(256), 0, st, P, B,
-                     static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin, part,
-                     tickets);
+                     static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_seal_merge(const Pools& P, const ReqBatch& B, const float* part, hipStream_t st) {
+  if (B.n_seal == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_seal_merge, dim3(B.n_seal), dim3(256), 0, st, P, B, part);
   return hipGetLastError();
 }
 

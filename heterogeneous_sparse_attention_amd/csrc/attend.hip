@@ -92,26 +92,36 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
+constexpr float kNoMax = -1e30f;   // running-max start: finite, so exp2 never sees inf - inf
+
+// Keys of one pipeline stage: four 16-byte pieces of the K row and of the V row
+// per lane, and whether each key counts (skipped slots read a valid dummy row).
 struct Stage {
   uint4 k[kStage][4];
   uint4 v[kStage][4];
   bool ok[kStage];
 };
 
-__device__ __forceinline__ void load_stage(Stage& S, const Pools& P, const Req& R, int x, int x1,
-                                           const int32_t* sel, int lane) {
+__device__ __forceinline__ const uint16_t* lane_ptr(uint64_t p, int i) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)p, i);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(p >> 32), i);
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// Issue the loads of keys i .. i+kStage-1 of the current 64-key group (their
+// addresses sit in lanes i.. of kp / vp); no branch around the loads.
+__device__ __forceinline__ void load_stage(Stage& S, uint64_t kp, uint64_t vp, uint64_t okmask,
+                                           int i, int lane) {
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
-    KeyAddr a;
-    a.k = a.v = nullptr;
-    if (x + u < x1) a = key_addr(P, R, x + u, sel);
-    S.ok[u] = a.k != nullptr;
-    if (S.ok[u]) {
+    const int j = (i + u) & 63;
+    const uint16_t* pk = lane_ptr(kp, j);
+    const uint16_t* pv = lane_ptr(vp, j);
+    S.ok[u] = (i + u < 64) && ((okmask >> j) & 1ull);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        S.k[u][c] = reinterpret_cast<const uint4*>(a.k + c * 512)[lane];
-        S.v[u][c] = reinterpret_cast<const uint4*>(a.v + c * 512)[lane];
-      }
+    for (int c = 0; c < 4; ++c) {
+      S.k[u][c] = reinterpret_cast<const uint4*>(pk + c * 512)[lane];
+      S.v[u][c] = reinterpret_cast<const uint4*>(pv + c * 512)[lane];
     }
   }
 }
@@ -125,18 +135,13 @@ __device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, f
     float mx = m[c];
 #pragma unroll
     for (int u = 0; u < kStage; ++u) {
-      if (S.ok[u]) {
-        float a = dot2(qw[c].x, S.k[u][c].x, 0.f);
-        a = dot2(qw[c].y, S.k[u][c].y, a);
-        a = dot2(qw[c].z, S.k[u][c].z, a);
-        a = dot2(qw[c].w, S.k[u][c].w, a);
-        s[u] = row_sum16(a) * qs;
-      } else {
-        s[u] = -INFINITY;
-      }
+      float a = dot2(qw[c].x, S.k[u][c].x, 0.f);
+      a = dot2(qw[c].y, S.k[u][c].y, a);
+      a = dot2(qw[c].z, S.k[u][c].z, a);
+      a = dot2(qw[c].w, S.k[u][c].w, a);
+      s[u] = S.ok[u] ? row_sum16(a) * qs : -INFINITY;
       mx = fmaxf(mx, s[u]);
     }
-    if (mx == -INFINITY) continue;   // no valid key for this head yet
     const float sc = exp2f(m[c] - mx);
     float p[kStage];
     float ps = 0.f;
@@ -150,12 +155,10 @@ __device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, f
     for (int i = 0; i < 8; ++i) acc[c][i] *= sc;
 #pragma unroll
     for (int u = 0; u < kStage; ++u) {
-      if (S.ok[u]) {
-        float vf[8];
-        unpack8(S.v[u][c], vf);
+      float vf[8];
+      unpack8(S.v[u][c], vf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p[u], vf[i], acc[c][i]);
-      }
+      for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p[u], vf[i], acc[c][i]);
     }
     m[c] = mx;
   }
@@ -163,16 +166,17 @@ __device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, f
 
 // One workgroup per chunk of a request's keys: four waves stream contiguous
 // quarters of the chunk with two stages of loads in flight, merge in LDS and write
-// one unnormalised partial (acc, max, sum per head). The last chunk of a request
-// to finish (ticket) merges all of the request's partials and writes the output.
+// one unnormalised partial (acc, max, sum per head), or the output itself when the
+// request is a single chunk. k_merge combines the partials in the next launch: a
+// kernel boundary costs far less on this GPU than a device-scope fence in every
+// workgroup.
 __global__ __launch_bounds__(kWaves * 64) void k_attend(Pools P, ReqBatch B, int32_t chunk,
                                                        const uint16_t* q, const int32_t* topk,
                                                        int32_t k, float* part_acc, float* part_ml,
-                                                       int32_t* tickets, float* out) {
+                                                       float* out) {
   __shared__ float s_acc[kWaves][kRow];
   __shared__ float s_m[kWaves][kH];
   __shared__ float s_l[kWaves][kH];
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -184,7 +188,6 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend(Pools P, ReqBatch B, int
     if (w < nch || r == B.n - 1) break;
     w -= nch;
   }
-  const int c0 = blockIdx.x - w;   // first chunk of request r
   const Req R = B.r[r];
   const int nk = n_keys(P, R, k);
   const int per_wave = chunk / kWaves;
@@ -202,21 +205,34 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend(Pools P, ReqBatch B, int
   float m[4], l[4], acc[4][8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    m[c] = -INFINITY;
+    m[c] = kNoMax;
     l[c] = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
   }
 
-  Stage A, Bs;
-  if (x0 < x1) load_stage(A, P, R, x0, x1, sel, lane);
-  for (int x = x0; x < x1; x += 2 * kStage) {
-    const bool more_b = x + kStage < x1;
-    if (more_b) load_stage(Bs, P, R, x + kStage, x1, sel, lane);
-    compute_stage(A, qw, qs, m, l, acc);
-    if (!more_b) break;
-    if (x + 2 * kStage < x1) load_stage(A, P, R, x + 2 * kStage, x1, sel, lane);
-    compute_stage(Bs, qw, qs, m, l, acc);
+  // a valid row for skipped slots: the state's first ring slot (L >= 1)
+  const uint16_t* dummy_k = P.swa_k + (int64_t)R.state * P.n_win * kRow;
+  const uint16_t* dummy_v = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  for (int g = x0; g < x1; g += 64) {
+    // lane i resolves the rows of key g + i (coalesced top-k / table gathers)
+    KeyAddr a;
+    a.k = a.v = nullptr;
+    if (g + lane < x1) a = key_addr(P, R, g + lane, sel);
+    const bool okl = a.k != nullptr;
+    const uint64_t okmask = __ballot(okl);
+    const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
+    const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
+    const int n = min(64, x1 - g);
+    Stage A, Bs;
+    load_stage(A, kp, vp, okmask, 0, lane);
+    for (int i = 0; i < n; i += 2 * kStage) {
+      load_stage(Bs, kp, vp, okmask, i + kStage, lane);
+      compute_stage(A, qw, qs, m, l, acc);
+      if (i + kStage >= n) break;
+      load_stage(A, kp, vp, okmask, i + 2 * kStage, lane);
+      compute_stage(Bs, qw, qs, m, l, acc);
+    }
   }
 
   // merge the four waves in LDS
@@ -234,13 +250,13 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend(Pools P, ReqBatch B, int
   __syncthreads();
   const int h = tid >> 4;
   const int d0 = (tid & 15) * 8;
-  float M = -INFINITY;
+  float M = kNoMax;
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v][h]);
   float L = 0.f, A8[8] = {};
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) {
-    const float wgt = (s_m[v][h] == -INFINITY) ? 0.f : exp2f(s_m[v][h] - M);
+    const float wgt = exp2f(s_m[v][h] - M);
     L = fmaf(wgt, s_l[v][h], L);
 #pragma unroll
     for (int i = 0; i < 8; ++i) A8[i] = fmaf(wgt, s_acc[v][h * kD + d0 + i], A8[i]);
@@ -259,44 +275,65 @@ __global__ __launch_bounds__(kWaves * 64) void k_attend(Pools P, ReqBatch B, int
     part_ml[(int64_t)blockIdx.x * 2 * kH + h] = M;
     part_ml[(int64_t)blockIdx.x * 2 * kH + kH + h] = L;
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&tickets[r], 1) == nch - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // last chunk of the request: log-sum-exp merge of its nch partials
-  float GM = -INFINITY, GL = 0.f, G[8] = {};
-#pragma unroll 4
-  for (int c = c0; c < c0 + nch; ++c) {
-    const float mc = part_ml[(int64_t)c * 2 * kH + h];
-    const float lc = part_ml[(int64_t)c * 2 * kH + kH + h];
-    const float4* pc = reinterpret_cast<const float4*>(part_acc + (int64_t)c * kRow + tid * 8);
-    const float4 a0 = pc[0], a1 = pc[1];
-    if (mc == -INFINITY) continue;
-    const float Mn = fmaxf(GM, mc);
-    const float sa = exp2f(GM - Mn), sb = exp2f(mc - Mn);
-    GL = GL * sa + lc * sb;
-    G[0] = fmaf(a0.x, sb, G[0] * sa); G[1] = fmaf(a0.y, sb, G[1] * sa);
-    G[2] = fmaf(a0.z, sb, G[2] * sa); G[3] = fmaf(a0.w, sb, G[3] * sa);
-    G[4] = fmaf(a1.x, sb, G[4] * sa); G[5] = fmaf(a1.y, sb, G[5] * sa);
-    G[6] = fmaf(a1.z, sb, G[6] * sa); G[7] = fmaf(a1.w, sb, G[7] * sa);
-    GM = Mn;
+}
+
+// Merge of a request's chunk partials (log-sum-exp), one workgroup per (request,
+// group of 4 heads); wave w takes head 4g + w, lane l dims 2l and 2l + 1. Lane c
+// holds chunk c's max and sum, so the max, the total and the chunk weights are wave
+// reductions and the partial rows are read with independent loads.
+__global__ __launch_bounds__(256) void k_merge(Pools P, ReqBatch B, int32_t chunk, int32_t k,
+                                               const float* part_acc, const float* part_ml,
+                                               float* out) {
+  const int r = blockIdx.x >> 2;
+  const int hg = blockIdx.x & 3;
+  const int nch = n_chunks(P, B.r[r], k, chunk);
+  if (nch < 2) return;            // written directly by k_attend
+  int c0 = 0;
+  for (int i = 0; i < r; ++i) c0 += n_chunks(P, B.r[i], k, chunk);
+  const int lane = threadIdx.x & 63;
+  const int h = 4 * hg + (threadIdx.x >> 6);
+  const float* ml = part_ml + (int64_t)c0 * 2 * kH;
+  float M = kNoMax;
+  for (int c = lane; c < nch; c += 64) M = fmaxf(M, ml[c * 2 * kH + h]);
+  M = fmaxf(M, __shfl_xor(M, 32));
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = row_max16(M);
+  float L = 0.f;
+  for (int c = lane; c < nch; c += 64) L += exp2f(ml[c * 2 * kH + h] - M) * ml[c * 2 * kH + kH + h];
+  L = wave_sum(L);
+  const float invL = 1.f / L;
+  const float* pa = part_acc + (int64_t)c0 * kRow + h * kD + 2 * lane;
+  float ox = 0.f, oy = 0.f;
+  for (int g = 0; g < nch; g += 64) {
+    const int n = min(64, nch - g);
+    const float w = (g + lane < nch) ? exp2f(ml[(g + lane) * 2 * kH + h] - M) * invL : 0.f;
+#pragma unroll 8
+    for (int c = 0; c < n; ++c) {
+      const float wc = __shfl(w, c);
+      const float2 a = *reinterpret_cast<const float2*>(pa + (int64_t)(g + c) * kRow);
+      ox = fmaf(wc, a.x, ox);
+      oy = fmaf(wc, a.y, oy);
+    }
   }
-  const float inv = 1.f / GL;
-  o4[0] = make_float4(G[0] * inv, G[1] * inv, G[2] * inv, G[3] * inv);
-  o4[1] = make_float4(G[4] * inv, G[5] * inv, G[6] * inv, G[7] * inv);
-  if (tid == 0) atomicExch(&tickets[r], 0);   // ready for the next launch
+  *reinterpret_cast<float2*>(out + (int64_t)r * kRow + h * kD + 2 * lane) = make_float2(ox, oy);
 }
 
 }  // namespace
 
 hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks, int32_t chunk,
                          const void* q, const int32_t* topk, int32_t k, float* part_acc,
-                         float* part_ml, int32_t* tickets, float* out, hipStream_t st) {
+                         float* part_ml, float* out, hipStream_t st) {
   if (total_chunks == 0) return hipSuccess;
   hipLaunchKernelGGL(k_attend, dim3((unsigned)total_chunks), dim3(kWaves * 64), 0, st, P, B, chunk,
-                     static_cast<const uint16_t*>(q), topk, k, part_acc, part_ml, tickets, out);
+                     static_cast<const uint16_t*>(q), topk, k, part_acc, part_ml, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,
+                        const float* part_acc, const float* part_ml, float* out, hipStream_t st) {
+  if (B.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_merge, dim3(4 * B.n), dim3(256), 0, st, P, B, chunk, k, part_acc, part_ml,
+                     out);
   return hipGetLastError();
 }
 

@@ -45,8 +45,7 @@ struct hsa_ctx {
   size_t part_acc_cap = 0;     // in chunks
   float* part_ml = nullptr;    // [chunks][2][16] running max and sum
   size_t part_ml_cap = 0;
-  float* seal_part = nullptr;  // kMaxReq * kSealSplit HCA partials
-  int32_t* tickets = nullptr;  // [2][kMaxReq]: seal merge, attention merge; zero between launches
+  float* seal_part = nullptr;  // kMaxReq * kSealSplit HCA partials of decode-time seals
 
   // bulk-plan staging: pinned host -> device
   void* plan_host = nullptr;
@@ -204,10 +203,16 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
       B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, new_id[b0 + i]};
       if (new_id[b0 + i] >= 0) B.seal_req[B.n_seal++] = (int8_t)i;
     }
-    Timed t(c, HSA_KERNEL_APPEND, st);
-    HIP_TRY(launch_decode_append(c->P, B, static_cast<const uint16_t*>(k) + b0 * kRow,
-                                 static_cast<const uint16_t*>(v) + b0 * kRow, ik + b0 * kIRow,
-                                 c->seal_part, c->tickets, st));
+    {
+      Timed t(c, HSA_KERNEL_APPEND, st);
+      HIP_TRY(launch_decode_append(c->P, B, static_cast<const uint16_t*>(k) + b0 * kRow,
+                                   static_cast<const uint16_t*>(v) + b0 * kRow, ik + b0 * kIRow,
+                                   c->seal_part, st));
+    }
+    if (B.n_seal) {
+      Timed t(c, HSA_KERNEL_SEAL, st);
+      HIP_TRY(launch_seal_merge(c->P, B, c->seal_part, st));
+    }
   }
   return kOk;
 }
@@ -281,9 +286,15 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
     if (s) return s;
     const void* qb = static_cast<const uint16_t*>(q) + (int64_t)b0 * kRow;
     const int32_t* tk = topk ? topk + (int64_t)b0 * k : nullptr;
-    Timed t(c, HSA_KERNEL_ATTEND, st);
-    HIP_TRY(launch_attend(c->P, B, total, chunk, qb, tk, k, c->part_acc, c->part_ml,
-                          c->tickets + kMaxReq, out + (int64_t)b0 * kRow, st));
+    {
+      Timed t(c, HSA_KERNEL_ATTEND, st);
+      HIP_TRY(launch_attend(c->P, B, total, chunk, qb, tk, k, c->part_acc, c->part_ml,
+                            out + (int64_t)b0 * kRow, st));
+    }
+    if (total > n) {   // some request spans two or more chunks
+      Timed t(c, HSA_KERNEL_MERGE, st);
+      HIP_TRY(launch_merge(c->P, B, chunk, k, c->part_acc, c->part_ml, out + (int64_t)b0 * kRow, st));
+    }
   }
   return kOk;
 }
@@ -321,16 +332,15 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   hsa_ctx* c = new hsa_ctx(cfg->n_win, cfg->max_states, cfg->max_blocks, bps);
   c->device = device;
   const size_t S = (size_t)cfg->max_states, NB = (size_t)cfg->max_blocks, W = (size_t)cfg->n_win;
-  void* p[12] = {};
-  const size_t bytes[12] = {
+  void* p[11] = {};
+  const size_t bytes[11] = {
       S * W * kRow * 2, S * W * kRow * 2, S * kBlk * kIRow * 4,            // swa_k, swa_v, idx_tail
       NB * kC4 * kRow * 2, NB * kC4 * kRow * 2, NB * kRow * 2, NB * kRow * 2,  // csa, hca
       NB * kBlk * kIRow * 4,                                              // idx_k
       S * (size_t)bps * 4,                                                // table
       2 * kRow * 4,                                                       // gates
-      (size_t)kMaxReq * kSealSplit * kPartFloats * 4,                     // seal partials
-      (size_t)2 * kMaxReq * 4};                                           // tickets
-  for (int i = 0; i < 12; ++i) {
+      (size_t)kMaxReq * kSealSplit * kPartFloats * 4};                    // seal partials
+  for (int i = 0; i < 11; ++i) {
     st = dev_alloc(c, &p[i], bytes[i]);
     if (st) {
       hsa_destroy(c);
@@ -353,10 +363,8 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   c->P.n_win = cfg->n_win;
   c->P.max_blocks = (int32_t)cfg->max_blocks;
   c->seal_part = static_cast<float*>(p[10]);
-  c->tickets = static_cast<int32_t*>(p[11]);
   hipError_t e = hipMemcpy(gates, cfg->gate_csa, kRow * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(gates + kRow, cfg->gate_hca, kRow * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(c->tickets, 0, 2 * kMaxReq * 4);
   if (e == hipSuccess) e = hipMemset(c->P.table, 0xff, bytes[8]);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();

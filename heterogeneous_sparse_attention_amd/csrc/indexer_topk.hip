@@ -161,18 +161,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, i
         }
         const unsigned long long bal = __ballot(incl >= (uint32_t)rem);
         const int first = (int)__ffsll((long long)bal) - 1;
-        if (tid == first) {
-          uint32_t cum = incl - tot;
-          for (int q = 0; q < 32; ++q) {
-            const int d = kBins - 1 - 32 * tid - q;
-            const uint32_t c = hist[d];
-            if (cum + c >= (uint32_t)rem) {
-              sh[0] = d;
-              sh[1] = (int)cum;
-              break;
-            }
-            cum += c;
-          }
+        const uint32_t base = __shfl(incl - tot, first);
+        // lanes 0..31 take the 32 digits of lane `first`, highest first
+        const int d = kBins - 1 - 32 * first - (tid & 31);
+        const uint32_t c = tid < 32 ? hist[d] : 0u;
+        uint32_t ci = c;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+          const uint32_t y = __shfl_up(ci, o);
+          if ((tid & 31) >= o) ci += y;
+        }
+        const unsigned long long b2 = __ballot(tid < 32 && base + ci >= (uint32_t)rem);
+        const int dl = (int)__ffsll((long long)b2) - 1;
+        if (tid == dl) {
+          sh[0] = d;
+          sh[1] = (int)(base + ci - c);
         }
       }
       __syncthreads();

@@ -9,7 +9,9 @@ namespace hsa {
 
 // append_seal.hip
 hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* kin, const void* vin,
-                                const float* iin, float* part, int32_t* tickets, hipStream_t st);
+                                const float* iin, float* part, hipStream_t st);
+// Fold the eight HCA partials of each block sealed by launch_decode_append.
+hipError_t launch_seal_merge(const Pools& P, const ReqBatch& B, const float* part, hipStream_t st);
 hipError_t launch_bulk_seal(const Pools& P, const SealDesc* seals, int64_t n_seals, const void* kin,
                             const void* vin, const float* iin, hipStream_t st);
 hipError_t launch_bulk_write(const Pools& P, const WriteDesc* w, int32_t n_req, int64_t total,
@@ -26,11 +28,13 @@ hipError_t launch_select(const ReqBatch& B, int32_t k, int32_t sorted, const flo
 
 // attend.hip
 // Keys of request i: min(len, n_win) SWA + nb HCA + min(k, 32 nb) C4 slots, cut in
-// chunks of `chunk` keys (a multiple of 16); one workgroup per chunk. The last chunk
-// of each request merges the request's partials into out[i]; tickets[i] counts
-// finished chunks and is back at zero when the launch ends.
+// chunks of `chunk` keys (a multiple of 16); one workgroup per chunk writes an
+// unnormalised partial, or out[i] directly when request i is one chunk.
 hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks, int32_t chunk,
                          const void* q, const int32_t* topk, int32_t k, float* part_acc,
-                         float* part_ml, int32_t* tickets, float* out, hipStream_t st);
+                         float* part_ml, float* out, hipStream_t st);
+// Merge the chunk partials of every request with two or more chunks into out.
+hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,
+                        const float* part_acc, const float* part_ml, float* out, hipStream_t st);
 
 }  // namespace hsa

@@ -197,12 +197,13 @@ hsa_status hsa_export_state(hsa_ctx* ctx, int32_t state, void* swa_k, void* swa_
  * hsa_timing_read waits for the recorded events, returns total milliseconds
  * and launch counts per kernel id (arrays of HSA_KERNEL_COUNT) and clears. */
 #define HSA_KERNEL_APPEND 0   /* decode append + fused seal            */
-#define HSA_KERNEL_SEAL 1     /* bulk seal                             */
+#define HSA_KERNEL_SEAL 1     /* bulk seal, or decode-seal HCA merge   */
 #define HSA_KERNEL_WRITE 2    /* bulk ring / indexer-tail write        */
 #define HSA_KERNEL_SCORE 3    /* indexer scores                        */
 #define HSA_KERNEL_SELECT 4   /* top-k select                          */
-#define HSA_KERNEL_ATTEND 5   /* split-KV attention + merge            */
-#define HSA_KERNEL_COUNT 6
+#define HSA_KERNEL_ATTEND 5   /* split-KV attention partials           */
+#define HSA_KERNEL_MERGE 6    /* attention partial merge               */
+#define HSA_KERNEL_COUNT 7
 hsa_status hsa_timing_enable(hsa_ctx* ctx, uint32_t mask);
 hsa_status hsa_timing_read(hsa_ctx* ctx, double* ms, int64_t* launches);
 
