@@ -37,17 +37,19 @@ IDX_BLOCK = 131072             # indexer keys of one block (128 x 4 x 64 fp32)
 SEAL_BYTES = 1581056           # per seal: read 128 tokens K/V + 128 indexer keys, write 32 C4 + 1 HCA + 128 keys
 KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
                  "attend": "k_attend", "merge": "k_merge", "seal": "k_seal_merge",
-                 "write": "k_bulk_write"}
-KERNEL_SOURCES = {"attend": ["attend.hip", "device.h"], "score": ["indexer_topk.hip", "device.h"],
-                  "select": ["indexer_topk.hip", "device.h"], "append": ["append_seal.hip", "device.h"],
-                  "merge": ["attend.hip", "device.h"]}
+                 "write": "k_bulk_write", "step1": "k_step1", "step2": "k_step2",
+                 "step3": "k_step3", "step4": "k_step4"}
+STEP_SOURCES = ["step.hip", "attn_dev.h", "score_dev.h", "seal_dev.h", "device.h"]
+KERNEL_SOURCES = {"step1": STEP_SOURCES, "step2": STEP_SOURCES, "step3": STEP_SOURCES,
+                  "step4": STEP_SOURCES}
+STEP_KERNELS = ("step1", "step2", "step3", "step4")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 # ------------------------------------------------------------------ algorithmic bytes
 
 def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray) -> dict:
-    """Bytes the method must move in one decode step, per kernel (scratch excluded).
+    """Bytes the method must move in one decode step, per launch (scratch excluded).
 
     L_after: lengths after the append; nb: sealed blocks after it; sealed: 1 where
     the step sealed a block."""
@@ -55,16 +57,19 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
     kk = np.minimum(k, 32 * nb)
     B = len(L_after)
     out = {
-        # token K, V, indexer key in; ring slot + tail slot out; seals
-        "append": int(B * 2 * (ROW + 1024) + sealed.sum() * SEAL_BYTES),
-        # indexer keys of every sealed block + the indexer query
-        "score": int((nb * IDX_BLOCK).sum() + B * 1024),
-        # top-k ordinals and scores out
-        "select": int((kk * 8).sum()),
-        # K and V rows of every attended key, the query, the top-k ordinals
-        "attend": int(((swa + nb + kk) * ROW).sum() + B * 4096 + (kk * 4).sum()),
-        # fp32 output
-        "merge": int(B * 8192),
+        # S1: token K, V, indexer key in + ring and tail slots out; seals (minus the
+        # HCA entry written in S2); indexer keys of every sealed block + the
+        # indexer query; K/V rows of the SWA tokens and earlier HCA entries + query
+        "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL_BYTES - ROW)
+                     + (nb * IDX_BLOCK).sum() + B * 1024
+                     + ((swa + nb - sealed) * ROW).sum() + B * 4096),
+        # S2: top-k ordinals (and scores) out; HCA entries of new blocks
+        "step2": int((kk * 8).sum() + sealed.sum() * ROW),
+        # S3: K/V rows of the new HCA entries and selected C4 entries, their
+        # ordinals, the query
+        "step3": int(((sealed + kk) * ROW).sum() + (kk * 4).sum() + B * 4096),
+        # S4: fp32 output
+        "step4": int(B * 8192),
     }
     out["step"] = sum(out.values())
     return out
@@ -147,9 +152,9 @@ def run_decode(args) -> dict:
     wl = workloads.make(args.workload)
     B, k = wl.batch, wl.topk
     W, K = args.warmup, args.steps
-    cache, states = setup_decode(wl, W + K)
+    cache, states = setup_decode(wl, W + 2 * K)
     L0 = wl.prefill.astype(np.int64)
-    inp = decode_inputs(wl, L0, W + K)
+    inp = decode_inputs(wl, L0, W + 2 * K)
     topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
     out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
 
@@ -162,20 +167,17 @@ def run_decode(args) -> dict:
     for t in range(half):
         step(t)
     torch.cuda.synchronize()
-    cache.timing_enable(list(KERNEL_SYMBOL))
+    cache.timing_enable(list(STEP_KERNELS))
     for t in range(half, W):
         step(t)
     torch.cuda.synchronize()
     warm = cache.timing_read()
-    dominant = max(("append", "score", "select", "attend", "merge"), key=lambda n: warm[n][0])
-    if args.kernel:
-        dominant = args.kernel
+    cache.timing_enable([])
+    dominant = args.kernel or max(STEP_KERNELS, key=lambda n: warm[n][0])
 
-    # timed region: HIP events (inside the library, on the launch stream) around the
-    # dominant kernel only
-    cache.timing_enable([dominant])
-    torch.cuda.synchronize()
+    # timed pass 1 (value): whole steps between two events, nothing inside
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for t in range(W, W + K):
@@ -184,22 +186,34 @@ def run_decode(args) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = ev0.elapsed_time(ev1)
+
+    # timed pass 2 (roofline): the next K steps with HIP events recorded by the library
+    # on the launch stream around each launch of the dominant kernel
+    cache.timing_enable([dominant])
+    torch.cuda.synchronize()
+    for t in range(W + K, W + 2 * K):
+        step(t)
+    torch.cuda.synchronize()
     kt = cache.timing_read()
     cache.timing_enable([])
 
-    # algorithmic bytes of the timed steps (host knows every length)
-    bytes_k = {n: 0 for n in ("append", "score", "select", "attend", "merge", "step")}
-    for t in range(W, W + K):
-        L_after = L0 + t + 1
-        nb = L_after // 128
-        sealed = (L_after % 128 == 0).astype(np.int64)
-        sb = step_bytes(L_after, nb, wl.n_win, k, sealed)
-        for n in bytes_k:
-            bytes_k[n] += sb[n]
+    def bytes_over(t_from, t_to):
+        acc = {n: 0 for n in STEP_KERNELS + ("step",)}
+        for t in range(t_from, t_to):
+            L_after = L0 + t + 1
+            nb = L_after // 128
+            sealed = (L_after % 128 == 0).astype(np.int64)
+            sb = step_bytes(L_after, nb, wl.n_win, k, sealed)
+            for n in acc:
+                acc[n] += sb[n]
+        return acc
+
+    bytes_1 = bytes_over(W, W + K)
+    bytes_2 = bytes_over(W + K, W + 2 * K)
     ms_per_step = ms_total / K
     dom_ms, dom_n = kt[dominant]
-    achieved = (bytes_k[dominant] / dom_n) / (dom_ms / dom_n * 1e-3) / 1e9 if dom_n else None
-    step_gbs = bytes_k["step"] / (ms_total * 1e-3) / 1e9
+    achieved = (bytes_2[dominant] / dom_n) / (dom_ms / dom_n * 1e-3) / 1e9 if dom_n else None
+    step_gbs = bytes_1["step"] / (ms_total * 1e-3) / 1e9
 
     traffic = None
     try:
@@ -230,16 +244,18 @@ def run_decode(args) -> dict:
                    "L0_mean": float(L0.mean()), "parallelism": "single GPU"},
         "hbm_gbps": step_gbs,
         "hbm_frac_of_peak": step_gbs / PEAK_HBM_GBS,
-        "bytes_per_step": bytes_k["step"] / K,
+        "bytes_per_step": bytes_1["step"] / K,
         "wall_s": wall,
         "roofline": {"bound": "hbm", "kernel": KERNEL_SYMBOL[dominant],
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": (achieved / PEAK_HBM_GBS) if achieved else None,
                      "traffic": traffic,
                      "avg_launch_us": (dom_ms / dom_n * 1e3) if dom_n else None,
-                     "algorithmic_bytes_per_launch": (bytes_k[dominant] / dom_n) if dom_n else None},
-        "kernels_us_per_step": {n: warm[n][0] / max(1, W - half) * 1e3 for n in
-                                ("append", "seal", "score", "select", "attend", "merge")},
+                     "algorithmic_bytes_per_launch": (bytes_2[dominant] / dom_n) if dom_n else None,
+                     "measured": f"HIP events around each {KERNEL_SYMBOL[dominant]} launch of "
+                                 f"{K} further steps"},
+        "kernels_us_per_step": {n: warm[n][0] / max(1, W - half) * 1e3 for n in STEP_KERNELS},
+        "bytes_per_step_by_kernel": {n: bytes_1[n] / K for n in STEP_KERNELS},
     }
     cache.close()
     return res

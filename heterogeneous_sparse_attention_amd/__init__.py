@@ -22,7 +22,8 @@ H, D, HI, DI = 16, 128, 4, 64
 MAX_TOPK = 4096
 APPEND_DEFER_SEAL = 1
 
-KERNELS = ("append", "seal", "write", "score", "select", "attend", "merge")
+KERNELS = ("append", "seal", "write", "score", "select", "attend", "merge",
+           "step1", "step2", "step3", "step4")
 TOPK_SORTED = 1
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 

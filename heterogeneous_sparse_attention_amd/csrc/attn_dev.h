@@ -1,0 +1,287 @@
+// attn_dev.h - streaming core of the heterogeneous decode attention (device code).
+//
+// Pages: [Q&A] "V4 为何要分池？块对齐与尾缓冲怎么配合？" §4 step 4 (attention reads the
+// compressed entries of the Classical pool sparsely / densely plus the exact tail
+// and SWA of the State pool); [Layout] "V4 KV Layout：Classical + State 双池",
+// Classical KV cache (HCA entries attended densely, CSA entries through top-k).
+//
+// Each key is one 4 KiB K row and one 4 KiB V row (16 heads x 128 bf16). The
+// contraction is 16 independent 128-long dot products per key (no operand is
+// shared across heads), about 1 flop per byte, so it is bound by HBM bandwidth and
+// runs on the vector ALUs. A wave takes one key at a time as four coalesced 1 KiB
+// loads per row; lane l holds heads {l/16 + 4c} x dims (l%16)*8..+8 for c = 0..3,
+// and the 16 lanes of a DPP row reduce one head's dot product. Key addresses of 64
+// keys are resolved at once, one per lane, and broadcast with readlane, so the
+// load stream has no dependent address loads and no branches; two stages of two
+// keys are in flight per wave.
+#pragma once
+
+#include "device.h"
+
+namespace hsa {
+
+constexpr int kAttnWaves = 4;
+constexpr int kStage = 2;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNoMax = -1e30f;   // running-max start: finite, so exp2 never sees inf - inf
+constexpr float kQScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
+
+struct KeyAddr {
+  const uint16_t* k;
+  const uint16_t* v;
+};
+
+struct AttnShared {
+  float acc[kAttnWaves][kRow];
+  float m[kAttnWaves][kH];
+  float l[kAttnWaves][kH];
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+struct Stage {
+  uint4 k[kStage][4];
+  uint4 v[kStage][4];
+  bool ok[kStage];
+};
+
+__device__ __forceinline__ const uint16_t* lane_ptr(uint64_t p, int i) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)p, i);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(p >> 32), i);
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// Issue the loads of keys i .. i+kStage-1 of the current 64-key group.
+__device__ __forceinline__ void load_stage(Stage& S, uint64_t kp, uint64_t vp, uint64_t okmask,
+                                           int i, int lane) {
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int j = (i + u) & 63;
+    const uint16_t* pk = lane_ptr(kp, j);
+    const uint16_t* pv = lane_ptr(vp, j);
+    S.ok[u] = (i + u < 64) && ((okmask >> j) & 1ull);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S.k[u][c] = reinterpret_cast<const uint4*>(pk + c * 512)[lane];
+      S.v[u][c] = reinterpret_cast<const uint4*>(pv + c * 512)[lane];
+    }
+  }
+}
+
+// Online softmax update of this lane's 4 heads with the keys of one stage.
+__device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, float* m, float* l,
+                                              float (*acc)[8]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float s[kStage];
+    float mx = m[c];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      float a = dot2(qw[c].x, S.k[u][c].x, 0.f);
+      a = dot2(qw[c].y, S.k[u][c].y, a);
+      a = dot2(qw[c].z, S.k[u][c].z, a);
+      a = dot2(qw[c].w, S.k[u][c].w, a);
+      s[u] = S.ok[u] ? row_sum16(a) * kQScale : -INFINITY;
+      mx = fmaxf(mx, s[u]);
+    }
+    const float sc = exp2f(m[c] - mx);
+    float p[kStage];
+    float ps = 0.f;
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      p[u] = exp2f(s[u] - mx);
+      ps += p[u];
+    }
+    l[c] = l[c] * sc + ps;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[c][i] *= sc;
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      float vf[8];
+      unpack8(S.v[u][c], vf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p[u], vf[i], acc[c][i]);
+    }
+    m[c] = mx;
+  }
+}
+
+// Attention of one workgroup (4 waves) over keys [x0, x1) of one request: wave w
+// streams a contiguous quarter. key_of(x) gives the K and V rows of key x or
+// nullptrs for a skipped slot; dummy_k / dummy_v are valid rows read in place of
+// skipped keys. On return thread t holds head t/16, dims (t%16)*8 .. +8 of the
+// unnormalised result: running max M (log2 units), sum L, accumulator A8.
+template <class KeyFn>
+__device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const uint16_t* qrow,
+                                            const uint16_t* dummy_k, const uint16_t* dummy_v,
+                                            AttnShared& sh, float& M, float& L, float* A8) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int per = (x1 - x0 + kAttnWaves - 1) / kAttnWaves;
+  const int w0 = x0 + wave * per;
+  const int w1 = min(w0 + per, x1);
+
+  uint4 qw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qw[c] = reinterpret_cast<const uint4*>(qrow + c * 512)[lane];
+  float m[4], l[4], acc[4][8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    m[c] = kNoMax;
+    l[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
+  }
+  for (int g = w0; g < w1; g += 64) {
+    KeyAddr a;
+    a.k = a.v = nullptr;
+    if (g + lane < w1) a = key_of(g + lane);
+    const bool okl = a.k != nullptr;
+    const uint64_t okmask = __ballot(okl);
+    const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
+    const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
+    const int n = min(64, w1 - g);
+    Stage A, Bs;
+    load_stage(A, kp, vp, okmask, 0, lane);
+    for (int i = 0; i < n; i += 2 * kStage) {
+      load_stage(Bs, kp, vp, okmask, i + kStage, lane);
+      compute_stage(A, qw, m, l, acc);
+      if (i + kStage >= n) break;
+      load_stage(A, kp, vp, okmask, i + 2 * kStage, lane);
+      compute_stage(Bs, qw, m, l, acc);
+    }
+  }
+  // merge the four waves in LDS
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int h = 4 * c + (lane >> 4);
+    float4* dst = reinterpret_cast<float4*>(&sh.acc[wave][h * kD + (lane & 15) * 8]);
+    dst[0] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+    dst[1] = make_float4(acc[c][4], acc[c][5], acc[c][6], acc[c][7]);
+    if ((lane & 15) == 0) {
+      sh.m[wave][h] = m[c];
+      sh.l[wave][h] = l[c];
+    }
+  }
+  __syncthreads();
+  const int h = tid >> 4;
+  const int d0 = (tid & 15) * 8;
+  M = kNoMax;
+#pragma unroll
+  for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, sh.m[v][h]);
+  L = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) A8[i] = 0.f;
+#pragma unroll
+  for (int v = 0; v < kAttnWaves; ++v) {
+    const float wgt = exp2f(sh.m[v][h] - M);
+    L = fmaf(wgt, sh.l[v][h], L);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A8[i] = fmaf(wgt, sh.acc[v][h * kD + d0 + i], A8[i]);
+  }
+}
+
+// Store one partial: part_acc row [16][128] (thread t: head t/16, dims (t%16)*8),
+// part_ml row [max 16][sum 16].
+__device__ __forceinline__ void store_partial(float* part_acc, float* part_ml, int64_t idx, float M,
+                                              float L, const float* A8) {
+  const int tid = threadIdx.x;
+  float* pa = part_acc + idx * kRow + tid * 8;
+  reinterpret_cast<float4*>(pa)[0] = make_float4(A8[0], A8[1], A8[2], A8[3]);
+  reinterpret_cast<float4*>(pa)[1] = make_float4(A8[4], A8[5], A8[6], A8[7]);
+  if ((tid & 15) == 0) {
+    part_ml[idx * 2 * kH + (tid >> 4)] = M;
+    part_ml[idx * 2 * kH + kH + (tid >> 4)] = L;
+  }
+}
+
+__device__ __forceinline__ void store_output(float* out_row, float L, const float* A8) {
+  const float inv = 1.f / L;
+  float4* o4 = reinterpret_cast<float4*>(out_row + threadIdx.x * 8);
+  o4[0] = make_float4(A8[0] * inv, A8[1] * inv, A8[2] * inv, A8[3] * inv);
+  o4[1] = make_float4(A8[4] * inv, A8[5] * inv, A8[6] * inv, A8[7] * inv);
+}
+
+// Log-sum-exp merge of n partials (index of the j-th given by part_of(j)) for one
+// request into out_row, by one wave per head: lane c holds partial c's max and
+// sum; lane l writes dims 2l, 2l+1 of head h.
+template <class PartFn>
+__device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, const float* part_acc,
+                                               const float* part_ml, float* out_row) {
+  const int lane = threadIdx.x & 63;
+  float M = kNoMax;
+  for (int c = lane; c < n; c += 64) M = fmaxf(M, part_ml[part_of(c) * 2 * kH + h]);
+  M = fmaxf(M, __shfl_xor(M, 32));
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = row_max16(M);
+  float L = 0.f;
+  for (int c = lane; c < n; c += 64) {
+    const int64_t p = part_of(c);
+    L += exp2f(part_ml[p * 2 * kH + h] - M) * part_ml[p * 2 * kH + kH + h];
+  }
+  L = wave_sum(L);
+  const float invL = 1.f / L;
+  float ox = 0.f, oy = 0.f;
+  for (int g = 0; g < n; g += 64) {
+    const int cnt = min(64, n - g);
+    int64_t pidx = 0;
+    float w = 0.f;
+    if (g + lane < n) {
+      pidx = part_of(g + lane);
+      w = exp2f(part_ml[pidx * 2 * kH + h] - M) * invL;
+    }
+#pragma unroll 8
+    for (int c = 0; c < cnt; ++c) {
+      const float wc = __shfl(w, c);
+      const int lo = __shfl((int)(pidx & 0xffffffff), c);
+      const int hi = __shfl((int)(pidx >> 32), c);
+      const int64_t pc = ((int64_t)hi << 32) | (uint32_t)lo;
+      const float2 a = *reinterpret_cast<const float2*>(part_acc + pc * kRow + h * kD + 2 * lane);
+      ox = fmaf(wc, a.x, ox);
+      oy = fmaf(wc, a.y, oy);
+    }
+  }
+  *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(ox, oy);
+}
+
+// For a workgroup-uniform index w over requests laid end to end with cnt(i) items
+// each (i < n <= 64), find its request r and offset in it. Lane i evaluates
+// cnt(i); a wave scan gives the prefix.
+template <class CntFn>
+__device__ __forceinline__ void find_item(int n, int w, CntFn cnt, int& r, int& off, int& first) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane < n ? cnt(lane) : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const unsigned long long bal = __ballot(lane < n && incl > w);
+  r = bal ? (int)__ffsll((long long)bal) - 1 : n - 1;
+  first = __shfl(incl - c, r);
+  off = w - first;
+}
+
+// Prefix (sum over i < r of cnt(i)) and total, lane-parallel as find_item.
+template <class CntFn>
+__device__ __forceinline__ void prefix_of(int n, int r, CntFn cnt, int& first, int& count) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane < n ? cnt(lane) : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  first = __shfl(incl - c, r);
+  count = __shfl(c, r);
+}
+
+}  // namespace hsa

@@ -86,6 +86,31 @@ struct WriteDesc {
   int64_t cum;       // tokens written by earlier requests of the call
 };
 
+// Arguments of the four decode-step launches (one batch of <= kMaxReq requests).
+struct StepArgs {
+  const uint16_t* kin;   // new tokens' K, V [n][16][128] bf16 and indexer keys [n][256]
+  const uint16_t* vin;
+  const float* iin;
+  const uint16_t* q;     // queries [n][16][128] bf16, indexer queries [n][256]
+  const float* qi;
+  float* scores;         // [n][ld] C4 scores (scratch)
+  int64_t ld;
+  float* part_acc;       // attention partials: part A [n_a] then part B [n_b]
+  float* part_ml;
+  float* seal_part;      // HCA partials of the blocks sealed in this step
+  int32_t* topk;         // [n][k]
+  float* score_out;      // [n][k] or null
+  float* out;            // [n][16][128] fp32
+  int32_t k;
+  int32_t sorted;
+  int32_t chunk_a;       // keys per part-A / part-B attention workgroup
+  int32_t chunk_b;
+  int32_t n_score;       // sealed blocks of the batch (one scoring workgroup each)
+  int32_t n_a;           // part-A workgroups
+  int32_t n_b;           // part-B workgroups
+  int32_t pad_;
+};
+
 // ---------------------------------------------------------------- helpers
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -64,6 +64,7 @@ struct hsa_ctx {
   std::vector<Rec> recs;
 
   int32_t attend_wgs = 512;   // attention workgroups per launch to aim for (one round)
+  int32_t step_a_wgs = 256;   // decode step: part-A attention workgroups to aim for
 
   hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {}
 };
@@ -299,6 +300,89 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
   return kOk;
 }
 
+// The decode step (committed one-token append + top-k + attention) in four launches
+// per batch of kMaxReq requests.
+int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const void* v_new,
+                    const float* idx_new, const void* q, const float* q_idx, int32_t k,
+                    uint32_t flags, int32_t* topk_out, float* score_out, float* out,
+                    hipStream_t st) {
+  std::vector<int32_t> new_id(plan.reqs.size(), -1);
+  for (const SealItem& s : plan.seals) new_id[s.req] = s.id;
+  const int32_t n_req = (int32_t)plan.reqs.size();
+  for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
+    const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
+    ReqBatch B{};
+    B.n = n;
+    std::vector<int64_t> na(n), nb(n);
+    int64_t keys_a = 0, keys_b = 0, maxnb = 0, n_score = 0;
+    for (int i = 0; i < n; ++i) {
+      const AppendReq& r = plan.reqs[b0 + i];
+      const int32_t id = new_id[b0 + i];
+      B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, id};
+      if (id >= 0) B.seal_req[B.n_seal++] = (int8_t)i;
+      const int64_t sealed = id >= 0 ? 1 : 0;
+      na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + r.nb_new - sealed;
+      nb[i] = sealed + std::min<int64_t>(k, (int64_t)kC4 * r.nb_new);
+      keys_a += na[i];
+      keys_b += nb[i];
+      maxnb = std::max<int64_t>(maxnb, r.nb_new);
+      n_score += r.nb_new;
+    }
+    StepArgs S{};
+    S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
+    S.vin = static_cast<const uint16_t*>(v_new) + (int64_t)b0 * kRow;
+    S.iin = idx_new + (int64_t)b0 * kIRow;
+    S.q = static_cast<const uint16_t*>(q) + (int64_t)b0 * kRow;
+    S.qi = q_idx + (int64_t)b0 * kIRow;
+    S.ld = std::max<int64_t>(kC4 * maxnb, 1);
+    S.topk = topk_out + (int64_t)b0 * k;
+    S.score_out = score_out ? score_out + (int64_t)b0 * k : nullptr;
+    S.out = out + (int64_t)b0 * kRow;
+    S.k = k;
+    S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
+    S.chunk_a = attend_chunk(keys_a, n, c->step_a_wgs);
+    S.chunk_b = attend_chunk(keys_b, n, c->attend_wgs);
+    S.n_score = (int32_t)n_score;
+    int64_t ta = 0, tb = 0;
+    for (int i = 0; i < n; ++i) {
+      ta += (na[i] + S.chunk_a - 1) / S.chunk_a;
+      tb += (nb[i] + S.chunk_b - 1) / S.chunk_b;
+    }
+    S.n_a = (int32_t)ta;
+    S.n_b = (int32_t)tb;
+    int s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(S.ld * n),
+                 sizeof(float));
+    if (s) return s;
+    s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)(ta + tb),
+             kRow * sizeof(float));
+    if (s) return s;
+    s = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, (size_t)(ta + tb),
+             2 * kH * sizeof(float));
+    if (s) return s;
+    S.scores = c->scores;
+    S.part_acc = c->part_acc;
+    S.part_ml = c->part_ml;
+    S.seal_part = c->seal_part;
+    {
+      Timed t(c, HSA_KERNEL_STEP1, st);
+      HIP_TRY(launch_step1(c->P, B, S, st));
+    }
+    {
+      Timed t(c, HSA_KERNEL_STEP2, st);
+      HIP_TRY(launch_step2(c->P, B, S, st));
+    }
+    {
+      Timed t(c, HSA_KERNEL_STEP3, st);
+      HIP_TRY(launch_step3(c->P, B, S, st));
+    }
+    {
+      Timed t(c, HSA_KERNEL_STEP4, st);
+      HIP_TRY(launch_step4(c->P, B, S, st));
+    }
+  }
+  return kOk;
+}
+
 int check_config(const hsa_config* cfg) {
   if (!cfg) return fail(kInvalid, "config is NULL");
   if (cfg->n_heads != kH || cfg->head_dim != kD)
@@ -514,10 +598,8 @@ hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, con
   if (st) return fail(st, why);
   if ((st = set_device(c))) return st;
   c->ctl.commit(&plan);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = run_decode_append(c, plan, k_new, v_new, idx_new, s))) return st;
-  if ((st = run_topk(c, n_req, states, q_idx, k, flags, topk_out, score_out, s))) return st;
-  return run_attend(c, n_req, states, q, topk_out, k, out, s);
+  return run_decode_step(c, plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out, score_out,
+                         out, static_cast<hipStream_t>(stream));
 }
 
 hsa_status hsa_state_query(hsa_ctx* c, int32_t s, hsa_state_info* out) {

@@ -1,243 +1,37 @@
-// indexer_topk.hip - indexer scores over sealed blocks and top-k selection.
-//
-// Pages: [Ch12] "Ch 12 · 推理框架 — KV 的异构调度" 名词速通 (the indexer holds tiny
-// K-only keys used for top-k selection) and §2.2 (each block keeps its 128
-// tokens' indexer keys); [Layout] "V4 KV Layout：Classical + State 双池", Classical KV
-// cache (CSA entries are read sparsely through top-k).
-//
-// The score is not defined on the pages. Reading used: score of token t = sum over
-// 4 heads x 64 dims of q_idx * k_idx_t; score of C4 entry j = mean of the scores
-// of its tokens 4j..4j+3. Top-k keeps kk = min(k, N_c) entries ordered by score
-// descending, ties to the lowest C4 ordinal, written in ascending ordinal order
-// (or in that selection order on request).
+// indexer_topk.hip - indexer scores over sealed blocks and top-k selection
+// (hsa_indexer_topk). The arithmetic and its readings are in score_dev.h.
+#include "attn_dev.h"
 #include "device.h"
 #include "kernels.h"
+#include "score_dev.h"
 
 namespace hsa {
 
 namespace {
 
-// One workgroup per sealed block (128 KiB of indexer keys): wave w scores C4
-// entries 8w .. 8w+7. Lane l owns dims 4l..4l+3 of every token row, so each
-// token row is one coalesced 1 KiB read per wave; the 4 tokens of an entry are
-// summed per lane before one wave reduction.
+// One workgroup per sealed block of the batch's requests (128 KiB of keys).
 __global__ __launch_bounds__(256, 4) void k_score(Pools P, ReqBatch B, const float* q_idx,
-                                               float* scores, int64_t ld) {
-  int w = blockIdx.x, r = 0;
-  for (; r < B.n - 1; ++r) {
-    if (w < B.r[r].nb) break;
-    w -= B.r[r].nb;
-  }
+                                                  float* scores, int64_t ld) {
+  int r, w, first;
+  find_item(B.n, blockIdx.x, [&](int i) { return B.r[i].nb; }, r, w, first);
   const Req R = B.r[r];
   const int32_t id = P.table[(int64_t)R.state * P.table_stride + w];
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  float* out = scores + (int64_t)r * ld + (int64_t)kC4 * w + 8 * wave;
+  float* out = scores + (int64_t)r * ld + (int64_t)kC4 * w;
   if (id < 0 || id >= P.max_blocks) {          // never taken: tables are written before use
-    if (lane < 8) out[lane] = -INFINITY;
+    if (threadIdx.x < kC4) out[threadIdx.x] = -INFINITY;
     return;
   }
   const float* blk = P.idx_k + (int64_t)id * kBlk * kIRow;
-  const float4 q = reinterpret_cast<const float4*>(q_idx + (int64_t)r * kIRow)[lane];
-  float4 kv[8][4];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      kv[e][u] = reinterpret_cast<const float4*>(blk + ((8 * wave + e) * 4 + u) * kIRow)[lane];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float a = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a = fmaf(q.x, kv[e][u].x, a);
-      a = fmaf(q.y, kv[e][u].y, a);
-      a = fmaf(q.z, kv[e][u].z, a);
-      a = fmaf(q.w, kv[e][u].w, a);
-    }
-    a = wave_sum(a);
-    if (lane == e) out[e] = a * 0.25f;
-  }
+  score_block([&](int t) { return blk + t * kIRow; }, q_idx + (int64_t)r * kIRow, out);
 }
 
-// Order-preserving map of a float score to uint32 (larger score -> larger key);
-// -0 is folded onto +0 so equal scores compare equal.
-__device__ __forceinline__ uint32_t okey(float f) {
-  uint32_t b = __float_as_uint(f);
-  if (b == 0x80000000u) b = 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float okey_inv(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCacheN = 16384;     // scores kept in LDS (64 KiB)
-constexpr int kBins = 2048;        // radix digits of 11, 11 and 10 bits
-
-// Ordered count: for a flag per thread, the number of set flags in lower threads of
-// the workgroup, and the workgroup total. Two barriers; `cnt` is LDS scratch.
-__device__ __forceinline__ int ordered_rank(bool f, int* cnt, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(f);
-  if (lane == 0) cnt[wv] = __popcll(bal);
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int c = cnt[w];
-    before += (w < wv) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + __popcll(bal & ((1ull << lane) - 1ull));
-}
-
-// One workgroup per request. Radix select over the order-preserving keys finds
-// tau, the key of the kk-th entry under (score desc, ordinal asc), and `rem`,
-// how many entries equal to tau make the cut. One ordered pass then takes every
-// entry above tau and the first `rem` entries equal to tau, writing them in
-// ascending ordinal order (ballot + prefix counts). With `sorted`, the taken
-// entries are instead ordered by (score desc, ordinal asc) with a bitonic sort in
-// LDS.
 __global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, int32_t sorted,
                                                         const float* scores, int64_t ld,
                                                         int32_t* idx_out, float* score_out) {
-  __shared__ uint32_t keys[kCacheN];
-  __shared__ uint32_t hist[kBins];
-  __shared__ unsigned long long cand[kMaxTopk];
-  __shared__ int sh[2];
-  __shared__ int cnt[kSelWaves];
+  __shared__ SelShared sh;
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int N = kC4 * B.r[r].nb;
-  const int kk = min(k, N);
-  const float* S = scores + (int64_t)r * ld;
-  int32_t* io = idx_out + (int64_t)r * k;
-  float* so = score_out ? score_out + (int64_t)r * k : nullptr;
-  const bool cached = N <= kCacheN;
-
-  if (kk > 0) {
-    if (cached) {   // N is a multiple of 32: float4 loads
-      for (int i = tid; i < N / 4; i += kSelThreads) {
-        const float4 v = reinterpret_cast<const float4*>(S)[i];
-        keys[4 * i] = okey(v.x);
-        keys[4 * i + 1] = okey(v.y);
-        keys[4 * i + 2] = okey(v.z);
-        keys[4 * i + 3] = okey(v.w);
-      }
-    }
-    auto key = [&](int i) -> uint32_t { return cached ? keys[i] : okey(S[i]); };
-
-    uint32_t prefix = 0u, pmask = 0u;
-    int rem = kk;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-      for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0u;
-      __syncthreads();
-      for (int i = tid; i < N; i += kSelThreads) {
-        const uint32_t u = key(i);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l holds digits 2047-32l down to 2016-32l
-        const uint4* h4 = reinterpret_cast<const uint4*>(hist + kBins - 32 * (tid + 1));
-        uint32_t tot = 0u;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint4 v = h4[q];
-          tot += v.x + v.y + v.z + v.w;
-        }
-        uint32_t incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(incl, o);
-          if (tid >= o) incl += y;
-        }
-        const unsigned long long bal = __ballot(incl >= (uint32_t)rem);
-        const int first = (int)__ffsll((long long)bal) - 1;
-        const uint32_t base = __shfl(incl - tot, first);
-        // lanes 0..31 take the 32 digits of lane `first`, highest first
-        const int d = kBins - 1 - 32 * first - (tid & 31);
-        const uint32_t c = tid < 32 ? hist[d] : 0u;
-        uint32_t ci = c;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          const uint32_t y = __shfl_up(ci, o);
-          if ((tid & 31) >= o) ci += y;
-        }
-        const unsigned long long b2 = __ballot(tid < 32 && base + ci >= (uint32_t)rem);
-        const int dl = (int)__ffsll((long long)b2) - 1;
-        if (tid == dl) {
-          sh[0] = d;
-          sh[1] = (int)(base + ci - c);
-        }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)sh[0] << shift;
-      pmask |= dmask << shift;
-      rem -= sh[1];
-      __syncthreads();
-    }
-    const uint32_t tau = prefix;
-    // ordered pass: take entries above tau and the first `rem` equal to tau
-    int base_eq = 0, base_take = 0;
-    for (int c0 = 0; c0 < N && base_take < kk; c0 += kSelThreads) {
-      const int i = c0 + tid;
-      const uint32_t u = i < N ? key(i) : 0u;
-      const bool eq = i < N && u == tau;
-      int n_eq;
-      const int req = base_eq + ordered_rank(eq, cnt, &n_eq);
-      const bool take = i < N && (u > tau || (eq && req < rem));
-      int n_take;
-      const int pos = base_take + ordered_rank(take, cnt, &n_take);
-      if (take) {
-        if (sorted) {
-          cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
-        } else {
-          io[pos] = i;
-          if (so) so[pos] = okey_inv(u);
-        }
-      }
-      base_eq += n_eq;
-      base_take += n_take;
-    }
-    if (sorted) {
-      int n2 = 1;
-      while (n2 < kk) n2 <<= 1;
-      for (int i = kk + tid; i < n2; i += kSelThreads) cand[i] = ~0ull;
-      __syncthreads();
-      for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          for (int t = tid; t < n2 / 2; t += kSelThreads) {
-            const int i = 2 * t - (t & (stride - 1));
-            const int j = i + stride;
-            const bool asc = (i & size) == 0;
-            const unsigned long long a = cand[i], b = cand[j];
-            if ((a > b) == asc) {
-              cand[i] = b;
-              cand[j] = a;
-            }
-          }
-          __syncthreads();
-        }
-      }
-      for (int i = tid; i < kk; i += kSelThreads) {
-        const unsigned long long c = cand[i];
-        io[i] = (int32_t)(c & 0xffffffffull);
-        if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
-      }
-    }
-  }
-  for (int i = kk + tid; i < k; i += kSelThreads) {
-    io[i] = -1;
-    if (so) so[i] = -INFINITY;
-  }
+  select_run(kC4 * B.r[r].nb, k, sorted, scores + (int64_t)r * ld, idx_out + (int64_t)r * k,
+             score_out ? score_out + (int64_t)r * k : nullptr, sh);
 }
 
 }  // namespace

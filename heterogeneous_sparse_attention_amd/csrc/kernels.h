@@ -37,4 +37,10 @@ hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks
 hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,
                         const float* part_acc, const float* part_ml, float* out, hipStream_t st);
 
+// step.hip: the decode step in four launches (see step.hip for what each does).
+hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st);
+hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st);
+hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st);
+hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st);
+
 }  // namespace hsa

@@ -1,0 +1,264 @@
+// seal_dev.h - compression of a full 128-token block (device code).
+//
+// Pages: [Q&A] "V4 为何要分池？块对齐与尾缓冲怎么配合？" §2.1 (m consecutive tokens'
+// K/V compress into one entry, aligned to the block), §3.1 (a full block is
+// compressed and appended to the Classical pool); [Ch12] "Ch 12 · 推理框架 — KV 的
+// 异构调度" §2.2 (each block yields 32 CSA + 1 HCA + 128 indexer keys).
+//
+// The compressor is not defined on the pages; the stand-in is gated pooling: per
+// head h, g_t = <W[h], K_t[h]>, alpha = softmax over the group's tokens, entry =
+// sum_t alpha_t (K_t[h], V_t[h]), stored as bf16 (round to nearest even). C4 entry
+// j of a block pools tokens 4j..4j+3 with W_csa; the HCA entry pools all 128 with
+// W_hca, as eight 16-token softmax partials folded in order.
+//
+// Thread layout (256 lanes): lane t owns head t/16 and dims (t%16)*8 .. +8 of every
+// token, i.e. 16 contiguous bytes of each 4 KiB K or V row, so a token is one
+// coalesced 4 KiB read per workgroup and the 16 lanes of a head form one DPP row
+// for the gate reduction.
+#pragma once
+
+#include "device.h"
+
+namespace hsa {
+
+// Where token t of the block being sealed lives: in the state (ring slot, indexer
+// tail slot) if its position precedes len_old, else in the packed input.
+struct TokSrc {
+  const uint16_t* ring_k;
+  const uint16_t* ring_v;
+  const float* tail_i;
+  const uint16_t* in_k;
+  const uint16_t* in_v;
+  const float* in_i;
+  int64_t pos0, len_old;
+  int32_t n_win;
+
+  __device__ __forceinline__ bool resident(int t) const { return pos0 + t < len_old; }
+  __device__ __forceinline__ const uint16_t* k(int t) const {
+    const int64_t p = pos0 + t;
+    return p < len_old ? ring_k + (p % n_win) * kRow : in_k + (p - len_old) * kRow;
+  }
+  __device__ __forceinline__ const uint16_t* v(int t) const {
+    const int64_t p = pos0 + t;
+    return p < len_old ? ring_v + (p % n_win) * kRow : in_v + (p - len_old) * kRow;
+  }
+  __device__ __forceinline__ const float* i(int t) const {
+    const int64_t p = pos0 + t;
+    return p < len_old ? tail_i + (p % kBlk) * kIRow : in_i + (p - len_old) * kIRow;
+  }
+};
+
+constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
+
+// Seal tokens [t0, t0 + 16) of one block: writes their 4 C4 entries and 16
+// indexer keys, and returns the HCA softmax partial (m, l, acc) of these tokens
+// for this lane's 8 dims. Both seal paths build the HCA entry from the same eight
+// partials merged in the same order, so bulk and one-token appends give
+// bit-identical blocks.
+__device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int32_t id, int t0,
+                                          float& m, float& l, float* acck, float* accv) {
+  const int tid = threadIdx.x;
+  const int h = tid >> 4;
+  const int d0 = (tid & 15) * 8;
+  const int off = h * kD + d0;     // == tid * 8
+  float wc[8], wh[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    wc[i] = P.gate_csa[off + i];
+    wh[i] = P.gate_hca[off + i];
+  }
+  uint16_t* csa_k = P.csa_k + (int64_t)id * kC4 * kRow;
+  uint16_t* csa_v = P.csa_v + (int64_t)id * kC4 * kRow;
+  float* idx_dst = P.idx_k + (int64_t)id * kBlk * kIRow;
+
+  m = -INFINITY;
+  l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acck[i] = accv[i] = 0.f;
+
+  for (int g = 0; g < kSubTok / 4; ++g) {
+    const int tb = t0 + 4 * g;
+    uint4 kw[4], vw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kw[u] = *reinterpret_cast<const uint4*>(src.k(tb + u) + off);
+      vw[u] = *reinterpret_cast<const uint4*>(src.v(tb + u) + off);
+    }
+    // indexer keys of the 4 tokens: 4 x 64 float4, one per lane
+    {
+      const int u = tid >> 6, c = tid & 63;
+      const float4 iv = reinterpret_cast<const float4*>(src.i(tb + u))[c];
+      reinterpret_cast<float4*>(idx_dst + (int64_t)(tb + u) * kIRow)[c] = iv;
+    }
+    float kf[4][8], vf[4][8], gc[4], gh[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      unpack8(kw[u], kf[u]);
+      unpack8(vw[u], vf[u]);
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        a = fmaf(wc[i], kf[u][i], a);
+        b = fmaf(wh[i], kf[u][i], b);
+      }
+      gc[u] = row_sum16(a);
+      gh[u] = row_sum16(b);
+    }
+    // C4 entry (tokens tb .. tb+3): softmax of the 4 CSA gates
+    {
+      const float mx = fmaxf(fmaxf(gc[0], gc[1]), fmaxf(gc[2], gc[3]));
+      float e[4], s = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        e[u] = __expf(gc[u] - mx);
+        s += e[u];
+      }
+      const float inv = 1.f / s;
+      float ck[8], cv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a = fmaf(e[u], kf[u][i], a);
+          b = fmaf(e[u], vf[u][i], b);
+        }
+        ck[i] = a * inv;
+        cv[i] = b * inv;
+      }
+      const int slot = tb >> 2;
+      uint4 ok, ov;
+      ok.x = pack_bf2(ck[0], ck[1]); ok.y = pack_bf2(ck[2], ck[3]);
+      ok.z = pack_bf2(ck[4], ck[5]); ok.w = pack_bf2(ck[6], ck[7]);
+      ov.x = pack_bf2(cv[0], cv[1]); ov.y = pack_bf2(cv[2], cv[3]);
+      ov.z = pack_bf2(cv[4], cv[5]); ov.w = pack_bf2(cv[6], cv[7]);
+      *reinterpret_cast<uint4*>(csa_k + (int64_t)slot * kRow + off) = ok;
+      *reinterpret_cast<uint4*>(csa_v + (int64_t)slot * kRow + off) = ov;
+    }
+    // HCA running softmax over the block's tokens
+    {
+      const float mx = fmaxf(m, fmaxf(fmaxf(gh[0], gh[1]), fmaxf(gh[2], gh[3])));
+      const float sc = __expf(m - mx);   // m = -inf on the first group -> 0
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = __expf(gh[u] - mx);
+      l = l * sc + ((e[0] + e[1]) + (e[2] + e[3]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = acck[i] * sc, b = accv[i] * sc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a = fmaf(e[u], kf[u][i], a);
+          b = fmaf(e[u], vf[u][i], b);
+        }
+        acck[i] = a;
+        accv[i] = b;
+      }
+      m = mx;
+    }
+  }
+}
+
+// Fold partial (m, l, acc) into the running HCA state (M, L, K, V).
+__device__ __forceinline__ void merge_part(float& M, float& L, float* K, float* V, float m, float l,
+                                          const float* acck, const float* accv) {
+  const float Mn = fmaxf(M, m);
+  const float a = __expf(M - Mn);   // 0 when M = -inf (first partial)
+  const float b = __expf(m - Mn);
+  L = L * a + l * b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    K[i] = fmaf(acck[i], b, K[i] * a);
+    V[i] = fmaf(accv[i], b, V[i] * a);
+  }
+  M = Mn;
+}
+
+__device__ __forceinline__ void store_hca(const Pools& P, int32_t id, float l, const float* acck,
+                                          const float* accv) {
+  const int off = threadIdx.x * 8;
+  const float inv = 1.f / l;
+  uint4 ok, ov;
+  ok.x = pack_bf2(acck[0] * inv, acck[1] * inv); ok.y = pack_bf2(acck[2] * inv, acck[3] * inv);
+  ok.z = pack_bf2(acck[4] * inv, acck[5] * inv); ok.w = pack_bf2(acck[6] * inv, acck[7] * inv);
+  ov.x = pack_bf2(accv[0] * inv, accv[1] * inv); ov.y = pack_bf2(accv[2] * inv, accv[3] * inv);
+  ov.z = pack_bf2(accv[4] * inv, accv[5] * inv); ov.w = pack_bf2(accv[6] * inv, accv[7] * inv);
+  *reinterpret_cast<uint4*>(P.hca_k + (int64_t)id * kRow + off) = ok;
+  *reinterpret_cast<uint4*>(P.hca_v + (int64_t)id * kRow + off) = ov;
+}
+
+// Decode-time append of request i's one new token (position p = r.len - 1): ring
+// slot p mod n_win, indexer-tail slot p mod 128, and the device table entry of a
+// block the token seals (r.aux = its id, else -1). 256 threads.
+__device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i,
+                                             const uint16_t* kin, const uint16_t* vin,
+                                             const float* iin) {
+  const int tid = threadIdx.x;
+  const int64_t p = r.len - 1;
+  const int64_t ring = ((int64_t)r.state * P.n_win + (p % P.n_win)) * kRow;
+  reinterpret_cast<uint4*>(P.swa_k + ring)[tid] = reinterpret_cast<const uint4*>(kin + (int64_t)i * kRow)[tid];
+  reinterpret_cast<uint4*>(P.swa_v + ring)[tid] = reinterpret_cast<const uint4*>(vin + (int64_t)i * kRow)[tid];
+  if (tid < kIRow / 4) {
+    const int64_t ti = ((int64_t)r.state * kBlk + (p % kBlk)) * kIRow;
+    reinterpret_cast<float4*>(P.idx_tail + ti)[tid] =
+        reinterpret_cast<const float4*>(iin + (int64_t)i * kIRow)[tid];
+  }
+  if (tid == 0 && r.aux >= 0) P.table[(int64_t)r.state * P.table_stride + (r.nb - 1)] = r.aux;
+}
+
+// One eighth (16 tokens) of the decode-time seal of request i's block r.aux: its
+// 4 C4 entries, 16 indexer keys and one HCA partial to part[item * 8 + sub]. The
+// newest token (position r.len - 1) is read from input row i, so this may run in
+// the same launch as append_token. 256 threads.
+__device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i, int item, int sub,
+                                            const uint16_t* kin, const uint16_t* vin,
+                                            const float* iin, float* part) {
+  const int tid = threadIdx.x;
+  TokSrc src;
+  src.ring_k = P.swa_k + (int64_t)r.state * P.n_win * kRow;
+  src.ring_v = P.swa_v + (int64_t)r.state * P.n_win * kRow;
+  src.tail_i = P.idx_tail + (int64_t)r.state * kBlk * kIRow;
+  src.in_k = kin + (int64_t)i * kRow;
+  src.in_v = vin + (int64_t)i * kRow;
+  src.in_i = iin + (int64_t)i * kIRow;
+  src.len_old = r.len - 1;
+  src.pos0 = (int64_t)(r.nb - 1) * kBlk;
+  src.n_win = P.n_win;
+  float m, l, acck[8], accv[8];
+  seal_part(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
+  float* mine = part + (int64_t)(item * kSealSplit + sub) * kPartFloats;
+  const int h = tid >> 4;
+  if ((tid & 15) == 0) {
+    mine[h] = m;
+    mine[kH + h] = l;
+  }
+  float4* pk = reinterpret_cast<float4*>(mine + 2 * kH + tid * 8);
+  float4* pv = reinterpret_cast<float4*>(mine + 2 * kH + kRow + tid * 8);
+  pk[0] = make_float4(acck[0], acck[1], acck[2], acck[3]);
+  pk[1] = make_float4(acck[4], acck[5], acck[6], acck[7]);
+  pv[0] = make_float4(accv[0], accv[1], accv[2], accv[3]);
+  pv[1] = make_float4(accv[4], accv[5], accv[6], accv[7]);
+}
+
+// Fold the eight HCA partials of seal `item` in order (the arithmetic of the bulk
+// seal) and store block id's HCA entry. Threads 0..255 take part.
+__device__ __forceinline__ void seal_merge(const Pools& P, int32_t id, const float* part, int item) {
+  const int tid = threadIdx.x;
+  if (tid >= 256) return;
+  const int h = tid >> 4;
+  const float* base = part + (int64_t)item * kSealSplit * kPartFloats;
+  float M = -INFINITY, L = 0.f, K8[8] = {}, V8[8] = {};
+  for (int s = 0; s < kSealSplit; ++s) {
+    const float* q = base + s * kPartFloats;
+    float pk[8], pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pk[i] = q[2 * kH + tid * 8 + i];
+      pv[i] = q[2 * kH + kRow + tid * 8 + i];
+    }
+    merge_part(M, L, K8, V8, q[h], q[kH + h], pk, pv);
+  }
+  store_hca(P, id, L, K8, V8);
+}
+
+}  // namespace hsa

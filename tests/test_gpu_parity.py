@@ -356,3 +356,50 @@ def test_errors_change_nothing_on_device():
     o.state_alloc()
     o.append([0], [host_tokens(seed, 0, np.arange(200))])
     assert np.array_equal(idx.cpu().numpy()[0], o.topk(0, hqi[0], 40)[0])
+
+
+def test_decode_step_matches_separate_calls():
+    """The four-launch decode step equals append_kv + indexer_topk + decode_attend:
+    same block tables and State, bit-identical blocks and top-k, attention equal to
+    fp32 rounding (only the order of the softmax sum differs)."""
+    import torch
+    import heterogeneous_sparse_attention_amd as hsa
+    seed = 0x4455
+    Wc, Wh = synth.gate_weights(seed)
+    rng = np.random.default_rng(seed)
+    B, k = 9, 40
+    L0 = np.array([1, 126, 127, 128, 255, 300, 511, 700, 1023])    # several seal on step 1 or 2
+    a = hsa.Cache(128, B, 64, Wc, Wh)
+    b = hsa.Cache(128, B, 64, Wc, Wh)
+    sa = [a.state_alloc() for _ in range(B)]
+    sb = [b.state_alloc() for _ in range(B)]
+    cu = np.concatenate([[0], np.cumsum(L0)])
+    pos = np.concatenate([np.arange(n) for n in L0])
+    keys = np.repeat(np.arange(B), L0)
+    K, V, KI = dev_tokens(seed, keys, pos)
+    a.append_kv(sa, cu, K, V, KI)
+    b.append_kv(sb, cu, K, V, KI)
+    for step in range(3):
+        p = L0 + step
+        Kn, Vn, KIn = dev_tokens(seed, np.arange(B), p)
+        Q, QI = dev_queries(seed, np.arange(B), p)
+        ta, _, oa = a.decode_step(sa, Kn, Vn, KIn, Q, QI, k)
+        b.append_kv(sb, np.arange(B + 1), Kn, Vn, KIn)
+        tb, _ = b.indexer_topk(sb, QI, k)
+        ob = b.decode_attend(sb, Q, tb, k)
+        assert torch.equal(ta, tb)
+        assert rel_l2(oa.cpu().numpy(), ob.cpu().numpy()) <= 1e-5
+    for x, y in zip(sa, sb):
+        assert a.block_table(x) == b.block_table(y)
+        for i, j in zip(a.block_table(x), b.block_table(y)):
+            ea, eb = a.export_block(i), b.export_block(j)
+            for f in ea:
+                assert np.array_equal(ea[f], eb[f]), f
+        ea, eb = a.export_state(x), b.export_state(y)
+        info = a.state_query(x)
+        L, nb = info["len"], info["n_blocks"]
+        live_swa = [p % 128 for p in range(max(0, L - 128), L)]
+        live_tail = [p % 128 for p in range(128 * nb, L)]
+        for f in ("swa_k", "swa_v"):
+            assert np.array_equal(ea[f][live_swa], eb[f][live_swa]), f
+        assert np.array_equal(ea["idx_tail"][live_tail], eb["idx_tail"][live_tail])
