@@ -31,11 +31,13 @@ struct KeyAddr {
   const uint16_t* v;
 };
 
-struct AttnShared {
-  float acc[kAttnWaves][kRow];
-  float m[kAttnWaves][kH];
-  float l[kAttnWaves][kH];
+template <int WAVES>
+struct AttnSharedT {
+  float acc[WAVES][kRow];
+  float m[WAVES][kH];
+  float l[WAVES][kH];
 };
+using AttnShared = AttnSharedT<kAttnWaves>;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -111,19 +113,19 @@ __device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, f
   }
 }
 
-// Attention of one workgroup (4 waves) over keys [x0, x1) of one request: wave w
-// streams a contiguous quarter. key_of(x) gives the K and V rows of key x or
+// Attention of one workgroup of WAVES waves over keys [x0, x1) of one request:
+// wave w streams a contiguous share. key_of(x) gives the K and V rows of key x or
 // nullptrs for a skipped slot; dummy_k / dummy_v are valid rows read in place of
-// skipped keys. On return thread t holds head t/16, dims (t%16)*8 .. +8 of the
-// unnormalised result: running max M (log2 units), sum L, accumulator A8.
-template <class KeyFn>
+// skipped keys. On return threads t < 256 hold head t/16, dims (t%16)*8 .. +8 of
+// the unnormalised result: running max M (log2 units), sum L, accumulator A8.
+template <int WAVES = kAttnWaves, class KeyFn>
 __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const uint16_t* qrow,
                                             const uint16_t* dummy_k, const uint16_t* dummy_v,
-                                            AttnShared& sh, float& M, float& L, float* A8) {
+                                            AttnSharedT<WAVES>& sh, float& M, float& L, float* A8) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int per = (x1 - x0 + kAttnWaves - 1) / kAttnWaves;
+  const int per = (x1 - x0 + WAVES - 1) / WAVES;
   const int w0 = x0 + wave * per;
   const int w1 = min(w0 + per, x1);
 
@@ -170,16 +172,16 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
     }
   }
   __syncthreads();
-  const int h = tid >> 4;
+  const int h = (tid >> 4) & (kH - 1);
   const int d0 = (tid & 15) * 8;
   M = kNoMax;
 #pragma unroll
-  for (int v = 0; v < kAttnWaves; ++v) M = fmaxf(M, sh.m[v][h]);
+  for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sh.m[v][h]);
   L = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) A8[i] = 0.f;
 #pragma unroll
-  for (int v = 0; v < kAttnWaves; ++v) {
+  for (int v = 0; v < WAVES; ++v) {
     const float wgt = exp2f(sh.m[v][h] - M);
     L = fmaf(wgt, sh.l[v][h], L);
 #pragma unroll
@@ -208,46 +210,103 @@ __device__ __forceinline__ void store_output(float* out_row, float L, const floa
   o4[1] = make_float4(A8[4] * inv, A8[5] * inv, A8[6] * inv, A8[7] * inv);
 }
 
-// Log-sum-exp merge of n partials (index of the j-th given by part_of(j)) for one
-// request into out_row, by one wave per head: lane c holds partial c's max and
-// sum; lane l writes dims 2l, 2l+1 of head h.
+// Log-sum-exp merge of n partials (index of the j-th given by part_of(j), plain
+// arithmetic) for one request into out_row, by one wave per head h; lane l writes
+// dims 2l, 2l+1. Lane j holds partial j's max and sum; the partial rows are loaded
+// together with them, so up to 32 partials cost one memory round trip.
 template <class PartFn>
 __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, const float* part_acc,
                                                const float* part_ml, float* out_row) {
+  const int lane = threadIdx.x & 63;
+  const float* accb = part_acc + h * kD + 2 * lane;
+  float ox = 0.f, oy = 0.f;
+  if (n <= 64) {
+    float2 a[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      if (c < n) a[c] = *reinterpret_cast<const float2*>(accb + part_of(c) * kRow);
+    float mm = kNoMax, ll = 0.f;
+    if (lane < n) {
+      const int64_t p = part_of(lane);
+      mm = part_ml[p * 2 * kH + h];
+      ll = part_ml[p * 2 * kH + kH + h];
+    }
+    float M = fmaxf(mm, __shfl_xor(mm, 32));
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = row_max16(M);
+    float w = lane < n ? exp2f(mm - M) : 0.f;
+    const float L = wave_sum(w * ll);
+    w *= 1.f / L;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      if (c < n) {
+        const float wc = __shfl(w, c);
+        ox = fmaf(wc, a[c].x, ox);
+        oy = fmaf(wc, a[c].y, oy);
+      }
+    }
+    if (n > 32) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (32 + c < n) a[c] = *reinterpret_cast<const float2*>(accb + part_of(32 + c) * kRow);
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        if (32 + c < n) {
+          const float wc = __shfl(w, 32 + c);
+          ox = fmaf(wc, a[c].x, ox);
+          oy = fmaf(wc, a[c].y, oy);
+        }
+      }
+    }
+  } else {
+    float M = kNoMax;
+    for (int c = lane; c < n; c += 64) M = fmaxf(M, part_ml[part_of(c) * 2 * kH + h]);
+    M = fmaxf(M, __shfl_xor(M, 32));
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = row_max16(M);
+    float L = 0.f;
+    for (int c = lane; c < n; c += 64) {
+      const int64_t p = part_of(c);
+      L += exp2f(part_ml[p * 2 * kH + h] - M) * part_ml[p * 2 * kH + kH + h];
+    }
+    L = wave_sum(L);
+    const float invL = 1.f / L;
+    for (int c = 0; c < n; ++c) {
+      const int64_t p = part_of(c);
+      const float wc = exp2f(part_ml[p * 2 * kH + h] - M) * invL;
+      const float2 v = *reinterpret_cast<const float2*>(accb + p * kRow);
+      ox = fmaf(wc, v.x, ox);
+      oy = fmaf(wc, v.y, oy);
+    }
+  }
+  *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(ox, oy);
+}
+
+// Log-sum-exp merge of n partials of one request into one partial (unnormalised)
+// at index dst, by one wave per head h; lane l holds dims 2l, 2l+1.
+template <class PartFn>
+__device__ __forceinline__ void merge_to_partial(PartFn part_of, int n, int h, float* part_acc,
+                                                 float* part_ml, int64_t dst) {
   const int lane = threadIdx.x & 63;
   float M = kNoMax;
   for (int c = lane; c < n; c += 64) M = fmaxf(M, part_ml[part_of(c) * 2 * kH + h]);
   M = fmaxf(M, __shfl_xor(M, 32));
   M = fmaxf(M, __shfl_xor(M, 16));
   M = row_max16(M);
-  float L = 0.f;
-  for (int c = lane; c < n; c += 64) {
+  float L = 0.f, ox = 0.f, oy = 0.f;
+  for (int c = 0; c < n; ++c) {
     const int64_t p = part_of(c);
-    L += exp2f(part_ml[p * 2 * kH + h] - M) * part_ml[p * 2 * kH + kH + h];
+    const float w = exp2f(part_ml[p * 2 * kH + h] - M);
+    L = fmaf(w, part_ml[p * 2 * kH + kH + h], L);
+    const float2 v = *reinterpret_cast<const float2*>(part_acc + p * kRow + h * kD + 2 * lane);
+    ox = fmaf(w, v.x, ox);
+    oy = fmaf(w, v.y, oy);
   }
-  L = wave_sum(L);
-  const float invL = 1.f / L;
-  float ox = 0.f, oy = 0.f;
-  for (int g = 0; g < n; g += 64) {
-    const int cnt = min(64, n - g);
-    int64_t pidx = 0;
-    float w = 0.f;
-    if (g + lane < n) {
-      pidx = part_of(g + lane);
-      w = exp2f(part_ml[pidx * 2 * kH + h] - M) * invL;
-    }
-#pragma unroll 8
-    for (int c = 0; c < cnt; ++c) {
-      const float wc = __shfl(w, c);
-      const int lo = __shfl((int)(pidx & 0xffffffff), c);
-      const int hi = __shfl((int)(pidx >> 32), c);
-      const int64_t pc = ((int64_t)hi << 32) | (uint32_t)lo;
-      const float2 a = *reinterpret_cast<const float2*>(part_acc + pc * kRow + h * kD + 2 * lane);
-      ox = fmaf(wc, a.x, ox);
-      oy = fmaf(wc, a.y, oy);
-    }
+  *reinterpret_cast<float2*>(part_acc + dst * kRow + h * kD + 2 * lane) = make_float2(ox, oy);
+  if (lane == 0) {
+    part_ml[dst * 2 * kH + h] = M;
+    part_ml[dst * 2 * kH + kH + h] = L;
   }
-  *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(ox, oy);
 }
 
 // For a workgroup-uniform index w over requests laid end to end with cnt(i) items

@@ -99,6 +99,7 @@ struct StepArgs {
   float* part_ml;
   float* seal_part;      // HCA partials of the blocks sealed in this step
   int32_t* topk;         // [n][k]
+  int32_t* rows;         // [n][k] physical C4 rows of the selected entries (scratch)
   float* score_out;      // [n][k] or null
   float* out;            // [n][16][128] fp32
   int32_t k;
@@ -109,7 +110,29 @@ struct StepArgs {
   int32_t n_a;           // part-A workgroups
   int32_t n_b;           // part-B workgroups
   int32_t pad_;
+  int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
+  int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])
+  int32_t first_s[kMaxReq + 1];   // request i's scoring workgroups (= its sealed blocks)
 };
+
+// The request owning item w of a list laid out by prefix `first` (first[0] = 0,
+// nondecreasing, first[n] = total): the largest r with first[r] <= w. Workgroup-
+// uniform binary search on kernel arguments (scalar loads).
+__device__ __forceinline__ int owner_of(const int32_t* first, int n, int w) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= w) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Range [x0, x1) of chunk w of c near-equal chunks over n keys.
+__device__ __forceinline__ void chunk_range(int n, int c, int w, int& x0, int& x1) {
+  x0 = (int)((int64_t)n * w / c);
+  x1 = (int)((int64_t)n * (w + 1) / c);
+}
 
 // ---------------------------------------------------------------- helpers
 

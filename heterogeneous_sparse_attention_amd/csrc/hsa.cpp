@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -64,9 +65,17 @@ struct hsa_ctx {
   std::vector<Rec> recs;
 
   int32_t attend_wgs = 512;   // attention workgroups per launch to aim for (one round)
-  int32_t step_a_wgs = 256;   // decode step: part-A attention workgroups to aim for
+  int32_t step_a_wgs = 256;   // decode step: part-A attention workgroups (8 waves each) to aim for
+  int32_t step_b_wgs = 256;   // decode step: part-B attention workgroups to aim for
+  int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
+  size_t rows_cap = 0;
 
-  hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {}
+  hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {
+    // launch-shape targets; the environment can override them for tuning sweeps
+    if (const char* e = std::getenv("HSA_ATTEND_WGS")) attend_wgs = std::max(16, std::atoi(e));
+    if (const char* e = std::getenv("HSA_STEP_A_WGS")) step_a_wgs = std::max(16, std::atoi(e));
+    if (const char* e = std::getenv("HSA_STEP_B_WGS")) step_b_wgs = std::max(16, std::atoi(e));
+  }
 };
 
 namespace {
@@ -341,24 +350,35 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.k = k;
     S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
     S.chunk_a = attend_chunk(keys_a, n, c->step_a_wgs);
-    S.chunk_b = attend_chunk(keys_b, n, c->attend_wgs);
+    S.chunk_b = attend_chunk(keys_b, n, c->step_b_wgs);
     S.n_score = (int32_t)n_score;
-    int64_t ta = 0, tb = 0;
+    int64_t ta = 0, tb = 0, ts = 0;
     for (int i = 0; i < n; ++i) {
+      S.first_a[i] = (int32_t)ta;
+      S.first_b[i] = (int32_t)tb;
+      S.first_s[i] = (int32_t)ts;
       ta += (na[i] + S.chunk_a - 1) / S.chunk_a;
       tb += (nb[i] + S.chunk_b - 1) / S.chunk_b;
+      ts += B.r[i].nb;
     }
+    S.first_a[n] = (int32_t)ta;
+    S.first_b[n] = (int32_t)tb;
+    S.first_s[n] = (int32_t)ts;
     S.n_a = (int32_t)ta;
     S.n_b = (int32_t)tb;
+
     int s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(S.ld * n),
                  sizeof(float));
     if (s) return s;
-    s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)(ta + tb),
+    s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)(ta + tb + n),
              kRow * sizeof(float));
     if (s) return s;
-    s = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, (size_t)(ta + tb),
+    s = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, (size_t)(ta + tb + n),
              2 * kH * sizeof(float));
     if (s) return s;
+    s = grow(c, reinterpret_cast<void**>(&c->rows), &c->rows_cap, (size_t)n * k, sizeof(int32_t));
+    if (s) return s;
+    S.rows = c->rows;
     S.scores = c->scores;
     S.part_acc = c->part_acc;
     S.part_ml = c->part_ml;

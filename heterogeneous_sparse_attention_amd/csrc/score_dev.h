@@ -59,35 +59,18 @@ __device__ __forceinline__ float okey_inv(uint32_t u) {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCacheN = 16384;     // scores kept in LDS (64 KiB)
+constexpr int kCacheN = 4096;      // scores kept in LDS (16 KiB); larger rows read through L2
 constexpr int kBins = 2048;        // radix digits of 11, 11 and 10 bits
+constexpr int kTabCache = 1024;    // block-table entries kept in LDS for the row output
 
 struct SelShared {
   uint32_t keys[kCacheN];
-  uint32_t hist[kBins];
+  uint32_t hist[3][kBins];
   unsigned long long cand[kMaxTopk];
+  int32_t tab[kTabCache];
   int sh[2];
-  int cnt[kSelWaves];
+  int cnt[2][2][kSelWaves];   // [parity][above tau, equal to tau][wave]
 };
-
-// Ordered count: for a flag per thread, the number of set flags in lower threads of
-// the workgroup, and the workgroup total. Two barriers; `cnt` is LDS scratch.
-__device__ __forceinline__ int ordered_rank(bool f, int* cnt, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(f);
-  if (lane == 0) cnt[wv] = __popcll(bal);
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int c = cnt[w];
-    before += (w < wv) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + __popcll(bal & ((1ull << lane) - 1ull));
-}
 
 // Top-k of one request's N scores S by one workgroup of 1024 threads. Radix select over the order-preserving keys finds
 // tau, the key of the kk-th entry under (score desc, ordinal asc), and `rem`,
@@ -96,15 +79,27 @@ __device__ __forceinline__ int ordered_rank(bool f, int* cnt, int* total) {
 // ascending ordinal order (ballot + prefix counts). With `sorted`, the taken
 // entries are instead ordered by (score desc, ordinal asc) with a bitonic sort in
 // LDS.
+// With `rows`, also writes each taken entry's physical C4 row (table[j / 32] * 32 +
+// j % 32) from the state's block table `tab`. NT = threads of the workgroup.
+template <int NT = kSelThreads>
 __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, const float* S,
-                                           int32_t* io, float* so, SelShared& sh) {
+                                           int32_t* io, float* so, SelShared& sh,
+                                           const int32_t* tab = nullptr, int32_t* rows = nullptr) {
+  static_assert(NT % 64 == 0 && NT <= kSelThreads && NT >= 256, "select workgroup size");
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int kk = min(k, N);
   const bool cached = N <= kCacheN;
+  const int nb = N / kC4;
+  const bool tab_lds = rows && nb <= kTabCache;
+  auto row_of = [&](int j) -> int32_t {
+    const int32_t id = tab_lds ? sh.tab[j / kC4] : tab[j / kC4];
+    return id * kC4 + j % kC4;
+  };
 
   if (kk > 0) {
     if (cached) {   // N is a multiple of 32: float4 loads
-      for (int i = tid; i < N / 4; i += kSelThreads) {
+      for (int i = tid; i < N / 4; i += NT) {
         const float4 v = reinterpret_cast<const float4*>(S)[i];
         sh.keys[4 * i] = okey(v.x);
         sh.keys[4 * i + 1] = okey(v.y);
@@ -114,22 +109,25 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     }
     auto key = [&](int i) -> uint32_t { return cached ? sh.keys[i] : okey(S[i]); };
 
+    for (int b = tid; b < 3 * kBins; b += NT) (&sh.hist[0][0])[b] = 0u;
+    if (tab_lds)
+      for (int b = tid; b < nb; b += NT) sh.tab[b] = tab[b];
+    __syncthreads();
     uint32_t prefix = 0u, pmask = 0u;
     int rem = kk;
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
       const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
       const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-      for (int b = tid; b < kBins; b += kSelThreads) sh.hist[b] = 0u;
-      __syncthreads();
-      for (int i = tid; i < N; i += kSelThreads) {
+      uint32_t* hist = sh.hist[pass];
+      for (int i = tid; i < N; i += NT) {
         const uint32_t u = key(i);
-        if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1u);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
       __syncthreads();
       if (tid < 64) {
         // lane l holds digits 2047-32l down to 2016-32l
-        const uint4* h4 = reinterpret_cast<const uint4*>(sh.hist + kBins - 32 * (tid + 1));
+        const uint4* h4 = reinterpret_cast<const uint4*>(hist + kBins - 32 * (tid + 1));
         uint32_t tot = 0u;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -147,7 +145,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         const uint32_t base = __shfl(incl - tot, first);
         // lanes 0..31 take the 32 digits of lane `first`, highest first
         const int d = kBins - 1 - 32 * first - (tid & 31);
-        const uint32_t c = tid < 32 ? sh.hist[d] : 0u;
+        const uint32_t c = tid < 32 ? hist[d] : 0u;
         uint32_t ci = c;
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) {
@@ -165,39 +163,55 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       prefix |= (uint32_t)sh.sh[0] << shift;
       pmask |= dmask << shift;
       rem -= sh.sh[1];
-      __syncthreads();
     }
     const uint32_t tau = prefix;
-    // ordered pass: take entries above tau and the first `rem` equal to tau
-    int base_eq = 0, base_take = 0;
-    for (int c0 = 0; c0 < N && base_take < kk; c0 += kSelThreads) {
+    // ordered pass: take entries above tau and the first `rem` equal to tau; the
+    // entries taken before i are (above tau before i) + min(equal before i, rem)
+    const int lane = tid & 63, wv = tid >> 6;
+    int base_gt = 0, base_eq = 0, parity = 0;
+    for (int c0 = 0; c0 < N; c0 += NT, parity ^= 1) {
       const int i = c0 + tid;
       const uint32_t u = i < N ? key(i) : 0u;
+      const bool gt = i < N && u > tau;
       const bool eq = i < N && u == tau;
-      int n_eq;
-      const int req = base_eq + ordered_rank(eq, sh.cnt, &n_eq);
-      const bool take = i < N && (u > tau || (eq && req < rem));
-      int n_take;
-      const int pos = base_take + ordered_rank(take, sh.cnt, &n_take);
-      if (take) {
+      const unsigned long long bg = __ballot(gt), be = __ballot(eq);
+      if (lane == 0) {
+        sh.cnt[parity][0][wv] = __popcll(bg);
+        sh.cnt[parity][1][wv] = __popcll(be);
+      }
+      __syncthreads();
+      int gt_before = base_gt, eq_before = base_eq;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cg = sh.cnt[parity][0][w], ce = sh.cnt[parity][1][w];
+        gt_before += (w < wv) ? cg : 0;
+        eq_before += (w < wv) ? ce : 0;
+        base_gt += cg;
+        base_eq += ce;
+      }
+      const unsigned long long below = (1ull << lane) - 1ull;
+      gt_before += __popcll(bg & below);
+      eq_before += __popcll(be & below);
+      if (gt || (eq && eq_before < rem)) {
+        const int pos = gt_before + min(eq_before, rem);
         if (sorted) {
           sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
         } else {
           io[pos] = i;
           if (so) so[pos] = okey_inv(u);
+          if (rows) rows[pos] = row_of(i);
         }
       }
-      base_eq += n_eq;
-      base_take += n_take;
+      if (base_gt + min(base_eq, rem) >= kk) break;   // every entry taken (uniform)
     }
     if (sorted) {
       int n2 = 1;
       while (n2 < kk) n2 <<= 1;
-      for (int i = kk + tid; i < n2; i += kSelThreads) sh.cand[i] = ~0ull;
+      for (int i = kk + tid; i < n2; i += NT) sh.cand[i] = ~0ull;
       __syncthreads();
       for (int size = 2; size <= n2; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          for (int t = tid; t < n2 / 2; t += kSelThreads) {
+          for (int t = tid; t < n2 / 2; t += NT) {
             const int i = 2 * t - (t & (stride - 1));
             const int j = i + stride;
             const bool asc = (i & size) == 0;
@@ -210,14 +224,16 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
           __syncthreads();
         }
       }
-      for (int i = tid; i < kk; i += kSelThreads) {
+      for (int i = tid; i < kk; i += NT) {
         const unsigned long long c = sh.cand[i];
-        io[i] = (int32_t)(c & 0xffffffffull);
+        const int j = (int32_t)(c & 0xffffffffull);
+        io[i] = j;
         if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
+        if (rows) rows[i] = row_of(j);
       }
     }
   }
-  for (int i = kk + tid; i < k; i += kSelThreads) {
+  for (int i = kk + tid; i < k; i += NT) {
     io[i] = -1;
     if (so) so[i] = -INFINITY;
   }

@@ -241,7 +241,7 @@ __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i,
 }
 
 // Fold the eight HCA partials of seal `item` in order (the arithmetic of the bulk
-// seal) and store block id's HCA entry. Threads 0..255 take part.
+// seal) and store block id's HCA entry. Threads 0..255 take part (of 256 or more).
 __device__ __forceinline__ void seal_merge(const Pools& P, int32_t id, const float* part, int item) {
   const int tid = threadIdx.x;
   if (tid >= 256) return;

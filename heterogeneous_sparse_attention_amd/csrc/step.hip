@@ -7,19 +7,20 @@
 // step, for every request of the batch:
 //
 //   S1  append the token (ring + indexer tail), seal a full block (C4 entries,
-//       indexer keys, eight HCA partials), indexer scores of every sealed block,
-//       and attention part A: the SWA tokens and the HCA entries of blocks sealed
-//       before this step. Nothing read in S1 is written in S1: the new token is
-//       read from the input wherever it is needed (SWA key, last indexer key of a
-//       block sealed now, last token of the seal).
-//   S2  top-k selection over the scores; the HCA merge of blocks sealed in S1.
+//       indexer keys, eight HCA partials) and indexer scores of every sealed
+//       block. Nothing read in S1 is written in S1: the new token is read from
+//       the input wherever it is needed (last indexer key of a block sealed now,
+//       last token of the seal).
+//   S2  top-k selection over the scores (with the selected entries' physical C4
+//       rows), one workgroup per request; the HCA merge of blocks sealed in S1;
+//       and attention part A, the SWA tokens and the HCA entries of blocks sealed
+//       before this step, on the CUs the selection leaves idle.
 //   S3  attention part B: the HCA entry of the block sealed now and the selected
 //       C4 entries.
 //   S4  log-sum-exp merge of every request's part A and part B partials.
 //
-// Part A does not depend on the top-k, so it streams alongside the indexer scan in
-// S1 and leaves only the C4 gather after the selection. Key order differs from
-// hsa_decode_attend only in the order of the softmax sum.
+// Part A does not depend on the top-k, so it streams while the selection runs.
+// Key order differs from hsa_decode_attend only in the order of the softmax sum.
 #include "attn_dev.h"
 #include "device.h"
 #include "kernels.h"
@@ -38,10 +39,8 @@ __device__ __forceinline__ int keys_b(const Req& r, int32_t k) {
   const int nc = kC4 * r.nb;
   return sealed_now(r) + (k < nc ? k : nc);
 }
-__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-__global__ __launch_bounds__(kAttnWaves * 64) void k_step1(Pools P, ReqBatch B, StepArgs S) {
-  __shared__ AttnShared sh;
+__global__ __launch_bounds__(256, 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
   int bid = blockIdx.x;
   // -- seal eighths (first, so the longest single workgroups start early)
   if (bid < kSealSplit * B.n_seal) {
@@ -59,8 +58,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_step1(Pools P, ReqBatch B, 
   bid -= B.n;
   // -- indexer scores, one workgroup per sealed block
   if (bid < S.n_score) {
-    int r, lb, first;
-    find_item(B.n, bid, [&](int i) { return B.r[i].nb; }, r, lb, first);
+    const int r = owner_of(S.first_s, B.n, bid);
+    const int lb = bid - S.first_s[r];
     const Req R = B.r[r];
     float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb;
     const float* qrow = S.qi + (int64_t)r * kIRow;
@@ -79,31 +78,53 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_step1(Pools P, ReqBatch B, 
       const float* blk = P.idx_k + (int64_t)id * kBlk * kIRow;
       score_block([&](int t) { return blk + t * kIRow; }, qrow, out);
     }
+  }
+}
+
+constexpr int kStep2Threads = 512;   // 8 waves: 256 VGPRs per wave for the attention role
+constexpr int kStep2Waves = kStep2Threads / 64;
+
+union Step2Shared {
+  SelShared sel;
+  AttnSharedT<kStep2Waves> attn;
+};
+
+__global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
+  __shared__ Step2Shared sh;
+  int bid = blockIdx.x;
+  if (bid < B.n) {
+    const int64_t k = S.k;
+    const Req R = B.r[bid];
+    select_run<kStep2Threads>(kC4 * R.nb, S.k, S.sorted, S.scores + (int64_t)bid * S.ld,
+                              S.topk + bid * k, S.score_out ? S.score_out + bid * k : nullptr, sh.sel,
+                              P.table + (int64_t)R.state * P.table_stride, S.rows + bid * k);
     return;
   }
-  bid -= S.n_score;
+  bid -= B.n;
+  if (bid < B.n_seal) {
+    seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
+    return;
+  }
+  bid -= B.n_seal;
   // -- attention part A: SWA tokens + HCA of blocks sealed before this step
-  int r, w, first;
-  find_item(B.n, bid, [&](int i) { return cdiv(keys_a(P, B.r[i]), S.chunk_a); }, r, w, first);
+  const int r = owner_of(S.first_a, B.n, bid);
+  const int w = bid - S.first_a[r];
+  const int nch = S.first_a[r + 1] - S.first_a[r];
   const Req R = B.r[r];
   const int swa = R.len < P.n_win ? R.len : P.n_win;
-  const int na = keys_a(P, R);
+  int x0, x1;
+  chunk_range(keys_a(P, R), nch, w, x0, x1);
   const uint16_t* ring_k = P.swa_k + (int64_t)R.state * P.n_win * kRow;
   const uint16_t* ring_v = P.swa_v + (int64_t)R.state * P.n_win * kRow;
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
-  const int64_t newest = (int64_t)R.len - 1;
+  const int64_t p0 = (int64_t)R.len - swa;   // oldest SWA position; the ring holds all (S1 wrote the newest)
   auto key_a = [&](int x) {
     KeyAddr a;
     a.k = a.v = nullptr;
     if (x < swa) {
-      const int64_t p = newest + 1 - swa + x;
-      if (p == newest) {
-        a.k = S.kin + (int64_t)r * kRow;
-        a.v = S.vin + (int64_t)r * kRow;
-      } else {
-        a.k = ring_k + (p % P.n_win) * kRow;
-        a.v = ring_v + (p % P.n_win) * kRow;
-      }
+      const int64_t slot = (p0 + x) % P.n_win;
+      a.k = ring_k + slot * kRow;
+      a.v = ring_v + slot * kRow;
       return a;
     }
     const int32_t id = tab[x - swa];
@@ -113,34 +134,28 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_step1(Pools P, ReqBatch B, 
     return a;
   };
   float M, L, A8[8];
-  attend_keys(key_a, w * S.chunk_a, min(na, (w + 1) * S.chunk_a), S.q + (int64_t)r * kRow,
-              S.kin + (int64_t)r * kRow, S.vin + (int64_t)r * kRow, sh, M, L, A8);
-  store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
+  attend_keys<kStep2Waves>(key_a, x0, x1, S.q + (int64_t)r * kRow, ring_k, ring_v, sh.attn, M, L,
+                           A8);
+  if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
-  __shared__ SelShared sh;
+#ifndef HSA_STEP3_WAVES
+#define HSA_STEP3_WAVES 4
+#endif
+constexpr int kStep3Waves = HSA_STEP3_WAVES;
+
+__global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B, StepArgs S) {
+  __shared__ AttnSharedT<kStep3Waves> sh;
   const int bid = blockIdx.x;
-  if (bid < B.n) {
-    const int64_t k = S.k;
-    select_run(kC4 * B.r[bid].nb, S.k, S.sorted, S.scores + (int64_t)bid * S.ld,
-               S.topk + bid * k, S.score_out ? S.score_out + bid * k : nullptr, sh);
-    return;
-  }
-  const int item = bid - B.n;
-  seal_merge(P, B.r[B.seal_req[item]].aux, S.seal_part, item);
-}
-
-__global__ __launch_bounds__(kAttnWaves * 64) void k_step3(Pools P, ReqBatch B, StepArgs S) {
-  __shared__ AttnShared sh;
-  int r, w, first;
-  find_item(B.n, blockIdx.x, [&](int i) { return cdiv(keys_b(B.r[i], S.k), S.chunk_b); }, r, w,
-            first);
+  const int r = owner_of(S.first_b, B.n, bid);
+  const int w = bid - S.first_b[r];
+  const int nch = S.first_b[r + 1] - S.first_b[r];
   const Req R = B.r[r];
-  const int nbk = keys_b(R, S.k);
+  int x0, x1;
+  chunk_range(keys_b(R, S.k), nch, w, x0, x1);
   const int sn = sealed_now(R);
-  const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
-  const int32_t* sel = S.topk + (int64_t)r * S.k;
+  const int32_t* rows = S.rows + (int64_t)r * S.k;
+  const int64_t max_row = (int64_t)P.max_blocks * kC4;
   auto key_b = [&](int x) {
     KeyAddr a;
     a.k = a.v = nullptr;
@@ -149,28 +164,23 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_step3(Pools P, ReqBatch B, 
       a.v = P.hca_v + (int64_t)R.aux * kRow;
       return a;
     }
-    const int32_t j = sel[x - sn];
-    if (j < 0 || j >= kC4 * R.nb) return a;
-    const int32_t id = tab[j / kC4];
-    if (id < 0 || id >= P.max_blocks) return a;
-    const int64_t off = ((int64_t)id * kC4 + j % kC4) * kRow;
-    a.k = P.csa_k + off;
-    a.v = P.csa_v + off;
+    const int64_t row = rows[x - sn];   // C4 row of a selected entry, from S2
+    if (row < 0 || row >= max_row) return a;   // never taken
+    a.k = P.csa_k + row * kRow;
+    a.v = P.csa_v + row * kRow;
     return a;
   };
   const uint16_t* dk = P.swa_k + (int64_t)R.state * P.n_win * kRow;   // valid row (L >= 1)
   const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
   float M, L, A8[8];
-  attend_keys(key_b, w * S.chunk_b, min(nbk, (w + 1) * S.chunk_b), S.q + (int64_t)r * kRow, dk, dv,
-              sh, M, L, A8);
-  store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + blockIdx.x, M, L, A8);
+  attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh, M, L, A8);
+  if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + blockIdx.x, M, L, A8);
 }
 
 __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) {
   const int r = blockIdx.x >> 2;
-  int fa, ca, fb, cb;
-  prefix_of(B.n, r, [&](int i) { return cdiv(keys_a(P, B.r[i]), S.chunk_a); }, fa, ca);
-  prefix_of(B.n, r, [&](int i) { return cdiv(keys_b(B.r[i], S.k), S.chunk_b); }, fb, cb);
+  const int fa = S.first_a[r], ca = S.first_a[r + 1] - fa;
+  const int fb = S.first_b[r], cb = S.first_b[r + 1] - fb;
   const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
   merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
                  h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow);
@@ -179,22 +189,22 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
 }  // namespace
 
 hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
-  const int grid = kSealSplit * B.n_seal + B.n + S.n_score + S.n_a;
+  const int grid = kSealSplit * B.n_seal + B.n + S.n_score;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(k_step1, dim3(grid), dim3(kAttnWaves * 64), 0, st, P, B, S);
   return hipGetLastError();
 }
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
-  const int grid = B.n + B.n_seal;
+  const int grid = B.n + B.n_seal + S.n_a;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_step2, dim3(grid), dim3(kSelThreads), 0, st, P, B, S);
+  hipLaunchKernelGGL(k_step2, dim3(grid), dim3(kStep2Threads), 0, st, P, B, S);
   return hipGetLastError();
 }
 
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
   if (S.n_b == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_step3, dim3(S.n_b), dim3(kAttnWaves * 64), 0, st, P, B, S);
+  hipLaunchKernelGGL(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), 0, st, P, B, S);
   return hipGetLastError();
 }
 
