@@ -96,35 +96,35 @@ __global__ __launch_bounds__(256) void k_bulk_write(Pools P, const WriteDesc* w,
 }  // namespace
 
 hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* kin, const void* vin,
-                                const float* iin, float* part, hipStream_t st) {
+                                const float* iin, float* part, hipStream_t st,
+                 const LaunchEv& ev) {
   const int grid = B.n + kSealSplit * B.n_seal;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_decode_append, dim3(grid), dim3(256), 0, st, P, B,
+  return launch_k(k_decode_append, dim3(grid), dim3(256), st, ev, P, B,
                      static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin, part);
-  return hipGetLastError();
 }
 
-hipError_t launch_seal_merge(const Pools& P, const ReqBatch& B, const float* part, hipStream_t st) {
+hipError_t launch_seal_merge(const Pools& P, const ReqBatch& B, const float* part, hipStream_t st,
+                 const LaunchEv& ev) {
   if (B.n_seal == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_seal_merge, dim3(B.n_seal), dim3(256), 0, st, P, B, part);
-  return hipGetLastError();
+  return launch_k(k_seal_merge, dim3(B.n_seal), dim3(256), st, ev, P, B, part);
 }
 
 hipError_t launch_bulk_seal(const Pools& P, const SealDesc* seals, int64_t n_seals, const void* kin,
-                            const void* vin, const float* iin, hipStream_t st) {
+                            const void* vin, const float* iin, hipStream_t st,
+                 const LaunchEv& ev) {
   if (n_seals == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bulk_seal, dim3((unsigned)n_seals), dim3(256), 0, st, P, seals,
+  return launch_k(k_bulk_seal, dim3((unsigned)n_seals), dim3(256), st, ev, P, seals,
                      static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin);
-  return hipGetLastError();
 }
 
 hipError_t launch_bulk_write(const Pools& P, const WriteDesc* w, int32_t n_req, int64_t total,
-                             const void* kin, const void* vin, const float* iin, hipStream_t st) {
+                             const void* kin, const void* vin, const float* iin, hipStream_t st,
+                 const LaunchEv& ev) {
   if (total == 0) return hipSuccess;
   const int64_t grid = total < 65536 ? total : 65536;
-  hipLaunchKernelGGL(k_bulk_write, dim3((unsigned)grid), dim3(256), 0, st, P, w, n_req, total,
+  return launch_k(k_bulk_write, dim3((unsigned)grid), dim3(256), st, ev, P, w, n_req, total,
                      static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin);
-  return hipGetLastError();
 }
 
 }  // namespace hsa

@@ -96,19 +96,19 @@ __global__ __launch_bounds__(256) void k_merge(Pools P, ReqBatch B, int32_t chun
 
 hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks, int32_t chunk,
                          const void* q, const int32_t* topk, int32_t k, float* part_acc,
-                         float* part_ml, float* out, hipStream_t st) {
+                         float* part_ml, float* out, hipStream_t st,
+                 const LaunchEv& ev) {
   if (total_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attend, dim3((unsigned)total_chunks), dim3(kAttnWaves * 64), 0, st, P, B,
+  return launch_k(k_attend, dim3((unsigned)total_chunks), dim3(kAttnWaves * 64), st, ev, P, B,
                      chunk, static_cast<const uint16_t*>(q), topk, k, part_acc, part_ml, out);
-  return hipGetLastError();
 }
 
 hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,
-                        const float* part_acc, const float* part_ml, float* out, hipStream_t st) {
+                        const float* part_acc, const float* part_ml, float* out, hipStream_t st,
+                 const LaunchEv& ev) {
   if (B.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_merge, dim3(4 * B.n), dim3(256), 0, st, P, B, chunk, k, part_acc, part_ml,
+  return launch_k(k_merge, dim3(4 * B.n), dim3(256), st, ev, P, B, chunk, k, part_acc, part_ml,
                      out);
-  return hipGetLastError();
 }
 
 }  // namespace hsa

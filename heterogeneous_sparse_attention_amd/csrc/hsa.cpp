@@ -88,7 +88,7 @@ int dev_alloc(hsa_ctx* c, void** p, size_t bytes) {
 
 int grow(hsa_ctx* c, void** p, size_t* cap, size_t need, size_t elem) {
   if (need <= *cap) return kOk;
-  size_t n = std::max(need, *cap + *cap / 2);
+  size_t n = std::max(need + need / 4, *cap + *cap / 2);   // headroom: growing synchronises the device
   HIP_TRY(hipDeviceSynchronize());
   if (*p) {
     c->allocs.erase(std::remove(c->allocs.begin(), c->allocs.end(), *p), c->allocs.end());
@@ -101,27 +101,36 @@ int grow(hsa_ctx* c, void** p, size_t* cap, size_t need, size_t elem) {
   return kOk;
 }
 
-// Timing around one launch of kernel `kid`.
+// Timing of one launch of kernel `kid`: the launch takes ev() and the dispatch
+// records the pair; the record is kept only if the kernel was launched.
 struct Timed {
   hsa_ctx* c;
   int kid;
-  hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
-  Timed(hsa_ctx* c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
+  bool fired = false;
+  Timed(hsa_ctx* c_, int kid_, hipStream_t) : c(c_), kid(kid_) {
     if (!(c->tmask & (1u << kid))) return;
     for (hipEvent_t* e : {&a, &b}) {
       if (!c->ev_free.empty()) {
         *e = c->ev_free.back();
         c->ev_free.pop_back();
-      } else if (hipEventCreate(e) != hipSuccess) {
+      } else if (hipEventCreateWithFlags(e, hipEventDisableSystemFence) != hipSuccess) {
+        // timing only: no system-scope cache writeback / invalidate around the kernel
         *e = nullptr;
       }
     }
-    if (a && b) hipEventRecord(a, st);
+  }
+  LaunchEv ev() {
+    LaunchEv e;
+    if (a && b) {
+      e.a = a;
+      e.b = b;
+      e.fired = &fired;
+    }
+    return e;
   }
   ~Timed() {
-    if (a && b) {
-      hipEventRecord(b, st);
+    if (a && b && fired) {
       c->recs.push_back({kid, a, b});
     } else {
       if (a) c->ev_free.push_back(a);
@@ -190,11 +199,11 @@ int run_bulk(hsa_ctx* c, const AppendPlan& plan, const void* k, const void* v, c
   const WriteDesc* dwrite = reinterpret_cast<const WriteDesc*>(static_cast<char*>(c->plan_dev) + sb);
   {
     Timed t(c, HSA_KERNEL_SEAL, st);
-    HIP_TRY(launch_bulk_seal(c->P, dseal, (int64_t)seals.size(), k, v, ik, st));
+    HIP_TRY(launch_bulk_seal(c->P, dseal, (int64_t)seals.size(), k, v, ik, st, t.ev()));
   }
   {
     Timed t(c, HSA_KERNEL_WRITE, st);
-    HIP_TRY(launch_bulk_write(c->P, dwrite, (int32_t)writes.size(), total, k, v, ik, st));
+    HIP_TRY(launch_bulk_write(c->P, dwrite, (int32_t)writes.size(), total, k, v, ik, st, t.ev()));
   }
   return kOk;
 }
@@ -217,11 +226,11 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
       Timed t(c, HSA_KERNEL_APPEND, st);
       HIP_TRY(launch_decode_append(c->P, B, static_cast<const uint16_t*>(k) + b0 * kRow,
                                    static_cast<const uint16_t*>(v) + b0 * kRow, ik + b0 * kIRow,
-                                   c->seal_part, st));
+                                   c->seal_part, st, t.ev()));
     }
     if (B.n_seal) {
       Timed t(c, HSA_KERNEL_SEAL, st);
-      HIP_TRY(launch_seal_merge(c->P, B, c->seal_part, st));
+      HIP_TRY(launch_seal_merge(c->P, B, c->seal_part, st, t.ev()));
     }
   }
   return kOk;
@@ -252,13 +261,13 @@ int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_id
     if (s) return s;
     {
       Timed t(c, HSA_KERNEL_SCORE, st);
-      HIP_TRY(launch_score(c->P, B, total, q_idx + (int64_t)b0 * kIRow, c->scores, ld, st));
+      HIP_TRY(launch_score(c->P, B, total, q_idx + (int64_t)b0 * kIRow, c->scores, ld, st, t.ev()));
     }
     {
       Timed t(c, HSA_KERNEL_SELECT, st);
       HIP_TRY(launch_select(B, k, (flags & HSA_TOPK_SORTED) ? 1 : 0, c->scores, ld,
                             idx_out + (int64_t)b0 * k, score_out ? score_out + (int64_t)b0 * k : nullptr,
-                            st));
+                            st, t.ev()));
     }
   }
   return kOk;
@@ -299,11 +308,11 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
     {
       Timed t(c, HSA_KERNEL_ATTEND, st);
       HIP_TRY(launch_attend(c->P, B, total, chunk, qb, tk, k, c->part_acc, c->part_ml,
-                            out + (int64_t)b0 * kRow, st));
+                            out + (int64_t)b0 * kRow, st, t.ev()));
     }
     if (total > n) {   // some request spans two or more chunks
       Timed t(c, HSA_KERNEL_MERGE, st);
-      HIP_TRY(launch_merge(c->P, B, chunk, k, c->part_acc, c->part_ml, out + (int64_t)b0 * kRow, st));
+      HIP_TRY(launch_merge(c->P, B, chunk, k, c->part_acc, c->part_ml, out + (int64_t)b0 * kRow, st, t.ev()));
     }
   }
   return kOk;
@@ -385,19 +394,19 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.seal_part = c->seal_part;
     {
       Timed t(c, HSA_KERNEL_STEP1, st);
-      HIP_TRY(launch_step1(c->P, B, S, st));
+      HIP_TRY(launch_step1(c->P, B, S, st, t.ev()));
     }
     {
       Timed t(c, HSA_KERNEL_STEP2, st);
-      HIP_TRY(launch_step2(c->P, B, S, st));
+      HIP_TRY(launch_step2(c->P, B, S, st, t.ev()));
     }
     {
       Timed t(c, HSA_KERNEL_STEP3, st);
-      HIP_TRY(launch_step3(c->P, B, S, st));
+      HIP_TRY(launch_step3(c->P, B, S, st, t.ev()));
     }
     {
       Timed t(c, HSA_KERNEL_STEP4, st);
-      HIP_TRY(launch_step4(c->P, B, S, st));
+      HIP_TRY(launch_step4(c->P, B, S, st, t.ev()));
     }
   }
   return kOk;
@@ -467,6 +476,19 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   c->P.n_win = cfg->n_win;
   c->P.max_blocks = (int32_t)cfg->max_blocks;
   c->seal_part = static_cast<float*>(p[10]);
+  // attention partials: a launch has at most max(64, target - n) + n <= target + 64
+  // chunks per part, so these never grow (no device synchronisation in a decode loop)
+  {
+    const size_t chunks = std::max<size_t>((size_t)c->step_a_wgs + c->step_b_wgs + 3 * kMaxReq,
+                                           (size_t)c->attend_wgs + kMaxReq);
+    st = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, chunks, kRow * sizeof(float));
+    if (st == kOk)
+      st = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, chunks, 2 * kH * sizeof(float));
+    if (st) {
+      hsa_destroy(c);
+      return st;
+    }
+  }
   hipError_t e = hipMemcpy(gates, cfg->gate_csa, kRow * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(gates + kRow, cfg->gate_hca, kRow * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(c->P.table, 0xff, bytes[8]);

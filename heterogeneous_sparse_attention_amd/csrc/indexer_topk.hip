@@ -37,18 +37,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, i
 }  // namespace
 
 hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks, const float* q_idx,
-                        float* scores, int64_t ld, hipStream_t st) {
+                        float* scores, int64_t ld, hipStream_t st,
+                 const LaunchEv& ev) {
   if (total_blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_score, dim3((unsigned)total_blocks), dim3(256), 0, st, P, B, q_idx, scores, ld);
-  return hipGetLastError();
+  return launch_k(k_score, dim3((unsigned)total_blocks), dim3(256), st, ev, P, B, q_idx, scores, ld);
 }
 
 hipError_t launch_select(const ReqBatch& B, int32_t k, int32_t sorted, const float* scores,
-                         int64_t ld, int32_t* idx_out, float* score_out, hipStream_t st) {
+                         int64_t ld, int32_t* idx_out, float* score_out, hipStream_t st,
+                 const LaunchEv& ev) {
   if (B.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_select, dim3(B.n), dim3(kSelThreads), 0, st, B, k, sorted, scores, ld,
+  return launch_k(k_select, dim3(B.n), dim3(kSelThreads), st, ev, B, k, sorted, scores, ld,
                      idx_out, score_out);
-  return hipGetLastError();
 }
 
 }  // namespace hsa

@@ -188,30 +188,30 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
 
 }  // namespace
 
-hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
+hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
+                 const LaunchEv& ev) {
   const int grid = kSealSplit * B.n_seal + B.n + S.n_score;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_step1, dim3(grid), dim3(kAttnWaves * 64), 0, st, P, B, S);
-  return hipGetLastError();
+  return launch_k(k_step1, dim3(grid), dim3(kAttnWaves * 64), st, ev, P, B, S);
 }
 
-hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
+hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
+                 const LaunchEv& ev) {
   const int grid = B.n + B.n_seal + S.n_a;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_step2, dim3(grid), dim3(kStep2Threads), 0, st, P, B, S);
-  return hipGetLastError();
+  return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
 }
 
-hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
+hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
+                 const LaunchEv& ev) {
   if (S.n_b == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), 0, st, P, B, S);
-  return hipGetLastError();
+  return launch_k(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), st, ev, P, B, S);
 }
 
-hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st) {
+hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
+                 const LaunchEv& ev) {
   if (B.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_step4, dim3(4 * B.n), dim3(256), 0, st, P, B, S);
-  return hipGetLastError();
+  return launch_k(k_step4, dim3(4 * B.n), dim3(256), st, ev, P, B, S);
 }
 
 }  // namespace hsa

@@ -203,9 +203,9 @@ hsa_status hsa_export_state(hsa_ctx* ctx, int32_t state, void* swa_k, void* swa_
 #define HSA_KERNEL_SELECT 4   /* top-k select                          */
 #define HSA_KERNEL_ATTEND 5   /* split-KV attention partials           */
 #define HSA_KERNEL_MERGE 6    /* attention partial merge               */
-#define HSA_KERNEL_STEP1 7    /* decode step: append, seal, scores,
+#define HSA_KERNEL_STEP1 7    /* decode step: append, seal, scores     */
+#define HSA_KERNEL_STEP2 8    /* decode step: top-k select, HCA merge,
                                  attention over SWA + earlier HCA      */
-#define HSA_KERNEL_STEP2 8    /* decode step: top-k select, HCA merge  */
 #define HSA_KERNEL_STEP3 9    /* decode step: attention over selected
                                  C4 + the new HCA                      */
 #define HSA_KERNEL_STEP4 10   /* decode step: partial merge            */
