@@ -11,5 +11,5 @@ See oracle/cache.py for what is computed and which passage each step follows.
 from .cache import (  # noqa: F401
     BLOCK, C4_PER_BLOCK, M_CSA, M_HCA, N_HEADS, HEAD_DIM, IDX_HEADS, IDX_DIM,
     OracleError, Oracle, bf16_round, gated_pool, token_scores, c4_scores,
-    select_topk, attention, length_split,
+    select_topk, attention, length_split, block_range_summary, decode_reference,
 )

@@ -154,6 +154,80 @@ def attention(q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray) -> np.ndarray:
     return np.einsum("hn,nhd->hd", p, Vc)
 
 
+# ---------------------------------------------------------------- one request, streamed
+
+def block_range_summary(args):
+    """HCA entries and C4 scores of the sealed blocks b0 .. b1-1 of one request.
+
+    args = (seq, gate_hca, q_idx_list, b0, b1); seq(pos) returns the request's
+    (K [n][H][D], V [n][H][D], kI [n][4][64]) at token positions pos. Block b holds
+    tokens 128b .. 128b+127 ([Q&A] §2.2): its HCA entry pools all 128 (reading R1)
+    and its 32 C4 scores follow reading R4, once per indexer query.
+    Returns (hca_k [n][H][D], hca_v, scores [len(q_idx_list)][32 n]).
+    """
+    seq, gate_hca, qis, b0, b1 = args
+    n = b1 - b0
+    K, V, KI = seq(np.arange(BLOCK * b0, BLOCK * b1, dtype=np.int64))
+    hk = np.empty((n, N_HEADS, HEAD_DIM), np.float32)
+    hv = np.empty_like(hk)
+    sc = np.empty((len(qis), C4_PER_BLOCK * n), np.float64)
+    for i in range(n):
+        g = slice(BLOCK * i, BLOCK * (i + 1))
+        hk[i], hv[i] = gated_pool(K[g], V[g], gate_hca)
+        for c, qi in enumerate(qis):
+            sc[c, C4_PER_BLOCK * i:C4_PER_BLOCK * (i + 1)] = c4_scores(KI[g], qi)
+    return hk, hv, sc
+
+
+def decode_reference(seq, n_win: int, gate_csa, gate_hca, cases, pmap=map, chunk: int = 32):
+    """Decode outputs of one request at several lengths, without holding its cache.
+
+    The same arithmetic as driving Oracle token by token, streamed block by block
+    so that a request of 2**20 tokens fits in memory: for each case (L, q, q_idx,
+    k), with L the length after the step's append, the request has L // 128 sealed
+    blocks (reading R2); every sealed C4 entry is scored (R4), the top-k is
+    selected (R8, R9), and one softmax runs over the SWA (the last min(L, n_win)
+    tokens, oldest first), the HCA entries of the sealed blocks in order, and the
+    selected C4 entries in ascending ordinal order ([Q&A] §4; R5, R6, R12).
+    seq(pos) gives the request's tokens (see block_range_summary); pmap maps
+    block_range_summary over block ranges (a process pool's map works).
+    Returns [(idx int32 [k], scores float64 [k], out float64 [H][D])] per case.
+    """
+    W_csa = np.asarray(gate_csa, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
+    W_hca = np.asarray(gate_hca, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
+    qis = [np.asarray(c[2], dtype=np.float64) for c in cases]
+    nb_max = max(int(c[0]) // BLOCK for c in cases)
+    ranges = [(seq, W_hca, qis, b, min(b + chunk, nb_max)) for b in range(0, nb_max, chunk)]
+    hk = np.empty((nb_max, N_HEADS, HEAD_DIM), np.float32)
+    hv = np.empty_like(hk)
+    sc = np.empty((len(cases), C4_PER_BLOCK * nb_max), np.float64)
+    for (_, _, _, b0, b1), (k_, v_, s_) in zip(ranges, pmap(block_range_summary, ranges)):
+        hk[b0:b1], hv[b0:b1], sc[:, C4_PER_BLOCK * b0:C4_PER_BLOCK * b1] = k_, v_, s_
+    res = []
+    for c, (L, q, _, k) in enumerate(cases):
+        L = int(L)
+        nb = L // BLOCK
+        idx, val = select_topk(sc[c, :C4_PER_BLOCK * nb], int(k))
+        sel = idx[idx >= 0].astype(np.int64)
+        Ks, Vs, _ = seq(np.arange(L - min(L, n_win), L, dtype=np.int64))
+        parts_k, parts_v = [np.asarray(Ks, np.float64), hk[:nb].astype(np.float64)], \
+                           [np.asarray(Vs, np.float64), hv[:nb].astype(np.float64)]
+        if sel.size:
+            pos = (M_CSA * sel[:, None] + np.arange(M_CSA)).reshape(-1)
+            Kc, Vc, _ = seq(pos)
+            Kc = np.asarray(Kc, np.float64).reshape(sel.size, M_CSA, N_HEADS, HEAD_DIM)
+            Vc = np.asarray(Vc, np.float64).reshape(sel.size, M_CSA, N_HEADS, HEAD_DIM)
+            ek = np.empty((sel.size, N_HEADS, HEAD_DIM))
+            ev = np.empty_like(ek)
+            for i in range(sel.size):                 # C4 entry j: tokens 4j .. 4j+3
+                ek[i], ev[i] = gated_pool(Kc[i], Vc[i], W_csa)
+            parts_k.append(ek)
+            parts_v.append(ev)
+        out = attention(q, np.concatenate(parts_k), np.concatenate(parts_v))
+        res.append((idx, val, out))
+    return res
+
+
 # ---------------------------------------------------------------- cache state
 
 class _Block:

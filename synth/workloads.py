@@ -77,6 +77,46 @@ class Workload:
         return int((self.prefill + self.decode_steps + extra_steps).max())
 
 
+class RequestTokens:
+    """Token source of request b of a workload: (K, V, kI) at any positions, as
+    float32 values (K and V are bf16 values), each keyed as the workload keys it.
+    Picklable, so that worker processes can regenerate tokens themselves."""
+
+    def __init__(self, index: int, b: int):
+        self.index, self.b = int(index), int(b)
+        self._wl = None
+
+    def __getstate__(self):
+        return {"index": self.index, "b": self.b}
+
+    def __setstate__(self, st):
+        self.index, self.b, self._wl = st["index"], st["b"], None
+
+    def __call__(self, pos):
+        from . import (STREAM_IDXK, STREAM_K, STREAM_V, bf16_bits_to_f32, tokens_bf16,
+                       tokens_f32)
+        if self._wl is None:
+            self._wl = make(self.index)
+        wl = self._wl
+        pos = np.asarray(pos, dtype=np.int64).reshape(-1)
+        key = wl.key(self.b, pos)
+        K = bf16_bits_to_f32(tokens_bf16(wl.seed, STREAM_K, key, pos))
+        V = bf16_bits_to_f32(tokens_bf16(wl.seed, STREAM_V, key, pos))
+        KI = tokens_f32(wl.seed, STREAM_IDXK, key, pos)
+        return K, V, KI
+
+    def query(self, p: int):
+        """(q [16][128] bf16 values as float32, q_idx [4][64]) of the decode token at p."""
+        from . import STREAM_Q, STREAM_QI, bf16_bits_to_f32, tokens_bf16, tokens_f32
+        if self._wl is None:
+            self._wl = make(self.index)
+        wl = self._wl
+        pos = np.array([p], np.int64)
+        key = wl.key(self.b, pos)
+        return (bf16_bits_to_f32(tokens_bf16(wl.seed, STREAM_Q, key, pos))[0],
+                tokens_f32(wl.seed, STREAM_QI, key, pos)[0])
+
+
 def seed_of(index: int) -> int:
     return 0x48534100 + index
 

@@ -1,0 +1,370 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench
+times (one hsa_decode_step per step over the whole batch, default launch shapes).
+
+- b32 (32 requests, L0 up to 8192, 64 steps): every step of every request against
+  the oracle driven token by token.
+- prefix (64 requests of 16K-64K tokens sharing 8 prefixes by fork, n_win 4096,
+  k 1024, 32 steps), long (4 requests of 2**20 tokens, k 2048, 16 steps across a
+  block boundary) and bulk (8 x 131072 tokens in one append): integer state and
+  refcounts exactly; selected scores exactly against the oracle's scores of those
+  entries; the selection against the oracle's scores of sampled blocks; sampled
+  block entries against the oracle's compressor; and, for sampled requests and
+  steps, the full top-k row and the attention output against
+  tests/golden/*_decode.npz, which tests/golden/make_fullsize.py writes with the
+  oracle alone.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import BLOCK, C4_PER_BLOCK, M_CSA, Oracle, gated_pool, token_scores
+from synth.workloads import RequestTokens, make
+from tests.gpu_util import bf16_to_f64, dev_rows, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import heterogeneous_sparse_attention_amd as hsa
+    hsa.load()          # raises if the library is missing: no fallback
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ oracle-side helpers
+
+def entry_scores(src, ordinals, q_idx):
+    """Oracle scores of the C4 entries `ordinals` of one request (reading R4)."""
+    ordinals = np.asarray(ordinals, np.int64)
+    pos = (M_CSA * ordinals[:, None] + np.arange(M_CSA)).reshape(-1)
+    _, _, KI = src(pos)
+    return token_scores(KI, q_idx).reshape(-1, M_CSA).sum(axis=1) / 4.0
+
+
+def check_selection(src, idx, val, nb, k, q_idx, sample_blocks):
+    """One request's top-k row against the oracle: kk valid ascending ordinals, -1
+    after; the returned scores equal the oracle's scores of those entries; and on
+    the sampled blocks no unselected entry beats the cut (ties go to the lowest
+    ordinal)."""
+    nc = C4_PER_BLOCK * nb
+    kk = min(k, nc)
+    assert np.all(idx[kk:] == -1) and np.all(np.isneginf(val[kk:]))
+    sel = idx[:kk].astype(np.int64)
+    assert np.all(sel >= 0) and np.all(sel < nc) and np.all(np.diff(sel) > 0)
+    ref = entry_scores(src, sel, q_idx)
+    assert np.array_equal(val[:kk].astype(np.float64), ref)
+    if kk == nc:
+        return
+    tau = ref.min()
+    tie_max = sel[ref == tau].max()
+    chosen = set(sel.tolist())
+    for lb in sample_blocks:
+        if lb >= nb:
+            continue
+        js = np.arange(C4_PER_BLOCK * lb, C4_PER_BLOCK * (lb + 1))
+        s = entry_scores(src, js, q_idx)
+        for j, sj in zip(js.tolist(), s.tolist()):
+            if j in chosen:
+                continue
+            assert sj <= tau, (j, sj, tau)
+            if sj == tau:
+                assert j > tie_max, (j, tie_max)
+
+
+def check_block(cache, block_id, src, lb, gates):
+    """A sealed block's device entries against the oracle's compressor of its tokens."""
+    Wc, Wh = gates
+    g = cache.export_block(block_id)
+    K, V, KI = src(np.arange(BLOCK * lb, BLOCK * (lb + 1)))
+    K = K.astype(np.float64)
+    V = V.astype(np.float64)
+    ck = np.empty((C4_PER_BLOCK, 16, 128))
+    cv = np.empty_like(ck)
+    for j in range(C4_PER_BLOCK):
+        ck[j], cv[j] = gated_pool(K[M_CSA * j:M_CSA * (j + 1)], V[M_CSA * j:M_CSA * (j + 1)], Wc)
+    hk, hv = gated_pool(K, V, Wh)
+    for name, ref in (("csa_k", ck), ("csa_v", cv), ("hca_k", hk), ("hca_v", hv)):
+        val = bf16_to_f64(g[name])
+        assert rel_l2(val, ref) <= TOL, (name, lb, rel_l2(val, ref))
+        assert np.mean(val == ref) > 0.97, (name, lb)
+    assert np.array_equal(g["idx"], KI)
+
+
+def check_ring(cache, state, src, L, n_win):
+    ex = cache.export_state(state)
+    p = np.arange(max(0, L - n_win), L)
+    K, V, KI = src(p)
+    assert np.array_equal(bf16_to_f64(ex["swa_k"][p % n_win]), K)
+    assert np.array_equal(bf16_to_f64(ex["swa_v"][p % n_win]), V)
+    t = np.arange(L - L % BLOCK, L)
+    assert np.array_equal(ex["idx_tail"][t % BLOCK], KI[len(p) - len(t):])
+
+
+def check_info(cache, state, L):
+    info = cache.state_query(state)
+    assert info["len"] == L and info["n_blocks"] == L // BLOCK
+    assert info["hca_tail"] == L % BLOCK and info["csa_tail"] == L % M_CSA
+
+
+def load_golden(name):
+    with np.load(os.path.join(GOLDEN, name), allow_pickle=False) as z:
+        return {k: z[k] for k in z.files}
+
+
+def step_inputs(wl, reqs, L0, t):
+    """Device inputs of decode step t: the token at position L0[b] + t of each request,
+    keyed as the workload keys it."""
+    pos = np.array([int(L0[b]) + t for b in reqs], np.int64)
+    keys = np.array([int(wl.key(b, p)) for b, p in zip(reqs, pos)], np.int64)
+    return (dev_rows(wl.seed, synth.STREAM_K, keys, pos, True),
+            dev_rows(wl.seed, synth.STREAM_V, keys, pos, True),
+            dev_rows(wl.seed, synth.STREAM_IDXK, keys, pos, False),
+            dev_rows(wl.seed, synth.STREAM_Q, keys, pos, True),
+            dev_rows(wl.seed, synth.STREAM_QI, keys, pos, False))
+
+
+def run_steps(cache, states, wl, L0, steps, on_step):
+    import torch
+    B, k = len(states), wl.topk
+    topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        kn, vn, ikn, q, qi = step_inputs(wl, list(range(B)), L0, t)
+        cache.decode_step(states, kn, vn, ikn, q, qi, k, topk_out=topk, score_out=sc, out=out)
+        torch.cuda.synchronize()
+        on_step(t, topk.cpu().numpy(), sc.cpu().numpy(), out.cpu().numpy())
+
+
+def check_golden_rows(gold, b, t, idx, out):
+    hit = np.nonzero((gold["req"] == b) & (gold["step"] == t))[0]
+    for i in hit:
+        assert np.array_equal(idx, gold["idx"][i]), (b, t)
+        assert rel_l2(out, gold["out"][i]) <= TOL, (b, t, rel_l2(out, gold["out"][i]))
+    return len(hit)
+
+
+# ------------------------------------------------------------------ b32
+
+def test_b32_every_step_against_oracle():
+    import bench
+    wl = make(2)
+    B, k = wl.batch, wl.topk
+    L0 = wl.prefill.astype(np.int64)
+    cache, inst = bench.setup_decode(wl, wl.decode_steps, 1)
+    states = inst[0]
+    say(f"b32: prefilled {int(L0.sum())} tokens on the GPU")
+    Wc, Wh = synth.gate_weights(wl.seed)
+    o = Oracle(wl.n_win, Wc, Wh, B, int(((L0 + wl.decode_steps) // BLOCK).sum()) + B)
+    srcs = [RequestTokens(2, b) for b in range(B)]
+    ost = []
+    for b in range(B):
+        s = o.state_alloc()
+        o.append([s], [srcs[b](np.arange(L0[b]))])
+        ost.append(s)
+    say("b32: oracle prefilled")
+    worst = [0.0]
+
+    def on_step(t, topk, sc, out):
+        for b in range(B):
+            p = int(L0[b]) + t
+            K, V, KI = srcs[b](np.array([p]))
+            o.append([ost[b]], [(K, V, KI)])
+            q, qi = srcs[b].query(p)
+            idx, val = o.topk(ost[b], qi, k)
+            assert np.array_equal(topk[b], idx), (t, b)
+            assert np.array_equal(sc[b].astype(np.float64), val), (t, b)
+            r = rel_l2(out[b], o.attend(ost[b], q, idx, k))
+            assert r <= TOL, (t, b, r)
+            worst[0] = max(worst[0], r)
+
+    run_steps(cache, states, wl, L0, wl.decode_steps, on_step)
+    for b in range(B):
+        check_info(cache, states[b], int(L0[b]) + wl.decode_steps)
+    say(f"b32: {wl.decode_steps} steps x {B} requests match; worst rel L2 {worst[0]:.2e}")
+    cache.close()
+
+
+# ------------------------------------------------------------------ long
+
+def test_long_context_full_size():
+    import bench
+    wl = make(5)
+    B, k, steps = wl.batch, wl.topk, wl.decode_steps
+    L0 = wl.prefill.astype(np.int64)
+    cache, inst = bench.setup_decode(wl, steps, 1)
+    states = inst[0]
+    say(f"long: prefilled {B} x {int(L0[0])} tokens on the GPU")
+    gold = load_golden("long_decode.npz")
+    srcs = [RequestTokens(5, b) for b in range(B)]
+    rng = np.random.default_rng(wl.seed + 7)
+    checked = [0]
+
+    def on_step(t, topk, sc, out):
+        for b in range(B):
+            L = int(L0[b]) + t + 1
+            nb = L // BLOCK
+            check_info(cache, states[b], L)
+            _, qi = srcs[b].query(L - 1)
+            sample = sorted({0, nb // 2, nb - 2, nb - 1, *rng.integers(0, nb, 4).tolist()})
+            check_selection(srcs[b], topk[b], sc[b], nb, k, qi, sample)
+            checked[0] += check_golden_rows(gold, b, t, topk[b], out[b])
+        say(f"long: step {t} ok")
+
+    run_steps(cache, states, wl, L0, steps, on_step)
+    assert checked[0] == len(gold["req"])
+    gates = synth.gate_weights(wl.seed)
+    for b in range(B):
+        table = cache.block_table(states[b])
+        nb = len(table)
+        for lb in sorted({0, 1, nb // 2, nb - 2, nb - 1, *rng.integers(0, nb, 3).tolist()}):
+            check_block(cache, table[lb], srcs[b], lb, gates)
+        check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win)
+    say("long: sampled blocks and rings ok")
+    cache.close()
+
+
+# ------------------------------------------------------------------ prefix
+
+def test_prefix_sharing_full_size():
+    import torch
+
+    from heterogeneous_sparse_attention_amd import Cache
+    wl = make(3)
+    B, k, steps = wl.batch, wl.topk, wl.decode_steps
+    L0 = wl.prefill.astype(np.int64)
+    Wc, Wh = synth.gate_weights(wl.seed)
+    max_len = wl.max_len()
+    cache = Cache(wl.n_win, B + wl.n_groups, wl.max_blocks_total() + 64, Wc, Wh,
+                  max_blocks_per_state=max_len // BLOCK + 2)
+    states = [None] * B
+    fork = {b: wl.fork_len(b) for b in range(B)}
+
+    def append(sts, reqs, p0s, p1s):
+        """Append positions [p0, p1) of each request, in pieces of at most 64K tokens."""
+        i = 0
+        while i < len(reqs):
+            grp, tot = [], 0
+            while i < len(reqs) and (tot + p1s[i] - p0s[i] <= 65536 or not grp):
+                grp.append(i)
+                tot += p1s[i] - p0s[i]
+                i += 1
+            pos = np.concatenate([np.arange(p0s[j], p1s[j]) for j in grp]).astype(np.int64)
+            keys = np.concatenate([wl.key(reqs[j], np.arange(p0s[j], p1s[j])) for j in grp])
+            keys = keys.astype(np.int64)
+            cu = np.concatenate([[0], np.cumsum([p1s[j] - p0s[j] for j in grp])]).astype(np.int64)
+            K = dev_rows(wl.seed, synth.STREAM_K, keys, pos, True)
+            V = dev_rows(wl.seed, synth.STREAM_V, keys, pos, True)
+            KI = dev_rows(wl.seed, synth.STREAM_IDXK, keys, pos, False)
+            cache.append_kv([sts[j] for j in grp], cu, K, V, KI)
+            del K, V, KI
+
+    # each group's parent grows through the shared prefix; children fork from it
+    for g in range(wl.n_groups):
+        kids = sorted((b for b in range(B) if wl.group(b) == g), key=lambda b: fork[b])
+        parent = cache.state_alloc()
+        cur = 0
+        for b in kids:
+            if fork[b] > cur:
+                append([parent], [b], [cur], [fork[b]])
+                cur = fork[b]
+            states[b] = cache.state_alloc()
+            cache.block_table_share(parent, states[b])
+        cache.state_free(parent)
+    append(states, list(range(B)), [fork[b] for b in range(B)], [int(L0[b]) for b in range(B)])
+    torch.cuda.synchronize()
+    say("prefix: forks and prefills done")
+
+    # shared blocks: one physical copy per group, refcount = number of sharers
+    for g in range(wl.n_groups):
+        kids = [b for b in range(B) if wl.group(b) == g]
+        tabs = {b: cache.block_table(states[b]) for b in kids}
+        for lb in range(wl.prefix_len // BLOCK):
+            users = [b for b in kids if fork[b] > BLOCK * lb]
+            if not users:
+                continue
+            ids = {tabs[b][lb] for b in users}
+            assert len(ids) == 1, (g, lb, ids)
+            assert cache.refcount(ids.pop()) == len(users)
+
+    gold = load_golden("prefix_decode.npz")
+    sampled = sorted(set(gold["req"].tolist()))
+    srcs = {b: RequestTokens(3, b) for b in range(B)}
+    rng = np.random.default_rng(wl.seed + 7)
+    checked = [0]
+
+    def on_step(t, topk, sc, out):
+        for b in range(B):
+            L = int(L0[b]) + t + 1
+            check_info(cache, states[b], L)
+            if b in sampled or t == steps - 1:
+                nb = L // BLOCK
+                _, qi = srcs[b].query(L - 1)
+                sample = sorted({0, nb - 1, *rng.integers(0, nb, 3).tolist()})
+                check_selection(srcs[b], topk[b], sc[b], nb, k, qi, sample)
+            checked[0] += check_golden_rows(gold, b, t, topk[b], out[b])
+        if t % 8 == 7:
+            say(f"prefix: step {t} ok")
+
+    run_steps(cache, states, wl, L0, steps, on_step)
+    assert checked[0] == len(gold["req"])
+    gates = (Wc, Wh)
+    for b in sampled:
+        table = cache.block_table(states[b])
+        nb = len(table)
+        last_shared = fork[b] // BLOCK - 1
+        for lb in sorted({0, last_shared, nb - 1}):
+            check_block(cache, table[lb], srcs[b], lb, gates)
+        check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win)
+    say("prefix: sampled blocks and rings ok")
+    cache.close()
+
+
+# ------------------------------------------------------------------ bulk
+
+def test_bulk_append_full_size():
+    import torch
+
+    from heterogeneous_sparse_attention_amd import Cache
+    wl = make(4)
+    B, n = wl.batch, int(wl.prefill[0])
+    Wc, Wh = synth.gate_weights(wl.seed)
+    nbq = n // BLOCK
+    cache = Cache(wl.n_win, B, B * nbq, Wc, Wh, max_blocks_per_state=nbq)
+    states = [cache.state_alloc() for _ in range(B)]
+    pos = np.tile(np.arange(n, dtype=np.int64), B)
+    keys = np.repeat(np.arange(B, dtype=np.int64), n)
+    K = dev_rows(wl.seed, synth.STREAM_K, keys, pos, True)
+    V = dev_rows(wl.seed, synth.STREAM_V, keys, pos, True)
+    KI = dev_rows(wl.seed, synth.STREAM_IDXK, keys, pos, False)
+    cache.append_kv(states, np.arange(B + 1, dtype=np.int64) * n, K, V, KI)   # one call
+    torch.cuda.synchronize()
+    del K, V, KI
+    say(f"bulk: appended {B} x {n} tokens in one call")
+    gates = (Wc, Wh)
+    rng = np.random.default_rng(wl.seed + 7)
+    for b in range(B):
+        check_info(cache, states[b], n)
+        table = cache.block_table(states[b])
+        # lowest free ids, requests in call order, blocks in token order (reading R10)
+        assert table == list(range(b * nbq, (b + 1) * nbq))
+        assert all(cache.refcount(i) == 1 for i in (table[0], table[-1]))
+        src = RequestTokens(4, b)
+        for lb in sorted({0, nbq // 2, nbq - 1, *rng.integers(0, nbq, 2).tolist()}):
+            check_block(cache, table[lb], src, lb, gates)
+        if b in (0, B - 1):
+            check_ring(cache, states[b], src, n, wl.n_win)
+    say("bulk: state, tables, sampled blocks and rings ok")
+    cache.close()

@@ -435,3 +435,36 @@ def test_errors_leave_state_unchanged():
     assert e.value.kind == "state"
     with pytest.raises(OracleError):
         o.append([a, a], [(K[:1], V[:1], KI[:1])] * 2)
+
+
+# ------------------------------------------------------------------ streamed reference
+
+@pytest.mark.parametrize("n_win,k", [(128, 20), (256, 4096)])
+def test_streamed_reference_matches_token_by_token(n_win, k):
+    """decode_reference (one request streamed block by block, used for the large
+    workloads) computes what the cache driven token by token computes: same top-k
+    rows, same selected scores, and the same attention output up to summation order."""
+    from oracle import decode_reference
+    from synth.workloads import RequestTokens, make
+
+    src = RequestTokens(2, 5)
+    wl = make(2)
+    Wc, Wh = synth.gate_weights(wl.seed)
+    o = Oracle(n_win, Wc, Wh, 2, 64)
+    s = o.state_alloc()
+    L_cases = [5, 127, 128, 300, 640, 777]
+    cases, expect = [], []
+    L = 0
+    for Lc in L_cases:
+        K, V, KI = src(np.arange(L, Lc))
+        o.append([s], [(K, V, KI)])
+        L = Lc
+        q, qi = src.query(Lc - 1)
+        idx, val = o.topk(s, qi, k)
+        expect.append((idx, val, o.attend(s, q, idx, k)))
+        cases.append((Lc, q, qi, k))
+    got = decode_reference(src, n_win, Wc, Wh, cases, chunk=2)
+    for (i0, v0, o0), (i1, v1, o1) in zip(expect, got):
+        np.testing.assert_array_equal(i0, i1)
+        np.testing.assert_array_equal(v0, v1)
+        np.testing.assert_allclose(o0, o1, rtol=1e-12, atol=1e-12)
