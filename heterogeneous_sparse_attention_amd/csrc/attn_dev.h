@@ -12,8 +12,8 @@
 // loads per row; lane l holds heads {l/16 + 4c} x dims (l%16)*8..+8 for c = 0..3,
 // and the 16 lanes of a DPP row reduce one head's dot product. Key addresses of 64
 // keys are resolved at once, one per lane, and broadcast with readlane, so the
-// load stream has no dependent address loads and no branches; two stages of two
-// keys are in flight per wave.
+// load stream has no dependent address loads; a ring of 4 or 5 keys per wave keeps
+// all but one of them in flight while one is consumed.
 #pragma once
 
 #include "device.h"
@@ -21,7 +21,6 @@
 namespace hsa {
 
 constexpr int kAttnWaves = 4;
-constexpr int kStage = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNoMax = -1e30f;   // running-max start: finite, so exp2 never sees inf - inf
 constexpr float kQScale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
@@ -46,69 +45,52 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-struct Stage {
-  uint4 k[kStage][4];
-  uint4 v[kStage][4];
-  bool ok[kStage];
-};
-
 __device__ __forceinline__ const uint16_t* lane_ptr(uint64_t p, int i) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)p, i);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(p >> 32), i);
   return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// Issue the loads of keys i .. i+kStage-1 of the current 64-key group.
-__device__ __forceinline__ void load_stage(Stage& S, uint64_t kp, uint64_t vp, uint64_t okmask,
-                                           int i, int lane) {
+// Keys in the load ring of a wave: RING - 1 keys stay in flight while one is
+// consumed. 5 keys fit the 512 VGPRs of a wave that has a SIMD to itself (4-wave
+// workgroups); 8-wave workgroups (two waves per SIMD, 256 VGPRs each) take 4.
+template <int WAVES>
+constexpr int ring_depth() { return WAVES > 4 ? 4 : 5; }
+
+struct KeyRegs {
+  uint4 k[4];
+  uint4 v[4];
+};
+
+// Issue the loads of key j (lane j's addresses) of the current 64-key group.
+__device__ __forceinline__ void load_key(KeyRegs& R, uint64_t kp, uint64_t vp, int j, int lane) {
+  const uint16_t* pk = lane_ptr(kp, j);
+  const uint16_t* pv = lane_ptr(vp, j);
 #pragma unroll
-  for (int u = 0; u < kStage; ++u) {
-    const int j = (i + u) & 63;
-    const uint16_t* pk = lane_ptr(kp, j);
-    const uint16_t* pv = lane_ptr(vp, j);
-    S.ok[u] = (i + u < 64) && ((okmask >> j) & 1ull);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      S.k[u][c] = reinterpret_cast<const uint4*>(pk + c * 512)[lane];
-      S.v[u][c] = reinterpret_cast<const uint4*>(pv + c * 512)[lane];
-    }
+  for (int c = 0; c < 4; ++c) {
+    R.k[c] = load_stream(reinterpret_cast<const uint4*>(pk + c * 512) + lane);
+    R.v[c] = load_stream(reinterpret_cast<const uint4*>(pv + c * 512) + lane);
   }
 }
 
-// Online softmax update of this lane's 4 heads with the keys of one stage.
-__device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, float* m, float* l,
-                                              float (*acc)[8]) {
+// Online softmax update of this lane's 4 heads with one key.
+__device__ __forceinline__ void compute_key(const KeyRegs& R, bool ok, const uint4* qw, float* m,
+                                            float* l, float (*acc)[8]) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    float s[kStage];
-    float mx = m[c];
-#pragma unroll
-    for (int u = 0; u < kStage; ++u) {
-      float a = dot2(qw[c].x, S.k[u][c].x, 0.f);
-      a = dot2(qw[c].y, S.k[u][c].y, a);
-      a = dot2(qw[c].z, S.k[u][c].z, a);
-      a = dot2(qw[c].w, S.k[u][c].w, a);
-      s[u] = S.ok[u] ? row_sum16(a) * kQScale : -INFINITY;
-      mx = fmaxf(mx, s[u]);
-    }
+    float a = dot2(qw[c].x, R.k[c].x, 0.f);
+    a = dot2(qw[c].y, R.k[c].y, a);
+    a = dot2(qw[c].z, R.k[c].z, a);
+    a = dot2(qw[c].w, R.k[c].w, a);
+    const float s = ok ? row_sum16(a) * kQScale : -INFINITY;
+    const float mx = fmaxf(m[c], s);
     const float sc = exp2f(m[c] - mx);
-    float p[kStage];
-    float ps = 0.f;
+    const float p = exp2f(s - mx);
+    l[c] = fmaf(l[c], sc, p);
+    float vf[8];
+    unpack8(R.v[c], vf);
 #pragma unroll
-    for (int u = 0; u < kStage; ++u) {
-      p[u] = exp2f(s[u] - mx);
-      ps += p[u];
-    }
-    l[c] = l[c] * sc + ps;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[c][i] *= sc;
-#pragma unroll
-    for (int u = 0; u < kStage; ++u) {
-      float vf[8];
-      unpack8(S.v[u][c], vf);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p[u], vf[i], acc[c][i]);
-    }
+    for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p, vf[i], acc[c][i] * sc);
     m[c] = mx;
   }
 }
@@ -118,7 +100,7 @@ __device__ __forceinline__ void compute_stage(const Stage& S, const uint4* qw, f
 // nullptrs for a skipped slot; dummy_k / dummy_v are valid rows read in place of
 // skipped keys. On return threads t < 256 hold head t/16, dims (t%16)*8 .. +8 of
 // the unnormalised result: running max M (log2 units), sum L, accumulator A8.
-template <int WAVES = kAttnWaves, class KeyFn>
+template <int WAVES = kAttnWaves, int RING = ring_depth<WAVES>(), class KeyFn>
 __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const uint16_t* qrow,
                                             const uint16_t* dummy_k, const uint16_t* dummy_v,
                                             AttnSharedT<WAVES>& sh, float& M, float& L, float* A8) {
@@ -149,14 +131,19 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
     const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
     const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
     const int n = min(64, w1 - g);
-    Stage A, Bs;
-    load_stage(A, kp, vp, okmask, 0, lane);
-    for (int i = 0; i < n; i += 2 * kStage) {
-      load_stage(Bs, kp, vp, okmask, i + kStage, lane);
-      compute_stage(A, qw, m, l, acc);
-      if (i + kStage >= n) break;
-      load_stage(A, kp, vp, okmask, i + 2 * kStage, lane);
-      compute_stage(Bs, qw, m, l, acc);
+    // ring of RING keys: RING - 1 keys stay in flight while one is consumed
+    KeyRegs ring[RING];
+#pragma unroll
+    for (int u = 0; u < RING - 1; ++u)
+      if (u < n) load_key(ring[u], kp, vp, u, lane);
+    for (int i = 0; i < n; i += RING) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        const int x = i + u;
+        if (x >= n) break;
+        if (x + RING - 1 < n) load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane);
+        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+      }
     }
   }
   // merge the four waves in LDS

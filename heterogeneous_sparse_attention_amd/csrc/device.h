@@ -28,6 +28,10 @@ constexpr int kBlk = 128;          // tokens per block = lcm(4, 128)
 constexpr int kC4 = 32;            // C4 entries per block
 constexpr int kMaxReq = 64;        // requests per launch descriptor
 constexpr int kSealSplit = 8;      // workgroups per decode-time seal (16 tokens each)
+#ifndef HSA_SCORE_SPLIT
+#define HSA_SCORE_SPLIT 2
+#endif
+constexpr int kScoreSplit = HSA_SCORE_SPLIT;   // decode-step scoring workgroups per sealed block
 constexpr int kPartFloats = 2 * kH + 2 * kRow;  // one HCA seal partial: m, l, acc K, acc V
 constexpr int kMaxTopk = 4096;
 
@@ -106,13 +110,13 @@ struct StepArgs {
   int32_t sorted;
   int32_t chunk_a;       // keys per part-A / part-B attention workgroup
   int32_t chunk_b;
-  int32_t n_score;       // sealed blocks of the batch (one scoring workgroup each)
+  int32_t n_score;       // scoring workgroups: kScoreSplit per sealed block
   int32_t n_a;           // part-A workgroups
   int32_t n_b;           // part-B workgroups
   int32_t pad_;
   int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
   int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])
-  int32_t first_s[kMaxReq + 1];   // request i's scoring workgroups (= its sealed blocks)
+  int32_t first_s[kMaxReq + 1];   // request i's first scoring workgroup
 };
 
 // The request owning item w of a list laid out by prefix `first` (first[0] = 0,
@@ -135,6 +139,19 @@ __device__ __forceinline__ void chunk_range(int n, int c, int w, int& x0, int& x
 }
 
 // ---------------------------------------------------------------- helpers
+
+// Streaming loads for data a step reads once (indexer keys, attention K/V rows):
+// non-temporal, so they do not displace lines that are reused.
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const f32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -344,7 +344,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       keys_a += na[i];
       keys_b += nb[i];
       maxnb = std::max<int64_t>(maxnb, r.nb_new);
-      n_score += r.nb_new;
+      n_score += (int64_t)kScoreSplit * r.nb_new;
     }
     StepArgs S{};
     S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
@@ -368,7 +368,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       S.first_s[i] = (int32_t)ts;
       ta += (na[i] + S.chunk_a - 1) / S.chunk_a;
       tb += (nb[i] + S.chunk_b - 1) / S.chunk_b;
-      ts += B.r[i].nb;
+      ts += (int64_t)kScoreSplit * B.r[i].nb;
     }
     S.first_a[n] = (int32_t)ta;
     S.first_b[n] = (int32_t)tb;

@@ -16,23 +16,24 @@
 
 namespace hsa {
 
-// Scores of the 32 C4 entries of one block by one workgroup of 256 threads: wave w
-// takes entries 8w .. 8w+7. Lane l owns dims 4l..4l+3 of every token row, so a
-// token row is one coalesced 1 KiB read per wave; the 4 tokens of an entry are
-// summed per lane before one wave reduction. row(t) is token t's indexer keys.
-template <class RowFn>
+// Scores of 4 * EPW consecutive C4 entries of one block by one workgroup of 256
+// threads: wave w takes entries EPW w .. EPW w + EPW - 1. Lane l owns dims
+// 4l..4l+3 of every token row, so a token row is one coalesced 1 KiB read per wave;
+// the 4 tokens of an entry are summed per lane before one wave reduction. row(t)
+// is the keys of the t-th token of the range, out the range's first score.
+template <int EPW = 8, class RowFn>
 __device__ __forceinline__ void score_block(RowFn row, const float* q_row, float* out32) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const float4 q = reinterpret_cast<const float4*>(q_row)[lane];
-  float4 kv[8][4];
+  float4 kv[EPW][4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+  for (int e = 0; e < EPW; ++e)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kv[e][u] = reinterpret_cast<const float4*>(row((8 * wave + e) * 4 + u))[lane];
-  float* out = out32 + 8 * wave;
+    for (int u = 0; u < 4; ++u) kv[e][u] = load_stream(reinterpret_cast<const float4*>(row((EPW * wave + e) * 4 + u)) + lane);
+  float* out = out32 + EPW * wave;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < EPW; ++e) {
     float a = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {

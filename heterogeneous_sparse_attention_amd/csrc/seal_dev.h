@@ -76,6 +76,7 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
 #pragma unroll
   for (int i = 0; i < 8; ++i) acck[i] = accv[i] = 0.f;
 
+#pragma unroll 1
   for (int g = 0; g < kSubTok / 4; ++g) {
     const int tb = t0 + 4 * g;
     uint4 kw[4], vw[4];
@@ -90,16 +91,18 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       const float4 iv = reinterpret_cast<const float4*>(src.i(tb + u))[c];
       reinterpret_cast<float4*>(idx_dst + (int64_t)(tb + u) * kIRow)[c] = iv;
     }
-    float kf[4][8], vf[4][8], gc[4], gh[4];
+    // the tokens stay packed (bf16 pairs) and are unpacked where used, which keeps
+    // the register count low enough for the scoring workgroups of the same launch
+    float gc[4], gh[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      unpack8(kw[u], kf[u]);
-      unpack8(vw[u], vf[u]);
+      float kf[8];
+      unpack8(kw[u], kf);
       float a = 0.f, b = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        a = fmaf(wc[i], kf[u][i], a);
-        b = fmaf(wh[i], kf[u][i], b);
+        a = fmaf(wc[i], kf[i], a);
+        b = fmaf(wh[i], kf[i], b);
       }
       gc[u] = row_sum16(a);
       gh[u] = row_sum16(b);
@@ -116,15 +119,22 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       const float inv = 1.f / s;
       float ck[8], cv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float a = 0.f, b = 0.f;
+      for (int i = 0; i < 8; ++i) ck[i] = cv[i] = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a = fmaf(e[u], kf[u][i], a);
-          b = fmaf(e[u], vf[u][i], b);
+      for (int u = 0; u < 4; ++u) {
+        float kf[8], vf[8];
+        unpack8(kw[u], kf);
+        unpack8(vw[u], vf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ck[i] = fmaf(e[u], kf[i], ck[i]);
+          cv[i] = fmaf(e[u], vf[i], cv[i]);
         }
-        ck[i] = a * inv;
-        cv[i] = b * inv;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ck[i] *= inv;
+        cv[i] *= inv;
       }
       const int slot = tb >> 2;
       uint4 ok, ov;
@@ -145,14 +155,19 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       l = l * sc + ((e[0] + e[1]) + (e[2] + e[3]));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float a = acck[i] * sc, b = accv[i] * sc;
+        acck[i] *= sc;
+        accv[i] *= sc;
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a = fmaf(e[u], kf[u][i], a);
-          b = fmaf(e[u], vf[u][i], b);
+      for (int u = 0; u < 4; ++u) {
+        float kf[8], vf[8];
+        unpack8(kw[u], kf);
+        unpack8(vw[u], vf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acck[i] = fmaf(e[u], kf[i], acck[i]);
+          accv[i] = fmaf(e[u], vf[i], accv[i]);
         }
-        acck[i] = a;
-        accv[i] = b;
       }
       m = mx;
     }

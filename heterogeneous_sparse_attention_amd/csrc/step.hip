@@ -58,55 +58,38 @@ __global__ __launch_bounds__(256, 4) void k_step1(Pools P, ReqBatch B, StepArgs 
   bid -= B.n;
   // -- indexer scores, one workgroup per sealed block
   if (bid < S.n_score) {
+    constexpr int kTok = kBlk / kScoreSplit;   // tokens per scoring workgroup
     const int r = owner_of(S.first_s, B.n, bid);
-    const int lb = bid - S.first_s[r];
+    const int u = bid - S.first_s[r];
+    const int lb = u / kScoreSplit;
+    const int t0 = kTok * (u % kScoreSplit);
     const Req R = B.r[r];
-    float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb;
+    float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb + t0 / 4;
     const float* qrow = S.qi + (int64_t)r * kIRow;
     if (R.aux >= 0 && lb == R.nb - 1) {
       // the block sealed in this step: keys from the indexer tail, the newest from
       // the input (its tail slot is being written in this launch)
       const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
       const float* inrow = S.iin + (int64_t)r * kIRow;
-      score_block([&](int t) { return t == kBlk - 1 ? inrow : tail + t * kIRow; }, qrow, out);
+      score_block<8 / kScoreSplit>(
+          [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; }, qrow, out);
     } else {
       const int32_t id = P.table[(int64_t)R.state * P.table_stride + lb];
       if (id < 0 || id >= P.max_blocks) {   // never taken: tables are written before use
-        if (threadIdx.x < kC4) out[threadIdx.x] = -INFINITY;
+        if (threadIdx.x < kTok / 4) out[threadIdx.x] = -INFINITY;
         return;
       }
-      const float* blk = P.idx_k + (int64_t)id * kBlk * kIRow;
-      score_block([&](int t) { return blk + t * kIRow; }, qrow, out);
+      const float* blk = P.idx_k + ((int64_t)id * kBlk + t0) * kIRow;
+      score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
     }
   }
 }
 
-constexpr int kStep2Threads = 512;   // 8 waves: 256 VGPRs per wave for the attention role
-constexpr int kStep2Waves = kStep2Threads / 64;
-
-union Step2Shared {
-  SelShared sel;
-  AttnSharedT<kStep2Waves> attn;
-};
-
-__global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
-  __shared__ Step2Shared sh;
-  int bid = blockIdx.x;
-  if (bid < B.n) {
-    const int64_t k = S.k;
-    const Req R = B.r[bid];
-    select_run<kStep2Threads>(kC4 * R.nb, S.k, S.sorted, S.scores + (int64_t)bid * S.ld,
-                              S.topk + bid * k, S.score_out ? S.score_out + bid * k : nullptr, sh.sel,
-                              P.table + (int64_t)R.state * P.table_stride, S.rows + bid * k);
-    return;
-  }
-  bid -= B.n;
-  if (bid < B.n_seal) {
-    seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
-    return;
-  }
-  bid -= B.n_seal;
-  // -- attention part A: SWA tokens + HCA of blocks sealed before this step
+// Attention part A (SWA tokens + HCA of blocks sealed before this step) of chunk
+// `bid`: it needs no top-k, so it runs beside the selection.
+template <int WAVES>
+__device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const StepArgs& S, int bid,
+                                       AttnSharedT<WAVES>& sh) {
   const int r = owner_of(S.first_a, B.n, bid);
   const int w = bid - S.first_a[r];
   const int nch = S.first_a[r + 1] - S.first_a[r];
@@ -134,9 +117,42 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
     return a;
   };
   float M, L, A8[8];
-  attend_keys<kStep2Waves>(key_a, x0, x1, S.q + (int64_t)r * kRow, ring_k, ring_v, sh.attn, M, L,
-                           A8);
+  attend_keys<WAVES>(key_a, x0, x1, S.q + (int64_t)r * kRow, ring_k, ring_v, sh, M, L, A8);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
+}
+
+#ifndef HSA_PART_A_IN_STEP3
+#define HSA_PART_A_IN_STEP3 0
+#endif
+constexpr bool kPartAInStep3 = HSA_PART_A_IN_STEP3;
+
+constexpr int kStep2Threads = 512;   // 8 waves: 256 VGPRs per wave for the attention role
+constexpr int kStep2Waves = kStep2Threads / 64;
+
+union Step2Shared {
+  SelShared sel;
+  AttnSharedT<kStep2Waves> attn;
+};
+
+__global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
+  __shared__ Step2Shared sh;
+  int bid = blockIdx.x;
+  if (bid < B.n) {
+    const int64_t k = S.k;
+    const Req R = B.r[bid];
+    select_run<kStep2Threads>(kC4 * R.nb, S.k, S.sorted, S.scores + (int64_t)bid * S.ld,
+                              S.topk + bid * k, S.score_out ? S.score_out + bid * k : nullptr, sh.sel,
+                              P.table + (int64_t)R.state * P.table_stride, S.rows + bid * k);
+    return;
+  }
+  bid -= B.n;
+  if (bid < B.n_seal) {
+    seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
+    return;
+  }
+  bid -= B.n_seal;
+  if (kPartAInStep3) return;
+  part_a<kStep2Waves>(P, B, S, bid, sh.attn);
 }
 
 #ifndef HSA_STEP3_WAVES
@@ -146,7 +162,14 @@ constexpr int kStep3Waves = HSA_STEP3_WAVES;
 
 __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B, StepArgs S) {
   __shared__ AttnSharedT<kStep3Waves> sh;
-  const int bid = blockIdx.x;
+  int bid = blockIdx.x;
+  if (kPartAInStep3) {
+    if (bid < S.n_a) {
+      part_a<kStep3Waves>(P, B, S, bid, sh);
+      return;
+    }
+    bid -= S.n_a;
+  }
   const int r = owner_of(S.first_b, B.n, bid);
   const int w = bid - S.first_b[r];
   const int nch = S.first_b[r + 1] - S.first_b[r];
@@ -174,7 +197,7 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
   const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
   float M, L, A8[8];
   attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh, M, L, A8);
-  if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + blockIdx.x, M, L, A8);
+  if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
 __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) {
@@ -197,15 +220,16 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = B.n + B.n_seal + S.n_a;
+  const int grid = B.n + B.n_seal + (kPartAInStep3 ? 0 : S.n_a);
   if (grid == 0) return hipSuccess;
   return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
 }
 
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  if (S.n_b == 0) return hipSuccess;
-  return launch_k(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), st, ev, P, B, S);
+  const int grid = S.n_b + (kPartAInStep3 ? S.n_a : 0);
+  if (grid == 0) return hipSuccess;
+  return launch_k(k_step3, dim3(grid), dim3(kStep3Waves * 64), st, ev, P, B, S);
 }
 
 hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
