@@ -120,16 +120,13 @@ struct StepArgs {
 };
 
 // The request owning item w of a list laid out by prefix `first` (first[0] = 0,
-// nondecreasing, first[n] = total): the largest r with first[r] <= w. Workgroup-
-// uniform binary search on kernel arguments (scalar loads).
+// nondecreasing, first[n] = total, n <= 64): the largest r with first[r] <= w. Each
+// lane reads one entry and a ballot counts the entries <= w, so the answer costs one
+// load latency instead of a chain of dependent loads. Wave-uniform.
 __device__ __forceinline__ int owner_of(const int32_t* first, int n, int w) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (first[mid] <= w) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
+  const int lane = threadIdx.x & 63;
+  const int v = lane < n ? first[lane] : 0x7fffffff;
+  return __builtin_amdgcn_readfirstlane(__popcll(__ballot(v <= w)) - 1);
 }
 
 // Range [x0, x1) of chunk w of c near-equal chunks over n keys.

@@ -40,6 +40,35 @@ __device__ __forceinline__ int keys_b(const Req& r, int32_t k) {
   return sealed_now(r) + (k < nc ? k : nc);
 }
 
+// Indexer scores of scoring unit `unit`: 128 / kScoreSplit tokens of one sealed block.
+__device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, const StepArgs& S,
+                                           int unit) {
+  constexpr int kTok = kBlk / kScoreSplit;   // tokens per scoring unit
+  const int r = owner_of(S.first_s, B.n, unit);
+  const int u = unit - S.first_s[r];
+  const int lb = u / kScoreSplit;
+  const int t0 = kTok * (u % kScoreSplit);
+  const Req R = B.r[r];
+  float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb + t0 / 4;
+  const float* qrow = S.qi + (int64_t)r * kIRow;
+  if (R.aux >= 0 && lb == R.nb - 1) {
+    // the block sealed in this step: keys from the indexer tail, the newest from
+    // the input (its tail slot is being written in this launch)
+    const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
+    const float* inrow = S.iin + (int64_t)r * kIRow;
+    score_block<8 / kScoreSplit>(
+        [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; }, qrow, out);
+  } else {
+    const int32_t id = P.table[(int64_t)R.state * P.table_stride + lb];
+    if (id < 0 || id >= P.max_blocks) {   // never taken: tables are written before use
+      if (threadIdx.x < kTok / 4) out[threadIdx.x] = -INFINITY;
+      return;
+    }
+    const float* blk = P.idx_k + ((int64_t)id * kBlk + t0) * kIRow;
+    score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
+  }
+}
+
 __global__ __launch_bounds__(256, 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
   int bid = blockIdx.x;
   // -- seal eighths (first, so the longest single workgroups start early)
@@ -56,34 +85,10 @@ __global__ __launch_bounds__(256, 4) void k_step1(Pools P, ReqBatch B, StepArgs 
     return;
   }
   bid -= B.n;
-  // -- indexer scores, one workgroup per sealed block
-  if (bid < S.n_score) {
-    constexpr int kTok = kBlk / kScoreSplit;   // tokens per scoring workgroup
-    const int r = owner_of(S.first_s, B.n, bid);
-    const int u = bid - S.first_s[r];
-    const int lb = u / kScoreSplit;
-    const int t0 = kTok * (u % kScoreSplit);
-    const Req R = B.r[r];
-    float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb + t0 / 4;
-    const float* qrow = S.qi + (int64_t)r * kIRow;
-    if (R.aux >= 0 && lb == R.nb - 1) {
-      // the block sealed in this step: keys from the indexer tail, the newest from
-      // the input (its tail slot is being written in this launch)
-      const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
-      const float* inrow = S.iin + (int64_t)r * kIRow;
-      score_block<8 / kScoreSplit>(
-          [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; }, qrow, out);
-    } else {
-      const int32_t id = P.table[(int64_t)R.state * P.table_stride + lb];
-      if (id < 0 || id >= P.max_blocks) {   // never taken: tables are written before use
-        if (threadIdx.x < kTok / 4) out[threadIdx.x] = -INFINITY;
-        return;
-      }
-      const float* blk = P.idx_k + ((int64_t)id * kBlk + t0) * kIRow;
-      score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
-    }
-  }
+  // -- indexer scores, one workgroup per unit (a 1/kScoreSplit block)
+  if (bid < S.n_score) score_unit(P, B, S, bid);
 }
+
 
 // Attention part A (SWA tokens + HCA of blocks sealed before this step) of chunk
 // `bid`: it needs no top-k, so it runs beside the selection.
