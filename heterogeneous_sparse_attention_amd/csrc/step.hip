@@ -126,11 +126,6 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
 }
 
-#ifndef HSA_PART_A_IN_STEP3
-#define HSA_PART_A_IN_STEP3 0
-#endif
-constexpr bool kPartAInStep3 = HSA_PART_A_IN_STEP3;
-
 constexpr int kStep2Threads = 512;   // 8 waves: 256 VGPRs per wave for the attention role
 constexpr int kStep2Waves = kStep2Threads / 64;
 
@@ -156,7 +151,6 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
     return;
   }
   bid -= B.n_seal;
-  if (kPartAInStep3) return;
   part_a<kStep2Waves>(P, B, S, bid, sh.attn);
 }
 
@@ -167,14 +161,7 @@ constexpr int kStep3Waves = HSA_STEP3_WAVES;
 
 __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B, StepArgs S) {
   __shared__ AttnSharedT<kStep3Waves> sh;
-  int bid = blockIdx.x;
-  if (kPartAInStep3) {
-    if (bid < S.n_a) {
-      part_a<kStep3Waves>(P, B, S, bid, sh);
-      return;
-    }
-    bid -= S.n_a;
-  }
+  const int bid = blockIdx.x;
   const int r = owner_of(S.first_b, B.n, bid);
   const int w = bid - S.first_b[r];
   const int nch = S.first_b[r + 1] - S.first_b[r];
@@ -225,16 +212,15 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = B.n + B.n_seal + (kPartAInStep3 ? 0 : S.n_a);
+  const int grid = B.n + B.n_seal + S.n_a;
   if (grid == 0) return hipSuccess;
   return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
 }
 
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = S.n_b + (kPartAInStep3 ? S.n_a : 0);
-  if (grid == 0) return hipSuccess;
-  return launch_k(k_step3, dim3(grid), dim3(kStep3Waves * 64), st, ev, P, B, S);
+  if (S.n_b == 0) return hipSuccess;
+  return launch_k(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), st, ev, P, B, S);
 }
 
 hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
