@@ -73,7 +73,49 @@ struct SelShared {
   int cnt[2][2][kSelWaves];   // [parity][above tau, equal to tau][wave]
 };
 
-// Top-k of one request's N scores S by one workgroup of 1024 threads. Radix select over the order-preserving keys finds
+constexpr int kSelBatch = 8;   // float4 loads in flight per thread when scores stream from L2
+
+// f(i, key) for every score i < N (N a multiple of 4) read from global memory: each
+// thread keeps kSelBatch float4 loads in flight, so a pass costs about N / (NT * 32)
+// memory latencies rather than one per element.
+template <int NT, class F>
+__device__ __forceinline__ void for_each_key(int N, const float* S, F f) {
+  const int n4 = N >> 2;
+  const float4* S4 = reinterpret_cast<const float4*>(S);
+  for (int b = 0; b < n4; b += NT * kSelBatch) {
+    float4 v[kSelBatch];
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const int j = b + u * NT + (int)threadIdx.x;
+      if (j < n4) v[u] = S4[j];
+    }
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const int j = b + u * NT + (int)threadIdx.x;
+      if (j < n4) {
+        f(4 * j, okey(v[u].x));
+        f(4 * j + 1, okey(v[u].y));
+        f(4 * j + 2, okey(v[u].z));
+        f(4 * j + 3, okey(v[u].w));
+      }
+    }
+  }
+}
+
+// Exclusive prefix sum over the wave's lanes, and the wave total in `total`.
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+  const int lane = threadIdx.x & 63;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  total = __shfl(incl, 63);
+  return incl - v;
+}
+
+// Top-k of one request's N scores S by one workgroup of NT threads. Radix select over the order-preserving keys finds
 // tau, the key of the kk-th entry under (score desc, ordinal asc), and `rem`,
 // how many entries equal to tau make the cut. One ordered pass then takes every
 // entry above tau and the first `rem` entries equal to tau, writing them in
@@ -108,7 +150,6 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         sh.keys[4 * i + 3] = okey(v.w);
       }
     }
-    auto key = [&](int i) -> uint32_t { return cached ? sh.keys[i] : okey(S[i]); };
 
     for (int b = tid; b < 3 * kBins; b += NT) (&sh.hist[0][0])[b] = 0u;
     if (tab_lds)
@@ -121,9 +162,13 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
       const uint32_t dmask = pass == 2 ? 1023u : 2047u;
       uint32_t* hist = sh.hist[pass];
-      for (int i = tid; i < N; i += NT) {
-        const uint32_t u = key(i);
+      auto count = [&](int, uint32_t u) {
         if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+      };
+      if (cached) {
+        for (int i = tid; i < N; i += NT) count(i, sh.keys[i]);
+      } else {
+        for_each_key<NT>(N, S, count);
       }
       __syncthreads();
       if (tid < 64) {
@@ -169,10 +214,81 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     // ordered pass: take entries above tau and the first `rem` equal to tau; the
     // entries taken before i are (above tau before i) + min(equal before i, rem)
     const int lane = tid & 63, wv = tid >> 6;
+    auto take = [&](int i, uint32_t u, int pos) {
+      if (sorted) {
+        sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
+      } else {
+        io[pos] = i;
+        if (so) so[pos] = okey_inv(u);
+        if (rows) rows[pos] = row_of(i);
+      }
+    };
+    if (!cached) {
+      // Scores stream from L2: wave w owns a contiguous range of float4s. Count its
+      // entries above / equal to tau, exchange the wave totals once, then write in
+      // order with in-wave prefix sums (no barrier per element).
+      const int n4 = N >> 2;
+      const int per = ((n4 + NW - 1) / NW + 63) & ~63;
+      const int j0 = wv * per, j1 = min(n4, j0 + per);
+      const float4* S4 = reinterpret_cast<const float4*>(S);
+      int gt_w = 0, eq_w = 0;
+      for (int j = j0 + lane; j < j1; j += 64) {
+        const float4 v = S4[j];
+        const uint32_t e[4] = {okey(v.x), okey(v.y), okey(v.z), okey(v.w)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gt_w += e[q] > tau;
+          eq_w += e[q] == tau;
+        }
+      }
+      int tot;
+      wave_excl_scan(gt_w, tot);
+      gt_w = tot;
+      wave_excl_scan(eq_w, tot);
+      eq_w = tot;
+      if (lane == 0) {
+        sh.cnt[0][0][wv] = gt_w;
+        sh.cnt[0][1][wv] = eq_w;
+      }
+      __syncthreads();
+      int base_gt = 0, base_eq = 0;
+      for (int w = 0; w < wv; ++w) {
+        base_gt += sh.cnt[0][0][w];
+        base_eq += sh.cnt[0][1][w];
+      }
+      for (int jb = j0; jb < j1; jb += 64) {
+        const int j = jb + lane;
+        uint32_t e[4] = {0u, 0u, 0u, 0u};
+        int g = 0, q_eq = 0;
+        if (j < j1) {
+          const float4 v = S4[j];
+          e[0] = okey(v.x); e[1] = okey(v.y); e[2] = okey(v.z); e[3] = okey(v.w);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            g += e[q] > tau;
+            q_eq += e[q] == tau;
+          }
+        }
+        int g_tot, e_tot;
+        int gb = base_gt + wave_excl_scan(g, g_tot);
+        int eb = base_eq + wave_excl_scan(q_eq, e_tot);
+        if (j < j1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bool gt = e[q] > tau, eq = e[q] == tau;
+            if (gt || (eq && eb < rem)) take(4 * j + q, e[q], gb + min(eb, rem));
+            gb += gt;
+            eb += eq;
+          }
+        }
+        base_gt += g_tot;
+        base_eq += e_tot;
+      }
+    }
     int base_gt = 0, base_eq = 0, parity = 0;
-    for (int c0 = 0; c0 < N; c0 += NT, parity ^= 1) {
+    for (int c0 = 0; cached && c0 < N; c0 += NT, parity ^= 1) {
       const int i = c0 + tid;
-      const uint32_t u = i < N ? key(i) : 0u;
+      const uint32_t u = i < N ? sh.keys[i] : 0u;
       const bool gt = i < N && u > tau;
       const bool eq = i < N && u == tau;
       const unsigned long long bg = __ballot(gt), be = __ballot(eq);
@@ -193,16 +309,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       const unsigned long long below = (1ull << lane) - 1ull;
       gt_before += __popcll(bg & below);
       eq_before += __popcll(be & below);
-      if (gt || (eq && eq_before < rem)) {
-        const int pos = gt_before + min(eq_before, rem);
-        if (sorted) {
-          sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
-        } else {
-          io[pos] = i;
-          if (so) so[pos] = okey_inv(u);
-          if (rows) rows[pos] = row_of(i);
-        }
-      }
+      if (gt || (eq && eq_before < rem)) take(i, u, gt_before + min(eq_before, rem));
       if (base_gt + min(base_eq, rem) >= kk) break;   // every entry taken (uniform)
     }
     if (sorted) {

@@ -328,6 +328,45 @@ def test_edge_cases_short_states_and_k_bounds():
     _decode_batch(cache, o, st, np.arange(5), seed, 64)
 
 
+def test_topk_large_rows_with_ties():
+    """Rows longer than the selection's LDS cache (N = 9600 > 4096 entries) stream
+    their scores from L2; request 1 has zero indexer keys in its first 150 blocks,
+    so 4800 entries score exactly 0 and the cut falls inside that tie. Both
+    selection kernels (hsa_indexer_topk and the decode step), sorted and unsorted,
+    against the oracle bit for bit; request 2 stays on the cached path."""
+    import torch
+    seed = 0x7070
+    L0 = [128 * 300 + 5, 128 * 300 + 5, 128 * 40 + 3]
+    cache, o = new_pair(128, 4, sum(L0) // 128 + 8, seed)
+    st = [cache.state_alloc() for _ in L0]
+    assert st == [o.state_alloc() for _ in L0]
+    cu = np.concatenate([[0], np.cumsum(L0)])
+    pos = np.concatenate([np.arange(n) for n in L0])
+    keys = np.repeat(np.arange(3), L0)
+    K, V, KI = dev_tokens(seed, keys, pos)
+    Kh, Vh, KIh = host_tokens(seed, keys, pos)
+    zero = np.nonzero((keys == 1) & (pos < 150 * 128))[0]
+    KI[torch.from_numpy(zero).cuda()] = 0.0
+    KIh[zero] = 0.0
+    cache.append_kv(st, cu, K, V, KI)
+    o.append(st, [(Kh[a:b], Vh[a:b], KIh[a:b]) for a, b in zip(cu[:-1], cu[1:])])
+    qpos = np.array(L0) - 1
+    _, QI = dev_queries(seed, np.arange(3), qpos)
+    _, qi = host_queries(seed, np.arange(3), qpos)
+    for k in (1, 777, 4096):
+        for srt in (False, True):
+            sc = torch.empty((3, k), dtype=torch.float32, device="cuda")
+            idx, _ = cache.indexer_topk(st, QI, k, score_out=sc, sorted=srt)
+            idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+            for i, s in enumerate(st):
+                ridx, rval = o.topk(s, qi[i], k, sorted=srt)
+                assert np.array_equal(idx[i], ridx), (k, srt, i)
+                m = ridx >= 0
+                assert np.array_equal(sc[i][m], rval[m]), (k, srt, i)
+    for k, srt in ((4096, False), (777, True), (1, False)):
+        _decode_batch(cache, o, st, np.arange(3), seed, k, sorted=srt)
+
+
 def test_errors_change_nothing_on_device():
     import heterogeneous_sparse_attention_amd as hsa
     seed = 3
