@@ -23,7 +23,7 @@ MAX_TOPK = 4096
 APPEND_DEFER_SEAL = 1
 
 KERNELS = ("append", "seal", "write", "score", "select", "attend", "merge",
-           "step1", "step2", "step3", "step4")
+           "step1", "step2", "step3", "step4", "step2b")
 TOPK_SORTED = 1
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 

@@ -258,12 +258,23 @@ __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, con
     }
     L = wave_sum(L);
     const float invL = 1.f / L;
-    for (int c = 0; c < n; ++c) {
-      const int64_t p = part_of(c);
-      const float wc = exp2f(part_ml[p * 2 * kH + h] - M) * invL;
-      const float2 v = *reinterpret_cast<const float2*>(accb + p * kRow);
-      ox = fmaf(wc, v.x, ox);
-      oy = fmaf(wc, v.y, oy);
+    // groups of 32 partials: the rows are loaded together, the weights are held by
+    // lanes 0..31 and broadcast
+    for (int g = 0; g < n; g += 32) {
+      float2 a[32];
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (g + c < n) a[c] = *reinterpret_cast<const float2*>(accb + part_of(g + c) * kRow);
+      const int cl = g + (lane & 31);
+      const float w = cl < n ? exp2f(part_ml[part_of(cl) * 2 * kH + h] - M) * invL : 0.f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        if (g + c < n) {
+          const float wc = __shfl(w, c);
+          ox = fmaf(wc, a[c].x, ox);
+          oy = fmaf(wc, a[c].y, oy);
+        }
+      }
     }
   }
   *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(ox, oy);

@@ -70,6 +70,26 @@ struct ReqBatch {
   int8_t seal_req[kMaxReq];    // decode append: batch index of each sealing request
 };
 
+// Rows of more than `slice` scores are selected in two rounds, so that one long row
+// is spread over many workgroups. Round 1: each slice of `slice` scores (the last
+// one shorter) keeps its own top-k1 (k1 = k rounded up to a multiple of 4) in
+// ascending ordinal order, padded with (-1, -inf). Round 2 (the next launch): the
+// slices' candidates, concatenated in slice order (hence in ordinal order), are
+// selected again. An entry of the row's top-k has fewer than k entries of its slice
+// ahead of it under (score desc, ordinal asc), so it is among its slice's top-k1:
+// the result is exact, ties included.
+constexpr int kSliceN = 16384;   // default slice length
+
+struct SelPlan {
+  int32_t n_wgs;                   // round-1 workgroups of the batch
+  int32_t gmax;                    // slices of the most-sliced row (1: no row is sliced)
+  int32_t k1;                      // candidates kept per slice
+  int32_t slice;                   // scores per slice, a multiple of 32
+  int32_t* cand_ord;               // [n][gmax][k1]
+  float* cand_score;               // [n][gmax][k1]
+  int32_t first[kMaxReq + 1];      // request i's round-1 workgroups: [first[i], first[i+1])
+};
+
 // A block to seal, read from device memory by the bulk seal kernel.
 struct SealDesc {
   int32_t state;
@@ -114,6 +134,7 @@ struct StepArgs {
   int32_t n_a;           // part-A workgroups
   int32_t n_b;           // part-B workgroups
   int32_t pad_;
+  SelPlan sel;           // top-k workgroups (rows longer than kSliceN are sliced)
   int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
   int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])
   int32_t first_s[kMaxReq + 1];   // request i's first scoring workgroup

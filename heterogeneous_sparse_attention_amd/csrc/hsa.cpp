@@ -67,14 +67,21 @@ struct hsa_ctx {
   int32_t attend_wgs = 512;   // attention workgroups per launch to aim for (one round)
   int32_t step_a_wgs = 256;   // decode step: part-A attention workgroups (8 waves each) to aim for
   int32_t step_b_wgs = 256;   // decode step: part-B attention workgroups to aim for
+  int32_t select_slice = kSliceN;   // top-k: longer score rows are selected in two rounds
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
+  int32_t* cand_ord = nullptr;  // top-k of sliced rows: per-slice candidates (ordinals, scores)
+  size_t cand_ord_cap = 0;
+  float* cand_score = nullptr;
+  size_t cand_score_cap = 0;
 
   hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {
     // launch-shape targets; the environment can override them for tuning sweeps
     if (const char* e = std::getenv("HSA_ATTEND_WGS")) attend_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_STEP_A_WGS")) step_a_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_STEP_B_WGS")) step_b_wgs = std::max(16, std::atoi(e));
+    if (const char* e = std::getenv("HSA_SELECT_SLICE"))   // a multiple of 32, at least 32
+      select_slice = std::max(32, std::min(1 << 24, std::atoi(e)) / 32 * 32);
   }
 };
 
@@ -236,6 +243,38 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
   return kOk;
 }
 
+// Top-k workgroups of a batch: one per row of at most `select_slice` scores, else
+// one per slice (the last one shorter), with room for each slice's candidates.
+int plan_select(hsa_ctx* c, const ReqBatch& B, int32_t k, SelPlan& SP) {
+  SP = SelPlan{};
+  SP.k1 = (k + 3) & ~3;
+  SP.slice = c->select_slice;
+  int32_t total = 0, gmax = 1;
+  for (int i = 0; i < B.n; ++i) {
+    const int64_t n = (int64_t)kC4 * B.r[i].nb;
+    // a sliced row holds more than k1 scores, so its slices keep at least k real
+    // candidates and round 2 never reaches their padding
+    const bool sliced = n > SP.slice && n > SP.k1;
+    const int32_t g = sliced ? (int32_t)((n + SP.slice - 1) / SP.slice) : 1;
+    SP.first[i] = total;
+    total += g;
+    gmax = std::max(gmax, g);
+  }
+  SP.first[B.n] = total;
+  SP.n_wgs = total;
+  SP.gmax = gmax;
+  if (gmax > 1) {
+    const size_t need = (size_t)B.n * gmax * SP.k1;
+    int s = grow(c, reinterpret_cast<void**>(&c->cand_ord), &c->cand_ord_cap, need, sizeof(int32_t));
+    if (s) return s;
+    s = grow(c, reinterpret_cast<void**>(&c->cand_score), &c->cand_score_cap, need, sizeof(float));
+    if (s) return s;
+    SP.cand_ord = c->cand_ord;
+    SP.cand_score = c->cand_score;
+  }
+  return kOk;
+}
+
 ReqBatch read_batch(hsa_ctx* c, const int32_t* states, int32_t b0, int32_t n) {
   ReqBatch B{};
   B.n = n;
@@ -263,9 +302,12 @@ int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_id
       Timed t(c, HSA_KERNEL_SCORE, st);
       HIP_TRY(launch_score(c->P, B, total, q_idx + (int64_t)b0 * kIRow, c->scores, ld, st, t.ev()));
     }
+    SelPlan SP;
+    s = plan_select(c, B, k, SP);
+    if (s) return s;
     {
       Timed t(c, HSA_KERNEL_SELECT, st);
-      HIP_TRY(launch_select(B, k, (flags & HSA_TOPK_SORTED) ? 1 : 0, c->scores, ld,
+      HIP_TRY(launch_select(B, SP, k, (flags & HSA_TOPK_SORTED) ? 1 : 0, c->scores, ld,
                             idx_out + (int64_t)b0 * k, score_out ? score_out + (int64_t)b0 * k : nullptr,
                             st, t.ev()));
     }
@@ -387,6 +429,8 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     if (s) return s;
     s = grow(c, reinterpret_cast<void**>(&c->rows), &c->rows_cap, (size_t)n * k, sizeof(int32_t));
     if (s) return s;
+    s = plan_select(c, B, k, S.sel);
+    if (s) return s;
     S.rows = c->rows;
     S.scores = c->scores;
     S.part_acc = c->part_acc;
@@ -399,6 +443,10 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     {
       Timed t(c, HSA_KERNEL_STEP2, st);
       HIP_TRY(launch_step2(c->P, B, S, st, t.ev()));
+    }
+    if (S.sel.gmax > 1) {
+      Timed t(c, HSA_KERNEL_STEP2B, st);
+      HIP_TRY(launch_step2b(c->P, B, S, st, t.ev()));
     }
     {
       Timed t(c, HSA_KERNEL_STEP3, st);

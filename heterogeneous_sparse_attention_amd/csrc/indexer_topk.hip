@@ -25,13 +25,20 @@ __global__ __launch_bounds__(256, 4) void k_score(Pools P, ReqBatch B, const flo
   score_block([&](int t) { return blk + t * kIRow; }, q_idx + (int64_t)r * kIRow, out);
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, int32_t k, int32_t sorted,
-                                                        const float* scores, int64_t ld,
+__global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, SelPlan SP, int32_t k,
+                                                        int32_t sorted, const float* scores, int64_t ld,
                                                         int32_t* idx_out, float* score_out) {
   __shared__ SelShared sh;
-  const int r = blockIdx.x;
-  select_run(kC4 * B.r[r].nb, k, sorted, scores + (int64_t)r * ld, idx_out + (int64_t)r * k,
-             score_out ? score_out + (int64_t)r * k : nullptr, sh);
+  select_round1<kSelThreads>(blockIdx.x, B.n, B.r, SP, k, sorted, scores, ld, idx_out, score_out, sh,
+                             nullptr, 0, nullptr);
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select2(ReqBatch B, SelPlan SP, int32_t k,
+                                                         int32_t sorted, int32_t* idx_out,
+                                                         float* score_out) {
+  __shared__ SelShared sh;
+  select_round2<kSelThreads>(blockIdx.x, B.r, SP, k, sorted, idx_out, score_out, sh, nullptr, 0,
+                             nullptr);
 }
 
 }  // namespace
@@ -43,12 +50,15 @@ hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks,
   return launch_k(k_score, dim3((unsigned)total_blocks), dim3(256), st, ev, P, B, q_idx, scores, ld);
 }
 
-hipError_t launch_select(const ReqBatch& B, int32_t k, int32_t sorted, const float* scores,
-                         int64_t ld, int32_t* idx_out, float* score_out, hipStream_t st,
-                 const LaunchEv& ev) {
+hipError_t launch_select(const ReqBatch& B, const SelPlan& SP, int32_t k, int32_t sorted,
+                         const float* scores, int64_t ld, int32_t* idx_out, float* score_out,
+                         hipStream_t st, const LaunchEv& ev) {
   if (B.n == 0) return hipSuccess;
-  return launch_k(k_select, dim3(B.n), dim3(kSelThreads), st, ev, B, k, sorted, scores, ld,
-                     idx_out, score_out);
+  hipError_t e = launch_k(k_select, dim3(SP.n_wgs), dim3(kSelThreads), st, ev, B, SP, k, sorted, scores,
+                          ld, idx_out, score_out);
+  if (e != hipSuccess || SP.gmax <= 1) return e;
+  return launch_k(k_select2, dim3(B.n), dim3(kSelThreads), st, LaunchEv{}, B, SP, k, sorted, idx_out,
+                  score_out);
 }
 
 }  // namespace hsa

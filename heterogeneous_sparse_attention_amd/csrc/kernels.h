@@ -54,11 +54,12 @@ hipError_t launch_bulk_write(const Pools& P, const WriteDesc* w, int32_t n_req, 
 hipError_t launch_score(const Pools& P, const ReqBatch& B, int64_t total_blocks, const float* q_idx,
                         float* scores, int64_t ld, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
-// Top-k of each request's scores (one workgroup per request), in ascending ordinal
-// order, or by (score desc, ordinal asc) when `sorted`.
-hipError_t launch_select(const ReqBatch& B, int32_t k, int32_t sorted, const float* scores,
-                         int64_t ld, int32_t* idx_out, float* score_out, hipStream_t st,
-                 const LaunchEv& ev = LaunchEv{});
+// Top-k of each request's scores (one workgroup per request or per slice of a long
+// row, then a second launch for sliced rows), in ascending ordinal order, or by
+// (score desc, ordinal asc) when `sorted`.
+hipError_t launch_select(const ReqBatch& B, const SelPlan& SP, int32_t k, int32_t sorted,
+                         const float* scores, int64_t ld, int32_t* idx_out, float* score_out,
+                         hipStream_t st, const LaunchEv& ev = LaunchEv{});
 
 // attend.hip
 // Keys of request i: min(len, n_win) SWA + nb HCA + min(k, 32 nb) C4 slots, cut in
@@ -77,6 +78,8 @@ hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_
 hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
+                 const LaunchEv& ev = LaunchEv{});
+hipError_t launch_step2b(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});

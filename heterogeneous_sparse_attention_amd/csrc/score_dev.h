@@ -102,6 +102,48 @@ __device__ __forceinline__ void for_each_key(int N, const float* S, F f) {
   }
 }
 
+// Round 1 of the top-k (see SelPlan), workgroup `bid`: the whole selection of an
+// unsliced row, or one slice.
+template <int NT>
+__device__ __forceinline__ void select_round1(int bid, int n_req, const Req* reqs, const SelPlan& SP,
+                                              int32_t k, int32_t sorted, const float* scores,
+                                              int64_t ld, int32_t* topk, float* score_out,
+                                              SelShared& sh, const int32_t* table, int64_t stride,
+                                              int32_t* rows) {
+  const int r = owner_of(SP.first, n_req, bid);
+  const int g = bid - SP.first[r];
+  const int G = SP.first[r + 1] - SP.first[r];
+  const Req R = reqs[r];
+  const int N = kC4 * R.nb;
+  const float* S = scores + (int64_t)r * ld;
+  if (G == 1) {
+    select_run<NT>(N, k, sorted, S, topk + (int64_t)r * k, score_out ? score_out + (int64_t)r * k : nullptr,
+                   sh, table ? table + (int64_t)R.state * stride : nullptr,
+                   rows ? rows + (int64_t)r * k : nullptr, R.nb);
+    return;
+  }
+  const int base = g * SP.slice;
+  const int64_t c0 = ((int64_t)r * SP.gmax + g) * SP.k1;
+  select_run<NT>(min(SP.slice, N - base), SP.k1, 0, S + base, SP.cand_ord + c0, SP.cand_score + c0, sh,
+                 nullptr, nullptr, 0, base);
+}
+
+// Round 2 for request `r` (no-op for an unsliced row).
+template <int NT>
+__device__ __forceinline__ void select_round2(int r, const Req* reqs, const SelPlan& SP, int32_t k,
+                                              int32_t sorted, int32_t* topk, float* score_out,
+                                              SelShared& sh, const int32_t* table, int64_t stride,
+                                              int32_t* rows) {
+  const int G = SP.first[r + 1] - SP.first[r];
+  if (G == 1) return;
+  const Req R = reqs[r];
+  const int64_t c0 = (int64_t)r * SP.gmax * SP.k1;
+  select_run<NT>(G * SP.k1, k, sorted, SP.cand_score + c0, topk + (int64_t)r * k,
+                 score_out ? score_out + (int64_t)r * k : nullptr, sh,
+                 table ? table + (int64_t)R.state * stride : nullptr, rows ? rows + (int64_t)r * k : nullptr,
+                 R.nb, 0, SP.cand_ord + c0);
+}
+
 // Exclusive prefix sum over the wave's lanes, and the wave total in `total`.
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
   const int lane = threadIdx.x & 63;
@@ -123,22 +165,27 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
 // entries are instead ordered by (score desc, ordinal asc) with a bitonic sort in
 // LDS.
 // With `rows`, also writes each taken entry's physical C4 row (table[j / 32] * 32 +
-// j % 32) from the state's block table `tab`. NT = threads of the workgroup.
+// j % 32) from the state's block table `tab` (nb_tab blocks). The ordinal written
+// for entry i is i + ord0, or ord_map[i] when a map is given. NT = threads of the
+// workgroup.
 template <int NT = kSelThreads>
 __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, const float* S,
                                            int32_t* io, float* so, SelShared& sh,
-                                           const int32_t* tab = nullptr, int32_t* rows = nullptr) {
+                                           const int32_t* tab = nullptr, int32_t* rows = nullptr,
+                                           int nb_tab = 0, int32_t ord0 = 0,
+                                           const int32_t* ord_map = nullptr) {
   static_assert(NT % 64 == 0 && NT <= kSelThreads && NT >= 256, "select workgroup size");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int kk = min(k, N);
   const bool cached = N <= kCacheN;
-  const int nb = N / kC4;
-  const bool tab_lds = rows && nb <= kTabCache;
+  const bool tab_lds = rows && nb_tab <= kTabCache;
   auto row_of = [&](int j) -> int32_t {
+    if (j < 0) return -1;
     const int32_t id = tab_lds ? sh.tab[j / kC4] : tab[j / kC4];
     return id * kC4 + j % kC4;
   };
+  auto ord_of = [&](int i) -> int32_t { return ord_map ? ord_map[i] : i + ord0; };
 
   if (kk > 0) {
     if (cached) {   // N is a multiple of 32: float4 loads
@@ -153,7 +200,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
 
     for (int b = tid; b < 3 * kBins; b += NT) (&sh.hist[0][0])[b] = 0u;
     if (tab_lds)
-      for (int b = tid; b < nb; b += NT) sh.tab[b] = tab[b];
+      for (int b = tid; b < nb_tab; b += NT) sh.tab[b] = tab[b];
     __syncthreads();
     uint32_t prefix = 0u, pmask = 0u;
     int rem = kk;
@@ -218,9 +265,10 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       if (sorted) {
         sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
       } else {
-        io[pos] = i;
+        const int32_t j = ord_of(i);
+        io[pos] = j;
         if (so) so[pos] = okey_inv(u);
-        if (rows) rows[pos] = row_of(i);
+        if (rows) rows[pos] = row_of(j);
       }
     };
     if (!cached) {
@@ -334,7 +382,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       }
       for (int i = tid; i < kk; i += NT) {
         const unsigned long long c = sh.cand[i];
-        const int j = (int32_t)(c & 0xffffffffull);
+        const int32_t j = ord_of((int32_t)(c & 0xffffffffull));
         io[i] = j;
         if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
         if (rows) rows[i] = row_of(j);

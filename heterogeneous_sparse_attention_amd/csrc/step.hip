@@ -137,21 +137,25 @@ union Step2Shared {
 __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
   __shared__ Step2Shared sh;
   int bid = blockIdx.x;
-  if (bid < B.n) {
-    const int64_t k = S.k;
-    const Req R = B.r[bid];
-    select_run<kStep2Threads>(kC4 * R.nb, S.k, S.sorted, S.scores + (int64_t)bid * S.ld,
-                              S.topk + bid * k, S.score_out ? S.score_out + bid * k : nullptr, sh.sel,
-                              P.table + (int64_t)R.state * P.table_stride, S.rows + bid * k);
+  if (bid < S.sel.n_wgs) {
+    select_round1<kStep2Threads>(bid, B.n, B.r, S.sel, S.k, S.sorted, S.scores, S.ld, S.topk,
+                                 S.score_out, sh.sel, P.table, P.table_stride, S.rows);
     return;
   }
-  bid -= B.n;
+  bid -= S.sel.n_wgs;
   if (bid < B.n_seal) {
     seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
     return;
   }
   bid -= B.n_seal;
   part_a<kStep2Waves>(P, B, S, bid, sh.attn);
+}
+
+// Round 2 of the top-k of rows sliced in k_step2 (launched only when some are).
+__global__ __launch_bounds__(kSelThreads) void k_step2b(Pools P, ReqBatch B, StepArgs S) {
+  __shared__ SelShared sh;
+  select_round2<kSelThreads>(blockIdx.x, B.r, S.sel, S.k, S.sorted, S.topk, S.score_out, sh, P.table,
+                             P.table_stride, S.rows);
 }
 
 #ifndef HSA_STEP3_WAVES
@@ -212,9 +216,15 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = B.n + B.n_seal + S.n_a;
+  const int grid = S.sel.n_wgs + B.n_seal + S.n_a;
   if (grid == 0) return hipSuccess;
   return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
+}
+
+hipError_t launch_step2b(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
+                         const LaunchEv& ev) {
+  if (B.n == 0 || S.sel.gmax <= 1) return hipSuccess;
+  return launch_k(k_step2b, dim3(B.n), dim3(kSelThreads), st, ev, P, B, S);
 }
 
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,

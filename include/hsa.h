@@ -209,7 +209,9 @@ hsa_status hsa_export_state(hsa_ctx* ctx, int32_t state, void* swa_k, void* swa_
 #define HSA_KERNEL_STEP3 9    /* decode step: attention over selected
                                  C4 + the new HCA                      */
 #define HSA_KERNEL_STEP4 10   /* decode step: partial merge            */
-#define HSA_KERNEL_COUNT 11
+#define HSA_KERNEL_STEP2B 11  /* decode step: second top-k round over
+                                 the candidates of sliced long rows    */
+#define HSA_KERNEL_COUNT 12
 hsa_status hsa_timing_enable(hsa_ctx* ctx, uint32_t mask);
 hsa_status hsa_timing_read(hsa_ctx* ctx, double* ms, int64_t* launches);
 

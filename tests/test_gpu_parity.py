@@ -334,6 +334,21 @@ def test_topk_large_rows_with_ties():
     so 4800 entries score exactly 0 and the cut falls inside that tie. Both
     selection kernels (hsa_indexer_topk and the decode step), sorted and unsorted,
     against the oracle bit for bit; request 2 stays on the cached path."""
+    _topk_rows_with_ties()
+
+
+@pytest.mark.parametrize("slice_n", [32, 1024])
+def test_topk_sliced_rows_with_ties(monkeypatch, slice_n):
+    """The same rows selected in two rounds (per-slice candidates, then a select
+    over them), with slices far shorter than the default so that 9600-entry rows
+    are cut into 10 or 300 slices: the tie of 4800 zero scores spans several slices,
+    short last slices pad their candidates, and request 2 (1280 entries) is sliced
+    for small k and whole for k = 4096."""
+    monkeypatch.setenv("HSA_SELECT_SLICE", str(slice_n))
+    _topk_rows_with_ties()
+
+
+def _topk_rows_with_ties():
     import torch
     seed = 0x7070
     L0 = [128 * 300 + 5, 128 * 300 + 5, 128 * 40 + 3]
