@@ -48,6 +48,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # ------------------------------------------------------------------ algorithmic bytes
 
+CACHE_N = 4096                 # score rows up to this length are selected in LDS
+
+
+def step_fused(nb: np.ndarray) -> bool:
+    """Whether the library runs this step in three launches: every score row fits the
+    selection's LDS cache (unless HSA_STEP_FUSED=0)."""
+    return os.environ.get("HSA_STEP_FUSED", "1") != "0" and bool((32 * nb <= CACHE_N).all())
+
+
 def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray) -> dict:
     """Bytes the method must move in one decode step, per launch (scratch excluded).
 
@@ -56,6 +65,20 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
     swa = np.minimum(L_after, n_win)
     kk = np.minimum(k, 32 * nb)
     B = len(L_after)
+    if step_fused(nb):
+        out = {
+            "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL_BYTES - ROW)
+                         + (nb * IDX_BLOCK).sum() + B * 1024),
+            # S2 (three-launch form): top-k out; HCA entries of new blocks; K/V rows
+            # of the SWA tokens, earlier HCA entries and selected C4 entries + the query
+            "step2": int((kk * 8).sum() + sealed.sum() * ROW
+                         + ((swa + nb - sealed + kk) * ROW).sum() + B * 4096),
+            "step3": 0,
+            # S4: the new HCA entries (K/V rows) and the fp32 output
+            "step4": int(sealed.sum() * ROW + B * 8192),
+        }
+        out["step"] = sum(out.values())
+        return out
     out = {
         # S1: token K, V, indexer key in + ring and tail slots out; seals (minus the
         # HCA entry written in S2); indexer keys of every sealed block + the
@@ -183,6 +206,10 @@ def run_decode(args) -> dict:
     warm = cache.timing_read()
     cache.timing_enable([])
     dominant = args.kernel or max(STEP_KERNELS, key=lambda n: warm[n][0])
+    # the byte split assumes the library's choice of form; check it against the launches
+    fused_steps = [step_fused((L0 + t // R + 1) // 128) for t in range(half, W)]
+    if W > half and (warm["step3"][1] == 0) != all(fused_steps):
+        raise RuntimeError("decode-step form differs from the one the byte split assumes")
 
     # timed pass 1 (value): whole steps between two events, nothing inside
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -197,15 +197,36 @@ __device__ __forceinline__ void store_output(float* out_row, float L, const floa
   o4[1] = make_float4(A8[4] * inv, A8[5] * inv, A8[6] * inv, A8[7] * inv);
 }
 
+// One extra key folded into a merge: its K and V rows and the request's query (bf16
+// [16][128] each), or null pointers for none.
+struct ExtraKey {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* q;
+};
+
 // Log-sum-exp merge of n partials (index of the j-th given by part_of(j), plain
 // arithmetic) for one request into out_row, by one wave per head h; lane l writes
 // dims 2l, 2l+1. Lane j holds partial j's max and sum; the partial rows are loaded
-// together with them, so up to 32 partials cost one memory round trip.
+// together with them, so up to 32 partials cost one memory round trip. With
+// xk.k set, the softmax also takes that key (score q.k / sqrt(128), weight on v),
+// as one more partial of max s, sum 1 and accumulator v.
 template <class PartFn>
 __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, const float* part_acc,
-                                               const float* part_ml, float* out_row) {
+                                               const float* part_ml, float* out_row,
+                                               ExtraKey xk = ExtraKey{nullptr, nullptr, nullptr}) {
   const int lane = threadIdx.x & 63;
   const float* accb = part_acc + h * kD + 2 * lane;
+  float xs = kNoMax, xvx = 0.f, xvy = 0.f;
+  if (xk.k) {
+    const int o = h * kD + 2 * lane;
+    const uint32_t qw = *reinterpret_cast<const uint32_t*>(xk.q + o);
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(xk.k + o);
+    const uint32_t vw = *reinterpret_cast<const uint32_t*>(xk.v + o);
+    xs = wave_sum(fmaf(bf_lo(qw), bf_lo(kw), bf_hi(qw) * bf_hi(kw))) * kQScale;
+    xvx = bf_lo(vw);
+    xvy = bf_hi(vw);
+  }
   float ox = 0.f, oy = 0.f;
   if (n <= 64) {
     float2 a[32];
@@ -220,10 +241,13 @@ __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, con
     }
     float M = fmaxf(mm, __shfl_xor(mm, 32));
     M = fmaxf(M, __shfl_xor(M, 16));
-    M = row_max16(M);
+    M = fmaxf(row_max16(M), xs);
     float w = lane < n ? exp2f(mm - M) : 0.f;
-    const float L = wave_sum(w * ll);
-    w *= 1.f / L;
+    const float xw = xk.k ? exp2f(xs - M) : 0.f;
+    const float invL = 1.f / (wave_sum(w * ll) + xw);
+    w *= invL;
+    ox = xw * invL * xvx;
+    oy = xw * invL * xvy;
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
       if (c < n) {
@@ -250,14 +274,16 @@ __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, con
     for (int c = lane; c < n; c += 64) M = fmaxf(M, part_ml[part_of(c) * 2 * kH + h]);
     M = fmaxf(M, __shfl_xor(M, 32));
     M = fmaxf(M, __shfl_xor(M, 16));
-    M = row_max16(M);
+    M = fmaxf(row_max16(M), xs);
     float L = 0.f;
     for (int c = lane; c < n; c += 64) {
       const int64_t p = part_of(c);
       L += exp2f(part_ml[p * 2 * kH + h] - M) * part_ml[p * 2 * kH + kH + h];
     }
-    L = wave_sum(L);
-    const float invL = 1.f / L;
+    const float xw = xk.k ? exp2f(xs - M) : 0.f;
+    const float invL = 1.f / (wave_sum(L) + xw);
+    ox = xw * invL * xvx;
+    oy = xw * invL * xvy;
     // groups of 32 partials: the rows are loaded together, the weights are held by
     // lanes 0..31 and broadcast
     for (int g = 0; g < n; g += 32) {

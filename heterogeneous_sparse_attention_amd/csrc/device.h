@@ -34,6 +34,7 @@ constexpr int kSealSplit = 8;      // workgroups per decode-time seal (16 tokens
 constexpr int kScoreSplit = HSA_SCORE_SPLIT;   // decode-step scoring workgroups per sealed block
 constexpr int kPartFloats = 2 * kH + 2 * kRow;  // one HCA seal partial: m, l, acc K, acc V
 constexpr int kMaxTopk = 4096;
+constexpr int kCacheN = 4096;      // top-k: scores kept in LDS (16 KiB); larger rows read through L2
 
 struct Pools {
   uint16_t* swa_k;
@@ -133,8 +134,8 @@ struct StepArgs {
   int32_t n_score;       // scoring workgroups: kScoreSplit per sealed block
   int32_t n_a;           // part-A workgroups
   int32_t n_b;           // part-B workgroups
-  int32_t pad_;
-  SelPlan sel;           // top-k workgroups (rows longer than kSliceN are sliced)
+  int32_t fused;         // 1: three launches, part B selects for itself (rows <= kCacheN)
+  SelPlan sel;           // top-k workgroups of the four-launch form (long rows are sliced)
   int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
   int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])
   int32_t first_s[kMaxReq + 1];   // request i's first scoring workgroup

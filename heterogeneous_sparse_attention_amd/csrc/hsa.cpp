@@ -68,6 +68,9 @@ struct hsa_ctx {
   int32_t step_a_wgs = 256;   // decode step: part-A attention workgroups (8 waves each) to aim for
   int32_t step_b_wgs = 256;   // decode step: part-B attention workgroups to aim for
   int32_t select_slice = kSliceN;   // top-k: longer score rows are selected in two rounds
+  int32_t step_fused = 1;     // decode step in three launches when every row fits the LDS cache
+  int32_t fused_a_wgs = 96;   // three-launch step: part-A / part-B workgroups to aim for
+  int32_t fused_b_wgs = 160;
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
   int32_t* cand_ord = nullptr;  // top-k of sliced rows: per-slice candidates (ordinals, scores)
@@ -80,6 +83,9 @@ struct hsa_ctx {
     if (const char* e = std::getenv("HSA_ATTEND_WGS")) attend_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_STEP_A_WGS")) step_a_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_STEP_B_WGS")) step_b_wgs = std::max(16, std::atoi(e));
+    if (const char* e = std::getenv("HSA_STEP_FUSED")) step_fused = std::atoi(e) != 0;
+    if (const char* e = std::getenv("HSA_FUSED_A_WGS")) fused_a_wgs = std::max(16, std::atoi(e));
+    if (const char* e = std::getenv("HSA_FUSED_B_WGS")) fused_b_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_SELECT_SLICE"))   // a multiple of 32, at least 32
       select_slice = std::max(32, std::min(1 << 24, std::atoi(e)) / 32 * 32);
   }
@@ -373,6 +379,11 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
     ReqBatch B{};
     B.n = n;
+    // three launches when every score row fits the selection's LDS cache: part-B
+    // workgroups then select for themselves and the new HCA key joins the merge
+    bool fused = c->step_fused != 0;
+    for (int i = 0; i < n; ++i)
+      fused = fused && (int64_t)kC4 * plan.reqs[b0 + i].nb_new <= kCacheN;
     std::vector<int64_t> na(n), nb(n);
     int64_t keys_a = 0, keys_b = 0, maxnb = 0, n_score = 0;
     for (int i = 0; i < n; ++i) {
@@ -382,7 +393,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       if (id >= 0) B.seal_req[B.n_seal++] = (int8_t)i;
       const int64_t sealed = id >= 0 ? 1 : 0;
       na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + r.nb_new - sealed;
-      nb[i] = sealed + std::min<int64_t>(k, (int64_t)kC4 * r.nb_new);
+      nb[i] = (fused ? 0 : sealed) + std::min<int64_t>(k, (int64_t)kC4 * r.nb_new);
       keys_a += na[i];
       keys_b += nb[i];
       maxnb = std::max<int64_t>(maxnb, r.nb_new);
@@ -400,8 +411,9 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.out = out + (int64_t)b0 * kRow;
     S.k = k;
     S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
-    S.chunk_a = attend_chunk(keys_a, n, c->step_a_wgs);
-    S.chunk_b = attend_chunk(keys_b, n, c->step_b_wgs);
+    S.fused = fused ? 1 : 0;
+    S.chunk_a = attend_chunk(keys_a, n, fused ? c->fused_a_wgs : c->step_a_wgs);
+    S.chunk_b = attend_chunk(keys_b, n, fused ? c->fused_b_wgs : c->step_b_wgs);
     S.n_score = (int32_t)n_score;
     int64_t ta = 0, tb = 0, ts = 0;
     for (int i = 0; i < n; ++i) {
@@ -409,7 +421,8 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       S.first_b[i] = (int32_t)tb;
       S.first_s[i] = (int32_t)ts;
       ta += (na[i] + S.chunk_a - 1) / S.chunk_a;
-      tb += (nb[i] + S.chunk_b - 1) / S.chunk_b;
+      // fused: at least one part-B workgroup per request, which writes the top-k padding
+      tb += std::max<int64_t>(fused ? 1 : 0, (nb[i] + S.chunk_b - 1) / S.chunk_b);
       ts += (int64_t)kScoreSplit * B.r[i].nb;
     }
     S.first_a[n] = (int32_t)ta;
@@ -429,8 +442,10 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     if (s) return s;
     s = grow(c, reinterpret_cast<void**>(&c->rows), &c->rows_cap, (size_t)n * k, sizeof(int32_t));
     if (s) return s;
-    s = plan_select(c, B, k, S.sel);
-    if (s) return s;
+    if (!fused) {
+      s = plan_select(c, B, k, S.sel);
+      if (s) return s;
+    }
     S.rows = c->rows;
     S.scores = c->scores;
     S.part_acc = c->part_acc;
@@ -444,7 +459,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       Timed t(c, HSA_KERNEL_STEP2, st);
       HIP_TRY(launch_step2(c->P, B, S, st, t.ev()));
     }
-    if (S.sel.gmax > 1) {
+    if (!fused && S.sel.gmax > 1) {
       Timed t(c, HSA_KERNEL_STEP2B, st);
       HIP_TRY(launch_step2b(c->P, B, S, st, t.ev()));
     }

@@ -60,7 +60,6 @@ __device__ __forceinline__ float okey_inv(uint32_t u) {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCacheN = 4096;      // scores kept in LDS (16 KiB); larger rows read through L2
 constexpr int kBins = 2048;        // radix digits of 11, 11 and 10 bits
 constexpr int kTabCache = 1024;    // block-table entries kept in LDS for the row output
 
@@ -144,6 +143,16 @@ __device__ __forceinline__ void select_round2(int r, const Req* reqs, const SelP
                  R.nb, 0, SP.cand_ord + c0);
 }
 
+// Which part of the selection one workgroup writes: the physical C4 rows of output
+// positions [x0, x1) of the ascending-ordinal list (position x to rows[x - x0]);
+// with `io`, the ordinals and scores of those positions (of every position, in
+// selection order, when sorted); with `pad`, the padding of positions [kk, k).
+struct SelWin {
+  int x0, x1;
+  bool io, pad;
+};
+constexpr SelWin kSelAll{0, 1 << 30, true, true};
+
 // Exclusive prefix sum over the wave's lanes, and the wave total in `total`.
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
   const int lane = threadIdx.x & 63;
@@ -165,15 +174,16 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
 // entries are instead ordered by (score desc, ordinal asc) with a bitonic sort in
 // LDS.
 // With `rows`, also writes each taken entry's physical C4 row (table[j / 32] * 32 +
-// j % 32) from the state's block table `tab` (nb_tab blocks). The ordinal written
-// for entry i is i + ord0, or ord_map[i] when a map is given. NT = threads of the
-// workgroup.
+// j % 32) from the state's block table `tab` (nb_tab blocks), in ascending ordinal
+// order. The ordinal written for entry i is i + ord0, or ord_map[i] when a map is
+// given. `win` limits what is written (SelWin). NT = threads of the workgroup.
 template <int NT = kSelThreads>
 __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, const float* S,
                                            int32_t* io, float* so, SelShared& sh,
                                            const int32_t* tab = nullptr, int32_t* rows = nullptr,
                                            int nb_tab = 0, int32_t ord0 = 0,
-                                           const int32_t* ord_map = nullptr) {
+                                           const int32_t* ord_map = nullptr,
+                                           SelWin win = kSelAll) {
   static_assert(NT % 64 == 0 && NT <= kSelThreads && NT >= 256, "select workgroup size");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
@@ -262,14 +272,15 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     // entries taken before i are (above tau before i) + min(equal before i, rem)
     const int lane = tid & 63, wv = tid >> 6;
     auto take = [&](int i, uint32_t u, int pos) {
-      if (sorted) {
-        sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
-      } else {
-        const int32_t j = ord_of(i);
+      const bool in = pos >= win.x0 && pos < win.x1;
+      if (sorted && win.io) sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
+      if (!in) return;
+      const int32_t j = ord_of(i);
+      if (!sorted && win.io) {
         io[pos] = j;
         if (so) so[pos] = okey_inv(u);
-        if (rows) rows[pos] = row_of(j);
       }
+      if (rows) rows[pos - win.x0] = row_of(j);
     };
     if (!cached) {
       // Scores stream from L2: wave w owns a contiguous range of float4s. Count its
@@ -360,7 +371,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       if (gt || (eq && eq_before < rem)) take(i, u, gt_before + min(eq_before, rem));
       if (base_gt + min(base_eq, rem) >= kk) break;   // every entry taken (uniform)
     }
-    if (sorted) {
+    if (sorted && win.io) {
       int n2 = 1;
       while (n2 < kk) n2 <<= 1;
       for (int i = kk + tid; i < n2; i += NT) sh.cand[i] = ~0ull;
@@ -385,13 +396,14 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         const int32_t j = ord_of((int32_t)(c & 0xffffffffull));
         io[i] = j;
         if (so) so[i] = okey_inv(~(uint32_t)(c >> 32));
-        if (rows) rows[i] = row_of(j);
       }
     }
   }
-  for (int i = kk + tid; i < k; i += NT) {
-    io[i] = -1;
-    if (so) so[i] = -INFINITY;
+  if (win.pad) {
+    for (int i = kk + tid; i < k; i += NT) {
+      io[i] = -1;
+      if (so) so[i] = -INFINITY;
+    }
   }
 }
 

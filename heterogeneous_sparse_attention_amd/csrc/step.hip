@@ -35,9 +35,11 @@ __device__ __forceinline__ int sealed_now(const Req& r) { return r.aux >= 0 ? 1 
 __device__ __forceinline__ int keys_a(const Pools& P, const Req& r) {
   return (r.len < P.n_win ? r.len : P.n_win) + r.nb - sealed_now(r);
 }
-__device__ __forceinline__ int keys_b(const Req& r, int32_t k) {
+// Part-B keys: the selected C4 entries, and in the four-launch form the HCA entry of
+// the block sealed now (the three-launch form takes that key in the merge).
+__device__ __forceinline__ int keys_b(const Req& r, int32_t k, int32_t fused) {
   const int nc = kC4 * r.nb;
-  return sealed_now(r) + (k < nc ? k : nc);
+  return (fused ? 0 : sealed_now(r)) + (k < nc ? k : nc);
 }
 
 // Indexer scores of scoring unit `unit`: 128 / kScoreSplit tokens of one sealed block.
@@ -129,20 +131,72 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
 constexpr int kStep2Threads = 512;   // 8 waves: 256 VGPRs per wave for the attention role
 constexpr int kStep2Waves = kStep2Threads / 64;
 
-union Step2Shared {
-  SelShared sel;
-  AttnSharedT<kStep2Waves> attn;
+struct Step2Shared {
+  union {
+    SelShared sel;
+    AttnSharedT<kStep2Waves> attn;
+  };
+  int32_t rows[kCacheN];   // three-launch part B: physical C4 rows of the workgroup's share
 };
+
+// Three-launch form, attention part B of chunk `bid`: the workgroup selects its
+// request's top-k itself (the row's at most kCacheN scores are read from L2 into
+// LDS), keeps in LDS the physical C4 rows of its own share [x0, x1) of the
+// selection, writes its share of the top-k output (its ordinals and scores, or,
+// when sorted, workgroup 0 all of them; workgroup 0 also writes the padding), then
+// attends those entries. Every part-B workgroup of a request runs the same
+// selection on the same scores, so the shares agree.
+template <int WAVES>
+__device__ __forceinline__ void part_b_fused(const Pools& P, const ReqBatch& B, const StepArgs& S,
+                                             int bid, Step2Shared& sh) {
+  const int r = owner_of(S.first_b, B.n, bid);
+  const int w = bid - S.first_b[r];
+  const int nch = S.first_b[r + 1] - S.first_b[r];
+  const Req R = B.r[r];
+  const int kk = keys_b(R, S.k, 1);
+  int x0, x1;
+  chunk_range(kk, nch, w, x0, x1);
+  const int64_t k = S.k;
+  select_run<WAVES * 64>(kC4 * R.nb, S.k, S.sorted, S.scores + (int64_t)r * S.ld, S.topk + r * k,
+                         S.score_out ? S.score_out + r * k : nullptr, sh.sel,
+                         P.table + (int64_t)R.state * P.table_stride, sh.rows, R.nb, 0, nullptr,
+                         SelWin{x0, x1, !S.sorted || w == 0, w == 0});
+  __syncthreads();   // rows in LDS complete; the selection's LDS is free for attention
+  const int64_t max_row = (int64_t)P.max_blocks * kC4;
+  auto key_b = [&](int x) {
+    KeyAddr a;
+    a.k = a.v = nullptr;
+    const int64_t row = sh.rows[x - x0];
+    if (row < 0 || row >= max_row) return a;   // never taken
+    a.k = P.csa_k + row * kRow;
+    a.v = P.csa_v + row * kRow;
+    return a;
+  };
+  const uint16_t* dk = P.swa_k + (int64_t)R.state * P.n_win * kRow;   // valid row (L >= 1)
+  const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  float M, L, A8[8];
+  attend_keys<WAVES>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh.attn, M, L, A8);
+  if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
+}
 
 __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
   __shared__ Step2Shared sh;
   int bid = blockIdx.x;
-  if (bid < S.sel.n_wgs) {
-    select_round1<kStep2Threads>(bid, B.n, B.r, S.sel, S.k, S.sorted, S.scores, S.ld, S.topk,
-                                 S.score_out, sh.sel, P.table, P.table_stride, S.rows);
-    return;
+  if (S.fused) {
+    // part B first: its workgroups select before they stream
+    if (bid < S.n_b) {
+      part_b_fused<kStep2Waves>(P, B, S, bid, sh);
+      return;
+    }
+    bid -= S.n_b;
+  } else {
+    if (bid < S.sel.n_wgs) {
+      select_round1<kStep2Threads>(bid, B.n, B.r, S.sel, S.k, S.sorted, S.scores, S.ld, S.topk,
+                                   S.score_out, sh.sel, P.table, P.table_stride, S.rows);
+      return;
+    }
+    bid -= S.sel.n_wgs;
   }
-  bid -= S.sel.n_wgs;
   if (bid < B.n_seal) {
     seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
     return;
@@ -171,7 +225,7 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
   const int nch = S.first_b[r + 1] - S.first_b[r];
   const Req R = B.r[r];
   int x0, x1;
-  chunk_range(keys_b(R, S.k), nch, w, x0, x1);
+  chunk_range(keys_b(R, S.k, 0), nch, w, x0, x1);
   const int sn = sealed_now(R);
   const int32_t* rows = S.rows + (int64_t)r * S.k;
   const int64_t max_row = (int64_t)P.max_blocks * kC4;
@@ -201,8 +255,13 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
   const int fa = S.first_a[r], ca = S.first_a[r + 1] - fa;
   const int fb = S.first_b[r], cb = S.first_b[r + 1] - fb;
   const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
+  const Req R = B.r[r];
+  ExtraKey xk{nullptr, nullptr, nullptr};
+  if (S.fused && R.aux >= 0)   // the HCA entry of the block sealed now, merged in S2
+    xk = ExtraKey{P.hca_k + (int64_t)R.aux * kRow, P.hca_v + (int64_t)R.aux * kRow,
+                  S.q + (int64_t)r * kRow};
   merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
-                 h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow);
+                 h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow, xk);
 }
 
 }  // namespace
@@ -216,20 +275,20 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = S.sel.n_wgs + B.n_seal + S.n_a;
+  const int grid = (S.fused ? S.n_b : S.sel.n_wgs) + B.n_seal + S.n_a;
   if (grid == 0) return hipSuccess;
   return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
 }
 
 hipError_t launch_step2b(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                          const LaunchEv& ev) {
-  if (B.n == 0 || S.sel.gmax <= 1) return hipSuccess;
+  if (B.n == 0 || S.fused || S.sel.gmax <= 1) return hipSuccess;
   return launch_k(k_step2b, dim3(B.n), dim3(kSelThreads), st, ev, P, B, S);
 }
 
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  if (S.n_b == 0) return hipSuccess;
+  if (S.n_b == 0 || S.fused) return hipSuccess;
   return launch_k(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), st, ev, P, B, S);
 }
 

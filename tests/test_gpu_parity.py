@@ -198,8 +198,11 @@ def _decode_batch(cache, o, states, keys, seed, k, check_scores=True, sorted=Fal
     return gidx
 
 
-def test_ragged_batch_over_64_requests():
-    """70 requests (two launch batches), lengths 1..1500, 4 decode steps."""
+@pytest.mark.parametrize("fused", ["0", "1"])
+def test_ragged_batch_over_64_requests(monkeypatch, fused):
+    """70 requests (two launch batches), lengths 1..1500, 4 decode steps, with the
+    decode step in four launches and in three."""
+    monkeypatch.setenv("HSA_STEP_FUSED", fused)
     seed = 0x5150
     rng = np.random.default_rng(seed)
     B = 70
@@ -412,12 +415,16 @@ def test_errors_change_nothing_on_device():
     assert np.array_equal(idx.cpu().numpy()[0], o.topk(0, hqi[0], 40)[0])
 
 
-def test_decode_step_matches_separate_calls():
-    """The four-launch decode step equals append_kv + indexer_topk + decode_attend:
-    same block tables and State, bit-identical blocks and top-k, attention equal to
-    fp32 rounding (only the order of the softmax sum differs)."""
+@pytest.mark.parametrize("fused", ["0", "1"])
+def test_decode_step_matches_separate_calls(monkeypatch, fused):
+    """The decode step, in four launches or in three (part-B workgroups selecting
+    for themselves, several per request so each writes a share of the top-k row),
+    equals append_kv + indexer_topk + decode_attend: same block tables and State,
+    bit-identical blocks, top-k ordinals and scores (sorted and unsorted), attention
+    equal to fp32 rounding (only the order of the softmax sum differs)."""
     import torch
     import heterogeneous_sparse_attention_amd as hsa
+    monkeypatch.setenv("HSA_STEP_FUSED", fused)
     seed = 0x4455
     Wc, Wh = synth.gate_weights(seed)
     rng = np.random.default_rng(seed)
@@ -435,13 +442,17 @@ def test_decode_step_matches_separate_calls():
     b.append_kv(sb, cu, K, V, KI)
     for step in range(3):
         p = L0 + step
+        srt = step == 1
         Kn, Vn, KIn = dev_tokens(seed, np.arange(B), p)
         Q, QI = dev_queries(seed, np.arange(B), p)
-        ta, _, oa = a.decode_step(sa, Kn, Vn, KIn, Q, QI, k)
+        sa_sc = torch.full((B, k), 7.0, dtype=torch.float32, device="cuda")
+        sb_sc = torch.full((B, k), 7.0, dtype=torch.float32, device="cuda")
+        ta, _, oa = a.decode_step(sa, Kn, Vn, KIn, Q, QI, k, score_out=sa_sc, sorted=srt)
         b.append_kv(sb, np.arange(B + 1), Kn, Vn, KIn)
-        tb, _ = b.indexer_topk(sb, QI, k)
+        tb, _ = b.indexer_topk(sb, QI, k, score_out=sb_sc, sorted=srt)
         ob = b.decode_attend(sb, Q, tb, k)
-        assert torch.equal(ta, tb)
+        assert torch.equal(ta, tb), step
+        assert torch.equal(sa_sc, sb_sc), step
         assert rel_l2(oa.cpu().numpy(), ob.cpu().numpy()) <= 1e-5
     for x, y in zip(sa, sb):
         assert a.block_table(x) == b.block_table(y)
