@@ -57,6 +57,12 @@ __device__ __forceinline__ const uint16_t* lane_ptr(uint64_t p, int i) {
 template <int WAVES>
 constexpr int ring_depth() { return WAVES > 4 ? 4 : 5; }
 
+// Ring of the three-launch decode step's attention (8 waves, one workgroup per CU):
+// one key in flight per wave while another is consumed. On the b32 workload this
+// measured faster than 3 or 4: with every CU streaming, fewer requests in flight
+// gather random rows from HBM at a higher rate.
+constexpr int kMixedRing = 2;
+
 struct KeyRegs {
   uint4 k[4];
   uint4 v[4];
@@ -92,6 +98,43 @@ __device__ __forceinline__ void compute_key(const KeyRegs& R, bool ok, const uin
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p, vf[i], acc[c][i] * sc);
     m[c] = mx;
+  }
+}
+
+// Merge the waves' running softmax states in LDS. On return threads t < 256 hold
+// head t/16, dims (t%16)*8 .. +8 of the workgroup's unnormalised result.
+template <int WAVES>
+__device__ __forceinline__ void merge_waves(const float* m, const float* l, const float (*acc)[8],
+                                            AttnSharedT<WAVES>& sh, float& M, float& L, float* A8) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int h = 4 * c + (lane >> 4);
+    float4* dst = reinterpret_cast<float4*>(&sh.acc[wave][h * kD + (lane & 15) * 8]);
+    dst[0] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+    dst[1] = make_float4(acc[c][4], acc[c][5], acc[c][6], acc[c][7]);
+    if ((lane & 15) == 0) {
+      sh.m[wave][h] = m[c];
+      sh.l[wave][h] = l[c];
+    }
+  }
+  __syncthreads();
+  const int h = (tid >> 4) & (kH - 1);
+  const int d0 = (tid & 15) * 8;
+  M = kNoMax;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sh.m[v][h]);
+  L = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) A8[i] = 0.f;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    const float wgt = exp2f(sh.m[v][h] - M);
+    L = fmaf(wgt, sh.l[v][h], L);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A8[i] = fmaf(wgt, sh.acc[v][h * kD + d0 + i], A8[i]);
   }
 }
 
@@ -146,34 +189,96 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
       }
     }
   }
-  // merge the four waves in LDS
+  merge_waves<WAVES>(m, l, acc, sh, M, L, A8);
+}
+
+// Attention of one workgroup over two key lists of one request, A = [a0, a1) and
+// B = [b0, b1): each wave streams a contiguous share of each, its A keys first, in
+// one online softmax. The addresses of the B keys are known only after mid(),
+// work that every wave of the workgroup runs once (it may hold barriers and must
+// issue no global load). The first RING - 1 keys of each wave are A keys where
+// it has them, and their loads are issued before mid(), so they arrive while mid()
+// runs; pre() runs just before those loads are issued (work that should wait for
+// earlier loads first). key_a / key_b return the rows of a key or nullptrs for a
+// skipped slot; dummy_k / dummy_v are valid rows read in their place. Result as
+// attend_keys.
+template <int WAVES, int RING, class KeyA, class KeyB, class Pre, class Mid>
+__device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_b, int b0, int b1, Pre pre, Mid mid,
+                                           const uint16_t* qrow, const uint16_t* dummy_k,
+                                           const uint16_t* dummy_v, AttnSharedT<WAVES>& sh, float& M,
+                                           float& L, float* A8) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int pa = (a1 - a0 + WAVES - 1) / WAVES;
+  const int wa0 = a0 + wave * pa;
+  const int na = max(0, min(wa0 + pa, a1) - wa0);
+  const int pb = (b1 - b0 + WAVES - 1) / WAVES;
+  const int wb0 = b0 + wave * pb;
+  const int nbk = max(0, min(wb0 + pb, b1) - wb0);
+  const int n = na + nbk;   // the wave's keys: j < na is A key wa0 + j, else B key wb0 + j - na
+
+  uint4 qw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qw[c] = load_global(reinterpret_cast<const uint4*>(qrow + c * 512) + lane);
+  float m[4], l[4], acc[4][8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int h = 4 * c + (lane >> 4);
-    float4* dst = reinterpret_cast<float4*>(&sh.acc[wave][h * kD + (lane & 15) * 8]);
-    dst[0] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-    dst[1] = make_float4(acc[c][4], acc[c][5], acc[c][6], acc[c][7]);
-    if ((lane & 15) == 0) {
-      sh.m[wave][h] = m[c];
-      sh.l[wave][h] = l[c];
+    m[c] = kNoMax;
+    l[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
+  }
+  auto key_j = [&](int j) { return j < na ? key_a(wa0 + j) : key_b(wb0 + j - na); };
+
+  // group 0: A addresses, then the prefetch of the first RING - 1 keys (every load
+  // issued, dummy rows where a slot has no A key)
+  const int n0 = min(64, n);
+  KeyAddr a;
+  a.k = a.v = nullptr;
+  if (lane < n0 && lane < na) a = key_a(wa0 + lane);
+  bool okl = a.k != nullptr;
+  uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
+  uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
+  KeyRegs ring[RING];
+  pre();
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane);
+  mid();
+  if (lane < n0 && lane >= na) {
+    a = key_b(wb0 + lane - na);
+    okl = a.k != nullptr;
+    kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
+    vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
+  }
+  uint64_t okmask = __ballot(okl);
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u)
+    if (u >= na && u < n0) load_key(ring[u], kp, vp, u, lane);   // slots that held dummies
+  for (int g = 0; g < n; g += 64) {
+    const int ng = min(64, n - g);
+    if (g > 0) {
+      a.k = a.v = nullptr;
+      if (lane < ng) a = key_j(g + lane);
+      okl = a.k != nullptr;
+      okmask = __ballot(okl);
+      kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
+      vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
+#pragma unroll
+      for (int u = 0; u < RING - 1; ++u)
+        if (u < ng) load_key(ring[u], kp, vp, u, lane);
+    }
+    for (int i = 0; i < ng; i += RING) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        const int x = i + u;
+        if (x >= ng) break;
+        if (x + RING - 1 < ng) load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane);
+        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+      }
     }
   }
-  __syncthreads();
-  const int h = (tid >> 4) & (kH - 1);
-  const int d0 = (tid & 15) * 8;
-  M = kNoMax;
-#pragma unroll
-  for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sh.m[v][h]);
-  L = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) A8[i] = 0.f;
-#pragma unroll
-  for (int v = 0; v < WAVES; ++v) {
-    const float wgt = exp2f(sh.m[v][h] - M);
-    L = fmaf(wgt, sh.l[v][h], L);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) A8[i] = fmaf(wgt, sh.acc[v][h * kD + d0 + i], A8[i]);
-  }
+  merge_waves<WAVES>(m, l, acc, sh, M, L, A8);
 }
 
 // Store one partial: part_acc row [16][128] (thread t: head t/16, dims (t%16)*8),

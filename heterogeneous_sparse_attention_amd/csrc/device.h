@@ -129,8 +129,6 @@ struct StepArgs {
   float* out;            // [n][16][128] fp32
   int32_t k;
   int32_t sorted;
-  int32_t chunk_a;       // keys per part-A / part-B attention workgroup
-  int32_t chunk_b;
   int32_t n_score;       // scoring workgroups: kScoreSplit per sealed block
   int32_t n_a;           // part-A workgroups
   int32_t n_b;           // part-B workgroups
@@ -159,18 +157,37 @@ __device__ __forceinline__ void chunk_range(int n, int c, int w, int& x0, int& x
 
 // ---------------------------------------------------------------- helpers
 
+// Global-memory view of a pointer: accesses through it are global (not flat)
+// instructions, which count only on the vector-memory counter, so waits for LDS
+// operations do not also wait for them.
+#define HSA_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ HSA_GLOBAL T* as_global(T* p) {
+  return (HSA_GLOBAL T*)p;
+}
+
 // Streaming loads for data a step reads once (indexer keys, attention K/V rows):
 // non-temporal, so they do not displace lines that are reused.
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 load_stream(const float4* p) {
-  const f32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_v*>(p));
+  const f32x4_v v = __builtin_nontemporal_load(as_global(reinterpret_cast<const f32x4_v*>(p)));
   return make_float4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  const u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(p));
+  const u32x4_v v = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x4_v*>(p)));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Plain loads as global instructions.
+__device__ __forceinline__ uint4 load_global(const uint4* p) {
+  const u32x4_v v = *as_global(reinterpret_cast<const u32x4_v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_global(const float4* p) {
+  const f32x4_v v = *as_global(reinterpret_cast<const f32x4_v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ int32_t load_global(const int32_t* p) { return *as_global(p); }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <queue>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -65,12 +66,10 @@ struct hsa_ctx {
   std::vector<Rec> recs;
 
   int32_t attend_wgs = 512;   // attention workgroups per launch to aim for (one round)
-  int32_t step_a_wgs = 256;   // decode step: part-A attention workgroups (8 waves each) to aim for
-  int32_t step_b_wgs = 256;   // decode step: part-B attention workgroups to aim for
+  int32_t step_slots = 256;   // decode step: attention workgroups one launch holds at once
+                              // (one per CU at the step kernels' register use)
   int32_t select_slice = kSliceN;   // top-k: longer score rows are selected in two rounds
   int32_t step_fused = 1;     // decode step in three launches when every row fits the LDS cache
-  int32_t fused_a_wgs = 96;   // three-launch step: part-A / part-B workgroups to aim for
-  int32_t fused_b_wgs = 160;
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
   int32_t* cand_ord = nullptr;  // top-k of sliced rows: per-slice candidates (ordinals, scores)
@@ -81,11 +80,8 @@ struct hsa_ctx {
   hsa_ctx(int32_t n_win, int32_t ms, int64_t mb, int64_t bps) : ctl(n_win, ms, mb, bps) {
     // launch-shape targets; the environment can override them for tuning sweeps
     if (const char* e = std::getenv("HSA_ATTEND_WGS")) attend_wgs = std::max(16, std::atoi(e));
-    if (const char* e = std::getenv("HSA_STEP_A_WGS")) step_a_wgs = std::max(16, std::atoi(e));
-    if (const char* e = std::getenv("HSA_STEP_B_WGS")) step_b_wgs = std::max(16, std::atoi(e));
+    if (const char* e = std::getenv("HSA_STEP_SLOTS")) step_slots = std::max(16, std::min(1 << 16, std::atoi(e)));
     if (const char* e = std::getenv("HSA_STEP_FUSED")) step_fused = std::atoi(e) != 0;
-    if (const char* e = std::getenv("HSA_FUSED_A_WGS")) fused_a_wgs = std::max(16, std::atoi(e));
-    if (const char* e = std::getenv("HSA_FUSED_B_WGS")) fused_b_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_SELECT_SLICE"))   // a multiple of 32, at least 32
       select_slice = std::max(32, std::min(1 << 24, std::atoi(e)) / 32 * 32);
   }
@@ -366,8 +362,49 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
   return kOk;
 }
 
-// The decode step (committed one-token append + top-k + attention) in four launches
-// per batch of kMaxReq requests.
+// Attention workgroups per request for the parts that share one launch. A request
+// gets one workgroup per part it has keys in (and at least min_wgs); the launch's
+// remaining slots go one at a time to the (part, request) whose workgroups are
+// estimated to finish last, the estimate being lat + keys / workgroups in units of
+// keys streamed (lat: what a part does before its first key). No workgroup is left
+// with fewer than kMinKeys keys.
+constexpr int64_t kMinKeys = 16;
+
+struct AttnPart {
+  const std::vector<int64_t>* keys;
+  int64_t lat;
+  int32_t min_wgs;
+  std::vector<int64_t> wgs;
+};
+
+void balance_wgs(const std::vector<AttnPart*>& parts, int64_t slots) {
+  using Item = std::pair<double, std::pair<int, int>>;
+  std::priority_queue<Item> pq;
+  int64_t used = 0;
+  auto can_split = [](int64_t keys, int64_t w) { return keys >= kMinKeys * (w + 1); };
+  for (int p = 0; p < (int)parts.size(); ++p) {
+    AttnPart& a = *parts[p];
+    a.wgs.assign(a.keys->size(), 0);
+    for (int i = 0; i < (int)a.keys->size(); ++i) {
+      const int64_t k = (*a.keys)[i];
+      a.wgs[i] = std::max<int64_t>(k > 0 ? 1 : 0, a.min_wgs);
+      used += a.wgs[i];
+      if (a.wgs[i] > 0 && can_split(k, a.wgs[i])) pq.push({a.lat + (double)k / a.wgs[i], {p, i}});
+    }
+  }
+  while (used < slots && !pq.empty()) {
+    const auto pi = pq.top().second;
+    pq.pop();
+    AttnPart& a = *parts[pi.first];
+    const int64_t k = (*a.keys)[pi.second];
+    const int64_t w = ++a.wgs[pi.second];
+    ++used;
+    if (can_split(k, w)) pq.push({a.lat + (double)k / w, pi});
+  }
+}
+
+// The decode step (committed one-token append + top-k + attention) in three or four
+// launches per batch of kMaxReq requests.
 int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const void* v_new,
                     const float* idx_new, const void* q, const float* q_idx, int32_t k,
                     uint32_t flags, int32_t* topk_out, float* score_out, float* out,
@@ -379,13 +416,14 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
     ReqBatch B{};
     B.n = n;
-    // three launches when every score row fits the selection's LDS cache: part-B
-    // workgroups then select for themselves and the new HCA key joins the merge
-    bool fused = c->step_fused != 0;
+    // three launches when every score row fits the selection's LDS cache (and the
+    // top-k is wanted in ordinal order): every attention workgroup then selects for
+    // itself and the new HCA key joins the merge
+    bool fused = c->step_fused != 0 && !(flags & HSA_TOPK_SORTED);
     for (int i = 0; i < n; ++i)
       fused = fused && (int64_t)kC4 * plan.reqs[b0 + i].nb_new <= kCacheN;
     std::vector<int64_t> na(n), nb(n);
-    int64_t keys_a = 0, keys_b = 0, maxnb = 0, n_score = 0;
+    int64_t maxnb = 0, n_score = 0;
     for (int i = 0; i < n; ++i) {
       const AppendReq& r = plan.reqs[b0 + i];
       const int32_t id = new_id[b0 + i];
@@ -394,8 +432,6 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       const int64_t sealed = id >= 0 ? 1 : 0;
       na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + r.nb_new - sealed;
       nb[i] = (fused ? 0 : sealed) + std::min<int64_t>(k, (int64_t)kC4 * r.nb_new);
-      keys_a += na[i];
-      keys_b += nb[i];
       maxnb = std::max<int64_t>(maxnb, r.nb_new);
       n_score += (int64_t)kScoreSplit * r.nb_new;
     }
@@ -412,17 +448,32 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.k = k;
     S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
     S.fused = fused ? 1 : 0;
-    S.chunk_a = attend_chunk(keys_a, n, fused ? c->fused_a_wgs : c->step_a_wgs);
-    S.chunk_b = attend_chunk(keys_b, n, fused ? c->fused_b_wgs : c->step_b_wgs);
     S.n_score = (int32_t)n_score;
+    int s = kOk;
+    if (!fused) {
+      s = plan_select(c, B, k, S.sel);
+      if (s) return s;
+    }
+    // workgroups: three-launch form, each S2 workgroup takes a share of both parts
+    // of one request (at least one per request: it writes the top-k padding);
+    // four-launch form, part A shares S2 with the selections, part B has S3
+    std::vector<int64_t> nab(n);
+    for (int i = 0; i < n; ++i) nab[i] = na[i] + nb[i];
+    AttnPart pa{&na, 0, 0, {}}, pb{fused ? &nab : &nb, 0, fused ? 1 : 0, {}};
+    if (fused) {
+      balance_wgs({&pb}, c->step_slots - B.n_seal);
+      pa.wgs.assign(n, 0);
+    } else {
+      balance_wgs({&pa}, c->step_slots - S.sel.n_wgs - B.n_seal);
+      balance_wgs({&pb}, c->step_slots);
+    }
     int64_t ta = 0, tb = 0, ts = 0;
     for (int i = 0; i < n; ++i) {
       S.first_a[i] = (int32_t)ta;
       S.first_b[i] = (int32_t)tb;
       S.first_s[i] = (int32_t)ts;
-      ta += (na[i] + S.chunk_a - 1) / S.chunk_a;
-      // fused: at least one part-B workgroup per request, which writes the top-k padding
-      tb += std::max<int64_t>(fused ? 1 : 0, (nb[i] + S.chunk_b - 1) / S.chunk_b);
+      ta += pa.wgs[i];
+      tb += pb.wgs[i];
       ts += (int64_t)kScoreSplit * B.r[i].nb;
     }
     S.first_a[n] = (int32_t)ta;
@@ -431,8 +482,9 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.n_a = (int32_t)ta;
     S.n_b = (int32_t)tb;
 
-    int s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(S.ld * n),
-                 sizeof(float));
+    // (+16: the three-launch selection reads one float4 at the start of every row)
+    s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(S.ld * n + 16),
+             sizeof(float));
     if (s) return s;
     s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)(ta + tb + n),
              kRow * sizeof(float));
@@ -442,10 +494,6 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     if (s) return s;
     s = grow(c, reinterpret_cast<void**>(&c->rows), &c->rows_cap, (size_t)n * k, sizeof(int32_t));
     if (s) return s;
-    if (!fused) {
-      s = plan_select(c, B, k, S.sel);
-      if (s) return s;
-    }
     S.rows = c->rows;
     S.scores = c->scores;
     S.part_acc = c->part_acc;
@@ -507,6 +555,11 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   const int64_t bps = cfg->max_blocks_per_state ? cfg->max_blocks_per_state : cfg->max_blocks;
   hsa_ctx* c = new hsa_ctx(cfg->n_win, cfg->max_states, cfg->max_blocks, bps);
   c->device = device;
+  if (!std::getenv("HSA_STEP_SLOTS")) {   // one step-kernel workgroup per CU
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n_cu > 0)
+      c->step_slots = n_cu;
+  }
   const size_t S = (size_t)cfg->max_states, NB = (size_t)cfg->max_blocks, W = (size_t)cfg->n_win;
   void* p[11] = {};
   const size_t bytes[11] = {
@@ -539,10 +592,11 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   c->P.n_win = cfg->n_win;
   c->P.max_blocks = (int32_t)cfg->max_blocks;
   c->seal_part = static_cast<float*>(p[10]);
-  // attention partials: a launch has at most max(64, target - n) + n <= target + 64
-  // chunks per part, so these never grow (no device synchronisation in a decode loop)
+  // attention partials: a decode step has at most max(slots, requests) workgroups per
+  // part, and hsa_decode_attend at most max(64, target - n) + n <= target + 64, so
+  // these never grow (no device synchronisation in a decode loop)
   {
-    const size_t chunks = std::max<size_t>((size_t)c->step_a_wgs + c->step_b_wgs + 3 * kMaxReq,
+    const size_t chunks = std::max<size_t>(2 * ((size_t)c->step_slots + kMaxReq),
                                            (size_t)c->attend_wgs + kMaxReq);
     st = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, chunks, kRow * sizeof(float));
     if (st == kOk)

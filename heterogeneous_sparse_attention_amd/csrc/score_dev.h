@@ -68,7 +68,7 @@ struct SelShared {
   uint32_t hist[3][kBins];
   unsigned long long cand[kMaxTopk];
   int32_t tab[kTabCache];
-  int sh[2];
+  int sh[3];
   int cnt[2][2][kSelWaves];   // [parity][above tau, equal to tau][wave]
 };
 
@@ -407,5 +407,173 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
   }
 }
 
+
+// ---------------------------------------------------------------- selection from LDS
+//
+// For a row of at most kCacheN scores whose workgroup prefetches attention keys
+// before selecting: the row is first loaded into registers, so the selection that
+// follows issues no global load. Global loads complete in order, so a load issued
+// after the prefetch would wait for all of it.
+
+template <int NT>
+struct SelPre {
+  float4 s[kCacheN / 4 / NT];
+  int32_t tab;
+};
+
+// Load row S (N scores, N a multiple of 32, at most kCacheN) and table entry t < nb
+// of the state. Every load is issued: out-of-row indexes read the row's first float4
+// (16 readable bytes are kept there) or table entry 0, and are ignored.
+template <int NT>
+__device__ __forceinline__ void sel_preload(int N, const float* S, const int32_t* tab, int nb,
+                                            SelPre<NT>& pre) {
+  static_assert(kCacheN % (4 * NT) == 0 && NT >= kCacheN / kC4 && NT <= kTabCache,
+                "selection preload shape");
+  const int tid = threadIdx.x;
+  const float4* S4 = reinterpret_cast<const float4*>(S);
+#pragma unroll
+  for (int q = 0; q < kCacheN / 4 / NT; ++q) {
+    const int i = tid + q * NT;
+    pre.s[q] = load_global(S4 + (i < N / 4 ? i : 0));
+  }
+  pre.tab = load_global(tab + (tid < nb ? tid : 0));
+}
+
+// Top-k of the staged row (N scores, N / 32 blocks) by one workgroup of NT threads,
+// in ascending ordinal order, writing what `win` asks for (ordinals and
+// scores when win.io; physical C4 rows of window positions into rows[x - win.x0]).
+// Same selection as select_run: radix passes of 11, 11 and 10 bits over the
+// order-preserving keys find the cut; the passes stop early once the bucket at the
+// cut is taken whole. One ordered pass then takes every key above the cut and the
+// first `rem` keys at it: each thread owns a run of consecutive keys, and one
+// workgroup-wide prefix count gives every run its output position.
+// Stage the preloaded row in LDS as order-preserving keys, with the table entries,
+// and clear the histograms; this waits for the row's loads. Every thread writes its
+// slots unconditionally (entries past the row are never read). The first barrier of
+// select_lds publishes the writes.
+template <int NT>
+__device__ __forceinline__ void select_stage(const SelPre<NT>& pre, SelShared& sh) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kCacheN / 4 / NT; ++q) {
+    const int i = tid + q * NT;
+    const float4 v = pre.s[q];
+    *reinterpret_cast<uint4*>(&sh.keys[4 * i]) = make_uint4(okey(v.x), okey(v.y), okey(v.z), okey(v.w));
+  }
+  sh.tab[tid] = pre.tab;
+  for (int b = tid; b < 3 * kBins; b += NT) (&sh.hist[0][0])[b] = 0u;
+}
+
+template <int NT>
+__device__ __forceinline__ void select_lds(int N, int32_t k, int32_t* io, float* so, SelShared& sh,
+                                           int32_t* rows, SelWin win) {
+  constexpr int NW = NT / 64;
+  constexpr int PMAX = kCacheN / NT;   // keys per thread in the ordered pass, at most
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int kk = min(k, N);
+  HSA_GLOBAL int32_t* gio = as_global(io);
+  HSA_GLOBAL float* gso = so ? as_global(so) : nullptr;
+  if (kk > 0) {
+    __syncthreads();   // the staged row
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = kk;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+      uint32_t* hist = sh.hist[pass];
+      for (int i = tid; i < N; i += NT) {
+        const uint32_t u = sh.keys[i];
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds digits 2047-32l down to 2016-32l
+        const uint4* h4 = reinterpret_cast<const uint4*>(hist + kBins - 32 * (tid + 1));
+        uint32_t tot = 0u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint4 v = h4[q];
+          tot += v.x + v.y + v.z + v.w;
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(incl, o);
+          if (tid >= o) incl += y;
+        }
+        const unsigned long long bal = __ballot(incl >= (uint32_t)rem);
+        const int first = (int)__ffsll((long long)bal) - 1;
+        const uint32_t base = __shfl(incl - tot, first);
+        const int d = kBins - 1 - 32 * first - (tid & 31);
+        const uint32_t c = tid < 32 ? hist[d] : 0u;
+        uint32_t ci = c;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+          const uint32_t y = __shfl_up(ci, o);
+          if ((tid & 31) >= o) ci += y;
+        }
+        const unsigned long long b2 = __ballot(tid < 32 && base + ci >= (uint32_t)rem);
+        const int dl = (int)__ffsll((long long)b2) - 1;
+        if (tid == dl) {
+          sh.sh[0] = d;
+          sh.sh[1] = (int)(base + ci - c);
+          sh.sh[2] = (int)c;
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sh.sh[0] << shift;
+      pmask |= dmask << shift;
+      rem -= sh.sh[1];
+      if (sh.sh[2] == rem) break;   // every key of the cut's bucket is taken (uniform)
+    }
+    // ordered pass over runs of consecutive keys
+    const int run = (N + NT - 1) / NT;
+    const int i0 = tid * run;
+    uint32_t e[PMAX];
+    int g = 0, q_eq = 0;
+#pragma unroll
+    for (int j = 0; j < PMAX; ++j) {
+      const bool ok = j < run && i0 + j < N;
+      e[j] = ok ? sh.keys[i0 + j] : 0u;
+      g += ok && (e[j] & pmask) > prefix;
+      q_eq += ok && (e[j] & pmask) == prefix;
+    }
+    int tot;
+    int before = wave_excl_scan((g << 16) | q_eq, tot);
+    if (lane == 0) sh.cnt[0][0][wv] = tot;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) before += w < wv ? sh.cnt[0][0][w] : 0;
+    int gb = before >> 16, eb = before & 0xffff;
+#pragma unroll
+    for (int j = 0; j < PMAX; ++j) {
+      if (j < run && i0 + j < N) {
+        const uint32_t m = e[j] & pmask;
+        const bool gt = m > prefix, eq = m == prefix;
+        if (gt || (eq && eb < rem)) {
+          const int pos = gb + min(eb, rem);
+          if (pos >= win.x0 && pos < win.x1) {
+            const int32_t i = i0 + j;
+            if (win.io) {
+              gio[pos] = i;
+              if (gso) gso[pos] = okey_inv(e[j]);
+            }
+            rows[pos - win.x0] = sh.tab[i / kC4] * kC4 + i % kC4;
+          }
+        }
+        gb += gt;
+        eb += eq;
+      }
+    }
+  }
+  if (win.pad) {
+    for (int i = kk + tid; i < k; i += NT) {
+      gio[i] = -1;
+      if (gso) gso[i] = -INFINITY;
+    }
+  }
+}
 
 }  // namespace hsa

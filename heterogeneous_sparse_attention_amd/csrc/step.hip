@@ -139,43 +139,74 @@ struct Step2Shared {
   int32_t rows[kCacheN];   // three-launch part B: physical C4 rows of the workgroup's share
 };
 
-// Three-launch form, attention part B of chunk `bid`: the workgroup selects its
-// request's top-k itself (the row's at most kCacheN scores are read from L2 into
-// LDS), keeps in LDS the physical C4 rows of its own share [x0, x1) of the
-// selection, writes its share of the top-k output (its ordinals and scores, or,
-// when sorted, workgroup 0 all of them; workgroup 0 also writes the padding), then
-// attends those entries. Every part-B workgroup of a request runs the same
-// selection on the same scores, so the shares agree.
+// Three-launch form, workgroup `bid` of request r (w of nch): it attends its share
+// of both of the request's key lists, part A (SWA tokens and HCA entries of earlier
+// blocks, share chunk w of nch) and part B (the selected C4 entries, same share of
+// the selection), in one online softmax. It first loads the request's scores (at
+// most kCacheN, into registers) and issues its first part-A key loads, then runs the
+// top-k itself from LDS while those loads are in flight: it keeps in LDS the
+// physical C4 rows of its share [b0, b1) of the selection and writes the same share
+// of the top-k output (workgroup 0 also the padding). Every workgroup of a request
+// selects from the same scores, so the shares agree.
 template <int WAVES>
-__device__ __forceinline__ void part_b_fused(const Pools& P, const ReqBatch& B, const StepArgs& S,
-                                             int bid, Step2Shared& sh) {
+__device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, const StepArgs& S, int bid,
+                                           Step2Shared& sh) {
+  constexpr int NT = WAVES * 64;
   const int r = owner_of(S.first_b, B.n, bid);
   const int w = bid - S.first_b[r];
   const int nch = S.first_b[r + 1] - S.first_b[r];
   const Req R = B.r[r];
-  const int kk = keys_b(R, S.k, 1);
-  int x0, x1;
-  chunk_range(kk, nch, w, x0, x1);
-  const int64_t k = S.k;
-  select_run<WAVES * 64>(kC4 * R.nb, S.k, S.sorted, S.scores + (int64_t)r * S.ld, S.topk + r * k,
-                         S.score_out ? S.score_out + r * k : nullptr, sh.sel,
-                         P.table + (int64_t)R.state * P.table_stride, sh.rows, R.nb, 0, nullptr,
-                         SelWin{x0, x1, !S.sorted || w == 0, w == 0});
-  __syncthreads();   // rows in LDS complete; the selection's LDS is free for attention
+  const int N = kC4 * R.nb;
+  const int kk = min(S.k, N);
+  int a0, a1, b0, b1;
+  chunk_range(keys_a(P, R), nch, w, a0, a1);
+  chunk_range(kk, nch, w, b0, b1);
+  const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
+  SelPre<NT> pre;
+  sel_preload<NT>(N, S.scores + (int64_t)r * S.ld, tab, R.nb, pre);
+  __builtin_amdgcn_sched_barrier(0);   // the row's loads go out ahead of the key prefetch
+
+  const uint16_t* ring_k = P.swa_k + (int64_t)R.state * P.n_win * kRow;
+  const uint16_t* ring_v = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  const int swa = R.len < P.n_win ? R.len : P.n_win;
+  const int64_t p0 = (int64_t)R.len - swa;
+  auto key_a = [&](int x) {
+    KeyAddr a;
+    a.k = a.v = nullptr;
+    if (x < swa) {
+      const int64_t slot = (p0 + x) % P.n_win;
+      a.k = ring_k + slot * kRow;
+      a.v = ring_v + slot * kRow;
+      return a;
+    }
+    const int32_t id = load_global(tab + (x - swa));
+    if (id < 0 || id >= P.max_blocks) return a;   // never taken
+    a.k = P.hca_k + (int64_t)id * kRow;
+    a.v = P.hca_v + (int64_t)id * kRow;
+    return a;
+  };
   const int64_t max_row = (int64_t)P.max_blocks * kC4;
   auto key_b = [&](int x) {
     KeyAddr a;
     a.k = a.v = nullptr;
-    const int64_t row = sh.rows[x - x0];
+    const int64_t row = sh.rows[x - b0];
     if (row < 0 || row >= max_row) return a;   // never taken
     a.k = P.csa_k + row * kRow;
     a.v = P.csa_v + row * kRow;
     return a;
   };
-  const uint16_t* dk = P.swa_k + (int64_t)R.state * P.n_win * kRow;   // valid row (L >= 1)
-  const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  const int64_t k = S.k;
+  // the row is staged in LDS (waiting for its loads) before the key prefetch goes
+  // out, so the prefetch does not queue ahead of it
+  auto stage = [&]() { select_stage<NT>(pre, sh.sel); };
+  auto select = [&]() {
+    select_lds<NT>(N, S.k, S.topk + r * k, S.score_out ? S.score_out + r * k : nullptr, sh.sel, sh.rows,
+                   SelWin{b0, b1, true, w == 0});
+    __syncthreads();   // rows in LDS complete; the selection's LDS is free for attention
+  };
   float M, L, A8[8];
-  attend_keys<WAVES>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh.attn, M, L, A8);
+  attend_two<WAVES, kMixedRing>(key_a, a0, a1, key_b, b0, b1, stage, select,
+                                         S.q + (int64_t)r * kRow, ring_k, ring_v, sh.attn, M, L, A8);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
@@ -183,9 +214,8 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
   __shared__ Step2Shared sh;
   int bid = blockIdx.x;
   if (S.fused) {
-    // part B first: its workgroups select before they stream
     if (bid < S.n_b) {
-      part_b_fused<kStep2Waves>(P, B, S, bid, sh);
+      part_mixed<kStep2Waves>(P, B, S, bid, sh);
       return;
     }
     bid -= S.n_b;
