@@ -1,5 +1,5 @@
-// step.hip - the decode step of the heterogeneous KV cache (hsa_decode_step) as four
-// launches.
+// step.hip - the decode step of the heterogeneous KV cache (hsa_decode_step) in
+// three or four launches.
 //
 // Pages: [Q&A] "V4 为何要分池？块对齐与尾缓冲怎么配合？" §4: a new token goes to the
 // tail, a full block is compressed into the Classical pool, the SWA slides, and
@@ -11,15 +11,21 @@
 //       block. Nothing read in S1 is written in S1: the new token is read from
 //       the input wherever it is needed (last indexer key of a block sealed now,
 //       last token of the seal).
-//   S2  top-k selection over the scores (with the selected entries' physical C4
-//       rows), one workgroup per request; the HCA merge of blocks sealed in S1;
-//       and attention part A, the SWA tokens and the HCA entries of blocks sealed
-//       before this step, on the CUs the selection leaves idle.
-//   S3  attention part B: the HCA entry of the block sealed now and the selected
-//       C4 entries.
-//   S4  log-sum-exp merge of every request's part A and part B partials.
+//   S2  the HCA merge of blocks sealed in S1, the top-k over the scores, and
+//       attention. Part A of the keys (the SWA tokens and the HCA entries of
+//       blocks sealed before this step) needs no top-k; part B (the selected C4
+//       entries, and the HCA entry of the block sealed now) does.
+//   S4  log-sum-exp merge of every request's attention partials.
 //
-// Part A does not depend on the top-k, so it streams while the selection runs.
+// Three-launch form (every score row fits the selection's LDS cache, top-k in
+// ordinal order): each S2 attention workgroup takes a share of both parts of one
+// request, loads the request's score row, starts loading its first part-A keys,
+// runs the top-k itself from LDS and then streams its keys; S4 also takes the
+// HCA entry of the block sealed now as one more key.
+// Four-launch form (long rows, or sorted top-k output): S2 runs the selections
+// (one workgroup per row, or per slice of a long row with a second round in
+// S2b) beside part A; S3 attends part B through the physical C4 rows S2 wrote.
+//
 // Key order differs from hsa_decode_attend only in the order of the softmax sum.
 #include "attn_dev.h"
 #include "device.h"
