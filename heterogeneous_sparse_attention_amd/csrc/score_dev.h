@@ -410,6 +410,19 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
 
 // ---------------------------------------------------------------- selection from LDS
 //
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4
+// and 8 lanes within each row of 16, then the row totals carried forward with the
+// row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+//
 // For a row of at most kCacheN scores whose workgroup prefetches attention keys
 // before selecting: the row is first loaded into registers, so the selection that
 // follows issues no global load. Global loads complete in order, so a load issued
@@ -497,23 +510,13 @@ __device__ __forceinline__ void select_lds(int N, int32_t k, int32_t* io, float*
           const uint4 v = h4[q];
           tot += v.x + v.y + v.z + v.w;
         }
-        uint32_t incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(incl, o);
-          if (tid >= o) incl += y;
-        }
+        const uint32_t incl = wave_incl_scan_dpp(tot);
         const unsigned long long bal = __ballot(incl >= (uint32_t)rem);
-        const int first = (int)__ffsll((long long)bal) - 1;
-        const uint32_t base = __shfl(incl - tot, first);
+        const int first = uniform((int)__ffsll((long long)bal) - 1);
+        const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(incl - tot), first);
         const int d = kBins - 1 - 32 * first - (tid & 31);
         const uint32_t c = tid < 32 ? hist[d] : 0u;
-        uint32_t ci = c;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          const uint32_t y = __shfl_up(ci, o);
-          if ((tid & 31) >= o) ci += y;
-        }
+        const uint32_t ci = wave_incl_scan_dpp(c);   // lanes 32..63 add zeros
         const unsigned long long b2 = __ballot(tid < 32 && base + ci >= (uint32_t)rem);
         const int dl = (int)__ffsll((long long)b2) - 1;
         if (tid == dl) {
@@ -540,9 +543,10 @@ __device__ __forceinline__ void select_lds(int N, int32_t k, int32_t* io, float*
       g += ok && (e[j] & pmask) > prefix;
       q_eq += ok && (e[j] & pmask) == prefix;
     }
-    int tot;
-    int before = wave_excl_scan((g << 16) | q_eq, tot);
-    if (lane == 0) sh.cnt[0][0][wv] = tot;
+    const int packed = (g << 16) | q_eq;
+    const int incl = (int)wave_incl_scan_dpp((uint32_t)packed);
+    int before = incl - packed;
+    if (lane == 63) sh.cnt[0][0][wv] = incl;
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) before += w < wv ? sh.cnt[0][0][w] : 0;
