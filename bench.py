@@ -7,7 +7,10 @@ SWA + HCA + selected C4 entries (hsa_decode_step). Inputs are synthetic and
 resident in HBM before timing starts.
 
   python bench.py [--steps K] [--warmup W] [--workload 2]
-prints one JSON line. Other modes (for the profiles):
+prints one JSON line. The default is the headline workload, b32 (2). The other
+workloads time the same step at their own shapes (1 l130, 3 prefix, 5 long) or,
+for 4 (bulk), whole append calls of 8 x 131072 tokens with fused seal.
+Other modes (for the profiles):
   python bench.py --copy-calibration      a plain copy kernel of known size
   python bench.py --counters DIR          summarise rocprofv3 --pmc output
 """
@@ -32,17 +35,21 @@ import synth  # noqa: E402
 from synth import workloads  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "decode tokens/s + achieved HBM GB/s (% of peak), append+attend, B=32 L<=8K"
+LENGTHS = {"l130": "L0 = 130", "b32": "L0 ~ U{1..8192}",
+           "prefix": "L0 ~ U{16384..65536}, 8 groups sharing a 32768-token prefix by fork",
+           "bulk": "131072 tokens each", "long": "L0 = 2**20 - 8"}
 ROW = 8192                     # K + V bytes of one token or entry (2 x 16 x 128 bf16)
 IDX_BLOCK = 131072             # indexer keys of one block (128 x 4 x 64 fp32)
 SEAL_BYTES = 1581056           # per seal: read 128 tokens K/V + 128 indexer keys, write 32 C4 + 1 HCA + 128 keys
 KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
                  "attend": "k_attend", "merge": "k_merge", "seal": "k_seal_merge",
                  "write": "k_bulk_write", "step1": "k_step1", "step2": "k_step2",
-                 "step3": "k_step3", "step4": "k_step4"}
+                 "step2b": "k_step2b", "step3": "k_step3", "step4": "k_step4"}
 STEP_SOURCES = ["step.hip", "attn_dev.h", "score_dev.h", "seal_dev.h", "device.h"]
-KERNEL_SOURCES = {"step1": STEP_SOURCES, "step2": STEP_SOURCES, "step3": STEP_SOURCES,
-                  "step4": STEP_SOURCES}
-STEP_KERNELS = ("step1", "step2", "step3", "step4")
+KERNEL_SOURCES = {"step1": STEP_SOURCES, "step2": STEP_SOURCES, "step2b": STEP_SOURCES,
+                  "step3": STEP_SOURCES, "step4": STEP_SOURCES}
+STEP_KERNELS = ("step1", "step2", "step2b", "step3", "step4")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -73,6 +80,7 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
             # of the SWA tokens, earlier HCA entries and selected C4 entries + the query
             "step2": int((kk * 8).sum() + sealed.sum() * ROW
                          + ((swa + nb - sealed + kk) * ROW).sum() + B * 4096),
+            "step2b": 0,
             "step3": 0,
             # S4: the new HCA entries (K/V rows) and the fp32 output
             "step4": int(sealed.sum() * ROW + B * 8192),
@@ -89,6 +97,8 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
         # of the SWA tokens and earlier HCA entries + the query
         "step2": int((kk * 8).sum() + sealed.sum() * ROW
                      + ((swa + nb - sealed) * ROW).sum() + B * 4096),
+        # S2b (rows cut into slices): the second selection round reads scratch only
+        "step2b": 0,
         # S3: K/V rows of the new HCA entries and selected C4 entries, their
         # ordinals, the query
         "step3": int(((sealed + kk) * ROW).sum() + (kk * 4).sum() + B * 4096),
@@ -109,45 +119,76 @@ def src_hash(kernel: str) -> str:
 
 # ------------------------------------------------------------------ the b32 decode workload
 
+def _append_device(cache, wl, states, reqs, p0s, p1s, chunk=65536):
+    """Append positions [p0, p1) of workload requests `reqs` to `states`, in calls of
+    at most `chunk` tokens, with inputs generated on the device (keys as the
+    workload keys them: shared-prefix positions carry their group's stream)."""
+    import torch
+    from synth.device import fill_rows
+    i = 0
+    while i < len(reqs):
+        grp, tot = [], 0
+        while i < len(reqs) and (tot + p1s[i] - p0s[i] <= chunk or not grp):
+            grp.append(i)
+            tot += p1s[i] - p0s[i]
+            i += 1
+        grp = [j for j in grp if p1s[j] > p0s[j]]
+        if not grp:
+            continue
+        pos = np.concatenate([np.arange(p0s[j], p1s[j]) for j in grp]).astype(np.int64)
+        keys = np.concatenate([wl.key(reqs[j], np.arange(p0s[j], p1s[j])) for j in grp]).astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum([p1s[j] - p0s[j] for j in grp])]).astype(np.int64)
+        T = int(cu[-1])
+        kt = torch.from_numpy(keys.astype(np.int32)).cuda()
+        pt = torch.from_numpy(pos).cuda()
+        K = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
+        V = torch.empty_like(K)
+        KI = torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")
+        fill_rows(K, wl.seed, synth.STREAM_K, keys=kt, pos=pt)
+        fill_rows(V, wl.seed, synth.STREAM_V, keys=kt, pos=pt)
+        fill_rows(KI, wl.seed, synth.STREAM_IDXK, keys=kt, pos=pt)
+        cache.append_kv([states[j] for j in grp], cu, K, V, KI)
+        del K, V, KI
+
+
 def setup_decode(wl, extra_steps: int, copies: int = 1):
     """Cache holding `copies` identical instances of the batch, every request
-    prefilled to L0 (bulk append of device-generated tokens). Returns the cache and
-    one list of state ids per instance."""
+    prefilled to L0 (bulk appends of device-generated tokens; in a prefix workload
+    each request forks off its group's parent at its fork length, sharing those
+    blocks, and appends the rest itself). Returns the cache and one list of state
+    ids per instance."""
     import torch
     import heterogeneous_sparse_attention_amd as hsa
-    from synth.device import fill_rows
 
     Wc, Wh = synth.gate_weights(wl.seed)
     L0 = wl.prefill.astype(np.int64)
     B = wl.batch
     max_len = int(L0.max()) + extra_steps + 1
     max_blocks = copies * (int(((L0 + extra_steps) // 128).sum()) + B) + 8
-    cache = hsa.Cache(wl.n_win, copies * B, max_blocks, Wc, Wh, max_blocks_per_state=max_len // 128 + 2)
-    inst = [[cache.state_alloc() for _ in range(B)] for _ in range(copies)]
-    # prefill in pieces of at most 64K tokens
-    chunk = 65536
-    order = [(c, b) for c in range(copies) for b in range(B)]
-    i = 0
-    while i < len(order):
-        grp, tot = [], 0
-        while i < len(order) and (tot + int(L0[order[i][1]]) <= chunk or not grp):
-            grp.append(order[i])
-            tot += int(L0[order[i][1]])
-            i += 1
-        sts = [inst[c][b] for c, b in grp]
-        grp = [b for _, b in grp]
-        cu = np.concatenate([[0], np.cumsum(L0[grp])]).astype(np.int64)
-        T = int(cu[-1])
-        keys = torch.from_numpy(np.repeat(np.array(grp, np.int64), L0[grp]).astype(np.int32)).cuda()
-        pos = torch.from_numpy(np.concatenate([np.arange(L0[b]) for b in grp]).astype(np.int64)).cuda()
-        K = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
-        V = torch.empty_like(K)
-        KI = torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")
-        fill_rows(K, wl.seed, synth.STREAM_K, keys=keys, pos=pos)
-        fill_rows(V, wl.seed, synth.STREAM_V, keys=keys, pos=pos)
-        fill_rows(KI, wl.seed, synth.STREAM_IDXK, keys=keys, pos=pos)
-        cache.append_kv(sts, cu, K, V, KI)
-        del K, V, KI
+    n_parents = wl.n_groups if wl.prefix_len else 0
+    cache = hsa.Cache(wl.n_win, copies * (B + n_parents), max_blocks + copies * n_parents * (wl.prefix_len // 128),
+                      Wc, Wh, max_blocks_per_state=max_len // 128 + 2)
+    inst = []
+    for _ in range(copies):
+        states = [None] * B
+        start = [0] * B
+        if wl.prefix_len:
+            fork = {b: wl.fork_len(b) for b in range(B)}
+            for g in range(wl.n_groups):
+                kids = sorted((b for b in range(B) if wl.group(b) == g), key=lambda b: fork[b])
+                parent, cur = cache.state_alloc(), 0
+                for b in kids:
+                    if fork[b] > cur:
+                        _append_device(cache, wl, [parent], [b], [cur], [fork[b]])
+                        cur = fork[b]
+                    states[b] = cache.state_alloc()
+                    cache.block_table_share(parent, states[b])
+                    start[b] = fork[b]
+                cache.state_free(parent)
+        else:
+            states = [cache.state_alloc() for _ in range(B)]
+        _append_device(cache, wl, states, list(range(B)), start, [int(x) for x in L0])
+        inst.append(states)
     torch.cuda.synchronize()
     return cache, inst
 
@@ -158,7 +199,8 @@ def decode_inputs(wl, L0: np.ndarray, n_steps: int):
     from synth.device import fill_rows
     B = wl.batch
     pos = (L0[None, :] + np.arange(n_steps)[:, None]).reshape(-1).astype(np.int64)
-    keys = np.tile(np.arange(B), n_steps).astype(np.int32)
+    req = np.tile(np.arange(B), n_steps)
+    keys = np.array([int(wl.key(int(b), p)) for b, p in zip(req, pos)], np.int64).astype(np.int32)
     kt = torch.from_numpy(keys).cuda()
     pt = torch.from_numpy(pos).cuda()
     n = n_steps * B
@@ -179,7 +221,8 @@ def run_decode(args) -> dict:
     import torch
     wl = workloads.make(args.workload)
     B, k = wl.batch, wl.topk
-    W, K, R = args.warmup, args.steps, args.copies
+    W, K = args.warmup, args.steps
+    R = args.copies if args.copies is not None else (4 if wl.name == "b32" else 1)
     local_steps = (W + 2 * K + R - 1) // R
     cache, inst = setup_decode(wl, local_steps, R)
     L0 = wl.prefill.astype(np.int64)
@@ -261,7 +304,7 @@ def run_decode(args) -> dict:
         pass
 
     res = {
-        "metric": "decode tokens/s + achieved HBM GB/s (% of peak), append+attend, B=32 L<=8K",
+        "metric": METRIC if wl.name == "b32" else f"decode tokens/s + achieved HBM GB/s, append+attend, {wl.name}",
         "value": B * K / (ms_total * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -273,7 +316,7 @@ def run_decode(args) -> dict:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: {B} requests, L0 ~ U{{1..8192}} (seed {wl.seed:#x}), "
+        "config": {"workload": f"{wl.name}: {B} requests, {LENGTHS[wl.name]} (seed {wl.seed:#x}), "
                                f"decode steps, n_win {wl.n_win}, top-k {k}, 16x128 bf16 K/V/Q, "
                                f"indexer 4x64 fp32, m=4, m'=128, 1 layer; steps rotate over {R} "
                                f"copies of the cache",
@@ -296,6 +339,80 @@ def run_decode(args) -> dict:
     }
     cache.close()
     return res
+
+
+def run_bulk(args) -> dict:
+    """Bulk prefill packing: every request's whole prompt appended in one call (fused
+    seal), into fresh states each time. Inputs are generated on the device first."""
+    import torch
+    import heterogeneous_sparse_attention_amd as hsa
+    from synth.device import fill_rows
+    wl = workloads.make(args.workload)
+    B = wl.batch
+    L0 = wl.prefill.astype(np.int64)
+    T = int(L0.sum())
+    Wc, Wh = synth.gate_weights(wl.seed)
+    nb = L0 // 128
+    cache = hsa.Cache(wl.n_win, B, int(nb.sum()) + B, Wc, Wh, max_blocks_per_state=int(L0.max()) // 128 + 2)
+    cu = np.concatenate([[0], np.cumsum(L0)]).astype(np.int64)
+    pos = torch.from_numpy(np.concatenate([np.arange(n) for n in L0]).astype(np.int64)).cuda()
+    keys = torch.from_numpy(np.repeat(np.arange(B), L0).astype(np.int32)).cuda()
+    K = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(K)
+    KI = torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")
+    fill_rows(K, wl.seed, synth.STREAM_K, keys=keys, pos=pos)
+    fill_rows(V, wl.seed, synth.STREAM_V, keys=keys, pos=pos)
+    fill_rows(KI, wl.seed, synth.STREAM_IDXK, keys=keys, pos=pos)
+    torch.cuda.synchronize()
+    # bytes the method must move: every token's K, V and indexer key read, every
+    # block's 32 C4 + 1 HCA entries and 128 indexer keys written, the ring's last
+    # n_win tokens and the indexer tail written
+    seal_bytes = int(nb.sum()) * (128 * (ROW + 1024) + 32 * ROW + ROW + IDX_BLOCK)
+    write_bytes = int((np.minimum(L0, wl.n_win) * 2 * ROW + (L0 % 128) * 2 * 1024).sum())
+    alg = T * (ROW + 1024) + int(nb.sum()) * (32 * ROW + ROW + IDX_BLOCK) \
+        + int((np.minimum(L0, wl.n_win) * ROW + (L0 % 128) * 1024).sum())
+    reps = max(2, args.steps)
+    times = []
+    for rep in range(reps + 1):
+        states = [cache.state_alloc() for _ in range(B)]
+        torch.cuda.synchronize()
+        if rep == reps:
+            cache.timing_enable(["seal", "write"])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.append_kv(states, cu, K, V, KI)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep > 0 and rep < reps:
+            times.append(e0.elapsed_time(e1))
+        for st in states:
+            cache.state_free(st)
+    kt = cache.timing_read()
+    cache.timing_enable([])
+    cache.close()
+    ms = float(np.median(times))
+    seal_ms = kt["seal"][0]
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {
+        "metric": f"bulk append tokens/s + achieved HBM GB/s, append+compress, {wl.name}",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": len(times), "warmup": 1,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {B} requests x {LENGTHS[wl.name]} (seed {wl.seed:#x}) in one "
+                               f"append call with fused seal, n_win {wl.n_win}; 16x128 bf16 K/V, indexer "
+                               f"4x64 fp32, m=4, m'=128, 1 layer",
+                   "batch": B, "tokens": T, "n_win": wl.n_win, "parallelism": "single GPU"},
+        "hbm_gbps": gbs, "hbm_frac_of_peak": gbs / PEAK_HBM_GBS, "bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "kernel": "k_bulk_seal",
+                     "achieved": seal_bytes / (seal_ms * 1e-3) / 1e9 if seal_ms else None,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": seal_bytes / (seal_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if seal_ms else None,
+                     "traffic": None, "avg_launch_us": seal_ms * 1e3 if seal_ms else None,
+                     "algorithmic_bytes_per_launch": seal_bytes,
+                     "measured": "HIP event pair attached to the k_bulk_seal dispatch of one call"},
+        "kernels_us_per_call": {"seal": kt["seal"][0] * 1e3, "write": kt["write"][0] * 1e3},
+        "bytes_per_call_by_kernel": {"seal": seal_bytes, "write": write_bytes},
+    }
 
 
 # ------------------------------------------------------------------ CPU baseline (the oracle)
@@ -422,9 +539,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", type=int, default=2, choices=[2])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="1 l130, 2 b32 (the headline), 3 prefix, 4 bulk append, 5 long")
     ap.add_argument("--kernel", default=None, help="time this kernel in the timed region")
-    ap.add_argument("--copies", type=int, default=4,
+    ap.add_argument("--copies", type=int, default=None,
                     help="identical cache instances the steps rotate over (defeats the 256 MB "
                          "last-level cache between steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -447,8 +565,8 @@ def main():
         copy_calibration(args)
         return
     args.warmup = max(args.warmup, 2)
-    res = run_decode(args)
-    if not args.no_cpu_baseline:
+    res = run_bulk(args) if args.workload == 4 else run_decode(args)
+    if not args.no_cpu_baseline and args.workload == 2:
         res["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(res), flush=True)
 
