@@ -27,7 +27,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 HIP_SOURCES = ["append_seal.hip", "indexer_topk.hip", "attend.hip", "step.hip", "hsa.cpp",
-               "control.cpp"]
+               "control.cpp", "launch_plan.cpp"]
 
 LIB = os.path.join(HERE, "libhsa.so")
 HOST_LIB = os.path.join(HERE, "libhsa_host.so")
@@ -74,7 +74,8 @@ def build_synth(verbose: bool = False) -> str:
 def build_host(verbose: bool = False) -> str:
     tmp = HOST_LIB + ".tmp"
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall",
-          os.path.join(CSRC, "control.cpp"), os.path.join(CSRC, "host_api.cpp"), "-o", tmp], verbose)
+          os.path.join(CSRC, "control.cpp"), os.path.join(CSRC, "launch_plan.cpp"),
+          os.path.join(CSRC, "host_api.cpp"), "-o", tmp], verbose)
     os.replace(tmp, HOST_LIB)
     return HOST_LIB
 

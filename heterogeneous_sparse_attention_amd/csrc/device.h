@@ -79,7 +79,7 @@ struct ReqBatch {
 // selected again. An entry of the row's top-k has fewer than k entries of its slice
 // ahead of it under (score desc, ordinal asc), so it is among its slice's top-k1:
 // the result is exact, ties included.
-constexpr int kSliceN = 16384;   // default slice length
+constexpr int kSliceN = 16384;   // shortest default slice
 
 struct SelPlan {
   int32_t n_wgs;                   // round-1 workgroups of the batch

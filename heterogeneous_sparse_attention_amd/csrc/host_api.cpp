@@ -4,8 +4,10 @@
 // product library links the same control.cpp.
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "control.h"
+#include "launch_plan.h"
 
 using hsa::AppendPlan;
 using hsa::Control;
@@ -82,5 +84,32 @@ int32_t hsah_table(void* c_, int32_t s, int32_t* ids, int64_t cap, int64_t* n) {
 int32_t hsah_refcount(void* c_, int64_t b) { return static_cast<Control*>(c_)->refcount(b); }
 
 int64_t hsah_free_blocks(void* c_) { return static_cast<Control*>(c_)->free_blocks(); }
+
+// Workgroup planning (launch_plan.h) for up to two parts of n requests: keys_a /
+// keys_b [n] (keys_b NULL for one part), lat and min_wgs per part; writes wgs_a /
+// wgs_b [n] and returns the workgroups handed out.
+int64_t hsah_balance(int32_t n, const int64_t* keys_a, int64_t lat_a, int32_t min_a, const int64_t* keys_b,
+                     int64_t lat_b, int32_t min_b, int64_t slots, int64_t* wgs_a, int64_t* wgs_b) {
+  std::vector<int64_t> ka(keys_a, keys_a + n), kb;
+  hsa::AttnPart pa{&ka, lat_a, min_a, {}}, pb{&kb, lat_b, min_b, {}};
+  std::vector<hsa::AttnPart*> parts{&pa};
+  if (keys_b) {
+    kb.assign(keys_b, keys_b + n);
+    parts.push_back(&pb);
+  }
+  const int64_t used = hsa::balance_wgs(parts, slots);
+  for (int i = 0; i < n; ++i) {
+    wgs_a[i] = pa.wgs[i];
+    if (keys_b) wgs_b[i] = pb.wgs[i];
+  }
+  return used;
+}
+
+// Slices of n score rows (launch_plan.h); first has n + 1 entries; out = {gmax,
+// slice, k1}.
+void hsah_slices(int32_t n, const int64_t* scores, int32_t k, int32_t slice_override, int32_t default_slice,
+                 int32_t* first, int32_t* out) {
+  hsa::plan_slices(scores, n, k, slice_override, default_slice, first, &out[0], &out[1], &out[2]);
+}
 
 }  // extern "C"

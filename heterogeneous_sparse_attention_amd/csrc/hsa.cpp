@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <queue>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -14,6 +13,7 @@
 #include "control.h"
 #include "device.h"
 #include "kernels.h"
+#include "launch_plan.h"
 
 using namespace hsa;
 
@@ -68,7 +68,7 @@ struct hsa_ctx {
   int32_t attend_wgs = 512;   // attention workgroups per launch to aim for (one round)
   int32_t step_slots = 256;   // decode step: attention workgroups one launch holds at once
                               // (one per CU at the step kernels' register use)
-  int32_t select_slice = kSliceN;   // top-k: longer score rows are selected in two rounds
+  int32_t select_slice = 0;   // top-k: longer score rows are selected in two rounds (0: by k)
   int32_t step_fused = 1;     // decode step in three launches when every row fits the LDS cache
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
@@ -245,28 +245,17 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
   return kOk;
 }
 
-// Top-k workgroups of a batch: one per row of at most `select_slice` scores, else
-// one per slice (the last one shorter), with room for each slice's candidates.
+// Top-k workgroups of a batch (plan_slices), with room for the candidates of
+// sliced rows. On the 4 x 2^20-token workload (k 2048), 32768-score slices measured
+// 736 us per step, against 759 us for 16384 and 764 us for 65536.
 int plan_select(hsa_ctx* c, const ReqBatch& B, int32_t k, SelPlan& SP) {
   SP = SelPlan{};
-  SP.k1 = (k + 3) & ~3;
-  SP.slice = c->select_slice;
-  int32_t total = 0, gmax = 1;
-  for (int i = 0; i < B.n; ++i) {
-    const int64_t n = (int64_t)kC4 * B.r[i].nb;
-    // a sliced row holds more than k1 scores, so its slices keep at least k real
-    // candidates and round 2 never reaches their padding
-    const bool sliced = n > SP.slice && n > SP.k1;
-    const int32_t g = sliced ? (int32_t)((n + SP.slice - 1) / SP.slice) : 1;
-    SP.first[i] = total;
-    total += g;
-    gmax = std::max(gmax, g);
-  }
-  SP.first[B.n] = total;
-  SP.n_wgs = total;
-  SP.gmax = gmax;
-  if (gmax > 1) {
-    const size_t need = (size_t)B.n * gmax * SP.k1;
+  int64_t n[kMaxReq];
+  for (int i = 0; i < B.n; ++i) n[i] = (int64_t)kC4 * B.r[i].nb;
+  plan_slices(n, B.n, k, c->select_slice, kSliceN, SP.first, &SP.gmax, &SP.slice, &SP.k1);
+  SP.n_wgs = SP.first[B.n];
+  if (SP.gmax > 1) {
+    const size_t need = (size_t)B.n * SP.gmax * SP.k1;
     int s = grow(c, reinterpret_cast<void**>(&c->cand_ord), &c->cand_ord_cap, need, sizeof(int32_t));
     if (s) return s;
     s = grow(c, reinterpret_cast<void**>(&c->cand_score), &c->cand_score_cap, need, sizeof(float));
@@ -360,47 +349,6 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
     }
   }
   return kOk;
-}
-
-// Attention workgroups per request for the parts that share one launch. A request
-// gets one workgroup per part it has keys in (and at least min_wgs); the launch's
-// remaining slots go one at a time to the (part, request) whose workgroups are
-// estimated to finish last, the estimate being lat + keys / workgroups in units of
-// keys streamed (lat: what a part does before its first key). No workgroup is left
-// with fewer than kMinKeys keys.
-constexpr int64_t kMinKeys = 16;
-
-struct AttnPart {
-  const std::vector<int64_t>* keys;
-  int64_t lat;
-  int32_t min_wgs;
-  std::vector<int64_t> wgs;
-};
-
-void balance_wgs(const std::vector<AttnPart*>& parts, int64_t slots) {
-  using Item = std::pair<double, std::pair<int, int>>;
-  std::priority_queue<Item> pq;
-  int64_t used = 0;
-  auto can_split = [](int64_t keys, int64_t w) { return keys >= kMinKeys * (w + 1); };
-  for (int p = 0; p < (int)parts.size(); ++p) {
-    AttnPart& a = *parts[p];
-    a.wgs.assign(a.keys->size(), 0);
-    for (int i = 0; i < (int)a.keys->size(); ++i) {
-      const int64_t k = (*a.keys)[i];
-      a.wgs[i] = std::max<int64_t>(k > 0 ? 1 : 0, a.min_wgs);
-      used += a.wgs[i];
-      if (a.wgs[i] > 0 && can_split(k, a.wgs[i])) pq.push({a.lat + (double)k / a.wgs[i], {p, i}});
-    }
-  }
-  while (used < slots && !pq.empty()) {
-    const auto pi = pq.top().second;
-    pq.pop();
-    AttnPart& a = *parts[pi.first];
-    const int64_t k = (*a.keys)[pi.second];
-    const int64_t w = ++a.wgs[pi.second];
-    ++used;
-    if (can_split(k, w)) pq.push({a.lat + (double)k / w, pi});
-  }
 }
 
 // The decode step (committed one-token append + top-k + attention) in three or four

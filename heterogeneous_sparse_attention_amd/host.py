@@ -34,6 +34,8 @@ def load():
             "hsah_table": (_I32, [_P, _I32, _P, _I64, ctypes.POINTER(_I64)]),
             "hsah_refcount": (_I32, [_P, _I64]),
             "hsah_free_blocks": (_I64, [_P]),
+            "hsah_balance": (_I64, [_I32, _P, _I64, _I32, _P, _I64, _I32, _I64, _P, _P]),
+            "hsah_slices": (None, [_I32, _P, _I32, _I32, _I32, _P, _P]),
         }
         for n, (res, args) in sig.items():
             f = getattr(lib, n)
@@ -98,3 +100,30 @@ class HostControl:
 
     def free_blocks(self):
         return self._lib.hsah_free_blocks(self._c)
+
+
+def balance_wgs(slots, keys_a, lat_a=0, min_a=0, keys_b=None, lat_b=0, min_b=0):
+    """Attention workgroups per request for one or two launch parts (launch_plan.h).
+    Returns (handed out, wgs_a, wgs_b or None)."""
+    lib = load()
+    ka = np.ascontiguousarray(np.asarray(keys_a, np.int64))
+    n = ka.size
+    wa = np.zeros(n, np.int64)
+    kb = wb = None
+    if keys_b is not None:
+        kb = np.ascontiguousarray(np.asarray(keys_b, np.int64))
+        wb = np.zeros(n, np.int64)
+    used = lib.hsah_balance(n, ka.ctypes.data_as(_P), lat_a, min_a, kb.ctypes.data_as(_P) if kb is not None else None,
+                            lat_b, min_b, slots, wa.ctypes.data_as(_P), wb.ctypes.data_as(_P) if wb is not None else None)
+    return used, wa, wb
+
+
+def plan_slices(n_scores, k, slice_override=0, default_slice=16384):
+    """Top-k slices of score rows (launch_plan.h): (first [n + 1], gmax, slice, k1)."""
+    lib = load()
+    ns = np.ascontiguousarray(np.asarray(n_scores, np.int64))
+    first = np.zeros(ns.size + 1, np.int32)
+    out = np.zeros(3, np.int32)
+    lib.hsah_slices(ns.size, ns.ctypes.data_as(_P), k, slice_override, default_slice, first.ctypes.data_as(_P),
+                    out.ctypes.data_as(_P))
+    return first, int(out[0]), int(out[1]), int(out[2])

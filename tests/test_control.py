@@ -115,3 +115,72 @@ def test_control_selftest_with_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "control selftest ok" in r.stdout
+
+
+# ------------------------------------------------------------------ launch planning
+
+def _brute_min_max(keys, lat, mins, slots, min_keys=16):
+    """Smallest achievable largest estimate lat + keys / wgs over every assignment of
+    at most `slots` workgroups (each item between its floor and its split cap)."""
+    import itertools
+    lo = [max(1 if k > 0 else 0, m) for k, m in zip(keys, mins)]
+    hi = [max(l, k // min_keys) if k >= 2 * min_keys else l for k, l in zip(keys, lo)]
+    best = None
+    for w in itertools.product(*[range(a, b + 1) for a, b in zip(lo, hi)]):
+        if sum(w) > max(slots, sum(lo)):
+            continue
+        t = max((la + k / x) if x else 0.0 for k, la, x in zip(keys, lat, w))
+        best = t if best is None else min(best, t)
+    return best
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balance_wgs_is_optimal_on_small_cases(seed):
+    """The planner's greedy hand-out reaches the smallest possible largest estimate
+    (brute force over every assignment), never gives a workgroup fewer than 16 keys
+    of a splittable item, and gives every request with keys a workgroup."""
+    from heterogeneous_sparse_attention_amd.host import balance_wgs
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 4))
+    ka = rng.integers(0, 120, n)
+    kb = rng.integers(0, 120, n)
+    slots = int(rng.integers(1, 12))
+    lat_b = int(rng.integers(0, 20))
+    used, wa, wb = balance_wgs(slots, ka, 0, 0, kb, lat_b, 1)
+    assert used == wa.sum() + wb.sum()
+    assert np.all(wb >= 1) and np.all((ka == 0) | (wa >= 1))
+    floor = int(((ka > 0).sum()) + n)
+    assert used <= max(slots, floor)
+    for k, w in list(zip(ka, wa)) + list(zip(kb, wb)):
+        assert w <= max(1, k // 16)
+    est = max([k / w for k, w in zip(ka, wa) if w] + [lat_b + k / w for k, w in zip(kb, wb)])
+    ref = _brute_min_max(list(ka) + list(kb), [0] * n + [lat_b] * n, [0] * n + [1] * n, slots)
+    assert abs(est - ref) < 1e-9, (est, ref)
+
+
+def test_balance_wgs_fills_the_launch():
+    """b32-like sizes: the planner hands out exactly the slots when work allows."""
+    from heterogeneous_sparse_attention_amd.host import balance_wgs
+    rng = np.random.default_rng(7)
+    keys = rng.integers(130, 700, 32)
+    used, w, _ = balance_wgs(256, keys, 0, 1)
+    assert used == 256 and w.sum() == 256 and np.all(w >= 1)
+    t = keys / w
+    assert t.max() <= np.sort(t)[-2] * 1.5 + 1
+
+
+def test_plan_slices():
+    """Rows longer than the slice and than k1 are cut into ceil(n / slice) slices;
+    the default slice is max(16384, 16 k1); first[] is the workgroup prefix."""
+    from heterogeneous_sparse_attention_amd.host import plan_slices
+    first, gmax, sl, k1 = plan_slices([262144, 100, 16384, 16385], 2048)
+    assert (sl, k1) == (32768, 2048)
+    assert list(first) == [0, 8, 9, 10, 11] and gmax == 8
+    first, gmax, sl, k1 = plan_slices([9600, 1280, 1280], 777, slice_override=1024)
+    assert (sl, k1) == (1024, 780)
+    assert list(first) == [0, 10, 12, 14] and gmax == 10
+    # a row no longer than k1 stays whole even when it is longer than the slice
+    first, gmax, _, k1 = plan_slices([2048, 4096], 4096, slice_override=1024)
+    assert k1 == 4096 and list(first) == [0, 1, 2] and gmax == 1
+    first, gmax, sl, _ = plan_slices([16384, 16416], 512)
+    assert sl == 16384 and list(first) == [0, 1, 3] and gmax == 2
