@@ -124,7 +124,8 @@ struct StepArgs {
   float* part_ml;
   float* seal_part;      // HCA partials of the blocks sealed in this step
   int32_t* topk;         // [n][k]
-  int32_t* rows;         // [n][k] physical C4 rows of the selected entries (scratch)
+  int32_t* rows;         // [n][k] physical C4 rows of the selected entries (scratch,
+                         // four-launch form)
   float* score_out;      // [n][k] or null
   float* out;            // [n][16][128] fp32
   int32_t k;

@@ -74,7 +74,8 @@ hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_
                         const float* part_acc, const float* part_ml, float* out, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
 
-// step.hip: the decode step in four launches (see step.hip for what each does).
+// step.hip: the decode step in three or four launches (see step.hip for what each
+// does; launch_step2b and launch_step3 enqueue nothing in the three-launch form).
 hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,

@@ -143,16 +143,6 @@ __device__ __forceinline__ void select_round2(int r, const Req* reqs, const SelP
                  R.nb, 0, SP.cand_ord + c0);
 }
 
-// Which part of the selection one workgroup writes: the physical C4 rows of output
-// positions [x0, x1) of the ascending-ordinal list (position x to rows[x - x0]);
-// with `io`, the ordinals and scores of those positions (of every position, in
-// selection order, when sorted); with `pad`, the padding of positions [kk, k).
-struct SelWin {
-  int x0, x1;
-  bool io, pad;
-};
-constexpr SelWin kSelAll{0, 1 << 30, true, true};
-
 // Exclusive prefix sum over the wave's lanes, and the wave total in `total`.
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
   const int lane = threadIdx.x & 63;
@@ -176,14 +166,13 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
 // With `rows`, also writes each taken entry's physical C4 row (table[j / 32] * 32 +
 // j % 32) from the state's block table `tab` (nb_tab blocks), in ascending ordinal
 // order. The ordinal written for entry i is i + ord0, or ord_map[i] when a map is
-// given. `win` limits what is written (SelWin). NT = threads of the workgroup.
+// given. NT = threads of the workgroup.
 template <int NT = kSelThreads>
 __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, const float* S,
                                            int32_t* io, float* so, SelShared& sh,
                                            const int32_t* tab = nullptr, int32_t* rows = nullptr,
                                            int nb_tab = 0, int32_t ord0 = 0,
-                                           const int32_t* ord_map = nullptr,
-                                           SelWin win = kSelAll) {
+                                           const int32_t* ord_map = nullptr) {
   static_assert(NT % 64 == 0 && NT <= kSelThreads && NT >= 256, "select workgroup size");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
@@ -272,15 +261,14 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     // entries taken before i are (above tau before i) + min(equal before i, rem)
     const int lane = tid & 63, wv = tid >> 6;
     auto take = [&](int i, uint32_t u, int pos) {
-      const bool in = pos >= win.x0 && pos < win.x1;
-      if (sorted && win.io) sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
-      if (!in) return;
       const int32_t j = ord_of(i);
-      if (!sorted && win.io) {
+      if (sorted) {
+        sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
+      } else {
         io[pos] = j;
         if (so) so[pos] = okey_inv(u);
       }
-      if (rows) rows[pos - win.x0] = row_of(j);
+      if (rows) rows[pos] = row_of(j);
     };
     if (!cached) {
       // Scores stream from L2: wave w owns a contiguous range of float4s. Count its
@@ -371,7 +359,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       if (gt || (eq && eq_before < rem)) take(i, u, gt_before + min(eq_before, rem));
       if (base_gt + min(base_eq, rem) >= kk) break;   // every entry taken (uniform)
     }
-    if (sorted && win.io) {
+    if (sorted) {
       int n2 = 1;
       while (n2 < kk) n2 <<= 1;
       for (int i = kk + tid; i < n2; i += NT) sh.cand[i] = ~0ull;
@@ -399,11 +387,9 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       }
     }
   }
-  if (win.pad) {
-    for (int i = kk + tid; i < k; i += NT) {
-      io[i] = -1;
-      if (so) so[i] = -INFINITY;
-    }
+  for (int i = kk + tid; i < k; i += NT) {
+    io[i] = -1;
+    if (so) so[i] = -INFINITY;
   }
 }
 
@@ -452,9 +438,16 @@ __device__ __forceinline__ void sel_preload(int N, const float* S, const int32_t
   pre.tab = load_global(tab + (tid < nb ? tid : 0));
 }
 
+// Which part of the selection one workgroup writes: output positions [x0, x1) of the
+// ascending-ordinal list (ordinals and scores, and the physical C4 row of position x
+// into rows[x - x0]); with `pad`, also the padding of positions [kk, k).
+struct SelWin {
+  int x0, x1;
+  bool pad;
+};
+
 // Top-k of the staged row (N scores, N / 32 blocks) by one workgroup of NT threads,
-// in ascending ordinal order, writing what `win` asks for (ordinals and
-// scores when win.io; physical C4 rows of window positions into rows[x - win.x0]).
+// in ascending ordinal order, writing what `win` asks for.
 // Same selection as select_run: radix passes of 11, 11 and 10 bits over the
 // order-preserving keys find the cut; the passes stop early once the bucket at the
 // cut is taken whole. One ordered pass then takes every key above the cut and the
@@ -560,10 +553,8 @@ __device__ __forceinline__ void select_lds(int N, int32_t k, int32_t* io, float*
           const int pos = gb + min(eb, rem);
           if (pos >= win.x0 && pos < win.x1) {
             const int32_t i = i0 + j;
-            if (win.io) {
-              gio[pos] = i;
-              if (gso) gso[pos] = okey_inv(e[j]);
-            }
+            gio[pos] = i;
+            if (gso) gso[pos] = okey_inv(e[j]);
             rows[pos - win.x0] = sh.tab[i / kC4] * kC4 + i % kC4;
           }
         }

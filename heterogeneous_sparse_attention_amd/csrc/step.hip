@@ -207,7 +207,7 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   auto stage = [&]() { select_stage<NT>(pre, sh.sel); };
   auto select = [&]() {
     select_lds<NT>(N, S.k, S.topk + r * k, S.score_out ? S.score_out + r * k : nullptr, sh.sel, sh.rows,
-                   SelWin{b0, b1, true, w == 0});
+                   SelWin{b0, b1, w == 0});
     __syncthreads();   // rows in LDS complete; the selection's LDS is free for attention
   };
   float M, L, A8[8];
