@@ -12,4 +12,5 @@ from .cache import (  # noqa: F401
     BLOCK, C4_PER_BLOCK, M_CSA, M_HCA, N_HEADS, HEAD_DIM, IDX_HEADS, IDX_DIM,
     OracleError, Oracle, bf16_round, gated_pool, token_scores, c4_scores,
     select_topk, attention, length_split, block_range_summary, decode_reference,
+    E4M3_MAX, e4m3_decode, e4m3_encode, quantize_e4m3_rows,
 )

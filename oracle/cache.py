@@ -41,6 +41,13 @@ Readings taken where the pages leave a step open (each also in the design notes)
   R11 share(src, dst): dst (fresh) references every sealed block of src
       (refcount + 1 each) and gets a copy of src's State (SWA, tail, L).
   R12 softmax scale 1/sqrt(128); no positional encoding, no mask.
+  R15 FP8 entries (optional format): the pages account compressed entries in FP8
+      ([Ch12] §2.2) without a scale scheme. Reading: each C4 entry's K and V are
+      stored per head as 128 OCP FP8 E4M3 codes and one float32 scale
+      s = max_d |x_d| / 448 (1 when the head is all zero); code_d = E4M3 of
+      x_d / s, nearest-even; the stored value is code_value * s. The decisions
+      (x as float32, s, x / s) are taken in float32, the precision the kernel
+      computes in. HCA entries stay bf16.
 """
 
 from __future__ import annotations
@@ -82,6 +89,59 @@ def bf16_round(x) -> np.ndarray:
     return np.ldexp(np.rint(m * 256.0) / 256.0, e)
 
 
+# OCP FP8 E4M3 (E4M3FN): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no
+# infinities; exponent 15 with mantissa 7 is NaN; largest finite value 448.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code (float64; NaN for 0x7f and 0xff), from the format:
+    exponent field 0 is subnormal, 2**-6 * m / 8; otherwise 2**(e - 7) * (1 + m / 8)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 code of each value (round to nearest, ties to the even code). Written
+    from the format: the representable magnitudes are enumerated and x goes to the
+    nearest; on a tie, to the one whose code is even. |x| above the largest finite
+    value rounds to it when below the midpoint toward the next binade (464) and is
+    NaN beyond; NaN stays NaN; -0 keeps its sign."""
+    x = np.asarray(x, dtype=np.float64)
+    finite_codes = np.arange(0, 0x7F)                         # 0 .. 126: 0 .. 448
+    vals = e4m3_decode(finite_codes)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (finite_codes[hi] % 2 == 0))
+    code = np.where(pick_hi, finite_codes[hi], finite_codes[lo])
+    code = np.where(a >= 464.0, 0x7F, code)
+    code = np.where(np.isnan(x), 0x7F, code)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def quantize_e4m3_rows(x) -> tuple:
+    """Per-row FP8 storage of [..., 128] rows (reading R15): returns (codes uint8,
+    scales float32 [...], values float64 = code value * scale). The row is taken as
+    float32; s = float32(max |x| / 448) (1 for an all-zero row); each code is the
+    E4M3 of float32(x / s)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    s = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0)).astype(np.float32)
+    y = (x32 / s[..., None]).astype(np.float32)
+    codes = e4m3_encode(y)
+    vals = e4m3_decode(codes) * s[..., None].astype(np.float64)
+    return codes, s, vals
+
+
 def length_split(L: int) -> dict:
     """L = 128 q + r: q sealed blocks hold 32q C4 + q HCA entries, r tokens stay
     in the tail ([Q&A] §2.2, §3.1; [Ch12] Demo)."""
@@ -90,12 +150,13 @@ def length_split(L: int) -> dict:
             "csa_tail": int(L) % M_CSA, "hca_tail": int(L) % M_HCA}
 
 
-def gated_pool(Kg: np.ndarray, Vg: np.ndarray, W: np.ndarray):
+def gated_pool(Kg: np.ndarray, Vg: np.ndarray, W: np.ndarray, rounded: bool = True):
     """Compress m consecutive tokens into one entry (reading R1).
 
     Kg, Vg: [m][H][D] token K/V; W: [H][D] gate weights. Per head h:
     g_t = <W[h], K_t[h]>, alpha = softmax_t(g), entry = sum_t alpha_t K_t[h]
-    (and the same alpha for V). Returns bf16-rounded (K, V) [H][D] as float32.
+    (and the same alpha for V). Returns bf16-rounded (K, V) [H][D] as float32, or
+    the float64 values when not `rounded`.
     The m -> 1 compression and its alignment to the block: [Q&A] §2.1.
     """
     Kg = np.asarray(Kg, dtype=np.float64)
@@ -107,6 +168,8 @@ def gated_pool(Kg: np.ndarray, Vg: np.ndarray, W: np.ndarray):
     a = a / a.sum(axis=0, keepdims=True)                # softmax over the m tokens
     Kh = np.einsum("th,thd->hd", a, Kg)
     Vh = np.einsum("th,thd->hd", a, Vg)
+    if not rounded:
+        return Kh, Vh
     return bf16_round(Kh).astype(np.float32), bf16_round(Vh).astype(np.float32)
 
 
@@ -232,8 +295,10 @@ def decode_reference(seq, n_win: int, gate_csa, gate_hca, cases, pmap=map, chunk
 
 class _Block:
     """One sealed, immutable Block Cache block: 32 C4 + 1 HCA + 128 indexer keys
-    ([Ch12] §2.2; [Q&A] §2.2)."""
-    __slots__ = ("csa_k", "csa_v", "hca_k", "hca_v", "idx")
+    ([Ch12] §2.2; [Q&A] §2.2). With FP8 entries (R15) csa_k / csa_v hold the stored
+    values (code value * scale) and the codes and scales are kept beside them."""
+    __slots__ = ("csa_k", "csa_v", "hca_k", "hca_v", "idx", "csa_k_codes", "csa_v_codes",
+                 "csa_k_scale", "csa_v_scale")
 
 
 class _State:
@@ -250,9 +315,13 @@ class _State:
 class Oracle:
     """The cache, driven call by call like the C ABI."""
 
-    def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int):
+    def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int,
+                 entry_format: str = "bf16"):
         if n_win < BLOCK or n_win % BLOCK:
             raise OracleError("invalid", "n_win must be a positive multiple of 128")
+        if entry_format not in ("bf16", "fp8"):
+            raise OracleError("invalid", "entry format is bf16 or fp8")
+        self.entry_format = entry_format
         self.n_win = int(n_win)
         self.W_csa = np.asarray(gate_csa, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
         self.W_hca = np.asarray(gate_hca, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
@@ -355,11 +424,22 @@ class Oracle:
         Kt = np.stack([t[0] for t in st.tail]).astype(np.float64)   # [128][H][D]
         Vt = np.stack([t[1] for t in st.tail]).astype(np.float64)
         blk = _Block()
-        blk.csa_k = np.empty((C4_PER_BLOCK, N_HEADS, HEAD_DIM), np.float32)
+        fp8 = self.entry_format == "fp8"
+        blk.csa_k = np.empty((C4_PER_BLOCK, N_HEADS, HEAD_DIM), np.float64 if fp8 else np.float32)
         blk.csa_v = np.empty_like(blk.csa_k)
+        if fp8:
+            blk.csa_k_codes = np.empty((C4_PER_BLOCK, N_HEADS, HEAD_DIM), np.uint8)
+            blk.csa_v_codes = np.empty_like(blk.csa_k_codes)
+            blk.csa_k_scale = np.empty((C4_PER_BLOCK, N_HEADS), np.float32)
+            blk.csa_v_scale = np.empty_like(blk.csa_k_scale)
         for j in range(C4_PER_BLOCK):                 # C4 entry j: tokens 4j .. 4j+3
             g = slice(M_CSA * j, M_CSA * (j + 1))
-            blk.csa_k[j], blk.csa_v[j] = gated_pool(Kt[g], Vt[g], self.W_csa)
+            if fp8:                                   # reading R15
+                Kj, Vj = gated_pool(Kt[g], Vt[g], self.W_csa, rounded=False)
+                blk.csa_k_codes[j], blk.csa_k_scale[j], blk.csa_k[j] = quantize_e4m3_rows(Kj)
+                blk.csa_v_codes[j], blk.csa_v_scale[j], blk.csa_v[j] = quantize_e4m3_rows(Vj)
+            else:
+                blk.csa_k[j], blk.csa_v[j] = gated_pool(Kt[g], Vt[g], self.W_csa)
         blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)     # all 128 tokens
         blk.idx = np.stack([t[2] for t in st.tail]).astype(np.float32)
         self.store[b] = blk

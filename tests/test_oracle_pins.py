@@ -468,3 +468,99 @@ def test_streamed_reference_matches_token_by_token(n_win, k):
         np.testing.assert_array_equal(i0, i1)
         np.testing.assert_array_equal(v0, v1)
         np.testing.assert_allclose(o0, o1, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ FP8 E4M3 entries (reading R15)
+
+def test_e4m3_decode_follows_the_format():
+    """Values fixed by the E4M3 definition (bias 7, 3 mantissa bits, subnormals,
+    no infinities, 0x7f / 0xff NaN), computed here with exact fractions."""
+    from oracle import e4m3_decode
+    c = np.arange(256)
+    v = e4m3_decode(c)
+    for code in range(256):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            assert math.isnan(v[code])
+            continue
+        mag = Fraction(m, 8) * Fraction(1, 2 ** 6) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        assert v[code] == float(-mag if s else mag), code
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert np.isnan(v).sum() == 2
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                      # codes 0..126 ascend
+
+
+def test_e4m3_encode_is_nearest_ties_to_even():
+    """Brute force against every finite value: the code's value is the nearest, and
+    exact midpoints go to the even code; decode(encode(v)) == v for every finite v."""
+    from oracle import e4m3_decode, e4m3_encode
+    vals = e4m3_decode(np.arange(0x7F))
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.uniform(0, 448, 4000), rng.uniform(0, 2 ** -5, 2000),
+                        (vals[1:] + vals[:-1]) / 2])      # every midpoint
+    codes = e4m3_encode(x)
+    for xi, c in zip(x, codes):
+        d = np.abs(vals - xi)
+        best = np.flatnonzero(d == d.min())
+        assert c in best
+        if len(best) == 2:
+            assert c % 2 == 0
+    fin = np.arange(256)[~np.isnan(e4m3_decode(np.arange(256)))]
+    assert np.array_equal(e4m3_encode(e4m3_decode(fin)), fin.astype(np.uint8))
+    assert np.array_equal(e4m3_encode(-x), codes | 0x80)
+    assert e4m3_encode([460.0])[0] == 0x7E and e4m3_encode([464.0])[0] == 0x7F
+
+
+def test_quantize_rows_bounds_and_special_cases():
+    """Per-row FP8 storage: the largest magnitude stores as +-448 * s (up to the
+    float32 rounding of s), every value within half a code spacing (times s) of
+    the row, an all-zero row stays zero with scale 1, and a row and its negation
+    store with mirrored codes."""
+    from oracle import e4m3_decode, quantize_e4m3_rows
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((64, 128)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    codes, s, vals = quantize_e4m3_rows(x)
+    x32 = x.astype(np.float32).astype(np.float64)
+    amax_i = np.abs(x32).argmax(axis=1)
+    assert np.all((codes[np.arange(64), amax_i] & 0x7F) == 0x7E)
+    y = x32 / s[:, None].astype(np.float64)
+    grid = e4m3_decode(np.arange(0x7F))
+    idx = np.clip(np.searchsorted(grid, np.abs(y)), 1, len(grid) - 1)
+    spacing = grid[idx] - grid[idx - 1]
+    assert np.all(np.abs(e4m3_decode(codes) - y) <= spacing / 2 * (1 + 1e-6) + 1e-12)
+    assert np.allclose(vals, e4m3_decode(codes) * s[:, None])
+    zc, zs, zv = quantize_e4m3_rows(np.zeros((2, 128)))
+    assert np.all(zc == 0) and np.all(zs == 1.0) and np.all(zv == 0)
+    nc, ns, _ = quantize_e4m3_rows(-x)
+    assert np.array_equal(ns, s) and np.array_equal(nc, codes ^ 0x80)
+
+
+def test_fp8_oracle_entries_quantize_the_pooled_entry():
+    """With FP8 entries the oracle's C4 entries are the per-head E4M3 storage of the
+    unrounded pooled entry (the bf16 oracle's entries come from the same pooling),
+    HCA entries and indexer keys are unchanged, and attention reads the stored
+    values."""
+    from oracle import quantize_e4m3_rows
+    Wc, Wh = synth.gate_weights(SEED)
+    a = Oracle(128, Wc, Wh, 2, 4)
+    b = Oracle(128, Wc, Wh, 2, 4, entry_format="fp8")
+    K, V, KI = toks(0, 0, 200)
+    for o in (a, b):
+        assert o.state_alloc() == 0
+        o.append([0], [(K, V, KI)])
+    ba, bb = a.block(0), b.block(0)
+    assert np.array_equal(ba.hca_k, bb.hca_k) and np.array_equal(ba.idx, bb.idx)
+    for j in (0, 13, 31):
+        kj, vj = gated_pool(K[4 * j:4 * j + 4], V[4 * j:4 * j + 4], Wc, rounded=False)
+        assert np.allclose(bf16_round(kj), ba.csa_k[j])
+        codes, sc, vals = quantize_e4m3_rows(kj)
+        assert np.array_equal(codes, bb.csa_k_codes[j]) and np.array_equal(sc, bb.csa_k_scale[j])
+        assert np.array_equal(vals, bb.csa_k[j])
+        rel = np.linalg.norm(bb.csa_v[j] - vj) / np.linalg.norm(vj)
+        assert rel < 0.05
+    q = synth.bf16_bits_to_f32(synth.tokens_bf16(SEED, synth.STREAM_Q, 0, np.array([199])))[0]
+    sel = np.array([3, 9, 30])
+    Kc = np.concatenate([np.stack([t[0] for t in b.states[0].swa]), bb.hca_k[None], bb.csa_k[sel]])
+    Vc = np.concatenate([np.stack([t[1] for t in b.states[0].swa]), bb.hca_v[None], bb.csa_v[sel]])
+    assert np.allclose(b.attend(0, q, sel, 3), attention(q, Kc, Vc), atol=1e-12)
