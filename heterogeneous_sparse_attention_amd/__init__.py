@@ -44,7 +44,10 @@ class _Config(ctypes.Structure):
                 ("idx_dim", ctypes.c_int32), ("max_states", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int64), ("max_blocks_per_state", ctypes.c_int64),
                 ("gate_csa", ctypes.POINTER(ctypes.c_float)),
-                ("gate_hca", ctypes.POINTER(ctypes.c_float))]
+                ("gate_hca", ctypes.POINTER(ctypes.c_float)),
+                ("entry_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+ENTRY_FORMATS = {"bf16": 0, "fp8": 1}     # HSA_ENTRY_BF16, HSA_ENTRY_FP8
 
 
 class _StateInfo(ctypes.Structure):
@@ -77,6 +80,8 @@ SIGNATURES = {
     "hsa_block_refcount": [_P, _I32, ctypes.POINTER(_I32)],
     "hsa_export_block": [_P, _I32, _P, _P, _P, _P, _P, _P],
     "hsa_export_state": [_P, _I32, _P, _P, _P, _P],
+    "hsa_export_c4_fp8": [_P, _I32, _P, _P, _P, _P, _P],
+    "hsa_fp8_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_timing_enable": [_P, _U32],
     "hsa_timing_read": [_P, _P, _P],
 }
@@ -149,13 +154,17 @@ class Cache:
     """One Block Cache + State Cache on one GPU (an hsa_ctx)."""
 
     def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
-                 max_blocks_per_state: int = 0, device: int = 0):
+                 max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16"):
         lib = load()
+        if entry_format not in ENTRY_FORMATS:
+            raise ValueError(f"entry_format must be one of {sorted(ENTRY_FORMATS)}")
         self._gc = np.ascontiguousarray(np.asarray(gate_csa, np.float32).reshape(H * D))
         self._gh = np.ascontiguousarray(np.asarray(gate_hca, np.float32).reshape(H * D))
         cfg = _Config(H, D, 4, 128, n_win, HI, DI, max_states, max_blocks, max_blocks_per_state,
                       self._gc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
-                      self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+                      self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                      ENTRY_FORMATS[entry_format], 0)
+        self.entry_format = entry_format
         ctx = ctypes.c_void_p()
         _check(lib.hsa_create(ctypes.byref(cfg), device, ctypes.byref(ctx)), "hsa_create")
         self._ctx = ctx
@@ -290,13 +299,26 @@ class Cache:
         return rc.value
 
     def export_block(self, b: int, stream=None) -> dict:
-        """bf16 arrays as uint16 bits; indexer keys as float32."""
-        out = {"csa_k": np.zeros((32, H, D), np.uint16), "csa_v": np.zeros((32, H, D), np.uint16),
-               "hca_k": np.zeros((H, D), np.uint16), "hca_v": np.zeros((H, D), np.uint16),
+        """bf16 arrays as uint16 bits; indexer keys as float32. With FP8 entries the C4
+        entries come as E4M3 codes (csa_k_codes, csa_v_codes uint8 [32][16][128]) and
+        per-head scales (csa_k_scale, csa_v_scale float32 [32][16])."""
+        fp8 = self.entry_format == "fp8"
+        out = {"hca_k": np.zeros((H, D), np.uint16), "hca_v": np.zeros((H, D), np.uint16),
                "idx": np.zeros((128, HI, DI), np.float32)}
+        if not fp8:
+            out["csa_k"] = np.zeros((32, H, D), np.uint16)
+            out["csa_v"] = np.zeros((32, H, D), np.uint16)
         p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
-        _check(_lib.hsa_export_block(self._ctx, int(b), p["csa_k"], p["csa_v"], p["hca_k"],
+        _check(_lib.hsa_export_block(self._ctx, int(b), p.get("csa_k"), p.get("csa_v"), p["hca_k"],
                                      p["hca_v"], p["idx"], _stream(stream)), "hsa_export_block")
+        if fp8:
+            q = {"csa_k_codes": np.zeros((32, H, D), np.uint8), "csa_v_codes": np.zeros((32, H, D), np.uint8),
+                 "csa_k_scale": np.zeros((32, H), np.float32), "csa_v_scale": np.zeros((32, H), np.float32)}
+            pq = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in q.items()}
+            _check(_lib.hsa_export_c4_fp8(self._ctx, int(b), pq["csa_k_codes"], pq["csa_v_codes"],
+                                          pq["csa_k_scale"], pq["csa_v_scale"], _stream(stream)),
+                   "hsa_export_c4_fp8")
+            out.update(q)
         return out
 
     def export_state(self, s: int, stream=None) -> dict:
@@ -321,3 +343,18 @@ class Cache:
         _check(_lib.hsa_timing_read(self._ctx, ms.ctypes.data_as(ctypes.c_void_p),
                                     n.ctypes.data_as(ctypes.c_void_p)), "hsa_timing_read")
         return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(KERNELS)}
+
+
+def fp8_quantize_rows(x, stream=None):
+    """The FP8 entry quantisation alone (hsa_fp8_quantize_rows): device float32
+    [n][128] -> (codes uint8 [n][128], scales float32 [n]) as device tensors."""
+    import torch
+    load()
+    n = x.shape[0]
+    codes = torch.empty((n, D), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n,), dtype=torch.float32, device=x.device)
+    _check(_lib.hsa_fp8_quantize_rows(_dev(x, torch.float32, (n, D), "x"), n,
+                                      _dev(codes, torch.uint8, (n, D), "codes"),
+                                      _dev(scales, torch.float32, (n,), "scales"), _stream(stream)),
+           "hsa_fp8_quantize_rows")
+    return codes, scales

@@ -22,6 +22,7 @@ namespace {
 // No slot written by the first group is read by the second: the new token's
 // ring slot differs from the 127 older ones (n_win >= 128), and its tail slot is
 // 127, which the seal reads from the input instead.
+template <bool FP8>
 __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, const uint16_t* kin,
                                                        const uint16_t* vin, const float* iin,
                                                        float* part) {
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, cons
   const int item = (bid - B.n) / kSealSplit;
   const int sub = (bid - B.n) % kSealSplit;
   const int ri = B.seal_req[item];
-  seal_eighth(P, B.r[ri], ri, item, sub, kin, vin, iin, part);
+  seal_eighth<FP8>(P, B.r[ri], ri, item, sub, kin, vin, iin, part);
 }
 
 // One workgroup per block sealed by k_decode_append (next launch, so the partials
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(256) void k_seal_merge(Pools P, ReqBatch B, const f
 
 // Bulk seal: one workgroup per block, its eight 16-token partials merged in
 // registers in order.
+template <bool FP8>
 __global__ __launch_bounds__(256) void k_bulk_seal(Pools P, const SealDesc* seals,
                                                    const uint16_t* kin, const uint16_t* vin,
                                                    const float* iin) {
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void k_bulk_seal(Pools P, const SealDesc* seal
   float M = -INFINITY, L = 0.f, K8[8] = {}, V8[8] = {};
   for (int sub = 0; sub < kSealSplit; ++sub) {
     float m, l, acck[8], accv[8];
-    seal_part(P, src, d.id, sub * kSubTok, m, l, acck, accv);
+    seal_part<FP8>(P, src, d.id, sub * kSubTok, m, l, acck, accv);
     merge_part(M, L, K8, V8, m, l, acck, accv);
   }
   store_hca(P, d.id, L, K8, V8);
@@ -93,14 +95,40 @@ __global__ __launch_bounds__(256) void k_bulk_write(Pools P, const WriteDesc* w,
   }
 }
 
+// Per-row FP8 storage: 16 rows of 128 floats per workgroup, lanes 16r .. 16r+15
+// holding row r as 8 values each (the seal's per-head layout).
+__global__ __launch_bounds__(256) void k_fp8_rows(const float* x, int64_t n_rows, uint8_t* codes,
+                                                  float* scales) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= n_rows) return;   // whole 16-lane rows, so the per-row max stays within active lanes
+  const int col = (threadIdx.x & 15) * 8;
+  const float4 a = reinterpret_cast<const float4*>(x + row * kD + col)[0];
+  const float4 b = reinterpret_cast<const float4*>(x + row * kD + col)[1];
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float sc;
+  const uint2 q = quantize8_e4m3(v, sc);
+  *reinterpret_cast<uint2*>(codes + row * kD + col) = q;
+  if ((threadIdx.x & 15) == 0) scales[row] = sc;
+}
+
 }  // namespace
+
+hipError_t launch_fp8_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
+                           hipStream_t st) {
+  if (n_rows <= 0) return hipSuccess;
+  return launch_k(k_fp8_rows, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), st, LaunchEv{}, x,
+                  n_rows, codes, scales);
+}
 
 hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* kin, const void* vin,
                                 const float* iin, float* part, hipStream_t st,
                  const LaunchEv& ev) {
   const int grid = B.n + kSealSplit * B.n_seal;
   if (grid == 0) return hipSuccess;
-  return launch_k(k_decode_append, dim3(grid), dim3(256), st, ev, P, B,
+  if (P.fp8)
+    return launch_k(k_decode_append<true>, dim3(grid), dim3(256), st, ev, P, B,
+                    static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin, part);
+  return launch_k(k_decode_append<false>, dim3(grid), dim3(256), st, ev, P, B,
                      static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin, part);
 }
 
@@ -114,7 +142,10 @@ hipError_t launch_bulk_seal(const Pools& P, const SealDesc* seals, int64_t n_sea
                             const void* vin, const float* iin, hipStream_t st,
                  const LaunchEv& ev) {
   if (n_seals == 0) return hipSuccess;
-  return launch_k(k_bulk_seal, dim3((unsigned)n_seals), dim3(256), st, ev, P, seals,
+  if (P.fp8)
+    return launch_k(k_bulk_seal<true>, dim3((unsigned)n_seals), dim3(256), st, ev, P, seals,
+                    static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin);
+  return launch_k(k_bulk_seal<false>, dim3((unsigned)n_seals), dim3(256), st, ev, P, seals,
                      static_cast<const uint16_t*>(kin), static_cast<const uint16_t*>(vin), iin);
 }
 

@@ -45,9 +45,9 @@ __device__ __forceinline__ KeyAddr key_addr(const Pools& P, const Req& R, int x,
   if (j < 0 || j >= kC4 * R.nb) return a;
   const int32_t id = tab[j / kC4];
   if (id < 0 || id >= P.max_blocks) return a;
-  const int64_t off = ((int64_t)id * kC4 + j % kC4) * kRow;
-  a.k = P.csa_k + off;
-  a.v = P.csa_v + off;
+  const C4Addr c = c4_addr(P, (int64_t)id * kC4 + j % kC4);
+  a.k = c.k;
+  a.v = c.v;
   return a;
 }
 
@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attend(Pools P, ReqBatch B,
   const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
   float M, L, A8[8];
   attend_keys([&](int x) { return key_addr(P, R, x, sel); }, w * chunk, min(nk, (w + 1) * chunk),
-              q + (int64_t)r * kRow, dk, dv, sh, M, L, A8);
+              q + (int64_t)r * kRow, dk, dv, sh, M, L, A8,
+              P.fp8 ? (R.len < P.n_win ? R.len : P.n_win) + R.nb : 0x7fffffff);
   if (nch == 1)
     store_output(out + (int64_t)r * kRow, L, A8);
   else

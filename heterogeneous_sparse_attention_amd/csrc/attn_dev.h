@@ -63,25 +63,82 @@ constexpr int ring_depth() { return WAVES > 4 ? 4 : 5; }
 // gather random rows from HBM at a higher rate.
 constexpr int kMixedRing = 2;
 
+// One key in the load ring. bf16 key: chunk c of the K and V rows (8 values each).
+// FP8 key: .x/.y hold the chunk's 8 E4M3 codes and .z the scale of its head.
 struct KeyRegs {
   uint4 k[4];
   uint4 v[4];
 };
 
-// Issue the loads of key j (lane j's addresses) of the current 64-key group.
-__device__ __forceinline__ void load_key(KeyRegs& R, uint64_t kp, uint64_t vp, int j, int lane) {
-  const uint16_t* pk = lane_ptr(kp, j);
-  const uint16_t* pv = lane_ptr(vp, j);
+// Issue the loads of key j (lane j's addresses) of the current 64-key group. For a
+// bf16 key kp/vp are its K and V rows; for an FP8 C4 key kp is its code row (K
+// codes, then V codes) and vp its scale row (K scales, then V scales, head h at
+// 4 (h % 4) + h / 4, so lane l's heads l/16 + 4c are 4 consecutive floats).
+__device__ __forceinline__ void load_key(KeyRegs& R, uint64_t kp, uint64_t vp, int j, int lane,
+                                         bool fp8) {
+  if (!fp8) {
+    const uint16_t* pk = lane_ptr(kp, j);
+    const uint16_t* pv = lane_ptr(vp, j);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      R.k[c] = load_stream(reinterpret_cast<const uint4*>(pk + c * 512) + lane);
+      R.v[c] = load_stream(reinterpret_cast<const uint4*>(pv + c * 512) + lane);
+    }
+    return;
+  }
+  const uint8_t* pq = reinterpret_cast<const uint8_t*>(lane_ptr(kp, j));
+  const float* ps = reinterpret_cast<const float*>(lane_ptr(vp, j)) + 4 * (lane >> 4);
+  const float4 sk = load_global(reinterpret_cast<const float4*>(ps));
+  const float4 sv = load_global(reinterpret_cast<const float4*>(ps + kH));
+  const float skc[4] = {sk.x, sk.y, sk.z, sk.w};
+  const float svc[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    R.k[c] = load_stream(reinterpret_cast<const uint4*>(pk + c * 512) + lane);
-    R.v[c] = load_stream(reinterpret_cast<const uint4*>(pv + c * 512) + lane);
+    const uint2 a = load_stream(reinterpret_cast<const uint2*>(pq + c * 512) + lane);
+    const uint2 b = load_stream(reinterpret_cast<const uint2*>(pq + kRow + c * 512) + lane);
+    R.k[c] = make_uint4(a.x, a.y, __float_as_uint(skc[c]), 0u);
+    R.v[c] = make_uint4(b.x, b.y, __float_as_uint(svc[c]), 0u);
   }
 }
 
-// Online softmax update of this lane's 4 heads with one key.
+// Online softmax update of this lane's 4 heads with one FP8 key: the codes become
+// exact bf16 pairs for the dot product, whose sum takes the K scale; the V scale
+// multiplies the softmax weight.
+__device__ __forceinline__ void compute_key_fp8(const KeyRegs& R, bool ok, const uint4* qw, float* m,
+                                                float* l, float (*acc)[8]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float kf[8];
+    e4m3x4_to_f32(R.k[c].x, kf);
+    e4m3x4_to_f32(R.k[c].y, kf + 4);
+    float a = dot2(qw[c].x, pack_exact_bf2(kf[0], kf[1]), 0.f);
+    a = dot2(qw[c].y, pack_exact_bf2(kf[2], kf[3]), a);
+    a = dot2(qw[c].z, pack_exact_bf2(kf[4], kf[5]), a);
+    a = dot2(qw[c].w, pack_exact_bf2(kf[6], kf[7]), a);
+    const float s = ok ? row_sum16(a) * (kQScale * __uint_as_float(R.k[c].z)) : -INFINITY;
+    const float mx = fmaxf(m[c], s);
+    const float sc = exp2f(m[c] - mx);
+    const float p = exp2f(s - mx);
+    l[c] = fmaf(l[c], sc, p);
+    // a skipped slot holds the bytes of a dummy bf16 row, which may read as the E4M3
+    // NaN code: its codes are zeroed, so its weight 0 multiplies zeros
+    const float pv = ok ? p * __uint_as_float(R.v[c].z) : 0.f;
+    float vf[8];
+    e4m3x4_to_f32(ok ? R.v[c].x : 0u, vf);
+    e4m3x4_to_f32(ok ? R.v[c].y : 0u, vf + 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(pv, vf[i], acc[c][i] * sc);
+    m[c] = mx;
+  }
+}
+
+// Online softmax update of this lane's 4 heads with one key (bf16, or FP8 when fp8).
 __device__ __forceinline__ void compute_key(const KeyRegs& R, bool ok, const uint4* qw, float* m,
-                                            float* l, float (*acc)[8]) {
+                                            float* l, float (*acc)[8], bool fp8 = false) {
+  if (fp8) {
+    compute_key_fp8(R, ok, qw, m, l, acc);
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     float a = dot2(qw[c].x, R.k[c].x, 0.f);
@@ -139,14 +196,16 @@ __device__ __forceinline__ void merge_waves(const float* m, const float* l, cons
 }
 
 // Attention of one workgroup of WAVES waves over keys [x0, x1) of one request:
-// wave w streams a contiguous share. key_of(x) gives the K and V rows of key x or
-// nullptrs for a skipped slot; dummy_k / dummy_v are valid rows read in place of
-// skipped keys. On return threads t < 256 hold head t/16, dims (t%16)*8 .. +8 of
-// the unnormalised result: running max M (log2 units), sum L, accumulator A8.
+// wave w streams a contiguous share. key_of(x) gives the K and V rows of key x (for
+// an FP8 key, x >= fp8_from: its code and scale rows) or nullptrs for a skipped
+// slot; dummy_k / dummy_v are valid rows (at least 4 KiB) read in place of skipped
+// keys. On return threads t < 256 hold head t/16, dims (t%16)*8 .. +8 of the
+// unnormalised result: running max M (log2 units), sum L, accumulator A8.
 template <int WAVES = kAttnWaves, int RING = ring_depth<WAVES>(), class KeyFn>
 __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const uint16_t* qrow,
                                             const uint16_t* dummy_k, const uint16_t* dummy_v,
-                                            AttnSharedT<WAVES>& sh, float& M, float& L, float* A8) {
+                                            AttnSharedT<WAVES>& sh, float& M, float& L, float* A8,
+                                            int fp8_from = 0x7fffffff) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -174,18 +233,20 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
     const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
     const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
     const int n = min(64, w1 - g);
+    const int f8 = fp8_from - g;   // keys x >= f8 of this group are FP8
     // ring of RING keys: RING - 1 keys stay in flight while one is consumed
     KeyRegs ring[RING];
 #pragma unroll
     for (int u = 0; u < RING - 1; ++u)
-      if (u < n) load_key(ring[u], kp, vp, u, lane);
+      if (u < n) load_key(ring[u], kp, vp, u, lane, u >= f8);
     for (int i = 0; i < n; i += RING) {
 #pragma unroll
       for (int u = 0; u < RING; ++u) {
         const int x = i + u;
         if (x >= n) break;
-        if (x + RING - 1 < n) load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane);
-        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+        if (x + RING - 1 < n)
+          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane, x + RING - 1 >= f8);
+        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, x >= f8);
       }
     }
   }
@@ -200,13 +261,14 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
 // it has them, and their loads are issued before mid(), so they arrive while mid()
 // runs; pre() runs just before those loads are issued (work that should wait for
 // earlier loads first). key_a / key_b return the rows of a key or nullptrs for a
-// skipped slot; dummy_k / dummy_v are valid rows read in their place. Result as
+// skipped slot (with fp8_b, key_b gives the code and scale rows of FP8 C4 keys);
+// dummy_k / dummy_v are valid rows (at least 4 KiB) read in their place. Result as
 // attend_keys.
 template <int WAVES, int RING, class KeyA, class KeyB, class Pre, class Mid>
 __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_b, int b0, int b1, Pre pre, Mid mid,
                                            const uint16_t* qrow, const uint16_t* dummy_k,
                                            const uint16_t* dummy_v, AttnSharedT<WAVES>& sh, float& M,
-                                           float& L, float* A8) {
+                                           float& L, float* A8, bool fp8_b = false) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -243,7 +305,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   KeyRegs ring[RING];
   pre();
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane);
+  for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane, false);
   mid();
   if (lane < n0 && lane >= na) {
     a = key_b(wb0 + lane - na);
@@ -254,7 +316,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   uint64_t okmask = __ballot(okl);
 #pragma unroll
   for (int u = 0; u < RING - 1; ++u)
-    if (u >= na && u < n0) load_key(ring[u], kp, vp, u, lane);   // slots that held dummies
+    if (u >= na && u < n0) load_key(ring[u], kp, vp, u, lane, fp8_b);   // slots that held dummies
   for (int g = 0; g < n; g += 64) {
     const int ng = min(64, n - g);
     if (g > 0) {
@@ -266,15 +328,16 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
       vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
 #pragma unroll
       for (int u = 0; u < RING - 1; ++u)
-        if (u < ng) load_key(ring[u], kp, vp, u, lane);
+        if (u < ng) load_key(ring[u], kp, vp, u, lane, fp8_b && g + u >= na);
     }
     for (int i = 0; i < ng; i += RING) {
 #pragma unroll
       for (int u = 0; u < RING; ++u) {
         const int x = i + u;
         if (x >= ng) break;
-        if (x + RING - 1 < ng) load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane);
-        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+        if (x + RING - 1 < ng)
+          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane, fp8_b && g + x + RING - 1 >= na);
+        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, fp8_b && g + x >= na);
       }
     }
   }

@@ -5,6 +5,8 @@
 //   swa_k, swa_v  [max_states][n_win][16][128] bf16   token p of state s in slot p mod n_win
 //   idx_tail      [max_states][128][4][64]   fp32     token p in slot p mod 128
 //   csa_k, csa_v  [max_blocks][32][16][128]  bf16     C4 entry j of a block = tokens 4j..4j+3
+//   (FP8 entries instead: c4q [max_blocks * 32][K, V][16][128] E4M3 codes and
+//    c4s [max_blocks * 32][K, V][16] fp32 per-head scales, head h at 4 (h % 4) + h / 4)
 //   hca_k, hca_v  [max_blocks][16][128]      bf16
 //   idx_k         [max_blocks][128][4][64]   fp32
 //   table         [max_states][table_stride] int32    logical block -> physical id
@@ -34,6 +36,9 @@ constexpr int kSealSplit = 8;      // workgroups per decode-time seal (16 tokens
 constexpr int kScoreSplit = HSA_SCORE_SPLIT;   // decode-step scoring workgroups per sealed block
 constexpr int kPartFloats = 2 * kH + 2 * kRow;  // one HCA seal partial: m, l, acc K, acc V
 constexpr int kMaxTopk = 4096;
+constexpr int kC4Bytes = 2 * kRow;      // FP8 C4 row: K codes then V codes, 2048 B each
+constexpr int kC4Scales = 2 * kH;       // FP8 C4 row: K scales then V scales
+constexpr float kE4M3Max = 448.f;       // largest finite OCP E4M3 value
 constexpr int kCacheN = 4096;      // top-k: scores kept in LDS (16 KiB); larger rows read through L2
 
 struct Pools {
@@ -49,8 +54,12 @@ struct Pools {
   int64_t table_stride;
   const float* gate_csa;
   const float* gate_hca;
+  uint8_t* c4q;         // FP8 entries: codes of C4 row r (block * 32 + slot) at r * kC4Bytes
+  float* c4s;           // FP8 entries: scales of C4 row r at r * kC4Scales
   int32_t n_win;
   int32_t max_blocks;   // physical ids are in [0, max_blocks)
+  int32_t fp8;          // 1: C4 entries are stored as FP8 (c4q, c4s); 0: bf16 (csa_k, csa_v)
+  int32_t pad_;
 };
 
 // One request of a launch: its state, its length and sealed-block count after the
@@ -189,6 +198,11 @@ __device__ __forceinline__ float4 load_global(const float4* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ int32_t load_global(const int32_t* p) { return *as_global(p); }
+typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2_v v = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x2_v*>(p)));
+  return make_uint2(v.x, v.y);
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -238,5 +252,56 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---------------------------------------------------------------- FP8 (OCP E4M3) entries
+
+// Address of C4 row `row` (block * 32 + slot) for attention: the bf16 K and V rows,
+// or, with FP8 entries, the code row and the scale row (see load_key).
+struct C4Addr {
+  const uint16_t* k;
+  const uint16_t* v;
+};
+__device__ __forceinline__ C4Addr c4_addr(const Pools& P, int64_t row) {
+  if (P.fp8)
+    return C4Addr{reinterpret_cast<const uint16_t*>(P.c4q + row * kC4Bytes),
+                  reinterpret_cast<const uint16_t*>(P.c4s + row * kC4Scales)};
+  return C4Addr{P.csa_k + row * kRow, P.csa_v + row * kRow};
+}
+
+// Per-head FP8 storage of 8 values per lane, the 16 lanes of a DPP row holding one
+// head's 128 values: with amax = max |x| over the head, scale = amax / 448 and
+// code = E4M3(x * (448 / amax)) rounded to nearest even (scale 1 and codes 0 for
+// an all-zero head); float32 throughout, each division correctly rounded. Returns
+// the 8 codes (value i in byte i) and the scale.
+__device__ __forceinline__ uint2 quantize8_e4m3(const float* x, float& scale) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = row_max16(amax);
+  // a head whose multiplier 448 / amax is not finite (zero, or amax below
+  // 448 / FLT_MAX) is stored as scale 1 and zero codes
+  float r = kE4M3Max / amax;
+  const bool ok = r <= __FLT_MAX__;
+  scale = ok ? amax / kE4M3Max : 1.f;
+  r = ok ? r : 0.f;
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * r, x[1] * r, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * r, x[3] * r, w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * r, x[5] * r, 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * r, x[7] * r, w1, true);
+  return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+// The four E4M3 codes of `w` (byte i = value i) as floats.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
+  const f32x2_v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo.x; f[1] = lo.y; f[2] = hi.x; f[3] = hi.y;
+}
+// Two values exactly representable in bf16 (every E4M3 value is) as a bf16 pair,
+// a in the low half.
+__device__ __forceinline__ uint32_t pack_exact_bf2(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
 
 }  // namespace hsa

@@ -484,6 +484,8 @@ int check_config(const hsa_config* cfg) {
   const int64_t bps = cfg->max_blocks_per_state ? cfg->max_blocks_per_state : cfg->max_blocks;
   if (bps < 1 || bps > (int64_t(1) << 24)) return fail(kInvalid, "max_blocks_per_state out of range");
   if (!cfg->gate_csa || !cfg->gate_hca) return fail(kInvalid, "gate weights are NULL");
+  if (cfg->entry_format != HSA_ENTRY_BF16 && cfg->entry_format != HSA_ENTRY_FP8)
+    return fail(kInvalid, "entry_format must be HSA_ENTRY_BF16 or HSA_ENTRY_FP8");
   return kOk;
 }
 
@@ -509,15 +511,18 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
       c->step_slots = n_cu;
   }
   const size_t S = (size_t)cfg->max_states, NB = (size_t)cfg->max_blocks, W = (size_t)cfg->n_win;
-  void* p[11] = {};
-  const size_t bytes[11] = {
+  const bool fp8 = cfg->entry_format == HSA_ENTRY_FP8;
+  void* p[13] = {};
+  const size_t bytes[13] = {
       S * W * kRow * 2, S * W * kRow * 2, S * kBlk * kIRow * 4,            // swa_k, swa_v, idx_tail
-      NB * kC4 * kRow * 2, NB * kC4 * kRow * 2, NB * kRow * 2, NB * kRow * 2,  // csa, hca
+      fp8 ? 0 : NB * kC4 * kRow * 2, fp8 ? 0 : NB * kC4 * kRow * 2,       // csa (bf16 entries)
+      NB * kRow * 2, NB * kRow * 2,                                       // hca
       NB * kBlk * kIRow * 4,                                              // idx_k
       S * (size_t)bps * 4,                                                // table
       2 * kRow * 4,                                                       // gates
-      (size_t)kMaxReq * kSealSplit * kPartFloats * 4};                    // seal partials
-  for (int i = 0; i < 11; ++i) {
+      (size_t)kMaxReq * kSealSplit * kPartFloats * 4,                     // seal partials
+      fp8 ? NB * kC4 * kC4Bytes : 0, fp8 ? NB * kC4 * kC4Scales * 4 : 0};  // FP8 C4 codes, scales
+  for (int i = 0; i < 13; ++i) {
     st = dev_alloc(c, &p[i], bytes[i]);
     if (st) {
       hsa_destroy(c);
@@ -540,6 +545,9 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   c->P.n_win = cfg->n_win;
   c->P.max_blocks = (int32_t)cfg->max_blocks;
   c->seal_part = static_cast<float*>(p[10]);
+  c->P.c4q = static_cast<uint8_t*>(p[11]);
+  c->P.c4s = static_cast<float*>(p[12]);
+  c->P.fp8 = fp8 ? 1 : 0;
   // attention partials: a decode step has at most max(slots, requests) workgroups per
   // part, and hsa_decode_attend at most max(64, target - n) + n <= target + 64, so
   // these never grow (no device synchronisation in a decode loop)
@@ -744,6 +752,7 @@ hsa_status hsa_export_block(hsa_ctx* c, int32_t b, void* csa_k, void* csa_v, voi
   if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
   int st = set_device(c);
   if (st) return st;
+  if (c->P.fp8 && (csa_k || csa_v)) return fail(kInvalid, "FP8 entries: export them with hsa_export_c4_fp8");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t B = (size_t)b;
   if (csa_k) HIP_TRY(hipMemcpyAsync(csa_k, c->P.csa_k + B * kC4 * kRow, kC4 * kRow * 2, hipMemcpyDeviceToHost, s));
@@ -752,6 +761,39 @@ hsa_status hsa_export_block(hsa_ctx* c, int32_t b, void* csa_k, void* csa_v, voi
   if (hca_v) HIP_TRY(hipMemcpyAsync(hca_v, c->P.hca_v + B * kRow, kRow * 2, hipMemcpyDeviceToHost, s));
   if (idx_k) HIP_TRY(hipMemcpyAsync(idx_k, c->P.idx_k + B * kBlk * kIRow, kBlk * kIRow * 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
+  return kOk;
+}
+
+hsa_status hsa_export_c4_fp8(hsa_ctx* c, int32_t b, uint8_t* codes_k, uint8_t* codes_v,
+                             float* scale_k, float* scale_v, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->P.fp8) return fail(kInvalid, "the context stores bf16 entries");
+  if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* q = c->P.c4q + (size_t)b * kC4 * kC4Bytes;
+  if (codes_k) HIP_TRY(hipMemcpy2DAsync(codes_k, kRow, q, kC4Bytes, kRow, kC4, hipMemcpyDeviceToHost, s));
+  if (codes_v) HIP_TRY(hipMemcpy2DAsync(codes_v, kRow, q + kRow, kC4Bytes, kRow, kC4, hipMemcpyDeviceToHost, s));
+  std::vector<float> sc((size_t)kC4 * kC4Scales);
+  HIP_TRY(hipMemcpyAsync(sc.data(), c->P.c4s + (size_t)b * kC4 * kC4Scales, sc.size() * 4,
+                         hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  for (int e = 0; e < kC4; ++e)
+    for (int h = 0; h < kH; ++h) {   // stored at 4 (h % 4) + h / 4 (the attention lane order)
+      const int hp = 4 * (h % 4) + h / 4;
+      if (scale_k) scale_k[e * kH + h] = sc[(size_t)e * kC4Scales + hp];
+      if (scale_v) scale_v[e * kH + h] = sc[(size_t)e * kC4Scales + kH + hp];
+    }
+  return kOk;
+}
+
+hsa_status hsa_fp8_quantize_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
+                                 void* stream) {
+  if (n_rows < 0 || n_rows > (int64_t(1) << 34)) return fail(kInvalid, "n_rows out of range");
+  if (n_rows == 0) return kOk;
+  if (!x || !codes || !scales) return fail(kInvalid, "NULL buffer");
+  HIP_TRY(launch_fp8_rows(x, n_rows, codes, scales, static_cast<hipStream_t>(stream)));
   return kOk;
 }
 

@@ -61,6 +61,10 @@ hipError_t launch_select(const ReqBatch& B, const SelPlan& SP, int32_t k, int32_
                          const float* scores, int64_t ld, int32_t* idx_out, float* score_out,
                          hipStream_t st, const LaunchEv& ev = LaunchEv{});
 
+// Per-row FP8 storage (the C4 entry quantisation) of n_rows rows of 128 floats.
+hipError_t launch_fp8_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
+                           hipStream_t st);
+
 // attend.hip
 // Keys of request i: min(len, n_win) SWA + nb HCA + min(k, 32 nb) C4 slots, cut in
 // chunks of `chunk` keys (a multiple of 16); one workgroup per chunk writes an

@@ -50,11 +50,13 @@ struct TokSrc {
 
 constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
 
-// Seal tokens [t0, t0 + 16) of one block: writes their 4 C4 entries and 16
+// Seal tokens [t0, t0 + 16) of one block (C4 entries bf16, or FP8 when FP8, which
+// the caller sets from P.fp8): writes their 4 C4 entries and 16
 // indexer keys, and returns the HCA softmax partial (m, l, acc) of these tokens
 // for this lane's 8 dims. Both seal paths build the HCA entry from the same eight
 // partials merged in the same order, so bulk and one-token appends give
 // bit-identical blocks.
+template <bool FP8>
 __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int32_t id, int t0,
                                           float& m, float& l, float* acck, float* accv) {
   const int tid = threadIdx.x;
@@ -107,7 +109,34 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       gc[u] = row_sum16(a);
       gh[u] = row_sum16(b);
     }
-    // C4 entry (tokens tb .. tb+3): softmax of the 4 CSA gates
+    // HCA running softmax over the block's tokens
+    {
+      const float mx = fmaxf(m, fmaxf(fmaxf(gh[0], gh[1]), fmaxf(gh[2], gh[3])));
+      const float sc = __expf(m - mx);   // m = -inf on the first group -> 0
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = __expf(gh[u] - mx);
+      l = l * sc + ((e[0] + e[1]) + (e[2] + e[3]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acck[i] *= sc;
+        accv[i] *= sc;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float kf[8], vf[8];
+        unpack8(kw[u], kf);
+        unpack8(vw[u], vf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acck[i] = fmaf(e[u], kf[i], acck[i]);
+          accv[i] = fmaf(e[u], vf[i], accv[i]);
+        }
+      }
+      m = mx;
+    }
+    // C4 entry (tokens tb .. tb+3): softmax of the 4 CSA gates (after the HCA
+    // update, so the packed tokens are dead while an FP8 entry is quantised)
     {
       const float mx = fmaxf(fmaxf(gc[0], gc[1]), fmaxf(gc[2], gc[3]));
       float e[4], s = 0.f;
@@ -137,39 +166,30 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
         cv[i] *= inv;
       }
       const int slot = tb >> 2;
-      uint4 ok, ov;
-      ok.x = pack_bf2(ck[0], ck[1]); ok.y = pack_bf2(ck[2], ck[3]);
-      ok.z = pack_bf2(ck[4], ck[5]); ok.w = pack_bf2(ck[6], ck[7]);
-      ov.x = pack_bf2(cv[0], cv[1]); ov.y = pack_bf2(cv[2], cv[3]);
-      ov.z = pack_bf2(cv[4], cv[5]); ov.w = pack_bf2(cv[6], cv[7]);
-      *reinterpret_cast<uint4*>(csa_k + (int64_t)slot * kRow + off) = ok;
-      *reinterpret_cast<uint4*>(csa_v + (int64_t)slot * kRow + off) = ov;
-    }
-    // HCA running softmax over the block's tokens
-    {
-      const float mx = fmaxf(m, fmaxf(fmaxf(gh[0], gh[1]), fmaxf(gh[2], gh[3])));
-      const float sc = __expf(m - mx);   // m = -inf on the first group -> 0
-      float e[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) e[u] = __expf(gh[u] - mx);
-      l = l * sc + ((e[0] + e[1]) + (e[2] + e[3]));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acck[i] *= sc;
-        accv[i] *= sc;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float kf[8], vf[8];
-        unpack8(kw[u], kf);
-        unpack8(vw[u], vf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          acck[i] = fmaf(e[u], kf[i], acck[i]);
-          accv[i] = fmaf(e[u], vf[i], accv[i]);
+      if (FP8) {
+        // FP8 entry: per head, E4M3 codes and a float32 scale (lanes 16h .. 16h+15
+        // hold head h, so the scale's max runs over one DPP row)
+        const int64_t row = (int64_t)id * kC4 + slot;
+        float sk, sv;
+        const uint2 qk = quantize8_e4m3(ck, sk);
+        const uint2 qv = quantize8_e4m3(cv, sv);
+        uint8_t* q = P.c4q + row * kC4Bytes;
+        *reinterpret_cast<uint2*>(q + off) = qk;
+        *reinterpret_cast<uint2*>(q + kRow + off) = qv;
+        if ((tid & 15) == 0) {
+          const int hp = 4 * (h & 3) + (h >> 2);   // the order attention lanes read
+          P.c4s[row * kC4Scales + hp] = sk;
+          P.c4s[row * kC4Scales + kH + hp] = sv;
         }
+      } else {
+        uint4 ok, ov;
+        ok.x = pack_bf2(ck[0], ck[1]); ok.y = pack_bf2(ck[2], ck[3]);
+        ok.z = pack_bf2(ck[4], ck[5]); ok.w = pack_bf2(ck[6], ck[7]);
+        ov.x = pack_bf2(cv[0], cv[1]); ov.y = pack_bf2(cv[2], cv[3]);
+        ov.z = pack_bf2(cv[4], cv[5]); ov.w = pack_bf2(cv[6], cv[7]);
+        *reinterpret_cast<uint4*>(csa_k + (int64_t)slot * kRow + off) = ok;
+        *reinterpret_cast<uint4*>(csa_v + (int64_t)slot * kRow + off) = ov;
       }
-      m = mx;
     }
   }
 }
@@ -225,6 +245,7 @@ __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i
 // 4 C4 entries, 16 indexer keys and one HCA partial to part[item * 8 + sub]. The
 // newest token (position r.len - 1) is read from input row i, so this may run in
 // the same launch as append_token. 256 threads.
+template <bool FP8>
 __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i, int item, int sub,
                                             const uint16_t* kin, const uint16_t* vin,
                                             const float* iin, float* part) {
@@ -240,7 +261,7 @@ __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i,
   src.pos0 = (int64_t)(r.nb - 1) * kBlk;
   src.n_win = P.n_win;
   float m, l, acck[8], accv[8];
-  seal_part(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
+  seal_part<FP8>(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
   float* mine = part + (int64_t)(item * kSealSplit + sub) * kPartFloats;
   const int h = tid >> 4;
   if ((tid & 15) == 0) {

@@ -77,13 +77,16 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
   }
 }
 
-__global__ __launch_bounds__(256, 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
+// FP8 entries: the seal's quantisation needs more registers than 4 workgroups per
+// CU leave, so that instance runs 3 per CU; the bf16 instance keeps 4.
+template <bool FP8>
+__global__ __launch_bounds__(256, FP8 ? 3 : 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
   int bid = blockIdx.x;
   // -- seal eighths (first, so the longest single workgroups start early)
   if (bid < kSealSplit * B.n_seal) {
     const int item = bid / kSealSplit;
     const int ri = B.seal_req[item];
-    seal_eighth(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
+    seal_eighth<FP8>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
     return;
   }
   bid -= kSealSplit * B.n_seal;
@@ -197,8 +200,9 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
     a.k = a.v = nullptr;
     const int64_t row = sh.rows[x - b0];
     if (row < 0 || row >= max_row) return a;   // never taken
-    a.k = P.csa_k + row * kRow;
-    a.v = P.csa_v + row * kRow;
+    const C4Addr c = c4_addr(P, row);
+    a.k = c.k;
+    a.v = c.v;
     return a;
   };
   const int64_t k = S.k;
@@ -212,7 +216,8 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   };
   float M, L, A8[8];
   attend_two<WAVES, kMixedRing>(key_a, a0, a1, key_b, b0, b1, stage, select,
-                                         S.q + (int64_t)r * kRow, ring_k, ring_v, sh.attn, M, L, A8);
+                                         S.q + (int64_t)r * kRow, ring_k, ring_v, sh.attn, M, L, A8,
+                                         P.fp8 != 0);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
@@ -275,14 +280,16 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
     }
     const int64_t row = rows[x - sn];   // C4 row of a selected entry, from S2
     if (row < 0 || row >= max_row) return a;   // never taken
-    a.k = P.csa_k + row * kRow;
-    a.v = P.csa_v + row * kRow;
+    const C4Addr c = c4_addr(P, row);
+    a.k = c.k;
+    a.v = c.v;
     return a;
   };
   const uint16_t* dk = P.swa_k + (int64_t)R.state * P.n_win * kRow;   // valid row (L >= 1)
   const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
   float M, L, A8[8];
-  attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh, M, L, A8);
+  attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh, M, L, A8,
+                           P.fp8 ? sn : 0x7fffffff);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
@@ -306,7 +313,8 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
                  const LaunchEv& ev) {
   const int grid = kSealSplit * B.n_seal + B.n + S.n_score;
   if (grid == 0) return hipSuccess;
-  return launch_k(k_step1, dim3(grid), dim3(kAttnWaves * 64), st, ev, P, B, S);
+  if (P.fp8) return launch_k(k_step1<true>, dim3(grid), dim3(kAttnWaves * 64), st, ev, P, B, S);
+  return launch_k(k_step1<false>, dim3(grid), dim3(kAttnWaves * 64), st, ev, P, B, S);
 }
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,

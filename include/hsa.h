@@ -74,7 +74,18 @@ typedef struct hsa_config {
   int64_t max_blocks_per_state; /* block-table row length; 0 = max_blocks           */
   const float* gate_csa;        /* host [n_heads][head_dim] compressor gate, copied */
   const float* gate_hca;        /* host [n_heads][head_dim] compressor gate, copied */
+  int32_t entry_format;         /* storage of C4 entries: HSA_ENTRY_BF16 or
+                                   HSA_ENTRY_FP8 ([Ch12] §2.2 accounts entries in FP8) */
+  int32_t reserved;             /* 0                                                */
 } hsa_config;
+
+/* C4 entry storage. BF16: K and V rows of 16 x 128 bf16. FP8: per head, 128 OCP
+ * FP8 E4M3 codes and one float32 scale s = max |x| / 448 over the head's 128 values
+ * (1 for an all-zero head); code = E4M3(x / s), round to nearest, ties to even,
+ * taken in float32; the entry reads as code value * s. The pages give no scale
+ * scheme: this per-head scale is the reading used. HCA entries are always bf16. */
+#define HSA_ENTRY_BF16 0
+#define HSA_ENTRY_FP8 1
 
 typedef struct hsa_state_info {
   int64_t len;          /* L, tokens appended so far                                 */
@@ -88,9 +99,11 @@ typedef struct hsa_state_info {
 /* Create a context on `device`: validates `cfg`, allocates every pool in device
  * memory (owned by the context until hsa_destroy) and copies the gates.
  * Pools: SWA ring K and V [max_states][n_win][16][128] bf16, indexer tail
- * [max_states][128][4][64] fp32, C4 K and V [max_blocks][32][16][128] bf16,
- * HCA K and V [max_blocks][16][128] bf16, indexer keys [max_blocks][128][4][64]
- * fp32, block table [max_states][max_blocks_per_state] int32.
+ * [max_states][128][4][64] fp32, C4 K and V [max_blocks][32][16][128] bf16 (FP8
+ * entries: codes [max_blocks][32][K, V][16][128] u8 and scales
+ * [max_blocks][32][K, V][16] fp32), HCA K and V [max_blocks][16][128] bf16, indexer
+ * keys [max_blocks][128][4][64] fp32, block table [max_states][max_blocks_per_state]
+ * int32.
  * ([Q&A] §1.1: two pools with different lifetimes; [Ch12] §2.1, §2.2.) */
 hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out);
 hsa_status hsa_destroy(hsa_ctx* ctx);
@@ -183,9 +196,23 @@ hsa_status hsa_block_table_get(hsa_ctx* ctx, int32_t state, int32_t* ids, int64_
                                int64_t* n);
 hsa_status hsa_block_refcount(hsa_ctx* ctx, int32_t block, int32_t* rc);
 /* Copy one block to host buffers (any may be NULL): csa_k, csa_v bf16
- * [32][16][128]; hca_k, hca_v bf16 [16][128]; idx_k fp32 [128][4][64]. */
+ * [32][16][128] (must be NULL with FP8 entries: see hsa_export_c4_fp8); hca_k,
+ * hca_v bf16 [16][128]; idx_k fp32 [128][4][64]. */
 hsa_status hsa_export_block(hsa_ctx* ctx, int32_t block, void* csa_k, void* csa_v,
                             void* hca_k, void* hca_v, float* idx_k, void* stream);
+/* FP8 entries only: copy one block's C4 entries to host buffers (any may be NULL):
+ * codes_k, codes_v u8 [32][16][128] E4M3 codes; scale_k, scale_v fp32 [32][16]
+ * per-head scales. HSA_ERR_INVALID with bf16 entries. */
+hsa_status hsa_export_c4_fp8(hsa_ctx* ctx, int32_t block, uint8_t* codes_k, uint8_t* codes_v,
+                             float* scale_k, float* scale_v, void* stream);
+
+/* The FP8 entry quantisation on its own (the one the seal applies to each head of a
+ * C4 entry): for each of n_rows rows of 128 float32 values (device x
+ * [n_rows][128]), writes device codes u8 [n_rows][128] and scales fp32 [n_rows].
+ * Needs no context; n_rows >= 0. */
+hsa_status hsa_fp8_quantize_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
+                                 void* stream);
+
 /* Copy one State block to host buffers (any may be NULL): swa_k, swa_v bf16
  * [n_win][16][128] in ring-slot order (token p sits in slot p mod n_win);
  * idx_tail fp32 [128][4][64] (token p in slot p mod 128). */

@@ -44,9 +44,11 @@ Readings taken where the pages leave a step open (each also in the design notes)
   R15 FP8 entries (optional format): the pages account compressed entries in FP8
       ([Ch12] §2.2) without a scale scheme. Reading: each C4 entry's K and V are
       stored per head as 128 OCP FP8 E4M3 codes and one float32 scale
-      s = max_d |x_d| / 448 (1 when the head is all zero); code_d = E4M3 of
-      x_d / s, nearest-even; the stored value is code_value * s. The decisions
-      (x as float32, s, x / s) are taken in float32, the precision the kernel
+      s = max_d |x_d| / 448; code_d = E4M3 of x_d * (448 / max_d |x_d|),
+      nearest-even; the stored value is code_value * s. A head whose 448 / max|x|
+      is not a finite float32 (all zero, or max|x| below 448 / FLT_MAX, about
+      1.3e-36) is stored as s = 1 and codes 0. The decisions (x as float32, both divisions correctly
+      rounded, the product) are taken in float32, the precision the kernel
       computes in. HCA entries stay bf16.
 """
 
@@ -131,12 +133,17 @@ def e4m3_encode(x) -> np.ndarray:
 def quantize_e4m3_rows(x) -> tuple:
     """Per-row FP8 storage of [..., 128] rows (reading R15): returns (codes uint8,
     scales float32 [...], values float64 = code value * scale). The row is taken as
-    float32; s = float32(max |x| / 448) (1 for an all-zero row); each code is the
-    E4M3 of float32(x / s)."""
+    float32; with amax = max |x|, s = float32(amax / 448) and each code is the E4M3
+    of float32(x * float32(448 / amax)). A row whose 448 / amax is not a finite
+    float32 (all zero, or amax below 448 / FLT_MAX) is stored as s = 1, codes 0."""
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     amax = np.abs(x32).max(axis=-1)
-    s = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0)).astype(np.float32)
-    y = (x32 / s[..., None]).astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        r = (np.float32(E4M3_MAX) / amax).astype(np.float32)
+    ok = np.isfinite(r)                 # amax > 448 / FLT_MAX (so also nonzero)
+    s = np.where(ok, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0)).astype(np.float32)
+    r = np.where(ok, r, np.float32(0.0)).astype(np.float32)
+    y = (x32 * r[..., None]).astype(np.float32)
     codes = e4m3_encode(y)
     vals = e4m3_decode(codes) * s[..., None].astype(np.float64)
     return codes, s, vals

@@ -513,10 +513,11 @@ def test_e4m3_encode_is_nearest_ties_to_even():
 
 
 def test_quantize_rows_bounds_and_special_cases():
-    """Per-row FP8 storage: the largest magnitude stores as +-448 * s (up to the
-    float32 rounding of s), every value within half a code spacing (times s) of
-    the row, an all-zero row stays zero with scale 1, and a row and its negation
-    store with mirrored codes."""
+    """Per-row FP8 storage: the largest magnitude stores as +-448 (code 0x7e), every
+    value within half a code spacing of x * 448 / max |x| (up to the float32
+    rounding of the product), an all-zero row or one too small for a finite
+    multiplier stays zero with scale 1, and a row and its negation store with
+    mirrored codes."""
     from oracle import e4m3_decode, quantize_e4m3_rows
     rng = np.random.default_rng(9)
     x = rng.standard_normal((64, 128)) * np.exp(rng.uniform(-8, 8, (64, 1)))
@@ -524,14 +525,20 @@ def test_quantize_rows_bounds_and_special_cases():
     x32 = x.astype(np.float32).astype(np.float64)
     amax_i = np.abs(x32).argmax(axis=1)
     assert np.all((codes[np.arange(64), amax_i] & 0x7F) == 0x7E)
-    y = x32 / s[:, None].astype(np.float64)
+    y = x32 * 448.0 / np.abs(x32).max(axis=1, keepdims=True)
     grid = e4m3_decode(np.arange(0x7F))
     idx = np.clip(np.searchsorted(grid, np.abs(y)), 1, len(grid) - 1)
     spacing = grid[idx] - grid[idx - 1]
-    assert np.all(np.abs(e4m3_decode(codes) - y) <= spacing / 2 * (1 + 1e-6) + 1e-12)
+    assert np.all(np.abs(e4m3_decode(codes) - y) <= spacing / 2 * (1 + 1e-5) + 1e-9)
     assert np.allclose(vals, e4m3_decode(codes) * s[:, None])
     zc, zs, zv = quantize_e4m3_rows(np.zeros((2, 128)))
     assert np.all(zc == 0) and np.all(zs == 1.0) and np.all(zv == 0)
+    # 448 / amax overflows float32 below amax = 448 / FLT_MAX (~1.32e-36): such a row
+    # is stored as zero; just above it the row quantizes normally
+    tiny = np.array([np.full(128, 1e-38), np.full(128, 1.0e-36), np.full(128, 2.0e-36)])
+    tc, ts, tv = quantize_e4m3_rows(tiny)
+    assert np.all(tc[:2] == 0) and np.all(ts[:2] == 1.0) and np.all(tv[:2] == 0)
+    assert np.all(tc[2] == 0x7E) and np.isclose(tv[2], 2.0e-36, rtol=1e-6).all()
     nc, ns, _ = quantize_e4m3_rows(-x)
     assert np.array_equal(ns, s) and np.array_equal(nc, codes ^ 0x80)
 
