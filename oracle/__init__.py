@@ -13,4 +13,5 @@ from .cache import (  # noqa: F401
     OracleError, Oracle, bf16_round, gated_pool, token_scores, c4_scores,
     select_topk, attention, length_split, block_range_summary, decode_reference,
     E4M3_MAX, e4m3_decode, e4m3_encode, quantize_e4m3_rows,
+    MX_BLOCK, e2m1_decode, e2m1_encode, quantize_mxfp4_rows,
 )

@@ -50,6 +50,16 @@ Readings taken where the pages leave a step open (each also in the design notes)
       1.3e-36) is stored as s = 1 and codes 0. The decisions (x as float32, both divisions correctly
       rounded, the product) are taken in float32, the precision the kernel
       computes in. HCA entries stay bf16.
+  R16 low-bit indexer keys (optional format): the pages store the indexer keys
+      of the Block Cache as FP4 ([Ch12] §1 worked figures, §2.2) without a scale
+      scheme. Reading: OCP MXFP4 (Microscaling Formats v1.0): each sealed key's
+      256 values split into 8 blocks of 32 (head h, half j = block 2h + j); a
+      block has one E8M0 scale 2**E, E = floor(log2 max|x|) - 2 (2 is E2M1's
+      largest exponent), at least -127 (-127 for an all-zero block), and each
+      value is the E2M1 code of x / 2**E: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+      ties to the even code, saturating at 6, sign bit set for x < 0. The key
+      reads as code value * 2**E. The open block's keys (the State's indexer
+      tail) stay float32 until the block seals; the query stays float32.
 """
 
 from __future__ import annotations
@@ -147,6 +157,60 @@ def quantize_e4m3_rows(x) -> tuple:
     codes = e4m3_encode(y)
     vals = e4m3_decode(codes) * s[..., None].astype(np.float64)
     return codes, s, vals
+
+
+# ---------------------------------------------------------------- MXFP4 (reading R16)
+# OCP Microscaling: E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa
+# bit; exponent field 0 is subnormal) under an E8M0 scale (a byte b = 2**(b - 127)).
+
+MX_BLOCK = 32
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each 4-bit E2M1 code (float64): exponent field 0 gives m / 2,
+    otherwise 2**(e - 1) * (1 + m / 2)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, m / 2.0, np.ldexp(1.0 + m / 2.0, e - 1))
+    return sign * mag
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """E2M1 code of each value: the nearest representable magnitude, ties to the
+    even code, magnitudes beyond the largest (6) saturating to it; the sign bit is
+    set for y < 0 (also when the magnitude rounds to 0)."""
+    y = np.asarray(y, dtype=np.float64)
+    codes = np.arange(8)
+    vals = e2m1_decode(codes)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (codes[hi] % 2 == 0))
+    c = np.where(pick_hi, codes[hi], codes[lo])
+    c = np.where(a >= vals[-1], 7, c)
+    return (c | np.where(y < 0, 8, 0)).astype(np.uint8)
+
+
+def quantize_mxfp4_rows(x) -> tuple:
+    """MXFP4 storage of indexer keys [..., 256] (reading R16): returns (codes uint8
+    [..., 128] with value 2i in the low nibble of byte i and value 2i + 1 in the
+    high nibble, scales uint8 [..., 8] E8M0 bytes E + 127, values float64 [..., 256]
+    = code value * 2**E). Keys are taken as float32."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    shp = x32.shape
+    blocks = x32.reshape(*shp[:-1], shp[-1] // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(amax)                    # amax = f * 2**ex, f in [0.5, 1)
+    E = np.where(amax > 0, np.maximum(ex - 1 - 2, -127), -127).astype(np.int64)
+    y = blocks / np.ldexp(1.0, E)[..., None]   # exact: a power-of-two scale
+    c = e2m1_encode(y)
+    vals = (e2m1_decode(c) * np.ldexp(1.0, E)[..., None]).reshape(shp)
+    c = c.reshape(shp).astype(np.uint8)
+    codes = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    return codes, (E + 127).astype(np.uint8), vals
 
 
 def length_split(L: int) -> dict:
@@ -303,9 +367,11 @@ def decode_reference(seq, n_win: int, gate_csa, gate_hca, cases, pmap=map, chunk
 class _Block:
     """One sealed, immutable Block Cache block: 32 C4 + 1 HCA + 128 indexer keys
     ([Ch12] §2.2; [Q&A] §2.2). With FP8 entries (R15) csa_k / csa_v hold the stored
-    values (code value * scale) and the codes and scales are kept beside them."""
+    values (code value * scale) and the codes and scales are kept beside them; with
+    MXFP4 indexer keys (R16) idx holds the stored values and idx_codes / idx_scales
+    the codes and E8M0 scales."""
     __slots__ = ("csa_k", "csa_v", "hca_k", "hca_v", "idx", "csa_k_codes", "csa_v_codes",
-                 "csa_k_scale", "csa_v_scale")
+                 "csa_k_scale", "csa_v_scale", "idx_codes", "idx_scales")
 
 
 class _State:
@@ -323,12 +389,15 @@ class Oracle:
     """The cache, driven call by call like the C ABI."""
 
     def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int,
-                 entry_format: str = "bf16"):
+                 entry_format: str = "bf16", index_format: str = "f32"):
         if n_win < BLOCK or n_win % BLOCK:
             raise OracleError("invalid", "n_win must be a positive multiple of 128")
         if entry_format not in ("bf16", "fp8"):
             raise OracleError("invalid", "entry format is bf16 or fp8")
+        if index_format not in ("f32", "mxfp4"):
+            raise OracleError("invalid", "index format is f32 or mxfp4")
         self.entry_format = entry_format
+        self.index_format = index_format
         self.n_win = int(n_win)
         self.W_csa = np.asarray(gate_csa, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
         self.W_hca = np.asarray(gate_hca, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
@@ -448,7 +517,13 @@ class Oracle:
             else:
                 blk.csa_k[j], blk.csa_v[j] = gated_pool(Kt[g], Vt[g], self.W_csa)
         blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)     # all 128 tokens
-        blk.idx = np.stack([t[2] for t in st.tail]).astype(np.float32)
+        keys = np.stack([t[2] for t in st.tail]).astype(np.float32)       # [128][4][64]
+        if self.index_format == "mxfp4":              # reading R16
+            codes, scales, vals = quantize_mxfp4_rows(keys.reshape(BLOCK, -1))
+            blk.idx = vals.reshape(keys.shape)
+            blk.idx_codes, blk.idx_scales = codes, scales
+        else:
+            blk.idx = keys
         self.store[b] = blk
         self.refcount[b] = 1
         st.blocks.append(b)

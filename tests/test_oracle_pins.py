@@ -571,3 +571,129 @@ def test_fp8_oracle_entries_quantize_the_pooled_entry():
     Kc = np.concatenate([np.stack([t[0] for t in b.states[0].swa]), bb.hca_k[None], bb.csa_k[sel]])
     Vc = np.concatenate([np.stack([t[1] for t in b.states[0].swa]), bb.hca_v[None], bb.csa_v[sel]])
     assert np.allclose(b.attend(0, q, sel, 3), attention(q, Kc, Vc), atol=1e-12)
+
+
+# ---------------------------------------------------------------- MXFP4 indexer keys (R16)
+
+def test_e2m1_decode_is_the_format_table():
+    """The 16 E2M1 codes against the element table of the OCP Microscaling spec:
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7, the same negated for 8..15."""
+    from oracle import e2m1_decode
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(e2m1_decode(np.arange(8)), table)
+    assert np.array_equal(e2m1_decode(np.arange(8, 16)), [-t for t in table])
+
+
+def test_e2m1_encode_is_nearest_ties_to_even_saturating():
+    """Brute force over the 8 magnitudes for random values and every midpoint: the
+    code is a nearest one, the even one on a tie; beyond 6 it saturates; the sign
+    bit follows y < 0."""
+    from oracle import e2m1_decode, e2m1_encode
+    vals = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rng = np.random.default_rng(3)
+    y = np.concatenate([rng.uniform(0, 7, 3000), (vals[1:] + vals[:-1]) / 2, vals])
+    c = e2m1_encode(y)
+    for yi, ci in zip(y, c):
+        d = np.abs(vals - min(yi, 6.0))
+        best = np.flatnonzero(d == d.min())
+        assert ci in best
+        if len(best) == 2:
+            assert ci % 2 == 0
+    assert list(e2m1_encode([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])) == [0, 2, 2, 4, 4, 6, 6]
+    assert list(e2m1_encode([6.0, 7.9, 100.0])) == [7, 7, 7]
+    nz = y > 0
+    assert np.array_equal(e2m1_encode(-y[nz]), c[nz] | 8) and e2m1_encode([-0.0])[0] == 0
+    assert e2m1_encode([-0.1])[0] == 8 and e2m1_decode([8])[0] == 0.0
+
+
+def test_mxfp4_hand_worked_row():
+    """A row worked by hand. Block 0 = [1, 2, -0.3, 0...]: max 2, E = 1 - 2 = -1, so
+    x / 2**E = [2, 4, -0.6]: codes 4 (2.0), 6 (4.0), 9 (-0.5); bytes 0x64, 0x09.
+    Block 1 all zero: E = -127 (byte 0), codes 0. Block 2 = [6 * 2**-5, 5 * 2**-5]:
+    max 0.1875 = 1.5 * 2**-3, E = -5: 6 -> code 7, 5 is the 4/6 midpoint -> code 6
+    (4.0, even); byte 0x67, value 4 * 2**-5 = 0.125."""
+    from oracle import quantize_mxfp4_rows
+    x = np.zeros(256, np.float32)
+    x[0:3] = [1.0, 2.0, -0.3]
+    x[64:66] = [6 * 2.0 ** -5, 5 * 2.0 ** -5]
+    codes, scales, vals = quantize_mxfp4_rows(x)
+    assert codes[0] == 0x64 and codes[1] == 0x09 and np.all(codes[2:16] == 0)
+    assert codes[32] == 0x67
+    assert scales[0] == 127 - 1 and scales[1] == 0 and scales[2] == 127 - 5
+    assert list(vals[:3]) == [1.0, 2.0, -0.25] and vals[64] == 0.1875 and vals[65] == 0.125
+
+
+def test_mxfp4_bounds_round_trip_and_scale():
+    """Each value within half an E2M1 spacing (times 2**E) of the key, block maxima
+    landing on code 6 or 7 (x / 2**E in [4, 8)), exact round trip of values already
+    on the grid, mirrored codes under negation, and 2**E as the E8M0 byte."""
+    from oracle import e2m1_decode, quantize_mxfp4_rows
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((40, 256)) * np.exp(rng.uniform(-10, 10, (40, 8))).repeat(32, axis=1)).astype(np.float32)
+    codes, scales, vals = quantize_mxfp4_rows(x)
+    E = scales.astype(np.int64) - 127
+    step = np.ldexp(1.0, E).repeat(32, axis=1)               # 2**E per value
+    c = np.stack([codes & 15, codes >> 4], axis=-1).reshape(40, 256)
+    assert np.array_equal(vals, e2m1_decode(c) * step)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    y = np.abs(x.astype(np.float64)) / step
+    idx = np.clip(np.searchsorted(grid, np.minimum(y, 6.0)), 1, 7)
+    half = (grid[idx] - grid[idx - 1]) / 2
+    assert np.all(np.abs(np.abs(vals) / step - np.minimum(y, 6.0)) <= half + 1e-12)
+    blk = np.abs(x.astype(np.float64)).reshape(40, 8, 32)
+    amax = blk.max(axis=-1)
+    assert np.all((amax / np.ldexp(1.0, E) >= 4) & (amax / np.ldexp(1.0, E) < 8))
+    cm = (c.reshape(40, 8, 32)[np.arange(40)[:, None], np.arange(8)[None], blk.argmax(-1)]) & 7
+    assert np.all((cm == 6) | (cm == 7))
+    c2, s2, v2 = quantize_mxfp4_rows(vals)
+    assert np.array_equal(v2, vals)
+    cn, sn, _ = quantize_mxfp4_rows(-x)
+    assert np.array_equal(sn, scales)
+    nz = (np.stack([codes & 15, codes >> 4], -1).reshape(40, 256) != 0) | (x != 0)
+    assert np.all(((np.stack([cn & 15, cn >> 4], -1).reshape(40, 256) ^ c) == 8)[nz])
+
+
+def test_mxfp4_scores_are_exact_in_float32():
+    """The property the bit-exact top-k parity rests on: with the dyadic synthetic
+    keys and queries (odd multiples of 2**-8 below 3), every partial sum of a C4
+    score over MXFP4 keys is a multiple of 2**(E_min - 9) far below 2**24 such
+    units, so float32 sums in any order equal the float64 score. Checked by summing
+    in float32 in two orders against c4_scores in float64."""
+    from oracle import quantize_mxfp4_rows
+    KI = synth.tokens_f32(SEED, synth.STREAM_IDXK, 7, np.arange(1024)).reshape(1024, -1).astype(np.float64)
+    qi = synth.tokens_f32(SEED, synth.STREAM_QI, 7, np.array([1024])).reshape(-1).astype(np.float64)
+    codes, scales, vals = quantize_mxfp4_rows(KI)
+    ref = c4_scores(vals.reshape(1024, 4, 64)[:128], qi.reshape(4, 64))
+    prod = (vals[:128] * qi[None, :]).reshape(32, 4 * 256)
+    E_min = int(scales.min()) - 127
+    assert np.abs(prod).sum(axis=1).max() < 2.0 ** (24 + E_min - 9)
+    fwd = np.zeros(32, np.float32)
+    for i in range(prod.shape[1]):
+        fwd = (fwd + prod[:, i].astype(np.float32)).astype(np.float32)
+    rev = np.zeros(32, np.float32)
+    for i in reversed(range(prod.shape[1])):
+        rev = (rev + prod[:, i].astype(np.float32)).astype(np.float32)
+    assert np.array_equal(fwd.astype(np.float64) / 4, ref) and np.array_equal(rev, fwd)
+
+
+def test_mxfp4_oracle_blocks_store_quantized_keys():
+    """With MXFP4 indexer keys the sealed block holds the MXFP4 storage of the raw
+    keys, C4/HCA entries are unchanged, and the scores read the stored values."""
+    from oracle import quantize_mxfp4_rows
+    Wc, Wh = synth.gate_weights(SEED)
+    a = Oracle(128, Wc, Wh, 2, 4)
+    b = Oracle(128, Wc, Wh, 2, 4, index_format="mxfp4")
+    K, V, KI = toks(0, 0, 300)
+    for o in (a, b):
+        assert o.state_alloc() == 0
+        o.append([0], [(K, V, KI)])
+    for blk in range(2):
+        ba, bb = a.block(blk), b.block(blk)
+        assert np.array_equal(ba.csa_k, bb.csa_k) and np.array_equal(ba.hca_v, bb.hca_v)
+        codes, scales, vals = quantize_mxfp4_rows(KI[128 * blk:128 * blk + 128].reshape(128, -1))
+        assert np.array_equal(bb.idx_codes, codes) and np.array_equal(bb.idx_scales, scales)
+        assert np.array_equal(bb.idx.reshape(128, -1), vals)
+    qi = synth.tokens_f32(SEED, synth.STREAM_QI, 0, np.array([299]))[0].astype(np.float64)
+    want = np.concatenate([c4_scores(b.block(i).idx, qi) for i in range(2)])
+    assert np.array_equal(b.scores(0, qi), want)
+    assert not np.array_equal(a.scores(0, qi), want)
