@@ -42,6 +42,7 @@ LENGTHS = {"l130": "L0 = 130", "b32": "L0 ~ U{1..8192}",
 ROW = 8192                     # K + V bytes of one token or entry (2 x 16 x 128 bf16)
 C4_FP8 = 4224                  # K + V bytes of one FP8 C4 entry (2 x 16 x 128 E4M3 + 2 x 16 fp32 scales)
 IDX_BLOCK = 131072             # indexer keys of one block (128 x 4 x 64 fp32)
+IDX_BLOCK_MX = 17408           # MXFP4 indexer keys of one block (128 x (128 code + 8 scale bytes))
 SEAL_BYTES = 1581056           # per seal: read 128 tokens K/V + 128 indexer keys, write 32 C4 + 1 HCA + 128 keys
 
 
@@ -49,8 +50,12 @@ def c4_bytes(entries: str) -> int:
     return C4_FP8 if entries == "fp8" else ROW
 
 
-def seal_bytes(entries: str) -> int:
-    return SEAL_BYTES - 32 * (ROW - c4_bytes(entries))
+def idx_bytes(index: str) -> int:
+    return IDX_BLOCK_MX if index == "mxfp4" else IDX_BLOCK
+
+
+def seal_bytes(entries: str, index: str = "f32") -> int:
+    return SEAL_BYTES - 32 * (ROW - c4_bytes(entries)) - (IDX_BLOCK - idx_bytes(index))
 KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
                  "attend": "k_attend", "merge": "k_merge", "seal": "k_seal_merge",
                  "write": "k_bulk_write", "step1": "k_step1", "step2": "k_step2",
@@ -74,20 +79,23 @@ def step_fused(nb: np.ndarray) -> bool:
 
 
 def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray,
-               entries: str = "bf16") -> dict:
+               entries: str = "bf16", index: str = "f32") -> dict:
     """Bytes the method must move in one decode step, per launch (scratch excluded).
 
     L_after: lengths after the append; nb: sealed blocks after it; sealed: 1 where
-    the step sealed a block; entries: storage format of the C4 entries."""
+    the step sealed a block; entries, index: storage formats of the C4 entries and
+    of the sealed indexer keys (the block sealed in the step is scored from the
+    float32 tail)."""
     C4 = c4_bytes(entries)
-    SEAL = seal_bytes(entries)
+    SEAL = seal_bytes(entries, index)
+    scan = (nb - sealed) * idx_bytes(index) + sealed * IDX_BLOCK
     swa = np.minimum(L_after, n_win)
     kk = np.minimum(k, 32 * nb)
     B = len(L_after)
     if step_fused(nb):
         out = {
             "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL - ROW)
-                         + (nb * IDX_BLOCK).sum() + B * 1024),
+                         + scan.sum() + B * 1024),
             # S2 (three-launch form): top-k out; HCA entries of new blocks; K/V rows
             # of the SWA tokens, earlier HCA entries and selected C4 entries + the query
             "step2": int((kk * 8).sum() + sealed.sum() * ROW
@@ -104,7 +112,7 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
         # HCA entry written in S2); indexer keys of every sealed block + the
         # indexer query
         "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL - ROW)
-                     + (nb * IDX_BLOCK).sum() + B * 1024),
+                     + scan.sum() + B * 1024),
         # S2: top-k ordinals (and scores) out; HCA entries of new blocks; K/V rows
         # of the SWA tokens and earlier HCA entries + the query
         "step2": int((kk * 8).sum() + sealed.sum() * ROW
@@ -163,7 +171,7 @@ def _append_device(cache, wl, states, reqs, p0s, p1s, chunk=65536):
         del K, V, KI
 
 
-def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16"):
+def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", index: str = "f32"):
     """Cache holding `copies` identical instances of the batch, every request
     prefilled to L0 (bulk appends of device-generated tokens; in a prefix workload
     each request forks off its group's parent at its fork length, sharing those
@@ -179,7 +187,8 @@ def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16"):
     max_blocks = copies * (int(((L0 + extra_steps) // 128).sum()) + B) + 8
     n_parents = wl.n_groups if wl.prefix_len else 0
     cache = hsa.Cache(wl.n_win, copies * (B + n_parents), max_blocks + copies * n_parents * (wl.prefix_len // 128),
-                      Wc, Wh, max_blocks_per_state=max_len // 128 + 2, entry_format=entries)
+                      Wc, Wh, max_blocks_per_state=max_len // 128 + 2, entry_format=entries,
+                      index_format=index)
     inst = []
     for _ in range(copies):
         states = [None] * B
@@ -236,7 +245,7 @@ def run_decode(args) -> dict:
     W, K = args.warmup, args.steps
     R = args.copies if args.copies is not None else (4 if wl.name == "b32" else 1)
     local_steps = (W + 2 * K + R - 1) // R
-    cache, inst = setup_decode(wl, local_steps, R, args.entries)
+    cache, inst = setup_decode(wl, local_steps, R, args.entries, args.index)
     L0 = wl.prefill.astype(np.int64)
     inp = decode_inputs(wl, L0, local_steps)
     topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
@@ -294,7 +303,7 @@ def run_decode(args) -> dict:
             L_after = L0 + t // R + 1
             nb = L_after // 128
             sealed = (L_after % 128 == 0).astype(np.int64)
-            sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries)
+            sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index)
             for n in acc:
                 acc[n] += sb[n]
         return acc
@@ -311,15 +320,16 @@ def run_decode(args) -> dict:
         tr = json.load(open(TRAFFIC_FILE))
         ent = tr.get(KERNEL_SYMBOL[dominant])
         if (ent and ent.get("src_sha") == src_hash(dominant) and ent.get("workload") == wl.name
-                and ent.get("entries", "bf16") == args.entries):
+                and ent.get("entries", "bf16") == args.entries and ent.get("index", "f32") == args.index):
             traffic = ent.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         pass
 
     fp8 = args.entries == "fp8"
+    mx4 = args.index == "mxfp4"
     metric = METRIC if wl.name == "b32" else f"decode tokens/s + achieved HBM GB/s, append+attend, {wl.name}"
     res = {
-        "metric": metric + (", FP8 C4 entries" if fp8 else ""),
+        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", MXFP4 indexer keys" if mx4 else ""),
         "value": B * K / (ms_total * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -334,10 +344,10 @@ def run_decode(args) -> dict:
         "config": {"workload": f"{wl.name}: {B} requests, {LENGTHS[wl.name]} (seed {wl.seed:#x}), "
                                f"decode steps, n_win {wl.n_win}, top-k {k}, 16x128 bf16 K/V/Q"
                                f"{' (C4 entries FP8 E4M3, fp32 scale per head)' if fp8 else ''}, "
-                               f"indexer 4x64 fp32, m=4, m'=128, 1 layer; steps rotate over {R} "
+                               f"indexer 4x64 fp32{' (sealed keys MXFP4)' if mx4 else ''}, m=4, m'=128, 1 layer; steps rotate over {R} "
                                f"copies of the cache",
                    "batch": B, "n_win": wl.n_win, "topk": k, "kv_dtype": "bf16",
-                   "c4_entries": args.entries, "cache_copies": R,
+                   "c4_entries": args.entries, "index_keys": args.index, "cache_copies": R,
                    "L0_mean": float(L0.mean()), "parallelism": "single GPU"},
         "hbm_gbps": step_gbs,
         "hbm_frac_of_peak": step_gbs / PEAK_HBM_GBS,
@@ -371,8 +381,9 @@ def run_bulk(args) -> dict:
     Wc, Wh = synth.gate_weights(wl.seed)
     nb = L0 // 128
     cache = hsa.Cache(wl.n_win, B, int(nb.sum()) + B, Wc, Wh, max_blocks_per_state=int(L0.max()) // 128 + 2,
-                      entry_format=args.entries)
+                      entry_format=args.entries, index_format=args.index)
     C4 = c4_bytes(args.entries)
+    IDX = idx_bytes(args.index)
     cu = np.concatenate([[0], np.cumsum(L0)]).astype(np.int64)
     pos = torch.from_numpy(np.concatenate([np.arange(n) for n in L0]).astype(np.int64)).cuda()
     keys = torch.from_numpy(np.repeat(np.arange(B), L0).astype(np.int32)).cuda()
@@ -386,9 +397,9 @@ def run_bulk(args) -> dict:
     # bytes the method must move: every token's K, V and indexer key read, every
     # block's 32 C4 + 1 HCA entries and 128 indexer keys written, the ring's last
     # n_win tokens and the indexer tail written
-    seal_b = int(nb.sum()) * (128 * (ROW + 1024) + 32 * C4 + ROW + IDX_BLOCK)
+    seal_b = int(nb.sum()) * (128 * (ROW + 1024) + 32 * C4 + ROW + IDX)
     write_bytes = int((np.minimum(L0, wl.n_win) * 2 * ROW + (L0 % 128) * 2 * 1024).sum())
-    alg = T * (ROW + 1024) + int(nb.sum()) * (32 * C4 + ROW + IDX_BLOCK) \
+    alg = T * (ROW + 1024) + int(nb.sum()) * (32 * C4 + ROW + IDX) \
         + int((np.minimum(L0, wl.n_win) * ROW + (L0 % 128) * 1024).sum())
     reps = max(2, args.steps)
     times = []
@@ -414,14 +425,15 @@ def run_bulk(args) -> dict:
     gbs = alg / (ms * 1e-3) / 1e9
     return {
         "metric": f"bulk append tokens/s + achieved HBM GB/s, append+compress, {wl.name}"
-                  + (", FP8 C4 entries" if args.entries == "fp8" else ""),
+                  + (", FP8 C4 entries" if args.entries == "fp8" else "")
+                  + (", MXFP4 indexer keys" if args.index == "mxfp4" else ""),
         "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": len(times), "warmup": 1,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name}: {B} requests x {LENGTHS[wl.name]} (seed {wl.seed:#x}) in one "
                                f"append call with fused seal, n_win {wl.n_win}; 16x128 bf16 K/V, indexer "
                                f"4x64 fp32, m=4, m'=128, 1 layer",
-                   "batch": B, "tokens": T, "c4_entries": args.entries, "n_win": wl.n_win, "parallelism": "single GPU"},
+                   "batch": B, "tokens": T, "c4_entries": args.entries, "index_keys": args.index, "n_win": wl.n_win, "parallelism": "single GPU"},
         "hbm_gbps": gbs, "hbm_frac_of_peak": gbs / PEAK_HBM_GBS, "bytes_per_step": alg,
         "roofline": {"bound": "hbm", "kernel": "k_bulk_seal",
                      "achieved": seal_b / (seal_ms * 1e-3) / 1e9 if seal_ms else None,
@@ -567,6 +579,8 @@ def main():
                          "last-level cache between steps)")
     ap.add_argument("--entries", default="bf16", choices=["bf16", "fp8"],
                     help="storage format of the C4 entries (bf16, or FP8 E4M3 with a per-head scale)")
+    ap.add_argument("--index", default="f32", choices=["f32", "mxfp4"],
+                    help="storage format of sealed indexer keys (fp32, or MXFP4 with E8M0 block scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters", default=None, help="comma-separated rocprofv3 --pmc output dirs")
@@ -588,7 +602,8 @@ def main():
         return
     args.warmup = max(args.warmup, 2)
     res = run_bulk(args) if args.workload == 4 else run_decode(args)
-    if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16":
+    if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16" \
+            and args.index == "f32":
         res["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(res), flush=True)
 

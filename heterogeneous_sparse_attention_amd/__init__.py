@@ -45,9 +45,10 @@ class _Config(ctypes.Structure):
                 ("max_blocks", ctypes.c_int64), ("max_blocks_per_state", ctypes.c_int64),
                 ("gate_csa", ctypes.POINTER(ctypes.c_float)),
                 ("gate_hca", ctypes.POINTER(ctypes.c_float)),
-                ("entry_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("entry_format", ctypes.c_int32), ("index_format", ctypes.c_int32)]
 
 ENTRY_FORMATS = {"bf16": 0, "fp8": 1}     # HSA_ENTRY_BF16, HSA_ENTRY_FP8
+INDEX_FORMATS = {"f32": 0, "mxfp4": 1}    # HSA_INDEX_F32, HSA_INDEX_MXFP4
 
 
 class _StateInfo(ctypes.Structure):
@@ -82,6 +83,8 @@ SIGNATURES = {
     "hsa_export_state": [_P, _I32, _P, _P, _P, _P],
     "hsa_export_c4_fp8": [_P, _I32, _P, _P, _P, _P, _P],
     "hsa_fp8_quantize_rows": [_P, _I64, _P, _P, _P],
+    "hsa_export_idx_mxfp4": [_P, _I32, _P, _P, _P],
+    "hsa_mxfp4_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_timing_enable": [_P, _U32],
     "hsa_timing_read": [_P, _P, _P],
 }
@@ -154,17 +157,21 @@ class Cache:
     """One Block Cache + State Cache on one GPU (an hsa_ctx)."""
 
     def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
-                 max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16"):
+                 max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16",
+                 index_format: str = "f32"):
         lib = load()
         if entry_format not in ENTRY_FORMATS:
             raise ValueError(f"entry_format must be one of {sorted(ENTRY_FORMATS)}")
+        if index_format not in INDEX_FORMATS:
+            raise ValueError(f"index_format must be one of {sorted(INDEX_FORMATS)}")
         self._gc = np.ascontiguousarray(np.asarray(gate_csa, np.float32).reshape(H * D))
         self._gh = np.ascontiguousarray(np.asarray(gate_hca, np.float32).reshape(H * D))
         cfg = _Config(H, D, 4, 128, n_win, HI, DI, max_states, max_blocks, max_blocks_per_state,
                       self._gc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
-                      ENTRY_FORMATS[entry_format], 0)
+                      ENTRY_FORMATS[entry_format], INDEX_FORMATS[index_format])
         self.entry_format = entry_format
+        self.index_format = index_format
         ctx = ctypes.c_void_p()
         _check(lib.hsa_create(ctypes.byref(cfg), device, ctypes.byref(ctx)), "hsa_create")
         self._ctx = ctx
@@ -301,16 +308,20 @@ class Cache:
     def export_block(self, b: int, stream=None) -> dict:
         """bf16 arrays as uint16 bits; indexer keys as float32. With FP8 entries the C4
         entries come as E4M3 codes (csa_k_codes, csa_v_codes uint8 [32][16][128]) and
-        per-head scales (csa_k_scale, csa_v_scale float32 [32][16])."""
+        per-head scales (csa_k_scale, csa_v_scale float32 [32][16]). With MXFP4 indexer
+        keys they come as idx_codes uint8 [128][128] and idx_scales uint8 [128][8]
+        (E8M0 bytes) instead of idx."""
         fp8 = self.entry_format == "fp8"
-        out = {"hca_k": np.zeros((H, D), np.uint16), "hca_v": np.zeros((H, D), np.uint16),
-               "idx": np.zeros((128, HI, DI), np.float32)}
+        mx4 = self.index_format == "mxfp4"
+        out = {"hca_k": np.zeros((H, D), np.uint16), "hca_v": np.zeros((H, D), np.uint16)}
+        if not mx4:
+            out["idx"] = np.zeros((128, HI, DI), np.float32)
         if not fp8:
             out["csa_k"] = np.zeros((32, H, D), np.uint16)
             out["csa_v"] = np.zeros((32, H, D), np.uint16)
         p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
         _check(_lib.hsa_export_block(self._ctx, int(b), p.get("csa_k"), p.get("csa_v"), p["hca_k"],
-                                     p["hca_v"], p["idx"], _stream(stream)), "hsa_export_block")
+                                     p["hca_v"], p.get("idx"), _stream(stream)), "hsa_export_block")
         if fp8:
             q = {"csa_k_codes": np.zeros((32, H, D), np.uint8), "csa_v_codes": np.zeros((32, H, D), np.uint8),
                  "csa_k_scale": np.zeros((32, H), np.float32), "csa_v_scale": np.zeros((32, H), np.float32)}
@@ -318,6 +329,13 @@ class Cache:
             _check(_lib.hsa_export_c4_fp8(self._ctx, int(b), pq["csa_k_codes"], pq["csa_v_codes"],
                                           pq["csa_k_scale"], pq["csa_v_scale"], _stream(stream)),
                    "hsa_export_c4_fp8")
+            out.update(q)
+        if mx4:
+            q = {"idx_codes": np.zeros((128, HI * DI // 2), np.uint8),
+                 "idx_scales": np.zeros((128, HI * DI // 32), np.uint8)}
+            _check(_lib.hsa_export_idx_mxfp4(self._ctx, int(b), q["idx_codes"].ctypes.data_as(ctypes.c_void_p),
+                                             q["idx_scales"].ctypes.data_as(ctypes.c_void_p), _stream(stream)),
+                   "hsa_export_idx_mxfp4")
             out.update(q)
         return out
 
@@ -357,4 +375,21 @@ def fp8_quantize_rows(x, stream=None):
                                       _dev(codes, torch.uint8, (n, D), "codes"),
                                       _dev(scales, torch.float32, (n,), "scales"), _stream(stream)),
            "hsa_fp8_quantize_rows")
+    return codes, scales
+
+
+def mxfp4_quantize_rows(x, stream=None):
+    """The MXFP4 indexer key quantisation alone (hsa_mxfp4_quantize_rows): device
+    float32 [n][256] -> (codes uint8 [n][128], E8M0 scale bytes uint8 [n][8]) as
+    device tensors."""
+    import torch
+    load()
+    n = x.shape[0]
+    R = HI * DI
+    codes = torch.empty((n, R // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n, R // 32), dtype=torch.uint8, device=x.device)
+    _check(_lib.hsa_mxfp4_quantize_rows(_dev(x, torch.float32, (n, R), "x"), n,
+                                        _dev(codes, torch.uint8, (n, R // 2), "codes"),
+                                        _dev(scales, torch.uint8, (n, R // 32), "scales"), _stream(stream)),
+           "hsa_mxfp4_quantize_rows")
     return codes, scales

@@ -111,7 +111,25 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const float* x, int64_t n_rows
   if ((threadIdx.x & 15) == 0) scales[row] = sc;
 }
 
+// MXFP4 storage of indexer key rows (256 fp32 each), exactly as the seal stores
+// them: a wave per row, 4 rows per workgroup.
+__global__ __launch_bounds__(256) void k_mx4_rows(const float* x, int64_t n_rows, uint8_t* codes,
+                                                  uint8_t* scales) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;   // whole waves, so the 8-lane scale reduction stays within active lanes
+  const int c = threadIdx.x & 63;
+  const float4 v = reinterpret_cast<const float4*>(x + row * kIRow)[c];
+  mx4_store_row(v, c, codes + row * kIRowQ, scales + row * kIRowE);
+}
+
 }  // namespace
+
+hipError_t launch_mx4_rows(const float* x, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                           hipStream_t st) {
+  if (n_rows <= 0) return hipSuccess;
+  return launch_k(k_mx4_rows, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), st, LaunchEv{}, x,
+                  n_rows, codes, scales);
+}
 
 hipError_t launch_fp8_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
                            hipStream_t st) {

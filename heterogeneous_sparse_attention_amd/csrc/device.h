@@ -9,6 +9,8 @@
 //    c4s [max_blocks * 32][K, V][16] fp32 per-head scales, head h at 4 (h % 4) + h / 4)
 //   hca_k, hca_v  [max_blocks][16][128]      bf16
 //   idx_k         [max_blocks][128][4][64]   fp32
+//   (MXFP4 indexer keys instead: idx_q [max_blocks][128][128] E2M1 code pairs and
+//    idx_e [max_blocks][128][8] E8M0 scales, one per 32 values)
 //   table         [max_states][table_stride] int32    logical block -> physical id
 // One K or V row (a token or an entry) is 16 x 128 bf16 = 4 KiB contiguous, so every
 // row read is a fully coalesced 4 KiB burst; one indexer row is 1 KiB.
@@ -40,6 +42,9 @@ constexpr int kC4Bytes = 2 * kRow;      // FP8 C4 row: K codes then V codes, 204
 constexpr int kC4Scales = 2 * kH;       // FP8 C4 row: K scales then V scales
 constexpr float kE4M3Max = 448.f;       // largest finite OCP E4M3 value
 constexpr int kCacheN = 4096;      // top-k: scores kept in LDS (16 KiB); larger rows read through L2
+constexpr int kMxBlk = 32;              // MXFP4 indexer keys: values per shared scale
+constexpr int kIRowQ = kIRow / 2;       // MXFP4 indexer key: 128 bytes of E2M1 codes
+constexpr int kIRowE = kIRow / kMxBlk;  // MXFP4 indexer key: 8 E8M0 scale bytes
 
 struct Pools {
   uint16_t* swa_k;
@@ -56,10 +61,12 @@ struct Pools {
   const float* gate_hca;
   uint8_t* c4q;         // FP8 entries: codes of C4 row r (block * 32 + slot) at r * kC4Bytes
   float* c4s;           // FP8 entries: scales of C4 row r at r * kC4Scales
+  uint8_t* idx_q;       // MXFP4 keys: codes of key row r (block * 128 + token) at r * kIRowQ
+  uint8_t* idx_e;       // MXFP4 keys: scale bytes of key row r at r * kIRowE
   int32_t n_win;
   int32_t max_blocks;   // physical ids are in [0, max_blocks)
   int32_t fp8;          // 1: C4 entries are stored as FP8 (c4q, c4s); 0: bf16 (csa_k, csa_v)
-  int32_t pad_;
+  int32_t mx4;          // 1: sealed indexer keys are MXFP4 (idx_q, idx_e); 0: fp32 (idx_k)
 };
 
 // One request of a launch: its state, its length and sealed-block count after the
@@ -255,6 +262,47 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 // ---------------------------------------------------------------- FP8 (OCP E4M3) entries
 
+// ---------------------------------------------------------------- MXFP4 indexer keys
+// OCP Microscaling MXFP4: a sealed key's 256 values form 8 blocks of 32 (block
+// 2h + j = head h, dims 32j .. 32j + 31). A block has one E8M0 scale byte E + 127,
+// E = floor(log2 max |x|) - 2 (2 being E2M1's largest exponent), at least -127 and
+// -127 for an all-zero block; each value is the E2M1 code of x / 2^E, nearest of
+// 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, saturating at 6, sign bit for
+// x < 0. Value 2i of a key sits in the low nibble of its byte i, 2i + 1 in the high.
+
+// Shared exponent E of a block whose largest magnitude is amax (subnormals included).
+__device__ __forceinline__ int mx_exp(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const uint32_t b = __float_as_uint(amax);
+  const int fe = (int)(b >> 23);
+  const int l2 = fe ? fe - 127 : (31 - (int)__clz(b & 0x7fffffu)) - 149;   // floor(log2 amax)
+  return l2 - 2 < -127 ? -127 : l2 - 2;
+}
+
+// E2M1 code of x / 2^E (the division by a power of two is exact).
+__device__ __forceinline__ uint32_t e2m1_code(float x, int E) {
+  const float y = ldexpf(fabsf(x), -E);
+  const uint32_t c = (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+                     (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) +
+                     (uint32_t)(y > 5.f);
+  return c | (x < 0.f ? 8u : 0u);
+}
+
+// Cooperative MXFP4 storage of one key row: lane c (0..63 of a wave, all active)
+// holds values 4c .. 4c+3; the 8 lanes of a block share its scale through DPP.
+// Writes the lane's 2 code bytes and, from the block's first lane, the scale byte.
+__device__ __forceinline__ void mx4_store_row(const float4& v, int c, uint8_t* codes, uint8_t* scales) {
+  float am = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  am = fmaxf(am, dpp<0xB1>(am));    // quad_perm [1,0,3,2]
+  am = fmaxf(am, dpp<0x4E>(am));    // quad_perm [2,3,0,1]
+  am = fmaxf(am, dpp<0x141>(am));   // row_half_mirror: the other quad of the 8 lanes
+  const int E = mx_exp(am);
+  const uint32_t q = e2m1_code(v.x, E) | (e2m1_code(v.y, E) << 4) | (e2m1_code(v.z, E) << 8) |
+                     (e2m1_code(v.w, E) << 12);
+  reinterpret_cast<uint16_t*>(codes)[c] = (uint16_t)q;
+  if ((c & 7) == 0) scales[c >> 3] = (uint8_t)(E + 127);
+}
+
 // Address of C4 row `row` (block * 32 + slot) for attention: the bf16 K and V rows,
 // or, with FP8 entries, the code row and the scale row (see load_key).
 struct C4Addr {
@@ -270,8 +318,9 @@ __device__ __forceinline__ C4Addr c4_addr(const Pools& P, int64_t row) {
 
 // Per-head FP8 storage of 8 values per lane, the 16 lanes of a DPP row holding one
 // head's 128 values: with amax = max |x| over the head, scale = amax / 448 and
-// code = E4M3(x * (448 / amax)) rounded to nearest even (scale 1 and codes 0 for
-// an all-zero head); float32 throughout, each division correctly rounded. Returns
+// code = E4M3(x * (448 / amax)) rounded to nearest even (scale 1 and codes 0 where
+// 448 / amax is not finite: an all-zero head, or amax below 448 / FLT_MAX); float32
+// throughout, each division correctly rounded. Returns
 // the 8 codes (value i in byte i) and the scale.
 __device__ __forceinline__ uint2 quantize8_e4m3(const float* x, float& scale) {
   float amax = 0.f;

@@ -486,6 +486,8 @@ int check_config(const hsa_config* cfg) {
   if (!cfg->gate_csa || !cfg->gate_hca) return fail(kInvalid, "gate weights are NULL");
   if (cfg->entry_format != HSA_ENTRY_BF16 && cfg->entry_format != HSA_ENTRY_FP8)
     return fail(kInvalid, "entry_format must be HSA_ENTRY_BF16 or HSA_ENTRY_FP8");
+  if (cfg->index_format != HSA_INDEX_F32 && cfg->index_format != HSA_INDEX_MXFP4)
+    return fail(kInvalid, "index_format must be HSA_INDEX_F32 or HSA_INDEX_MXFP4");
   return kOk;
 }
 
@@ -512,17 +514,20 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   }
   const size_t S = (size_t)cfg->max_states, NB = (size_t)cfg->max_blocks, W = (size_t)cfg->n_win;
   const bool fp8 = cfg->entry_format == HSA_ENTRY_FP8;
-  void* p[13] = {};
-  const size_t bytes[13] = {
+  const bool mx4 = cfg->index_format == HSA_INDEX_MXFP4;
+  constexpr int kPools = 15;
+  void* p[kPools] = {};
+  const size_t bytes[kPools] = {
       S * W * kRow * 2, S * W * kRow * 2, S * kBlk * kIRow * 4,            // swa_k, swa_v, idx_tail
       fp8 ? 0 : NB * kC4 * kRow * 2, fp8 ? 0 : NB * kC4 * kRow * 2,       // csa (bf16 entries)
       NB * kRow * 2, NB * kRow * 2,                                       // hca
-      NB * kBlk * kIRow * 4,                                              // idx_k
+      mx4 ? 0 : NB * kBlk * kIRow * 4,                                    // idx_k (fp32 keys)
       S * (size_t)bps * 4,                                                // table
       2 * kRow * 4,                                                       // gates
       (size_t)kMaxReq * kSealSplit * kPartFloats * 4,                     // seal partials
-      fp8 ? NB * kC4 * kC4Bytes : 0, fp8 ? NB * kC4 * kC4Scales * 4 : 0};  // FP8 C4 codes, scales
-  for (int i = 0; i < 13; ++i) {
+      fp8 ? NB * kC4 * kC4Bytes : 0, fp8 ? NB * kC4 * kC4Scales * 4 : 0,   // FP8 C4 codes, scales
+      mx4 ? NB * kBlk * kIRowQ : 0, mx4 ? NB * kBlk * kIRowE : 0};       // MXFP4 key codes, scales
+  for (int i = 0; i < kPools; ++i) {
     st = dev_alloc(c, &p[i], bytes[i]);
     if (st) {
       hsa_destroy(c);
@@ -548,6 +553,9 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   c->P.c4q = static_cast<uint8_t*>(p[11]);
   c->P.c4s = static_cast<float*>(p[12]);
   c->P.fp8 = fp8 ? 1 : 0;
+  c->P.idx_q = static_cast<uint8_t*>(p[13]);
+  c->P.idx_e = static_cast<uint8_t*>(p[14]);
+  c->P.mx4 = mx4 ? 1 : 0;
   // attention partials: a decode step has at most max(slots, requests) workgroups per
   // part, and hsa_decode_attend at most max(64, target - n) + n <= target + 64, so
   // these never grow (no device synchronisation in a decode loop)
@@ -753,6 +761,7 @@ hsa_status hsa_export_block(hsa_ctx* c, int32_t b, void* csa_k, void* csa_v, voi
   int st = set_device(c);
   if (st) return st;
   if (c->P.fp8 && (csa_k || csa_v)) return fail(kInvalid, "FP8 entries: export them with hsa_export_c4_fp8");
+  if (c->P.mx4 && idx_k) return fail(kInvalid, "MXFP4 indexer keys: export them with hsa_export_idx_mxfp4");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t B = (size_t)b;
   if (csa_k) HIP_TRY(hipMemcpyAsync(csa_k, c->P.csa_k + B * kC4 * kRow, kC4 * kRow * 2, hipMemcpyDeviceToHost, s));
@@ -785,6 +794,29 @@ hsa_status hsa_export_c4_fp8(hsa_ctx* c, int32_t b, uint8_t* codes_k, uint8_t* c
       if (scale_k) scale_k[e * kH + h] = sc[(size_t)e * kC4Scales + hp];
       if (scale_v) scale_v[e * kH + h] = sc[(size_t)e * kC4Scales + kH + hp];
     }
+  return kOk;
+}
+
+hsa_status hsa_export_idx_mxfp4(hsa_ctx* c, int32_t b, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->P.mx4) return fail(kInvalid, "the context stores fp32 indexer keys");
+  if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t R = (size_t)b * kBlk;
+  if (codes) HIP_TRY(hipMemcpyAsync(codes, c->P.idx_q + R * kIRowQ, kBlk * kIRowQ, hipMemcpyDeviceToHost, s));
+  if (scales) HIP_TRY(hipMemcpyAsync(scales, c->P.idx_e + R * kIRowE, kBlk * kIRowE, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return kOk;
+}
+
+hsa_status hsa_mxfp4_quantize_rows(const float* x, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                                   void* stream) {
+  if (n_rows < 0 || n_rows > (int64_t(1) << 32)) return fail(kInvalid, "n_rows out of range");
+  if (n_rows == 0) return kOk;
+  if (!x || !codes || !scales) return fail(kInvalid, "NULL buffer");
+  HIP_TRY(launch_mx4_rows(x, n_rows, codes, scales, static_cast<hipStream_t>(stream)));
   return kOk;
 }
 

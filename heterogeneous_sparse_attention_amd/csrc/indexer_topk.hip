@@ -9,7 +9,8 @@ namespace hsa {
 
 namespace {
 
-// One workgroup per sealed block of the batch's requests (128 KiB of keys).
+// One workgroup per sealed block of the batch's requests (128 KiB of fp32 keys, or
+// 17 KiB of MXFP4 keys).
 __global__ __launch_bounds__(256, 4) void k_score(Pools P, ReqBatch B, const float* q_idx,
                                                   float* scores, int64_t ld) {
   int r, w, first;
@@ -21,8 +22,13 @@ __global__ __launch_bounds__(256, 4) void k_score(Pools P, ReqBatch B, const flo
     if (threadIdx.x < kC4) out[threadIdx.x] = -INFINITY;
     return;
   }
-  const float* blk = P.idx_k + (int64_t)id * kBlk * kIRow;
-  score_block([&](int t) { return blk + t * kIRow; }, q_idx + (int64_t)r * kIRow, out);
+  const int64_t kr = (int64_t)id * kBlk;
+  if (P.mx4) {
+    score_block_mx<kBlk / 32>(P.idx_q + kr * kIRowQ, P.idx_e + kr * kIRowE, q_idx + (int64_t)r * kIRow, out);
+  } else {
+    const float* blk = P.idx_k + kr * kIRow;
+    score_block([&](int t) { return blk + t * kIRow; }, q_idx + (int64_t)r * kIRow, out);
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_select(ReqBatch B, SelPlan SP, int32_t k,

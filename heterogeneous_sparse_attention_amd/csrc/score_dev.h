@@ -47,6 +47,113 @@ __device__ __forceinline__ void score_block(RowFn row, const float* q_row, float
   }
 }
 
+// ---- MXFP4 keys. Lane l of a wave takes token l / 8 of a group of 8 and MX block
+// b = l % 8 of it (32 values: one 16-byte code load and one scale byte), so a wave
+// load covers 8 tokens = 2 C4 entries.
+
+typedef float mx_f2 __attribute__((ext_vector_type(2)));
+
+// Sum over the lane's 32 values of q * value, times 2^E. With the codes' values
+// (multiples of 1/2 up to 6) and fp32 queries, the lane sum is exact whenever the
+// query's values share a fine enough grid, as the dyadic synthetic queries do.
+__device__ __forceinline__ float mx_dot(const uint4& w, int E, const float* q) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const mx_f2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[j], 1.f, 0);
+    const mx_f2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[j], 1.f, 1);
+    const mx_f2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[j], 1.f, 2);
+    const mx_f2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[j], 1.f, 3);
+    a = fmaf(q[8 * j + 0], p0.x, a);
+    a = fmaf(q[8 * j + 1], p0.y, a);
+    a = fmaf(q[8 * j + 2], p1.x, a);
+    a = fmaf(q[8 * j + 3], p1.y, a);
+    a = fmaf(q[8 * j + 4], p2.x, a);
+    a = fmaf(q[8 * j + 5], p2.y, a);
+    a = fmaf(q[8 * j + 6], p3.x, a);
+    a = fmaf(q[8 * j + 7], p3.y, a);
+  }
+  return ldexpf(a, E);
+}
+
+__device__ __forceinline__ void mx_load_q(const float* q_row, int b, float* q) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(q_row + kMxBlk * b)[i];
+    q[4 * i] = v.x;
+    q[4 * i + 1] = v.y;
+    q[4 * i + 2] = v.z;
+    q[4 * i + 3] = v.w;
+  }
+}
+
+// C4 scores of a group's 2 entries from the lanes' block sums: lanes 0..31 hold
+// entry 0's 4 tokens, lanes 32..63 entry 1's; written as the mean of the token scores.
+__device__ __forceinline__ void mx_write_pair(float a, float* out2) {
+  a = row_sum16(a);
+  a += __shfl_xor(a, 16);
+  const int lane = threadIdx.x & 63;
+  if ((lane & 31) == 0) out2[lane >> 5] = a * 0.25f;
+}
+
+// Scores of 32 * NG tokens (8 * NG C4 entries) of stored MXFP4 keys: key rows
+// [0, 32 NG) at codes + t * kIRowQ, scales + t * kIRowE; wave w takes groups
+// w NG .. w NG + NG - 1 of 8 tokens.
+template <int NG>
+__device__ __forceinline__ void score_block_mx(const uint8_t* codes, const uint8_t* scales,
+                                               const float* q_row, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int b = lane & 7;
+  uint4 w[NG];
+  int e[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int t = (wave * NG + g) * 8 + (lane >> 3);
+    w[g] = load_stream(reinterpret_cast<const uint4*>(codes + (int64_t)t * kIRowQ) + b);
+    e[g] = scales[(int64_t)t * kIRowE + b];
+  }
+  float q[32];
+  mx_load_q(q_row, b, q);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) mx_write_pair(mx_dot(w[g], e[g] - 127, q), out + 2 * (wave * NG + g));
+}
+
+// The same scores for keys not yet stored (the block being sealed in the same
+// launch): each lane quantises its 32 fp32 values as the seal does (the block's
+// maximum is the same however it is reduced), then takes the stored path's sum.
+template <int NG, typename RowFn>
+__device__ __forceinline__ void score_block_mx_raw(RowFn row, const float* q_row, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int b = lane & 7;
+  float q[32];
+  mx_load_q(q_row, b, q);
+#pragma unroll 1
+  for (int g = 0; g < NG; ++g) {
+    const int t = (wave * NG + g) * 8 + (lane >> 3);
+    const float4* src = reinterpret_cast<const float4*>(row(t) + kMxBlk * b);
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = src[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+    const int E = mx_exp(am);
+    uint32_t ws[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ws[i >> 3] |= e2m1_code(x[i], E) << (4 * (i & 7));
+    mx_write_pair(mx_dot(make_uint4(ws[0], ws[1], ws[2], ws[3]), E, q), out + 2 * (wave * NG + g));
+  }
+}
+
 // Order-preserving map of a float score to uint32 (larger score -> larger key);
 // -0 is folded onto +0 so equal scores compare equal.
 __device__ __forceinline__ uint32_t okey(float f) {

@@ -87,11 +87,17 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       kw[u] = *reinterpret_cast<const uint4*>(src.k(tb + u) + off);
       vw[u] = *reinterpret_cast<const uint4*>(src.v(tb + u) + off);
     }
-    // indexer keys of the 4 tokens: 4 x 64 float4, one per lane
+    // indexer keys of the 4 tokens: 4 x 64 float4, one per lane (stored as MXFP4
+    // when P.mx4, a wave per key)
     {
       const int u = tid >> 6, c = tid & 63;
       const float4 iv = reinterpret_cast<const float4*>(src.i(tb + u))[c];
-      reinterpret_cast<float4*>(idx_dst + (int64_t)(tb + u) * kIRow)[c] = iv;
+      if (P.mx4) {
+        const int64_t kr = (int64_t)id * kBlk + tb + u;
+        mx4_store_row(iv, c, P.idx_q + kr * kIRowQ, P.idx_e + kr * kIRowE);
+      } else {
+        reinterpret_cast<float4*>(idx_dst + (int64_t)(tb + u) * kIRow)[c] = iv;
+      }
     }
     // the tokens stay packed (bf16 pairs) and are unpacked where used, which keeps
     // the register count low enough for the scoring workgroups of the same launch

@@ -64,16 +64,24 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
     // the input (its tail slot is being written in this launch)
     const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
     const float* inrow = S.iin + (int64_t)r * kIRow;
-    score_block<8 / kScoreSplit>(
-        [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; }, qrow, out);
+    auto row = [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; };
+    if (P.mx4)
+      score_block_mx_raw<kTok / 32>(row, qrow, out);
+    else
+      score_block<8 / kScoreSplit>(row, qrow, out);
   } else {
     const int32_t id = P.table[(int64_t)R.state * P.table_stride + lb];
     if (id < 0 || id >= P.max_blocks) {   // never taken: tables are written before use
       if (threadIdx.x < kTok / 4) out[threadIdx.x] = -INFINITY;
       return;
     }
-    const float* blk = P.idx_k + ((int64_t)id * kBlk + t0) * kIRow;
-    score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
+    const int64_t kr = (int64_t)id * kBlk + t0;
+    if (P.mx4) {
+      score_block_mx<kTok / 32>(P.idx_q + kr * kIRowQ, P.idx_e + kr * kIRowE, qrow, out);
+    } else {
+      const float* blk = P.idx_k + kr * kIRow;
+      score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
+    }
   }
 }
 

@@ -76,16 +76,31 @@ typedef struct hsa_config {
   const float* gate_hca;        /* host [n_heads][head_dim] compressor gate, copied */
   int32_t entry_format;         /* storage of C4 entries: HSA_ENTRY_BF16 or
                                    HSA_ENTRY_FP8 ([Ch12] §2.2 accounts entries in FP8) */
-  int32_t reserved;             /* 0                                                */
+  int32_t index_format;         /* storage of sealed indexer keys: HSA_INDEX_F32 or
+                                   HSA_INDEX_MXFP4 ([Ch12] §2.2 stores them as FP4) */
 } hsa_config;
 
 /* C4 entry storage. BF16: K and V rows of 16 x 128 bf16. FP8: per head, 128 OCP
- * FP8 E4M3 codes and one float32 scale s = max |x| / 448 over the head's 128 values
- * (1 for an all-zero head); code = E4M3(x / s), round to nearest, ties to even,
- * taken in float32; the entry reads as code value * s. The pages give no scale
- * scheme: this per-head scale is the reading used. HCA entries are always bf16. */
+ * FP8 E4M3 codes and one float32 scale s = amax / 448, amax = max |x| over the
+ * head's 128 values; code = E4M3(x * (448 / amax)), round to nearest, ties to even,
+ * taken in float32; the entry reads as code value * s. A head whose 448 / amax is
+ * not a finite float32 (all zero, or amax below 448 / FLT_MAX) stores s = 1 and
+ * codes 0. The pages give no scale scheme: this per-head scale is the reading
+ * used. HCA entries are always bf16. */
 #define HSA_ENTRY_BF16 0
 #define HSA_ENTRY_FP8 1
+
+/* Sealed indexer key storage. F32: [128][4][64] float32 per block. MXFP4 (OCP
+ * Microscaling): each key's 256 values form 8 blocks of 32 (block 2h + j = head h,
+ * dims 32j .. 32j + 31) with one E8M0 scale byte E + 127, E = floor(log2 max |x|)
+ * - 2, at least -127 (-127 for an all-zero block), and E2M1 codes of x / 2^E
+ * (nearest of 0, .5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturating at 6,
+ * sign bit for x < 0); value 2i in the low nibble of byte i. The key reads as code
+ * value * 2^E. The open block's keys (the State's indexer tail) stay float32 until
+ * the block seals; queries are float32. The pages give no scale scheme: the OCP
+ * block scaling is the reading used. */
+#define HSA_INDEX_F32 0
+#define HSA_INDEX_MXFP4 1
 
 typedef struct hsa_state_info {
   int64_t len;          /* L, tokens appended so far                                 */
@@ -197,7 +212,8 @@ hsa_status hsa_block_table_get(hsa_ctx* ctx, int32_t state, int32_t* ids, int64_
 hsa_status hsa_block_refcount(hsa_ctx* ctx, int32_t block, int32_t* rc);
 /* Copy one block to host buffers (any may be NULL): csa_k, csa_v bf16
  * [32][16][128] (must be NULL with FP8 entries: see hsa_export_c4_fp8); hca_k,
- * hca_v bf16 [16][128]; idx_k fp32 [128][4][64]. */
+ * hca_v bf16 [16][128]; idx_k fp32 [128][4][64] (must be NULL with MXFP4 indexer
+ * keys: see hsa_export_idx_mxfp4). */
 hsa_status hsa_export_block(hsa_ctx* ctx, int32_t block, void* csa_k, void* csa_v,
                             void* hca_k, void* hca_v, float* idx_k, void* stream);
 /* FP8 entries only: copy one block's C4 entries to host buffers (any may be NULL):
@@ -212,6 +228,19 @@ hsa_status hsa_export_c4_fp8(hsa_ctx* ctx, int32_t block, uint8_t* codes_k, uint
  * Needs no context; n_rows >= 0. */
 hsa_status hsa_fp8_quantize_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
                                  void* stream);
+
+/* MXFP4 indexer keys only: copy one block's 128 sealed keys to host buffers (either
+ * may be NULL): codes u8 [128][128] (E2M1 code pairs), scales u8 [128][8] (E8M0
+ * bytes). HSA_ERR_INVALID with fp32 keys. */
+hsa_status hsa_export_idx_mxfp4(hsa_ctx* ctx, int32_t block, uint8_t* codes, uint8_t* scales,
+                                void* stream);
+
+/* The MXFP4 key quantisation on its own (the one the seal applies to each indexer
+ * key): for each of n_rows keys of 256 float32 values (device x [n_rows][256]),
+ * writes device codes u8 [n_rows][128] and scale bytes u8 [n_rows][8]. Needs no
+ * context; 0 <= n_rows <= 2^32. */
+hsa_status hsa_mxfp4_quantize_rows(const float* x, int64_t n_rows, uint8_t* codes, uint8_t* scales,
+                                   void* stream);
 
 /* Copy one State block to host buffers (any may be NULL): swa_k, swa_v bf16
  * [n_win][16][128] in ring-slot order (token p sits in slot p mod n_win);
