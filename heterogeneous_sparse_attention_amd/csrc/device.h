@@ -45,6 +45,14 @@ constexpr int kCacheN = 4096;      // top-k: scores kept in LDS (16 KiB); larger
 constexpr int kMxBlk = 32;              // MXFP4 indexer keys: values per shared scale
 constexpr int kIRowQ = kIRow / 2;       // MXFP4 indexer key: 128 bytes of E2M1 codes
 constexpr int kIRowE = kIRow / kMxBlk;  // MXFP4 indexer key: 8 E8M0 scale bytes
+constexpr int kMxUnitMax = 8;           // MXFP4 keys: at most 8 sealed blocks (136 KiB) per scoring workgroup
+
+// Decode-step scoring workgroups of a request with nb sealed blocks: kScoreSplit per
+// block of fp32 keys (64 KiB each, mx_unit 0), or one per mx_unit blocks of MXFP4
+// keys (17 KiB each).
+__host__ __device__ inline int64_t score_units(int64_t nb, int mx_unit) {
+  return mx_unit > 0 ? (nb + mx_unit - 1) / mx_unit : (int64_t)kScoreSplit * nb;
+}
 
 struct Pools {
   uint16_t* swa_k;
@@ -146,10 +154,11 @@ struct StepArgs {
   float* out;            // [n][16][128] fp32
   int32_t k;
   int32_t sorted;
-  int32_t n_score;       // scoring workgroups: kScoreSplit per sealed block
+  int32_t n_score;       // scoring workgroups (score_units per request)
   int32_t n_a;           // part-A workgroups
   int32_t n_b;           // part-B workgroups
   int32_t fused;         // 1: three launches, part B selects for itself (rows <= kCacheN)
+  int32_t mx_unit;       // MXFP4 keys: sealed blocks per scoring workgroup (0: fp32 keys)
   SelPlan sel;           // top-k workgroups of the four-launch form (long rows are sliced)
   int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
   int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])

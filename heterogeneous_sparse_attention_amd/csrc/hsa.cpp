@@ -70,6 +70,7 @@ struct hsa_ctx {
                               // (one per CU at the step kernels' register use)
   int32_t select_slice = 0;   // top-k: longer score rows are selected in two rounds (0: by k)
   int32_t step_fused = 1;     // decode step in three launches when every row fits the LDS cache
+  int32_t mx_unit = 0;        // MXFP4 keys: blocks per scoring workgroup (0: by batch size)
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
   int32_t* cand_ord = nullptr;  // top-k of sliced rows: per-slice candidates (ordinals, scores)
@@ -82,6 +83,7 @@ struct hsa_ctx {
     if (const char* e = std::getenv("HSA_ATTEND_WGS")) attend_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_STEP_SLOTS")) step_slots = std::max(16, std::min(1 << 16, std::atoi(e)));
     if (const char* e = std::getenv("HSA_STEP_FUSED")) step_fused = std::atoi(e) != 0;
+    if (const char* e = std::getenv("HSA_MX_UNIT")) mx_unit = std::max(1, std::min(kMxUnitMax, std::atoi(e)));
     if (const char* e = std::getenv("HSA_SELECT_SLICE"))   // a multiple of 32, at least 32
       select_slice = std::max(32, std::min(1 << 24, std::atoi(e)) / 32 * 32);
   }
@@ -371,7 +373,15 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     for (int i = 0; i < n; ++i)
       fused = fused && (int64_t)kC4 * plan.reqs[b0 + i].nb_new <= kCacheN;
     std::vector<int64_t> na(n), nb(n);
-    int64_t maxnb = 0, n_score = 0;
+    int64_t maxnb = 0, n_score = 0, all_nb = 0;
+    for (int i = 0; i < n; ++i) all_nb += plan.reqs[b0 + i].nb_new;
+    // MXFP4 keys: as many blocks per scoring workgroup as leave about two workgroups
+    // per attention slot (more blocks per workgroup hide latency; fewer spread a
+    // small batch over the chip)
+    const int mx_unit = !c->P.mx4 ? 0
+                        : c->mx_unit ? c->mx_unit
+                                     : (int)std::max<int64_t>(1, std::min<int64_t>(kMxUnitMax,
+                                                                  (all_nb + 2 * c->step_slots - 1) / (2 * c->step_slots)));
     for (int i = 0; i < n; ++i) {
       const AppendReq& r = plan.reqs[b0 + i];
       const int32_t id = new_id[b0 + i];
@@ -381,7 +391,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + r.nb_new - sealed;
       nb[i] = (fused ? 0 : sealed) + std::min<int64_t>(k, (int64_t)kC4 * r.nb_new);
       maxnb = std::max<int64_t>(maxnb, r.nb_new);
-      n_score += (int64_t)kScoreSplit * r.nb_new;
+      n_score += score_units(r.nb_new, mx_unit);
     }
     StepArgs S{};
     S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
@@ -396,6 +406,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.k = k;
     S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
     S.fused = fused ? 1 : 0;
+    S.mx_unit = mx_unit;
     S.n_score = (int32_t)n_score;
     int s = kOk;
     if (!fused) {
@@ -422,7 +433,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       S.first_s[i] = (int32_t)ts;
       ta += pa.wgs[i];
       tb += pb.wgs[i];
-      ts += (int64_t)kScoreSplit * B.r[i].nb;
+      ts += score_units(B.r[i].nb, mx_unit);
     }
     S.first_a[n] = (int32_t)ta;
     S.first_b[n] = (int32_t)tb;

@@ -48,7 +48,8 @@ __device__ __forceinline__ int keys_b(const Req& r, int32_t k, int32_t fused) {
   return (fused ? 0 : sealed_now(r)) + (k < nc ? k : nc);
 }
 
-// Indexer scores of scoring unit `unit`: 128 / kScoreSplit tokens of one sealed block.
+// Indexer scores of scoring unit `unit` (fp32 keys): 128 / kScoreSplit tokens of one
+// sealed block.
 __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, const StepArgs& S,
                                            int unit) {
   constexpr int kTok = kBlk / kScoreSplit;   // tokens per scoring unit
@@ -64,24 +65,75 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
     // the input (its tail slot is being written in this launch)
     const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
     const float* inrow = S.iin + (int64_t)r * kIRow;
-    auto row = [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; };
-    if (P.mx4)
-      score_block_mx_raw<kTok / 32>(row, qrow, out);
-    else
-      score_block<8 / kScoreSplit>(row, qrow, out);
+    score_block<8 / kScoreSplit>(
+        [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (t0 + t) * kIRow; }, qrow, out);
   } else {
     const int32_t id = P.table[(int64_t)R.state * P.table_stride + lb];
     if (id < 0 || id >= P.max_blocks) {   // never taken: tables are written before use
       if (threadIdx.x < kTok / 4) out[threadIdx.x] = -INFINITY;
       return;
     }
-    const int64_t kr = (int64_t)id * kBlk + t0;
-    if (P.mx4) {
-      score_block_mx<kTok / 32>(P.idx_q + kr * kIRowQ, P.idx_e + kr * kIRowE, qrow, out);
-    } else {
-      const float* blk = P.idx_k + kr * kIRow;
-      score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
+    const float* blk = P.idx_k + ((int64_t)id * kBlk + t0) * kIRow;
+    score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
+  }
+}
+
+// Indexer scores of scoring unit `unit` with MXFP4 keys: sealed blocks
+// [u G, u G + G) of one request (G = S.mx_unit), two blocks' loads in flight at a
+// time; a block sealed in this step (the request's last) is scored from the fp32
+// tail and the input, quantised as the seal stores it.
+__device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B, const StepArgs& S,
+                                              int unit) {
+  const int r = owner_of(S.first_s, B.n, unit);
+  const Req R = B.r[r];
+  const int lb0 = (unit - S.first_s[r]) * S.mx_unit;
+  const int lb1 = min(lb0 + S.mx_unit, R.nb);
+  const int lbs = (R.aux >= 0 && lb1 == R.nb) ? lb1 - 1 : lb1;   // stored blocks: [lb0, lbs)
+  const float* qrow = S.qi + (int64_t)r * kIRow;
+  float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb0;
+  const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int b = lane & 7;
+  float q[32];
+  mx_load_q(qrow, b, q);
+#pragma unroll 1
+  for (int p = 0; lb0 + p < lbs; p += 2) {
+    uint4 w[2][4];
+    int e[2][4];
+    bool ok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int lb = lb0 + p + j;
+      const int32_t id = lb < lbs ? tab[lb] : -1;
+      ok[j] = id >= 0 && id < P.max_blocks;   // false past the stored blocks (bad ids never occur)
+      const int64_t kr = (int64_t)(ok[j] ? id : 0) * kBlk;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t t = kr + (wave * 4 + g) * 8 + (lane >> 3);
+        w[j][g] = ok[j] ? load_stream(reinterpret_cast<const uint4*>(P.idx_q + t * kIRowQ) + b)
+                        : make_uint4(0u, 0u, 0u, 0u);
+        e[j][g] = ok[j] ? (int)P.idx_e[t * kIRowE + b] : 127;
+      }
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int lb = lb0 + p + j;
+      if (lb >= lbs) continue;
+      float* o = out + kC4 * (p + j);
+      if (!ok[j]) {
+        if (threadIdx.x < kC4) o[threadIdx.x] = -INFINITY;
+        continue;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) mx_write_pair(mx_dot(w[j][g], e[j][g] - 127, q), o + 2 * (wave * 4 + g));
+    }
+  }
+  if (lbs < lb1) {
+    const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
+    const float* inrow = S.iin + (int64_t)r * kIRow;
+    score_block_mx_raw<kBlk / 32>([&](int t) { return t == kBlk - 1 ? inrow : tail + t * kIRow; }, qrow,
+                                  out + kC4 * (lbs - lb0));
   }
 }
 
@@ -104,8 +156,14 @@ __global__ __launch_bounds__(256, FP8 ? 3 : 4) void k_step1(Pools P, ReqBatch B,
     return;
   }
   bid -= B.n;
-  // -- indexer scores, one workgroup per unit (a 1/kScoreSplit block)
-  if (bid < S.n_score) score_unit(P, B, S, bid);
+  // -- indexer scores, one workgroup per unit (a 1/kScoreSplit block of fp32 keys,
+  //    or S.mx_unit blocks of MXFP4 keys)
+  if (bid < S.n_score) {
+    if (P.mx4)
+      score_unit_mx(P, B, S, bid);
+    else
+      score_unit(P, B, S, bid);
+  }
 }
 
 
