@@ -60,6 +60,15 @@ Readings taken where the pages leave a step open (each also in the design notes)
       ties to the even code, saturating at 6, sign bit set for x < 0. The key
       reads as code value * 2**E. The open block's keys (the State's indexer
       tail) stay float32 until the block seals; the query stays float32.
+  R17 prefix hits under the three SWA policies ([Ch12] §3.1; [Disk] SWA three
+      policies): a prefix entry holds the prefix's sealed blocks (a block
+      reference with no State). Zero: a new request takes the blocks and length
+      len and rebuilds its window from the prefix's raw tokens [len - n_win, len)
+      (in a model they come from a partial prefill; here the caller passes them),
+      never sealing the shared blocks again. Periodic: a checkpoint of the State
+      (SWA window, indexer tail, length) is kept every p tokens; a hit restores the
+      latest checkpoint c <= len and replays [c, len). Full: the checkpoint at len
+      itself. Each yields the State a fork of a live prefix request would have.
 """
 
 from __future__ import annotations
@@ -376,7 +385,8 @@ class _Block:
 
 class _State:
     """Per-request State block: SWA window of exact K/V (oldest first) and the
-    in-flight tail of fewer than 128 tokens ([Q&A] §1.1, §3.3; [Ch12] §2.1)."""
+    in-flight tail of fewer than 128 tokens ([Q&A] §1.1, §3.3; [Ch12] §2.1).
+    After a prefix attach (R17) the window and tail hold None until replayed."""
 
     def __init__(self, n_win: int):
         self.L = 0
@@ -461,6 +471,7 @@ class Oracle:
                 continue
             if len(st.tail) == BLOCK:
                 raise OracleError("state", "tail full: flush before appending")
+            self._filled(st)
             if defer_seal:
                 if len(st.tail) + n > BLOCK:
                     raise OracleError("state", "deferred append past one block")
@@ -539,12 +550,110 @@ class Oracle:
             raise OracleError("state", "dst not fresh")
         if len(a.tail) == BLOCK:
             raise OracleError("state", "src has a pending seal")
+        self._filled(a)
         for b in a.blocks:
             self.refcount[b] += 1
         d.blocks = list(a.blocks)
         d.L = a.L
         d.swa = deque(a.swa, maxlen=self.n_win)
         d.tail = list(a.tail)
+
+    # -- prefix hits (reading R17) -------------------------------------------------
+    def block_ref(self, blocks, delta: int):
+        """Add delta (+1 or -1) to each listed block's refcount: a prefix entry
+        holding blocks without a State ([Ch12] §2.2 refcount; [Disk]). A block whose
+        count reaches 0 is freed. All-or-nothing."""
+        blocks = [int(b) for b in blocks]
+        if delta not in (1, -1):
+            raise OracleError("invalid", "delta must be +1 or -1")
+        for b in set(blocks):
+            if not (0 <= b < self.max_blocks) or self.refcount[b] <= 0:
+                raise OracleError("invalid", f"block {b} not in use")
+            if delta < 0 and blocks.count(b) > self.refcount[b]:
+                raise OracleError("invalid", f"block {b} released more than held")
+        for b in blocks:
+            self.refcount[b] += delta
+            if self.refcount[b] == 0:
+                del self.store[b]
+                heapq.heappush(self.free_blocks, b)
+
+    def prefix_attach(self, dst: int, blocks, length: int):
+        """dst (fresh) takes the prefix's first length // 128 blocks (refcount + 1)
+        and length; its window and tail are unfilled until replayed or restored."""
+        d = self._get(dst)
+        length = int(length)
+        if d.L != 0 or d.blocks:
+            raise OracleError("state", "dst not fresh")
+        nb = length // BLOCK if length >= 0 else -1
+        blocks = [int(b) for b in blocks][:max(nb, 0)]
+        if length < 0 or len(blocks) < nb:
+            raise OracleError("invalid", "length needs length // 128 blocks")
+        for b in blocks:
+            if not (0 <= b < self.max_blocks) or self.refcount[b] <= 0:
+                raise OracleError("invalid", f"block {b} not in use")
+        for b in blocks:
+            self.refcount[b] += 1
+        d.blocks = blocks
+        d.L = length
+        d.swa = deque([None] * min(length, self.n_win), maxlen=self.n_win)
+        d.tail = [None] * (length - BLOCK * nb)
+
+    def state_write(self, states, tokens, pos0):
+        """Replay raw tokens into States without sealing: tokens[i] = (K, V, kI) of
+        positions pos0[i] .. pos0[i] + n - 1, all below the state's L. Positions in
+        the window [L - n_win, L) fill their SWA slot, those of the open block also
+        their tail slot; older ones are dropped. L and blocks are unchanged."""
+        states = [int(x) for x in states]
+        if len(set(states)) != len(states) or len(tokens) != len(states) or len(pos0) != len(states):
+            raise OracleError("invalid", "duplicate or mismatched states")
+        for s_, (K, V, KI), p0 in zip(states, tokens, pos0):
+            st = self._get(s_)
+            n = len(K)
+            if len(V) != n or len(KI) != n:
+                raise OracleError("invalid", "ragged K/V/kI")
+            if n and (int(p0) < 0 or int(p0) + n > st.L):
+                raise OracleError("invalid", "positions outside [0, L)")
+        for s_, (K, V, KI), p0 in zip(states, tokens, pos0):
+            st = self.states[s_]
+            w0 = st.L - len(st.swa)                    # first position in the window
+            t0 = st.L - len(st.tail)                   # first position of the tail
+            for t in range(len(K)):
+                p = int(p0) + t
+                k = np.asarray(K[t], dtype=np.float32)
+                v = np.asarray(V[t], dtype=np.float32)
+                if p >= w0:
+                    st.swa[p - w0] = (k, v)
+                if p >= t0:
+                    st.tail[p - t0] = (k, v, np.asarray(KI[t], dtype=np.float32))
+
+    def checkpoint(self, s: int) -> dict:
+        """The State's SWA window, tail and length (a Periodic / Full checkpoint)."""
+        st = self._get(s)
+        if any(x is None for x in st.swa) or any(x is None for x in st.tail):
+            raise OracleError("state", "state not filled")
+        return {"len": st.L, "swa": list(st.swa), "tail": list(st.tail)}
+
+    def restore(self, s: int, ck: dict):
+        """Fill a state attached at L >= c from the checkpoint taken at c: window
+        positions [max(c - n_win, L - n_win), c) and the tail positions below c that
+        belong to the state's open block. Positions [c, L) stay for replay."""
+        st = self._get(s)
+        c = int(ck["len"])
+        if c > st.L or c < 0:
+            raise OracleError("invalid", "checkpoint is past the state's length")
+        w0, t0 = st.L - len(st.swa), st.L - len(st.tail)
+        for i, item in enumerate(ck["swa"]):
+            p = c - len(ck["swa"]) + i
+            if p >= w0:
+                st.swa[p - w0] = item
+        for i, item in enumerate(ck["tail"]):
+            p = c - len(ck["tail"]) + i
+            if p >= t0:
+                st.tail[p - t0] = item
+
+    def _filled(self, st: _State):
+        if any(x is None for x in st.swa) or any(x is None for x in st.tail):
+            raise OracleError("state", "state not filled: replay or restore first")
 
     # -- indexer top-k -----------------------------------------------------------
     def scores(self, s: int, q_idx) -> np.ndarray:
@@ -565,6 +674,7 @@ class Oracle:
         Classical KV cache read modes). Only the first min(k, N_c) entries of sel
         are read; -1 and out-of-range ordinals are skipped."""
         st = self._get(s)
+        self._filled(st)
         K = [t[0] for t in st.swa]
         V = [t[1] for t in st.swa]
         for b in st.blocks:

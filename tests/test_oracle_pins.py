@@ -697,3 +697,100 @@ def test_mxfp4_oracle_blocks_store_quantized_keys():
     want = np.concatenate([c4_scores(b.block(i).idx, qi) for i in range(2)])
     assert np.array_equal(b.scores(0, qi), want)
     assert not np.array_equal(a.scores(0, qi), want)
+
+
+# ---------------------------------------------------------------- prefix hits (R17)
+
+def _same_state(o, a, b):
+    sa, sb = o.states[a], o.states[b]
+    assert sa.L == sb.L and sa.blocks == sb.blocks
+    assert len(sa.swa) == len(sb.swa) and len(sa.tail) == len(sb.tail)
+    for x, y in zip(sa.swa, sb.swa):
+        assert np.array_equal(x[0], y[0]) and np.array_equal(x[1], y[1])
+    for x, y in zip(sa.tail, sb.tail):
+        assert all(np.array_equal(u, w) for u, w in zip(x, y))
+
+
+@pytest.mark.parametrize("n_win,P,c", [(128, 1000, 512), (128, 1000, 900), (256, 640, 0), (256, 200, 128),
+                                       (128, 384, 256), (512, 1500, 1024)])
+def test_prefix_policies_equal_the_fork(n_win, P, c):
+    """Zero (attach + replay of the window), Periodic (attach + checkpoint at c +
+    replay of [c, P)) and Full (attach + checkpoint at P) each give the State that
+    forking the live prefix request gives, with the blocks shared, not sealed again;
+    the next decode step's top-k and attention agree exactly."""
+    o = make_oracle(n_win=n_win, max_states=8, max_blocks=64)
+    K, V, KI = toks(3, 0, P + 1)
+    src = o.state_alloc()
+    o.append([src], [(K[:c], V[:c], KI[:c])])
+    ck_c = o.checkpoint(src)
+    o.append([src], [(K[c:P], V[c:P], KI[c:P])])
+    ck_p = o.checkpoint(src)
+    fork = o.state_alloc()
+    o.share(src, fork)
+    blocks = o.table(src)
+    o.block_ref(blocks, +1)                      # the prefix entry holds the blocks
+    o.state_free(src)
+    free_before = len(o.free_blocks)
+    zero, per, full = o.state_alloc(), o.state_alloc(), o.state_alloc()
+    for d in (zero, per, full):
+        o.prefix_attach(d, blocks, P)
+    w0 = max(0, P - n_win)
+    o.state_write([zero], [(K[w0:P], V[w0:P], KI[w0:P])], [w0])
+    o.restore(per, ck_c)
+    o.state_write([per], [(K[c:P], V[c:P], KI[c:P])], [c])
+    o.restore(full, ck_p)
+    assert len(o.free_blocks) == free_before     # nothing sealed again
+    for d in (zero, per, full):
+        _same_state(o, fork, d)
+        assert all(o.refcount[b] == 5 for b in blocks)   # fork, entry and three hits
+    qi = synth.tokens_f32(SEED, synth.STREAM_QI, 3, np.array([P]))[0].astype(np.float64)
+    q = synth.bf16_bits_to_f32(synth.tokens_bf16(SEED, synth.STREAM_Q, 3, np.array([P])))[0]
+    for d in (zero, per, full):
+        o.append([d], [(K[P:P + 1], V[P:P + 1], KI[P:P + 1])])
+    o.append([fork], [(K[P:P + 1], V[P:P + 1], KI[P:P + 1])])
+    kk = 64
+    ref_idx, ref_val = o.topk(fork, qi, kk)
+    ref_out = o.attend(fork, q, ref_idx, kk)
+    for d in (zero, per, full):
+        idx, val = o.topk(d, qi, kk)
+        assert np.array_equal(idx, ref_idx) and np.array_equal(val, ref_val)
+        assert np.array_equal(o.attend(d, q, idx, kk), ref_out)
+
+
+def test_prefix_attach_errors_and_unfilled_state():
+    """An attached state cannot be read, appended to or forked before its window is
+    filled; a partial replay leaves it unfilled; bad arguments change nothing; a
+    released prefix entry frees its blocks at refcount 0."""
+    o = make_oracle(n_win=128, max_states=4, max_blocks=16)
+    K, V, KI = toks(4, 0, 300)
+    src = o.state_alloc()
+    o.append([src], [(K, V, KI)])
+    blocks = o.table(src)
+    d = o.state_alloc()
+    with pytest.raises(OracleError):
+        o.prefix_attach(d, blocks[:1], 300)      # needs 2 blocks
+    with pytest.raises(OracleError):
+        o.prefix_attach(src, blocks, 300)        # not fresh
+    assert o.states[d].L == 0 and all(o.refcount[b] == 1 for b in blocks)
+    o.prefix_attach(d, blocks, 300)
+    q = np.zeros((N_HEADS, HEAD_DIM))
+    with pytest.raises(OracleError):
+        o.attend(d, q, [], 1)
+    o.state_write([d], [(K[200:300], V[200:300], KI[200:300])], [200])   # window is [172, 300)
+    with pytest.raises(OracleError):
+        o.append([d], [(K[:1], V[:1], KI[:1])])
+    with pytest.raises(OracleError):
+        o.state_write([d], [(K[250:300], V[250:300], KI[250:300])], [251])   # past L
+    o.state_write([d], [(K[100:200], V[100:200], KI[100:200])], [100])     # 100..171 dropped
+    assert all(x is not None for x in o.states[d].swa)
+    e = o.state_alloc()
+    o.share(src, e)
+    _same_state(o, e, d)
+    with pytest.raises(OracleError):
+        o.block_ref(blocks + blocks + blocks + blocks, -1)   # more than held (3 each)
+    o.block_ref(blocks, +1)
+    for s_ in (src, d, e):
+        o.state_free(s_)
+    assert all(o.refcount[b] == 1 for b in blocks) and len(o.free_blocks) == 14
+    o.block_ref(blocks, -1)
+    assert len(o.free_blocks) == 16 and all(b not in o.store for b in blocks)
