@@ -447,6 +447,123 @@ def run_bulk(args) -> dict:
     }
 
 
+# ------------------------------------------------------------------ prefix hits (SWA policies)
+
+PERIOD = 16384                 # Periodic policy: a State checkpoint every 16384 tokens
+
+
+def run_hits(args) -> dict:
+    """A batch of prefix hits on the prefix workload: each of its 64 requests starts
+    fresh at its fork length (16K-32K tokens, a multiple of 128) of its group's shared
+    prefix, which a prefix entry holds as blocks only (the source request is freed).
+    zero: attach + replay of the last n_win prefix tokens; periodic: attach + restore
+    of the checkpoint at 16384 floor(len / 16384) + replay of the gap; full: attach +
+    restore of the checkpoint at len. The timed region is the whole batch, host calls
+    included, with the replayed tokens already in HBM."""
+    import torch
+    import heterogeneous_sparse_attention_amd as hsa
+    from synth.device import fill_rows
+    wl = workloads.make(3)
+    B, W, pol = wl.batch, wl.n_win, args.hit
+    P = np.array([wl.fork_len(b) for b in range(B)], np.int64)
+    grp = np.array([wl.group(b) for b in range(B)])
+    Wc, Wh = synth.gate_weights(wl.seed)
+    n_blk = wl.n_groups * (wl.prefix_len // 128) + 8
+    cache = hsa.Cache(W, 2 * B + wl.n_groups, n_blk, Wc, Wh, max_blocks_per_state=wl.prefix_len // 128 + 2)
+    lists, ck = [], {}
+    for g in range(wl.n_groups):
+        kids = np.flatnonzero(grp == g)
+        stops = sorted(set(int(x) for x in P[kids]) | {PERIOD * (int(x) // PERIOD) for x in P[kids]})
+        par = cache.state_alloc()
+        done = 0
+        for stop in stops:
+            if stop > done:
+                _append_device(cache, wl, [par], [int(kids[0])], [done], [stop])
+                done = stop
+            if stop > 0:
+                ck[(g, stop)] = cache.state_checkpoint(par)[0]
+        blocks = cache.block_table(par)
+        cache.block_ref(blocks, +1)                      # the prefix entry
+        cache.state_free(par)
+        lists.append(blocks)
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])[:-1]]).astype(np.int64)
+    flat = np.concatenate(lists).astype(np.int32)
+    # replayed rows: zero [len - n_win, len); periodic [c, len); full none
+    c = PERIOD * (P // PERIOD)
+    lo = np.maximum(P - W, 0) if pol == "zero" else (c if pol == "periodic" else P)
+    rows = P - lo
+    T = int(rows.sum())
+    cu = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    if T:
+        pos = np.concatenate([np.arange(a, b) for a, b in zip(lo, P)]).astype(np.int64)
+        keys = np.concatenate([wl.key(b, np.arange(a, e)) for b, (a, e) in enumerate(zip(lo, P))]).astype(np.int64)
+        kt, pt = torch.from_numpy(keys.astype(np.int32)).cuda(), torch.from_numpy(pos).cuda()
+        K = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
+        V = torch.empty_like(K)
+        KI = torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")
+        for t, sid in ((K, synth.STREAM_K), (V, synth.STREAM_V), (KI, synth.STREAM_IDXK)):
+            fill_rows(t, wl.seed, sid, keys=kt, pos=pt)
+    torch.cuda.synchronize()
+
+    def hit_batch():
+        states = [cache.state_alloc() for _ in range(B)]
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.prefix_attach(states, flat, P, offsets=off[grp])
+        if pol in ("periodic", "full"):
+            for b, s in enumerate(states):
+                at = int(c[b]) if pol == "periodic" else int(P[b])
+                if at > 0:
+                    cache.state_restore(s, ck[(int(grp[b]), at)], at)
+        if T:
+            cache.state_write(states, cu, lo, K, V, KI)
+        e1.record()
+        torch.cuda.synchronize()
+        for s in states:
+            cache.state_free(s)
+        return e0.elapsed_time(e1)
+
+    for _ in range(max(1, args.warmup)):
+        hit_batch()
+    times = [hit_batch() for _ in range(args.steps)]
+    cache.timing_enable(["write"])
+    hit_batch()
+    kt_ = cache.timing_read()
+    cache.timing_enable([])
+    cache.close()
+    ms = float(np.median(times))
+    # algorithmic bytes: ring slots (and tail keys) read + written by restores and
+    # replays, table rows written
+    rest = np.minimum(c if pol == "periodic" else (P if pol == "full" else 0), W)
+    repl = np.minimum(rows, W)
+    write_b = int((repl * 2 * ROW).sum())
+    alg = int((rest * 2 * ROW).sum()) + write_b + int((P // 128).sum()) * 8
+    wr_ms = kt_["write"][0]
+    return {
+        "metric": f"prefix-hit setup, hits/s + achieved HBM GB/s, {pol} SWA policy",
+        "value": B / (ms * 1e-3), "unit": "hits/s", "n_gpus": 1, "steps": len(times),
+        "warmup": max(1, args.warmup), "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefix: {B} requests each starting at its fork length (16K-32K tokens) "
+                               f"of one of {wl.n_groups} shared 32768-token prefixes held as blocks; "
+                               f"n_win {W}; {pol} policy (checkpoint period {PERIOD})",
+                   "batch": B, "n_win": W, "policy": pol, "replayed_tokens": T,
+                   "parallelism": "single GPU"},
+        "hbm_gbps": alg / (ms * 1e-3) / 1e9, "hbm_frac_of_peak": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "kernel": "k_bulk_write" if T else "hipMemcpyAsync (restore)",
+                     "achieved": (write_b / (wr_ms * 1e-3) / 1e9) if (T and wr_ms) else alg / (ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ((write_b / (wr_ms * 1e-3) / 1e9) if (T and wr_ms) else alg / (ms * 1e-3) / 1e9)
+                     / PEAK_HBM_GBS,
+                     "traffic": None, "avg_launch_us": wr_ms * 1e3 if T else None,
+                     "algorithmic_bytes_per_launch": write_b if T else alg,
+                     "measured": "HIP event pair on the k_bulk_write dispatch of one batch" if T
+                                 else "events around the whole batch"},
+    }
+
+
 # ------------------------------------------------------------------ CPU baseline (the oracle)
 
 def cpu_baseline(args, budget_s: float = 15.0) -> dict:
@@ -581,6 +698,8 @@ def main():
                     help="storage format of the C4 entries (bf16, or FP8 E4M3 with a per-head scale)")
     ap.add_argument("--index", default="f32", choices=["f32", "mxfp4"],
                     help="storage format of sealed indexer keys (fp32, or MXFP4 with E8M0 block scales)")
+    ap.add_argument("--hit", default=None, choices=["zero", "periodic", "full"],
+                    help="time a batch of prefix hits on the prefix workload under this SWA policy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters", default=None, help="comma-separated rocprofv3 --pmc output dirs")
@@ -601,6 +720,9 @@ def main():
         copy_calibration(args)
         return
     args.warmup = max(args.warmup, 2)
+    if args.hit:
+        print(json.dumps(run_hits(args)), flush=True)
+        return
     res = run_bulk(args) if args.workload == 4 else run_decode(args)
     if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16" \
             and args.index == "f32":

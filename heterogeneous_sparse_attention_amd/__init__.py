@@ -84,6 +84,12 @@ SIGNATURES = {
     "hsa_export_c4_fp8": [_P, _I32, _P, _P, _P, _P, _P],
     "hsa_fp8_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_export_idx_mxfp4": [_P, _I32, _P, _P, _P],
+    "hsa_block_ref": [_P, _P, _I64, _I32],
+    "hsa_prefix_attach": [_P, _I32, _P, _P, _P, _I64, _P, _P],
+    "hsa_state_write": [_P, _I32, _P, _P, _P, _P, _P, _P, _P],
+    "hsa_checkpoint_bytes": [_P, _P],
+    "hsa_state_checkpoint": [_P, _I32, _P, _P, _P],
+    "hsa_state_restore": [_P, _I32, _P, _I64, _P],
     "hsa_mxfp4_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_timing_enable": [_P, _U32],
     "hsa_timing_read": [_P, _P, _P],
@@ -228,6 +234,65 @@ class Cache:
     def block_table_share(self, src: int, dst: int, stream=None):
         _check(_lib.hsa_block_table_share(self._ctx, int(src), int(dst), _stream(stream)),
                "hsa_block_table_share")
+
+    # -- prefix hits (Zero / Periodic / Full SWA policies) ----------------------------
+    def block_ref(self, blocks, delta: int):
+        """Hold (+1) or release (-1) one reference of each listed block."""
+        b, bp = _host_i32(blocks)
+        _check(_lib.hsa_block_ref(self._ctx, bp, b.size, int(delta)), "hsa_block_ref")
+
+    def prefix_attach(self, states, blocks, lengths, offsets=None, stream=None):
+        """states[i] (empty) takes blocks[offsets[i] : offsets[i] + lengths[i] // 128]
+        (offsets default to 0: every state attaches to the same list) and length
+        lengths[i]; fill its window next. A single state and length are accepted."""
+        st, stp = _host_i32([states] if np.isscalar(states) else states)
+        ln, lnp = _host_i64([lengths] if np.isscalar(lengths) else lengths)
+        off, offp = _host_i64(np.zeros(st.size, np.int64) if offsets is None else offsets)
+        b, bp = _host_i32(blocks)
+        if ln.size != st.size or off.size != st.size:
+            raise ValueError("lengths and offsets need one entry per state")
+        if np.any(off + ln // 128 > b.size):
+            raise ValueError("prefix_attach needs length // 128 blocks from each offset")
+        _check(_lib.hsa_prefix_attach(self._ctx, st.size, stp, lnp, bp, b.size, offp, _stream(stream)),
+               "hsa_prefix_attach")
+
+    def state_write(self, states, cu_tokens, pos0, k, v, idx_k, stream=None):
+        """Replay raw tokens (rows cu[i] .. cu[i+1]) as positions pos0[i] .. of states[i]."""
+        import torch
+        st, stp = _host_i32(states)
+        cu, cup = _host_i64(cu_tokens)
+        p0, p0p = _host_i64(pos0)
+        if cu.size != st.size + 1 or p0.size != st.size:
+            raise ValueError("cu_tokens needs len(states) + 1 entries and pos0 len(states)")
+        T = int(cu[-1]) if cu.size else 0
+        kp = _dev(k, torch.bfloat16, (T, H, D), "k")
+        vp = _dev(v, torch.bfloat16, (T, H, D), "v")
+        ip = _dev(idx_k, torch.float32, (T, HI, DI), "idx_k")
+        _check(_lib.hsa_state_write(self._ctx, st.size, stp, cup, p0p, kp, vp, ip, _stream(stream)),
+               "hsa_state_write")
+
+    def checkpoint_bytes(self) -> int:
+        n = ctypes.c_int64()
+        _check(_lib.hsa_checkpoint_bytes(self._ctx, ctypes.byref(n)), "hsa_checkpoint_bytes")
+        return n.value
+
+    def state_checkpoint(self, s: int, buf=None, stream=None):
+        """Checkpoint of a state's window and tail into a device uint8 tensor (new if
+        buf is None); returns (buf, length)."""
+        import torch
+        nb = self.checkpoint_bytes()
+        if buf is None:
+            buf = torch.empty((nb,), dtype=torch.uint8, device=f"cuda:{self.device}")
+        n = ctypes.c_int64()
+        _check(_lib.hsa_state_checkpoint(self._ctx, int(s), _dev(buf, torch.uint8, (nb,), "buf"),
+                                         ctypes.byref(n), _stream(stream)), "hsa_state_checkpoint")
+        return buf, n.value
+
+    def state_restore(self, s: int, buf, length: int, stream=None):
+        import torch
+        nb = self.checkpoint_bytes()
+        _check(_lib.hsa_state_restore(self._ctx, int(s), _dev(buf, torch.uint8, (nb,), "buf"), int(length),
+                                      _stream(stream)), "hsa_state_restore")
 
     # -- indexer top-k --------------------------------------------------------------
     def indexer_topk(self, states, q_idx, k: int, idx_out=None, score_out=None, sorted=False,

@@ -79,9 +79,18 @@ __global__ __launch_bounds__(256) void k_bulk_write(Pools P, const WriteDesc* w,
                                                     int64_t total, const uint16_t* kin,
                                                     const uint16_t* vin, const float* iin) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   for (int64_t x = blockIdx.x; x < total; x += gridDim.x) {
-    int r = 0;
-    while (r + 1 < n_req && w[r + 1].cum <= x) ++r;
+    // the request owning token x: the number of descriptors with cum <= x, minus one
+    // (cum is nondecreasing), counted 64 descriptors per ballot
+    int r = -1;
+    for (int base = 0; base < n_req; base += 64) {
+      const int i = base + lane;
+      const int c = __popcll(__ballot(i < n_req && w[i].cum <= x));
+      r = base + c - 1;
+      if (c < 64) break;
+    }
+    r = uniform(r);
     const WriteDesc d = w[r];
     const int64_t p = d.w0 + (x - d.cum);
     const int64_t row = d.row0 + (p - d.len_old);
@@ -111,6 +120,14 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const float* x, int64_t n_rows
   if ((threadIdx.x & 15) == 0) scales[row] = sc;
 }
 
+// Table rows of attached states: one workgroup per state copies its block ids.
+__global__ __launch_bounds__(256) void k_attach_rows(int32_t* table, int64_t stride, const AttachDesc* d,
+                                                     const int32_t* ids) {
+  const AttachDesc a = d[blockIdx.x];
+  for (int64_t j = threadIdx.x; j < a.nb; j += 256)
+    table[(int64_t)a.state * stride + j] = ids[a.off + j];
+}
+
 // MXFP4 storage of indexer key rows (256 fp32 each), exactly as the seal stores
 // them: a wave per row, 4 rows per workgroup.
 __global__ __launch_bounds__(256) void k_mx4_rows(const float* x, int64_t n_rows, uint8_t* codes,
@@ -123,6 +140,13 @@ __global__ __launch_bounds__(256) void k_mx4_rows(const float* x, int64_t n_rows
 }
 
 }  // namespace
+
+hipError_t launch_attach_rows(const Pools& P, const AttachDesc* d, int32_t n, const int32_t* ids,
+                              hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  return launch_k(k_attach_rows, dim3((unsigned)n), dim3(256), st, LaunchEv{}, P.table, P.table_stride, d,
+                  ids);
+}
 
 hipError_t launch_mx4_rows(const float* x, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                            hipStream_t st) {

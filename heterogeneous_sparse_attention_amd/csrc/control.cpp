@@ -226,4 +226,112 @@ void Control::commit_share(int32_t src, int32_t dst) {
   len_[dst] = len_[src];
 }
 
+int Control::check_block_ref(const int32_t* blocks, int64_t n, int32_t delta, std::string* why) const {
+  if (delta != 1 && delta != -1) {
+    *why = "block_ref: delta must be +1 or -1";
+    return kInvalid;
+  }
+  if (n < 0 || (n > 0 && !blocks)) {
+    *why = "block_ref: bad block list";
+    return kInvalid;
+  }
+  std::vector<int32_t> sorted(blocks, blocks + n);
+  std::sort(sorted.begin(), sorted.end());
+  for (int64_t i = 0; i < n;) {
+    int64_t j = i;
+    while (j < n && sorted[j] == sorted[i]) ++j;
+    const int32_t b = sorted[i];
+    if (!valid_block(b) || refcount_[b] <= 0) {
+      *why = "block_ref: block not in use";
+      return kInvalid;
+    }
+    if (delta < 0 && j - i > refcount_[b]) {
+      *why = "block_ref: block released more times than it is held";
+      return kInvalid;
+    }
+    i = j;
+  }
+  return kOk;
+}
+
+void Control::commit_block_ref(const int32_t* blocks, int64_t n, int32_t delta) {
+  for (int64_t i = 0; i < n; ++i) {
+    refcount_[blocks[i]] += delta;
+    if (refcount_[blocks[i]] == 0) blocks_.give(blocks[i]);
+  }
+}
+
+int Control::check_attach(int32_t dst, const int32_t* blocks, int64_t len, std::string* why) const {
+  if (!valid_state(dst)) {
+    *why = "attach: state not allocated";
+    return kInvalid;
+  }
+  if (len_[dst] != 0 || !table_[dst].empty()) {
+    *why = "attach: dst is not empty";
+    return kState;
+  }
+  const int64_t nb = len / kBlockTokens;
+  if (len < 0 || nb > max_bps_ || (nb > 0 && !blocks)) {
+    *why = "attach: bad length or block list";
+    return kInvalid;
+  }
+  for (int64_t i = 0; i < nb; ++i)
+    if (!valid_block(blocks[i]) || refcount_[blocks[i]] <= 0) {
+      *why = "attach: block not in use";
+      return kInvalid;
+    }
+  return kOk;
+}
+
+void Control::commit_attach(int32_t dst, const int32_t* blocks, int64_t len) {
+  const int64_t nb = len / kBlockTokens;
+  for (int64_t i = 0; i < nb; ++i) ++refcount_[blocks[i]];
+  table_[dst].assign(blocks, blocks + nb);
+  len_[dst] = len;
+}
+
+int Control::check_attach_batch(int32_t n_req, const int32_t* states, const int64_t* len,
+                                const int32_t* blocks, int64_t n_blocks, const int64_t* off,
+                                std::string* why) const {
+  int st = check_states(n_req, states, true, false, why);
+  if (st) return st;
+  if (n_req > 0 && (!len || !off) ) {
+    *why = "attach: NULL lengths or offsets";
+    return kInvalid;
+  }
+  for (int32_t i = 0; i < n_req; ++i) {
+    const int64_t nb = len[i] >= 0 ? len[i] / kBlockTokens : 0;
+    if (len[i] < 0 || off[i] < 0 || off[i] + nb > n_blocks) {
+      *why = "attach: length or block offset out of range";
+      return kInvalid;
+    }
+    st = check_attach(states[i], nb > 0 ? blocks + off[i] : nullptr, len[i], why);
+    if (st) return st;
+  }
+  return kOk;
+}
+
+int Control::check_state_write(int32_t n_req, const int32_t* states, const int64_t* cu,
+                               const int64_t* pos0, std::string* why) const {
+  int st = check_states(n_req, states, true, false, why);
+  if (st) return st;
+  if (n_req == 0) return kOk;
+  if (!cu || !pos0 || cu[0] != 0) {
+    *why = "state_write: bad cu_tokens or pos0";
+    return kInvalid;
+  }
+  for (int32_t i = 0; i < n_req; ++i) {
+    const int64_t n = cu[i + 1] - cu[i];
+    if (n < 0) {
+      *why = "state_write: cu_tokens must be nondecreasing";
+      return kInvalid;
+    }
+    if (n > 0 && (pos0[i] < 0 || pos0[i] + n > len_[states[i]])) {
+      *why = "state_write: positions outside [0, L)";
+      return kInvalid;
+    }
+  }
+  return kOk;
+}
+
 }  // namespace hsa

@@ -94,6 +94,21 @@ class Control {
   int check_share(int32_t src, int32_t dst, std::string* why) const;
   void commit_share(int32_t src, int32_t dst);
 
+  // Prefix hits ([Ch12] §3.1; [Disk] SWA policies): block references held by a
+  // prefix entry (delta +1 / -1; a block at 0 is freed), and a fresh state taking
+  // a prefix's first len / 128 blocks and length len (its window is filled later).
+  int check_block_ref(const int32_t* blocks, int64_t n, int32_t delta, std::string* why) const;
+  void commit_block_ref(const int32_t* blocks, int64_t n, int32_t delta);
+  int check_attach(int32_t dst, const int32_t* blocks, int64_t len, std::string* why) const;
+  void commit_attach(int32_t dst, const int32_t* blocks, int64_t len);
+  // A batch: states[i] (distinct) takes blocks[off[i] .. off[i] + len[i] / 128) of a
+  // list of n_blocks ids (lists may overlap) and length len[i].
+  int check_attach_batch(int32_t n_req, const int32_t* states, const int64_t* len, const int32_t* blocks,
+                         int64_t n_blocks, const int64_t* off, std::string* why) const;
+  // Replay of raw tokens into states: distinct states, cu[0] = 0 and nondecreasing,
+  // positions [pos0[i], pos0[i] + n_i) inside [0, L) of states[i].
+  int check_state_write(int32_t n_req, const int32_t* states, const int64_t* cu, const int64_t* pos0,
+                        std::string* why) const;
   // Read-side validation: allocated states; optionally distinct / non-empty.
   int check_states(int32_t n_req, const int32_t* states, bool distinct, bool nonempty,
                    std::string* why) const;

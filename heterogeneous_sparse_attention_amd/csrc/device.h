@@ -135,6 +135,14 @@ struct WriteDesc {
   int64_t cum;       // tokens written by earlier requests of the call
 };
 
+// One state of a prefix attach: its table row takes ids[off .. off + nb).
+struct AttachDesc {
+  int32_t state;
+  int32_t pad_;
+  int64_t nb;
+  int64_t off;
+};
+
 // Arguments of the four decode-step launches (one batch of <= kMaxReq requests).
 struct StepArgs {
   const uint16_t* kin;   // new tokens' K, V [n][16][128] bf16 and indexer keys [n][256]

@@ -63,6 +63,24 @@ int32_t hsah_share(void* c_, int32_t src, int32_t dst) {
   return 0;
 }
 
+int32_t hsah_block_ref(void* c_, const int32_t* blocks, int64_t n, int32_t delta) {
+  Control* c = static_cast<Control*>(c_);
+  std::string why;
+  int st = c->check_block_ref(blocks, n, delta, &why);
+  if (st) return st;
+  c->commit_block_ref(blocks, n, delta);
+  return 0;
+}
+
+int32_t hsah_attach(void* c_, int32_t dst, const int32_t* blocks, int64_t len) {
+  Control* c = static_cast<Control*>(c_);
+  std::string why;
+  int st = c->check_attach(dst, blocks, len, &why);
+  if (st) return st;
+  c->commit_attach(dst, blocks, len);
+  return 0;
+}
+
 int32_t hsah_query(void* c_, int32_t s, int64_t* len, int64_t* nb, int32_t* pending) {
   Control* c = static_cast<Control*>(c_);
   if (!c->valid_state(s)) return hsa::kInvalid;

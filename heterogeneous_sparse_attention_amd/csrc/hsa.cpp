@@ -682,6 +682,131 @@ hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* str
   return kOk;
 }
 
+// ---- prefix hits: block references, attach, replay, checkpoints -------------------
+
+hsa_status hsa_block_ref(hsa_ctx* c, const int32_t* blocks, int64_t n, int32_t delta) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  int st = c->ctl.check_block_ref(blocks, n, delta, &why);
+  if (st) return fail(st, why);
+  c->ctl.commit_block_ref(blocks, n, delta);
+  return kOk;
+}
+
+hsa_status hsa_prefix_attach(hsa_ctx* c, int32_t n_req, const int32_t* states, const int64_t* len,
+                             const int32_t* blocks, int64_t n_blocks, const int64_t* block_off,
+                             void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  if (n_blocks < 0 || (n_blocks > 0 && !blocks)) return fail(kInvalid, "bad block list");
+  int st = c->ctl.check_attach_batch(n_req, states, len, blocks, n_blocks, block_off, &why);
+  if (st) return fail(st, why);
+  if ((st = set_device(c))) return st;
+  std::vector<AttachDesc> d;
+  int64_t used = 0;   // ids needed: the list up to the furthest one referenced
+  for (int32_t i = 0; i < n_req; ++i) {
+    const int64_t nb = len[i] / kBlk;
+    c->ctl.commit_attach(states[i], blocks + block_off[i], len[i]);
+    if (nb == 0) continue;
+    d.push_back(AttachDesc{states[i], 0, nb, block_off[i]});
+    used = std::max(used, block_off[i] + nb);
+  }
+  if (d.empty()) return kOk;
+  // descriptors, then the ids, staged in one upload; one launch writes every row
+  const size_t db = d.size() * sizeof(AttachDesc);
+  std::vector<char> buf(db + (size_t)used * 4);
+  std::memcpy(buf.data(), d.data(), db);
+  std::memcpy(buf.data() + db, blocks, (size_t)used * 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = upload_plan(c, buf.data(), buf.size(), s);
+  if (st) return st;
+  const char* dev = static_cast<const char*>(c->plan_dev);
+  HIP_TRY(launch_attach_rows(c->P, reinterpret_cast<const AttachDesc*>(dev), (int32_t)d.size(),
+                             reinterpret_cast<const int32_t*>(dev + db), s));
+  return kOk;
+}
+
+hsa_status hsa_state_write(hsa_ctx* c, int32_t n_req, const int32_t* states, const int64_t* cu_tokens,
+                           const int64_t* pos0, const void* k, const void* v, const float* idx,
+                           void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  std::string why;
+  int st = c->ctl.check_state_write(n_req, states, cu_tokens, pos0, &why);
+  if (st) return fail(st, why);
+  if (n_req == 0 || cu_tokens[n_req] == 0) return kOk;
+  if (!k || !v || !idx) return fail(kInvalid, "input pointer is NULL");
+  if ((st = set_device(c))) return st;
+  std::vector<WriteDesc> writes;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_req; ++i) {
+    const int64_t n = cu_tokens[i + 1] - cu_tokens[i];
+    const int32_t s = states[i];
+    const int64_t L = c->ctl.len(s);
+    const int64_t w0 = std::max(pos0[i], L - (int64_t)c->P.n_win);   // older positions are dropped
+    if (n == 0 || w0 >= pos0[i] + n) continue;
+    writes.push_back(WriteDesc{s, (int32_t)c->ctl.n_blocks(s), pos0[i], pos0[i] + n, w0, cu_tokens[i], total});
+    total += pos0[i] + n - w0;
+  }
+  if (writes.empty()) return kOk;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = upload_plan(c, writes.data(), writes.size() * sizeof(WriteDesc), hs);
+  if (st) return st;
+  Timed t(c, HSA_KERNEL_WRITE, hs);
+  HIP_TRY(launch_bulk_write(c->P, static_cast<const WriteDesc*>(c->plan_dev), (int32_t)writes.size(), total,
+                            k, v, idx, hs, t.ev()));
+  return kOk;
+}
+
+hsa_status hsa_checkpoint_bytes(hsa_ctx* c, int64_t* bytes) {
+  if (!c || !bytes) return fail(kInvalid, "NULL argument");
+  *bytes = 2 * (int64_t)c->P.n_win * kRow * 2 + (int64_t)kBlk * kIRow * 4;
+  return kOk;
+}
+
+hsa_status hsa_state_checkpoint(hsa_ctx* c, int32_t s_, void* buf, int64_t* len_out, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->ctl.valid_state(s_)) return fail(kInvalid, "state not allocated");
+  if (!buf || !len_out) return fail(kInvalid, "NULL argument");
+  if (c->ctl.pending(s_)) return fail(kState, "the state has a pending seal");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t L = c->ctl.len(s_), W = c->P.n_win, tail = L - kBlk * c->ctl.n_blocks(s_);
+  const int64_t slots = std::min(L, W);
+  char* b = static_cast<char*>(buf);
+  const size_t ring = (size_t)W * kRow * 2, S = (size_t)s_;
+  if (slots > 0) {
+    HIP_TRY(hipMemcpyAsync(b, c->P.swa_k + S * W * kRow, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
+    HIP_TRY(hipMemcpyAsync(b + ring, c->P.swa_v + S * W * kRow, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
+  }
+  if (tail > 0)
+    HIP_TRY(hipMemcpyAsync(b + 2 * ring, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4,
+                           hipMemcpyDefault, s));
+  *len_out = L;
+  return kOk;
+}
+
+hsa_status hsa_state_restore(hsa_ctx* c, int32_t s_, const void* buf, int64_t ckpt_len, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->ctl.valid_state(s_)) return fail(kInvalid, "state not allocated");
+  if (!buf) return fail(kInvalid, "NULL buffer");
+  if (ckpt_len < 0 || ckpt_len > c->ctl.len(s_)) return fail(kInvalid, "checkpoint is past the state's length");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t W = c->P.n_win, slots = std::min(ckpt_len, W), tail = ckpt_len % kBlk;
+  const char* b = static_cast<const char*>(buf);
+  const size_t ring = (size_t)W * kRow * 2, S = (size_t)s_;
+  if (slots > 0) {
+    HIP_TRY(hipMemcpyAsync(c->P.swa_k + S * W * kRow, b, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
+    HIP_TRY(hipMemcpyAsync(c->P.swa_v + S * W * kRow, b + ring, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
+  }
+  if (tail > 0)
+    HIP_TRY(hipMemcpyAsync(c->P.idx_tail + S * kBlk * kIRow, b + 2 * ring, (size_t)tail * kIRow * 4,
+                           hipMemcpyDefault, s));
+  return kOk;
+}
+
 hsa_status hsa_indexer_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx,
                             int32_t k, uint32_t flags, int32_t* idx_out, float* score_out,
                             void* stream) {

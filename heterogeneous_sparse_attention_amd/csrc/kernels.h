@@ -64,6 +64,9 @@ hipError_t launch_select(const ReqBatch& B, const SelPlan& SP, int32_t k, int32_
 // Per-row FP8 storage (the C4 entry quantisation) of n_rows rows of 128 floats.
 hipError_t launch_fp8_rows(const float* x, int64_t n_rows, uint8_t* codes, float* scales,
                            hipStream_t st);
+// Table rows of states attached to a prefix (block ids staged on the device).
+hipError_t launch_attach_rows(const Pools& P, const AttachDesc* d, int32_t n, const int32_t* ids,
+                              hipStream_t st);
 // Per-key MXFP4 storage (the sealed indexer key quantisation) of n_rows keys of 256 floats.
 hipError_t launch_mx4_rows(const float* x, int64_t n_rows, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);

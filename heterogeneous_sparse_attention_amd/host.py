@@ -30,6 +30,8 @@ def load():
             "hsah_append": (_I32, [_P, _I32, _P, _P, _U32, _P, _I64, ctypes.POINTER(_I64)]),
             "hsah_flush": (_I32, [_P, _I32, _P, ctypes.POINTER(_I64)]),
             "hsah_share": (_I32, [_P, _I32, _I32]),
+            "hsah_block_ref": (_I32, [_P, _P, _I64, _I32]),
+            "hsah_attach": (_I32, [_P, _I32, _P, _I64]),
             "hsah_query": (_I32, [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
             "hsah_table": (_I32, [_P, _I32, _P, _I64, ctypes.POINTER(_I64)]),
             "hsah_refcount": (_I32, [_P, _I64]),
@@ -82,6 +84,14 @@ class HostControl:
 
     def share(self, src, dst):
         return self._lib.hsah_share(self._c, int(src), int(dst))
+
+    def block_ref(self, blocks, delta):
+        b = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32).reshape(-1))
+        return self._lib.hsah_block_ref(self._c, b.ctypes.data_as(_P), b.size, int(delta))
+
+    def attach(self, dst, blocks, length):
+        b = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32).reshape(-1))
+        return self._lib.hsah_attach(self._c, int(dst), b.ctypes.data_as(_P) if b.size else None, int(length))
 
     def query(self, s):
         L, nb, pend = _I64(), _I64(), _I32()

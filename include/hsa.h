@@ -164,6 +164,65 @@ hsa_status hsa_compress_flush(hsa_ctx* ctx, int32_t n_req, const int32_t* states
  * (bad ids, src == dst), STATE (dst not empty, src has a pending seal). */
 hsa_status hsa_block_table_share(hsa_ctx* ctx, int32_t src, int32_t dst, void* stream);
 
+/* ---- prefix hits under the three SWA policies ([Ch12] "Ch 12" §3.1 and the
+ * "V4 磁盘 Prefix Cache" page, SWA policies: Full / Periodic Checkpointing / Zero).
+ * A prefix entry holds the prefix's sealed blocks by reference (hsa_block_ref) and,
+ * by policy, State checkpoints. A hit makes a fresh state from it:
+ *   Zero      hsa_prefix_attach, then hsa_state_write of the prefix's tokens
+ *             [max(0, len - n_win), len) (raw K, V, indexer keys);
+ *   Periodic  hsa_prefix_attach, hsa_state_restore of the latest checkpoint c <= len,
+ *             then hsa_state_write of the tokens [c, len);
+ *   Full      hsa_prefix_attach, then hsa_state_restore of the checkpoint at len.
+ * Each gives the state, slot for slot, that hsa_block_table_share of a live request
+ * at len gives; the shared blocks are never sealed again. Until its window is
+ * filled that way, an attached state must not be read or appended to (the library
+ * cannot tell). */
+
+/* Add delta (+1 or -1) to the refcount of each listed block (host [n]; a block may
+ * repeat), so that a prefix entry can hold blocks with no state. +1 needs each block
+ * in use; -1 may not release more than is held; a block reaching 0 is freed. Checked
+ * as a whole: on error nothing changes. No device work. Errors: INVALID. */
+hsa_status hsa_block_ref(hsa_ctx* ctx, const int32_t* blocks, int64_t n, int32_t delta);
+
+/* Each of n_req distinct states (allocated, L = 0) takes len[i] and, as its sealed
+ * blocks, blocks[block_off[i] .. block_off[i] + len[i] / 128) of a host list of
+ * n_blocks ids (each used one in use; requests of one prefix may point at the same
+ * range), refcount + 1 per reference. The table rows are written on `stream` (one
+ * launch); the SWA rings and indexer tails are left as they are (fill them as
+ * above). len, block_off: host [n_req]. Checked as a whole. Errors: INVALID (bad ids,
+ * lengths or offsets), STATE (a state not empty). */
+hsa_status hsa_prefix_attach(hsa_ctx* ctx, int32_t n_req, const int32_t* states, const int64_t* len,
+                             const int32_t* blocks, int64_t n_blocks, const int64_t* block_off,
+                             void* stream);
+
+/* Replay raw tokens into states without sealing. Request i writes input rows
+ * [cu_tokens[i], cu_tokens[i+1]) as positions pos0[i] .. pos0[i] + n_i - 1, which must
+ * lie in [0, L) of states[i] (distinct states). A position in the window
+ * [L - n_win, L) goes to ring slot p mod n_win, one of the open block also to indexer
+ * tail slot p mod 128; older positions are skipped. L and the block table do not
+ * change. k, v: device bf16 [T][16][128]; idx: device fp32 [T][4][64]; cu_tokens,
+ * pos0: host [n_req + 1], [n_req]. Errors: INVALID. */
+hsa_status hsa_state_write(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                           const int64_t* cu_tokens, const int64_t* pos0, const void* k,
+                           const void* v, const float* idx, void* stream);
+
+/* Bytes of one State checkpoint: SWA ring K and V (n_win x 4 KiB each), then the
+ * indexer tail (128 x 1 KiB). */
+hsa_status hsa_checkpoint_bytes(hsa_ctx* ctx, int64_t* bytes);
+
+/* Copy a state's SWA ring and indexer tail into `buf` (device or pinned host memory,
+ * hsa_checkpoint_bytes long, owned by the caller) on `stream`; *len_out = its L, the
+ * checkpoint's position. Errors: INVALID, STATE (pending seal). */
+hsa_status hsa_state_checkpoint(hsa_ctx* ctx, int32_t state, void* buf, int64_t* len_out,
+                                void* stream);
+
+/* Copy a checkpoint taken at ckpt_len (<= the state's L, from the same prefix) into
+ * the state's ring and tail slots on `stream`. Positions [ckpt_len, L) keep whatever
+ * their slots hold until replayed with hsa_state_write, so restore first. Errors:
+ * INVALID. */
+hsa_status hsa_state_restore(hsa_ctx* ctx, int32_t state, const void* buf, int64_t ckpt_len,
+                             void* stream);
+
 /* Indexer top-k over each state's sealed C4 entries ([Ch12] 名词速通: the
  * indexer's K-only keys serve top-k selection; [Layout] Classical KV cache:
  * CSA entries are read sparsely through top-k).

@@ -46,9 +46,9 @@ def test_control_matches_oracle(seed):
     n_win, max_states, max_blocks = 256, 6, 24
     o = Oracle(n_win, Z, Z, max_states, max_blocks)
     h = HostControl(n_win, max_states, max_blocks)
-    live = []
-    for op in range(120):
-        kind = int(rng.integers(6))
+    live, held = [], []
+    for op in range(160):
+        kind = int(rng.integers(8))
         if kind == 0:
             ro, so = run_oracle(o.state_alloc)
             rh, sh = h.state_alloc()
@@ -80,6 +80,34 @@ def test_control_matches_oracle(seed):
         elif kind == 5 and len(live) >= 2:
             a, b = (int(x) for x in rng.choice(live, 2))
             assert run_oracle(lambda: o.share(a, b))[0] == h.share(a, b)
+        elif kind == 6 and len(live) >= 2:
+            # prefix hit: attach to a (prefix of a) live state's blocks, then fill the
+            # window in the oracle (the host plane does not track filling)
+            a, d = (int(x) for x in rng.choice(live, 2))
+            blocks = o.table(a)
+            n = int(rng.integers(0, len(blocks) + 1))
+            length = 128 * n + int(rng.integers(0, 128)) if rng.random() < 0.9 else 128 * (n + 1)
+            ro, _ = run_oracle(lambda: o.prefix_attach(d, blocks, length))
+            assert ro == h.attach(d, blocks, length), (ro, length, n)
+            if ro == 0:
+                m = min(length, n_win)
+                o.state_write([d], [zeros(m)], [length - m])
+        elif kind == 7:
+            if held and rng.random() < 0.5:
+                blocks = held.pop(int(rng.integers(len(held))))
+                delta = -1
+            else:
+                pool = [b for s in live for b in o.table(s)]
+                blocks = [int(x) for x in rng.choice(pool, int(rng.integers(1, 4)))] if pool else [0]
+                if rng.random() < 0.1:
+                    blocks = blocks + [int(rng.integers(max_blocks))]   # maybe a free one -> invalid
+                delta = 1
+            ro, _ = run_oracle(lambda: o.block_ref(blocks, delta))
+            assert ro == h.block_ref(blocks, delta)
+            if ro == 0 and delta == 1:
+                held.append(blocks)
+            elif ro != 0 and delta == -1:
+                held.append(blocks)
         compare(o, h, live, max_blocks)
 
 
