@@ -667,8 +667,10 @@ def summarize_counters(args):
     sw = copy_bytes / (cw * 1024) if cw else None
     out["fetch_scale"], out["write_scale"] = sf, sw
     for name, sym in KERNEL_SYMBOL.items():
-        f, nf = per_kernel("FETCH_SIZE", lambda n, s=sym: s + "(" in n)
-        w, nw = per_kernel("WRITE_SIZE", lambda n, s=sym: s + "(" in n)
+        # the symbol, possibly with template arguments (k_step1<false>(...))
+        hit = lambda n, s=sym: (s + "(") in n or (s + "<") in n
+        f, nf = per_kernel("FETCH_SIZE", hit)
+        w, nw = per_kernel("WRITE_SIZE", hit)
         if not nf:
             continue
         ent = {"fetch_kib": f, "write_kib": w, "dispatches": nf, "src_sha": src_hash(name),
