@@ -69,6 +69,14 @@ Readings taken where the pages leave a step open (each also in the design notes)
       (SWA window, indexer tail, length) is kept every p tokens; a hit restores the
       latest checkpoint c <= len and replays [c, len). Full: the checkpoint at len
       itself. Each yields the State a fork of a live prefix request would have.
+  R18 layer types ([Ch12] Figure 12-1: one State quota per request over all
+      layers, per block every layer's compressed KV). Every layer keeps an SWA
+      window; "csa" layers keep 32 C4 entries + 128 indexer keys per block and
+      attend SWA + top-k C4; "hca" layers keep 1 HCA entry per block and attend SWA
+      + every HCA entry; "swa" layers keep nothing in the Block Cache; "mixed"
+      (the single-layer path) keeps both and attends all three. Layers share the
+      State lengths and the block ids; a multi-layer cache is one oracle per
+      layer, driven by the same calls.
 """
 
 from __future__ import annotations
@@ -399,13 +407,18 @@ class Oracle:
     """The cache, driven call by call like the C ABI."""
 
     def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int,
-                 entry_format: str = "bf16", index_format: str = "f32"):
+                 entry_format: str = "bf16", index_format: str = "f32", layer_type: str = "mixed"):
         if n_win < BLOCK or n_win % BLOCK:
             raise OracleError("invalid", "n_win must be a positive multiple of 128")
         if entry_format not in ("bf16", "fp8"):
             raise OracleError("invalid", "entry format is bf16 or fp8")
         if index_format not in ("f32", "mxfp4"):
             raise OracleError("invalid", "index format is f32 or mxfp4")
+        if layer_type not in ("mixed", "swa", "csa", "hca"):
+            raise OracleError("invalid", "layer type is mixed, swa, csa or hca")
+        self.layer_type = layer_type
+        self.has_c4 = layer_type in ("mixed", "csa")          # reading R18
+        self.has_hca = layer_type in ("mixed", "hca")
         self.entry_format = entry_format
         self.index_format = index_format
         self.n_win = int(n_win)
@@ -511,6 +524,19 @@ class Oracle:
         Kt = np.stack([t[0] for t in st.tail]).astype(np.float64)   # [128][H][D]
         Vt = np.stack([t[1] for t in st.tail]).astype(np.float64)
         blk = _Block()
+        for name in _Block.__slots__:
+            setattr(blk, name, None)
+        self.store[b] = blk
+        self.refcount[b] = 1
+        st.blocks.append(b)
+        if self.has_c4:
+            self._seal_c4(blk, st, Kt, Vt)
+        if self.has_hca:
+            blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)     # all 128 tokens
+        st.tail = []                                  # tail cleared ([Q&A] §3.1)
+
+    def _seal_c4(self, blk: _Block, st: _State, Kt, Vt):
+        """The 32 C4 entries and 128 indexer keys of the block being sealed."""
         fp8 = self.entry_format == "fp8"
         blk.csa_k = np.empty((C4_PER_BLOCK, N_HEADS, HEAD_DIM), np.float64 if fp8 else np.float32)
         blk.csa_v = np.empty_like(blk.csa_k)
@@ -527,7 +553,6 @@ class Oracle:
                 blk.csa_v_codes[j], blk.csa_v_scale[j], blk.csa_v[j] = quantize_e4m3_rows(Vj)
             else:
                 blk.csa_k[j], blk.csa_v[j] = gated_pool(Kt[g], Vt[g], self.W_csa)
-        blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)     # all 128 tokens
         keys = np.stack([t[2] for t in st.tail]).astype(np.float32)       # [128][4][64]
         if self.index_format == "mxfp4":              # reading R16
             codes, scales, vals = quantize_mxfp4_rows(keys.reshape(BLOCK, -1))
@@ -535,10 +560,6 @@ class Oracle:
             blk.idx_codes, blk.idx_scales = codes, scales
         else:
             blk.idx = keys
-        self.store[b] = blk
-        self.refcount[b] = 1
-        st.blocks.append(b)
-        st.tail = []                                  # tail cleared ([Q&A] §3.1)
 
     # -- prefix sharing --------------------------------------------------------
     def share(self, src: int, dst: int):
@@ -659,6 +680,8 @@ class Oracle:
     def scores(self, s: int, q_idx) -> np.ndarray:
         """Scores of the request's sealed C4 entries, ordinal j = 32 * block + slot."""
         st = self._get(s)
+        if not self.has_c4:
+            return np.zeros(0)
         out = [c4_scores(self.store[b].idx, q_idx) for b in st.blocks]
         return np.concatenate(out) if out else np.zeros(0)
 
@@ -677,10 +700,10 @@ class Oracle:
         self._filled(st)
         K = [t[0] for t in st.swa]
         V = [t[1] for t in st.swa]
-        for b in st.blocks:
+        for b in st.blocks if self.has_hca else []:
             K.append(self.store[b].hca_k)
             V.append(self.store[b].hca_v)
-        nc = C4_PER_BLOCK * len(st.blocks)
+        nc = C4_PER_BLOCK * len(st.blocks) if self.has_c4 else 0
         sel = np.asarray(sel if sel is not None else [], dtype=np.int64).reshape(-1)
         kk = min(len(sel) if k is None else int(k), nc)
         for j in sel[:kk]:

@@ -794,3 +794,47 @@ def test_prefix_attach_errors_and_unfilled_state():
     assert all(o.refcount[b] == 1 for b in blocks) and len(o.free_blocks) == 14
     o.block_ref(blocks, -1)
     assert len(o.free_blocks) == 16 and all(b not in o.store for b in blocks)
+
+
+# ---------------------------------------------------------------- layer types (R18)
+
+def test_layer_types_attend_their_parts_of_the_block():
+    """One call sequence into a mixed, an SWA, a CSA and an HCA layer (same gates,
+    same tokens): block ids match across types; the CSA layer's C4 entries and keys
+    and the HCA layer's HCA entries equal the mixed layer's; the SWA layer's output
+    is plain attention over the window; the CSA and HCA outputs equal brute force
+    over SWA + the selected C4 / SWA + every HCA; layers without C4 select nothing."""
+    Wc, Wh = synth.gate_weights(SEED)
+    orc = {t: Oracle(128, Wc, Wh, 4, 16, layer_type=t) for t in ("mixed", "swa", "csa", "hca")}
+    K, V, KI = toks(6, 0, 700)
+    for o in orc.values():
+        assert o.state_alloc() == 0
+        o.append([0], [(K[:650], V[:650], KI[:650])])
+        o.append([0], [(K[650:], V[650:], KI[650:])])
+    tables = {t: o.table(0) for t, o in orc.items()}
+    assert all(tb == tables["mixed"] for tb in tables.values()) and len(tables["mixed"]) == 5
+    m, c, h = orc["mixed"], orc["csa"], orc["hca"]
+    for b in tables["mixed"]:
+        assert np.array_equal(m.block(b).csa_k, c.block(b).csa_k) and np.array_equal(m.block(b).idx, c.block(b).idx)
+        assert np.array_equal(m.block(b).hca_v, h.block(b).hca_v)
+        assert c.block(b).hca_k is None and h.block(b).csa_k is None and orc["swa"].block(b).csa_k is None
+    q = synth.bf16_bits_to_f32(synth.tokens_bf16(SEED, synth.STREAM_Q, 6, np.array([699])))[0].astype(np.float64)
+    qi = synth.tokens_f32(SEED, synth.STREAM_QI, 6, np.array([699]))[0].astype(np.float64)
+    kk = 40
+    sel, _ = m.topk(0, qi, kk)
+    assert np.array_equal(c.topk(0, qi, kk)[0], sel)
+    for t in ("swa", "hca"):
+        assert np.all(orc[t].topk(0, qi, kk)[0] == -1)
+    Kw, Vw = K[700 - 128:], V[700 - 128:]
+    assert np.allclose(orc["swa"].attend(0, q, [], kk), attention(q, Kw, Vw), atol=1e-13)
+    blocks = [m.block(b) for b in tables["mixed"]]
+    Kc = np.stack([blocks[j // 32].csa_k[j % 32] for j in sel])
+    Vc = np.stack([blocks[j // 32].csa_v[j % 32] for j in sel])
+    assert np.allclose(c.attend(0, q, sel, kk), attention(q, np.concatenate([Kw, Kc]), np.concatenate([Vw, Vc])),
+                       atol=1e-13)
+    Kh = np.stack([x.hca_k for x in blocks])
+    Vh = np.stack([x.hca_v for x in blocks])
+    assert np.allclose(h.attend(0, q, sel, kk), attention(q, np.concatenate([Kw, Kh]), np.concatenate([Vw, Vh])),
+                       atol=1e-13)
+    assert np.allclose(m.attend(0, q, sel, kk),
+                       attention(q, np.concatenate([Kw, Kh, Kc]), np.concatenate([Vw, Vh, Vc])), atol=1e-13)
