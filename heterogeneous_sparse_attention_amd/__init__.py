@@ -45,10 +45,12 @@ class _Config(ctypes.Structure):
                 ("max_blocks", ctypes.c_int64), ("max_blocks_per_state", ctypes.c_int64),
                 ("gate_csa", ctypes.POINTER(ctypes.c_float)),
                 ("gate_hca", ctypes.POINTER(ctypes.c_float)),
-                ("entry_format", ctypes.c_int32), ("index_format", ctypes.c_int32)]
+                ("entry_format", ctypes.c_int32), ("index_format", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("layer_types", ctypes.c_void_p)]
 
 ENTRY_FORMATS = {"bf16": 0, "fp8": 1}     # HSA_ENTRY_BF16, HSA_ENTRY_FP8
 INDEX_FORMATS = {"f32": 0, "mxfp4": 1}    # HSA_INDEX_F32, HSA_INDEX_MXFP4
+LAYER_TYPES = {"mixed": 0, "swa": 1, "csa": 2, "hca": 3}   # HSA_LAYER_*
 
 
 class _StateInfo(ctypes.Structure):
@@ -85,6 +87,7 @@ SIGNATURES = {
     "hsa_fp8_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_export_idx_mxfp4": [_P, _I32, _P, _P, _P],
     "hsa_block_ref": [_P, _P, _I64, _I32],
+    "hsa_set_layer": [_P, _I32],
     "hsa_prefix_attach": [_P, _I32, _P, _P, _P, _I64, _P, _P],
     "hsa_state_write": [_P, _I32, _P, _P, _P, _P, _P, _P, _P],
     "hsa_checkpoint_bytes": [_P, _P],
@@ -164,18 +167,28 @@ class Cache:
 
     def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
                  max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16",
-                 index_format: str = "f32"):
+                 index_format: str = "f32", layer_types=None):
+        """layer_types: None (one heterogeneous layer) or a list of "mixed", "swa",
+        "csa", "hca"; then gate_csa / gate_hca hold one [16][128] set per layer."""
         lib = load()
         if entry_format not in ENTRY_FORMATS:
             raise ValueError(f"entry_format must be one of {sorted(ENTRY_FORMATS)}")
         if index_format not in INDEX_FORMATS:
             raise ValueError(f"index_format must be one of {sorted(INDEX_FORMATS)}")
-        self._gc = np.ascontiguousarray(np.asarray(gate_csa, np.float32).reshape(H * D))
-        self._gh = np.ascontiguousarray(np.asarray(gate_hca, np.float32).reshape(H * D))
+        types = ["mixed"] if layer_types is None else list(layer_types)
+        if not types or any(t not in LAYER_TYPES for t in types):
+            raise ValueError(f"layer_types must be a non-empty list of {sorted(LAYER_TYPES)}")
+        nl = len(types)
+        self._gc = np.ascontiguousarray(np.asarray(gate_csa, np.float32).reshape(nl * H * D))
+        self._gh = np.ascontiguousarray(np.asarray(gate_hca, np.float32).reshape(nl * H * D))
+        self._lt = np.ascontiguousarray(np.array([LAYER_TYPES[t] for t in types], np.int32))
+        self.layer_types = types
+        self.layer = 0
         cfg = _Config(H, D, 4, 128, n_win, HI, DI, max_states, max_blocks, max_blocks_per_state,
                       self._gc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
-                      ENTRY_FORMATS[entry_format], INDEX_FORMATS[index_format])
+                      ENTRY_FORMATS[entry_format], INDEX_FORMATS[index_format], nl,
+                      self._lt.ctypes.data_as(ctypes.c_void_p))
         self.entry_format = entry_format
         self.index_format = index_format
         ctx = ctypes.c_void_p()
@@ -234,6 +247,12 @@ class Cache:
     def block_table_share(self, src: int, dst: int, stream=None):
         _check(_lib.hsa_block_table_share(self._ctx, int(src), int(dst), _stream(stream)),
                "hsa_block_table_share")
+
+    # -- layers ------------------------------------------------------------------------
+    def set_layer(self, layer: int):
+        """Data calls act on this layer from now on (appends go 0, 1, ..., n-1)."""
+        _check(_lib.hsa_set_layer(self._ctx, int(layer)), "hsa_set_layer")
+        self.layer = int(layer)
 
     # -- prefix hits (Zero / Periodic / Full SWA policies) ----------------------------
     def block_ref(self, blocks, delta: int):
@@ -376,17 +395,22 @@ class Cache:
         per-head scales (csa_k_scale, csa_v_scale float32 [32][16]). With MXFP4 indexer
         keys they come as idx_codes uint8 [128][128] and idx_scales uint8 [128][8]
         (E8M0 bytes) instead of idx."""
-        fp8 = self.entry_format == "fp8"
-        mx4 = self.index_format == "mxfp4"
-        out = {"hca_k": np.zeros((H, D), np.uint16), "hca_v": np.zeros((H, D), np.uint16)}
-        if not mx4:
+        t = self.layer_types[self.layer]        # what the current layer keeps
+        c4, hca = t in ("mixed", "csa"), t in ("mixed", "hca")
+        fp8 = self.entry_format == "fp8" and c4
+        mx4 = self.index_format == "mxfp4" and c4
+        out = {}
+        if hca:
+            out["hca_k"] = np.zeros((H, D), np.uint16)
+            out["hca_v"] = np.zeros((H, D), np.uint16)
+        if c4 and not mx4:
             out["idx"] = np.zeros((128, HI, DI), np.float32)
-        if not fp8:
+        if c4 and not fp8:
             out["csa_k"] = np.zeros((32, H, D), np.uint16)
             out["csa_v"] = np.zeros((32, H, D), np.uint16)
         p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
-        _check(_lib.hsa_export_block(self._ctx, int(b), p.get("csa_k"), p.get("csa_v"), p["hca_k"],
-                                     p["hca_v"], p.get("idx"), _stream(stream)), "hsa_export_block")
+        _check(_lib.hsa_export_block(self._ctx, int(b), p.get("csa_k"), p.get("csa_v"), p.get("hca_k"),
+                                     p.get("hca_v"), p.get("idx"), _stream(stream)), "hsa_export_block")
         if fp8:
             q = {"csa_k_codes": np.zeros((32, H, D), np.uint8), "csa_v_codes": np.zeros((32, H, D), np.uint8),
                  "csa_k_scale": np.zeros((32, H), np.float32), "csa_v_scale": np.zeros((32, H), np.float32)}
@@ -405,11 +429,13 @@ class Cache:
         return out
 
     def export_state(self, s: int, stream=None) -> dict:
+        """The current layer's SWA ring and (layers with C4 entries) indexer tail."""
         out = {"swa_k": np.zeros((self.n_win, H, D), np.uint16),
-               "swa_v": np.zeros((self.n_win, H, D), np.uint16),
-               "idx_tail": np.zeros((128, HI, DI), np.float32)}
+               "swa_v": np.zeros((self.n_win, H, D), np.uint16)}
+        if self.layer_types[self.layer] in ("mixed", "csa"):
+            out["idx_tail"] = np.zeros((128, HI, DI), np.float32)
         p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
-        _check(_lib.hsa_export_state(self._ctx, int(s), p["swa_k"], p["swa_v"], p["idx_tail"],
+        _check(_lib.hsa_export_state(self._ctx, int(s), p["swa_k"], p["swa_v"], p.get("idx_tail"),
                                      _stream(stream)), "hsa_export_state")
         return out
 

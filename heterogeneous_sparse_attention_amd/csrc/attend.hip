@@ -1,9 +1,9 @@
 // attend.hip - heterogeneous decode attention over the two pools (hsa_decode_attend).
 //
 // Keys of request i, in this order: the min(L, n_win) SWA tokens (oldest first),
-// the HCA entry of each of its nb sealed blocks, then the C4 entries named in the
-// first min(k, 32 nb) slots of its top-k row (-1 and out-of-range ordinals are
-// skipped). One softmax over all of them per head, scale 1/sqrt(128). The
+// the HCA entry of each of its nb sealed blocks (layers with HCA entries), then the
+// C4 entries named in the first min(k, 32 nb) slots of its top-k row (layers with
+// C4 entries; -1 and out-of-range ordinals are skipped). One softmax over all of them per head, scale 1/sqrt(128). The
 // streaming core and its page citations are in attn_dev.h.
 #include "attn_dev.h"
 #include "device.h"
@@ -15,8 +15,8 @@ namespace {
 
 __device__ __forceinline__ int n_keys(const Pools& P, const Req& R, int32_t k) {
   const int swa = R.len < P.n_win ? R.len : P.n_win;
-  const int nc = kC4 * R.nb;
-  return swa + R.nb + (k < nc ? k : nc);
+  const int nc = P.c4 ? kC4 * R.nb : 0;
+  return swa + (P.hca ? R.nb : 0) + (k < nc ? k : nc);
 }
 
 // K and V rows of key x of request R (nullptrs for a skipped top-k slot).
@@ -33,16 +33,17 @@ __device__ __forceinline__ KeyAddr key_addr(const Pools& P, const Req& R, int x,
   }
   x -= swa;
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
-  if (x < R.nb) {
+  const int nh = P.hca ? R.nb : 0;
+  if (x < nh) {
     const int32_t id = tab[x];
     if (id < 0 || id >= P.max_blocks) return a;   // never taken: tables are written before use
     a.k = P.hca_k + (int64_t)id * kRow;
     a.v = P.hca_v + (int64_t)id * kRow;
     return a;
   }
-  x -= R.nb;
+  x -= nh;
   const int32_t j = sel[x];
-  if (j < 0 || j >= kC4 * R.nb) return a;
+  if (j < 0 || j >= (P.c4 ? kC4 * R.nb : 0)) return a;
   const int32_t id = tab[j / kC4];
   if (id < 0 || id >= P.max_blocks) return a;
   const C4Addr c = c4_addr(P, (int64_t)id * kC4 + j % kC4);
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attend(Pools P, ReqBatch B,
   float M, L, A8[8];
   attend_keys([&](int x) { return key_addr(P, R, x, sel); }, w * chunk, min(nk, (w + 1) * chunk),
               q + (int64_t)r * kRow, dk, dv, sh, M, L, A8,
-              P.fp8 ? (R.len < P.n_win ? R.len : P.n_win) + R.nb : 0x7fffffff);
+              P.fp8 ? (R.len < P.n_win ? R.len : P.n_win) + (P.hca ? R.nb : 0) : 0x7fffffff);
   if (nch == 1)
     store_output(out + (int64_t)r * kRow, L, A8);
   else

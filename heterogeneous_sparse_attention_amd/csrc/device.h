@@ -75,6 +75,8 @@ struct Pools {
   int32_t max_blocks;   // physical ids are in [0, max_blocks)
   int32_t fp8;          // 1: C4 entries are stored as FP8 (c4q, c4s); 0: bf16 (csa_k, csa_v)
   int32_t mx4;          // 1: sealed indexer keys are MXFP4 (idx_q, idx_e); 0: fp32 (idx_k)
+  int32_t c4;           // layer type: 1 if the layer keeps C4 entries, indexer keys and tail
+  int32_t hca;          // layer type: 1 if the layer keeps HCA entries
 };
 
 // One request of a launch: its state, its length and sealed-block count after the

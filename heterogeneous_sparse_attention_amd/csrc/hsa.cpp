@@ -71,6 +71,19 @@ struct hsa_ctx {
   int32_t select_slice = 0;   // top-k: longer score rows are selected in two rounds (0: by k)
   int32_t step_fused = 1;     // decode step in three launches when every row fits the LDS cache
   int32_t mx_unit = 0;        // MXFP4 keys: blocks per scoring workgroup (0: by batch size)
+  // layers: the pools of each (P is the current layer's); an append made at layer 0
+  // and not yet repeated on every layer is kept in `seq` for the later layers
+  std::vector<Pools> layers;
+  int32_t cur_layer = 0;
+  struct Seq {
+    int kind = 0;                 // 1 append, 2 flush, 3 decode step
+    std::vector<int32_t> states;
+    std::vector<int64_t> cu;
+    uint32_t flags = 0;
+    AppendPlan plan;
+    int32_t next = 0;             // the layer whose turn it is
+  } seq;
+  bool seq_open = false;
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
   int32_t* cand_ord = nullptr;  // top-k of sliced rows: per-slice candidates (ordinals, scores)
@@ -189,8 +202,9 @@ int run_bulk(hsa_ctx* c, const AppendPlan& plan, const void* k, const void* v, c
              hipStream_t st) {
   std::vector<SealDesc> seals;
   seals.reserve(plan.seals.size());
-  for (const SealItem& s : plan.seals)
-    seals.push_back(SealDesc{s.state, s.id, s.lblock * kBlk, s.len_old, s.row0});
+  if (c->P.c4 || c->P.hca)   // an SWA layer keeps nothing in the Block Cache
+    for (const SealItem& s : plan.seals)
+      seals.push_back(SealDesc{s.state, s.id, s.lblock * kBlk, s.len_old, s.row0});
   std::vector<WriteDesc> writes;
   int64_t total = 0;
   for (const AppendReq& r : plan.reqs) {
@@ -231,7 +245,7 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
     for (int i = 0; i < B.n; ++i) {
       const AppendReq& r = plan.reqs[b0 + i];
       B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, new_id[b0 + i]};
-      if (new_id[b0 + i] >= 0) B.seal_req[B.n_seal++] = (int8_t)i;
+      if (new_id[b0 + i] >= 0 && (c->P.c4 || c->P.hca)) B.seal_req[B.n_seal++] = (int8_t)i;
     }
     {
       Timed t(c, HSA_KERNEL_APPEND, st);
@@ -239,7 +253,7 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
                                    static_cast<const uint16_t*>(v) + b0 * kRow, ik + b0 * kIRow,
                                    c->seal_part, st, t.ev()));
     }
-    if (B.n_seal) {
+    if (B.n_seal && c->P.hca) {
       Timed t(c, HSA_KERNEL_SEAL, st);
       HIP_TRY(launch_seal_merge(c->P, B, c->seal_part, st, t.ev()));
     }
@@ -283,6 +297,8 @@ int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_id
   for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
     const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
     ReqBatch B = read_batch(c, states, b0, n);
+    if (!c->P.c4)   // no C4 entries in this layer: every row is padding
+      for (int i = 0; i < n; ++i) B.r[i].nb = 0;
     int64_t total = 0, maxnb = 0;
     for (int i = 0; i < n; ++i) {
       total += B.r[i].nb;
@@ -326,7 +342,7 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
     int64_t keys = 0;
     for (int i = 0; i < n; ++i) {
       const int64_t swa = std::min<int64_t>(B.r[i].len, c->P.n_win);
-      nk[i] = swa + B.r[i].nb + std::min<int64_t>(k, (int64_t)kC4 * B.r[i].nb);
+      nk[i] = swa + (c->P.hca ? B.r[i].nb : 0) + (c->P.c4 ? std::min<int64_t>(k, (int64_t)kC4 * B.r[i].nb) : 0);
       keys += nk[i];
     }
     const int32_t chunk = attend_chunk(keys, n, c->attend_wgs);
@@ -369,9 +385,12 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     // three launches when every score row fits the selection's LDS cache (and the
     // top-k is wanted in ordinal order): every attention workgroup then selects for
     // itself and the new HCA key joins the merge
-    bool fused = c->step_fused != 0 && !(flags & HSA_TOPK_SORTED);
+    // (a layer without C4 entries has empty rows: always three launches, its top-k
+    // rows all padding)
+    const bool c4 = c->P.c4 != 0, hca = c->P.hca != 0;
+    bool fused = !c4 || (c->step_fused != 0 && !(flags & HSA_TOPK_SORTED));
     for (int i = 0; i < n; ++i)
-      fused = fused && (int64_t)kC4 * plan.reqs[b0 + i].nb_new <= kCacheN;
+      fused = fused && (!c4 || (int64_t)kC4 * plan.reqs[b0 + i].nb_new <= kCacheN);
     std::vector<int64_t> na(n), nb(n);
     int64_t maxnb = 0, n_score = 0, all_nb = 0;
     for (int i = 0; i < n; ++i) all_nb += plan.reqs[b0 + i].nb_new;
@@ -386,12 +405,12 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       const AppendReq& r = plan.reqs[b0 + i];
       const int32_t id = new_id[b0 + i];
       B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, id};
-      if (id >= 0) B.seal_req[B.n_seal++] = (int8_t)i;
+      if (id >= 0 && (c4 || hca)) B.seal_req[B.n_seal++] = (int8_t)i;   // an SWA layer seals nothing
       const int64_t sealed = id >= 0 ? 1 : 0;
-      na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + r.nb_new - sealed;
-      nb[i] = (fused ? 0 : sealed) + std::min<int64_t>(k, (int64_t)kC4 * r.nb_new);
+      na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + (hca ? r.nb_new - sealed : 0);
+      nb[i] = (fused || !hca ? 0 : sealed) + (c4 ? std::min<int64_t>(k, (int64_t)kC4 * r.nb_new) : 0);
       maxnb = std::max<int64_t>(maxnb, r.nb_new);
-      n_score += score_units(r.nb_new, mx_unit);
+      if (c4) n_score += score_units(r.nb_new, mx_unit);
     }
     StepArgs S{};
     S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
@@ -433,7 +452,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       S.first_s[i] = (int32_t)ts;
       ta += pa.wgs[i];
       tb += pb.wgs[i];
-      ts += score_units(B.r[i].nb, mx_unit);
+      ts += c4 ? score_units(B.r[i].nb, mx_unit) : 0;
     }
     S.first_a[n] = (int32_t)ta;
     S.first_b[n] = (int32_t)tb;
@@ -482,6 +501,61 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
   return kOk;
 }
 
+// ---- layers: an append made at layer 0 is repeated at layers 1 .. n-1 ----
+
+enum SeqKind { kSeqAppend = 1, kSeqFlush = 2, kSeqStep = 3 };
+
+// Gate of an appending call at the current layer. Layer 0 (or a one-layer context)
+// plans and commits it (*replay = false). A later layer must repeat, in layer order,
+// the call made at layer 0 (same kind, states, token counts and flags), whose
+// committed plan it runs on its own pools (*replay = true).
+int layer_gate(hsa_ctx* c, int kind, int32_t n_req, const int32_t* states, const int64_t* cu,
+               uint32_t flags, bool* replay) {
+  *replay = false;
+  if (c->layers.size() <= 1) return kOk;
+  if (c->cur_layer == 0) {
+    if (c->seq_open)
+      return fail(kState, "layer " + std::to_string(c->seq.next) + " of the previous append is pending");
+    return kOk;
+  }
+  if (!c->seq_open || c->seq.next != c->cur_layer)
+    return fail(kState, "an append is made at layer 0, then at each later layer in order");
+  const hsa_ctx::Seq& q = c->seq;
+  bool same = q.kind == kind && n_req >= 0 && (size_t)n_req == q.states.size() && q.flags == flags &&
+              (n_req == 0 || states);
+  for (int32_t i = 0; same && i < n_req; ++i) same = states[i] == q.states[i];
+  if (same && kind == kSeqAppend) {
+    same = cu != nullptr || n_req == 0;
+    for (int32_t i = 0; same && i <= n_req && n_req > 0; ++i) same = cu[i] == q.cu[i];
+  }
+  if (!same) return fail(kInvalid, "the call differs from the one made at layer 0");
+  *replay = true;
+  return kOk;
+}
+
+void layer_record(hsa_ctx* c, int kind, int32_t n_req, const int32_t* states, const int64_t* cu,
+                  uint32_t flags, const AppendPlan& plan) {
+  if (c->layers.size() <= 1) return;
+  hsa_ctx::Seq& q = c->seq;
+  q.kind = kind;
+  q.states.assign(states, states + std::max(n_req, 0));
+  q.cu.assign(cu && n_req > 0 ? cu : nullptr, cu && n_req > 0 ? cu + n_req + 1 : nullptr);
+  q.flags = flags;
+  q.plan = plan;
+  q.next = 1;
+  c->seq_open = true;
+}
+
+void layer_advance(hsa_ctx* c) {
+  if (++c->seq.next >= (int32_t)c->layers.size()) c->seq_open = false;
+}
+
+// Calls that change states or blocks wait until every layer has taken the last append.
+int no_open_seq(hsa_ctx* c) {
+  return c->seq_open ? fail(kState, "layer " + std::to_string(c->seq.next) + " of the last append is pending")
+                     : kOk;
+}
+
 int check_config(const hsa_config* cfg) {
   if (!cfg) return fail(kInvalid, "config is NULL");
   if (cfg->n_heads != kH || cfg->head_dim != kD)
@@ -499,6 +573,11 @@ int check_config(const hsa_config* cfg) {
     return fail(kInvalid, "entry_format must be HSA_ENTRY_BF16 or HSA_ENTRY_FP8");
   if (cfg->index_format != HSA_INDEX_F32 && cfg->index_format != HSA_INDEX_MXFP4)
     return fail(kInvalid, "index_format must be HSA_INDEX_F32 or HSA_INDEX_MXFP4");
+  if (cfg->n_layers < 0 || cfg->n_layers > 1024) return fail(kInvalid, "n_layers must be in [0, 1024]");
+  if (cfg->layer_types)
+    for (int l = 0; l < std::max(1, cfg->n_layers); ++l)
+      if (cfg->layer_types[l] < HSA_LAYER_MIXED || cfg->layer_types[l] > HSA_LAYER_HCA)
+        return fail(kInvalid, "layer_types must be HSA_LAYER_MIXED, _SWA, _CSA or _HCA");
   return kOk;
 }
 
@@ -526,47 +605,70 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   const size_t S = (size_t)cfg->max_states, NB = (size_t)cfg->max_blocks, W = (size_t)cfg->n_win;
   const bool fp8 = cfg->entry_format == HSA_ENTRY_FP8;
   const bool mx4 = cfg->index_format == HSA_INDEX_MXFP4;
-  constexpr int kPools = 15;
-  void* p[kPools] = {};
-  const size_t bytes[kPools] = {
-      S * W * kRow * 2, S * W * kRow * 2, S * kBlk * kIRow * 4,            // swa_k, swa_v, idx_tail
-      fp8 ? 0 : NB * kC4 * kRow * 2, fp8 ? 0 : NB * kC4 * kRow * 2,       // csa (bf16 entries)
-      NB * kRow * 2, NB * kRow * 2,                                       // hca
-      mx4 ? 0 : NB * kBlk * kIRow * 4,                                    // idx_k (fp32 keys)
-      S * (size_t)bps * 4,                                                // table
-      2 * kRow * 4,                                                       // gates
-      (size_t)kMaxReq * kSealSplit * kPartFloats * 4,                     // seal partials
-      fp8 ? NB * kC4 * kC4Bytes : 0, fp8 ? NB * kC4 * kC4Scales * 4 : 0,   // FP8 C4 codes, scales
-      mx4 ? NB * kBlk * kIRowQ : 0, mx4 ? NB * kBlk * kIRowE : 0};       // MXFP4 key codes, scales
-  for (int i = 0; i < kPools; ++i) {
-    st = dev_alloc(c, &p[i], bytes[i]);
+  const int n_layers = cfg->n_layers > 0 ? cfg->n_layers : 1;
+  // shared by the layers: block tables, seal partials, every layer's gates
+  void* sh[3] = {};
+  const size_t sh_bytes[3] = {S * (size_t)bps * 4, (size_t)kMaxReq * kSealSplit * kPartFloats * 4,
+                              (size_t)n_layers * 2 * kRow * 4};
+  for (int i = 0; i < 3; ++i) {
+    st = dev_alloc(c, &sh[i], sh_bytes[i]);
     if (st) {
       hsa_destroy(c);
       return st;
     }
   }
-  c->P.swa_k = static_cast<uint16_t*>(p[0]);
-  c->P.swa_v = static_cast<uint16_t*>(p[1]);
-  c->P.idx_tail = static_cast<float*>(p[2]);
-  c->P.csa_k = static_cast<uint16_t*>(p[3]);
-  c->P.csa_v = static_cast<uint16_t*>(p[4]);
-  c->P.hca_k = static_cast<uint16_t*>(p[5]);
-  c->P.hca_v = static_cast<uint16_t*>(p[6]);
-  c->P.idx_k = static_cast<float*>(p[7]);
-  c->P.table = static_cast<int32_t*>(p[8]);
-  c->P.table_stride = bps;
-  float* gates = static_cast<float*>(p[9]);
-  c->P.gate_csa = gates;
-  c->P.gate_hca = gates + kRow;
-  c->P.n_win = cfg->n_win;
-  c->P.max_blocks = (int32_t)cfg->max_blocks;
-  c->seal_part = static_cast<float*>(p[10]);
-  c->P.c4q = static_cast<uint8_t*>(p[11]);
-  c->P.c4s = static_cast<float*>(p[12]);
-  c->P.fp8 = fp8 ? 1 : 0;
-  c->P.idx_q = static_cast<uint8_t*>(p[13]);
-  c->P.idx_e = static_cast<uint8_t*>(p[14]);
-  c->P.mx4 = mx4 ? 1 : 0;
+  int32_t* table = static_cast<int32_t*>(sh[0]);
+  c->seal_part = static_cast<float*>(sh[1]);
+  float* gates = static_cast<float*>(sh[2]);
+  c->layers.resize(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    const int type = cfg->layer_types ? cfg->layer_types[l] : HSA_LAYER_MIXED;
+    const bool c4 = type == HSA_LAYER_MIXED || type == HSA_LAYER_CSA;
+    const bool hca = type == HSA_LAYER_MIXED || type == HSA_LAYER_HCA;
+    // per layer, by type: the SWA ring always; C4 entries, indexer keys and the
+    // indexer tail for C4 layers; HCA entries for HCA layers
+    constexpr int kPools = 12;
+    void* p[kPools] = {};
+    const size_t bytes[kPools] = {
+        S * W * kRow * 2, S * W * kRow * 2,                                     // swa_k, swa_v
+        c4 ? S * kBlk * kIRow * 4 : 0,                                          // idx_tail
+        c4 && !fp8 ? NB * kC4 * kRow * 2 : 0, c4 && !fp8 ? NB * kC4 * kRow * 2 : 0,   // csa (bf16)
+        hca ? NB * kRow * 2 : 0, hca ? NB * kRow * 2 : 0,                       // hca
+        c4 && !mx4 ? NB * kBlk * kIRow * 4 : 0,                                 // idx_k (fp32 keys)
+        c4 && fp8 ? NB * kC4 * kC4Bytes : 0, c4 && fp8 ? NB * kC4 * kC4Scales * 4 : 0,   // FP8 C4
+        c4 && mx4 ? NB * kBlk * kIRowQ : 0, c4 && mx4 ? NB * kBlk * kIRowE : 0};       // MXFP4 keys
+    for (int i = 0; i < kPools; ++i) {
+      st = dev_alloc(c, &p[i], bytes[i]);
+      if (st) {
+        hsa_destroy(c);
+        return st;
+      }
+    }
+    Pools& P = c->layers[l];
+    P.swa_k = static_cast<uint16_t*>(p[0]);
+    P.swa_v = static_cast<uint16_t*>(p[1]);
+    P.idx_tail = static_cast<float*>(p[2]);
+    P.csa_k = static_cast<uint16_t*>(p[3]);
+    P.csa_v = static_cast<uint16_t*>(p[4]);
+    P.hca_k = static_cast<uint16_t*>(p[5]);
+    P.hca_v = static_cast<uint16_t*>(p[6]);
+    P.idx_k = static_cast<float*>(p[7]);
+    P.c4q = static_cast<uint8_t*>(p[8]);
+    P.c4s = static_cast<float*>(p[9]);
+    P.idx_q = static_cast<uint8_t*>(p[10]);
+    P.idx_e = static_cast<uint8_t*>(p[11]);
+    P.table = table;
+    P.table_stride = bps;
+    P.gate_csa = gates + (size_t)l * 2 * kRow;
+    P.gate_hca = gates + (size_t)l * 2 * kRow + kRow;
+    P.n_win = cfg->n_win;
+    P.max_blocks = (int32_t)cfg->max_blocks;
+    P.fp8 = fp8 ? 1 : 0;
+    P.mx4 = mx4 ? 1 : 0;
+    P.c4 = c4 ? 1 : 0;
+    P.hca = hca ? 1 : 0;
+  }
+  c->P = c->layers[0];
   // attention partials: a decode step has at most max(slots, requests) workgroups per
   // part, and hsa_decode_attend at most max(64, target - n) + n <= target + 64, so
   // these never grow (no device synchronisation in a decode loop)
@@ -581,9 +683,14 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
       return st;
     }
   }
-  hipError_t e = hipMemcpy(gates, cfg->gate_csa, kRow * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(gates + kRow, cfg->gate_hca, kRow * 4, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(c->P.table, 0xff, bytes[8]);
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+    e = hipMemcpy(gates + (size_t)l * 2 * kRow, cfg->gate_csa + (size_t)l * kRow, kRow * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(gates + (size_t)l * 2 * kRow + kRow, cfg->gate_hca + (size_t)l * kRow, kRow * 4,
+                    hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess) e = hipMemset(table, 0xff, sh_bytes[0]);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -618,7 +725,9 @@ hsa_status hsa_state_alloc(hsa_ctx* c, int32_t* out) {
 
 hsa_status hsa_state_free(hsa_ctx* c, int32_t s) {
   if (!c) return fail(kInvalid, "NULL context");
-  int st = c->ctl.state_free(s);
+  int st = no_open_seq(c);
+  if (st) return st;
+  st = c->ctl.state_free(s);
   return st ? fail(st, "state " + std::to_string(s) + " is not allocated") : kOk;
 }
 
@@ -627,36 +736,59 @@ hsa_status hsa_append_kv(hsa_ctx* c, int32_t n_req, const int32_t* states, const
                          void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   if (flags & ~HSA_APPEND_DEFER_SEAL) return fail(kInvalid, "unknown flags");
+  bool replay = false;
+  int st = layer_gate(c, kSeqAppend, n_req, states, cu, flags, &replay);
+  if (st) return st;
   std::string why;
-  AppendPlan plan;
-  int st = c->ctl.plan_append(n_req, states, cu, (flags & HSA_APPEND_DEFER_SEAL) != 0, &plan, &why);
-  if (st) return fail(st, why);
+  AppendPlan fresh;
+  if (!replay) {
+    st = c->ctl.plan_append(n_req, states, cu, (flags & HSA_APPEND_DEFER_SEAL) != 0, &fresh, &why);
+    if (st) return fail(st, why);
+  }
+  const AppendPlan& plan = replay ? c->seq.plan : fresh;
   const int64_t T = n_req > 0 ? cu[n_req] : 0;
-  if (T > 0 && (!k || !v || !idx_k)) return fail(kInvalid, "input pointer is NULL");
+  if (T > 0 && (!k || !v || (!idx_k && c->P.c4))) return fail(kInvalid, "input pointer is NULL");
   if ((st = set_device(c))) return st;
   bool one_each = n_req > 0;
   for (const AppendReq& r : plan.reqs) one_each = one_each && (r.len_new - r.len_old == 1);
-  c->ctl.commit(&plan);
+  if (replay) {
+    layer_advance(c);
+  } else {
+    c->ctl.commit(&fresh);
+    layer_record(c, kSeqAppend, n_req, states, cu, flags, fresh);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return one_each ? run_decode_append(c, plan, k, v, idx_k, s) : run_bulk(c, plan, k, v, idx_k, s);
 }
 
 hsa_status hsa_compress_flush(hsa_ctx* c, int32_t n_req, const int32_t* states, void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
+  bool replay = false;
+  int st = layer_gate(c, kSeqFlush, n_req, states, nullptr, 0, &replay);
+  if (st) return st;
+  if (replay) {
+    layer_advance(c);
+    if (c->seq.plan.new_blocks == 0) return kOk;
+    if ((st = set_device(c))) return st;
+    return run_bulk(c, c->seq.plan, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream));
+  }
   std::string why;
   AppendPlan plan;
-  int st = c->ctl.plan_flush(n_req, states, &plan, &why);
+  st = c->ctl.plan_flush(n_req, states, &plan, &why);
   if (st) return fail(st, why);
-  if (plan.new_blocks == 0) return kOk;
   if ((st = set_device(c))) return st;
   c->ctl.commit(&plan);
+  layer_record(c, kSeqFlush, n_req, states, nullptr, 0, plan);
+  if (plan.new_blocks == 0) return kOk;
   return run_bulk(c, plan, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
 hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   std::string why;
-  int st = c->ctl.check_share(src, dst, &why);
+  int st = no_open_seq(c);
+  if (st) return st;
+  st = c->ctl.check_share(src, dst, &why);
   if (st) return fail(st, why);
   if ((st = set_device(c))) return st;
   c->ctl.commit_share(src, dst);
@@ -666,19 +798,19 @@ hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* str
   if (nb > 0)
     HIP_TRY(hipMemcpyAsync(c->P.table + dst * stride, c->P.table + src * stride, nb * 4,
                            hipMemcpyDeviceToDevice, s));
-  const int64_t slots = std::min(L, W);
-  if (slots > 0) {
-    const size_t bytes = (size_t)slots * kRow * 2;
-    HIP_TRY(hipMemcpyAsync(c->P.swa_k + (size_t)dst * W * kRow, c->P.swa_k + (size_t)src * W * kRow,
-                           bytes, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(hipMemcpyAsync(c->P.swa_v + (size_t)dst * W * kRow, c->P.swa_v + (size_t)src * W * kRow,
-                           bytes, hipMemcpyDeviceToDevice, s));
+  const int64_t slots = std::min(L, W), tail = L - kBlk * nb;
+  for (const Pools& P : c->layers) {   // the State of every layer
+    if (slots > 0) {
+      const size_t bytes = (size_t)slots * kRow * 2;
+      HIP_TRY(hipMemcpyAsync(P.swa_k + (size_t)dst * W * kRow, P.swa_k + (size_t)src * W * kRow, bytes,
+                             hipMemcpyDeviceToDevice, s));
+      HIP_TRY(hipMemcpyAsync(P.swa_v + (size_t)dst * W * kRow, P.swa_v + (size_t)src * W * kRow, bytes,
+                             hipMemcpyDeviceToDevice, s));
+    }
+    if (tail > 0 && P.c4)
+      HIP_TRY(hipMemcpyAsync(P.idx_tail + (size_t)dst * kBlk * kIRow, P.idx_tail + (size_t)src * kBlk * kIRow,
+                             (size_t)tail * kIRow * 4, hipMemcpyDeviceToDevice, s));
   }
-  const int64_t tail = L - kBlk * nb;
-  if (tail > 0)
-    HIP_TRY(hipMemcpyAsync(c->P.idx_tail + (size_t)dst * kBlk * kIRow,
-                           c->P.idx_tail + (size_t)src * kBlk * kIRow, (size_t)tail * kIRow * 4,
-                           hipMemcpyDeviceToDevice, s));
   return kOk;
 }
 
@@ -687,7 +819,9 @@ hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* str
 hsa_status hsa_block_ref(hsa_ctx* c, const int32_t* blocks, int64_t n, int32_t delta) {
   if (!c) return fail(kInvalid, "NULL context");
   std::string why;
-  int st = c->ctl.check_block_ref(blocks, n, delta, &why);
+  int st = no_open_seq(c);
+  if (st) return st;
+  st = c->ctl.check_block_ref(blocks, n, delta, &why);
   if (st) return fail(st, why);
   c->ctl.commit_block_ref(blocks, n, delta);
   return kOk;
@@ -699,7 +833,9 @@ hsa_status hsa_prefix_attach(hsa_ctx* c, int32_t n_req, const int32_t* states, c
   if (!c) return fail(kInvalid, "NULL context");
   std::string why;
   if (n_blocks < 0 || (n_blocks > 0 && !blocks)) return fail(kInvalid, "bad block list");
-  int st = c->ctl.check_attach_batch(n_req, states, len, blocks, n_blocks, block_off, &why);
+  int st = no_open_seq(c);
+  if (st) return st;
+  st = c->ctl.check_attach_batch(n_req, states, len, blocks, n_blocks, block_off, &why);
   if (st) return fail(st, why);
   if ((st = set_device(c))) return st;
   std::vector<AttachDesc> d;
@@ -734,7 +870,7 @@ hsa_status hsa_state_write(hsa_ctx* c, int32_t n_req, const int32_t* states, con
   int st = c->ctl.check_state_write(n_req, states, cu_tokens, pos0, &why);
   if (st) return fail(st, why);
   if (n_req == 0 || cu_tokens[n_req] == 0) return kOk;
-  if (!k || !v || !idx) return fail(kInvalid, "input pointer is NULL");
+  if (!k || !v || (!idx && c->P.c4)) return fail(kInvalid, "input pointer is NULL");
   if ((st = set_device(c))) return st;
   std::vector<WriteDesc> writes;
   int64_t total = 0;
@@ -779,7 +915,7 @@ hsa_status hsa_state_checkpoint(hsa_ctx* c, int32_t s_, void* buf, int64_t* len_
     HIP_TRY(hipMemcpyAsync(b, c->P.swa_k + S * W * kRow, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
     HIP_TRY(hipMemcpyAsync(b + ring, c->P.swa_v + S * W * kRow, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
   }
-  if (tail > 0)
+  if (tail > 0 && c->P.c4)
     HIP_TRY(hipMemcpyAsync(b + 2 * ring, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4,
                            hipMemcpyDefault, s));
   *len_out = L;
@@ -801,7 +937,7 @@ hsa_status hsa_state_restore(hsa_ctx* c, int32_t s_, const void* buf, int64_t ck
     HIP_TRY(hipMemcpyAsync(c->P.swa_k + S * W * kRow, b, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
     HIP_TRY(hipMemcpyAsync(c->P.swa_v + S * W * kRow, b + ring, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
   }
-  if (tail > 0)
+  if (tail > 0 && c->P.c4)
     HIP_TRY(hipMemcpyAsync(c->P.idx_tail + S * kBlk * kIRow, b + 2 * ring, (size_t)tail * kIRow * 4,
                            hipMemcpyDefault, s));
   return kOk;
@@ -847,18 +983,36 @@ hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, con
   if (n_req == 0) return kOk;
   if (k < 1 || k > HSA_MAX_TOPK) return fail(kInvalid, "k must be in [1, 4096]");
   if (flags & ~HSA_TOPK_SORTED) return fail(kInvalid, "unknown flags");
-  if (!k_new || !v_new || !idx_new || !q || !q_idx || !topk_out || !out)
+  if (!k_new || !v_new || (c->P.c4 && (!idx_new || !q_idx)) || !q || !topk_out || !out)
     return fail(kInvalid, "NULL device pointer");
+  bool replay = false;
+  int st = layer_gate(c, kSeqStep, n_req, states, nullptr, 0, &replay);
+  if (st) return st;
+  if (replay) {
+    if ((st = set_device(c))) return st;
+    layer_advance(c);
+    return run_decode_step(c, c->seq.plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out,
+                           score_out, out, static_cast<hipStream_t>(stream));
+  }
   std::vector<int64_t> cu(n_req + 1);
   for (int32_t i = 0; i <= n_req; ++i) cu[i] = i;
   std::string why;
   AppendPlan plan;
-  int st = c->ctl.plan_append(n_req, states, cu.data(), false, &plan, &why);
+  st = c->ctl.plan_append(n_req, states, cu.data(), false, &plan, &why);
   if (st) return fail(st, why);
   if ((st = set_device(c))) return st;
   c->ctl.commit(&plan);
+  layer_record(c, kSeqStep, n_req, states, nullptr, 0, plan);
   return run_decode_step(c, plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out, score_out,
                          out, static_cast<hipStream_t>(stream));
+}
+
+hsa_status hsa_set_layer(hsa_ctx* c, int32_t layer) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (layer < 0 || layer >= (int32_t)c->layers.size()) return fail(kInvalid, "no such layer");
+  c->cur_layer = layer;
+  c->P = c->layers[layer];
+  return kOk;
 }
 
 hsa_status hsa_state_query(hsa_ctx* c, int32_t s, hsa_state_info* out) {
@@ -898,6 +1052,8 @@ hsa_status hsa_export_block(hsa_ctx* c, int32_t b, void* csa_k, void* csa_v, voi
   if (st) return st;
   if (c->P.fp8 && (csa_k || csa_v)) return fail(kInvalid, "FP8 entries: export them with hsa_export_c4_fp8");
   if (c->P.mx4 && idx_k) return fail(kInvalid, "MXFP4 indexer keys: export them with hsa_export_idx_mxfp4");
+  if (!c->P.c4 && (csa_k || csa_v || idx_k)) return fail(kInvalid, "this layer keeps no C4 entries or indexer keys");
+  if (!c->P.hca && (hca_k || hca_v)) return fail(kInvalid, "this layer keeps no HCA entries");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t B = (size_t)b;
   if (csa_k) HIP_TRY(hipMemcpyAsync(csa_k, c->P.csa_k + B * kC4 * kRow, kC4 * kRow * 2, hipMemcpyDeviceToHost, s));
@@ -913,6 +1069,7 @@ hsa_status hsa_export_c4_fp8(hsa_ctx* c, int32_t b, uint8_t* codes_k, uint8_t* c
                              float* scale_k, float* scale_v, void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   if (!c->P.fp8) return fail(kInvalid, "the context stores bf16 entries");
+  if (!c->P.c4) return fail(kInvalid, "this layer keeps no C4 entries");
   if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
   int st = set_device(c);
   if (st) return st;
@@ -936,6 +1093,7 @@ hsa_status hsa_export_c4_fp8(hsa_ctx* c, int32_t b, uint8_t* codes_k, uint8_t* c
 hsa_status hsa_export_idx_mxfp4(hsa_ctx* c, int32_t b, uint8_t* codes, uint8_t* scales, void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   if (!c->P.mx4) return fail(kInvalid, "the context stores fp32 indexer keys");
+  if (!c->P.c4) return fail(kInvalid, "this layer keeps no indexer keys");
   if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
   int st = set_device(c);
   if (st) return st;
@@ -969,6 +1127,7 @@ hsa_status hsa_export_state(hsa_ctx* c, int32_t s_, void* swa_k, void* swa_v, fl
                             void* stream) {
   if (!c) return fail(kInvalid, "NULL context");
   if (!c->ctl.valid_state(s_)) return fail(kInvalid, "state not allocated");
+  if (idx_tail && !c->P.c4) return fail(kInvalid, "this layer keeps no indexer tail");
   int st = set_device(c);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -51,12 +51,13 @@ struct TokSrc {
 constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
 
 // Seal tokens [t0, t0 + 16) of one block (C4 entries bf16, or FP8 when FP8, which
-// the caller sets from P.fp8): writes their 4 C4 entries and 16
+// the caller sets from P.fp8; C4 false for layers without C4 entries, set from
+// P.c4): writes their 4 C4 entries and 16
 // indexer keys, and returns the HCA softmax partial (m, l, acc) of these tokens
 // for this lane's 8 dims. Both seal paths build the HCA entry from the same eight
 // partials merged in the same order, so bulk and one-token appends give
 // bit-identical blocks.
-template <bool FP8>
+template <bool FP8, bool C4>
 __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int32_t id, int t0,
                                           float& m, float& l, float* acck, float* accv) {
   const int tid = threadIdx.x;
@@ -88,8 +89,8 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       vw[u] = *reinterpret_cast<const uint4*>(src.v(tb + u) + off);
     }
     // indexer keys of the 4 tokens: 4 x 64 float4, one per lane (stored as MXFP4
-    // when P.mx4, a wave per key)
-    {
+    // when P.mx4, a wave per key); layers without C4 entries keep none
+    if constexpr (C4) {
       const int u = tid >> 6, c = tid & 63;
       const float4 iv = reinterpret_cast<const float4*>(src.i(tb + u))[c];
       if (P.mx4) {
@@ -143,7 +144,7 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
     }
     // C4 entry (tokens tb .. tb+3): softmax of the 4 CSA gates (after the HCA
     // update, so the packed tokens are dead while an FP8 entry is quantised)
-    {
+    if constexpr (C4) {
       const float mx = fmaxf(fmaxf(gc[0], gc[1]), fmaxf(gc[2], gc[3]));
       float e[4], s = 0.f;
 #pragma unroll
@@ -231,6 +232,7 @@ __device__ __forceinline__ void store_hca(const Pools& P, int32_t id, float l, c
 // Decode-time append of request i's one new token (position p = r.len - 1): ring
 // slot p mod n_win, indexer-tail slot p mod 128, and the device table entry of a
 // block the token seals (r.aux = its id, else -1). 256 threads.
+template <bool C4>
 __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i,
                                              const uint16_t* kin, const uint16_t* vin,
                                              const float* iin) {
@@ -239,7 +241,7 @@ __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i
   const int64_t ring = ((int64_t)r.state * P.n_win + (p % P.n_win)) * kRow;
   reinterpret_cast<uint4*>(P.swa_k + ring)[tid] = reinterpret_cast<const uint4*>(kin + (int64_t)i * kRow)[tid];
   reinterpret_cast<uint4*>(P.swa_v + ring)[tid] = reinterpret_cast<const uint4*>(vin + (int64_t)i * kRow)[tid];
-  if (tid < kIRow / 4) {
+  if (C4 && tid < kIRow / 4) {   // the indexer tail (layers with C4 entries)
     const int64_t ti = ((int64_t)r.state * kBlk + (p % kBlk)) * kIRow;
     reinterpret_cast<float4*>(P.idx_tail + ti)[tid] =
         reinterpret_cast<const float4*>(iin + (int64_t)i * kIRow)[tid];
@@ -251,7 +253,7 @@ __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i
 // 4 C4 entries, 16 indexer keys and one HCA partial to part[item * 8 + sub]. The
 // newest token (position r.len - 1) is read from input row i, so this may run in
 // the same launch as append_token. 256 threads.
-template <bool FP8>
+template <bool FP8, bool C4>
 __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i, int item, int sub,
                                             const uint16_t* kin, const uint16_t* vin,
                                             const float* iin, float* part) {
@@ -267,7 +269,7 @@ __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i,
   src.pos0 = (int64_t)(r.nb - 1) * kBlk;
   src.n_win = P.n_win;
   float m, l, acck[8], accv[8];
-  seal_part<FP8>(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
+  seal_part<FP8, C4>(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
   float* mine = part + (int64_t)(item * kSealSplit + sub) * kPartFloats;
   const int h = tid >> 4;
   if ((tid & 15) == 0) {

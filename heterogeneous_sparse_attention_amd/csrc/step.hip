@@ -38,14 +38,17 @@ namespace hsa {
 namespace {
 
 __device__ __forceinline__ int sealed_now(const Req& r) { return r.aux >= 0 ? 1 : 0; }
+// Part-A keys: the SWA tokens and, in layers with HCA entries, the HCA entries of
+// blocks sealed before this step.
 __device__ __forceinline__ int keys_a(const Pools& P, const Req& r) {
-  return (r.len < P.n_win ? r.len : P.n_win) + r.nb - sealed_now(r);
+  return (r.len < P.n_win ? r.len : P.n_win) + (P.hca ? r.nb - sealed_now(r) : 0);
 }
-// Part-B keys: the selected C4 entries, and in the four-launch form the HCA entry of
-// the block sealed now (the three-launch form takes that key in the merge).
-__device__ __forceinline__ int keys_b(const Req& r, int32_t k, int32_t fused) {
-  const int nc = kC4 * r.nb;
-  return (fused ? 0 : sealed_now(r)) + (k < nc ? k : nc);
+// Part-B keys: the selected C4 entries (layers with C4 entries), and in the
+// four-launch form the HCA entry of the block sealed now (layers with HCA entries;
+// the three-launch form takes that key in the merge).
+__device__ __forceinline__ int keys_b(const Pools& P, const Req& r, int32_t k, int32_t fused) {
+  const int nc = P.c4 ? kC4 * r.nb : 0;
+  return (fused || !P.hca ? 0 : sealed_now(r)) + (k < nc ? k : nc);
 }
 
 // Indexer scores of scoring unit `unit` (fp32 keys): 128 / kScoreSplit tokens of one
@@ -139,20 +142,21 @@ __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B,
 
 // FP8 entries: the seal's quantisation needs more registers than 4 workgroups per
 // CU leave, so that instance runs 3 per CU; the bf16 instance keeps 4.
-template <bool FP8>
+// (C4 false: a layer without C4 entries, whose seal keeps only the HCA partial)
+template <bool FP8, bool C4>
 __global__ __launch_bounds__(256, FP8 ? 3 : 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
   int bid = blockIdx.x;
   // -- seal eighths (first, so the longest single workgroups start early)
   if (bid < kSealSplit * B.n_seal) {
     const int item = bid / kSealSplit;
     const int ri = B.seal_req[item];
-    seal_eighth<FP8>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
+    seal_eighth<FP8, C4>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
     return;
   }
   bid -= kSealSplit * B.n_seal;
   // -- append
   if (bid < B.n) {
-    append_token(P, B.r[bid], bid, S.kin, S.vin, S.iin);
+    append_token<C4>(P, B.r[bid], bid, S.kin, S.vin, S.iin);
     return;
   }
   bid -= B.n;
@@ -231,7 +235,7 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   const int w = bid - S.first_b[r];
   const int nch = S.first_b[r + 1] - S.first_b[r];
   const Req R = B.r[r];
-  const int N = kC4 * R.nb;
+  const int N = P.c4 ? kC4 * R.nb : 0;
   const int kk = min(S.k, N);
   int a0, a1, b0, b1;
   chunk_range(keys_a(P, R), nch, w, a0, a1);
@@ -304,8 +308,8 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
     }
     bid -= S.sel.n_wgs;
   }
-  if (bid < B.n_seal) {
-    seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
+  if (bid < B.n_seal) {   // the HCA entries of blocks sealed in S1
+    if (P.hca) seal_merge(P, B.r[B.seal_req[bid]].aux, S.seal_part, bid);
     return;
   }
   bid -= B.n_seal;
@@ -332,8 +336,8 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
   const int nch = S.first_b[r + 1] - S.first_b[r];
   const Req R = B.r[r];
   int x0, x1;
-  chunk_range(keys_b(R, S.k, 0), nch, w, x0, x1);
-  const int sn = sealed_now(R);
+  chunk_range(keys_b(P, R, S.k, 0), nch, w, x0, x1);
+  const int sn = P.hca ? sealed_now(R) : 0;
   const int32_t* rows = S.rows + (int64_t)r * S.k;
   const int64_t max_row = (int64_t)P.max_blocks * kC4;
   auto key_b = [&](int x) {
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
   const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
   const Req R = B.r[r];
   ExtraKey xk{nullptr, nullptr, nullptr};
-  if (S.fused && R.aux >= 0)   // the HCA entry of the block sealed now, merged in S2
+  if (S.fused && R.aux >= 0 && P.hca)   // the HCA entry of the block sealed now, merged in S2
     xk = ExtraKey{P.hca_k + (int64_t)R.aux * kRow, P.hca_v + (int64_t)R.aux * kRow,
                   S.q + (int64_t)r * kRow};
   merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
@@ -379,8 +383,10 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
                  const LaunchEv& ev) {
   const int grid = kSealSplit * B.n_seal + B.n + S.n_score;
   if (grid == 0) return hipSuccess;
-  if (P.fp8) return launch_k(k_step1<true>, dim3(grid), dim3(kAttnWaves * 64), st, ev, P, B, S);
-  return launch_k(k_step1<false>, dim3(grid), dim3(kAttnWaves * 64), st, ev, P, B, S);
+  const dim3 g(grid), t(kAttnWaves * 64);
+  if (!P.c4) return launch_k(k_step1<false, false>, g, t, st, ev, P, B, S);
+  if (P.fp8) return launch_k(k_step1<true, true>, g, t, st, ev, P, B, S);
+  return launch_k(k_step1<false, true>, g, t, st, ev, P, B, S);
 }
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,

@@ -72,13 +72,41 @@ typedef struct hsa_config {
   int32_t max_states;           /* State slots                                      */
   int64_t max_blocks;           /* physical blocks in the Block Cache               */
   int64_t max_blocks_per_state; /* block-table row length; 0 = max_blocks           */
-  const float* gate_csa;        /* host [n_heads][head_dim] compressor gate, copied */
-  const float* gate_hca;        /* host [n_heads][head_dim] compressor gate, copied */
+  const float* gate_csa;        /* host [n_layers][n_heads][head_dim] compressor gates,
+                                   copied (one [n_heads][head_dim] row set per layer) */
+  const float* gate_hca;        /* host [n_layers][n_heads][head_dim], copied       */
   int32_t entry_format;         /* storage of C4 entries: HSA_ENTRY_BF16 or
                                    HSA_ENTRY_FP8 ([Ch12] §2.2 accounts entries in FP8) */
   int32_t index_format;         /* storage of sealed indexer keys: HSA_INDEX_F32 or
                                    HSA_INDEX_MXFP4 ([Ch12] §2.2 stores them as FP4) */
+  int32_t n_layers;             /* attention layers sharing the State quota and the
+                                   Block Cache; 0 means 1                           */
+  const int32_t* layer_types;   /* host [n_layers] HSA_LAYER_*, copied; NULL: every
+                                   layer HSA_LAYER_MIXED                            */
 } hsa_config;
+
+/* Layer types ([Ch12] Figure 12-1: per request one State quota over all layers - SWA
+ * layers, CSA state, HCA state - and per block the layers' compressed KV - CSA
+ * indexer keys, CSA main KV, HCA KV). Every type keeps an SWA window of n_win tokens.
+ *   MIXED  32 C4 + 1 HCA + 128 indexer keys per block; attention over SWA, every HCA
+ *          entry and the top-k C4 entries in one softmax (the single-layer path).
+ *   SWA    nothing in the Block Cache; attention over the SWA only.
+ *   CSA    32 C4 + 128 indexer keys per block; attention over SWA and the top-k C4.
+ *   HCA    1 HCA entry per block; attention over SWA and every HCA entry.
+ * A top-k row of a layer without C4 entries is all -1.
+ *
+ * Layers: data calls act on the current layer (hsa_set_layer; 0 after create). An
+ * append (hsa_append_kv, hsa_compress_flush, hsa_decode_step) is made at layer 0,
+ * which checks it and commits it to the shared State lengths and block tables; the
+ * same call (same states, token counts, flags) must then be made at layers 1 .. n-1
+ * in order, each with its own layer's K/V (and indexer keys, queries), before any
+ * other call that changes states or blocks (those return HSA_ERR_STATE meanwhile).
+ * Reads, exports, hsa_state_write, checkpoints and restores act on the current layer
+ * at any time. */
+#define HSA_LAYER_MIXED 0
+#define HSA_LAYER_SWA 1
+#define HSA_LAYER_CSA 2
+#define HSA_LAYER_HCA 3
 
 /* C4 entry storage. BF16: K and V rows of 16 x 128 bf16. FP8: per head, 128 OCP
  * FP8 E4M3 codes and one float32 scale s = amax / 448, amax = max |x| over the
@@ -262,6 +290,9 @@ hsa_status hsa_decode_step(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
                            const void* k_new, const void* v_new, const float* idx_new,
                            const void* q, const float* q_idx, int32_t k, uint32_t flags,
                            int32_t* topk_out, float* score_out, float* out, void* stream);
+
+/* Select the layer that data calls act on (0 <= layer < n_layers). Errors: INVALID. */
+hsa_status hsa_set_layer(hsa_ctx* ctx, int32_t layer);
 
 /* ---- introspection (host side; the export calls synchronise `stream`) ---- */
 hsa_status hsa_state_query(hsa_ctx* ctx, int32_t state, hsa_state_info* out);
