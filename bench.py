@@ -79,13 +79,15 @@ def step_fused(nb: np.ndarray) -> bool:
 
 
 def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray,
-               entries: str = "bf16", index: str = "f32") -> dict:
+               entries: str = "bf16", index: str = "f32", layer: str = "mixed") -> dict:
     """Bytes the method must move in one decode step, per launch (scratch excluded).
 
     L_after: lengths after the append; nb: sealed blocks after it; sealed: 1 where
     the step sealed a block; entries, index: storage formats of the C4 entries and
     of the sealed indexer keys (the block sealed in the step is scored from the
     float32 tail)."""
+    if layer != "mixed":
+        return layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer)
     C4 = c4_bytes(entries)
     SEAL = seal_bytes(entries, index)
     scan = (nb - sealed) * idx_bytes(index) + sealed * IDX_BLOCK
@@ -129,6 +131,31 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
     return out
 
 
+def layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer) -> dict:
+    """step_bytes of an SWA, CSA or HCA layer, always in three launches: what the
+    layer keeps and attends (the SWA always; C4 entries, indexer keys and the tail
+    for CSA; HCA entries for HCA)."""
+    c4, hca = layer == "csa", layer == "hca"
+    C4 = c4_bytes(entries)
+    swa = np.minimum(L_after, n_win)
+    kk = np.minimum(k, 32 * nb) if c4 else 0 * nb
+    B = len(L_after)
+    tok = ROW + (1024 if c4 else 0)                      # one token in, and into the State
+    seal = 128 * ROW + (128 * 1024 + 32 * C4 + idx_bytes(index) if c4 else 0) + (ROW if hca else 0)
+    scan = ((nb - sealed) * idx_bytes(index) + sealed * IDX_BLOCK) if c4 else 0 * nb
+    out = {
+        "step1": int(B * 2 * tok + sealed.sum() * (seal - (ROW if hca else 0)) + (scan.sum() if c4 else 0)
+                     + (B * 1024 if c4 else 0)),
+        "step2": int((kk * 8).sum() + B * k * 4 * (0 if c4 else 1) + (sealed.sum() * ROW if hca else 0)
+                     + (swa * ROW + (nb - sealed) * ROW * hca + kk * C4).sum() + B * 4096),
+        "step2b": 0,
+        "step3": 0,
+        "step4": int((sealed.sum() * ROW if hca else 0) + B * 8192),
+    }
+    out["step"] = sum(out.values())
+    return out
+
+
 def src_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(kernel, []):
@@ -139,7 +166,7 @@ def src_hash(kernel: str) -> str:
 
 # ------------------------------------------------------------------ the b32 decode workload
 
-def _append_device(cache, wl, states, reqs, p0s, p1s, chunk=65536):
+def _append_device(cache, wl, states, reqs, p0s, p1s, chunk=65536, seeds=None):
     """Append positions [p0, p1) of workload requests `reqs` to `states`, in calls of
     at most `chunk` tokens, with inputs generated on the device (keys as the
     workload keys them: shared-prefix positions carry their group's stream)."""
@@ -164,14 +191,24 @@ def _append_device(cache, wl, states, reqs, p0s, p1s, chunk=65536):
         K = torch.empty((T, 16, 128), dtype=torch.bfloat16, device="cuda")
         V = torch.empty_like(K)
         KI = torch.empty((T, 4, 64), dtype=torch.float32, device="cuda")
-        fill_rows(K, wl.seed, synth.STREAM_K, keys=kt, pos=pt)
-        fill_rows(V, wl.seed, synth.STREAM_V, keys=kt, pos=pt)
-        fill_rows(KI, wl.seed, synth.STREAM_IDXK, keys=kt, pos=pt)
-        cache.append_kv([states[j] for j in grp], cu, K, V, KI)
+        # a layer stack: the same append through every layer, each with its own tokens
+        for l, sd in enumerate(seeds or [wl.seed]):
+            if seeds:
+                cache.set_layer(l)
+            fill_rows(K, sd, synth.STREAM_K, keys=kt, pos=pt)
+            fill_rows(V, sd, synth.STREAM_V, keys=kt, pos=pt)
+            fill_rows(KI, sd, synth.STREAM_IDXK, keys=kt, pos=pt)
+            cache.append_kv([states[j] for j in grp], cu, K, V, KI)
         del K, V, KI
 
 
-def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", index: str = "f32"):
+def layer_seed(wl, layer: int) -> int:
+    """Token seed of one layer of a layer stack (layer 0 keeps the workload's)."""
+    return wl.seed + 101 * layer
+
+
+def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", index: str = "f32",
+                 layers=None):
     """Cache holding `copies` identical instances of the batch, every request
     prefilled to L0 (bulk appends of device-generated tokens; in a prefix workload
     each request forks off its group's parent at its fork length, sharing those
@@ -180,7 +217,12 @@ def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", i
     import torch
     import heterogeneous_sparse_attention_amd as hsa
 
-    Wc, Wh = synth.gate_weights(wl.seed)
+    types = layers or ["mixed"]
+    if layers:
+        gates = [synth.gate_weights(wl.seed + 7 * l) for l in range(len(types))]
+        Wc, Wh = np.stack([g[0] for g in gates]), np.stack([g[1] for g in gates])
+    else:
+        Wc, Wh = synth.gate_weights(wl.seed)
     L0 = wl.prefill.astype(np.int64)
     B = wl.batch
     max_len = int(L0.max()) + extra_steps + 1
@@ -188,7 +230,9 @@ def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", i
     n_parents = wl.n_groups if wl.prefix_len else 0
     cache = hsa.Cache(wl.n_win, copies * (B + n_parents), max_blocks + copies * n_parents * (wl.prefix_len // 128),
                       Wc, Wh, max_blocks_per_state=max_len // 128 + 2, entry_format=entries,
-                      index_format=index)
+                      index_format=index, layer_types=layers)
+    if layers and wl.prefix_len:
+        raise SystemExit("layer stacks are measured on workloads without shared prefixes")
     inst = []
     for _ in range(copies):
         states = [None] * B
@@ -208,13 +252,14 @@ def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", i
                 cache.state_free(parent)
         else:
             states = [cache.state_alloc() for _ in range(B)]
-        _append_device(cache, wl, states, list(range(B)), start, [int(x) for x in L0])
+        _append_device(cache, wl, states, list(range(B)), start, [int(x) for x in L0],
+                       seeds=[layer_seed(wl, l) for l in range(len(types))] if layers else None)
         inst.append(states)
     torch.cuda.synchronize()
     return cache, inst
 
 
-def decode_inputs(wl, L0: np.ndarray, n_steps: int):
+def decode_inputs(wl, L0: np.ndarray, n_steps: int, seed=None):
     """Per-step device inputs: the token at position L0 + t for each request."""
     import torch
     from synth.device import fill_rows
@@ -234,7 +279,7 @@ def decode_inputs(wl, L0: np.ndarray, n_steps: int):
     }
     for name, sid in (("k", synth.STREAM_K), ("v", synth.STREAM_V), ("ki", synth.STREAM_IDXK),
                       ("q", synth.STREAM_Q), ("qi", synth.STREAM_QI)):
-        fill_rows(t[name], wl.seed, sid, keys=kt, pos=pt)
+        fill_rows(t[name], wl.seed if seed is None else seed, sid, keys=kt, pos=pt)
     return {n_: x.view(n_steps, B, *x.shape[1:]) for n_, x in t.items()}
 
 
@@ -243,20 +288,27 @@ def run_decode(args) -> dict:
     wl = workloads.make(args.workload)
     B, k = wl.batch, wl.topk
     W, K = args.warmup, args.steps
-    R = args.copies if args.copies is not None else (4 if wl.name == "b32" else 1)
+    layers = args.layers.split(",") * args.layer_repeat if args.layers else None
+    types = layers or ["mixed"]
+    # a layer stack streams different data layer after layer by itself: one copy
+    R = args.copies if args.copies is not None else (4 if wl.name == "b32" and not layers else 1)
     local_steps = (W + 2 * K + R - 1) // R
-    cache, inst = setup_decode(wl, local_steps, R, args.entries, args.index)
+    cache, inst = setup_decode(wl, local_steps, R, args.entries, args.index, layers)
     L0 = wl.prefill.astype(np.int64)
-    inp = decode_inputs(wl, L0, local_steps)
+    inp = [decode_inputs(wl, L0, local_steps, seed=layer_seed(wl, l)) for l in range(len(types))]
     topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
     out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
 
     # step t advances instance t % R by its step t // R: consecutive steps read
-    # different copies of the cache, as consecutive layers of a model would
+    # different copies of the cache, as consecutive layers of a model would; a step
+    # of a layer stack is one decode step of every layer, in layer order
     def step(t):
         j = t // R
-        cache.decode_step(inst[t % R], inp["k"][j], inp["v"][j], inp["ki"][j], inp["q"][j],
-                          inp["qi"][j], k, topk_out=topk, out=out)
+        for l, x in enumerate(inp):
+            if layers:
+                cache.set_layer(l)
+            cache.decode_step(inst[t % R], x["k"][j], x["v"][j], x["ki"][j], x["q"][j],
+                              x["qi"][j], k, topk_out=topk, out=out)
 
     # warmup; its second half also times every kernel to find the dominant one
     half = W // 2
@@ -303,9 +355,10 @@ def run_decode(args) -> dict:
             L_after = L0 + t // R + 1
             nb = L_after // 128
             sealed = (L_after % 128 == 0).astype(np.int64)
-            sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index)
-            for n in acc:
-                acc[n] += sb[n]
+            for typ in types:
+                sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index, typ)
+                for n in acc:
+                    acc[n] += sb[n]
         return acc
 
     bytes_1 = bytes_over(W, W + K)
@@ -328,8 +381,9 @@ def run_decode(args) -> dict:
     fp8 = args.entries == "fp8"
     mx4 = args.index == "mxfp4"
     metric = METRIC if wl.name == "b32" else f"decode tokens/s + achieved HBM GB/s, append+attend, {wl.name}"
+    stack = f", {len(types)}-layer stack ({args.layers} x {args.layer_repeat})" if layers else ""
     res = {
-        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", MXFP4 indexer keys" if mx4 else ""),
+        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", MXFP4 indexer keys" if mx4 else "") + stack,
         "value": B * K / (ms_total * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -344,10 +398,13 @@ def run_decode(args) -> dict:
         "config": {"workload": f"{wl.name}: {B} requests, {LENGTHS[wl.name]} (seed {wl.seed:#x}), "
                                f"decode steps, n_win {wl.n_win}, top-k {k}, 16x128 bf16 K/V/Q"
                                f"{' (C4 entries FP8 E4M3, fp32 scale per head)' if fp8 else ''}, "
-                               f"indexer 4x64 fp32{' (sealed keys MXFP4)' if mx4 else ''}, m=4, m'=128, 1 layer; steps rotate over {R} "
+                               f"indexer 4x64 fp32{' (sealed keys MXFP4)' if mx4 else ''}, m=4, m'=128, "
+                               f"{len(types)} layer{'s' if len(types) > 1 else ''}"
+                               f"{' (' + ','.join(types) + ')' if layers else ''}; steps rotate over {R} "
                                f"copies of the cache",
                    "batch": B, "n_win": wl.n_win, "topk": k, "kv_dtype": "bf16",
                    "c4_entries": args.entries, "index_keys": args.index, "cache_copies": R,
+                   "layers": types,
                    "L0_mean": float(L0.mean()), "parallelism": "single GPU"},
         "hbm_gbps": step_gbs,
         "hbm_frac_of_peak": step_gbs / PEAK_HBM_GBS,
@@ -702,6 +759,10 @@ def main():
                     help="storage format of sealed indexer keys (fp32, or MXFP4 with E8M0 block scales)")
     ap.add_argument("--hit", default=None, choices=["zero", "periodic", "full"],
                     help="time a batch of prefix hits on the prefix workload under this SWA policy")
+    ap.add_argument("--layers", default=None,
+                    help="a layer stack: comma-separated types (mixed, swa, csa, hca), each step "
+                         "runs every layer")
+    ap.add_argument("--layer-repeat", type=int, default=1, help="repeat the --layers pattern")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters", default=None, help="comma-separated rocprofv3 --pmc output dirs")
@@ -727,7 +788,7 @@ def main():
         return
     res = run_bulk(args) if args.workload == 4 else run_decode(args)
     if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16" \
-            and args.index == "f32":
+            and args.index == "f32" and not args.layers:
         res["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(res), flush=True)
 
