@@ -77,6 +77,14 @@ Readings taken where the pages leave a step open (each also in the design notes)
       (the single-layer path) keeps both and attends all three. Layers share the
       State lengths and the block ids; a multi-layer cache is one oracle per
       layer, driven by the same calls.
+  R19 eager C4 (optional mode; the other reading of [Q&A] §3.1, where the CSA tail
+      is full at L mod 4 = 0): the C4 entry of each complete group of 4 tokens of
+      the open block exists as soon as the group is, pooled exactly as the seal
+      pools it, and is a top-k candidate and an attention key like a sealed one.
+      The open block's g = (L mod 128) // 4 entries (32 with a deferred full tail)
+      take ordinals 32 nb .. 32 nb + g - 1 after the sealed entries; their scores
+      use the tail's indexer keys. When the block seals, the entries move into it
+      unchanged. Supported with bf16 entries and float32 indexer keys.
 """
 
 from __future__ import annotations
@@ -407,7 +415,8 @@ class Oracle:
     """The cache, driven call by call like the C ABI."""
 
     def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int,
-                 entry_format: str = "bf16", index_format: str = "f32", layer_type: str = "mixed"):
+                 entry_format: str = "bf16", index_format: str = "f32", layer_type: str = "mixed",
+                 c4_mode: str = "sealed"):
         if n_win < BLOCK or n_win % BLOCK:
             raise OracleError("invalid", "n_win must be a positive multiple of 128")
         if entry_format not in ("bf16", "fp8"):
@@ -416,6 +425,11 @@ class Oracle:
             raise OracleError("invalid", "index format is f32 or mxfp4")
         if layer_type not in ("mixed", "swa", "csa", "hca"):
             raise OracleError("invalid", "layer type is mixed, swa, csa or hca")
+        if c4_mode not in ("sealed", "eager"):
+            raise OracleError("invalid", "c4 mode is sealed or eager")
+        if c4_mode == "eager" and (entry_format != "bf16" or index_format != "f32"):
+            raise OracleError("invalid", "eager C4 takes bf16 entries and f32 indexer keys")
+        self.eager = c4_mode == "eager"                       # reading R19
         self.layer_type = layer_type
         self.has_c4 = layer_type in ("mixed", "csa")          # reading R18
         self.has_hca = layer_type in ("mixed", "hca")
@@ -672,6 +686,17 @@ class Oracle:
             if p >= t0:
                 st.tail[p - t0] = item
 
+    def _open_groups(self, st: _State) -> int:
+        """Complete groups of 4 tokens in the open block that have eager entries."""
+        return len(st.tail) // M_CSA if (self.eager and self.has_c4) else 0
+
+    def _open_entry(self, st: _State, i: int):
+        """C4 entry of group i of the open block, pooled as the seal pools it."""
+        g = st.tail[M_CSA * i:M_CSA * (i + 1)]
+        Kg = np.stack([t[0] for t in g]).astype(np.float64)
+        Vg = np.stack([t[1] for t in g]).astype(np.float64)
+        return gated_pool(Kg, Vg, self.W_csa)
+
     def _filled(self, st: _State):
         if any(x is None for x in st.swa) or any(x is None for x in st.tail):
             raise OracleError("state", "state not filled: replay or restore first")
@@ -683,6 +708,11 @@ class Oracle:
         if not self.has_c4:
             return np.zeros(0)
         out = [c4_scores(self.store[b].idx, q_idx) for b in st.blocks]
+        g = self._open_groups(st)
+        if g:                                          # the open block's entries (R19)
+            keys = np.stack([t[2] for t in st.tail[:M_CSA * g]])
+            out.append(c4_scores(np.concatenate([keys, np.zeros((BLOCK - len(keys),) + keys.shape[1:])]),
+                                 q_idx)[:g])
         return np.concatenate(out) if out else np.zeros(0)
 
     def topk(self, s: int, q_idx, k: int, sorted: bool = False):
@@ -703,14 +733,19 @@ class Oracle:
         for b in st.blocks if self.has_hca else []:
             K.append(self.store[b].hca_k)
             V.append(self.store[b].hca_v)
-        nc = C4_PER_BLOCK * len(st.blocks) if self.has_c4 else 0
+        ns = C4_PER_BLOCK * len(st.blocks) if self.has_c4 else 0
+        nc = ns + self._open_groups(st)
         sel = np.asarray(sel if sel is not None else [], dtype=np.int64).reshape(-1)
         kk = min(len(sel) if k is None else int(k), nc)
         for j in sel[:kk]:
-            if 0 <= j < nc:
+            if 0 <= j < ns:
                 blk = self.store[st.blocks[j // C4_PER_BLOCK]]
                 K.append(blk.csa_k[j % C4_PER_BLOCK])
                 V.append(blk.csa_v[j % C4_PER_BLOCK])
+            elif ns <= j < nc:                         # an open-block entry (R19)
+                ke, ve = self._open_entry(st, int(j - ns))
+                K.append(ke)
+                V.append(ve)
         return np.stack(K), np.stack(V)
 
     def attend(self, s: int, q, sel, k: int | None = None) -> np.ndarray:

@@ -838,3 +838,48 @@ def test_layer_types_attend_their_parts_of_the_block():
                        atol=1e-13)
     assert np.allclose(m.attend(0, q, sel, kk),
                        attention(q, np.concatenate([Kw, Kh, Kc]), np.concatenate([Vw, Vh, Vc])), atol=1e-13)
+
+
+# ---------------------------------------------------------------- eager C4 (R19)
+
+def test_eager_c4_entries_match_the_sealed_ones():
+    """Eager mode: the open block's candidates are its complete groups (g = (L mod
+    128) // 4) after the sealed ones; each open entry and its score equal the entry
+    and score the same group has once its block seals; blocks are the sealed mode's;
+    with k covering every candidate, attention is brute force over SWA + HCA + all
+    sealed C4 + the open entries."""
+    Wc, Wh = synth.gate_weights(SEED)
+    e = Oracle(128, Wc, Wh, 2, 8, c4_mode="eager")
+    d = Oracle(128, Wc, Wh, 2, 8)
+    K, V, KI = toks(9, 0, 400)
+    qi = synth.tokens_f32(SEED, synth.STREAM_QI, 9, np.array([0]))[0].astype(np.float64)
+    q = synth.bf16_bits_to_f32(synth.tokens_bf16(SEED, synth.STREAM_Q, 9, np.array([0])))[0].astype(np.float64)
+    for o in (e, d):
+        assert o.state_alloc() == 0
+        o.append([0], [(K[:290], V[:290], KI[:290])])     # 2 blocks + 34 tail tokens
+    se, sd = e.scores(0, qi), d.scores(0, qi)
+    assert len(sd) == 64 and len(se) == 64 + 8 and np.array_equal(se[:64], sd)
+    st = e.states[0]
+    open_entries = [e._open_entry(st, i) for i in range(8)]
+    for o in (e, d):
+        o.append([0], [(K[290:384], V[290:384], KI[290:384])])   # the block seals at 384
+    assert len(e.scores(0, qi)) == 96 and len(e.states[0].tail) == 0
+    blk = e.block(e.table(0)[2])
+    for i, (ke, ve) in enumerate(open_entries):
+        assert np.array_equal(ke, blk.csa_k[i]) and np.array_equal(ve, blk.csa_v[i])
+    assert np.array_equal(e.scores(0, qi)[64:72], se[64:72])
+    assert np.array_equal(e.scores(0, qi), d.scores(0, qi))
+    e.append([0], [(K[384:391], V[384:391], KI[384:391])])      # 7 tokens: one open group
+    sel, _ = e.topk(0, qi, 200)
+    assert (sel >= 0).sum() == 97 and sel[96] == 96
+    st = e.states[0]
+    Kc = [e.block(b).csa_k[j] for b in e.table(0) for j in range(32)] + [e._open_entry(st, 0)[0]]
+    Vc = [e.block(b).csa_v[j] for b in e.table(0) for j in range(32)] + [e._open_entry(st, 0)[1]]
+    Kh = [e.block(b).hca_k for b in e.table(0)]
+    Vh = [e.block(b).hca_v for b in e.table(0)]
+    Kw, Vw = K[391 - 128:391], V[391 - 128:391]
+    ref = attention(q, np.concatenate([Kw, np.stack(Kh), np.stack(Kc)]),
+                    np.concatenate([Vw, np.stack(Vh), np.stack(Vc)]))
+    assert np.allclose(e.attend(0, q, sel, 200), ref, atol=1e-13)
+    with pytest.raises(OracleError):
+        Oracle(128, Wc, Wh, 1, 1, c4_mode="eager", entry_format="fp8")
