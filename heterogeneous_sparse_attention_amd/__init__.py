@@ -46,11 +46,13 @@ class _Config(ctypes.Structure):
                 ("gate_csa", ctypes.POINTER(ctypes.c_float)),
                 ("gate_hca", ctypes.POINTER(ctypes.c_float)),
                 ("entry_format", ctypes.c_int32), ("index_format", ctypes.c_int32),
-                ("n_layers", ctypes.c_int32), ("layer_types", ctypes.c_void_p)]
+                ("n_layers", ctypes.c_int32), ("layer_types", ctypes.c_void_p),
+                ("c4_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 ENTRY_FORMATS = {"bf16": 0, "fp8": 1}     # HSA_ENTRY_BF16, HSA_ENTRY_FP8
 INDEX_FORMATS = {"f32": 0, "mxfp4": 1}    # HSA_INDEX_F32, HSA_INDEX_MXFP4
 LAYER_TYPES = {"mixed": 0, "swa": 1, "csa": 2, "hca": 3}   # HSA_LAYER_*
+C4_MODES = {"sealed": 0, "eager": 1}                       # HSA_C4_SEALED, HSA_C4_EAGER
 
 
 class _StateInfo(ctypes.Structure):
@@ -167,7 +169,7 @@ class Cache:
 
     def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
                  max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16",
-                 index_format: str = "f32", layer_types=None):
+                 index_format: str = "f32", layer_types=None, c4_mode: str = "sealed"):
         """layer_types: None (one heterogeneous layer) or a list of "mixed", "swa",
         "csa", "hca"; then gate_csa / gate_hca hold one [16][128] set per layer."""
         lib = load()
@@ -175,6 +177,9 @@ class Cache:
             raise ValueError(f"entry_format must be one of {sorted(ENTRY_FORMATS)}")
         if index_format not in INDEX_FORMATS:
             raise ValueError(f"index_format must be one of {sorted(INDEX_FORMATS)}")
+        if c4_mode not in C4_MODES:
+            raise ValueError(f"c4_mode must be one of {sorted(C4_MODES)}")
+        self.c4_mode = c4_mode
         types = ["mixed"] if layer_types is None else list(layer_types)
         if not types or any(t not in LAYER_TYPES for t in types):
             raise ValueError(f"layer_types must be a non-empty list of {sorted(LAYER_TYPES)}")
@@ -188,7 +193,7 @@ class Cache:
                       self._gc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       ENTRY_FORMATS[entry_format], INDEX_FORMATS[index_format], nl,
-                      self._lt.ctypes.data_as(ctypes.c_void_p))
+                      self._lt.ctypes.data_as(ctypes.c_void_p), C4_MODES[c4_mode], 0)
         self.entry_format = entry_format
         self.index_format = index_format
         ctx = ctypes.c_void_p()

@@ -122,6 +122,12 @@ __global__ __launch_bounds__(256) void k_fp8_rows(const float* x, int64_t n_rows
   if ((threadIdx.x & 15) == 0) scales[row] = sc;
 }
 
+// Eager C4: one workgroup per open-block entry, every token from the state's ring.
+__global__ __launch_bounds__(256) void k_open_c4(Pools P, const OpenDesc* d) {
+  const OpenDesc o = d[blockIdx.x];
+  open_entry(P, o.state, o.nb, o.gi, -1, nullptr, nullptr);
+}
+
 // Table rows of attached states: one workgroup per state copies its block ids.
 __global__ __launch_bounds__(256) void k_attach_rows(int32_t* table, int64_t stride, const AttachDesc* d,
                                                      const int32_t* ids) {
@@ -142,6 +148,11 @@ __global__ __launch_bounds__(256) void k_mx4_rows(const float* x, int64_t n_rows
 }
 
 }  // namespace
+
+hipError_t launch_open_c4(const Pools& P, const OpenDesc* d, int32_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  return launch_k(k_open_c4, dim3((unsigned)n), dim3(256), st, LaunchEv{}, P, d);
+}
 
 hipError_t launch_attach_rows(const Pools& P, const AttachDesc* d, int32_t n, const int32_t* ids,
                               hipStream_t st) {

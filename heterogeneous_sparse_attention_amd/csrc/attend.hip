@@ -15,7 +15,7 @@ namespace {
 
 __device__ __forceinline__ int n_keys(const Pools& P, const Req& R, int32_t k) {
   const int swa = R.len < P.n_win ? R.len : P.n_win;
-  const int nc = P.c4 ? kC4 * R.nb : 0;
+  const int nc = c4_cands(P.c4, P.eager, R);
   return swa + (P.hca ? R.nb : 0) + (k < nc ? k : nc);
 }
 
@@ -43,9 +43,9 @@ __device__ __forceinline__ KeyAddr key_addr(const Pools& P, const Req& R, int x,
   }
   x -= nh;
   const int32_t j = sel[x];
-  if (j < 0 || j >= (P.c4 ? kC4 * R.nb : 0)) return a;
-  const int32_t id = tab[j / kC4];
-  if (id < 0 || id >= P.max_blocks) return a;
+  if (j < 0 || j >= c4_cands(P.c4, P.eager, R)) return a;
+  const int32_t id = tab[j / kC4];   // the open block's entry holds max_blocks + state (eager)
+  if (id < 0 || id >= P.c4_ids) return a;
   const C4Addr c = c4_addr(P, (int64_t)id * kC4 + j % kC4);
   a.k = c.k;
   a.v = c.v;

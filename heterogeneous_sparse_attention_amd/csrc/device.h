@@ -77,7 +77,11 @@ struct Pools {
   int32_t mx4;          // 1: sealed indexer keys are MXFP4 (idx_q, idx_e); 0: fp32 (idx_k)
   int32_t c4;           // layer type: 1 if the layer keeps C4 entries, indexer keys and tail
   int32_t hca;          // layer type: 1 if the layer keeps HCA entries
+  int32_t eager;        // 1: the open block's complete groups have C4 entries (eager C4)
+  int32_t c4_ids;       // C4 block ids in [0, c4_ids): the blocks, then (eager) one open
+                        // block per state at max_blocks + state
 };
+
 
 // One request of a launch: its state, its length and sealed-block count after the
 // call, and a kernel-specific field (decode append: id of the block this token
@@ -92,10 +96,27 @@ struct Req {
 struct ReqBatch {
   int32_t n;
   int32_t n_seal;              // decode append: how many requests seal
-  int32_t pad_[2];
+  int32_t n_open;              // eager C4: how many requests complete a group of the open block
+  int32_t pad_;
   Req r[kMaxReq];
   int8_t seal_req[kMaxReq];    // decode append: batch index of each sealing request
+  int8_t open_req[kMaxReq];    // eager C4: batch index of each request completing a group
 };
+
+// Eager C4: complete groups of 4 tokens in request R's open block (32 with a deferred
+// full tail), each with a C4 entry in the state's open block max_blocks + state.
+__device__ __forceinline__ int open_groups(int eager, const Req& R) {
+  return eager ? (R.len - kBlk * R.nb) >> 2 : 0;
+}
+// Top-k candidates of R: 32 per sealed block, then the open block's entries.
+__device__ __forceinline__ int c4_cands(int c4, int eager, const Req& R) {
+  return c4 ? kC4 * R.nb + open_groups(eager, R) : 0;
+}
+// Length of R's score row: 32 per block holding candidates (the open block's entries
+// past its groups score -inf), so always a multiple of 32.
+__device__ __forceinline__ int c4_rowlen(int c4, int eager, const Req& R) {
+  return c4 ? kC4 * (R.nb + (open_groups(eager, R) > 0 ? 1 : 0)) : 0;
+}
 
 // Rows of more than `slice` scores are selected in two rounds, so that one long row
 // is spread over many workgroups. Round 1: each slice of `slice` scores (the last
@@ -112,6 +133,8 @@ struct SelPlan {
   int32_t gmax;                    // slices of the most-sliced row (1: no row is sliced)
   int32_t k1;                      // candidates kept per slice
   int32_t slice;                   // scores per slice, a multiple of 32
+  int32_t eager;                   // rows include the open block's entries (eager C4)
+  int32_t pad_;
   int32_t* cand_ord;               // [n][gmax][k1]
   float* cand_score;               // [n][gmax][k1]
   int32_t first[kMaxReq + 1];      // request i's round-1 workgroups: [first[i], first[i+1])
@@ -135,6 +158,15 @@ struct WriteDesc {
   int64_t w0;        // first position written: max(len_old, len_new - n_win)
   int64_t row0;      // packed input row of position len_old
   int64_t cum;       // tokens written by earlier requests of the call
+};
+
+// Eager C4: entry gi of the open block (logical block nb) of a state, recomputed from
+// its ring after a bulk append, a fork, a replay or a restore.
+struct OpenDesc {
+  int32_t state;
+  int32_t nb;
+  int32_t gi;
+  int32_t pad_;
 };
 
 // One state of a prefix attach: its table row takes ids[off .. off + nb).

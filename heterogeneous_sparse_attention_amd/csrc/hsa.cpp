@@ -261,13 +261,40 @@ int run_decode_append(hsa_ctx* c, const AppendPlan& plan, const void* k, const v
   return kOk;
 }
 
+// Eager C4, host side: complete groups of the open block, top-k candidates and
+// score-row length of a request of length len with nb sealed blocks (as open_groups,
+// c4_cands and c4_rowlen on the device).
+int64_t h_open(const Pools& P, int64_t len, int64_t nb) { return P.eager ? (len - kBlk * nb) / 4 : 0; }
+int64_t h_cands(const Pools& P, int64_t len, int64_t nb) { return P.c4 ? kC4 * nb + h_open(P, len, nb) : 0; }
+int64_t h_rowlen(const Pools& P, int64_t len, int64_t nb) {
+  return P.c4 ? kC4 * (nb + (h_open(P, len, nb) > 0 ? 1 : 0)) : 0;
+}
+
+// Eager C4: recompute every open-block entry of the listed states from their rings
+// (after a bulk append, a fork, a replay or a restore). No-op otherwise.
+int recompute_open(hsa_ctx* c, const int32_t* states, int32_t n, hipStream_t st) {
+  if (!c->P.eager) return kOk;
+  std::vector<OpenDesc> d;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = states[i];
+    const int64_t nb = c->ctl.n_blocks(s), g = h_open(c->P, c->ctl.len(s), nb);
+    for (int64_t gi = 0; gi < g; ++gi) d.push_back(OpenDesc{s, (int32_t)nb, (int32_t)gi, 0});
+  }
+  if (d.empty()) return kOk;
+  int s = upload_plan(c, d.data(), d.size() * sizeof(OpenDesc), st);
+  if (s) return s;
+  HIP_TRY(launch_open_c4(c->P, static_cast<const OpenDesc*>(c->plan_dev), (int32_t)d.size(), st));
+  return kOk;
+}
+
 // Top-k workgroups of a batch (plan_slices), with room for the candidates of
 // sliced rows. On the 4 x 2^20-token workload (k 2048), 32768-score slices measured
 // 736 us per step, against 759 us for 16384 and 764 us for 65536.
 int plan_select(hsa_ctx* c, const ReqBatch& B, int32_t k, SelPlan& SP) {
   SP = SelPlan{};
   int64_t n[kMaxReq];
-  for (int i = 0; i < B.n; ++i) n[i] = (int64_t)kC4 * B.r[i].nb;
+  for (int i = 0; i < B.n; ++i) n[i] = h_rowlen(c->P, B.r[i].len, B.r[i].nb);
+  SP.eager = c->P.eager;
   plan_slices(n, B.n, k, c->select_slice, kSliceN, SP.first, &SP.gmax, &SP.slice, &SP.k1);
   SP.n_wgs = SP.first[B.n];
   if (SP.gmax > 1) {
@@ -299,10 +326,11 @@ int run_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_id
     ReqBatch B = read_batch(c, states, b0, n);
     if (!c->P.c4)   // no C4 entries in this layer: every row is padding
       for (int i = 0; i < n; ++i) B.r[i].nb = 0;
-    int64_t total = 0, maxnb = 0;
+    int64_t total = 0, maxnb = 0;   // scored blocks (eager C4: the open block too)
     for (int i = 0; i < n; ++i) {
-      total += B.r[i].nb;
-      maxnb = std::max<int64_t>(maxnb, B.r[i].nb);
+      const int64_t bl = h_rowlen(c->P, B.r[i].len, B.r[i].nb) / kC4;
+      total += bl;
+      maxnb = std::max<int64_t>(maxnb, bl);
     }
     const int64_t ld = std::max<int64_t>(kC4 * maxnb, 1);
     int s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(ld * n), sizeof(float));
@@ -342,7 +370,7 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
     int64_t keys = 0;
     for (int i = 0; i < n; ++i) {
       const int64_t swa = std::min<int64_t>(B.r[i].len, c->P.n_win);
-      nk[i] = swa + (c->P.hca ? B.r[i].nb : 0) + (c->P.c4 ? std::min<int64_t>(k, (int64_t)kC4 * B.r[i].nb) : 0);
+      nk[i] = swa + (c->P.hca ? B.r[i].nb : 0) + std::min<int64_t>(k, h_cands(c->P, B.r[i].len, B.r[i].nb));
       keys += nk[i];
     }
     const int32_t chunk = attend_chunk(keys, n, c->attend_wgs);
@@ -390,7 +418,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     const bool c4 = c->P.c4 != 0, hca = c->P.hca != 0;
     bool fused = !c4 || (c->step_fused != 0 && !(flags & HSA_TOPK_SORTED));
     for (int i = 0; i < n; ++i)
-      fused = fused && (!c4 || (int64_t)kC4 * plan.reqs[b0 + i].nb_new <= kCacheN);
+      fused = fused && h_rowlen(c->P, plan.reqs[b0 + i].len_new, plan.reqs[b0 + i].nb_new) <= kCacheN;
     std::vector<int64_t> na(n), nb(n);
     int64_t maxnb = 0, n_score = 0, all_nb = 0;
     for (int i = 0; i < n; ++i) all_nb += plan.reqs[b0 + i].nb_new;
@@ -408,9 +436,12 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       if (id >= 0 && (c4 || hca)) B.seal_req[B.n_seal++] = (int8_t)i;   // an SWA layer seals nothing
       const int64_t sealed = id >= 0 ? 1 : 0;
       na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + (hca ? r.nb_new - sealed : 0);
-      nb[i] = (fused || !hca ? 0 : sealed) + (c4 ? std::min<int64_t>(k, (int64_t)kC4 * r.nb_new) : 0);
-      maxnb = std::max<int64_t>(maxnb, r.nb_new);
-      if (c4) n_score += score_units(r.nb_new, mx_unit);
+      nb[i] = (fused || !hca ? 0 : sealed) + std::min<int64_t>(k, h_cands(c->P, r.len_new, r.nb_new));
+      maxnb = std::max<int64_t>(maxnb, h_rowlen(c->P, r.len_new, r.nb_new) / kC4);
+      // eager C4: the open block is scored too, and a completed group gets its entry
+      const bool open = h_open(c->P, r.len_new, r.nb_new) > 0;
+      if (c4) n_score += score_units(r.nb_new, mx_unit) + (open ? kScoreSplit : 0);
+      if (c->P.eager && r.len_new % 4 == 0 && r.len_new % kBlk != 0) B.open_req[B.n_open++] = (int8_t)i;
     }
     StepArgs S{};
     S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
@@ -452,7 +483,8 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       S.first_s[i] = (int32_t)ts;
       ta += pa.wgs[i];
       tb += pb.wgs[i];
-      ts += c4 ? score_units(B.r[i].nb, mx_unit) : 0;
+      ts += c4 ? score_units(B.r[i].nb, mx_unit) + (h_open(c->P, B.r[i].len, B.r[i].nb) > 0 ? kScoreSplit : 0)
+               : 0;
     }
     S.first_a[n] = (int32_t)ta;
     S.first_b[n] = (int32_t)tb;
@@ -574,6 +606,11 @@ int check_config(const hsa_config* cfg) {
   if (cfg->index_format != HSA_INDEX_F32 && cfg->index_format != HSA_INDEX_MXFP4)
     return fail(kInvalid, "index_format must be HSA_INDEX_F32 or HSA_INDEX_MXFP4");
   if (cfg->n_layers < 0 || cfg->n_layers > 1024) return fail(kInvalid, "n_layers must be in [0, 1024]");
+  if (cfg->c4_mode != HSA_C4_SEALED && cfg->c4_mode != HSA_C4_EAGER)
+    return fail(kInvalid, "c4_mode must be HSA_C4_SEALED or HSA_C4_EAGER");
+  if (cfg->c4_mode == HSA_C4_EAGER &&
+      (cfg->entry_format != HSA_ENTRY_BF16 || cfg->index_format != HSA_INDEX_F32))
+    return fail(kInvalid, "eager C4 takes bf16 entries and fp32 indexer keys");
   if (cfg->layer_types)
     for (int l = 0; l < std::max(1, cfg->n_layers); ++l)
       if (cfg->layer_types[l] < HSA_LAYER_MIXED || cfg->layer_types[l] > HSA_LAYER_HCA)
@@ -606,9 +643,13 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   const bool fp8 = cfg->entry_format == HSA_ENTRY_FP8;
   const bool mx4 = cfg->index_format == HSA_INDEX_MXFP4;
   const int n_layers = cfg->n_layers > 0 ? cfg->n_layers : 1;
+  const bool eager = cfg->c4_mode == HSA_C4_EAGER;
+  // eager C4: each state's open block is C4 block id max_blocks + state, and its table
+  // row has one more entry (the open block's)
+  const size_t NB4 = NB + (eager ? S : 0), stride = (size_t)bps + (eager ? 1 : 0);
   // shared by the layers: block tables, seal partials, every layer's gates
   void* sh[3] = {};
-  const size_t sh_bytes[3] = {S * (size_t)bps * 4, (size_t)kMaxReq * kSealSplit * kPartFloats * 4,
+  const size_t sh_bytes[3] = {S * stride * 4, (size_t)kMaxReq * kSealSplit * kPartFloats * 4,
                               (size_t)n_layers * 2 * kRow * 4};
   for (int i = 0; i < 3; ++i) {
     st = dev_alloc(c, &sh[i], sh_bytes[i]);
@@ -632,7 +673,7 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
     const size_t bytes[kPools] = {
         S * W * kRow * 2, S * W * kRow * 2,                                     // swa_k, swa_v
         c4 ? S * kBlk * kIRow * 4 : 0,                                          // idx_tail
-        c4 && !fp8 ? NB * kC4 * kRow * 2 : 0, c4 && !fp8 ? NB * kC4 * kRow * 2 : 0,   // csa (bf16)
+        c4 && !fp8 ? NB4 * kC4 * kRow * 2 : 0, c4 && !fp8 ? NB4 * kC4 * kRow * 2 : 0,   // csa (bf16)
         hca ? NB * kRow * 2 : 0, hca ? NB * kRow * 2 : 0,                       // hca
         c4 && !mx4 ? NB * kBlk * kIRow * 4 : 0,                                 // idx_k (fp32 keys)
         c4 && fp8 ? NB * kC4 * kC4Bytes : 0, c4 && fp8 ? NB * kC4 * kC4Scales * 4 : 0,   // FP8 C4
@@ -658,7 +699,7 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
     P.idx_q = static_cast<uint8_t*>(p[10]);
     P.idx_e = static_cast<uint8_t*>(p[11]);
     P.table = table;
-    P.table_stride = bps;
+    P.table_stride = (int64_t)stride;
     P.gate_csa = gates + (size_t)l * 2 * kRow;
     P.gate_hca = gates + (size_t)l * 2 * kRow + kRow;
     P.n_win = cfg->n_win;
@@ -667,6 +708,8 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
     P.mx4 = mx4 ? 1 : 0;
     P.c4 = c4 ? 1 : 0;
     P.hca = hca ? 1 : 0;
+    P.eager = eager && c4 ? 1 : 0;
+    P.c4_ids = (int32_t)(c4 ? NB4 : NB);
   }
   c->P = c->layers[0];
   // attention partials: a decode step has at most max(slots, requests) workgroups per
@@ -758,7 +801,9 @@ hsa_status hsa_append_kv(hsa_ctx* c, int32_t n_req, const int32_t* states, const
     layer_record(c, kSeqAppend, n_req, states, cu, flags, fresh);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return one_each ? run_decode_append(c, plan, k, v, idx_k, s) : run_bulk(c, plan, k, v, idx_k, s);
+  st = one_each ? run_decode_append(c, plan, k, v, idx_k, s) : run_bulk(c, plan, k, v, idx_k, s);
+  if (st) return st;
+  return recompute_open(c, states, n_req, s);   // eager C4: the open blocks' entries
 }
 
 hsa_status hsa_compress_flush(hsa_ctx* c, int32_t n_req, const int32_t* states, void* stream) {
@@ -811,7 +856,15 @@ hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* str
       HIP_TRY(hipMemcpyAsync(P.idx_tail + (size_t)dst * kBlk * kIRow, P.idx_tail + (size_t)src * kBlk * kIRow,
                              (size_t)tail * kIRow * 4, hipMemcpyDeviceToDevice, s));
   }
-  return kOk;
+  // eager C4: dst's own open-block entries, from its copied ring, in every layer
+  const Pools cur = c->P;
+  for (const Pools& P : c->layers) {
+    c->P = P;
+    st = recompute_open(c, &dst, 1, s);
+    if (st) break;
+  }
+  c->P = cur;
+  return st;
 }
 
 // ---- prefix hits: block references, attach, replay, checkpoints -------------------
@@ -890,7 +943,7 @@ hsa_status hsa_state_write(hsa_ctx* c, int32_t n_req, const int32_t* states, con
   Timed t(c, HSA_KERNEL_WRITE, hs);
   HIP_TRY(launch_bulk_write(c->P, static_cast<const WriteDesc*>(c->plan_dev), (int32_t)writes.size(), total,
                             k, v, idx, hs, t.ev()));
-  return kOk;
+  return recompute_open(c, states, n_req, hs);   // eager C4: entries of the replayed groups
 }
 
 hsa_status hsa_checkpoint_bytes(hsa_ctx* c, int64_t* bytes) {
@@ -940,7 +993,7 @@ hsa_status hsa_state_restore(hsa_ctx* c, int32_t s_, const void* buf, int64_t ck
   if (tail > 0 && c->P.c4)
     HIP_TRY(hipMemcpyAsync(c->P.idx_tail + S * kBlk * kIRow, b + 2 * ring, (size_t)tail * kIRow * 4,
                            hipMemcpyDefault, s));
-  return kOk;
+  return recompute_open(c, &s_, 1, s);   // eager C4: the open block's entries
 }
 
 hsa_status hsa_indexer_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx,

@@ -14,8 +14,14 @@ namespace {
 __global__ __launch_bounds__(256, 4) void k_score(Pools P, ReqBatch B, const float* q_idx,
                                                   float* scores, int64_t ld) {
   int r, w, first;
-  find_item(B.n, blockIdx.x, [&](int i) { return B.r[i].nb; }, r, w, first);
+  find_item(B.n, blockIdx.x, [&](int i) { return c4_rowlen(P.c4, P.eager, B.r[i]) / kC4; }, r, w, first);
   const Req R = B.r[r];
+  if (w == R.nb) {   // eager C4: the open block, its keys in the indexer tail
+    const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
+    score_block([&](int t) { return tail + t * kIRow; }, q_idx + (int64_t)r * kIRow,
+                scores + (int64_t)r * ld + (int64_t)kC4 * w, open_groups(P.eager, R));
+    return;
+  }
   const int32_t id = P.table[(int64_t)R.state * P.table_stride + w];
   float* out = scores + (int64_t)r * ld + (int64_t)kC4 * w;
   if (id < 0 || id >= P.max_blocks) {          // never taken: tables are written before use

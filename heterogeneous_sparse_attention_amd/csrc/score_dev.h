@@ -22,7 +22,8 @@ namespace hsa {
 // the 4 tokens of an entry are summed per lane before one wave reduction. row(t)
 // is the keys of the t-th token of the range, out the range's first score.
 template <int EPW = 8, class RowFn>
-__device__ __forceinline__ void score_block(RowFn row, const float* q_row, float* out32) {
+__device__ __forceinline__ void score_block(RowFn row, const float* q_row, float* out32,
+                                            int n_valid = 0x7fffffff) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const float4 q = reinterpret_cast<const float4*>(q_row)[lane];
@@ -43,7 +44,8 @@ __device__ __forceinline__ void score_block(RowFn row, const float* q_row, float
       a = fmaf(q.w, kv[e][u].w, a);
     }
     a = wave_sum(a);
-    if (lane == e) out[e] = a * 0.25f;
+    // entries from n_valid on (an open block's incomplete groups) score -inf
+    if (lane == e) out[e] = EPW * wave + e < n_valid ? a * 0.25f : -INFINITY;
   }
 }
 
@@ -220,12 +222,12 @@ __device__ __forceinline__ void select_round1(int bid, int n_req, const Req* req
   const int g = bid - SP.first[r];
   const int G = SP.first[r + 1] - SP.first[r];
   const Req R = reqs[r];
-  const int N = kC4 * R.nb;
+  const int N = c4_rowlen(1, SP.eager, R);
   const float* S = scores + (int64_t)r * ld;
   if (G == 1) {
     select_run<NT>(N, k, sorted, S, topk + (int64_t)r * k, score_out ? score_out + (int64_t)r * k : nullptr,
                    sh, table ? table + (int64_t)R.state * stride : nullptr,
-                   rows ? rows + (int64_t)r * k : nullptr, R.nb);
+                   rows ? rows + (int64_t)r * k : nullptr, N / kC4, 0, nullptr, c4_cands(1, SP.eager, R));
     return;
   }
   const int base = g * SP.slice;
@@ -247,7 +249,7 @@ __device__ __forceinline__ void select_round2(int r, const Req* reqs, const SelP
   select_run<NT>(G * SP.k1, k, sorted, SP.cand_score + c0, topk + (int64_t)r * k,
                  score_out ? score_out + (int64_t)r * k : nullptr, sh,
                  table ? table + (int64_t)R.state * stride : nullptr, rows ? rows + (int64_t)r * k : nullptr,
-                 R.nb, 0, SP.cand_ord + c0);
+                 c4_rowlen(1, SP.eager, R) / kC4, 0, SP.cand_ord + c0, c4_cands(1, SP.eager, R));
 }
 
 // Exclusive prefix sum over the wave's lanes, and the wave total in `total`.
@@ -279,11 +281,11 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
                                            int32_t* io, float* so, SelShared& sh,
                                            const int32_t* tab = nullptr, int32_t* rows = nullptr,
                                            int nb_tab = 0, int32_t ord0 = 0,
-                                           const int32_t* ord_map = nullptr) {
+                                           const int32_t* ord_map = nullptr, int kmax = 0x7fffffff) {
   static_assert(NT % 64 == 0 && NT <= kSelThreads && NT >= 256, "select workgroup size");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
-  const int kk = min(k, N);
+  const int kk = min(min(k, N), kmax);   // kmax: candidates of the row (eager rows end in -inf)
   const bool cached = N <= kCacheN;
   const bool tab_lds = rows && nb_tab <= kTabCache;
   auto row_of = [&](int j) -> int32_t {
@@ -579,12 +581,12 @@ __device__ __forceinline__ void select_stage(const SelPre<NT>& pre, SelShared& s
 
 template <int NT>
 __device__ __forceinline__ void select_lds(int N, int32_t k, int32_t* io, float* so, SelShared& sh,
-                                           int32_t* rows, SelWin win) {
+                                           int32_t* rows, SelWin win, int kmax) {
   constexpr int NW = NT / 64;
   constexpr int PMAX = kCacheN / NT;   // keys per thread in the ordered pass, at most
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int kk = min(k, N);
+  const int kk = min(min(k, N), kmax);   // kmax: candidates of the row (eager rows end in -inf)
   HSA_GLOBAL int32_t* gio = as_global(io);
   HSA_GLOBAL float* gso = so ? as_global(so) : nullptr;
   if (kk > 0) {

@@ -50,6 +50,100 @@ struct TokSrc {
 
 constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
 
+// C4 entry of 4 tokens: this lane's 8 dims of each (packed bf16) and their CSA gate
+// logits gc (<W_csa[h], K_t[h]>); softmax over the 4 gates, the weighted sums of K
+// and V, stored in C4 row `row` as bf16 or, with FP8, as per-head E4M3 codes and a
+// scale (lanes 16h .. 16h+15 hold head h, so the scale's max runs over one DPP row).
+// The seal and the eager entries of an open block both store through it, so an
+// entry is the same bits before and after its block seals.
+template <bool FP8>
+__device__ __forceinline__ void c4_pool_store(const Pools& P, int64_t row, const uint4* kw, const uint4* vw,
+                                              const float* gc) {
+  const int tid = threadIdx.x;
+  const int h = tid >> 4;
+  const int off = tid * 8;
+  const float mx = fmaxf(fmaxf(gc[0], gc[1]), fmaxf(gc[2], gc[3]));
+  float e[4], s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    e[u] = __expf(gc[u] - mx);
+    s += e[u];
+  }
+  const float inv = 1.f / s;
+  float ck[8], cv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ck[i] = cv[i] = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float kf[8], vf[8];
+    unpack8(kw[u], kf);
+    unpack8(vw[u], vf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ck[i] = fmaf(e[u], kf[i], ck[i]);
+      cv[i] = fmaf(e[u], vf[i], cv[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ck[i] *= inv;
+    cv[i] *= inv;
+  }
+  if (FP8) {
+    float sk, sv;
+    const uint2 qk = quantize8_e4m3(ck, sk);
+    const uint2 qv = quantize8_e4m3(cv, sv);
+    uint8_t* q = P.c4q + row * kC4Bytes;
+    *reinterpret_cast<uint2*>(q + off) = qk;
+    *reinterpret_cast<uint2*>(q + kRow + off) = qv;
+    if ((tid & 15) == 0) {
+      const int hp = 4 * (h & 3) + (h >> 2);   // the order attention lanes read
+      P.c4s[row * kC4Scales + hp] = sk;
+      P.c4s[row * kC4Scales + kH + hp] = sv;
+    }
+  } else {
+    uint4 ok, ov;
+    ok.x = pack_bf2(ck[0], ck[1]); ok.y = pack_bf2(ck[2], ck[3]);
+    ok.z = pack_bf2(ck[4], ck[5]); ok.w = pack_bf2(ck[6], ck[7]);
+    ov.x = pack_bf2(cv[0], cv[1]); ov.y = pack_bf2(cv[2], cv[3]);
+    ov.z = pack_bf2(cv[4], cv[5]); ov.w = pack_bf2(cv[6], cv[7]);
+    *reinterpret_cast<uint4*>(P.csa_k + row * kRow + off) = ok;
+    *reinterpret_cast<uint4*>(P.csa_v + row * kRow + off) = ov;
+  }
+}
+
+// Eager C4: entry `gi` of state `state`'s open block (logical block nb), from the
+// state's ring, except the token at position `in_pos`, read from `in_k` / `in_v`
+// (the token appended in the same launch; -1: none). Gate logits and pooling are
+// the seal's own, so the entry is bit-identical to the one the seal stores later.
+// Also points the table entry of the open block at the state's open block.
+__device__ __forceinline__ void open_entry(const Pools& P, int32_t state, int32_t nb, int gi,
+                                           int64_t in_pos, const uint16_t* in_k, const uint16_t* in_v) {
+  const int tid = threadIdx.x;
+  const int off = tid * 8;
+  float wc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wc[i] = P.gate_csa[off + i];
+  const int64_t p0 = (int64_t)kBlk * nb + 4 * gi;
+  uint4 kw[4], vw[4];
+  float gc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t p = p0 + u;
+    const int64_t ring = ((int64_t)state * P.n_win + p % P.n_win) * kRow;
+    kw[u] = *reinterpret_cast<const uint4*>((p == in_pos ? in_k : P.swa_k + ring) + off);
+    vw[u] = *reinterpret_cast<const uint4*>((p == in_pos ? in_v : P.swa_v + ring) + off);
+    float kf[8];
+    unpack8(kw[u], kf);
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaf(wc[i], kf[i], a);
+    gc[u] = row_sum16(a);
+  }
+  c4_pool_store<false>(P, (int64_t)(P.max_blocks + state) * kC4 + gi, kw, vw, gc);
+  if (tid == 0) P.table[(int64_t)state * P.table_stride + nb] = P.max_blocks + state;
+}
+
 // Seal tokens [t0, t0 + 16) of one block (C4 entries bf16, or FP8 when FP8, which
 // the caller sets from P.fp8; C4 false for layers without C4 entries, set from
 // P.c4): writes their 4 C4 entries and 16
@@ -70,8 +164,6 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
     wc[i] = P.gate_csa[off + i];
     wh[i] = P.gate_hca[off + i];
   }
-  uint16_t* csa_k = P.csa_k + (int64_t)id * kC4 * kRow;
-  uint16_t* csa_v = P.csa_v + (int64_t)id * kC4 * kRow;
   float* idx_dst = P.idx_k + (int64_t)id * kBlk * kIRow;
 
   m = -INFINITY;
@@ -142,62 +234,9 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       }
       m = mx;
     }
-    // C4 entry (tokens tb .. tb+3): softmax of the 4 CSA gates (after the HCA
-    // update, so the packed tokens are dead while an FP8 entry is quantised)
-    if constexpr (C4) {
-      const float mx = fmaxf(fmaxf(gc[0], gc[1]), fmaxf(gc[2], gc[3]));
-      float e[4], s = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        e[u] = __expf(gc[u] - mx);
-        s += e[u];
-      }
-      const float inv = 1.f / s;
-      float ck[8], cv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ck[i] = cv[i] = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float kf[8], vf[8];
-        unpack8(kw[u], kf);
-        unpack8(vw[u], vf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ck[i] = fmaf(e[u], kf[i], ck[i]);
-          cv[i] = fmaf(e[u], vf[i], cv[i]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ck[i] *= inv;
-        cv[i] *= inv;
-      }
-      const int slot = tb >> 2;
-      if (FP8) {
-        // FP8 entry: per head, E4M3 codes and a float32 scale (lanes 16h .. 16h+15
-        // hold head h, so the scale's max runs over one DPP row)
-        const int64_t row = (int64_t)id * kC4 + slot;
-        float sk, sv;
-        const uint2 qk = quantize8_e4m3(ck, sk);
-        const uint2 qv = quantize8_e4m3(cv, sv);
-        uint8_t* q = P.c4q + row * kC4Bytes;
-        *reinterpret_cast<uint2*>(q + off) = qk;
-        *reinterpret_cast<uint2*>(q + kRow + off) = qv;
-        if ((tid & 15) == 0) {
-          const int hp = 4 * (h & 3) + (h >> 2);   // the order attention lanes read
-          P.c4s[row * kC4Scales + hp] = sk;
-          P.c4s[row * kC4Scales + kH + hp] = sv;
-        }
-      } else {
-        uint4 ok, ov;
-        ok.x = pack_bf2(ck[0], ck[1]); ok.y = pack_bf2(ck[2], ck[3]);
-        ok.z = pack_bf2(ck[4], ck[5]); ok.w = pack_bf2(ck[6], ck[7]);
-        ov.x = pack_bf2(cv[0], cv[1]); ov.y = pack_bf2(cv[2], cv[3]);
-        ov.z = pack_bf2(cv[4], cv[5]); ov.w = pack_bf2(cv[6], cv[7]);
-        *reinterpret_cast<uint4*>(csa_k + (int64_t)slot * kRow + off) = ok;
-        *reinterpret_cast<uint4*>(csa_v + (int64_t)slot * kRow + off) = ov;
-      }
-    }
+    // C4 entry (tokens tb .. tb+3) after the HCA update, so the packed tokens are
+    // dead while an FP8 entry is quantised
+    if constexpr (C4) c4_pool_store<FP8>(P, (int64_t)id * kC4 + (tb >> 2), kw, vw, gc);
   }
 }
 

@@ -47,8 +47,21 @@ __device__ __forceinline__ int keys_a(const Pools& P, const Req& r) {
 // four-launch form the HCA entry of the block sealed now (layers with HCA entries;
 // the three-launch form takes that key in the merge).
 __device__ __forceinline__ int keys_b(const Pools& P, const Req& r, int32_t k, int32_t fused) {
-  const int nc = P.c4 ? kC4 * r.nb : 0;
+  const int nc = c4_cands(P.c4, P.eager, r);
   return (fused || !P.hca ? 0 : sealed_now(r)) + (k < nc ? k : nc);
+}
+
+// Eager C4: the open block's unit (lb == R.nb): keys from the indexer tail, the
+// newest token's from the input; entries past the block's complete groups score -inf.
+__device__ __forceinline__ void score_open_unit(const Pools& P, const ReqBatch& B, const StepArgs& S,
+                                                int r, int t0) {
+  const Req R = B.r[r];
+  float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * R.nb + t0 / 4;
+  const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
+  const float* inrow = S.iin + (int64_t)r * kIRow;
+  const int newest = R.len - 1 - kBlk * R.nb;   // the input token's slot in the block
+  score_block<8 / kScoreSplit>([&](int t) { return t0 + t == newest ? inrow : tail + (t0 + t) * kIRow; },
+                               S.qi + (int64_t)r * kIRow, out, open_groups(1, R) - t0 / 4);
 }
 
 // Indexer scores of scoring unit `unit` (fp32 keys): 128 / kScoreSplit tokens of one
@@ -61,6 +74,10 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
   const int lb = u / kScoreSplit;
   const int t0 = kTok * (u % kScoreSplit);
   const Req R = B.r[r];
+  if (lb == R.nb) {   // eager C4: the open block
+    score_open_unit(P, B, S, r, t0);
+    return;
+  }
   float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb + t0 / 4;
   const float* qrow = S.qi + (int64_t)r * kIRow;
   if (R.aux >= 0 && lb == R.nb - 1) {
@@ -80,6 +97,7 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
     score_block<8 / kScoreSplit>([&](int t) { return blk + t * kIRow; }, qrow, out);
   }
 }
+
 
 // Indexer scores of scoring unit `unit` with MXFP4 keys: sealed blocks
 // [u G, u G + G) of one request (G = S.mx_unit), two blocks' loads in flight at a
@@ -160,6 +178,15 @@ __global__ __launch_bounds__(256, FP8 ? 3 : 4) void k_step1(Pools P, ReqBatch B,
     return;
   }
   bid -= B.n;
+  // -- eager C4: the entry of the open block's group this token completes
+  if (bid < B.n_open) {
+    const int ri = B.open_req[bid];
+    const Req R = B.r[ri];
+    open_entry(P, R.state, R.nb, open_groups(1, R) - 1, R.len - 1, S.kin + (int64_t)ri * kRow,
+               S.vin + (int64_t)ri * kRow);
+    return;
+  }
+  bid -= B.n_open;
   // -- indexer scores, one workgroup per unit (a 1/kScoreSplit block of fp32 keys,
   //    or S.mx_unit blocks of MXFP4 keys)
   if (bid < S.n_score) {
@@ -235,14 +262,15 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   const int w = bid - S.first_b[r];
   const int nch = S.first_b[r + 1] - S.first_b[r];
   const Req R = B.r[r];
-  const int N = P.c4 ? kC4 * R.nb : 0;
-  const int kk = min(S.k, N);
+  const int N = c4_rowlen(P.c4, P.eager, R);     // score-row length
+  const int nc = c4_cands(P.c4, P.eager, R);     // candidates
+  const int kk = min(S.k, nc);
   int a0, a1, b0, b1;
   chunk_range(keys_a(P, R), nch, w, a0, a1);
   chunk_range(kk, nch, w, b0, b1);
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
   SelPre<NT> pre;
-  sel_preload<NT>(N, S.scores + (int64_t)r * S.ld, tab, R.nb, pre);
+  sel_preload<NT>(N, S.scores + (int64_t)r * S.ld, tab, N / kC4, pre);
   __builtin_amdgcn_sched_barrier(0);   // the row's loads go out ahead of the key prefetch
 
   const uint16_t* ring_k = P.swa_k + (int64_t)R.state * P.n_win * kRow;
@@ -264,7 +292,7 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
     a.v = P.hca_v + (int64_t)id * kRow;
     return a;
   };
-  const int64_t max_row = (int64_t)P.max_blocks * kC4;
+  const int64_t max_row = (int64_t)P.c4_ids * kC4;   // blocks and (eager) open blocks
   auto key_b = [&](int x) {
     KeyAddr a;
     a.k = a.v = nullptr;
@@ -281,7 +309,7 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   auto stage = [&]() { select_stage<NT>(pre, sh.sel); };
   auto select = [&]() {
     select_lds<NT>(N, S.k, S.topk + r * k, S.score_out ? S.score_out + r * k : nullptr, sh.sel, sh.rows,
-                   SelWin{b0, b1, w == 0});
+                   SelWin{b0, b1, w == 0}, nc);
     __syncthreads();   // rows in LDS complete; the selection's LDS is free for attention
   };
   float M, L, A8[8];
@@ -339,7 +367,7 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
   chunk_range(keys_b(P, R, S.k, 0), nch, w, x0, x1);
   const int sn = P.hca ? sealed_now(R) : 0;
   const int32_t* rows = S.rows + (int64_t)r * S.k;
-  const int64_t max_row = (int64_t)P.max_blocks * kC4;
+  const int64_t max_row = (int64_t)P.c4_ids * kC4;   // blocks and (eager) open blocks
   auto key_b = [&](int x) {
     KeyAddr a;
     a.k = a.v = nullptr;
@@ -381,7 +409,7 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
 
 hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = kSealSplit * B.n_seal + B.n + S.n_score;
+  const int grid = kSealSplit * B.n_seal + B.n + B.n_open + S.n_score;
   if (grid == 0) return hipSuccess;
   const dim3 g(grid), t(kAttnWaves * 64);
   if (!P.c4) return launch_k(k_step1<false, false>, g, t, st, ev, P, B, S);

@@ -83,7 +83,19 @@ typedef struct hsa_config {
                                    Block Cache; 0 means 1                           */
   const int32_t* layer_types;   /* host [n_layers] HSA_LAYER_*, copied; NULL: every
                                    layer HSA_LAYER_MIXED                            */
+  int32_t c4_mode;              /* HSA_C4_SEALED or HSA_C4_EAGER                    */
+  int32_t reserved;             /* 0                                                */
 } hsa_config;
+
+/* When C4 entries exist. SEALED: a block's 32 entries are written when its 128 tokens
+ * are complete ([Q&A] §3.1 block-level sealing). EAGER: each complete group of 4
+ * tokens of the open block (L mod 4 = 0, the CSA tail of [Q&A] §3.1) has its entry
+ * at once, pooled as the seal pools it (bit-identical), kept in the State; the
+ * open block's g = (L mod 128) / 4 entries (32 with a deferred full tail) are top-k
+ * candidates with ordinals 32 nb .. 32 nb + g - 1, scored from the indexer tail, and
+ * attention keys when selected. EAGER takes bf16 entries and fp32 indexer keys. */
+#define HSA_C4_SEALED 0
+#define HSA_C4_EAGER 1
 
 /* Layer types ([Ch12] Figure 12-1: per request one State quota over all layers - SWA
  * layers, CSA state, HCA state - and per block the layers' compressed KV - CSA
