@@ -72,14 +72,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CACHE_N = 4096                 # score rows up to this length are selected in LDS
 
 
-def step_fused(nb: np.ndarray) -> bool:
+def step_fused(nb: np.ndarray, open_g=None) -> bool:
     """Whether the library runs this step in three launches: every score row fits the
-    selection's LDS cache (unless HSA_STEP_FUSED=0)."""
-    return os.environ.get("HSA_STEP_FUSED", "1") != "0" and bool((32 * nb <= CACHE_N).all())
+    selection's LDS cache (unless HSA_STEP_FUSED=0). open_g: eager C4 open groups."""
+    rows = 32 * (nb + (open_g > 0 if open_g is not None else 0))
+    return os.environ.get("HSA_STEP_FUSED", "1") != "0" and bool((rows <= CACHE_N).all())
 
 
 def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray,
-               entries: str = "bf16", index: str = "f32", layer: str = "mixed") -> dict:
+               entries: str = "bf16", index: str = "f32", layer: str = "mixed", c4_mode: str = "sealed") -> dict:
     """Bytes the method must move in one decode step, per launch (scratch excluded).
 
     L_after: lengths after the append; nb: sealed blocks after it; sealed: 1 where
@@ -90,14 +91,20 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
         return layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer)
     C4 = c4_bytes(entries)
     SEAL = seal_bytes(entries, index)
-    scan = (nb - sealed) * idx_bytes(index) + sealed * IDX_BLOCK
+    # eager C4: the open block's g entries are candidates too; its 4g tokens' indexer
+    # keys are scanned, and a step that completes a group reads 3 ring tokens and
+    # writes the entry
+    g = (L_after - 128 * nb) // 4 if c4_mode == "eager" else 0 * nb
+    done = ((L_after % 4 == 0) & (L_after % 128 != 0)) if c4_mode == "eager" else 0 * nb
+    scan = (nb - sealed) * idx_bytes(index) + sealed * IDX_BLOCK + 4 * g * 1024
     swa = np.minimum(L_after, n_win)
-    kk = np.minimum(k, 32 * nb)
+    kk = np.minimum(k, 32 * nb + g)
     B = len(L_after)
-    if step_fused(nb):
+    eager_b = int((done * (3 * ROW + ROW)).sum())
+    if step_fused(nb, g):
         out = {
             "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL - ROW)
-                         + scan.sum() + B * 1024),
+                         + scan.sum() + B * 1024) + eager_b,
             # S2 (three-launch form): top-k out; HCA entries of new blocks; K/V rows
             # of the SWA tokens, earlier HCA entries and selected C4 entries + the query
             "step2": int((kk * 8).sum() + sealed.sum() * ROW
@@ -114,7 +121,7 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
         # HCA entry written in S2); indexer keys of every sealed block + the
         # indexer query
         "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL - ROW)
-                     + scan.sum() + B * 1024),
+                     + scan.sum() + B * 1024) + eager_b,
         # S2: top-k ordinals (and scores) out; HCA entries of new blocks; K/V rows
         # of the SWA tokens and earlier HCA entries + the query
         "step2": int((kk * 8).sum() + sealed.sum() * ROW
@@ -208,7 +215,7 @@ def layer_seed(wl, layer: int) -> int:
 
 
 def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", index: str = "f32",
-                 layers=None):
+                 layers=None, c4_mode: str = "sealed"):
     """Cache holding `copies` identical instances of the batch, every request
     prefilled to L0 (bulk appends of device-generated tokens; in a prefix workload
     each request forks off its group's parent at its fork length, sharing those
@@ -230,7 +237,7 @@ def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", i
     n_parents = wl.n_groups if wl.prefix_len else 0
     cache = hsa.Cache(wl.n_win, copies * (B + n_parents), max_blocks + copies * n_parents * (wl.prefix_len // 128),
                       Wc, Wh, max_blocks_per_state=max_len // 128 + 2, entry_format=entries,
-                      index_format=index, layer_types=layers)
+                      index_format=index, layer_types=layers, c4_mode=c4_mode)
     if layers and wl.prefix_len:
         raise SystemExit("layer stacks are measured on workloads without shared prefixes")
     inst = []
@@ -293,7 +300,7 @@ def run_decode(args) -> dict:
     # a layer stack streams different data layer after layer by itself: one copy
     R = args.copies if args.copies is not None else (4 if wl.name == "b32" and not layers else 1)
     local_steps = (W + 2 * K + R - 1) // R
-    cache, inst = setup_decode(wl, local_steps, R, args.entries, args.index, layers)
+    cache, inst = setup_decode(wl, local_steps, R, args.entries, args.index, layers, args.c4_mode)
     L0 = wl.prefill.astype(np.int64)
     inp = [decode_inputs(wl, L0, local_steps, seed=layer_seed(wl, l)) for l in range(len(types))]
     topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
@@ -323,7 +330,9 @@ def run_decode(args) -> dict:
     cache.timing_enable([])
     dominant = args.kernel or max(STEP_KERNELS, key=lambda n: warm[n][0])
     # the byte split assumes the library's choice of form; check it against the launches
-    fused_steps = [step_fused((L0 + t // R + 1) // 128) for t in range(half, W)]
+    def open_g(L):
+        return (L - 128 * (L // 128)) // 4 if args.c4_mode == "eager" else None
+    fused_steps = [step_fused((L0 + t // R + 1) // 128, open_g(L0 + t // R + 1)) for t in range(half, W)]
     if W > half and (warm["step3"][1] == 0) != all(fused_steps):
         raise RuntimeError("decode-step form differs from the one the byte split assumes")
 
@@ -356,7 +365,7 @@ def run_decode(args) -> dict:
             nb = L_after // 128
             sealed = (L_after % 128 == 0).astype(np.int64)
             for typ in types:
-                sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index, typ)
+                sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index, typ, args.c4_mode)
                 for n in acc:
                     acc[n] += sb[n]
         return acc
@@ -383,7 +392,8 @@ def run_decode(args) -> dict:
     metric = METRIC if wl.name == "b32" else f"decode tokens/s + achieved HBM GB/s, append+attend, {wl.name}"
     stack = f", {len(types)}-layer stack ({args.layers} x {args.layer_repeat})" if layers else ""
     res = {
-        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", MXFP4 indexer keys" if mx4 else "") + stack,
+        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", MXFP4 indexer keys" if mx4 else "") + stack
+                  + (", eager C4" if args.c4_mode == "eager" else ""),
         "value": B * K / (ms_total * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -404,7 +414,7 @@ def run_decode(args) -> dict:
                                f"copies of the cache",
                    "batch": B, "n_win": wl.n_win, "topk": k, "kv_dtype": "bf16",
                    "c4_entries": args.entries, "index_keys": args.index, "cache_copies": R,
-                   "layers": types,
+                   "layers": types, "c4_mode": args.c4_mode,
                    "L0_mean": float(L0.mean()), "parallelism": "single GPU"},
         "hbm_gbps": step_gbs,
         "hbm_frac_of_peak": step_gbs / PEAK_HBM_GBS,
@@ -763,6 +773,8 @@ def main():
                     help="a layer stack: comma-separated types (mixed, swa, csa, hca), each step "
                          "runs every layer")
     ap.add_argument("--layer-repeat", type=int, default=1, help="repeat the --layers pattern")
+    ap.add_argument("--c4-mode", default="sealed", choices=["sealed", "eager"],
+                    help="when C4 entries exist: at block seal, or at every completed group of 4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--counters", default=None, help="comma-separated rocprofv3 --pmc output dirs")
@@ -788,7 +800,7 @@ def main():
         return
     res = run_bulk(args) if args.workload == 4 else run_decode(args)
     if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16" \
-            and args.index == "f32" and not args.layers:
+            and args.index == "f32" and not args.layers and args.c4_mode == "sealed":
         res["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(res), flush=True)
 
