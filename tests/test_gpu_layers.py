@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import Oracle
+from oracle import Oracle, e4m3_decode
 from tests.gpu_util import bf16_to_f64, dev_queries, dev_tokens, host_queries, host_tokens, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -41,15 +41,24 @@ def _stack(seed):
 
 
 def _check_layer(cache, o, states, t):
+    fp8, mx4 = cache.entry_format == "fp8", cache.index_format == "mxfp4"
     for s in states:
         assert cache.block_table(s) == o.table(s)
         for b in cache.block_table(s):
             g = cache.export_block(b)
             r = o.block(b)
-            assert ("csa_k" in g) == (t in ("csa", "mixed")) and ("hca_k" in g) == (t in ("hca", "mixed"))
-            if t in ("csa", "mixed"):
+            c4 = t in ("csa", "mixed")
+            assert (("csa_k" in g) or ("csa_k_codes" in g)) == c4 and ("hca_k" in g) == (t in ("hca", "mixed"))
+            if c4 and fp8:
+                for n in ("k", "v"):
+                    val = e4m3_decode(g[f"csa_{n}_codes"]) * g[f"csa_{n}_scale"][..., None].astype(np.float64)
+                    assert rel_l2(val, getattr(r, f"csa_{n}")) <= TOL, (t, n)
+            elif c4:
                 for n in ("csa_k", "csa_v"):
                     assert rel_l2(bf16_to_f64(g[n]), getattr(r, n)) <= TOL, (t, n)
+            if c4 and mx4:
+                assert np.array_equal(g["idx_codes"], r.idx_codes) and np.array_equal(g["idx_scales"], r.idx_scales)
+            elif c4:
                 assert np.array_equal(g["idx"], r.idx)
             if t in ("hca", "mixed"):
                 for n in ("hca_k", "hca_v"):
@@ -66,8 +75,12 @@ def _check_layer(cache, o, states, t):
                 assert np.array_equal(ex["idx_tail"][(L - len(st.tail) + i) % 128], ki)
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
-def test_layers_match_per_layer_oracles(monkeypatch, fused):
+MODES = [("1", "bf16", "f32", "sealed"), ("0", "bf16", "f32", "sealed"), ("1", "fp8", "f32", "sealed"),
+         ("0", "bf16", "mxfp4", "sealed"), ("1", "bf16", "f32", "eager"), ("0", "bf16", "f32", "eager")]
+
+
+@pytest.mark.parametrize("fused,entries,index,c4_mode", MODES)
+def test_layers_match_per_layer_oracles(monkeypatch, fused, entries, index, c4_mode):
     import torch
     import heterogeneous_sparse_attention_amd as hsa
     monkeypatch.setenv("HSA_STEP_FUSED", fused)
@@ -76,8 +89,9 @@ def test_layers_match_per_layer_oracles(monkeypatch, fused):
     B = 6
     L0 = np.array([1, 127, 128, 300, 700, 1100])
     nbk = int((L0 + 140).sum() // 128 + B)
-    cache = hsa.Cache(128, B, nbk, Wc, Wh, layer_types=TYPES)
-    orc = [Oracle(128, g[0], g[1], B, nbk, layer_type=t) for g, t in zip(gates, TYPES)]
+    kw = dict(entry_format=entries, index_format=index, c4_mode=c4_mode)
+    cache = hsa.Cache(128, B, nbk, Wc, Wh, layer_types=TYPES, **kw)
+    orc = [Oracle(128, g[0], g[1], B, nbk, layer_type=t, **kw) for g, t in zip(gates, TYPES)]
     st = [cache.state_alloc() for _ in range(B)]
     for o in orc:
         assert [o.state_alloc() for _ in range(B)] == st
