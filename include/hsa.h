@@ -12,10 +12,17 @@
  *                tokens, each holding 32 CSA (C4) entries, 1 HCA entry and the
  *                128 tokens' indexer keys.
  *
+ * Options at create time: a stack of layers of four types over one State quota
+ * and one Block Cache (HSA_LAYER_*), FP8 C4 entries (HSA_ENTRY_FP8), MXFP4 indexer
+ * keys (HSA_INDEX_MXFP4) and eager C4 entries of the open block (HSA_C4_EAGER).
+ * Prefix hits under the pages' three SWA policies are built from hsa_block_ref,
+ * hsa_prefix_attach, hsa_state_write and State checkpoints.
+ *
  * Pages cited (by title and section):
  *   [Q&A]    "V4 为何要分池？块对齐与尾缓冲怎么配合？" (deepseek-tech-notes)
  *   [Layout] "V4 KV Layout：Classical + State 双池" (deepseek-tech-notes)
  *   [Ch12]   "Ch 12 · 推理框架 — KV 的异构调度" (DeepSeek-V4-book)
+ *   [Disk]   "V4 磁盘 Prefix Cache" (deepseek-tech-notes)
  *
  * Conventions for every call:
  *   - Shapes are fixed: 16 heads x 128 bf16 for K/V/Q, 4 heads x 64 fp32 for
