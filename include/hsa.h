@@ -211,8 +211,8 @@ hsa_status hsa_compress_flush(hsa_ctx* ctx, int32_t n_req, const int32_t* states
  * (bad ids, src == dst), STATE (dst not empty, src has a pending seal). */
 hsa_status hsa_block_table_share(hsa_ctx* ctx, int32_t src, int32_t dst, void* stream);
 
-/* ---- prefix hits under the three SWA policies ([Ch12] "Ch 12" §3.1 and the
- * "V4 磁盘 Prefix Cache" page, SWA policies: Full / Periodic Checkpointing / Zero).
+/* ---- prefix hits under the three SWA policies ([Ch12] §3.1; [Disk] SWA
+ * policies: Full / Periodic Checkpointing / Zero).
  * A prefix entry holds the prefix's sealed blocks by reference (hsa_block_ref) and,
  * by policy, State checkpoints. A hit makes a fresh state from it:
  *   Zero      hsa_prefix_attach, then hsa_state_write of the prefix's tokens
