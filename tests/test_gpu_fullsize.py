@@ -158,16 +158,23 @@ def check_golden_rows(gold, b, t, idx, out):
 
 # ------------------------------------------------------------------ b32
 
-def test_b32_every_step_against_oracle():
+B32_MODES = [("bf16", "f32", "sealed", 64), ("fp8", "mxfp4", "sealed", 16), ("bf16", "f32", "eager", 16)]
+
+
+@pytest.mark.parametrize("entries,index,c4_mode,steps", B32_MODES)
+def test_b32_every_step_against_oracle(entries, index, c4_mode, steps):
+    """Every step of every request; besides the measured storage, the pages' own
+    (FP8 entries, MXFP4 indexer keys) and eager C4 for 16 steps each."""
     import bench
     wl = make(2)
     B, k = wl.batch, wl.topk
     L0 = wl.prefill.astype(np.int64)
-    cache, inst = bench.setup_decode(wl, wl.decode_steps, 1)
+    cache, inst = bench.setup_decode(wl, steps, 1, entries, index, None, c4_mode)
     states = inst[0]
-    say(f"b32: prefilled {int(L0.sum())} tokens on the GPU")
+    say(f"b32 ({entries}, {index}, {c4_mode}): prefilled {int(L0.sum())} tokens on the GPU")
     Wc, Wh = synth.gate_weights(wl.seed)
-    o = Oracle(wl.n_win, Wc, Wh, B, int(((L0 + wl.decode_steps) // BLOCK).sum()) + B)
+    o = Oracle(wl.n_win, Wc, Wh, B, int(((L0 + steps) // BLOCK).sum()) + B, entry_format=entries,
+               index_format=index, c4_mode=c4_mode)
     srcs = [RequestTokens(2, b) for b in range(B)]
     ost = []
     for b in range(B):
@@ -190,10 +197,10 @@ def test_b32_every_step_against_oracle():
             assert r <= TOL, (t, b, r)
             worst[0] = max(worst[0], r)
 
-    run_steps(cache, states, wl, L0, wl.decode_steps, on_step)
+    run_steps(cache, states, wl, L0, steps, on_step)
     for b in range(B):
-        check_info(cache, states[b], int(L0[b]) + wl.decode_steps)
-    say(f"b32: {wl.decode_steps} steps x {B} requests match; worst rel L2 {worst[0]:.2e}")
+        check_info(cache, states[b], int(L0[b]) + steps)
+    say(f"b32: {steps} steps x {B} requests match; worst rel L2 {worst[0]:.2e}")
     cache.close()
 
 
