@@ -201,6 +201,10 @@ struct StepArgs {
   int32_t n_b;           // part-B workgroups
   int32_t fused;         // 1: three launches, part B selects for itself (rows <= kCacheN)
   int32_t mx_unit;       // MXFP4 keys: sealed blocks per scoring workgroup (0: fp32 keys)
+  int32_t a_only;        // a layer without C4 entries: part A only, the new HCA key in the
+                         // merge, padding top-k rows
+  int32_t s2_append;     // S1 is not launched: S2 appends the tokens (and part A reads the
+                         // newest from the input)
   SelPlan sel;           // top-k workgroups of the four-launch form (long rows are sliced)
   int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
   int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])

@@ -413,10 +413,11 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     // three launches when every score row fits the selection's LDS cache (and the
     // top-k is wanted in ordinal order): every attention workgroup then selects for
     // itself and the new HCA key joins the merge
-    // (a layer without C4 entries has empty rows: always three launches, its top-k
-    // rows all padding)
+    // A layer without C4 entries needs no selection and no part B: part A only, the
+    // new HCA key in the merge, padding top-k rows, and no S1 when nothing seals.
     const bool c4 = c->P.c4 != 0, hca = c->P.hca != 0;
-    bool fused = !c4 || (c->step_fused != 0 && !(flags & HSA_TOPK_SORTED));
+    const bool a_only = !c4;
+    bool fused = !a_only && c->step_fused != 0 && !(flags & HSA_TOPK_SORTED);
     for (int i = 0; i < n; ++i)
       fused = fused && h_rowlen(c->P, plan.reqs[b0 + i].len_new, plan.reqs[b0 + i].nb_new) <= kCacheN;
     std::vector<int64_t> na(n), nb(n);
@@ -436,7 +437,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
       if (id >= 0 && (c4 || hca)) B.seal_req[B.n_seal++] = (int8_t)i;   // an SWA layer seals nothing
       const int64_t sealed = id >= 0 ? 1 : 0;
       na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + (hca ? r.nb_new - sealed : 0);
-      nb[i] = (fused || !hca ? 0 : sealed) + std::min<int64_t>(k, h_cands(c->P, r.len_new, r.nb_new));
+      nb[i] = (fused || !hca || a_only ? 0 : sealed) + std::min<int64_t>(k, h_cands(c->P, r.len_new, r.nb_new));
       maxnb = std::max<int64_t>(maxnb, h_rowlen(c->P, r.len_new, r.nb_new) / kC4);
       // eager C4: the open block is scored too, and a completed group gets its entry
       const bool open = h_open(c->P, r.len_new, r.nb_new) > 0;
@@ -457,9 +458,11 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
     S.fused = fused ? 1 : 0;
     S.mx_unit = mx_unit;
+    S.a_only = a_only ? 1 : 0;
+    S.s2_append = a_only && B.n_seal == 0 ? 1 : 0;
     S.n_score = (int32_t)n_score;
     int s = kOk;
-    if (!fused) {
+    if (!fused && !a_only) {
       s = plan_select(c, B, k, S.sel);
       if (s) return s;
     }
@@ -472,6 +475,9 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     if (fused) {
       balance_wgs({&pb}, c->step_slots - B.n_seal);
       pa.wgs.assign(n, 0);
+    } else if (a_only) {
+      balance_wgs({&pa}, c->step_slots - B.n_seal - (S.s2_append ? n : 0));
+      pb.wgs.assign(n, 0);
     } else {
       balance_wgs({&pa}, c->step_slots - S.sel.n_wgs - B.n_seal);
       balance_wgs({&pb}, c->step_slots);
@@ -509,7 +515,7 @@ int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const
     S.part_acc = c->part_acc;
     S.part_ml = c->part_ml;
     S.seal_part = c->seal_part;
-    {
+    if (!S.s2_append) {
       Timed t(c, HSA_KERNEL_STEP1, st);
       HIP_TRY(launch_step1(c->P, B, S, st, t.ev()));
     }

@@ -218,6 +218,11 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
     KeyAddr a;
     a.k = a.v = nullptr;
     if (x < swa) {
+      if (S.s2_append && p0 + x == R.len - 1) {   // being appended in this launch: from the input
+        a.k = S.kin + (int64_t)r * kRow;
+        a.v = S.vin + (int64_t)r * kRow;
+        return a;
+      }
       const int64_t slot = (p0 + x) % P.n_win;
       a.k = ring_k + slot * kRow;
       a.v = ring_v + slot * kRow;
@@ -329,6 +334,16 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
     }
     bid -= S.n_b;
   } else {
+    // a layer without C4 entries whose step seals nothing skips S1: its appends
+    // come first. The slot a token is written to holds a position outside every
+    // window of this step (or none), so part A's reads do not race with it.
+    if (S.s2_append) {
+      if (bid < B.n) {
+        if (threadIdx.x < 256) append_token<false>(P, B.r[bid], bid, S.kin, S.vin, S.iin);
+        return;
+      }
+      bid -= B.n;
+    }
     if (bid < S.sel.n_wgs) {
       select_round1<kStep2Threads>(bid, B.n, B.r, S.sel, S.k, S.sorted, S.scores, S.ld, S.topk,
                                    S.score_out, sh.sel, P.table, P.table_stride, S.rows);
@@ -398,7 +413,12 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
   const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
   const Req R = B.r[r];
   ExtraKey xk{nullptr, nullptr, nullptr};
-  if (S.fused && R.aux >= 0 && P.hca)   // the HCA entry of the block sealed now, merged in S2
+  if (S.a_only && (blockIdx.x & 3) == 0)   // no C4 entries: the top-k row is padding
+    for (int i = threadIdx.x; i < S.k; i += 256) {
+      S.topk[(int64_t)r * S.k + i] = -1;
+      if (S.score_out) S.score_out[(int64_t)r * S.k + i] = -INFINITY;
+    }
+  if ((S.fused || S.a_only) && R.aux >= 0 && P.hca)   // the HCA entry of the block sealed now, merged in S2
     xk = ExtraKey{P.hca_k + (int64_t)R.aux * kRow, P.hca_v + (int64_t)R.aux * kRow,
                   S.q + (int64_t)r * kRow};
   merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
@@ -419,7 +439,7 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
-  const int grid = (S.fused ? S.n_b : S.sel.n_wgs) + B.n_seal + S.n_a;
+  const int grid = (S.fused ? S.n_b : S.sel.n_wgs) + B.n_seal + S.n_a + (S.s2_append ? B.n : 0);
   if (grid == 0) return hipSuccess;
   return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
 }
