@@ -317,23 +317,34 @@ def run_decode(args) -> dict:
             cache.decode_step(inst[t % R], x["k"][j], x["v"][j], x["ki"][j], x["q"][j],
                               x["qi"][j], k, topk_out=topk, out=out)
 
-    # warmup; its second half also times every kernel to find the dominant one
+    # warmup; its second half times one kernel per step, in rotation, with the steps
+    # back to back, to find the dominant one. (With an event pair on every kernel of
+    # a step, the first kernel's start event can fire while the host is still
+    # writing that kernel's dispatch, which inflates it whenever the host falls
+    # behind; the roofline pass below also times one kernel only.)
     half = W // 2
     for t in range(half):
         step(t)
     torch.cuda.synchronize()
-    cache.timing_enable(list(STEP_KERNELS))
-    for t in range(half, W):
+    order = ("step2", "step1", "step3", "step4", "step2b")
+    timed_at = {n: [] for n in STEP_KERNELS}
+    for j, t in enumerate(range(half, W)):
+        n = order[j % len(order)]
+        cache.timing_enable([n])
+        timed_at[n].append(t)
         step(t)
     torch.cuda.synchronize()
     warm = cache.timing_read()
     cache.timing_enable([])
-    dominant = args.kernel or max(STEP_KERNELS, key=lambda n: warm[n][0])
+    per_step = {n: warm[n][0] / len(timed_at[n]) if timed_at[n] else 0.0 for n in STEP_KERNELS}
+    dominant = args.kernel or max(STEP_KERNELS, key=lambda n: per_step[n])
     # the byte split assumes the library's choice of form; check it against the launches
     def open_g(L):
         return (L - 128 * (L // 128)) // 4 if args.c4_mode == "eager" else None
-    fused_steps = [step_fused((L0 + t // R + 1) // 128, open_g(L0 + t // R + 1)) for t in range(half, W)]
-    if W > half and (warm["step3"][1] == 0) != all(fused_steps):
+    def fused_at(t):
+        return step_fused((L0 + t // R + 1) // 128, open_g(L0 + t // R + 1))
+    has_c4 = any(ty in ("mixed", "csa") for ty in types)   # layers with a part B
+    if timed_at["step3"] and (warm["step3"][1] > 0) != (has_c4 and not all(map(fused_at, timed_at["step3"]))):
         raise RuntimeError("decode-step form differs from the one the byte split assumes")
 
     # timed pass 1 (value): whole steps between two events, nothing inside
@@ -428,7 +439,7 @@ def run_decode(args) -> dict:
                      "algorithmic_bytes_per_launch": (bytes_2[dominant] / dom_n) if dom_n else None,
                      "measured": f"HIP event pair attached to each {KERNEL_SYMBOL[dominant]} "
                                  f"dispatch (hipExtLaunchKernel) over {K} further steps"},
-        "kernels_us_per_step": {n: warm[n][0] / max(1, W - half) * 1e3 for n in STEP_KERNELS},
+        "kernels_us_per_step": {n: per_step[n] * 1e3 for n in STEP_KERNELS},
         "bytes_per_step_by_kernel": {n: bytes_1[n] / K for n in STEP_KERNELS},
     }
     cache.close()
