@@ -87,7 +87,10 @@ def test_layers_match_per_layer_oracles(monkeypatch, fused, entries, index, c4_m
     seed = 0x1A7
     gates, Wc, Wh = _stack(seed)
     B = 6
-    L0 = np.array([1, 127, 128, 300, 700, 1100])
+    # decode steps: request 0 inside its first window, the others past it (ring
+    # wrap); requests 3 and 4 seal a block at the second step (lengths 256, 768), so
+    # an HCA layer's step then runs its seal launch and the others skip it
+    L0 = np.array([1, 127, 128, 254, 766, 1100])
     nbk = int((L0 + 140).sum() // 128 + B)
     kw = dict(entry_format=entries, index_format=index, c4_mode=c4_mode)
     cache = hsa.Cache(128, B, nbk, Wc, Wh, layer_types=TYPES, **kw)
