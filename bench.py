@@ -590,10 +590,10 @@ def run_hits(args) -> dict:
         e0.record()
         cache.prefix_attach(states, flat, P, offsets=off[grp])
         if pol in ("periodic", "full"):
-            for b, s in enumerate(states):
-                at = int(c[b]) if pol == "periodic" else int(P[b])
-                if at > 0:
-                    cache.state_restore(s, ck[(int(grp[b]), at)], at)
+            at = [int(c[b]) if pol == "periodic" else int(P[b]) for b in range(B)]
+            rb = [b for b in range(B) if at[b] > 0]
+            cache.state_restore_batch([states[b] for b in rb], [ck[(int(grp[b]), at[b])] for b in rb],
+                                      [at[b] for b in rb])
         if T:
             cache.state_write(states, cu, lo, K, V, KI)
         e1.record()
@@ -630,7 +630,7 @@ def run_hits(args) -> dict:
                    "parallelism": "single GPU"},
         "hbm_gbps": alg / (ms * 1e-3) / 1e9, "hbm_frac_of_peak": alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "bytes_per_step": alg,
-        "roofline": {"bound": "hbm", "kernel": "k_bulk_write" if T else "hipMemcpyAsync (restore)",
+        "roofline": {"bound": "hbm", "kernel": "k_bulk_write" if T else "k_copy_segs (restore)",
                      "achieved": (write_b / (wr_ms * 1e-3) / 1e9) if (T and wr_ms) else alg / (ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": ((write_b / (wr_ms * 1e-3) / 1e9) if (T and wr_ms) else alg / (ms * 1e-3) / 1e9)

@@ -95,6 +95,7 @@ SIGNATURES = {
     "hsa_checkpoint_bytes": [_P, _P],
     "hsa_state_checkpoint": [_P, _I32, _P, _P, _P],
     "hsa_state_restore": [_P, _I32, _P, _I64, _P],
+    "hsa_state_restore_batch": [_P, _I32, _P, _P, _P, _P],
     "hsa_mxfp4_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_timing_enable": [_P, _U32],
     "hsa_timing_read": [_P, _P, _P],
@@ -317,6 +318,19 @@ class Cache:
         nb = self.checkpoint_bytes()
         _check(_lib.hsa_state_restore(self._ctx, int(s), _dev(buf, torch.uint8, (nb,), "buf"), int(length),
                                       _stream(stream)), "hsa_state_restore")
+
+    def state_restore_batch(self, states, bufs, lengths, stream=None):
+        """hsa_state_restore of several states in one launch: states[i] takes the
+        checkpoint bufs[i] (a device uint8 tensor) taken at lengths[i]."""
+        import torch
+        nb = self.checkpoint_bytes()
+        st, stp = _host_i32(states)
+        ln, lnp = _host_i64(lengths)
+        if len(bufs) != st.size or ln.size != st.size:
+            raise ValueError("states, bufs and lengths must have the same length")
+        ptrs = (ctypes.c_void_p * max(1, st.size))(*[_dev(b, torch.uint8, (nb,), "bufs[i]").value for b in bufs])
+        _check(_lib.hsa_state_restore_batch(self._ctx, int(st.size), stp, ctypes.cast(ptrs, ctypes.c_void_p),
+                                            lnp, _stream(stream)), "hsa_state_restore_batch")
 
     # -- indexer top-k --------------------------------------------------------------
     def indexer_topk(self, states, q_idx, k: int, idx_out=None, score_out=None, sorted=False,

@@ -136,6 +136,37 @@ __global__ __launch_bounds__(256) void k_attach_rows(int32_t* table, int64_t str
     table[(int64_t)a.state * stride + j] = ids[a.off + j];
 }
 
+// Batched copy: chunk x belongs to the last segment whose first chunk is <= x
+// (counted 64 segments per ballot); its workgroup moves up to 64 KiB, every thread
+// with 16 loads in flight before its stores.
+__global__ __launch_bounds__(256) void k_copy_segs(const CopySeg* s, int32_t n, int64_t total) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t x = blockIdx.x; x < total; x += gridDim.x) {
+    int r = -1;
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + lane;
+      const int c = __popcll(__ballot(i < n && s[i].first <= x));
+      r = base + c - 1;
+      if (c < 64) break;
+    }
+    r = uniform(r);
+    const CopySeg d = s[r];
+    const int64_t base = (x - d.first) * kCopyChunk16;
+    const int64_t len = min((int64_t)kCopyChunk16, d.n16 - base);
+    const HSA_GLOBAL u32x4_v* src = as_global(reinterpret_cast<const u32x4_v*>(d.src + base));
+    HSA_GLOBAL u32x4_v* dst = as_global(reinterpret_cast<u32x4_v*>(d.dst + base));
+    if (len == kCopyChunk16) {   // a whole chunk: unguarded, so the words stay in registers
+      u32x4_v v[kCopyChunk16 / 256];
+#pragma unroll
+      for (int u = 0; u < kCopyChunk16 / 256; ++u) v[u] = src[threadIdx.x + u * 256];
+#pragma unroll
+      for (int u = 0; u < kCopyChunk16 / 256; ++u) dst[threadIdx.x + u * 256] = v[u];
+    } else {
+      for (int64_t w = threadIdx.x; w < len; w += 256) dst[w] = src[w];
+    }
+  }
+}
+
 // MXFP4 storage of indexer key rows (256 fp32 each), exactly as the seal stores
 // them: a wave per row, 4 rows per workgroup.
 __global__ __launch_bounds__(256) void k_mx4_rows(const float* x, int64_t n_rows, uint8_t* codes,
@@ -152,6 +183,12 @@ __global__ __launch_bounds__(256) void k_mx4_rows(const float* x, int64_t n_rows
 hipError_t launch_open_c4(const Pools& P, const OpenDesc* d, int32_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   return launch_k(k_open_c4, dim3((unsigned)n), dim3(256), st, LaunchEv{}, P, d);
+}
+
+hipError_t launch_copy_segs(const CopySeg* d, int32_t n, int64_t total, hipStream_t st) {
+  if (n <= 0 || total <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>(total, 8 * 256);   // grid-strided beyond 8 per CU
+  return launch_k(k_copy_segs, dim3((unsigned)grid), dim3(256), st, LaunchEv{}, d, n, total);
 }
 
 hipError_t launch_attach_rows(const Pools& P, const AttachDesc* d, int32_t n, const int32_t* ids,

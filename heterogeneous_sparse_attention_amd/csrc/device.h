@@ -169,6 +169,16 @@ struct OpenDesc {
   int32_t pad_;
 };
 
+// One contiguous copy of a batched restore: n16 16-byte words from src to dst, as
+// the launch's chunks [first, first + ceil(n16 / kCopyChunk16)).
+struct CopySeg {
+  const uint4* src;
+  uint4* dst;
+  int64_t n16;
+  int64_t first;
+};
+constexpr int kCopyChunk16 = 4096;   // 16-byte words per chunk (64 KiB, 16 per thread)
+
 // One state of a prefix attach: its table row takes ids[off .. off + nb).
 struct AttachDesc {
   int32_t state;

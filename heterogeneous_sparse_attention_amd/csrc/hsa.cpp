@@ -1002,6 +1002,63 @@ hsa_status hsa_state_restore(hsa_ctx* c, int32_t s_, const void* buf, int64_t ck
   return recompute_open(c, &s_, 1, s);   // eager C4: the open block's entries
 }
 
+hsa_status hsa_state_restore_batch(hsa_ctx* c, int32_t n, const int32_t* states, const void* const* bufs,
+                                   const int64_t* ckpt_lens, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (n < 0) return fail(kInvalid, "n must be >= 0");
+  if (n == 0) return kOk;
+  if (!states || !bufs || !ckpt_lens) return fail(kInvalid, "NULL argument");
+  int st = set_device(c);
+  if (st) return st;
+  std::vector<int32_t> seen(states, states + n);
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return fail(kInvalid, "a state appears twice");
+  const int64_t W = c->P.n_win;
+  const size_t ring = (size_t)W * kRow * 2;
+  std::vector<CopySeg> segs;
+  int64_t total = 0;
+  auto add = [&](const char* src, void* dst, size_t bytes) {
+    if (bytes == 0) return;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    segs.push_back(CopySeg{reinterpret_cast<const uint4*>(src), static_cast<uint4*>(dst), n16, total});
+    total += (n16 + kCopyChunk16 - 1) / kCopyChunk16;
+  };
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s_ = states[i];
+    if (!c->ctl.valid_state(s_)) return fail(kInvalid, "state not allocated");
+    if (ckpt_lens[i] < 0 || ckpt_lens[i] > c->ctl.len(s_))
+      return fail(kInvalid, "checkpoint is past the state's length");
+    if (!bufs[i] || reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0)
+      return fail(kInvalid, "checkpoint buffer is NULL or not 16-byte aligned");
+    // the kernel reads the buffer: device memory, or pinned host memory through its
+    // device address
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, bufs[i]) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(kInvalid, "checkpoint buffer is not device or pinned host memory");
+    }
+    const char* b = nullptr;
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) b = static_cast<const char*>(bufs[i]);
+    else if (a.type == hipMemoryTypeHost && a.devicePointer)
+      b = static_cast<const char*>(a.devicePointer) +
+          (static_cast<const char*>(bufs[i]) - static_cast<const char*>(a.hostPointer));
+    if (!b) return fail(kInvalid, "checkpoint buffer is not device or pinned host memory");
+    const int64_t slots = std::min<int64_t>(ckpt_lens[i], W), tail = ckpt_lens[i] % kBlk;
+    const size_t S = (size_t)s_;
+    add(b, c->P.swa_k + S * W * kRow, (size_t)slots * kRow * 2);
+    add(b + ring, c->P.swa_v + S * W * kRow, (size_t)slots * kRow * 2);
+    if (tail > 0 && c->P.c4) add(b + 2 * ring, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4);
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!segs.empty()) {
+    if (segs.size() > (size_t)INT32_MAX) return fail(kInvalid, "too many states");
+    st = upload_plan(c, segs.data(), segs.size() * sizeof(CopySeg), hs);
+    if (st) return st;
+    HIP_TRY(launch_copy_segs(static_cast<const CopySeg*>(c->plan_dev), (int32_t)segs.size(), total, hs));
+  }
+  return recompute_open(c, states, n, hs);   // eager C4: the open blocks' entries
+}
+
 hsa_status hsa_indexer_topk(hsa_ctx* c, int32_t n_req, const int32_t* states, const float* q_idx,
                             int32_t k, uint32_t flags, int32_t* idx_out, float* score_out,
                             void* stream) {

@@ -66,6 +66,8 @@ hipError_t launch_fp8_rows(const float* x, int64_t n_rows, uint8_t* codes, float
                            hipStream_t st);
 // Eager C4: recompute the listed open-block entries from the states' rings.
 hipError_t launch_open_c4(const Pools& P, const OpenDesc* d, int32_t n, hipStream_t st);
+// Batched copy of n segments (total chunks of 64 KiB), staged on the device.
+hipError_t launch_copy_segs(const CopySeg* d, int32_t n, int64_t total, hipStream_t st);
 // Table rows of states attached to a prefix (block ids staged on the device).
 hipError_t launch_attach_rows(const Pools& P, const AttachDesc* d, int32_t n, const int32_t* ids,
                               hipStream_t st);

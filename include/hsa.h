@@ -220,6 +220,7 @@ hsa_status hsa_block_table_share(hsa_ctx* ctx, int32_t src, int32_t dst, void* s
  *   Periodic  hsa_prefix_attach, hsa_state_restore of the latest checkpoint c <= len,
  *             then hsa_state_write of the tokens [c, len);
  *   Full      hsa_prefix_attach, then hsa_state_restore of the checkpoint at len.
+ * (hsa_state_restore_batch restores a whole batch of hits in one launch.)
  * Each gives the state, slot for slot, that hsa_block_table_share of a live request
  * at len gives; the shared blocks are never sealed again. Until its window is
  * filled that way, an attached state must not be read or appended to (the library
@@ -269,6 +270,17 @@ hsa_status hsa_state_checkpoint(hsa_ctx* ctx, int32_t state, void* buf, int64_t*
  * INVALID. */
 hsa_status hsa_state_restore(hsa_ctx* ctx, int32_t state, const void* buf, int64_t ckpt_len,
                              void* stream);
+
+/* hsa_state_restore of n distinct states in one copy launch (the Full and Periodic
+ * policies restore a whole batch of hits at once; same source as hsa_state_restore):
+ * state states[i] takes the checkpoint in bufs[i], taken at ckpt_lens[i]. states,
+ * bufs and ckpt_lens are host arrays of n; each bufs[i] is a checkpoint
+ * (hsa_checkpoint_bytes long, 16-byte aligned, owned by the caller) in device
+ * memory or in pinned host memory the device can read. Every argument is checked
+ * before anything is copied. Errors: INVALID (bad or repeated state, a length past
+ * the state's L, a NULL, misaligned or pageable host buffer). */
+hsa_status hsa_state_restore_batch(hsa_ctx* ctx, int32_t n, const int32_t* states,
+                                   const void* const* bufs, const int64_t* ckpt_lens, void* stream);
 
 /* Indexer top-k over each state's sealed C4 entries ([Ch12] 名词速通: the
  * indexer's K-only keys serve top-k selection; [Layout] Classical KV cache:

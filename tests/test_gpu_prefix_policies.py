@@ -156,3 +156,117 @@ def test_prefix_errors_change_nothing():
     with pytest.raises(hsa.HsaError):
         cache.state_restore(d, buf, 301)                 # checkpoint past L
     cache.close()
+
+
+@pytest.mark.parametrize("c4_mode", ["sealed", "eager"])
+def test_restore_batch_matches_single_restores(c4_mode):
+    """hsa_state_restore_batch: one launch for many states, each with its own
+    checkpoint (lengths inside and past the first window, with and without a tail),
+    equals one hsa_state_restore per state bit for bit, and the oracle's restore;
+    the next decode step agrees too (eager C4: the open blocks' entries recomputed)."""
+    import ctypes
+    import torch
+    import heterogeneous_sparse_attention_amd as hsa
+    seed = 0x5A7
+    W = 256
+    lens = [100, 256, 300, 700, 1000]
+    n = len(lens)
+    cache, o = new_pair(W, 3 * n + 2, 64, seed, c4_mode=c4_mode)
+    srcs, bufs, cks, blocks = [], [], [], []
+    for i, L in enumerate(lens):
+        s = cache.state_alloc()
+        assert s == o.state_alloc()
+        pos = np.arange(L)
+        cache.append_kv([s], [0, L], *dev_tokens(seed, i, pos))
+        o.append([s], [host_tokens(seed, i, pos)])
+        b, ln = cache.state_checkpoint(s)
+        assert ln == L
+        srcs.append(s), bufs.append(b), cks.append(o.checkpoint(s)), blocks.append(cache.block_table(s))
+    one = [cache.state_alloc() for _ in range(n)]
+    many = [cache.state_alloc() for _ in range(n)]
+    assert one + many == [o.state_alloc() for _ in range(2 * n)]
+    for group in (one, many):
+        for i, d in enumerate(group):
+            cache.prefix_attach(d, blocks[i], lens[i])
+            o.prefix_attach(d, blocks[i], lens[i])
+    for i, d in enumerate(one):
+        cache.state_restore(d, bufs[i], lens[i])
+    cache.state_restore_batch(many[::-1], bufs[::-1], lens[::-1])     # any order
+    for i in range(n):
+        o.restore(one[i], cks[i])
+        o.restore(many[i], cks[i])
+    for i in range(n):
+        ea, eb = cache.export_state(one[i]), cache.export_state(many[i])
+        L = lens[i]
+        for p in range(max(0, L - W), L):
+            assert np.array_equal(ea["swa_k"][p % W], eb["swa_k"][p % W]), (i, p)
+            assert np.array_equal(ea["swa_v"][p % W], eb["swa_v"][p % W]), (i, p)
+        assert np.array_equal(ea["idx_tail"][:L % 128], eb["idx_tail"][:L % 128]), i
+        if c4_mode == "sealed":
+            check_state(cache, o, many[i], many[i])
+    # pinned host memory: the kernel reads it through its device address
+    pinned = bufs[2].cpu().pin_memory()
+    st = np.array([many[2]], np.int32)
+    ln = np.array([lens[2]], np.int64)
+    ptr = (ctypes.c_void_p * 1)(pinned.data_ptr())
+    hsa._check(hsa._lib.hsa_state_restore_batch(cache._ctx, 1, st.ctypes.data_as(ctypes.c_void_p),
+                                                ctypes.cast(ptr, ctypes.c_void_p),
+                                                ln.ctypes.data_as(ctypes.c_void_p), None),
+               "hsa_state_restore_batch")
+    torch.cuda.synchronize()
+    ea, eb = cache.export_state(one[2]), cache.export_state(many[2])
+    for p in range(lens[2] - W, lens[2]):
+        assert np.array_equal(ea["swa_k"][p % W], eb["swa_k"][p % W]), p
+        assert np.array_equal(ea["swa_v"][p % W], eb["swa_v"][p % W]), p
+    assert np.array_equal(ea["idx_tail"][:lens[2] % 128], eb["idx_tail"][:lens[2] % 128])
+    # the next decode step of every pair agrees bit for bit
+    states = one + many
+    k = 24
+    keys = np.tile(np.arange(n), 2)
+    P = np.tile(np.array(lens), 2)
+    Kn, Vn, KIn = dev_tokens(seed, keys, P)
+    Q, QI = dev_queries(seed, keys, P)
+    sc = torch.empty((2 * n, k), dtype=torch.float32, device="cuda")
+    idx, _, out = cache.decode_step(states, Kn, Vn, KIn, Q, QI, k, score_out=sc)
+    gidx, gout, gsc = idx.cpu().numpy(), out.cpu().numpy(), sc.cpu().numpy()
+    for i in range(n):
+        assert np.array_equal(gidx[i], gidx[n + i]) and np.array_equal(gsc[i], gsc[n + i]), i
+        assert np.array_equal(gout[i], gout[n + i]), i
+    cache.close()
+
+
+def test_restore_batch_errors_change_nothing():
+    import ctypes
+    import heterogeneous_sparse_attention_amd as hsa
+    seed = 0x5A8
+    cache, _ = new_pair(128, 6, 16, seed)
+    a = cache.state_alloc()
+    cache.append_kv([a], [0, 300], *dev_tokens(seed, 1, np.arange(300)))
+    buf, n = cache.state_checkpoint(a)
+    blocks = cache.block_table(a)
+    d, e = cache.state_alloc(), cache.state_alloc()
+    cache.prefix_attach([d, e], blocks + blocks, [300, 300], offsets=[0, 0])
+    cache.state_restore(d, buf, 300)
+    before = cache.export_state(d)
+    with pytest.raises(hsa.HsaError):                    # a state twice
+        cache.state_restore_batch([e, e], [buf, buf], [300, 300])
+    with pytest.raises(hsa.HsaError):                    # past the state's length
+        cache.state_restore_batch([d, e], [buf, buf], [300, 301])
+    with pytest.raises(hsa.HsaError):                    # not an allocated state
+        cache.state_restore_batch([d, 5], [buf, buf], [300, 0])
+    host = np.zeros(cache.checkpoint_bytes(), np.uint8)  # pageable host memory
+    st = np.array([d], np.int32)
+    ln = np.array([300], np.int64)
+    ptr = (ctypes.c_void_p * 1)(host.ctypes.data)
+    assert hsa._lib.hsa_state_restore_batch(cache._ctx, 1, st.ctypes.data_as(ctypes.c_void_p),
+                                            ctypes.cast(ptr, ctypes.c_void_p),
+                                            ln.ctypes.data_as(ctypes.c_void_p), None) != 0
+    ptr = (ctypes.c_void_p * 1)(buf.data_ptr() + 8)      # misaligned
+    assert hsa._lib.hsa_state_restore_batch(cache._ctx, 1, st.ctypes.data_as(ctypes.c_void_p),
+                                            ctypes.cast(ptr, ctypes.c_void_p),
+                                            ln.ctypes.data_as(ctypes.c_void_p), None) != 0
+    after = cache.export_state(d)
+    for name in before:
+        assert np.array_equal(before[name].view(np.uint8), after[name].view(np.uint8)), name
+    cache.state_restore_batch([], [], [])                # nothing to do
+    cache.close()
