@@ -265,13 +265,14 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
   return incl - v;
 }
 
-// Top-k of one request's N scores S by one workgroup of NT threads. Radix select over the order-preserving keys finds
-// tau, the key of the kk-th entry under (score desc, ordinal asc), and `rem`,
-// how many entries equal to tau make the cut. One ordered pass then takes every
-// entry above tau and the first `rem` entries equal to tau, writing them in
-// ascending ordinal order (ballot + prefix counts). With `sorted`, the taken
-// entries are instead ordered by (score desc, ordinal asc) with a bitonic sort in
-// LDS.
+// Top-k of one request's N scores S by one workgroup of NT threads. Radix select
+// over the order-preserving keys finds tau, the key of the kk-th entry under (score
+// desc, ordinal asc), and `rem`, how many entries equal to tau make the cut (the
+// passes stop early once the bucket at the cut is taken whole; tau is then that
+// bucket's leading digits). One ordered pass then takes every entry above tau and
+// the first `rem` entries equal to tau, writing them in ascending ordinal order
+// (ballot + prefix counts). With `sorted`, the taken entries are instead ordered by
+// (score desc, ordinal asc) with a bitonic sort in LDS.
 // With `rows`, also writes each taken entry's physical C4 row (table[j / 32] * 32 +
 // j % 32) from the state's block table `tab` (nb_tab blocks), in ascending ordinal
 // order. The ordinal written for entry i is i + ord0, or ord_map[i] when a map is
@@ -358,14 +359,19 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         if (tid == dl) {
           sh.sh[0] = d;
           sh.sh[1] = (int)(base + ci - c);
+          sh.sh[2] = (int)c;
         }
       }
       __syncthreads();
       prefix |= (uint32_t)sh.sh[0] << shift;
       pmask |= dmask << shift;
       rem -= sh.sh[1];
+      if (sh.sh[2] == rem) break;   // every key of the cut's bucket is taken (uniform)
     }
-    const uint32_t tau = prefix;
+    // tau: the cut's digits so far (the keys under pmask); the later digits cannot
+    // change what is taken once the cut's bucket is taken whole
+    auto above = [&](uint32_t u) { return (u & pmask) > prefix; };
+    auto at_tau = [&](uint32_t u) { return (u & pmask) == prefix; };
     // ordered pass: take entries above tau and the first `rem` equal to tau; the
     // entries taken before i are (above tau before i) + min(equal before i, rem)
     const int lane = tid & 63, wv = tid >> 6;
@@ -393,8 +399,8 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         const uint32_t e[4] = {okey(v.x), okey(v.y), okey(v.z), okey(v.w)};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          gt_w += e[q] > tau;
-          eq_w += e[q] == tau;
+          gt_w += above(e[q]);
+          eq_w += at_tau(e[q]);
         }
       }
       int tot;
@@ -421,8 +427,8 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
           e[0] = okey(v.x); e[1] = okey(v.y); e[2] = okey(v.z); e[3] = okey(v.w);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            g += e[q] > tau;
-            q_eq += e[q] == tau;
+            g += above(e[q]);
+            q_eq += at_tau(e[q]);
           }
         }
         int g_tot, e_tot;
@@ -431,7 +437,7 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         if (j < j1) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const bool gt = e[q] > tau, eq = e[q] == tau;
+            const bool gt = above(e[q]), eq = at_tau(e[q]);
             if (gt || (eq && eb < rem)) take(4 * j + q, e[q], gb + min(eb, rem));
             gb += gt;
             eb += eq;
@@ -445,8 +451,8 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     for (int c0 = 0; cached && c0 < N; c0 += NT, parity ^= 1) {
       const int i = c0 + tid;
       const uint32_t u = i < N ? sh.keys[i] : 0u;
-      const bool gt = i < N && u > tau;
-      const bool eq = i < N && u == tau;
+      const bool gt = i < N && above(u);
+      const bool eq = i < N && at_tau(u);
       const unsigned long long bg = __ballot(gt), be = __ballot(eq);
       if (lane == 0) {
         sh.cnt[parity][0][wv] = __popcll(bg);
