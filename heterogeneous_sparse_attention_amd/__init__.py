@@ -10,6 +10,7 @@ PyTorch supplies device memory and streams only.
 
 from __future__ import annotations
 
+import array
 import ctypes
 import os
 
@@ -136,7 +137,10 @@ def _check(code: int, where: str):
 
 def _stream(stream):
     import torch
-    if stream is None:
+    if stream is None:   # the current stream's handle (no Stream object: ~3 us less per call)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return ctypes.c_void_p(raw(torch.cuda.current_device()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
 
@@ -144,6 +148,17 @@ def _stream(stream):
 def _host_i32(a):
     a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
     return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_i32_fast(a):
+    """(length, address, owner) of a host int32 copy of a list or array of ids: the
+    per-step calls take this path (array.array: about 1 us for 32 ids, against
+    about 4 us through numpy's ctypes view)."""
+    if isinstance(a, np.ndarray):
+        b, p = _host_i32(a)
+        return b.size, p, b
+    buf = array.array("i", a)
+    return len(buf), buf.buffer_info()[0], buf
 
 
 def _host_i64(a):
@@ -368,8 +383,7 @@ class Cache:
     def decode_step(self, states, k_new, v_new, idx_new, q, q_idx, k: int,
                     topk_out=None, score_out=None, out=None, sorted=False, stream=None):
         import torch
-        st, stp = _host_i32(states)
-        n = st.size
+        n, stp, _keep = _host_i32_fast(states)
         dev = q.device
         if topk_out is None:
             topk_out = torch.empty((n, k), dtype=torch.int32, device=dev)

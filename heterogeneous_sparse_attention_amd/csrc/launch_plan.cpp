@@ -2,35 +2,78 @@
 #include "launch_plan.h"
 
 #include <algorithm>
+#include <cmath>
 #include <queue>
 #include <utility>
 
 namespace hsa {
 
 int64_t balance_wgs(const std::vector<AttnPart*>& parts, int64_t slots) {
-  using Item = std::pair<double, std::pair<int, int>>;
-  std::priority_queue<Item> pq;
+  // Every (part, request) with keys starts at its floor w0; one that can be split
+  // may grow up to cap = max(w0, keys / kMinKeys) (no workgroup under kMinKeys keys).
+  struct Item {
+    double lat;
+    int64_t keys, w0, cap, w;
+    int64_t* out;
+  };
+  std::vector<Item> items;
   int64_t used = 0;
-  auto can_split = [](int64_t keys, int64_t w) { return keys >= kMinKeys * (w + 1); };
-  for (int p = 0; p < (int)parts.size(); ++p) {
-    AttnPart& a = *parts[p];
-    a.wgs.assign(a.keys->size(), 0);
-    for (int i = 0; i < (int)a.keys->size(); ++i) {
-      const int64_t k = (*a.keys)[i];
-      a.wgs[i] = std::max<int64_t>(k > 0 ? 1 : 0, a.min_wgs);
-      used += a.wgs[i];
-      if (a.wgs[i] > 0 && can_split(k, a.wgs[i])) pq.push({a.lat + (double)k / a.wgs[i], {p, i}});
+  for (AttnPart* a : parts) {
+    a->wgs.assign(a->keys->size(), 0);
+    for (size_t i = 0; i < a->keys->size(); ++i) {
+      const int64_t k = (*a->keys)[i];
+      const int64_t w0 = std::max<int64_t>(k > 0 ? 1 : 0, a->min_wgs);
+      a->wgs[i] = w0;
+      used += w0;
+      if (w0 > 0 && k >= kMinKeys * (w0 + 1))
+        items.push_back(Item{(double)a->lat, k, w0, std::max(w0, k / kMinKeys), w0, &a->wgs[i]});
     }
   }
-  while (used < slots && !pq.empty()) {
-    const auto pi = pq.top().second;
-    pq.pop();
-    AttnPart& a = *parts[pi.first];
-    const int64_t k = (*a.keys)[pi.second];
-    const int64_t w = ++a.wgs[pi.second];
-    ++used;
-    if (can_split(k, w)) pq.push({a.lat + (double)k / w, pi});
+  if (used >= slots || items.empty()) return used;
+  // The greedy hand-out (one slot at a time to the largest estimate lat + keys / w)
+  // ends at the smallest largest estimate E the slots allow, where every item holds
+  // at least need(E), the fewest w with lat + keys / w <= E (within [w0, cap]). So
+  // start every item at need(T) for some feasible T >= E, found from the
+  // proportional share (the estimate with every workgroup equally loaded) in a few
+  // tries, and hand out the rest greedily.
+  auto need = [](const Item& t, double T) -> int64_t {
+    if (T <= t.lat) return t.cap;
+    const double w = std::ceil((double)t.keys / (T - t.lat) * (1.0 - 1e-12));
+    return std::min(t.cap, std::max(t.w0, (int64_t)w));
+  };
+  double ksum = 0.0, tmin = 0.0, lmax = 0.0;
+  int64_t wsum = 0;
+  for (const Item& t : items) {
+    ksum += (double)t.keys;
+    wsum += t.w0;
+    lmax = std::max(lmax, t.lat);
+    tmin = std::max(tmin, t.lat + (double)t.keys / (double)t.cap);
   }
+  double T = 1.02 * std::max(tmin, lmax + ksum / (double)(slots - used + wsum));
+  int64_t sum = 0;
+  for (;;) {
+    sum = used;
+    for (const Item& t : items) sum += need(t, T) - t.w0;
+    if (sum <= slots) break;
+    T *= 1.25;
+  }
+  for (Item& t : items) t.w = need(t, T);
+  used = sum;
+  // the slots left over go one at a time to the largest estimate, as the greedy
+  // hand-out would give them
+  using Entry = std::pair<double, int>;
+  std::priority_queue<Entry> pq;
+  for (int j = 0; j < (int)items.size(); ++j)
+    if (items[j].w < items[j].cap) pq.push({items[j].lat + (double)items[j].keys / items[j].w, j});
+  while (used < slots && !pq.empty()) {
+    const int j = pq.top().second;
+    pq.pop();
+    Item& t = items[j];
+    ++t.w;
+    ++used;
+    if (t.w < t.cap) pq.push({t.lat + (double)t.keys / t.w, j});
+  }
+  for (const Item& t : items) *t.out = t.w;
   return used;
 }
 

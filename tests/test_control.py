@@ -186,6 +186,49 @@ def test_balance_wgs_is_optimal_on_small_cases(seed):
     assert abs(est - ref) < 1e-9, (est, ref)
 
 
+def _greedy(slots, parts):
+    """One slot at a time to the (part, request) with the largest lat + keys / w that
+    can still split (keys >= 16 (w + 1)); parts = [(keys, lat, min_wgs)]."""
+    import heapq
+    ws, heap, used = [], [], 0
+    for p, (keys, lat, mn) in enumerate(parts):
+        w = [max(1 if k > 0 else 0, mn) for k in keys]
+        used += sum(w)
+        ws.append(w)
+        for i, k in enumerate(keys):
+            if w[i] > 0 and k >= 16 * (w[i] + 1):
+                heapq.heappush(heap, (-(lat + k / w[i]), p, i))
+    while used < slots and heap:
+        _, p, i = heapq.heappop(heap)
+        keys, lat, _ = parts[p]
+        ws[p][i] += 1
+        used += 1
+        if keys[i] >= 16 * (ws[p][i] + 1):
+            heapq.heappush(heap, (-(lat + keys[i] / ws[p][i]), p, i))
+    return used, ws
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_balance_wgs_matches_the_greedy_hand_out(seed):
+    """The planner starts every item at a feasible share and hands out the rest one
+    at a time; it must end where the one-at-a-time greedy ends: same workgroups used
+    and the same largest estimate (b32-like and long-request sizes, two parts)."""
+    from heterogeneous_sparse_attention_amd.host import balance_wgs
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(40):
+        n = int(rng.integers(1, 41))
+        ka = rng.integers(0, 3000, n) * (rng.random(n) > 0.2)
+        kb = rng.integers(0, 1500, n)
+        slots = int(rng.integers(1, 600))
+        lat_b = int(rng.integers(0, 50))
+        used, wa, wb = balance_wgs(slots, ka, 0, 0, kb, lat_b, 1)
+        g_used, (ga, gb) = _greedy(slots, [(ka, 0, 0), (kb, lat_b, 1)])
+        assert used == g_used
+        est = max([k / w for k, w in zip(ka, wa) if w] + [lat_b + k / w for k, w in zip(kb, wb)])
+        g_est = max([k / w for k, w in zip(ka, ga) if w] + [lat_b + k / w for k, w in zip(kb, gb)])
+        assert abs(est - g_est) <= 1e-9 * max(1.0, g_est)
+
+
 def test_balance_wgs_fills_the_launch():
     """b32-like sizes: the planner hands out exactly the slots when work allows."""
     from heterogeneous_sparse_attention_amd.host import balance_wgs
