@@ -375,16 +375,10 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     // ordered pass: take entries above tau and the first `rem` equal to tau; the
     // entries taken before i are (above tau before i) + min(equal before i, rem)
     const int lane = tid & 63, wv = tid >> 6;
-    auto take = [&](int i, uint32_t u, int pos) {
-      const int32_t j = ord_of(i);
-      if (sorted) {
-        sh.cand[pos] = ((unsigned long long)(~u) << 32) | (uint32_t)i;
-      } else {
-        io[pos] = j;
-        if (so) so[pos] = okey_inv(u);
-      }
-      if (rows) rows[pos] = row_of(j);
-    };
+    // a taken entry is staged in LDS at its output position; its ordinal, score and
+    // row are written after the pass, so their global lookups (ord_map, the block
+    // table) are not waited for inside the pass
+    auto take = [&](int i, uint32_t u, int pos) { sh.cand[pos] = ((unsigned long long)u << 32) | (uint32_t)i; };
     if (!cached) {
       // Scores stream from L2: wave w owns a contiguous range of float4s. Count its
       // entries above / equal to tau, exchange the wave totals once, then write in
@@ -473,6 +467,19 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       eq_before += __popcll(be & below);
       if (gt || (eq && eq_before < rem)) take(i, u, gt_before + min(eq_before, rem));
       if (base_gt + min(base_eq, rem) >= kk) break;   // every entry taken (uniform)
+    }
+    __syncthreads();   // every taken entry staged
+    for (int p = tid; p < kk; p += NT) {
+      const unsigned long long c = sh.cand[p];
+      const uint32_t u = (uint32_t)(c >> 32);
+      const int32_t j = ord_of((int32_t)(c & 0xffffffffull));
+      if (sorted) {
+        sh.cand[p] = ((unsigned long long)(~u) << 32) | (c & 0xffffffffull);
+      } else {
+        io[p] = j;
+        if (so) so[p] = okey_inv(u);
+      }
+      if (rows) rows[p] = row_of(j);
     }
     if (sorted) {
       int n2 = 1;
