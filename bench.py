@@ -792,7 +792,7 @@ def main():
     ap.add_argument("--counters-workload", default="b32")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU "
               "path: the cache shards by request, see the design notes.", file=sys.stderr)
         sys.exit(2)
     if args.counters:
