@@ -155,8 +155,8 @@ def _host_i32_fast(a):
     per-step calls take this path (array.array: about 1 us for 32 ids, against
     about 4 us through numpy's ctypes view)."""
     if isinstance(a, np.ndarray):
-        b, p = _host_i32(a)
-        return b.size, p, b
+        b, _ = _host_i32(a)
+        return b.size, b.ctypes.data, b
     buf = array.array("i", a)
     return len(buf), buf.buffer_info()[0], buf
 

@@ -62,3 +62,16 @@ def test_product_path_does_not_import_oracle(root):
         if p.endswith((".py", ".cpp", ".hip", ".h")):
             txt = open(p, errors="replace").read()
             assert "import oracle" not in txt and "from oracle" not in txt, p
+
+
+def test_state_list_marshalling():
+    """The per-step state list reaches the C ABI as host int32 values, whether it is
+    a list or an array; values outside int32 are refused, not wrapped."""
+    import numpy as np
+    from heterogeneous_sparse_attention_amd import _host_i32_fast
+    for ids in ([3, 0, 7, 2 ** 31 - 1], np.array([3, 0, 7, 2 ** 31 - 1], np.int64), (5,)):
+        n, addr, keep = _host_i32_fast(ids)
+        got = np.ctypeslib.as_array((ctypes.c_int32 * n).from_address(addr))
+        assert n == len(ids) and np.array_equal(got, np.asarray(ids, np.int64))
+    with pytest.raises(OverflowError):
+        _host_i32_fast([2 ** 31])
