@@ -44,12 +44,14 @@ Readings taken where the pages leave a step open (each also in the design notes)
   R15 FP8 entries (optional format): the pages account compressed entries in FP8
       ([Ch12] §2.2) without a scale scheme. Reading: each C4 entry's K and V are
       stored per head as 128 OCP FP8 E4M3 codes and one float32 scale
-      s = max_d |x_d| / 448; code_d = E4M3 of x_d * (448 / max_d |x_d|),
-      nearest-even; the stored value is code_value * s. A head whose 448 / max|x|
-      is not a finite float32 (all zero, or max|x| below 448 / FLT_MAX, about
-      1.3e-36) is stored as s = 1 and codes 0. The decisions (x as float32, both divisions correctly
-      rounded, the product) are taken in float32, the precision the kernel
-      computes in. HCA entries stay bf16.
+      s = max_d |x_d| / 448, so that the largest magnitude maps onto E4M3's largest
+      finite value; the stored value of x_d is code_d * s. Since the stored value
+      multiplies by s, the quantiser divides by the same s: code_d is the E4M3 of
+      x_d / s, nearest, ties to the even code. x, s and the quotient are float32
+      values, each division correctly rounded (the precision the kernel computes
+      in). A head whose s would not be a normal float32 (all zero, or max |x| below
+      448 * 2**-126) keeps s = 1; its codes, by the same rule, are then all 0.
+      HCA entries stay bf16.
   R16 low-bit indexer keys (optional format): the pages store the indexer keys
       of the Block Cache as FP4 ([Ch12] §1 worked figures, §2.2) without a scale
       scheme. Reading: OCP MXFP4 (Microscaling Formats v1.0): each sealed key's
@@ -168,17 +170,13 @@ def e4m3_encode(x) -> np.ndarray:
 def quantize_e4m3_rows(x) -> tuple:
     """Per-row FP8 storage of [..., 128] rows (reading R15): returns (codes uint8,
     scales float32 [...], values float64 = code value * scale). The row is taken as
-    float32; with amax = max |x|, s = float32(amax / 448) and each code is the E4M3
-    of float32(x * float32(448 / amax)). A row whose 448 / amax is not a finite
-    float32 (all zero, or amax below 448 / FLT_MAX) is stored as s = 1, codes 0."""
+    float32; with amax = max |x|, s = float32(amax / 448), or 1 where that is not a
+    normal float32; each code is the E4M3 of float32(x / s)."""
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     amax = np.abs(x32).max(axis=-1)
-    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
-        r = (np.float32(E4M3_MAX) / amax).astype(np.float32)
-    ok = np.isfinite(r)                 # amax > 448 / FLT_MAX (so also nonzero)
-    s = np.where(ok, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0)).astype(np.float32)
-    r = np.where(ok, r, np.float32(0.0)).astype(np.float32)
-    y = (x32 * r[..., None]).astype(np.float32)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(s >= np.float32(np.finfo(np.float32).tiny), s, np.float32(1.0)).astype(np.float32)
+    y = (x32 / s[..., None]).astype(np.float32)
     codes = e4m3_encode(y)
     vals = e4m3_decode(codes) * s[..., None].astype(np.float64)
     return codes, s, vals

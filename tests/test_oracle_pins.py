@@ -513,11 +513,12 @@ def test_e4m3_encode_is_nearest_ties_to_even():
 
 
 def test_quantize_rows_bounds_and_special_cases():
-    """Per-row FP8 storage: the largest magnitude stores as +-448 (code 0x7e), every
-    value within half a code spacing of x * 448 / max |x| (up to the float32
-    rounding of the product), an all-zero row or one too small for a finite
-    multiplier stays zero with scale 1, and a row and its negation store with
-    mirrored codes."""
+    """Per-row FP8 storage: the largest magnitude stores as +-448 (code 0x7e); every
+    code is within half a code spacing of x / s, s the stored scale, up to the
+    float32 rounding of the quotient (at most 2**-24 |x / s|, which is at most
+    2**-20 of half a spacing anywhere on the E4M3 grid, hence the 1e-6 margin); an
+    all-zero row, or one whose s would not be a normal float32, stays zero with
+    scale 1; a row and its negation store with mirrored codes."""
     from oracle import e4m3_decode, quantize_e4m3_rows
     rng = np.random.default_rng(9)
     x = rng.standard_normal((64, 128)) * np.exp(rng.uniform(-8, 8, (64, 1)))
@@ -525,22 +526,92 @@ def test_quantize_rows_bounds_and_special_cases():
     x32 = x.astype(np.float32).astype(np.float64)
     amax_i = np.abs(x32).argmax(axis=1)
     assert np.all((codes[np.arange(64), amax_i] & 0x7F) == 0x7E)
-    y = x32 * 448.0 / np.abs(x32).max(axis=1, keepdims=True)
+    np.testing.assert_allclose(s, np.abs(x32).max(axis=1) / 448.0, rtol=2.0 ** -24)
+    y = x32 / s[:, None].astype(np.float64)
     grid = e4m3_decode(np.arange(0x7F))
     idx = np.clip(np.searchsorted(grid, np.abs(y)), 1, len(grid) - 1)
     spacing = grid[idx] - grid[idx - 1]
-    assert np.all(np.abs(e4m3_decode(codes) - y) <= spacing / 2 * (1 + 1e-5) + 1e-9)
+    assert np.all(np.abs(np.abs(e4m3_decode(codes)) - np.abs(y)) <= spacing / 2 * (1 + 1e-6) + 1e-12)
     assert np.allclose(vals, e4m3_decode(codes) * s[:, None])
     zc, zs, zv = quantize_e4m3_rows(np.zeros((2, 128)))
     assert np.all(zc == 0) and np.all(zs == 1.0) and np.all(zv == 0)
-    # 448 / amax overflows float32 below amax = 448 / FLT_MAX (~1.32e-36): such a row
-    # is stored as zero; just above it the row quantizes normally
-    tiny = np.array([np.full(128, 1e-38), np.full(128, 1.0e-36), np.full(128, 2.0e-36)])
+    # s = amax / 448 is a normal float32 from amax = 448 * 2**-126 (about 5.27e-36) up;
+    # below, the row keeps s = 1 and its codes (x / 1 < 2**-10) are 0
+    edge = 448.0 * 2.0 ** -126
+    tiny = np.array([np.full(128, 1e-38), np.full(128, edge * 0.99), np.full(128, edge),
+                     np.full(128, 2.0e-35)])
     tc, ts, tv = quantize_e4m3_rows(tiny)
     assert np.all(tc[:2] == 0) and np.all(ts[:2] == 1.0) and np.all(tv[:2] == 0)
-    assert np.all(tc[2] == 0x7E) and np.isclose(tv[2], 2.0e-36, rtol=1e-6).all()
+    assert ts[2] == np.float32(2.0 ** -126) and np.all(tc[2] == 0x7E) and np.all(tv[2] == edge)
+    assert np.all(tc[3] == 0x7E) and np.isclose(tv[3], 2.0e-35, rtol=1e-6).all()
     nc, ns, _ = quantize_e4m3_rows(-x)
     assert np.array_equal(ns, s) and np.array_equal(nc, codes ^ 0x80)
+
+
+def _f32_exact(v: Fraction) -> Fraction:
+    """v rounded to the nearest float32 (ties to even; normal and subnormal range),
+    in exact rational arithmetic."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    q = a / ulp
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return (n * ulp) if v > 0 else -(n * ulp)
+
+
+def _e4m3_exact(y: Fraction) -> int:
+    """E4M3 code of y: nearest finite value, ties to the even code, by enumeration."""
+    best = None
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        val = Fraction(m, 8 * 2 ** 6) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        d = abs(abs(y) - val)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (0x80 if y < 0 else 0)
+
+
+def test_quantize_rows_exact_fractions():
+    """The quantiser rule computed in exact rational arithmetic, in its own order of
+    operations: s = float32(amax / 448) (1 if not a normal float32), y =
+    float32(x / s), code = nearest E4M3 value of y with ties to the even code. Rows:
+    random magnitudes; rows with amax = 448 * 2**k (s exact) holding every E4M3
+    midpoint, so that the ties are decided by the even-code rule; and rows with an
+    inexact s."""
+    from oracle import quantize_e4m3_rows
+    rng = np.random.default_rng(41)
+    grid = np.array([float(Fraction(m, 8 * 2 ** 6) if (c >> 3) == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** ((c >> 3) - 7))
+                     for c in range(0x7F) for m in [c & 7]])
+    mids = (grid[1:] + grid[:-1]) / 2
+    rows = [rng.standard_normal(128) * np.exp(rng.uniform(-6, 6)) for _ in range(10)]
+    for k in (0, -3, 5):
+        r = np.resize(np.concatenate([mids, -mids]), 128) * 2.0 ** k
+        r[0] = 448.0 * 2.0 ** k
+        rows.append(r)
+    for amax in (1.0, 3.0, 0.1):
+        r = rng.uniform(-amax, amax, 128)
+        r[7] = -amax
+        rows.append(r)
+    x = np.array(rows).astype(np.float32)
+    codes, s, _ = quantize_e4m3_rows(x)
+    for i, row in enumerate(x):
+        xf = [Fraction(float(v)) for v in row]
+        amax = max(abs(v) for v in xf)
+        se = _f32_exact(amax / 448)
+        if se < Fraction(2) ** -126:
+            se = Fraction(1)
+        assert Fraction(float(s[i])) == se, i
+        for d in range(128):
+            assert codes[i, d] == _e4m3_exact(_f32_exact(xf[d] / se)), (i, d)
+    # the midpoint rows hit ties: the even code wins there
+    assert np.all(codes[10:13, 1:126] % 2 == 0)
 
 
 def test_fp8_oracle_entries_quantize_the_pooled_entry():
