@@ -382,26 +382,27 @@ __device__ __forceinline__ C4Addr c4_addr(const Pools& P, int64_t row) {
 }
 
 // Per-head FP8 storage of 8 values per lane, the 16 lanes of a DPP row holding one
-// head's 128 values: with amax = max |x| over the head, scale = amax / 448 and
-// code = E4M3(x * (448 / amax)) rounded to nearest even (scale 1 and codes 0 where
-// 448 / amax is not finite: an all-zero head, or amax below 448 / FLT_MAX); float32
-// throughout, each division correctly rounded. Returns
-// the 8 codes (value i in byte i) and the scale.
+// head's 128 values: with amax = max |x| over the head, the scale is s = amax / 448
+// (1 where that is not a normal float32: an all-zero head, or amax below
+// 448 * 2^-126) and each code is the E4M3 of x / s, rounded to nearest even. The
+// stored value reads as code * s, so the quotient is taken against that same s;
+// float32 throughout, each division correctly rounded. Returns the 8 codes (value i
+// in byte i) and the scale.
 __device__ __forceinline__ uint2 quantize8_e4m3(const float* x, float& scale) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
   amax = row_max16(amax);
-  // a head whose multiplier 448 / amax is not finite (zero, or amax below
-  // 448 / FLT_MAX) is stored as scale 1 and zero codes
-  float r = kE4M3Max / amax;
-  const bool ok = r <= __FLT_MAX__;
-  scale = ok ? amax / kE4M3Max : 1.f;
-  r = ok ? r : 0.f;
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * r, x[1] * r, 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * r, x[3] * r, w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * r, x[5] * r, 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * r, x[7] * r, w1, true);
+  float s = amax / kE4M3Max;
+  s = s >= __FLT_MIN__ ? s : 1.f;
+  scale = s;
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[i] / s;
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
   return make_uint2((uint32_t)w0, (uint32_t)w1);
 }
 

@@ -129,11 +129,11 @@ typedef struct hsa_config {
 
 /* C4 entry storage. BF16: K and V rows of 16 x 128 bf16. FP8: per head, 128 OCP
  * FP8 E4M3 codes and one float32 scale s = amax / 448, amax = max |x| over the
- * head's 128 values; code = E4M3(x * (448 / amax)), round to nearest, ties to even,
- * taken in float32; the entry reads as code value * s. A head whose 448 / amax is
- * not a finite float32 (all zero, or amax below 448 / FLT_MAX) stores s = 1 and
- * codes 0. The pages give no scale scheme: this per-head scale is the reading
- * used. HCA entries are always bf16. */
+ * head's 128 values (s = 1 where amax / 448 is not a normal float32: an all-zero
+ * head, or amax below 448 * 2^-126); code = E4M3(x / s), round to nearest, ties to
+ * even, with x, s and the quotient float32 and each division correctly rounded;
+ * the entry reads as code value * s. The pages give no scale scheme: this
+ * per-head scale is the reading used. HCA entries are always bf16. */
 #define HSA_ENTRY_BF16 0
 #define HSA_ENTRY_FP8 1
 
