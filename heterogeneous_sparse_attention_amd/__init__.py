@@ -81,6 +81,8 @@ SIGNATURES = {
     "hsa_indexer_topk": [_P, _I32, _P, _P, _I32, _U32, _P, _P, _P],
     "hsa_decode_attend": [_P, _I32, _P, _P, _P, _I32, _P, _P],
     "hsa_decode_step": [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _U32, _P, _P, _P, _P],
+    "hsa_decode_step_noalloc": [_P, _I32, _P, _P, _P, _P, _P, _P, _I32, _U32, _P, _P, _P, _P],
+    "hsa_noalloc_scratch_bytes": [_P],
     "hsa_state_query": [_P, _I32, ctypes.POINTER(_StateInfo)],
     "hsa_block_table_get": [_P, _I32, _P, _I64, ctypes.POINTER(_I64)],
     "hsa_block_refcount": [_P, _I32, ctypes.POINTER(_I32)],
@@ -381,7 +383,10 @@ class Cache:
         return out
 
     def decode_step(self, states, k_new, v_new, idx_new, q, q_idx, k: int,
-                    topk_out=None, score_out=None, out=None, sorted=False, stream=None):
+                    topk_out=None, score_out=None, out=None, sorted=False, stream=None,
+                    noalloc: bool = False):
+        """hsa_decode_step, or with noalloc=True hsa_decode_step_noalloc (scratch from
+        the library's fixed buffer; the caller passes every output)."""
         import torch
         n, stp, _keep = _host_i32_fast(states)
         dev = q.device
@@ -392,7 +397,9 @@ class Cache:
         sp = ctypes.c_void_p(0)
         if score_out is not None:
             sp = _dev(score_out, torch.float32, (n, k), "score_out")
-        _check(_lib.hsa_decode_step(
+        fn, name = ((_lib.hsa_decode_step_noalloc, "hsa_decode_step_noalloc") if noalloc
+                    else (_lib.hsa_decode_step, "hsa_decode_step"))
+        _check(fn(
             self._ctx, n, stp,
             _dev(k_new, torch.bfloat16, (n, H, D), "k_new"),
             _dev(v_new, torch.bfloat16, (n, H, D), "v_new"),
@@ -400,7 +407,7 @@ class Cache:
             _dev(q, torch.bfloat16, (n, H, D), "q"),
             _dev(q_idx, torch.float32, (n, HI, DI), "q_idx"),
             int(k), TOPK_SORTED if sorted else 0, _dev(topk_out, torch.int32, (n, k), "topk_out"), sp,
-            _dev(out, torch.float32, (n, H, D), "out"), _stream(stream)), "hsa_decode_step")
+            _dev(out, torch.float32, (n, H, D), "out"), _stream(stream)), name)
         return topk_out, score_out, out
 
     # -- introspection -----------------------------------------------------------------

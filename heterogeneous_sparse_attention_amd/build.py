@@ -26,8 +26,8 @@ ARCH = "gfx950"
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-HIP_SOURCES = ["append_seal.hip", "indexer_topk.hip", "attend.hip", "step.hip", "hsa.cpp",
-               "control.cpp", "launch_plan.cpp"]
+HIP_SOURCES = ["append_seal.hip", "indexer_topk.hip", "attend.hip", "step.hip", "noalloc.hip",
+               "hsa.cpp", "control.cpp", "launch_plan.cpp"]
 
 LIB = os.path.join(HERE, "libhsa.so")
 HOST_LIB = os.path.join(HERE, "libhsa_host.so")

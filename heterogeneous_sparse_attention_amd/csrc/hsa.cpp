@@ -14,6 +14,7 @@
 #include "device.h"
 #include "kernels.h"
 #include "launch_plan.h"
+#include "noalloc.h"
 
 using namespace hsa;
 
@@ -84,6 +85,7 @@ struct hsa_ctx {
     int32_t next = 0;             // the layer whose turn it is
   } seq;
   bool seq_open = false;
+  void* fixed = nullptr;      // this device's fixed scratch buffer (hsa_decode_step_noalloc)
   int32_t* rows = nullptr;    // decode step: physical C4 rows of the selected entries
   size_t rows_cap = 0;
   int32_t* cand_ord = nullptr;  // top-k of sliced rows: per-slice candidates (ordinals, scores)
@@ -287,18 +289,26 @@ int recompute_open(hsa_ctx* c, const int32_t* states, int32_t n, hipStream_t st)
   return kOk;
 }
 
-// Top-k workgroups of a batch (plan_slices), with room for the candidates of
-// sliced rows. On the 4 x 2^20-token workload (k 2048), 32768-score slices measured
-// 736 us per step, against 759 us for 16384 and 764 us for 65536.
-int plan_select(hsa_ctx* c, const ReqBatch& B, int32_t k, SelPlan& SP) {
+// Top-k workgroups of a batch (plan_slices). On the 4 x 2^20-token workload (k 2048),
+// 32768-score slices measured 736 us per step, against 759 us for 16384 and 764 us
+// for 65536. The candidates of sliced rows need n * gmax * k1 entries of scratch.
+void plan_select_host(hsa_ctx* c, const ReqBatch& B, int32_t k, SelPlan& SP) {
   SP = SelPlan{};
   int64_t n[kMaxReq];
   for (int i = 0; i < B.n; ++i) n[i] = h_rowlen(c->P, B.r[i].len, B.r[i].nb);
   SP.eager = c->P.eager;
   plan_slices(n, B.n, k, c->select_slice, kSliceN, SP.first, &SP.gmax, &SP.slice, &SP.k1);
   SP.n_wgs = SP.first[B.n];
-  if (SP.gmax > 1) {
-    const size_t need = (size_t)B.n * SP.gmax * SP.k1;
+}
+size_t sel_cand_need(const ReqBatch& B, const SelPlan& SP) {
+  return SP.gmax > 1 ? (size_t)B.n * SP.gmax * SP.k1 : 0;
+}
+
+// plan_select_host, with the candidates in the context's scratch.
+int plan_select(hsa_ctx* c, const ReqBatch& B, int32_t k, SelPlan& SP) {
+  plan_select_host(c, B, k, SP);
+  const size_t need = sel_cand_need(B, SP);
+  if (need) {
     int s = grow(c, reinterpret_cast<void**>(&c->cand_ord), &c->cand_ord_cap, need, sizeof(int32_t));
     if (s) return s;
     s = grow(c, reinterpret_cast<void**>(&c->cand_score), &c->cand_score_cap, need, sizeof(float));
@@ -397,144 +407,234 @@ int run_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* q,
   return kOk;
 }
 
+// One batch (at most kMaxReq requests) of a decode step: the launch descriptors and
+// the scratch they need, in elements.
+struct StepBatch {
+  ReqBatch B;
+  StepArgs S;
+  size_t n_scores = 0;   // floats: score rows (+16: the three-launch selection reads one
+                         // float4 at the start of every row)
+  size_t n_chunks = 0;   // attention partials (kRow + 2 kH floats each)
+  size_t n_rows = 0;     // int32: physical C4 rows of the selected entries
+  size_t n_cand = 0;     // top-k candidates of sliced rows (an int32 and a float each)
+  size_t n_seal = 0;     // floats: HCA partials of the blocks sealed in this step
+};
+
+// Host plan of the batch of requests b0 .. b0 + kMaxReq - 1 of a one-token-per-request
+// append plan (committed or not): form, workgroups, and scratch sizes. No device work.
+void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32_t>& new_id, int32_t b0,
+                     int32_t k, uint32_t flags, StepBatch& sb) {
+  const int32_t n = std::min<int32_t>(kMaxReq, (int32_t)plan.reqs.size() - b0);
+  ReqBatch& B = sb.B;
+  StepArgs& S = sb.S;
+  B = ReqBatch{};
+  S = StepArgs{};
+  B.n = n;
+  // three launches when every score row fits the selection's LDS cache (and the
+  // top-k is wanted in ordinal order): every attention workgroup then selects for
+  // itself and the new HCA key joins the merge
+  // A layer without C4 entries needs no selection and no part B: part A only, the
+  // new HCA key in the merge, padding top-k rows, and no S1 when nothing seals.
+  const bool c4 = c->P.c4 != 0, hca = c->P.hca != 0;
+  const bool a_only = !c4;
+  bool fused = !a_only && c->step_fused != 0 && !(flags & HSA_TOPK_SORTED);
+  for (int i = 0; i < n; ++i)
+    fused = fused && h_rowlen(c->P, plan.reqs[b0 + i].len_new, plan.reqs[b0 + i].nb_new) <= kCacheN;
+  std::vector<int64_t> na(n), nb(n);
+  int64_t maxnb = 0, n_score = 0, all_nb = 0;
+  for (int i = 0; i < n; ++i) all_nb += plan.reqs[b0 + i].nb_new;
+  // MXFP4 keys: as many blocks per scoring workgroup as leave about two workgroups
+  // per attention slot (more blocks per workgroup hide latency; fewer spread a
+  // small batch over the chip)
+  const int mx_unit = !c->P.mx4 ? 0
+                      : c->mx_unit ? c->mx_unit
+                                   : (int)std::max<int64_t>(1, std::min<int64_t>(kMxUnitMax,
+                                                                (all_nb + 2 * c->step_slots - 1) / (2 * c->step_slots)));
+  for (int i = 0; i < n; ++i) {
+    const AppendReq& r = plan.reqs[b0 + i];
+    const int32_t id = new_id[b0 + i];
+    B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, id};
+    if (id >= 0 && (c4 || hca)) B.seal_req[B.n_seal++] = (int8_t)i;   // an SWA layer seals nothing
+    const int64_t sealed = id >= 0 ? 1 : 0;
+    na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + (hca ? r.nb_new - sealed : 0);
+    nb[i] = (fused || !hca || a_only ? 0 : sealed) + std::min<int64_t>(k, h_cands(c->P, r.len_new, r.nb_new));
+    maxnb = std::max<int64_t>(maxnb, h_rowlen(c->P, r.len_new, r.nb_new) / kC4);
+    // eager C4: the open block is scored too, and a completed group gets its entry
+    const bool open = h_open(c->P, r.len_new, r.nb_new) > 0;
+    if (c4) n_score += score_units(r.nb_new, mx_unit) + (open ? kScoreSplit : 0);
+    if (c->P.eager && r.len_new % 4 == 0 && r.len_new % kBlk != 0) B.open_req[B.n_open++] = (int8_t)i;
+  }
+  S.ld = std::max<int64_t>(kC4 * maxnb, 1);
+  S.k = k;
+  S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
+  S.fused = fused ? 1 : 0;
+  S.mx_unit = mx_unit;
+  S.a_only = a_only ? 1 : 0;
+  S.s2_append = a_only && B.n_seal == 0 ? 1 : 0;
+  S.n_score = (int32_t)n_score;
+  if (!fused && !a_only) plan_select_host(c, B, k, S.sel);
+  // workgroups: three-launch form, each S2 workgroup takes a share of both parts
+  // of one request (at least one per request: it writes the top-k padding);
+  // four-launch form, part A shares S2 with the selections, part B has S3
+  std::vector<int64_t> nab(n);
+  for (int i = 0; i < n; ++i) nab[i] = na[i] + nb[i];
+  AttnPart pa{&na, 0, 0, {}}, pb{fused ? &nab : &nb, 0, fused ? 1 : 0, {}};
+  if (fused) {
+    balance_wgs({&pb}, c->step_slots - B.n_seal);
+    pa.wgs.assign(n, 0);
+  } else if (a_only) {
+    balance_wgs({&pa}, c->step_slots - B.n_seal - (S.s2_append ? n : 0));
+    pb.wgs.assign(n, 0);
+  } else {
+    balance_wgs({&pa}, c->step_slots - S.sel.n_wgs - B.n_seal);
+    balance_wgs({&pb}, c->step_slots);
+  }
+  int64_t ta = 0, tb = 0, ts = 0;
+  for (int i = 0; i < n; ++i) {
+    S.first_a[i] = (int32_t)ta;
+    S.first_b[i] = (int32_t)tb;
+    S.first_s[i] = (int32_t)ts;
+    ta += pa.wgs[i];
+    tb += pb.wgs[i];
+    ts += c4 ? score_units(B.r[i].nb, mx_unit) + (h_open(c->P, B.r[i].len, B.r[i].nb) > 0 ? kScoreSplit : 0)
+             : 0;
+  }
+  S.first_a[n] = (int32_t)ta;
+  S.first_b[n] = (int32_t)tb;
+  S.first_s[n] = (int32_t)ts;
+  S.n_a = (int32_t)ta;
+  S.n_b = (int32_t)tb;
+  sb.n_scores = (size_t)(S.ld * n + 16);
+  sb.n_chunks = (size_t)(ta + tb + n);
+  sb.n_rows = (size_t)n * k;
+  sb.n_cand = sel_cand_need(B, S.sel);
+  sb.n_seal = (size_t)B.n_seal * kSealSplit * kPartFloats;
+}
+
+// The batch's input and output pointers (rows b0 .. of the caller's arrays).
+void bind_step_io(StepBatch& sb, int32_t b0, const void* k_new, const void* v_new, const float* idx_new,
+                  const void* q, const float* q_idx, int32_t* topk_out, float* score_out, float* out) {
+  StepArgs& S = sb.S;
+  S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
+  S.vin = static_cast<const uint16_t*>(v_new) + (int64_t)b0 * kRow;
+  S.iin = idx_new + (int64_t)b0 * kIRow;
+  S.q = static_cast<const uint16_t*>(q) + (int64_t)b0 * kRow;
+  S.qi = q_idx + (int64_t)b0 * kIRow;
+  S.topk = topk_out + (int64_t)b0 * S.k;
+  S.score_out = score_out ? score_out + (int64_t)b0 * S.k : nullptr;
+  S.out = out + (int64_t)b0 * kRow;
+}
+
+// The batch's scratch in the context's buffers (grown when too small).
+int bind_ctx_scratch(hsa_ctx* c, StepBatch& sb) {
+  StepArgs& S = sb.S;
+  int s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, sb.n_scores, sizeof(float));
+  if (!s) s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, sb.n_chunks, kRow * sizeof(float));
+  if (!s) s = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, sb.n_chunks, 2 * kH * sizeof(float));
+  if (!s) s = grow(c, reinterpret_cast<void**>(&c->rows), &c->rows_cap, sb.n_rows, sizeof(int32_t));
+  if (!s && sb.n_cand) {
+    s = grow(c, reinterpret_cast<void**>(&c->cand_ord), &c->cand_ord_cap, sb.n_cand, sizeof(int32_t));
+    if (!s) s = grow(c, reinterpret_cast<void**>(&c->cand_score), &c->cand_score_cap, sb.n_cand, sizeof(float));
+    S.sel.cand_ord = c->cand_ord;
+    S.sel.cand_score = c->cand_score;
+  }
+  if (s) return s;
+  S.scores = c->scores;
+  S.part_acc = c->part_acc;
+  S.part_ml = c->part_ml;
+  S.rows = c->rows;
+  S.seal_part = c->seal_part;
+  return kOk;
+}
+
+// Fixed-buffer layout of a batch's scratch: each segment at a 256-byte boundary.
+size_t seg_bytes(size_t n, size_t elem) { return (n * elem + 255) / 256 * 256; }
+size_t fixed_scratch_bytes(const StepBatch& sb) {
+  return seg_bytes(sb.n_scores, 4) + seg_bytes(sb.n_chunks, kRow * 4) + seg_bytes(sb.n_chunks, 2 * kH * 4) +
+         seg_bytes(sb.n_rows, 4) + 2 * seg_bytes(sb.n_cand, 4) + seg_bytes(sb.n_seal, 4);
+}
+void bind_fixed_scratch(char* base, StepBatch& sb) {
+  StepArgs& S = sb.S;
+  auto take = [&](size_t n, size_t elem) {
+    char* p = base;
+    base += seg_bytes(n, elem);
+    return p;
+  };
+  S.scores = reinterpret_cast<float*>(take(sb.n_scores, 4));
+  S.part_acc = reinterpret_cast<float*>(take(sb.n_chunks, kRow * 4));
+  S.part_ml = reinterpret_cast<float*>(take(sb.n_chunks, 2 * kH * 4));
+  S.rows = reinterpret_cast<int32_t*>(take(sb.n_rows, 4));
+  S.sel.cand_ord = reinterpret_cast<int32_t*>(take(sb.n_cand, 4));
+  S.sel.cand_score = reinterpret_cast<float*>(take(sb.n_cand, 4));
+  S.seal_part = reinterpret_cast<float*>(take(sb.n_seal, 4));
+}
+
+// Enqueue the three or four launches of a planned and bound batch.
+int launch_step_batch(hsa_ctx* c, const StepBatch& sb, hipStream_t st) {
+  const ReqBatch& B = sb.B;
+  const StepArgs& S = sb.S;
+  if (!S.s2_append) {
+    Timed t(c, HSA_KERNEL_STEP1, st);
+    HIP_TRY(launch_step1(c->P, B, S, st, t.ev()));
+  }
+  {
+    Timed t(c, HSA_KERNEL_STEP2, st);
+    HIP_TRY(launch_step2(c->P, B, S, st, t.ev()));
+  }
+  if (!S.fused && S.sel.gmax > 1) {
+    Timed t(c, HSA_KERNEL_STEP2B, st);
+    HIP_TRY(launch_step2b(c->P, B, S, st, t.ev()));
+  }
+  {
+    Timed t(c, HSA_KERNEL_STEP3, st);
+    HIP_TRY(launch_step3(c->P, B, S, st, t.ev()));
+  }
+  {
+    Timed t(c, HSA_KERNEL_STEP4, st);
+    HIP_TRY(launch_step4(c->P, B, S, st, t.ev()));
+  }
+  return kOk;
+}
+
+std::vector<int32_t> sealed_ids(const AppendPlan& plan) {
+  std::vector<int32_t> new_id(plan.reqs.size(), -1);
+  for (const SealItem& s : plan.seals) new_id[s.req] = s.id;
+  return new_id;
+}
+
+// Largest fixed-buffer scratch of any batch of a decode step over `plan`.
+size_t step_fixed_need(hsa_ctx* c, const AppendPlan& plan, int32_t k, uint32_t flags) {
+  const std::vector<int32_t> new_id = sealed_ids(plan);
+  size_t need = 0;
+  StepBatch sb;
+  for (int32_t b0 = 0; b0 < (int32_t)plan.reqs.size(); b0 += kMaxReq) {
+    plan_step_batch(c, plan, new_id, b0, k, flags, sb);
+    need = std::max(need, fixed_scratch_bytes(sb));
+  }
+  return need;
+}
+
 // The decode step (committed one-token append + top-k + attention) in three or four
-// launches per batch of kMaxReq requests.
+// launches per batch of kMaxReq requests. Scratch: the context's buffers, or, with
+// `fixed` (at least step_fixed_need bytes of device memory), that buffer, reused by
+// every batch in stream order.
 int run_decode_step(hsa_ctx* c, const AppendPlan& plan, const void* k_new, const void* v_new,
                     const float* idx_new, const void* q, const float* q_idx, int32_t k,
                     uint32_t flags, int32_t* topk_out, float* score_out, float* out,
-                    hipStream_t st) {
-  std::vector<int32_t> new_id(plan.reqs.size(), -1);
-  for (const SealItem& s : plan.seals) new_id[s.req] = s.id;
-  const int32_t n_req = (int32_t)plan.reqs.size();
-  for (int32_t b0 = 0; b0 < n_req; b0 += kMaxReq) {
-    const int32_t n = std::min<int32_t>(kMaxReq, n_req - b0);
-    ReqBatch B{};
-    B.n = n;
-    // three launches when every score row fits the selection's LDS cache (and the
-    // top-k is wanted in ordinal order): every attention workgroup then selects for
-    // itself and the new HCA key joins the merge
-    // A layer without C4 entries needs no selection and no part B: part A only, the
-    // new HCA key in the merge, padding top-k rows, and no S1 when nothing seals.
-    const bool c4 = c->P.c4 != 0, hca = c->P.hca != 0;
-    const bool a_only = !c4;
-    bool fused = !a_only && c->step_fused != 0 && !(flags & HSA_TOPK_SORTED);
-    for (int i = 0; i < n; ++i)
-      fused = fused && h_rowlen(c->P, plan.reqs[b0 + i].len_new, plan.reqs[b0 + i].nb_new) <= kCacheN;
-    std::vector<int64_t> na(n), nb(n);
-    int64_t maxnb = 0, n_score = 0, all_nb = 0;
-    for (int i = 0; i < n; ++i) all_nb += plan.reqs[b0 + i].nb_new;
-    // MXFP4 keys: as many blocks per scoring workgroup as leave about two workgroups
-    // per attention slot (more blocks per workgroup hide latency; fewer spread a
-    // small batch over the chip)
-    const int mx_unit = !c->P.mx4 ? 0
-                        : c->mx_unit ? c->mx_unit
-                                     : (int)std::max<int64_t>(1, std::min<int64_t>(kMxUnitMax,
-                                                                  (all_nb + 2 * c->step_slots - 1) / (2 * c->step_slots)));
-    for (int i = 0; i < n; ++i) {
-      const AppendReq& r = plan.reqs[b0 + i];
-      const int32_t id = new_id[b0 + i];
-      B.r[i] = Req{r.state, (int32_t)r.len_new, (int32_t)r.nb_new, id};
-      if (id >= 0 && (c4 || hca)) B.seal_req[B.n_seal++] = (int8_t)i;   // an SWA layer seals nothing
-      const int64_t sealed = id >= 0 ? 1 : 0;
-      na[i] = std::min<int64_t>(r.len_new, c->P.n_win) + (hca ? r.nb_new - sealed : 0);
-      nb[i] = (fused || !hca || a_only ? 0 : sealed) + std::min<int64_t>(k, h_cands(c->P, r.len_new, r.nb_new));
-      maxnb = std::max<int64_t>(maxnb, h_rowlen(c->P, r.len_new, r.nb_new) / kC4);
-      // eager C4: the open block is scored too, and a completed group gets its entry
-      const bool open = h_open(c->P, r.len_new, r.nb_new) > 0;
-      if (c4) n_score += score_units(r.nb_new, mx_unit) + (open ? kScoreSplit : 0);
-      if (c->P.eager && r.len_new % 4 == 0 && r.len_new % kBlk != 0) B.open_req[B.n_open++] = (int8_t)i;
-    }
-    StepArgs S{};
-    S.kin = static_cast<const uint16_t*>(k_new) + (int64_t)b0 * kRow;
-    S.vin = static_cast<const uint16_t*>(v_new) + (int64_t)b0 * kRow;
-    S.iin = idx_new + (int64_t)b0 * kIRow;
-    S.q = static_cast<const uint16_t*>(q) + (int64_t)b0 * kRow;
-    S.qi = q_idx + (int64_t)b0 * kIRow;
-    S.ld = std::max<int64_t>(kC4 * maxnb, 1);
-    S.topk = topk_out + (int64_t)b0 * k;
-    S.score_out = score_out ? score_out + (int64_t)b0 * k : nullptr;
-    S.out = out + (int64_t)b0 * kRow;
-    S.k = k;
-    S.sorted = (flags & HSA_TOPK_SORTED) ? 1 : 0;
-    S.fused = fused ? 1 : 0;
-    S.mx_unit = mx_unit;
-    S.a_only = a_only ? 1 : 0;
-    S.s2_append = a_only && B.n_seal == 0 ? 1 : 0;
-    S.n_score = (int32_t)n_score;
-    int s = kOk;
-    if (!fused && !a_only) {
-      s = plan_select(c, B, k, S.sel);
+                    hipStream_t st, char* fixed = nullptr) {
+  const std::vector<int32_t> new_id = sealed_ids(plan);
+  StepBatch sb;
+  for (int32_t b0 = 0; b0 < (int32_t)plan.reqs.size(); b0 += kMaxReq) {
+    plan_step_batch(c, plan, new_id, b0, k, flags, sb);
+    bind_step_io(sb, b0, k_new, v_new, idx_new, q, q_idx, topk_out, score_out, out);
+    if (fixed) {
+      bind_fixed_scratch(fixed, sb);
+    } else {
+      const int s = bind_ctx_scratch(c, sb);
       if (s) return s;
     }
-    // workgroups: three-launch form, each S2 workgroup takes a share of both parts
-    // of one request (at least one per request: it writes the top-k padding);
-    // four-launch form, part A shares S2 with the selections, part B has S3
-    std::vector<int64_t> nab(n);
-    for (int i = 0; i < n; ++i) nab[i] = na[i] + nb[i];
-    AttnPart pa{&na, 0, 0, {}}, pb{fused ? &nab : &nb, 0, fused ? 1 : 0, {}};
-    if (fused) {
-      balance_wgs({&pb}, c->step_slots - B.n_seal);
-      pa.wgs.assign(n, 0);
-    } else if (a_only) {
-      balance_wgs({&pa}, c->step_slots - B.n_seal - (S.s2_append ? n : 0));
-      pb.wgs.assign(n, 0);
-    } else {
-      balance_wgs({&pa}, c->step_slots - S.sel.n_wgs - B.n_seal);
-      balance_wgs({&pb}, c->step_slots);
-    }
-    int64_t ta = 0, tb = 0, ts = 0;
-    for (int i = 0; i < n; ++i) {
-      S.first_a[i] = (int32_t)ta;
-      S.first_b[i] = (int32_t)tb;
-      S.first_s[i] = (int32_t)ts;
-      ta += pa.wgs[i];
-      tb += pb.wgs[i];
-      ts += c4 ? score_units(B.r[i].nb, mx_unit) + (h_open(c->P, B.r[i].len, B.r[i].nb) > 0 ? kScoreSplit : 0)
-               : 0;
-    }
-    S.first_a[n] = (int32_t)ta;
-    S.first_b[n] = (int32_t)tb;
-    S.first_s[n] = (int32_t)ts;
-    S.n_a = (int32_t)ta;
-    S.n_b = (int32_t)tb;
-
-    // (+16: the three-launch selection reads one float4 at the start of every row)
-    s = grow(c, reinterpret_cast<void**>(&c->scores), &c->scores_cap, (size_t)(S.ld * n + 16),
-             sizeof(float));
+    const int s = launch_step_batch(c, sb, st);
     if (s) return s;
-    s = grow(c, reinterpret_cast<void**>(&c->part_acc), &c->part_acc_cap, (size_t)(ta + tb + n),
-             kRow * sizeof(float));
-    if (s) return s;
-    s = grow(c, reinterpret_cast<void**>(&c->part_ml), &c->part_ml_cap, (size_t)(ta + tb + n),
-             2 * kH * sizeof(float));
-    if (s) return s;
-    s = grow(c, reinterpret_cast<void**>(&c->rows), &c->rows_cap, (size_t)n * k, sizeof(int32_t));
-    if (s) return s;
-    S.rows = c->rows;
-    S.scores = c->scores;
-    S.part_acc = c->part_acc;
-    S.part_ml = c->part_ml;
-    S.seal_part = c->seal_part;
-    if (!S.s2_append) {
-      Timed t(c, HSA_KERNEL_STEP1, st);
-      HIP_TRY(launch_step1(c->P, B, S, st, t.ev()));
-    }
-    {
-      Timed t(c, HSA_KERNEL_STEP2, st);
-      HIP_TRY(launch_step2(c->P, B, S, st, t.ev()));
-    }
-    if (!fused && S.sel.gmax > 1) {
-      Timed t(c, HSA_KERNEL_STEP2B, st);
-      HIP_TRY(launch_step2b(c->P, B, S, st, t.ev()));
-    }
-    {
-      Timed t(c, HSA_KERNEL_STEP3, st);
-      HIP_TRY(launch_step3(c->P, B, S, st, t.ev()));
-    }
-    {
-      Timed t(c, HSA_KERNEL_STEP4, st);
-      HIP_TRY(launch_step4(c->P, B, S, st, t.ev()));
-    }
   }
   return kOk;
 }
@@ -637,9 +737,12 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   HIP_TRY(hipGetDeviceCount(&ndev));
   if (device < 0 || device >= ndev) return fail(kInvalid, "no such device");
   HIP_TRY(hipSetDevice(device));
+  void* fixed = nullptr;   // the fixed scratch buffer's address on this device
+  HIP_TRY(noalloc_scratch(device, &fixed));
   const int64_t bps = cfg->max_blocks_per_state ? cfg->max_blocks_per_state : cfg->max_blocks;
   hsa_ctx* c = new hsa_ctx(cfg->n_win, cfg->max_states, cfg->max_blocks, bps);
   c->device = device;
+  c->fixed = fixed;
   if (!std::getenv("HSA_STEP_SLOTS")) {   // one step-kernel workgroup per CU
     int n_cu = 0;
     if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && n_cu > 0)
@@ -1090,10 +1193,15 @@ hsa_status hsa_decode_attend(hsa_ctx* c, int32_t n_req, const int32_t* states, c
                     static_cast<hipStream_t>(stream));
 }
 
-hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* k_new,
-                           const void* v_new, const float* idx_new, const void* q,
-                           const float* q_idx, int32_t k, uint32_t flags, int32_t* topk_out,
-                           float* score_out, float* out, void* stream) {
+namespace {
+
+// hsa_decode_step and hsa_decode_step_noalloc: with `noalloc`, every kernel's scratch
+// comes from the fixed buffer, which must hold the step's largest batch (checked
+// before anything changes), and no device memory is allocated.
+int decode_step_impl(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* k_new,
+                     const void* v_new, const float* idx_new, const void* q, const float* q_idx,
+                     int32_t k, uint32_t flags, int32_t* topk_out, float* score_out, float* out,
+                     void* stream, bool noalloc) {
   if (!c) return fail(kInvalid, "NULL context");
   if (n_req < 0) return fail(kInvalid, "n_req < 0");
   if (n_req == 0) return kOk;
@@ -1101,26 +1209,65 @@ hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, con
   if (flags & ~HSA_TOPK_SORTED) return fail(kInvalid, "unknown flags");
   if (!k_new || !v_new || (c->P.c4 && (!idx_new || !q_idx)) || !q || !topk_out || !out)
     return fail(kInvalid, "NULL device pointer");
+  if (noalloc && !c->fixed) return fail(kDevice, "the fixed scratch buffer was not found");
   bool replay = false;
   int st = layer_gate(c, kSeqStep, n_req, states, nullptr, 0, &replay);
   if (st) return st;
-  if (replay) {
-    if ((st = set_device(c))) return st;
-    layer_advance(c);
-    return run_decode_step(c, c->seq.plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out,
-                           score_out, out, static_cast<hipStream_t>(stream));
+  AppendPlan fresh;
+  if (!replay) {
+    std::vector<int64_t> cu(n_req + 1);
+    for (int32_t i = 0; i <= n_req; ++i) cu[i] = i;
+    std::string why;
+    st = c->ctl.plan_append(n_req, states, cu.data(), false, &fresh, &why);
+    if (st) return fail(st, why);
   }
-  std::vector<int64_t> cu(n_req + 1);
-  for (int32_t i = 0; i <= n_req; ++i) cu[i] = i;
-  std::string why;
-  AppendPlan plan;
-  st = c->ctl.plan_append(n_req, states, cu.data(), false, &plan, &why);
-  if (st) return fail(st, why);
+  const AppendPlan& plan = replay ? c->seq.plan : fresh;
+  if (noalloc) {
+    const size_t need = step_fixed_need(c, plan, k, flags);
+    if (need > kNoAllocScratchBytes)
+      return fail(kInvalid, "the step needs " + std::to_string(need) + " bytes of scratch; the fixed buffer holds " +
+                                std::to_string(kNoAllocScratchBytes));
+  }
   if ((st = set_device(c))) return st;
-  c->ctl.commit(&plan);
-  layer_record(c, kSeqStep, n_req, states, nullptr, 0, plan);
-  return run_decode_step(c, plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out, score_out,
-                         out, static_cast<hipStream_t>(stream));
+  if (replay) {
+    layer_advance(c);
+  } else {
+    c->ctl.commit(&fresh);
+    layer_record(c, kSeqStep, n_req, states, nullptr, 0, fresh);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!noalloc)
+    return run_decode_step(c, plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out, score_out, out, s);
+  const uint32_t tmask = c->tmask;   // no timing events either
+  c->tmask = 0;
+  st = run_decode_step(c, plan, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out, score_out, out, s,
+                       static_cast<char*>(c->fixed));
+  c->tmask = tmask;
+  return st;
+}
+
+}  // namespace
+
+hsa_status hsa_decode_step(hsa_ctx* c, int32_t n_req, const int32_t* states, const void* k_new,
+                           const void* v_new, const float* idx_new, const void* q,
+                           const float* q_idx, int32_t k, uint32_t flags, int32_t* topk_out,
+                           float* score_out, float* out, void* stream) {
+  return decode_step_impl(c, n_req, states, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out,
+                          score_out, out, stream, false);
+}
+
+hsa_status hsa_decode_step_noalloc(hsa_ctx* c, int32_t n_req, const int32_t* states,
+                                   const void* k_new, const void* v_new, const float* idx_new,
+                                   const void* q, const float* q_idx, int32_t k, uint32_t flags,
+                                   int32_t* topk_out, float* score_out, float* out, void* stream) {
+  return decode_step_impl(c, n_req, states, k_new, v_new, idx_new, q, q_idx, k, flags, topk_out,
+                          score_out, out, stream, true);
+}
+
+hsa_status hsa_noalloc_scratch_bytes(int64_t* bytes) {
+  if (!bytes) return fail(kInvalid, "NULL argument");
+  *bytes = (int64_t)kNoAllocScratchBytes;
+  return kOk;
 }
 
 hsa_status hsa_set_layer(hsa_ctx* c, int32_t layer) {

@@ -322,6 +322,27 @@ hsa_status hsa_decode_step(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
                            const void* q, const float* q_idx, int32_t k, uint32_t flags,
                            int32_t* topk_out, float* score_out, float* out, void* stream);
 
+/* hsa_decode_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, results and errors as hsa_decode_step, and the same kernels; every
+ * kernel's scratch (score rows, attention partials, selected rows, top-k candidates,
+ * seal partials) comes from one fixed device buffer of hsa_noalloc_scratch_bytes
+ * bytes (32 MiB) that the library holds on each GPU until the process ends, so the
+ * call allocates no device memory and never synchronises the device (it makes
+ * no timing records either). A step whose largest batch of 64 requests needs more
+ * scratch than the buffer holds returns HSA_ERR_INVALID before anything changes
+ * (the need grows with the batch's longest score row: 128 B per sealed block of it
+ * for each of the batch's requests, up to 64). Every context on a GPU shares that
+ * GPU's buffer, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap on one GPU - on different streams, or from different
+ * contexts - race, so issue them in one stream order. */
+hsa_status hsa_decode_step_noalloc(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
+                                   const void* k_new, const void* v_new, const float* idx_new,
+                                   const void* q, const float* q_idx, int32_t k, uint32_t flags,
+                                   int32_t* topk_out, float* score_out, float* out, void* stream);
+/* Size in bytes of the fixed scratch buffer of hsa_decode_step_noalloc. */
+hsa_status hsa_noalloc_scratch_bytes(int64_t* bytes);
+
 /* Select the layer that data calls act on (0 <= layer < n_layers). Errors: INVALID. */
 hsa_status hsa_set_layer(hsa_ctx* ctx, int32_t layer);
 
