@@ -147,8 +147,19 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_I32_MIN, _I32_MAX = -(1 << 31), (1 << 31) - 1
+
+
 def _host_i32(a):
-    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    """Host int32 copy of ids; values outside int32 raise OverflowError (a cast
+    would wrap them onto other, valid ids)."""
+    a = np.asarray(a)
+    if a.size and a.dtype != np.int32:
+        if a.dtype.kind not in "iu":
+            a = a.astype(np.int64)
+        if int(a.min()) < _I32_MIN or int(a.max()) > _I32_MAX:
+            raise OverflowError("an id does not fit int32")
+    a = np.ascontiguousarray(a.astype(np.int32, copy=False).reshape(-1))
     return a, a.ctypes.data_as(ctypes.c_void_p)
 
 

@@ -75,3 +75,13 @@ def test_state_list_marshalling():
         assert n == len(ids) and np.array_equal(got, np.asarray(ids, np.int64))
     with pytest.raises(OverflowError):
         _host_i32_fast([2 ** 31])
+    # arrays too: an int64 id past int32 must not wrap onto a valid id
+    for bad in (np.array([2 ** 32 + 3], np.int64), np.array([1, -(2 ** 31) - 1], np.int64),
+                np.array([2 ** 31], np.uint64)):
+        with pytest.raises(OverflowError):
+            _host_i32_fast(bad)
+    from heterogeneous_sparse_attention_amd import _host_i32
+    with pytest.raises(OverflowError):
+        _host_i32(np.array([2 ** 31, 2 ** 32 + 3], np.int64))
+    a, _ = _host_i32(np.array([-(2 ** 31), 2 ** 31 - 1], np.int64))
+    assert a.dtype == np.int32 and a.tolist() == [-(2 ** 31), 2 ** 31 - 1]
