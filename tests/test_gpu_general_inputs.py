@@ -1,0 +1,296 @@
+"""GPU parity on general inputs, where float32 rounding decides close calls.
+
+The other GPU tests feed dyadic inputs, on which the GPU's float32 indexer scores
+equal the oracle's float64 ones, so their top-k comparisons are bit-exact. Here the
+indexer keys and queries are float32 draws of N(0, 1), so every score rounds. K and
+Q are bf16 roundings of 3 N(0, 1), so attention logits q.k / sqrt(128) have a
+standard deviation of about 9 and span about +-30 over a request's keys. V is a
+bf16 rounding of N(0, 1). Everything is uploaded from the host.
+
+The workload has the b32 shape: 32 requests, L0 ~ U{1..8192}, n_win 128, k 512.
+A few lengths sit just below a block boundary, so that some steps seal a block.
+Bars, against the fp64 oracle fed the same values:
+- top-k rows: accepted within the tie band. The row must have kk distinct entries,
+  -1 after them, in ascending ordinals (or with scores non-increasing when sorted).
+  Every entry that differs from the oracle's selection must have an oracle score
+  within 1e-4 max(1, |tau|) of the oracle's kk-th score tau.
+- returned scores: each within float32 summation error of the oracle's score of
+  the same entry. The bound is 1024 products times 2^-24 times the sum of their
+  magnitudes.
+- attention: rel L2 <= 1e-3 against the oracle's attention over the GPU's own
+  selection (inside the tie band several selections are correct).
+- the integer state: bit-exact.
+Both step forms are covered: the three-launch form (the default for these rows),
+and the four-launch form (forced by HSA_STEP_FUSED=0, and by sorted rows). So are
+the standalone hsa_indexer_topk and hsa_decode_attend (after the three-launch
+steps).
+"""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import BLOCK, M_CSA, Oracle, select_topk, token_scores
+from tests.gpu_util import rel_l2, topk_accept
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+EPS_REL = 1e-4
+SEED = 0x47454E
+N_REQ, N_WIN, K = 32, 128, 512
+KQ_SCALE = 3.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import heterogeneous_sparse_attention_amd as hsa
+    hsa.load()          # raises if the library is missing: no fallback
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bf16_bits(x):
+    """float32 -> bf16 bit patterns, round to nearest even (finite values)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_vals(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+class GeneralTokens:
+    """Request b's tokens: K, Q = bf16(3 N(0,1)), V = bf16(N(0,1)), indexer keys and
+    queries float32 N(0,1); position p's values come from rng((seed, b, p // 1024))."""
+
+    CH = 1024
+
+    def __init__(self, b):
+        self.b = b
+        self._cache = {}
+
+    def _chunk(self, c):
+        if c not in self._cache:
+            rng = np.random.default_rng([SEED, self.b, c])
+            n = self.CH
+            K = bf16_bits(KQ_SCALE * rng.standard_normal((n, 16, 128), np.float32))
+            V = bf16_bits(rng.standard_normal((n, 16, 128), np.float32))
+            KI = rng.standard_normal((n, 4, 64), np.float32)
+            Q = bf16_bits(KQ_SCALE * rng.standard_normal((n, 16, 128), np.float32))
+            QI = rng.standard_normal((n, 4, 64), np.float32)
+            self._cache = {c: (K, V, KI, Q, QI)}   # keep one chunk: positions are read in order
+        return self._cache[c]
+
+    def rows(self, pos):
+        """bf16 bits of K, V, Q and float32 indexer keys and queries at positions."""
+        pos = np.asarray(pos, np.int64).reshape(-1)
+        out = [[] for _ in range(5)]
+        for c in np.unique(pos // self.CH):
+            sel = pos[pos // self.CH == c] % self.CH
+            for i, a in enumerate(self._chunk(int(c))):
+                out[i].append(a[sel])
+        return [np.concatenate(o) for o in out]
+
+
+def lengths():
+    L0 = np.random.default_rng(SEED).integers(1, 8193, size=N_REQ).astype(np.int64)
+    L0[:4] = [127, 1023, 4094, 8191]     # these seal a block within the first steps
+    return L0
+
+
+def to_dev(bits_or_f32, bf16):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits_or_f32))
+    if bf16:
+        return t.view(torch.int16).cuda().view(torch.bfloat16)
+    return t.cuda()
+
+
+def build(monkeypatch, fused):
+    """The GPU cache and the oracle, both prefilled with the same tokens."""
+    from heterogeneous_sparse_attention_amd import Cache
+    if not fused:
+        monkeypatch.setenv("HSA_STEP_FUSED", "0")
+    L0 = lengths()
+    Wc, Wh = synth.gate_weights(SEED)
+    nb = int(((L0 + 16) // BLOCK).sum()) + N_REQ
+    cache = Cache(N_WIN, N_REQ, nb, Wc, Wh)
+    o = Oracle(N_WIN, Wc, Wh, N_REQ, nb)
+    srcs = [GeneralTokens(b) for b in range(N_REQ)]
+    st = [cache.state_alloc() for _ in range(N_REQ)]
+    assert st == [o.state_alloc() for _ in range(N_REQ)]
+    for b in range(N_REQ):
+        K, V, KI, _, _ = srcs[b].rows(np.arange(L0[b]))
+        cache.append_kv([st[b]], [0, int(L0[b])], to_dev(K, True), to_dev(V, True), to_dev(KI, False))
+        o.append([st[b]], [(bf16_vals(K), bf16_vals(V), KI)])
+    return cache, o, st, srcs, L0
+
+
+def check_row(o, s, idx, val, qi, k, sorted=False):
+    """One request's top-k row (and scores) against the oracle, within the tie band.
+    Returns the number of entries that differ from the oracle's selection."""
+    ref = o.scores(s, qi)
+    assert topk_accept(idx, val, ref, k, eps_rel=EPS_REL, sorted=sorted)
+    kk = min(k, len(ref))
+    assert np.all(np.isneginf(val[kk:]))
+    if kk == 0:
+        return 0
+    sel = idx[:kk].astype(np.int64)
+    # float32 summation error of each selected score: 1024 products, each sum
+    # rounding by at most 2^-24 of the magnitudes summed so far
+    tab = o.table(s)
+    keys = np.stack([o.block(tab[j // 32]).idx[4 * (j % 32):4 * (j % 32) + 4] for j in sel])
+    mag = np.abs(keys.reshape(kk, 4 * 256).astype(np.float64)) @ np.tile(np.abs(qi.reshape(256)), 4)
+    bound = 1024 * 2.0 ** -24 * mag / 4
+    assert np.all(np.abs(val[:kk].astype(np.float64) - ref[sel]) <= bound)
+    ref_idx, _ = select_topk(ref, k)
+    return len(set(sel.tolist()) ^ set(ref_idx[:kk].tolist()))
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["three_launch", "four_launch"])
+def test_general_inputs_decode_steps(monkeypatch, fused):
+    import torch
+    cache, o, st, srcs, L0 = build(monkeypatch, fused)
+    say(f"general inputs ({'three' if fused else 'four'}-launch form): prefilled {int(L0.sum())} tokens")
+    try:
+        L = L0.copy()
+        topk = torch.empty((N_REQ, K), dtype=torch.int32, device="cuda")
+        sc = torch.empty((N_REQ, K), dtype=torch.float32, device="cuda")
+        out = torch.empty((N_REQ, 16, 128), dtype=torch.float32, device="cuda")
+        swaps = worst = 0.0
+        steps = 6
+        for t in range(steps + 2):
+            sorted_ = t >= steps          # the last two steps return sorted rows
+            rows = [srcs[b].rows([L[b]]) for b in range(N_REQ)]
+            Kn, Vn, KIn, Qn, QIn = (np.concatenate([r[i] for r in rows]) for i in range(5))
+            cache.decode_step(st, to_dev(Kn, True), to_dev(Vn, True), to_dev(KIn, False),
+                              to_dev(Qn, True), to_dev(QIn, False), K, topk_out=topk, score_out=sc,
+                              out=out, sorted=sorted_)
+            torch.cuda.synchronize()
+            g_idx, g_val, g_out = topk.cpu().numpy(), sc.cpu().numpy(), out.cpu().numpy()
+            for b in range(N_REQ):
+                o.append([st[b]], [(bf16_vals(Kn[b:b + 1]), bf16_vals(Vn[b:b + 1]), KIn[b:b + 1])])
+                swaps += check_row(o, st[b], g_idx[b], g_val[b], QIn[b], K, sorted=sorted_)
+                r = rel_l2(g_out[b], o.attend(st[b], bf16_vals(Qn[b]), g_idx[b], K))
+                assert r <= TOL, (t, b, r)
+                worst = max(worst, r)
+            L += 1
+        for b in range(N_REQ):
+            info, oi = cache.state_query(st[b]), o.info(st[b])
+            assert info["len"] == oi["len"] and info["n_blocks"] == oi["n_blocks"]
+            assert cache.block_table(st[b]) == o.table(st[b])
+        say(f"general inputs: {steps + 2} steps x {N_REQ} requests, worst rel L2 {worst:.2e}, "
+            f"{int(swaps)} entries swapped inside the tie band")
+        if fused:
+            standalone_calls(cache, o, st)
+    finally:
+        cache.close()
+
+
+def standalone_calls(cache, o, st):
+    """hsa_indexer_topk (ascending and sorted rows) and hsa_decode_attend on general
+    inputs; k from 1 to past every candidate."""
+    import torch
+    rng = np.random.default_rng(SEED + 1)
+    qi = rng.standard_normal((N_REQ, 4, 64), np.float32)
+    q = bf16_bits(KQ_SCALE * rng.standard_normal((N_REQ, 16, 128), np.float32))
+    for k, sorted_ in ((1, False), (512, False), (512, True), (2048, False), (4096, True)):
+        val = torch.empty((N_REQ, k), dtype=torch.float32, device="cuda")
+        idx, _ = cache.indexer_topk(st, to_dev(qi, False), k, score_out=val, sorted=sorted_)
+        out = cache.decode_attend(st, to_dev(q, True), idx, k)
+        torch.cuda.synchronize()
+        g_idx, g_val, g_out = idx.cpu().numpy(), val.cpu().numpy(), out.cpu().numpy()
+        for b in range(N_REQ):
+            check_row(o, st[b], g_idx[b], g_val[b], qi[b], k, sorted=sorted_)
+            r = rel_l2(g_out[b], o.attend(st[b], bf16_vals(q[b]), g_idx[b], k))
+            assert r <= TOL, (k, b, r)
+
+
+def test_near_tie_cluster(monkeypatch):
+    """The cut falls inside a cluster of near-equal scores, so float32 rounding
+    reorders entries near it. Every indexer key of a request is one base vector plus
+    a relative perturbation of 1e-7, so the request's C4 scores agree to about 1e-6.
+    The oracle ranks them by the perturbations; the GPU's float32 sums differ from
+    the float64 ones by about as much. Both step forms, and sorted rows. The rows are
+    accepted within the tie band, and attention matches the oracle's over the GPU's
+    selection. At least one entry must differ from the oracle's selection, so that
+    the band is really used."""
+    import torch
+    from heterogeneous_sparse_attention_amd import Cache
+    n_req, k = 6, 512
+    rng = np.random.default_rng(SEED + 7)
+    L0 = np.array([8192, 8200, 6000, 4100, 8191, 300])
+    Wc, Wh = synth.gate_weights(SEED)
+    swaps = 0
+    for fused in (True, False):
+        if not fused:
+            monkeypatch.setenv("HSA_STEP_FUSED", "0")
+        nb = int(((L0 + 8) // BLOCK).sum()) + n_req
+        cache = Cache(N_WIN, n_req, nb, Wc, Wh)
+        o = Oracle(N_WIN, Wc, Wh, n_req, nb)
+        try:
+            st = [cache.state_alloc() for _ in range(n_req)]
+            assert st == [o.state_alloc() for _ in range(n_req)]
+            base = rng.standard_normal((n_req, 4, 64)).astype(np.float32)
+            srcs = [GeneralTokens(100 + b) for b in range(n_req)]
+
+            def near(b, n):
+                return (base[b] * (1 + 1e-7 * rng.standard_normal((n, 4, 64)))).astype(np.float32)
+
+            for b in range(n_req):
+                K, V, _, _, _ = srcs[b].rows(np.arange(L0[b]))
+                KI = near(b, L0[b])
+                cache.append_kv([st[b]], [0, int(L0[b])], to_dev(K, True), to_dev(V, True), to_dev(KI, False))
+                o.append([st[b]], [(bf16_vals(K), bf16_vals(V), KI)])
+            L = L0.copy()
+            topk = torch.empty((n_req, k), dtype=torch.int32, device="cuda")
+            sc = torch.empty((n_req, k), dtype=torch.float32, device="cuda")
+            out = torch.empty((n_req, 16, 128), dtype=torch.float32, device="cuda")
+            for t in range(4):
+                sorted_ = t == 3
+                rows = [srcs[b].rows([L[b]]) for b in range(n_req)]
+                Kn, Vn, _, Qn, _ = (np.concatenate([r[i] for r in rows]) for i in range(5))
+                KIn = np.concatenate([near(b, 1) for b in range(n_req)])
+                QIn = rng.standard_normal((n_req, 4, 64)).astype(np.float32)
+                cache.decode_step(st, to_dev(Kn, True), to_dev(Vn, True), to_dev(KIn, False),
+                                  to_dev(Qn, True), to_dev(QIn, False), k, topk_out=topk, score_out=sc,
+                                  out=out, sorted=sorted_)
+                torch.cuda.synchronize()
+                g_idx, g_val, g_out = topk.cpu().numpy(), sc.cpu().numpy(), out.cpu().numpy()
+                for b in range(n_req):
+                    o.append([st[b]], [(bf16_vals(Kn[b:b + 1]), bf16_vals(Vn[b:b + 1]), KIn[b:b + 1])])
+                    swaps += check_row(o, st[b], g_idx[b], g_val[b], QIn[b], k, sorted=sorted_)
+                    r = rel_l2(g_out[b], o.attend(st[b], bf16_vals(Qn[b]), g_idx[b], k))
+                    assert r <= TOL, (fused, t, b, r)
+                L += 1
+            # the standalone top-k on the same cluster
+            QI = rng.standard_normal((n_req, 4, 64)).astype(np.float32)
+            val = torch.empty((n_req, k), dtype=torch.float32, device="cuda")
+            idx, _ = cache.indexer_topk(st, to_dev(QI, False), k, score_out=val)
+            torch.cuda.synchronize()
+            for b in range(n_req):
+                swaps += check_row(o, st[b], idx.cpu().numpy()[b], val.cpu().numpy()[b], QI[b], k)
+        finally:
+            cache.close()
+    say(f"near-tie cluster: {swaps} entries differ from the oracle's selection, all inside the tie band")
+    assert swaps > 0
+
+
+def test_general_inputs_host_pins():
+    """The inputs are what the docstring says (checked on the host): the scores do
+    round in float32, and the logits do span about +-30."""
+    src = GeneralTokens(0)
+    K, V, KI, Q, QI = src.rows(np.arange(600))
+    s32 = (KI.reshape(600, 256).astype(np.float32) @ QI[0].reshape(256).astype(np.float32))
+    s64 = token_scores(KI.astype(np.float64), QI[0].astype(np.float64))
+    assert np.mean(s32.astype(np.float64) != s64) > 0.5
+    logits = np.einsum("hd,thd->th", bf16_vals(Q[0]).astype(np.float64),
+                       bf16_vals(K).astype(np.float64)) / np.sqrt(128.0)
+    assert 20 < np.abs(logits).max() < 60 and 6 < logits.std() < 12
+    assert M_CSA == 4
