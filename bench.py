@@ -290,53 +290,73 @@ def decode_inputs(wl, L0: np.ndarray, n_steps: int, seed=None):
     return {n_: x.view(n_steps, B, *x.shape[1:]) for n_, x in t.items()}
 
 
+def gpu_lead(cycles: int = 500_000):
+    """Keep the GPU busy for about 0.2 ms (a spin kernel) so that the host queues the
+    first timed steps before the start event fires: the timed region then holds the
+    steps' GPU time back to back, without the host's latency to its first launch."""
+    import torch
+    try:
+        torch.cuda._sleep(cycles)
+    except (AttributeError, RuntimeError):
+        pass
+
+
 def run_decode(args) -> dict:
     import torch
     wl = workloads.make(args.workload)
     B, k = wl.batch, wl.topk
     W, K = args.warmup, args.steps
+    reps = max(1, args.repeats)
     layers = args.layers.split(",") * args.layer_repeat if args.layers else None
     types = layers or ["mixed"]
     # a layer stack streams different data layer after layer by itself: one copy
     R = args.copies if args.copies is not None else (4 if wl.name == "b32" and not layers else 1)
-    local_steps = (W + 2 * K + R - 1) // R
-    cache, inst = setup_decode(wl, local_steps, R, args.entries, args.index, layers, args.c4_mode)
+    # Cache instances: set 0 (R copies) takes the warmup, the per-kernel timing steps
+    # and the roofline pass; sets 1 .. reps (R copies each) each take one timed pass of
+    # K steps from the prefill lengths, i.e. every timed pass runs the same workload,
+    # as from a restored snapshot of the pools.
+    n_kt = max(4, min(K, 16))                     # steps per kernel in the kernel timing
+    set0 = W + len(STEP_KERNELS) * n_kt + K
+    local_steps = (max(set0, K) + R - 1) // R
+    cache, inst = setup_decode(wl, local_steps, R * (1 + reps), args.entries, args.index, layers,
+                               args.c4_mode)
     L0 = wl.prefill.astype(np.int64)
     inp = [decode_inputs(wl, L0, local_steps, seed=layer_seed(wl, l)) for l in range(len(types))]
     topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
     out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
 
-    # step t advances instance t % R by its step t // R: consecutive steps read
-    # different copies of the cache, as consecutive layers of a model would; a step
-    # of a layer stack is one decode step of every layer, in layer order
-    def step(t):
+    # step t of set c advances instance c R + t % R by its step t // R: consecutive
+    # steps read different copies of the cache, as consecutive layers of a model
+    # would; a step of a layer stack is one decode step of every layer, in layer order
+    def step(t, c=0):
         j = t // R
         for l, x in enumerate(inp):
             if layers:
                 cache.set_layer(l)
-            cache.decode_step(inst[t % R], x["k"][j], x["v"][j], x["ki"][j], x["q"][j],
+            cache.decode_step(inst[c * R + t % R], x["k"][j], x["v"][j], x["ki"][j], x["q"][j],
                               x["qi"][j], k, topk_out=topk, out=out)
 
-    # warmup; its second half times one kernel per step, in rotation, with the steps
-    # back to back, to find the dominant one. (With an event pair on every kernel of
-    # a step, the first kernel's start event can fire while the host is still
-    # writing that kernel's dispatch, which inflates it whenever the host falls
-    # behind; the roofline pass below also times one kernel only.)
-    half = W // 2
-    for t in range(half):
+    for t in range(W):                            # warmup
         step(t)
     torch.cuda.synchronize()
-    order = ("step2", "step1", "step3", "step4", "step2b")
-    timed_at = {n: [] for n in STEP_KERNELS}
-    for j, t in enumerate(range(half, W)):
-        n = order[j % len(order)]
+    # per-kernel timing: n_kt steps per step kernel, one kernel timed at a time (an
+    # event pair on every kernel of a step lets the first kernel's start event fire
+    # while the host still writes its dispatch, which inflates it whenever the host
+    # falls behind)
+    t_next = W
+    per_step, timed_at, launches = {}, {}, {}
+    for n in STEP_KERNELS:
         cache.timing_enable([n])
-        timed_at[n].append(t)
-        step(t)
-    torch.cuda.synchronize()
-    warm = cache.timing_read()
+        gpu_lead()
+        timed_at[n] = list(range(t_next, t_next + n_kt))
+        for t in timed_at[n]:
+            step(t)
+        t_next += n_kt
+        torch.cuda.synchronize()
+        ms_, cnt = cache.timing_read()[n]
+        per_step[n] = ms_ / n_kt
+        launches[n] = cnt
     cache.timing_enable([])
-    per_step = {n: warm[n][0] / len(timed_at[n]) if timed_at[n] else 0.0 for n in STEP_KERNELS}
     dominant = args.kernel or max(STEP_KERNELS, key=lambda n: per_step[n])
     # the byte split assumes the library's choice of form; check it against the launches
     def open_g(L):
@@ -344,30 +364,37 @@ def run_decode(args) -> dict:
     def fused_at(t):
         return step_fused((L0 + t // R + 1) // 128, open_g(L0 + t // R + 1))
     has_c4 = any(ty in ("mixed", "csa") for ty in types)   # layers with a part B
-    if timed_at["step3"] and (warm["step3"][1] > 0) != (has_c4 and not all(map(fused_at, timed_at["step3"]))):
+    if (launches["step3"] > 0) != (has_c4 and not all(map(fused_at, timed_at["step3"]))):
         raise RuntimeError("decode-step form differs from the one the byte split assumes")
 
-    # timed pass 1 (value): whole steps between two events, nothing inside
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for t in range(W, W + K):
-        step(t)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
-
-    # timed pass 2 (roofline): the next K steps, the library attaching a start/stop
-    # event pair to each dispatch of the dominant kernel on the launch stream
+    # roofline pass: K steps of set 0, the library attaching a start/stop event pair
+    # to each dispatch of the dominant kernel on the launch stream
     cache.timing_enable([dominant])
-    torch.cuda.synchronize()
-    for t in range(W + K, W + 2 * K):
+    roof_from = t_next
+    gpu_lead()
+    for t in range(roof_from, roof_from + K):
         step(t)
     torch.cuda.synchronize()
     kt = cache.timing_read()
     cache.timing_enable([])
+
+    # timed passes (value): whole steps between two events, nothing inside; one pass
+    # per set of fresh copies, the median reported
+    times, walls = [], []
+    for c in range(1, reps + 1):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gpu_lead()
+        ev0.record()
+        for t in range(K):
+            step(t, c)
+        ev1.record()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        times.append(ev0.elapsed_time(ev1))
+    ms_total = float(np.median(times))
+    wall = float(np.median(walls))
 
     def bytes_over(t_from, t_to):
         acc = {n: 0 for n in STEP_KERNELS + ("step",)}
@@ -381,8 +408,8 @@ def run_decode(args) -> dict:
                     acc[n] += sb[n]
         return acc
 
-    bytes_1 = bytes_over(W, W + K)
-    bytes_2 = bytes_over(W + K, W + 2 * K)
+    bytes_1 = bytes_over(0, K)                       # every timed pass
+    bytes_2 = bytes_over(roof_from, roof_from + K)
     ms_per_step = ms_total / K
     dom_ms, dom_n = kt[dominant]
     achieved = (bytes_2[dominant] / dom_n) / (dom_ms / dom_n * 1e-3) / 1e9 if dom_n else None
@@ -431,6 +458,9 @@ def run_decode(args) -> dict:
         "hbm_frac_of_peak": step_gbs / PEAK_HBM_GBS,
         "bytes_per_step": bytes_1["step"] / K,
         "wall_s": wall,
+        "timed_passes_ms": times,
+        "timing": f"median of {reps} passes of {K} steps, each on its own fresh copies of the "
+                  f"prefilled cache; events around each pass",
         "roofline": {"bound": "hbm", "kernel": KERNEL_SYMBOL[dominant],
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": (achieved / PEAK_HBM_GBS) if achieved else None,
@@ -438,7 +468,7 @@ def run_decode(args) -> dict:
                      "avg_launch_us": (dom_ms / dom_n * 1e3) if dom_n else None,
                      "algorithmic_bytes_per_launch": (bytes_2[dominant] / dom_n) if dom_n else None,
                      "measured": f"HIP event pair attached to each {KERNEL_SYMBOL[dominant]} "
-                                 f"dispatch (hipExtLaunchKernel) over {K} further steps"},
+                                 f"dispatch (hipExtLaunchKernel) over {K} steps"},
         "kernels_us_per_step": {n: per_step[n] * 1e3 for n in STEP_KERNELS},
         "bytes_per_step_by_kernel": {n: bytes_1[n] / K for n in STEP_KERNELS},
     }
@@ -644,21 +674,22 @@ def run_hits(args) -> dict:
 
 # ------------------------------------------------------------------ CPU baseline (the oracle)
 
-def cpu_baseline(args, budget_s: float = 15.0) -> dict:
-    """The oracle, as it stands, on the host: decode steps of a sample of requests."""
+def _oracle_worker(job):
+    """One host worker of the CPU baseline: build the oracle state of its requests
+    (untimed), wait for the others, then run decode steps of its requests until the
+    budget is spent. Returns (tokens, seconds)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import Oracle
 
-    wl = workloads.make(args.workload)
+    index, reqs, budget_s, max_steps, barrier = job
+    wl = workloads.make(index)
     Wc, Wh = synth.gate_weights(wl.seed)
-    sample = list(range(wl.batch))
     L0 = wl.prefill.astype(np.int64)
-    max_steps = 128
     with threadpool_limits(1):
-        o = Oracle(wl.n_win, Wc, Wh, wl.batch, int((L0 // 128).sum()) + 64)
+        o = Oracle(wl.n_win, Wc, Wh, len(reqs), int((L0[reqs] // 128).sum()) + len(reqs) * (max_steps // 128 + 2))
         st = {}
-        for b in sample:                              # untimed: build the prefill state
+        for b in reqs:
             st[b] = o.state_alloc()
             pos = np.arange(L0[b])
             key = np.full(pos.shape, b, np.uint64)
@@ -666,33 +697,57 @@ def cpu_baseline(args, budget_s: float = 15.0) -> dict:
             V = synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_V, key, pos))
             KI = synth.tokens_f32(wl.seed, synth.STREAM_IDXK, key, pos)
             o.append([st[b]], [(K, V, KI)])
-        inputs = []
-        for t in range(max_steps):                    # untimed: the decode inputs
-            row = []
-            for b in sample:
-                p = np.array([L0[b] + t])
-                key = np.array([b], np.uint64)
-                row.append((synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_K, key, p)),
-                            synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_V, key, p)),
-                            synth.tokens_f32(wl.seed, synth.STREAM_IDXK, key, p),
-                            synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_Q, key, p))[0],
-                            synth.tokens_f32(wl.seed, synth.STREAM_QI, key, p)[0]))
-            inputs.append(row)
+        steps_in = {}                                 # each request's decode inputs, by step
+        for b in reqs:
+            p = L0[b] + np.arange(max_steps)
+            key = np.full(p.shape, b, np.uint64)
+            steps_in[b] = (synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_K, key, p)),
+                           synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_V, key, p)),
+                           synth.tokens_f32(wl.seed, synth.STREAM_IDXK, key, p),
+                           synth.bf16_bits_to_f32(synth.tokens_bf16(wl.seed, synth.STREAM_Q, key, p)),
+                           synth.tokens_f32(wl.seed, synth.STREAM_QI, key, p))
+        inputs = [[tuple(a[t:t + 1] for a in steps_in[b][:3]) + (steps_in[b][3][t], steps_in[b][4][t])
+                   for b in reqs] for t in range(max_steps)]
+        barrier.wait()
         t0 = time.perf_counter()
-        steps = 0
+        tokens = 0
         for t in range(max_steps):
-            for b, (K, V, KI, q, qi) in zip(sample, inputs[t]):
+            for b, (K, V, KI, q, qi) in zip(reqs, inputs[t]):
                 o.append([st[b]], [(K, V, KI)])
                 idx, _ = o.topk(st[b], qi, wl.topk)
                 o.attend(st[b], q, idx, wl.topk)
-            steps += 1
+            tokens += len(reqs)
             if time.perf_counter() - t0 > budget_s:
                 break
-        dt = time.perf_counter() - t0
-    return {"value": len(sample) * steps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(sample)} of {wl.batch} requests, {steps} decode steps each "
-                      f"(append with seals, indexer top-k, attention; fp64 NumPy, 1 thread), "
-                      f"{dt:.1f} s"}
+        return tokens, time.perf_counter() - t0
+
+
+def cpu_baseline(args, budget_s: float = 10.0) -> dict:
+    """The oracle, as it stands, on the host's cores: the batch's requests split over
+    worker processes (one BLAS thread each), each running decode steps of its
+    requests (append with seals, indexer top-k, attention) for about budget_s."""
+    import multiprocessing as mp
+
+    wl = workloads.make(args.workload)
+    visible = len(os.sched_getaffinity(0))
+    # the host's share of cores for this GPU: the affinity set, capped by the thread
+    # count the environment grants (OMP_NUM_THREADS)
+    share = int(os.environ.get("OMP_NUM_THREADS", visible) or visible)
+    workers = max(1, min(visible, share, wl.batch))
+    groups = [list(range(w, wl.batch, workers)) for w in range(workers)]
+    ctx = mp.get_context("spawn")            # the workers never touch the GPU
+    with ctx.Manager() as mgr:
+        barrier = mgr.Barrier(workers)
+        with ctx.Pool(workers) as pool:
+            res = pool.map(_oracle_worker, [(args.workload, g, budget_s, 3072, barrier) for g in groups])
+    tokens = sum(r[0] for r in res)
+    secs = max(r[1] for r in res)
+    steps = [r[0] // len(g) for r, g in zip(res, groups)]
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpus_visible": visible, "blas_threads_per_worker": 1,
+            "sample": f"all {wl.batch} requests over {workers} worker processes (one BLAS thread each); "
+                      f"{min(steps)}-{max(steps)} decode steps per request (append with seals, indexer "
+                      f"top-k, attention; fp64 NumPy) in {secs:.1f} s; prefill state built untimed"}
 
 
 # ------------------------------------------------------------------ counters
@@ -768,6 +823,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed passes of --steps steps, each on fresh copies; the median is reported")
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="1 l130, 2 b32 (the headline), 3 prefix, 4 bulk append, 5 long")
     ap.add_argument("--kernel", default=None, help="time this kernel in the timed region")
