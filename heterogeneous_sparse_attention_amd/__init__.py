@@ -26,6 +26,7 @@ APPEND_DEFER_SEAL = 1
 KERNELS = ("append", "seal", "write", "score", "select", "attend", "merge",
            "step1", "step2", "step3", "step4", "step2b")
 TOPK_SORTED = 1
+CREATE_POISON = 1
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "Block Cache full", -3: "no free State slot",
@@ -48,7 +49,7 @@ class _Config(ctypes.Structure):
                 ("gate_hca", ctypes.POINTER(ctypes.c_float)),
                 ("entry_format", ctypes.c_int32), ("index_format", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("layer_types", ctypes.c_void_p),
-                ("c4_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("c4_mode", ctypes.c_int32), ("create_flags", ctypes.c_uint32)]
 
 ENTRY_FORMATS = {"bf16": 0, "fp8": 1}     # HSA_ENTRY_BF16, HSA_ENTRY_FP8
 INDEX_FORMATS = {"f32": 0, "mxfp4": 1}    # HSA_INDEX_F32, HSA_INDEX_MXFP4
@@ -198,9 +199,12 @@ class Cache:
 
     def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
                  max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16",
-                 index_format: str = "f32", layer_types=None, c4_mode: str = "sealed"):
+                 index_format: str = "f32", layer_types=None, c4_mode: str = "sealed",
+                 poison: bool = False):
         """layer_types: None (one heterogeneous layer) or a list of "mixed", "swa",
-        "csa", "hca"; then gate_csa / gate_hca hold one [16][128] set per layer."""
+        "csa", "hca"; then gate_csa / gate_hca hold one [16][128] set per layer.
+        poison: fill every pool and scratch buffer with NaN bytes when allocated
+        (HSA_CREATE_POISON), so that reads of never-written slots show."""
         lib = load()
         if entry_format not in ENTRY_FORMATS:
             raise ValueError(f"entry_format must be one of {sorted(ENTRY_FORMATS)}")
@@ -222,7 +226,8 @@ class Cache:
                       self._gc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       ENTRY_FORMATS[entry_format], INDEX_FORMATS[index_format], nl,
-                      self._lt.ctypes.data_as(ctypes.c_void_p), C4_MODES[c4_mode], 0)
+                      self._lt.ctypes.data_as(ctypes.c_void_p), C4_MODES[c4_mode],
+                      CREATE_POISON if poison else 0)
         self.entry_format = entry_format
         self.index_format = index_format
         ctx = ctypes.c_void_p()

@@ -37,6 +37,7 @@ int fail(int code, const std::string& why) {
 
 struct hsa_ctx {
   int device = 0;
+  bool poison = false;        // HSA_CREATE_POISON: fill every allocation with 0xFF bytes
   Control ctl;
   Pools P{};
   std::vector<void*> allocs;
@@ -109,6 +110,10 @@ namespace {
 int dev_alloc(hsa_ctx* c, void** p, size_t bytes) {
   HIP_TRY(hipMalloc(p, bytes ? bytes : 16));
   c->allocs.push_back(*p);
+  if (c->poison) {   // a debugging aid: never on a hot path (allocations are not)
+    HIP_TRY(hipMemset(*p, 0xff, bytes ? bytes : 16));
+    HIP_TRY(hipDeviceSynchronize());
+  }
   return kOk;
 }
 
@@ -712,6 +717,7 @@ int check_config(const hsa_config* cfg) {
   if (cfg->index_format != HSA_INDEX_F32 && cfg->index_format != HSA_INDEX_MXFP4)
     return fail(kInvalid, "index_format must be HSA_INDEX_F32 or HSA_INDEX_MXFP4");
   if (cfg->n_layers < 0 || cfg->n_layers > 1024) return fail(kInvalid, "n_layers must be in [0, 1024]");
+  if (cfg->create_flags & ~HSA_CREATE_POISON) return fail(kInvalid, "unknown create_flags");
   if (cfg->c4_mode != HSA_C4_SEALED && cfg->c4_mode != HSA_C4_EAGER)
     return fail(kInvalid, "c4_mode must be HSA_C4_SEALED or HSA_C4_EAGER");
   if (cfg->c4_mode == HSA_C4_EAGER &&
@@ -742,6 +748,7 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   const int64_t bps = cfg->max_blocks_per_state ? cfg->max_blocks_per_state : cfg->max_blocks;
   hsa_ctx* c = new hsa_ctx(cfg->n_win, cfg->max_states, cfg->max_blocks, bps);
   c->device = device;
+  c->poison = (cfg->create_flags & HSA_CREATE_POISON) != 0;
   c->fixed = fixed;
   if (!std::getenv("HSA_STEP_SLOTS")) {   // one step-kernel workgroup per CU
     int n_cu = 0;

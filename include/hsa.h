@@ -91,8 +91,14 @@ typedef struct hsa_config {
   const int32_t* layer_types;   /* host [n_layers] HSA_LAYER_*, copied; NULL: every
                                    layer HSA_LAYER_MIXED                            */
   int32_t c4_mode;              /* HSA_C4_SEALED or HSA_C4_EAGER                    */
-  int32_t reserved;             /* 0                                                */
+  uint32_t create_flags;        /* 0 or HSA_CREATE_POISON                           */
 } hsa_config;
+
+/* Create flag: fill every pool and every scratch buffer with 0xFF bytes when it is
+ * allocated (bf16, fp32 and E4M3 NaN, E8M0 NaN scales, table entries -1), so that a
+ * read of a slot that was never written shows as NaN in the results. A debugging and
+ * test aid; it costs one device fill per allocation. */
+#define HSA_CREATE_POISON 1u
 
 /* When C4 entries exist. SEALED: a block's 32 entries are written when its 128 tokens
  * are complete ([Q&A] §3.1 block-level sealing). EAGER: each complete group of 4
