@@ -52,6 +52,16 @@ Readings taken where the pages leave a step open (each also in the design notes)
       in). A head whose s would not be a normal float32 (all zero, or max |x| below
       448 * 2**-126) keeps s = 1; its codes, by the same rule, are then all 0.
       HCA entries stay bf16.
+  R20 FP8 SWA ring and HCA entries (optional format, kv_format="fp8"): the pages
+      account every KV kind in FP8, the SWA's raw tokens and the HCA entries too
+      ([Ch12] §1 worked figures: SWA 2048 B, HCA 16 B per token), without a scale
+      scheme. Reading: the R15 per-head quantiser applied to each token's K and V as
+      it enters the State (the ring slot holds its codes and scales; the stored
+      value is code * s) and to each HCA entry as it is sealed (from the float64
+      pooled entry, in place of the bf16 rounding). The State keeps no other copy
+      of a token, so a block's compressor pools the stored (dequantized) K/V of its
+      128 tokens, and attention reads the stored values. Indexer keys are not
+      affected.
   R16 low-bit indexer keys (optional format): the pages store the indexer keys
       of the Block Cache as FP4 ([Ch12] §1 worked figures, §2.2) without a scale
       scheme. Reading: OCP MXFP4 (Microscaling Formats v1.0): each sealed key's
@@ -392,9 +402,11 @@ class _Block:
     ([Ch12] §2.2; [Q&A] §2.2). With FP8 entries (R15) csa_k / csa_v hold the stored
     values (code value * scale) and the codes and scales are kept beside them; with
     MXFP4 indexer keys (R16) idx holds the stored values and idx_codes / idx_scales
-    the codes and E8M0 scales."""
+    the codes and E8M0 scales; with FP8 KV (R20) hca_k / hca_v hold the stored HCA
+    values and hca_*_codes / hca_*_scale their codes and scales."""
     __slots__ = ("csa_k", "csa_v", "hca_k", "hca_v", "idx", "csa_k_codes", "csa_v_codes",
-                 "csa_k_scale", "csa_v_scale", "idx_codes", "idx_scales")
+                 "csa_k_scale", "csa_v_scale", "idx_codes", "idx_scales", "hca_k_codes", "hca_v_codes",
+                 "hca_k_scale", "hca_v_scale")
 
 
 class _State:
@@ -405,6 +417,8 @@ class _State:
     def __init__(self, n_win: int):
         self.L = 0
         self.swa = deque(maxlen=n_win)     # (K, V) per token; drops the oldest ([Q&A] §4)
+        self.swa_q = deque(maxlen=n_win)   # FP8 KV (R20): (K codes, K scales, V codes,
+                                           # V scales) of each window token, else None
         self.tail = []                     # (K, V, kI) per token of the open block
         self.blocks = []                   # physical block ids, logical order
 
@@ -414,7 +428,7 @@ class Oracle:
 
     def __init__(self, n_win: int, gate_csa, gate_hca, max_states: int, max_blocks: int,
                  entry_format: str = "bf16", index_format: str = "f32", layer_type: str = "mixed",
-                 c4_mode: str = "sealed"):
+                 c4_mode: str = "sealed", kv_format: str = "bf16"):
         if n_win < BLOCK or n_win % BLOCK:
             raise OracleError("invalid", "n_win must be a positive multiple of 128")
         if entry_format not in ("bf16", "fp8"):
@@ -425,8 +439,11 @@ class Oracle:
             raise OracleError("invalid", "layer type is mixed, swa, csa or hca")
         if c4_mode not in ("sealed", "eager"):
             raise OracleError("invalid", "c4 mode is sealed or eager")
-        if c4_mode == "eager" and (entry_format != "bf16" or index_format != "f32"):
-            raise OracleError("invalid", "eager C4 takes bf16 entries and f32 indexer keys")
+        if kv_format not in ("bf16", "fp8"):
+            raise OracleError("invalid", "kv format is bf16 or fp8")
+        if c4_mode == "eager" and (entry_format != "bf16" or index_format != "f32" or kv_format != "bf16"):
+            raise OracleError("invalid", "eager C4 takes bf16 entries, bf16 KV and f32 indexer keys")
+        self.kv_format = kv_format
         self.eager = c4_mode == "eager"                       # reading R19
         self.layer_type = layer_type
         self.has_c4 = layer_type in ("mixed", "csa")          # reading R18
@@ -445,6 +462,16 @@ class Oracle:
         self.refcount = np.zeros(self.max_blocks, np.int64)
         self.store: dict[int, _Block] = {}
         self.states: dict[int, _State] = {}
+
+    def _stored(self, K, V):
+        """A token's K and V as the State stores them: bf16 values as they come, or
+        (R20) the per-head FP8 storage: returns (k, v, q), q = (K codes, K scales,
+        V codes, V scales) with FP8 KV, else None."""
+        if self.kv_format != "fp8":
+            return np.asarray(K, dtype=np.float32), np.asarray(V, dtype=np.float32), None
+        kc, ks, kv_ = quantize_e4m3_rows(np.asarray(K, dtype=np.float64))
+        vc, vs, vv = quantize_e4m3_rows(np.asarray(V, dtype=np.float64))
+        return kv_, vv, (kc, ks, vc, vs)
 
     # -- State pool --------------------------------------------------------
     def state_alloc(self) -> int:
@@ -507,10 +534,10 @@ class Oracle:
         for s, (K, V, KI) in zip(states, tokens):
             st = self.states[s]
             for t in range(len(K)):
-                k = np.asarray(K[t], dtype=np.float32)
-                v = np.asarray(V[t], dtype=np.float32)
+                k, v, q = self._stored(K[t], V[t])
                 ki = np.asarray(KI[t], dtype=np.float32)
                 st.swa.append((k, v))
+                st.swa_q.append(q)
                 st.tail.append((k, v, ki))
                 st.L += 1
                 if len(st.tail) == BLOCK and not defer_seal:
@@ -543,8 +570,13 @@ class Oracle:
         st.blocks.append(b)
         if self.has_c4:
             self._seal_c4(blk, st, Kt, Vt)
-        if self.has_hca:
-            blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)     # all 128 tokens
+        if self.has_hca:                              # all 128 tokens
+            if self.kv_format == "fp8":               # reading R20
+                Kh, Vh = gated_pool(Kt, Vt, self.W_hca, rounded=False)
+                blk.hca_k_codes, blk.hca_k_scale, blk.hca_k = quantize_e4m3_rows(Kh)
+                blk.hca_v_codes, blk.hca_v_scale, blk.hca_v = quantize_e4m3_rows(Vh)
+            else:
+                blk.hca_k, blk.hca_v = gated_pool(Kt, Vt, self.W_hca)
         st.tail = []                                  # tail cleared ([Q&A] §3.1)
 
     def _seal_c4(self, blk: _Block, st: _State, Kt, Vt):
@@ -589,6 +621,7 @@ class Oracle:
         d.blocks = list(a.blocks)
         d.L = a.L
         d.swa = deque(a.swa, maxlen=self.n_win)
+        d.swa_q = deque(a.swa_q, maxlen=self.n_win)
         d.tail = list(a.tail)
 
     # -- prefix hits (reading R17) -------------------------------------------------
@@ -629,6 +662,7 @@ class Oracle:
         d.blocks = blocks
         d.L = length
         d.swa = deque([None] * min(length, self.n_win), maxlen=self.n_win)
+        d.swa_q = deque([None] * min(length, self.n_win), maxlen=self.n_win)
         d.tail = [None] * (length - BLOCK * nb)
 
     def state_write(self, states, tokens, pos0):
@@ -652,10 +686,10 @@ class Oracle:
             t0 = st.L - len(st.tail)                   # first position of the tail
             for t in range(len(K)):
                 p = int(p0) + t
-                k = np.asarray(K[t], dtype=np.float32)
-                v = np.asarray(V[t], dtype=np.float32)
+                k, v, q = self._stored(K[t], V[t])
                 if p >= w0:
                     st.swa[p - w0] = (k, v)
+                    st.swa_q[p - w0] = q
                 if p >= t0:
                     st.tail[p - t0] = (k, v, np.asarray(KI[t], dtype=np.float32))
 
@@ -664,7 +698,7 @@ class Oracle:
         st = self._get(s)
         if any(x is None for x in st.swa) or any(x is None for x in st.tail):
             raise OracleError("state", "state not filled")
-        return {"len": st.L, "swa": list(st.swa), "tail": list(st.tail)}
+        return {"len": st.L, "swa": list(st.swa), "swa_q": list(st.swa_q), "tail": list(st.tail)}
 
     def restore(self, s: int, ck: dict):
         """Fill a state attached at L >= c from the checkpoint taken at c: window
@@ -675,10 +709,11 @@ class Oracle:
         if c > st.L or c < 0:
             raise OracleError("invalid", "checkpoint is past the state's length")
         w0, t0 = st.L - len(st.swa), st.L - len(st.tail)
-        for i, item in enumerate(ck["swa"]):
+        for i, (item, q) in enumerate(zip(ck["swa"], ck["swa_q"])):
             p = c - len(ck["swa"]) + i
             if p >= w0:
                 st.swa[p - w0] = item
+                st.swa_q[p - w0] = q
         for i, item in enumerate(ck["tail"]):
             p = c - len(ck["tail"]) + i
             if p >= t0:

@@ -614,6 +614,137 @@ def test_quantize_rows_exact_fractions():
     assert np.all(codes[10:13, 1:126] % 2 == 0)
 
 
+# ------------------------------------------------------------------ FP8 SWA ring and HCA entries (R20)
+
+def fp8_grid_tokens(rng, n):
+    """Tokens every head of which already sits on its own E4M3 grid: values are E4M3
+    values times 2**e (one e per token, head and K/V) and each head holds +-448 * 2**e,
+    so the per-head quantiser stores them exactly (s = 2**e, x / s = a code value).
+    E4M3 values have at most 4 significant bits, so the tokens are bf16 values too."""
+    from oracle import e4m3_decode
+    codes = rng.integers(0, 0x7F, (2, n, N_HEADS, HEAD_DIM))
+    vals = e4m3_decode(codes) * np.where(rng.random(codes.shape) < 0.5, -1.0, 1.0)
+    vals[..., 0] = 448.0 * np.where(rng.random(vals.shape[:-1]) < 0.5, -1.0, 1.0)
+    e = rng.integers(-12, -6, (2, n, N_HEADS, 1)).astype(np.float64)
+    vals = vals * np.exp2(e)
+    assert np.array_equal(bf16_round(vals), vals)
+    return vals[0], vals[1]
+
+
+def test_fp8_kv_is_exact_on_fp8_grid_tokens():
+    """On tokens that the FP8 storage holds exactly, the FP8-KV oracle's window, C4
+    entries, top-k rows and attention equal the bf16 oracle's; its HCA entries are
+    the per-head E4M3 storage of the unrounded pooled entry of those tokens."""
+    from oracle import quantize_e4m3_rows
+    rng = np.random.default_rng(20)
+    Wc, Wh = synth.gate_weights(SEED)
+    K, V = fp8_grid_tokens(rng, 300)
+    KI = rng.standard_normal((300, 4, 64))
+    a = Oracle(128, Wc, Wh, 1, 4)
+    b = Oracle(128, Wc, Wh, 1, 4, kv_format="fp8")
+    for o in (a, b):
+        assert o.state_alloc() == 0
+        o.append([0], [(K[:257], V[:257], KI[:257])])
+    for (ka, va), (kb, vb) in zip(a.states[0].swa, b.states[0].swa):
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    for lb in range(2):
+        ba, bb = a.block(a.table(0)[lb]), b.block(b.table(0)[lb])
+        assert np.array_equal(ba.csa_k, bb.csa_k) and np.array_equal(ba.csa_v, bb.csa_v)
+        Kh, Vh = gated_pool(K[128 * lb:128 * (lb + 1)], V[128 * lb:128 * (lb + 1)], Wh, rounded=False)
+        codes, sc, vals = quantize_e4m3_rows(Kh)
+        assert np.array_equal(bb.hca_k_codes, codes) and np.array_equal(bb.hca_k_scale, sc)
+        assert np.array_equal(bb.hca_k, vals)
+        assert np.array_equal(bb.hca_v, quantize_e4m3_rows(Vh)[2])
+    q = rng.standard_normal((N_HEADS, HEAD_DIM))
+    qi = rng.standard_normal((4, 64))
+    ia, _ = a.topk(0, qi, 20)
+    ib, _ = b.topk(0, qi, 20)
+    assert np.array_equal(ia, ib)
+    Ka, Va = a.keys(0, ia, 20)
+    Kb, Vb = b.keys(0, ib, 20)
+    n_hca = 2
+    keep = np.r_[0:128, 128 + n_hca:len(Ka)]           # every key but the HCA entries
+    assert np.array_equal(Ka[keep], Kb[keep]) and np.array_equal(Va[keep], Vb[keep])
+
+
+def test_fp8_kv_stores_each_token_through_the_quantiser():
+    """With FP8 KV every path that writes the window stores a token's per-head E4M3
+    codes and scales: append, replay (state_write), fork (share) and restore. The
+    stored values stay within half a code spacing (times s) of the raw ones, and a
+    block pools the stored values of its 128 tokens."""
+    from oracle import e4m3_decode, quantize_e4m3_rows
+    Wc, Wh = synth.gate_weights(SEED)
+    o = Oracle(128, Wc, Wh, 4, 8, kv_format="fp8")
+    grid = e4m3_decode(np.arange(0x7F))
+    K, V, KI = toks(3, 0, 260)
+    s0 = o.state_alloc()
+    o.append([s0], [(K, V, KI)])
+
+    def check_window(s):
+        st = o.states[s]
+        L = st.L
+        for i, ((k, v), q) in enumerate(zip(st.swa, st.swa_q)):
+            p = L - len(st.swa) + i
+            for raw, got, (codes, sc) in ((K[p], k, q[0:2]), (V[p], v, q[2:4])):
+                rc, rs, rv = quantize_e4m3_rows(raw)
+                assert np.array_equal(codes, rc) and np.array_equal(sc, rs) and np.array_equal(got, rv)
+                assert np.array_equal(got, e4m3_decode(codes) * sc[:, None].astype(np.float64))
+                y = np.abs(raw) / sc[:, None].astype(np.float64)
+                idx = np.clip(np.searchsorted(grid, y), 1, len(grid) - 1)
+                half = (grid[idx] - grid[idx - 1]) / 2 * sc[:, None].astype(np.float64)
+                assert np.all(np.abs(got - raw) <= half * (1 + 1e-6))
+    check_window(s0)
+    # the seal pooled the stored tokens
+    blk = o.block(o.table(s0)[1])
+    Kq = quantize_e4m3_rows(K[128:256])[2]
+    Vq = quantize_e4m3_rows(V[128:256])[2]
+    for j in (0, 17, 31):
+        ek, ev = gated_pool(Kq[4 * j:4 * j + 4], Vq[4 * j:4 * j + 4], Wc)
+        assert np.array_equal(blk.csa_k[j], ek) and np.array_equal(blk.csa_v[j], ev)
+    # fork, attach + replay, and restore store the same codes
+    s1 = o.state_alloc()
+    o.share(s0, s1)
+    check_window(s1)
+    s2 = o.state_alloc()
+    o.prefix_attach(s2, o.table(s0), 260)
+    o.state_write([s2], [(K[132:260], V[132:260], KI[132:260])], [132])
+    check_window(s2)
+    ck = o.checkpoint(s0)
+    s3 = o.state_alloc()
+    o.prefix_attach(s3, o.table(s0), 260)
+    o.restore(s3, ck)
+    check_window(s3)
+
+
+def test_fp8_kv_attention_without_blocks_is_sdpa_over_the_stored_window():
+    """Below one block there are no entries: attention is plain softmax attention over
+    the window's stored (dequantized) K/V, checked against the library routine."""
+    Wc, Wh = synth.gate_weights(SEED)
+    o = Oracle(128, Wc, Wh, 1, 2, kv_format="fp8")
+    K, V, KI = toks(5, 0, 100)
+    o.append([o.state_alloc()], [(K, V, KI)])
+    st = o.states[0]
+    Ks = torch.tensor(np.stack([t[0] for t in st.swa]), dtype=torch.float64)   # [n][H][D]
+    Vs = torch.tensor(np.stack([t[1] for t in st.swa]), dtype=torch.float64)
+    q = synth.bf16_bits_to_f32(synth.tokens_bf16(SEED, synth.STREAM_Q, 5, np.array([99])))[0].astype(np.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[:, None, :], Ks.permute(1, 0, 2), Vs.permute(1, 0, 2))[:, 0, :].numpy()
+    np.testing.assert_allclose(o.attend(0, q, [], 0), ref, rtol=1e-12, atol=1e-12)
+    # and it stays close to the bf16 oracle's (FP8 storage error only)
+    b = Oracle(128, Wc, Wh, 1, 2)
+    b.append([b.state_alloc()], [(K, V, KI)])
+    r = b.attend(0, q, [], 0)
+    assert np.linalg.norm(o.attend(0, q, [], 0) - r) / np.linalg.norm(r) < 0.05
+
+
+def test_fp8_kv_refuses_eager_c4():
+    Wc, Wh = synth.gate_weights(SEED)
+    with pytest.raises(OracleError):
+        Oracle(128, Wc, Wh, 1, 1, c4_mode="eager", kv_format="fp8")
+    with pytest.raises(OracleError):
+        Oracle(128, Wc, Wh, 1, 1, kv_format="fp4")
+
+
 def test_fp8_oracle_entries_quantize_the_pooled_entry():
     """With FP8 entries the oracle's C4 entries are the per-head E4M3 storage of the
     unrounded pooled entry (the bf16 oracle's entries come from the same pooling),
