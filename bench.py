@@ -54,8 +54,17 @@ def idx_bytes(index: str) -> int:
     return IDX_BLOCK_MX if index == "mxfp4" else IDX_BLOCK
 
 
-def seal_bytes(entries: str, index: str = "f32") -> int:
-    return SEAL_BYTES - 32 * (ROW - c4_bytes(entries)) - (IDX_BLOCK - idx_bytes(index))
+def kv_bytes(kv: str) -> int:
+    """K + V bytes of one SWA ring token or HCA entry as stored (bf16, or FP8 codes and
+    per-head scales)."""
+    return C4_FP8 if kv == "fp8" else ROW
+
+
+def seal_bytes(entries: str, index: str = "f32", kv: str = "bf16") -> int:
+    """Bytes a seal moves: the block's 128 stored tokens and indexer keys read, 32 C4
+    entries, 1 HCA entry and 128 indexer keys written."""
+    return (SEAL_BYTES - 32 * (ROW - c4_bytes(entries)) - (IDX_BLOCK - idx_bytes(index))
+            - 129 * (ROW - kv_bytes(kv)))
 KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
                  "attend": "k_attend", "merge": "k_merge", "seal": "k_seal_merge",
                  "write": "k_bulk_write", "step1": "k_step1", "step2": "k_step2",
@@ -80,7 +89,8 @@ def step_fused(nb: np.ndarray, open_g=None) -> bool:
 
 
 def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: np.ndarray,
-               entries: str = "bf16", index: str = "f32", layer: str = "mixed", c4_mode: str = "sealed") -> dict:
+               entries: str = "bf16", index: str = "f32", layer: str = "mixed", c4_mode: str = "sealed",
+               kv: str = "bf16") -> dict:
     """Bytes the method must move in one decode step, per launch (scratch excluded).
 
     L_after: lengths after the append; nb: sealed blocks after it; sealed: 1 where
@@ -88,9 +98,10 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
     of the sealed indexer keys (the block sealed in the step is scored from the
     float32 tail)."""
     if layer != "mixed":
-        return layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer)
+        return layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer, kv)
     C4 = c4_bytes(entries)
-    SEAL = seal_bytes(entries, index)
+    KV = kv_bytes(kv)              # one ring token or HCA entry as stored
+    SEAL = seal_bytes(entries, index, kv)
     # eager C4: the open block's g entries are candidates too; its 4g tokens' indexer
     # keys are scanned, and a step that completes a group reads 3 ring tokens and
     # writes the entry
@@ -103,16 +114,16 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
     eager_b = int((done * (3 * ROW + ROW)).sum())
     if step_fused(nb, g):
         out = {
-            "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL - ROW)
+            "step1": int(B * (ROW + 1024 + KV + 1024) + sealed.sum() * (SEAL - KV)
                          + scan.sum() + B * 1024) + eager_b,
             # S2 (three-launch form): top-k out; HCA entries of new blocks; K/V rows
             # of the SWA tokens, earlier HCA entries and selected C4 entries + the query
-            "step2": int((kk * 8).sum() + sealed.sum() * ROW
-                         + ((swa + nb - sealed) * ROW + kk * C4).sum() + B * 4096),
+            "step2": int((kk * 8).sum() + sealed.sum() * KV
+                         + ((swa + nb - sealed) * KV + kk * C4).sum() + B * 4096),
             "step2b": 0,
             "step3": 0,
             # S4: the new HCA entries (K/V rows) and the fp32 output
-            "step4": int(sealed.sum() * ROW + B * 8192),
+            "step4": int(sealed.sum() * KV + B * 8192),
         }
         out["step"] = sum(out.values())
         return out
@@ -120,17 +131,17 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
         # S1: token K, V, indexer key in + ring and tail slots out; seals (minus the
         # HCA entry written in S2); indexer keys of every sealed block + the
         # indexer query
-        "step1": int(B * 2 * (ROW + 1024) + sealed.sum() * (SEAL - ROW)
+        "step1": int(B * (ROW + 1024 + KV + 1024) + sealed.sum() * (SEAL - KV)
                      + scan.sum() + B * 1024) + eager_b,
         # S2: top-k ordinals (and scores) out; HCA entries of new blocks; K/V rows
         # of the SWA tokens and earlier HCA entries + the query
-        "step2": int((kk * 8).sum() + sealed.sum() * ROW
-                     + ((swa + nb - sealed) * ROW).sum() + B * 4096),
+        "step2": int((kk * 8).sum() + sealed.sum() * KV
+                     + ((swa + nb - sealed) * KV).sum() + B * 4096),
         # S2b (rows cut into slices): the second selection round reads scratch only
         "step2b": 0,
         # S3: K/V rows of the new HCA entries and selected C4 entries, their
         # ordinals, the query
-        "step3": int((sealed * ROW + kk * C4).sum() + (kk * 4).sum() + B * 4096),
+        "step3": int((sealed * KV + kk * C4).sum() + (kk * 4).sum() + B * 4096),
         # S4: fp32 output
         "step4": int(B * 8192),
     }
@@ -138,26 +149,27 @@ def step_bytes(L_after: np.ndarray, nb: np.ndarray, n_win: int, k: int, sealed: 
     return out
 
 
-def layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer) -> dict:
+def layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer, kv="bf16") -> dict:
     """step_bytes of an SWA, CSA or HCA layer, always in three launches: what the
     layer keeps and attends (the SWA always; C4 entries, indexer keys and the tail
     for CSA; HCA entries for HCA)."""
     c4, hca = layer == "csa", layer == "hca"
     C4 = c4_bytes(entries)
+    KV = kv_bytes(kv)
     swa = np.minimum(L_after, n_win)
     kk = np.minimum(k, 32 * nb) if c4 else 0 * nb
     B = len(L_after)
-    tok = ROW + (1024 if c4 else 0)                      # one token in, and into the State
-    seal = 128 * ROW + (128 * 1024 + 32 * C4 + idx_bytes(index) if c4 else 0) + (ROW if hca else 0)
+    tok_in, tok_st = ROW + (1024 if c4 else 0), KV + (1024 if c4 else 0)   # one token in, into the State
+    seal = 128 * KV + (128 * 1024 + 32 * C4 + idx_bytes(index) if c4 else 0) + (KV if hca else 0)
     scan = ((nb - sealed) * idx_bytes(index) + sealed * IDX_BLOCK) if c4 else 0 * nb
     out = {
-        "step1": int(B * 2 * tok + sealed.sum() * (seal - (ROW if hca else 0)) + (scan.sum() if c4 else 0)
+        "step1": int(B * (tok_in + tok_st) + sealed.sum() * (seal - (KV if hca else 0)) + (scan.sum() if c4 else 0)
                      + (B * 1024 if c4 else 0)),
-        "step2": int((kk * 8).sum() + B * k * 4 * (0 if c4 else 1) + (sealed.sum() * ROW if hca else 0)
-                     + (swa * ROW + (nb - sealed) * ROW * hca + kk * C4).sum() + B * 4096),
+        "step2": int((kk * 8).sum() + B * k * 4 * (0 if c4 else 1) + (sealed.sum() * KV if hca else 0)
+                     + (swa * KV + (nb - sealed) * KV * hca + kk * C4).sum() + B * 4096),
         "step2b": 0,
         "step3": 0,
-        "step4": int((sealed.sum() * ROW if hca else 0) + B * 8192),
+        "step4": int((sealed.sum() * KV if hca else 0) + B * 8192),
     }
     out["step"] = sum(out.values())
     return out
@@ -215,7 +227,7 @@ def layer_seed(wl, layer: int) -> int:
 
 
 def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", index: str = "f32",
-                 layers=None, c4_mode: str = "sealed"):
+                 layers=None, c4_mode: str = "sealed", kv: str = "bf16"):
     """Cache holding `copies` identical instances of the batch, every request
     prefilled to L0 (bulk appends of device-generated tokens; in a prefix workload
     each request forks off its group's parent at its fork length, sharing those
@@ -237,7 +249,7 @@ def setup_decode(wl, extra_steps: int, copies: int = 1, entries: str = "bf16", i
     n_parents = wl.n_groups if wl.prefix_len else 0
     cache = hsa.Cache(wl.n_win, copies * (B + n_parents), max_blocks + copies * n_parents * (wl.prefix_len // 128),
                       Wc, Wh, max_blocks_per_state=max_len // 128 + 2, entry_format=entries,
-                      index_format=index, layer_types=layers, c4_mode=c4_mode)
+                      index_format=index, layer_types=layers, c4_mode=c4_mode, kv_format=kv)
     if layers and wl.prefix_len:
         raise SystemExit("layer stacks are measured on workloads without shared prefixes")
     inst = []
@@ -319,7 +331,7 @@ def run_decode(args) -> dict:
     set0 = W + len(STEP_KERNELS) * n_kt + K
     local_steps = (max(set0, K) + R - 1) // R
     cache, inst = setup_decode(wl, local_steps, R * (1 + reps), args.entries, args.index, layers,
-                               args.c4_mode)
+                               args.c4_mode, args.kv)
     L0 = wl.prefill.astype(np.int64)
     inp = [decode_inputs(wl, L0, local_steps, seed=layer_seed(wl, l)) for l in range(len(types))]
     topk = torch.empty((B, k), dtype=torch.int32, device="cuda")
@@ -403,7 +415,8 @@ def run_decode(args) -> dict:
             nb = L_after // 128
             sealed = (L_after % 128 == 0).astype(np.int64)
             for typ in types:
-                sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index, typ, args.c4_mode)
+                sb = step_bytes(L_after, nb, wl.n_win, k, sealed, args.entries, args.index, typ, args.c4_mode,
+                                args.kv)
                 for n in acc:
                     acc[n] += sb[n]
         return acc
@@ -430,7 +443,8 @@ def run_decode(args) -> dict:
     metric = METRIC if wl.name == "b32" else f"decode tokens/s + achieved HBM GB/s, append+attend, {wl.name}"
     stack = f", {len(types)}-layer stack ({args.layers} x {args.layer_repeat})" if layers else ""
     res = {
-        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", MXFP4 indexer keys" if mx4 else "") + stack
+        "metric": metric + (", FP8 C4 entries" if fp8 else "") + (", FP8 SWA and HCA" if args.kv == "fp8" else "")
+                  + (", MXFP4 indexer keys" if mx4 else "") + stack
                   + (", eager C4" if args.c4_mode == "eager" else ""),
         "value": B * K / (ms_total * 1e-3),
         "unit": "tokens/s",
@@ -445,13 +459,14 @@ def run_decode(args) -> dict:
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {B} requests, {LENGTHS[wl.name]} (seed {wl.seed:#x}), "
                                f"decode steps, n_win {wl.n_win}, top-k {k}, 16x128 bf16 K/V/Q"
+                               f"{' (SWA ring and HCA entries FP8 E4M3, fp32 scale per head)' if args.kv == 'fp8' else ''}"
                                f"{' (C4 entries FP8 E4M3, fp32 scale per head)' if fp8 else ''}, "
                                f"indexer 4x64 fp32{' (sealed keys MXFP4)' if mx4 else ''}, m=4, m'=128, "
                                f"{len(types)} layer{'s' if len(types) > 1 else ''}"
                                f"{' (' + ','.join(types) + ')' if layers else ''}; steps rotate over {R} "
                                f"copies of the cache",
                    "batch": B, "n_win": wl.n_win, "topk": k, "kv_dtype": "bf16",
-                   "c4_entries": args.entries, "index_keys": args.index, "cache_copies": R,
+                   "c4_entries": args.entries, "swa_hca": args.kv, "index_keys": args.index, "cache_copies": R,
                    "layers": types, "c4_mode": args.c4_mode,
                    "L0_mean": float(L0.mean()), "parallelism": "single GPU"},
         "hbm_gbps": step_gbs,
@@ -833,6 +848,9 @@ def main():
                          "last-level cache between steps)")
     ap.add_argument("--entries", default="bf16", choices=["bf16", "fp8"],
                     help="storage format of the C4 entries (bf16, or FP8 E4M3 with a per-head scale)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="storage of SWA ring tokens and HCA entries (bf16, or FP8 E4M3 with a "
+                         "per-head scale)")
     ap.add_argument("--index", default="f32", choices=["f32", "mxfp4"],
                     help="storage format of sealed indexer keys (fp32, or MXFP4 with E8M0 block scales)")
     ap.add_argument("--hit", default=None, choices=["zero", "periodic", "full"],
@@ -868,7 +886,7 @@ def main():
         return
     res = run_bulk(args) if args.workload == 4 else run_decode(args)
     if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16" \
-            and args.index == "f32" and not args.layers and args.c4_mode == "sealed":
+            and args.index == "f32" and not args.layers and args.c4_mode == "sealed" and args.kv == "bf16":
         res["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(res), flush=True)
 

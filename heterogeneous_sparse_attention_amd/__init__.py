@@ -49,12 +49,14 @@ class _Config(ctypes.Structure):
                 ("gate_hca", ctypes.POINTER(ctypes.c_float)),
                 ("entry_format", ctypes.c_int32), ("index_format", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("layer_types", ctypes.c_void_p),
-                ("c4_mode", ctypes.c_int32), ("create_flags", ctypes.c_uint32)]
+                ("c4_mode", ctypes.c_int32), ("create_flags", ctypes.c_uint32),
+                ("kv_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 ENTRY_FORMATS = {"bf16": 0, "fp8": 1}     # HSA_ENTRY_BF16, HSA_ENTRY_FP8
 INDEX_FORMATS = {"f32": 0, "mxfp4": 1}    # HSA_INDEX_F32, HSA_INDEX_MXFP4
 LAYER_TYPES = {"mixed": 0, "swa": 1, "csa": 2, "hca": 3}   # HSA_LAYER_*
 C4_MODES = {"sealed": 0, "eager": 1}                       # HSA_C4_SEALED, HSA_C4_EAGER
+KV_FORMATS = {"bf16": 0, "fp8": 1}                         # HSA_KV_BF16, HSA_KV_FP8
 
 
 class _StateInfo(ctypes.Structure):
@@ -90,6 +92,8 @@ SIGNATURES = {
     "hsa_export_block": [_P, _I32, _P, _P, _P, _P, _P, _P],
     "hsa_export_state": [_P, _I32, _P, _P, _P, _P],
     "hsa_export_c4_fp8": [_P, _I32, _P, _P, _P, _P, _P],
+    "hsa_export_state_fp8": [_P, _I32, _P, _P, _P],
+    "hsa_export_hca_fp8": [_P, _I32, _P, _P, _P],
     "hsa_fp8_quantize_rows": [_P, _I64, _P, _P, _P],
     "hsa_export_idx_mxfp4": [_P, _I32, _P, _P, _P],
     "hsa_block_ref": [_P, _P, _I64, _I32],
@@ -200,7 +204,7 @@ class Cache:
     def __init__(self, n_win: int, max_states: int, max_blocks: int, gate_csa, gate_hca,
                  max_blocks_per_state: int = 0, device: int = 0, entry_format: str = "bf16",
                  index_format: str = "f32", layer_types=None, c4_mode: str = "sealed",
-                 poison: bool = False):
+                 poison: bool = False, kv_format: str = "bf16"):
         """layer_types: None (one heterogeneous layer) or a list of "mixed", "swa",
         "csa", "hca"; then gate_csa / gate_hca hold one [16][128] set per layer.
         poison: fill every pool and scratch buffer with NaN bytes when allocated
@@ -212,6 +216,9 @@ class Cache:
             raise ValueError(f"index_format must be one of {sorted(INDEX_FORMATS)}")
         if c4_mode not in C4_MODES:
             raise ValueError(f"c4_mode must be one of {sorted(C4_MODES)}")
+        if kv_format not in KV_FORMATS:
+            raise ValueError(f"kv_format must be one of {sorted(KV_FORMATS)}")
+        self.kv_format = kv_format
         self.c4_mode = c4_mode
         types = ["mixed"] if layer_types is None else list(layer_types)
         if not types or any(t not in LAYER_TYPES for t in types):
@@ -227,7 +234,7 @@ class Cache:
                       self._gh.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                       ENTRY_FORMATS[entry_format], INDEX_FORMATS[index_format], nl,
                       self._lt.ctypes.data_as(ctypes.c_void_p), C4_MODES[c4_mode],
-                      CREATE_POISON if poison else 0)
+                      CREATE_POISON if poison else 0, KV_FORMATS[kv_format], 0)
         self.entry_format = entry_format
         self.index_format = index_format
         ctx = ctypes.c_void_p()
@@ -456,7 +463,7 @@ class Cache:
         fp8 = self.entry_format == "fp8" and c4
         mx4 = self.index_format == "mxfp4" and c4
         out = {}
-        if hca:
+        if hca and self.kv_format != "fp8":
             out["hca_k"] = np.zeros((H, D), np.uint16)
             out["hca_v"] = np.zeros((H, D), np.uint16)
         if c4 and not mx4:
@@ -475,6 +482,14 @@ class Cache:
                                           pq["csa_k_scale"], pq["csa_v_scale"], _stream(stream)),
                    "hsa_export_c4_fp8")
             out.update(q)
+        if hca and self.kv_format == "fp8":
+            codes = np.zeros((2, H, D), np.uint8)
+            sc = np.zeros((2, H), np.float32)
+            _check(_lib.hsa_export_hca_fp8(self._ctx, int(b), codes.ctypes.data_as(ctypes.c_void_p),
+                                           sc.ctypes.data_as(ctypes.c_void_p), _stream(stream)),
+                   "hsa_export_hca_fp8")
+            out.update({"hca_k_codes": codes[0], "hca_v_codes": codes[1], "hca_k_scale": sc[0],
+                        "hca_v_scale": sc[1]})
         if mx4:
             q = {"idx_codes": np.zeros((128, HI * DI // 2), np.uint8),
                  "idx_scales": np.zeros((128, HI * DI // 32), np.uint8)}
@@ -485,14 +500,25 @@ class Cache:
         return out
 
     def export_state(self, s: int, stream=None) -> dict:
-        """The current layer's SWA ring and (layers with C4 entries) indexer tail."""
-        out = {"swa_k": np.zeros((self.n_win, H, D), np.uint16),
-               "swa_v": np.zeros((self.n_win, H, D), np.uint16)}
+        """The current layer's SWA ring and (layers with C4 entries) indexer tail. bf16
+        KV: swa_k, swa_v uint16 bits [n_win][16][128]. FP8 KV: swa_k_codes, swa_v_codes
+        uint8 [n_win][16][128] and swa_k_scale, swa_v_scale float32 [n_win][16]."""
+        fp8 = self.kv_format == "fp8"
+        out = {} if fp8 else {"swa_k": np.zeros((self.n_win, H, D), np.uint16),
+                              "swa_v": np.zeros((self.n_win, H, D), np.uint16)}
         if self.layer_types[self.layer] in ("mixed", "csa"):
             out["idx_tail"] = np.zeros((128, HI, DI), np.float32)
         p = {n: a.ctypes.data_as(ctypes.c_void_p) for n, a in out.items()}
-        _check(_lib.hsa_export_state(self._ctx, int(s), p["swa_k"], p["swa_v"], p.get("idx_tail"),
+        _check(_lib.hsa_export_state(self._ctx, int(s), p.get("swa_k"), p.get("swa_v"), p.get("idx_tail"),
                                      _stream(stream)), "hsa_export_state")
+        if fp8:
+            codes = np.zeros((self.n_win, 2, H, D), np.uint8)
+            sc = np.zeros((self.n_win, 2, H), np.float32)
+            _check(_lib.hsa_export_state_fp8(self._ctx, int(s), codes.ctypes.data_as(ctypes.c_void_p),
+                                             sc.ctypes.data_as(ctypes.c_void_p), _stream(stream)),
+                   "hsa_export_state_fp8")
+            out.update({"swa_k_codes": codes[:, 0], "swa_v_codes": codes[:, 1], "swa_k_scale": sc[:, 0],
+                        "swa_v_scale": sc[:, 1]})
         return out
 
     # -- timing -----------------------------------------------------------------------

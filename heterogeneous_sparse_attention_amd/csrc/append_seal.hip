@@ -22,8 +22,8 @@ namespace {
 // No slot written by the first group is read by the second: the new token's
 // ring slot differs from the 127 older ones (n_win >= 128), and its tail slot is
 // 127, which the seal reads from the input instead.
-// Templates: FP8 C4 entries; C4 false for layers without C4 entries.
-template <bool FP8, bool C4>
+// Templates: FP8 C4 entries; C4 false for layers without C4 entries; KV8 FP8 KV.
+template <bool FP8, bool C4, bool KV8>
 __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, const uint16_t* kin,
                                                        const uint16_t* vin, const float* iin,
                                                        float* part) {
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, cons
   const int item = (bid - B.n) / kSealSplit;
   const int sub = (bid - B.n) % kSealSplit;
   const int ri = B.seal_req[item];
-  seal_eighth<FP8, C4>(P, B.r[ri], ri, item, sub, kin, vin, iin, part);
+  seal_eighth<FP8, C4, KV8>(P, B.r[ri], ri, item, sub, kin, vin, iin, part);
 }
 
 // One workgroup per block sealed by k_decode_append (next launch, so the partials
@@ -46,15 +46,14 @@ __global__ __launch_bounds__(256) void k_seal_merge(Pools P, ReqBatch B, const f
 
 // Bulk seal: one workgroup per block, its eight 16-token partials merged in
 // registers in order. Templates: FP8 C4 entries; the layer keeps C4 entries (C4)
-// and HCA entries (HCA).
-template <bool FP8, bool C4, bool HCA>
+// and HCA entries (HCA); KV8 FP8 KV.
+template <bool FP8, bool C4, bool HCA, bool KV8>
 __global__ __launch_bounds__(256) void k_bulk_seal(Pools P, const SealDesc* seals,
                                                    const uint16_t* kin, const uint16_t* vin,
                                                    const float* iin) {
   const SealDesc d = seals[blockIdx.x];
   TokSrc src;
-  src.ring_k = P.swa_k + (int64_t)d.state * P.n_win * kRow;
-  src.ring_v = P.swa_v + (int64_t)d.state * P.n_win * kRow;
+  ring_src(P, d.state, src);
   src.tail_i = P.idx_tail + (int64_t)d.state * kBlk * kIRow;
   // rows of positions >= len_old (row0 < 0 only when every token is resident)
   const int64_t row0 = d.row0 < 0 ? 0 : d.row0;
@@ -67,7 +66,7 @@ __global__ __launch_bounds__(256) void k_bulk_seal(Pools P, const SealDesc* seal
   float M = -INFINITY, L = 0.f, K8[8] = {}, V8[8] = {};
   for (int sub = 0; sub < kSealSplit; ++sub) {
     float m, l, acck[8], accv[8];
-    seal_part<FP8, C4>(P, src, d.id, sub * kSubTok, m, l, acck, accv);
+    seal_part<FP8, C4, KV8>(P, src, d.id, sub * kSubTok, m, l, acck, accv);
     merge_part(M, L, K8, V8, m, l, acck, accv);
   }
   if constexpr (HCA) store_hca(P, d.id, L, K8, V8);
@@ -96,9 +95,7 @@ __global__ __launch_bounds__(256) void k_bulk_write(Pools P, const WriteDesc* w,
     const WriteDesc d = w[r];
     const int64_t p = d.w0 + (x - d.cum);
     const int64_t row = d.row0 + (p - d.len_old);
-    const int64_t ring = ((int64_t)d.state * P.n_win + (p % P.n_win)) * kRow;
-    reinterpret_cast<uint4*>(P.swa_k + ring)[tid] = reinterpret_cast<const uint4*>(kin + row * kRow)[tid];
-    reinterpret_cast<uint4*>(P.swa_v + ring)[tid] = reinterpret_cast<const uint4*>(vin + row * kRow)[tid];
+    write_ring_token(P, (int64_t)d.state * P.n_win + (p % P.n_win), kin + row * kRow, vin + row * kRow);
     if (P.c4 && p >= (int64_t)d.nb_new * kBlk && tid < kIRow / 4) {
       const int64_t ti = ((int64_t)d.state * kBlk + (p % kBlk)) * kIRow;
       reinterpret_cast<float4*>(P.idx_tail + ti)[tid] = reinterpret_cast<const float4*>(iin + row * kIRow)[tid];
@@ -219,9 +216,15 @@ hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* k
   if (grid == 0) return hipSuccess;
   const uint16_t* k = static_cast<const uint16_t*>(kin);
   const uint16_t* v = static_cast<const uint16_t*>(vin);
-  if (!P.c4) return launch_k(k_decode_append<false, false>, dim3(grid), dim3(256), st, ev, P, B, k, v, iin, part);
-  if (P.fp8) return launch_k(k_decode_append<true, true>, dim3(grid), dim3(256), st, ev, P, B, k, v, iin, part);
-  return launch_k(k_decode_append<false, true>, dim3(grid), dim3(256), st, ev, P, B, k, v, iin, part);
+  const dim3 g(grid), t(256);
+  if (P.kv8) {
+    if (!P.c4) return launch_k(k_decode_append<false, false, true>, g, t, st, ev, P, B, k, v, iin, part);
+    if (P.fp8) return launch_k(k_decode_append<true, true, true>, g, t, st, ev, P, B, k, v, iin, part);
+    return launch_k(k_decode_append<false, true, true>, g, t, st, ev, P, B, k, v, iin, part);
+  }
+  if (!P.c4) return launch_k(k_decode_append<false, false, false>, g, t, st, ev, P, B, k, v, iin, part);
+  if (P.fp8) return launch_k(k_decode_append<true, true, false>, g, t, st, ev, P, B, k, v, iin, part);
+  return launch_k(k_decode_append<false, true, false>, g, t, st, ev, P, B, k, v, iin, part);
 }
 
 hipError_t launch_seal_merge(const Pools& P, const ReqBatch& B, const float* part, hipStream_t st,
@@ -237,11 +240,19 @@ hipError_t launch_bulk_seal(const Pools& P, const SealDesc* seals, int64_t n_sea
   const dim3 g((unsigned)n_seals);
   const uint16_t* k = static_cast<const uint16_t*>(kin);
   const uint16_t* v = static_cast<const uint16_t*>(vin);
-  if (!P.c4) return launch_k(k_bulk_seal<false, false, true>, g, dim3(256), st, ev, P, seals, k, v, iin);
-  if (P.fp8 && P.hca) return launch_k(k_bulk_seal<true, true, true>, g, dim3(256), st, ev, P, seals, k, v, iin);
-  if (P.fp8) return launch_k(k_bulk_seal<true, true, false>, g, dim3(256), st, ev, P, seals, k, v, iin);
-  if (P.hca) return launch_k(k_bulk_seal<false, true, true>, g, dim3(256), st, ev, P, seals, k, v, iin);
-  return launch_k(k_bulk_seal<false, true, false>, g, dim3(256), st, ev, P, seals, k, v, iin);
+  const dim3 t(256);
+  if (P.kv8) {
+    if (!P.c4) return launch_k(k_bulk_seal<false, false, true, true>, g, t, st, ev, P, seals, k, v, iin);
+    if (P.fp8 && P.hca) return launch_k(k_bulk_seal<true, true, true, true>, g, t, st, ev, P, seals, k, v, iin);
+    if (P.fp8) return launch_k(k_bulk_seal<true, true, false, true>, g, t, st, ev, P, seals, k, v, iin);
+    if (P.hca) return launch_k(k_bulk_seal<false, true, true, true>, g, t, st, ev, P, seals, k, v, iin);
+    return launch_k(k_bulk_seal<false, true, false, true>, g, t, st, ev, P, seals, k, v, iin);
+  }
+  if (!P.c4) return launch_k(k_bulk_seal<false, false, true, false>, g, t, st, ev, P, seals, k, v, iin);
+  if (P.fp8 && P.hca) return launch_k(k_bulk_seal<true, true, true, false>, g, t, st, ev, P, seals, k, v, iin);
+  if (P.fp8) return launch_k(k_bulk_seal<true, true, false, false>, g, t, st, ev, P, seals, k, v, iin);
+  if (P.hca) return launch_k(k_bulk_seal<false, true, true, false>, g, t, st, ev, P, seals, k, v, iin);
+  return launch_k(k_bulk_seal<false, true, false, false>, g, t, st, ev, P, seals, k, v, iin);
 }
 
 hipError_t launch_bulk_write(const Pools& P, const WriteDesc* w, int32_t n_req, int64_t total,

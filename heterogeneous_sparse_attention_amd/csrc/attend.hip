@@ -26,9 +26,9 @@ __device__ __forceinline__ KeyAddr key_addr(const Pools& P, const Req& R, int x,
   a.k = a.v = nullptr;
   if (x < swa) {
     const int64_t p = (int64_t)R.len - swa + x;
-    const int64_t off = ((int64_t)R.state * P.n_win + p % P.n_win) * kRow;
-    a.k = P.swa_k + off;
-    a.v = P.swa_v + off;
+    const C4Addr c = ring_addr(P, (int64_t)R.state * P.n_win + p % P.n_win);
+    a.k = c.k;
+    a.v = c.v;
     return a;
   }
   x -= swa;
@@ -37,8 +37,9 @@ __device__ __forceinline__ KeyAddr key_addr(const Pools& P, const Req& R, int x,
   if (x < nh) {
     const int32_t id = tab[x];
     if (id < 0 || id >= P.max_blocks) return a;   // never taken: tables are written before use
-    a.k = P.hca_k + (int64_t)id * kRow;
-    a.v = P.hca_v + (int64_t)id * kRow;
+    const C4Addr c = hca_addr(P, id);
+    a.k = c.k;
+    a.v = c.v;
     return a;
   }
   x -= nh;
@@ -68,12 +69,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attend(Pools P, ReqBatch B,
   const int nk = n_keys(P, R, k);
   const int nch = (nk + chunk - 1) / chunk;
   const int32_t* sel = topk ? topk + (int64_t)r * k : nullptr;
-  const uint16_t* dk = P.swa_k + (int64_t)R.state * P.n_win * kRow;   // valid row (L >= 1)
-  const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  const C4Addr dm = dummy_rows(P, R.state);   // valid rows (L >= 1)
   float M, L, A8[8];
+  // keys below the C4 entries (SWA tokens, HCA entries) follow the KV format
   attend_keys([&](int x) { return key_addr(P, R, x, sel); }, w * chunk, min(nk, (w + 1) * chunk),
-              q + (int64_t)r * kRow, dk, dv, sh, M, L, A8,
-              P.fp8 ? (R.len < P.n_win ? R.len : P.n_win) + (P.hca ? R.nb : 0) : 0x7fffffff);
+              q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8,
+              (R.len < P.n_win ? R.len : P.n_win) + (P.hca ? R.nb : 0), P.kv8 != 0, P.fp8 != 0);
   if (nch == 1)
     store_output(out + (int64_t)r * kRow, L, A8);
   else

@@ -197,15 +197,17 @@ __device__ __forceinline__ void merge_waves(const float* m, const float* l, cons
 
 // Attention of one workgroup of WAVES waves over keys [x0, x1) of one request:
 // wave w streams a contiguous share. key_of(x) gives the K and V rows of key x (for
-// an FP8 key, x >= fp8_from: its code and scale rows) or nullptrs for a skipped
-// slot; dummy_k / dummy_v are valid rows (at least 4 KiB) read in place of skipped
-// keys. On return threads t < 256 hold head t/16, dims (t%16)*8 .. +8 of the
-// unnormalised result: running max M (log2 units), sum L, accumulator A8.
+// an FP8 key: its code and scale rows) or nullptrs for a skipped slot; keys x <
+// fp8_split are FP8 when fp8_lo, the others when fp8_hi. dummy_k / dummy_v are
+// valid rows (at least 4 KiB) read in place of skipped keys. On return threads
+// t < 256 hold head t/16, dims (t%16)*8 .. +8 of the unnormalised result: running
+// max M (log2 units), sum L, accumulator A8.
 template <int WAVES = kAttnWaves, int RING = ring_depth<WAVES>(), class KeyFn>
 __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const uint16_t* qrow,
                                             const uint16_t* dummy_k, const uint16_t* dummy_v,
                                             AttnSharedT<WAVES>& sh, float& M, float& L, float* A8,
-                                            int fp8_from = 0x7fffffff) {
+                                            int fp8_split = 0x7fffffff, bool fp8_lo = false,
+                                            bool fp8_hi = true) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -233,20 +235,21 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
     const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
     const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
     const int n = min(64, w1 - g);
-    const int f8 = fp8_from - g;   // keys x >= f8 of this group are FP8
+    const int f8 = fp8_split - g;   // keys x < f8 of this group follow fp8_lo, the others fp8_hi
+    auto is8 = [&](int x) { return x < f8 ? fp8_lo : fp8_hi; };
     // ring of RING keys: RING - 1 keys stay in flight while one is consumed
     KeyRegs ring[RING];
 #pragma unroll
     for (int u = 0; u < RING - 1; ++u)
-      if (u < n) load_key(ring[u], kp, vp, u, lane, u >= f8);
+      if (u < n) load_key(ring[u], kp, vp, u, lane, is8(u));
     for (int i = 0; i < n; i += RING) {
 #pragma unroll
       for (int u = 0; u < RING; ++u) {
         const int x = i + u;
         if (x >= n) break;
         if (x + RING - 1 < n)
-          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane, x + RING - 1 >= f8);
-        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, x >= f8);
+          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane, is8(x + RING - 1));
+        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, is8(x));
       }
     }
   }
@@ -261,14 +264,14 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
 // it has them, and their loads are issued before mid(), so they arrive while mid()
 // runs; pre() runs just before those loads are issued (work that should wait for
 // earlier loads first). key_a / key_b return the rows of a key or nullptrs for a
-// skipped slot (with fp8_b, key_b gives the code and scale rows of FP8 C4 keys);
+// skipped slot (with fp8_a / fp8_b, key_a / key_b give the code and scale rows of FP8 keys);
 // dummy_k / dummy_v are valid rows (at least 4 KiB) read in their place. Result as
 // attend_keys.
 template <int WAVES, int RING, class KeyA, class KeyB, class Pre, class Mid>
 __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_b, int b0, int b1, Pre pre, Mid mid,
                                            const uint16_t* qrow, const uint16_t* dummy_k,
                                            const uint16_t* dummy_v, AttnSharedT<WAVES>& sh, float& M,
-                                           float& L, float* A8, bool fp8_b = false) {
+                                           float& L, float* A8, bool fp8_b = false, bool fp8_a = false) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -305,7 +308,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   KeyRegs ring[RING];
   pre();
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane, false);
+  for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane, fp8_a);
   mid();
   if (lane < n0 && lane >= na) {
     a = key_b(wb0 + lane - na);
@@ -328,7 +331,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
       vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
 #pragma unroll
       for (int u = 0; u < RING - 1; ++u)
-        if (u < ng) load_key(ring[u], kp, vp, u, lane, fp8_b && g + u >= na);
+        if (u < ng) load_key(ring[u], kp, vp, u, lane, g + u >= na ? fp8_b : fp8_a);
     }
     for (int i = 0; i < ng; i += RING) {
 #pragma unroll
@@ -336,8 +339,9 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
         const int x = i + u;
         if (x >= ng) break;
         if (x + RING - 1 < ng)
-          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane, fp8_b && g + x + RING - 1 >= na);
-        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, fp8_b && g + x >= na);
+          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane,
+                   g + x + RING - 1 >= na ? fp8_b : fp8_a);
+        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, g + x >= na ? fp8_b : fp8_a);
       }
     }
   }
@@ -368,9 +372,10 @@ __device__ __forceinline__ void store_output(float* out_row, float L, const floa
 // One extra key folded into a merge: its K and V rows and the request's query (bf16
 // [16][128] each), or null pointers for none.
 struct ExtraKey {
-  const uint16_t* k;
-  const uint16_t* v;
+  const uint16_t* k;   // bf16 K row, or (fp8) the code row: K codes, then V codes
+  const uint16_t* v;   // bf16 V row, or (fp8) the scale row: K scales, then V scales
   const uint16_t* q;
+  bool fp8;
 };
 
 // Log-sum-exp merge of n partials (index of the j-th given by part_of(j), plain
@@ -382,18 +387,34 @@ struct ExtraKey {
 template <class PartFn>
 __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, const float* part_acc,
                                                const float* part_ml, float* out_row,
-                                               ExtraKey xk = ExtraKey{nullptr, nullptr, nullptr}) {
+                                               ExtraKey xk = ExtraKey{nullptr, nullptr, nullptr, false}) {
   const int lane = threadIdx.x & 63;
   const float* accb = part_acc + h * kD + 2 * lane;
   float xs = kNoMax, xvx = 0.f, xvy = 0.f;
   if (xk.k) {
     const int o = h * kD + 2 * lane;
     const uint32_t qw = *reinterpret_cast<const uint32_t*>(xk.q + o);
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(xk.k + o);
-    const uint32_t vw = *reinterpret_cast<const uint32_t*>(xk.v + o);
-    xs = wave_sum(fmaf(bf_lo(qw), bf_lo(kw), bf_hi(qw) * bf_hi(kw))) * kQScale;
-    xvx = bf_lo(vw);
-    xvy = bf_hi(vw);
+    float k0, k1;
+    if (xk.fp8) {   // two codes of K and of V, and the head's scales
+      const uint8_t* codes = reinterpret_cast<const uint8_t*>(xk.k);
+      const float* sc = reinterpret_cast<const float*>(xk.v);
+      const int hp = 4 * (h & 3) + (h >> 2);
+      const f32x2_v kc = __builtin_amdgcn_cvt_pk_f32_fp8((int)*reinterpret_cast<const uint16_t*>(codes + o), false);
+      const f32x2_v vc =
+          __builtin_amdgcn_cvt_pk_f32_fp8((int)*reinterpret_cast<const uint16_t*>(codes + kRow + o), false);
+      k0 = kc.x * sc[hp];
+      k1 = kc.y * sc[hp];
+      xvx = vc.x * sc[kH + hp];
+      xvy = vc.y * sc[kH + hp];
+    } else {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(xk.k + o);
+      const uint32_t vw = *reinterpret_cast<const uint32_t*>(xk.v + o);
+      k0 = bf_lo(kw);
+      k1 = bf_hi(kw);
+      xvx = bf_lo(vw);
+      xvy = bf_hi(vw);
+    }
+    xs = wave_sum(fmaf(bf_lo(qw), k0, bf_hi(qw) * k1)) * kQScale;
   }
   float ox = 0.f, oy = 0.f;
   if (n <= 64) {

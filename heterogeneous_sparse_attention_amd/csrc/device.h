@@ -11,6 +11,9 @@
 //   idx_k         [max_blocks][128][4][64]   fp32
 //   (MXFP4 indexer keys instead: idx_q [max_blocks][128][128] E2M1 code pairs and
 //    idx_e [max_blocks][128][8] E8M0 scales, one per 32 values)
+//   (FP8 KV instead of swa_k, swa_v and hca_k, hca_v: swq [max_states * n_win][K, V][16][128]
+//    and hcq [max_blocks][K, V][16][128] E4M3 codes, sws and hcs [..][K, V][16] fp32
+//    scales, the C4 FP8 row layout)
 //   table         [max_states][table_stride] int32    logical block -> physical id
 // One K or V row (a token or an entry) is 16 x 128 bf16 = 4 KiB contiguous, so every
 // row read is a fully coalesced 4 KiB burst; one indexer row is 1 KiB.
@@ -71,6 +74,10 @@ struct Pools {
   float* c4s;           // FP8 entries: scales of C4 row r at r * kC4Scales
   uint8_t* idx_q;       // MXFP4 keys: codes of key row r (block * 128 + token) at r * kIRowQ
   uint8_t* idx_e;       // MXFP4 keys: scale bytes of key row r at r * kIRowE
+  uint8_t* swq;         // FP8 KV: codes of ring slot g (state * n_win + p % n_win) at g * kC4Bytes
+  float* sws;           // FP8 KV: scales of ring slot g at g * kC4Scales
+  uint8_t* hcq;         // FP8 KV: codes of block id's HCA entry at id * kC4Bytes
+  float* hcs;           // FP8 KV: scales of block id's HCA entry at id * kC4Scales
   int32_t n_win;
   int32_t max_blocks;   // physical ids are in [0, max_blocks)
   int32_t fp8;          // 1: C4 entries are stored as FP8 (c4q, c4s); 0: bf16 (csa_k, csa_v)
@@ -78,6 +85,7 @@ struct Pools {
   int32_t c4;           // layer type: 1 if the layer keeps C4 entries, indexer keys and tail
   int32_t hca;          // layer type: 1 if the layer keeps HCA entries
   int32_t eager;        // 1: the open block's complete groups have C4 entries (eager C4)
+  int32_t kv8;          // 1: SWA ring tokens and HCA entries are FP8 (swq, sws, hcq, hcs); 0: bf16
   int32_t c4_ids;       // C4 block ids in [0, c4_ids): the blocks, then (eager) one open
                         // block per state at max_blocks + state
 };
@@ -368,8 +376,9 @@ __device__ __forceinline__ void mx4_store_row(const float4& v, int c, uint8_t* c
   if ((c & 7) == 0) scales[c >> 3] = (uint8_t)(E + 127);
 }
 
-// Address of C4 row `row` (block * 32 + slot) for attention: the bf16 K and V rows,
-// or, with FP8 entries, the code row and the scale row (see load_key).
+// The two rows of a key for attention: the bf16 K and V rows, or, for an FP8 key,
+// its code row (K codes, then V codes) and its scale row (K scales, then V scales,
+// head h at 4 (h % 4) + h / 4, see load_key).
 struct C4Addr {
   const uint16_t* k;
   const uint16_t* v;
@@ -379,6 +388,27 @@ __device__ __forceinline__ C4Addr c4_addr(const Pools& P, int64_t row) {
     return C4Addr{reinterpret_cast<const uint16_t*>(P.c4q + row * kC4Bytes),
                   reinterpret_cast<const uint16_t*>(P.c4s + row * kC4Scales)};
   return C4Addr{P.csa_k + row * kRow, P.csa_v + row * kRow};
+}
+// Ring slot g = state * n_win + p % n_win (the token at position p).
+__device__ __forceinline__ C4Addr ring_addr(const Pools& P, int64_t g) {
+  if (P.kv8)
+    return C4Addr{reinterpret_cast<const uint16_t*>(P.swq + g * kC4Bytes),
+                  reinterpret_cast<const uint16_t*>(P.sws + g * kC4Scales)};
+  return C4Addr{P.swa_k + g * kRow, P.swa_v + g * kRow};
+}
+// The HCA entry of block id.
+__device__ __forceinline__ C4Addr hca_addr(const Pools& P, int64_t id) {
+  if (P.kv8)
+    return C4Addr{reinterpret_cast<const uint16_t*>(P.hcq + id * kC4Bytes),
+                  reinterpret_cast<const uint16_t*>(P.hcs + id * kC4Scales)};
+  return C4Addr{P.hca_k + id * kRow, P.hca_v + id * kRow};
+}
+// A pair of rows that is valid to read in place of a skipped key of either kind: a
+// bf16 key reads 4 KiB from each, an FP8 key 4 KiB of codes and 128 B of scales.
+// The state's first ring slot: its K row and V row, or (FP8 KV) its code row twice.
+__device__ __forceinline__ C4Addr dummy_rows(const Pools& P, int32_t state) {
+  const C4Addr a = ring_addr(P, (int64_t)state * P.n_win);
+  return P.kv8 ? C4Addr{a.k, a.k} : a;
 }
 
 // Per-head FP8 storage of 8 values per lane, the 16 lanes of a DPP row holding one
@@ -406,6 +436,20 @@ __device__ __forceinline__ uint2 quantize8_e4m3(const float* x, float& scale) {
   return make_uint2((uint32_t)w0, (uint32_t)w1);
 }
 
+// Store 8 values per lane of one K or V row of 16 heads x 128 in FP8 (256 lanes,
+// lane t holding head t / 16, dims (t % 16) * 8 .. + 8): codes to q + 8 t, the head's
+// scale to scale[4 (h % 4) + h / 4] from the head's first lane.
+__device__ __forceinline__ void store_row_fp8(const float* x8, uint8_t* q, float* scale) {
+  const int tid = threadIdx.x;
+  float sc;
+  const uint2 c = quantize8_e4m3(x8, sc);
+  *reinterpret_cast<uint2*>(q + tid * 8) = c;
+  if ((tid & 15) == 0) {
+    const int h = tid >> 4;
+    scale[4 * (h & 3) + (h >> 2)] = sc;
+  }
+}
+
 typedef float f32x2_v __attribute__((ext_vector_type(2)));
 // The four E4M3 codes of `w` (byte i = value i) as floats.
 __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
@@ -417,6 +461,14 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
 // a in the low half.
 __device__ __forceinline__ uint32_t pack_exact_bf2(float a, float b) {
   return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+// Eight E4M3 codes (value i in byte i) as eight exact bf16 values, packed in pairs.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c) {
+  float f[8];
+  e4m3x4_to_f32(c.x, f);
+  e4m3x4_to_f32(c.y, f + 4);
+  return make_uint4(pack_exact_bf2(f[0], f[1]), pack_exact_bf2(f[2], f[3]), pack_exact_bf2(f[4], f[5]),
+                    pack_exact_bf2(f[6], f[7]));
 }
 
 }  // namespace hsa

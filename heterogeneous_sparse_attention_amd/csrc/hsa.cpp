@@ -475,7 +475,9 @@ void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32
   S.fused = fused ? 1 : 0;
   S.mx_unit = mx_unit;
   S.a_only = a_only ? 1 : 0;
-  S.s2_append = a_only && B.n_seal == 0 ? 1 : 0;
+  // (with FP8 KV the part-A read of the newest token must see its stored value, so
+  // the append stays in S1)
+  S.s2_append = a_only && B.n_seal == 0 && !c->P.kv8 ? 1 : 0;
   S.n_score = (int32_t)n_score;
   if (!fused && !a_only) plan_select_host(c, B, k, S.sel);
   // workgroups: three-launch form, each S2 workgroup takes a share of both parts
@@ -699,6 +701,23 @@ int no_open_seq(hsa_ctx* c) {
                      : kOk;
 }
 
+// The SWA ring of a layer as two byte arrays of one row per slot (slot g = state *
+// n_win + p % n_win): the bf16 K and V rows, or with FP8 KV the code rows (K codes,
+// V codes) and the scale rows. A checkpoint holds n_win rows of each, then the tail.
+struct RingPart {
+  char* base;
+  size_t row;
+};
+void ring_parts(const Pools& P, RingPart out[2]) {
+  if (P.kv8) {
+    out[0] = RingPart{reinterpret_cast<char*>(P.swq), (size_t)kC4Bytes};
+    out[1] = RingPart{reinterpret_cast<char*>(P.sws), (size_t)kC4Scales * 4};
+  } else {
+    out[0] = RingPart{reinterpret_cast<char*>(P.swa_k), (size_t)kRow * 2};
+    out[1] = RingPart{reinterpret_cast<char*>(P.swa_v), (size_t)kRow * 2};
+  }
+}
+
 int check_config(const hsa_config* cfg) {
   if (!cfg) return fail(kInvalid, "config is NULL");
   if (cfg->n_heads != kH || cfg->head_dim != kD)
@@ -720,9 +739,11 @@ int check_config(const hsa_config* cfg) {
   if (cfg->create_flags & ~HSA_CREATE_POISON) return fail(kInvalid, "unknown create_flags");
   if (cfg->c4_mode != HSA_C4_SEALED && cfg->c4_mode != HSA_C4_EAGER)
     return fail(kInvalid, "c4_mode must be HSA_C4_SEALED or HSA_C4_EAGER");
+  if (cfg->kv_format != HSA_KV_BF16 && cfg->kv_format != HSA_KV_FP8)
+    return fail(kInvalid, "kv_format must be HSA_KV_BF16 or HSA_KV_FP8");
   if (cfg->c4_mode == HSA_C4_EAGER &&
-      (cfg->entry_format != HSA_ENTRY_BF16 || cfg->index_format != HSA_INDEX_F32))
-    return fail(kInvalid, "eager C4 takes bf16 entries and fp32 indexer keys");
+      (cfg->entry_format != HSA_ENTRY_BF16 || cfg->index_format != HSA_INDEX_F32 || cfg->kv_format != HSA_KV_BF16))
+    return fail(kInvalid, "eager C4 takes bf16 entries, bf16 KV and fp32 indexer keys");
   if (cfg->layer_types)
     for (int l = 0; l < std::max(1, cfg->n_layers); ++l)
       if (cfg->layer_types[l] < HSA_LAYER_MIXED || cfg->layer_types[l] > HSA_LAYER_HCA)
@@ -760,6 +781,7 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
   const bool mx4 = cfg->index_format == HSA_INDEX_MXFP4;
   const int n_layers = cfg->n_layers > 0 ? cfg->n_layers : 1;
   const bool eager = cfg->c4_mode == HSA_C4_EAGER;
+  const bool kv8 = cfg->kv_format == HSA_KV_FP8;
   // eager C4: each state's open block is C4 block id max_blocks + state, and its table
   // row has one more entry (the open block's)
   const size_t NB4 = NB + (eager ? S : 0), stride = (size_t)bps + (eager ? 1 : 0);
@@ -784,16 +806,18 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
     const bool hca = type == HSA_LAYER_MIXED || type == HSA_LAYER_HCA;
     // per layer, by type: the SWA ring always; C4 entries, indexer keys and the
     // indexer tail for C4 layers; HCA entries for HCA layers
-    constexpr int kPools = 12;
+    constexpr int kPools = 16;
     void* p[kPools] = {};
     const size_t bytes[kPools] = {
-        S * W * kRow * 2, S * W * kRow * 2,                                     // swa_k, swa_v
+        kv8 ? 0 : S * W * kRow * 2, kv8 ? 0 : S * W * kRow * 2,                // swa_k, swa_v
         c4 ? S * kBlk * kIRow * 4 : 0,                                          // idx_tail
         c4 && !fp8 ? NB4 * kC4 * kRow * 2 : 0, c4 && !fp8 ? NB4 * kC4 * kRow * 2 : 0,   // csa (bf16)
-        hca ? NB * kRow * 2 : 0, hca ? NB * kRow * 2 : 0,                       // hca
+        hca && !kv8 ? NB * kRow * 2 : 0, hca && !kv8 ? NB * kRow * 2 : 0,       // hca
         c4 && !mx4 ? NB * kBlk * kIRow * 4 : 0,                                 // idx_k (fp32 keys)
         c4 && fp8 ? NB * kC4 * kC4Bytes : 0, c4 && fp8 ? NB * kC4 * kC4Scales * 4 : 0,   // FP8 C4
-        c4 && mx4 ? NB * kBlk * kIRowQ : 0, c4 && mx4 ? NB * kBlk * kIRowE : 0};       // MXFP4 keys
+        c4 && mx4 ? NB * kBlk * kIRowQ : 0, c4 && mx4 ? NB * kBlk * kIRowE : 0,        // MXFP4 keys
+        kv8 ? S * W * kC4Bytes : 0, kv8 ? S * W * kC4Scales * 4 : 0,            // FP8 ring
+        kv8 && hca ? NB * kC4Bytes : 0, kv8 && hca ? NB * kC4Scales * 4 : 0};   // FP8 HCA
     for (int i = 0; i < kPools; ++i) {
       st = dev_alloc(c, &p[i], bytes[i]);
       if (st) {
@@ -814,6 +838,11 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
     P.c4s = static_cast<float*>(p[9]);
     P.idx_q = static_cast<uint8_t*>(p[10]);
     P.idx_e = static_cast<uint8_t*>(p[11]);
+    P.swq = static_cast<uint8_t*>(p[12]);
+    P.sws = static_cast<float*>(p[13]);
+    P.hcq = static_cast<uint8_t*>(p[14]);
+    P.hcs = static_cast<float*>(p[15]);
+    P.kv8 = kv8 ? 1 : 0;
     P.table = table;
     P.table_stride = (int64_t)stride;
     P.gate_csa = gates + (size_t)l * 2 * kRow;
@@ -961,13 +990,12 @@ hsa_status hsa_block_table_share(hsa_ctx* c, int32_t src, int32_t dst, void* str
                            hipMemcpyDeviceToDevice, s));
   const int64_t slots = std::min(L, W), tail = L - kBlk * nb;
   for (const Pools& P : c->layers) {   // the State of every layer
-    if (slots > 0) {
-      const size_t bytes = (size_t)slots * kRow * 2;
-      HIP_TRY(hipMemcpyAsync(P.swa_k + (size_t)dst * W * kRow, P.swa_k + (size_t)src * W * kRow, bytes,
-                             hipMemcpyDeviceToDevice, s));
-      HIP_TRY(hipMemcpyAsync(P.swa_v + (size_t)dst * W * kRow, P.swa_v + (size_t)src * W * kRow, bytes,
-                             hipMemcpyDeviceToDevice, s));
-    }
+    RingPart rp[2];
+    ring_parts(P, rp);
+    if (slots > 0)
+      for (const RingPart& q : rp)
+        HIP_TRY(hipMemcpyAsync(q.base + (size_t)dst * W * q.row, q.base + (size_t)src * W * q.row,
+                               (size_t)slots * q.row, hipMemcpyDeviceToDevice, s));
     if (tail > 0 && P.c4)
       HIP_TRY(hipMemcpyAsync(P.idx_tail + (size_t)dst * kBlk * kIRow, P.idx_tail + (size_t)src * kBlk * kIRow,
                              (size_t)tail * kIRow * 4, hipMemcpyDeviceToDevice, s));
@@ -1064,7 +1092,9 @@ hsa_status hsa_state_write(hsa_ctx* c, int32_t n_req, const int32_t* states, con
 
 hsa_status hsa_checkpoint_bytes(hsa_ctx* c, int64_t* bytes) {
   if (!c || !bytes) return fail(kInvalid, "NULL argument");
-  *bytes = 2 * (int64_t)c->P.n_win * kRow * 2 + (int64_t)kBlk * kIRow * 4;
+  RingPart rp[2];
+  ring_parts(c->P, rp);
+  *bytes = (int64_t)c->P.n_win * (int64_t)(rp[0].row + rp[1].row) + (int64_t)kBlk * kIRow * 4;
   return kOk;
 }
 
@@ -1079,13 +1109,17 @@ hsa_status hsa_state_checkpoint(hsa_ctx* c, int32_t s_, void* buf, int64_t* len_
   const int64_t L = c->ctl.len(s_), W = c->P.n_win, tail = L - kBlk * c->ctl.n_blocks(s_);
   const int64_t slots = std::min(L, W);
   char* b = static_cast<char*>(buf);
-  const size_t ring = (size_t)W * kRow * 2, S = (size_t)s_;
-  if (slots > 0) {
-    HIP_TRY(hipMemcpyAsync(b, c->P.swa_k + S * W * kRow, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
-    HIP_TRY(hipMemcpyAsync(b + ring, c->P.swa_v + S * W * kRow, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
+  const size_t S = (size_t)s_;
+  RingPart rp[2];
+  ring_parts(c->P, rp);
+  size_t at = 0;   // the parts' rows, n_win of each, then the tail
+  for (const RingPart& q : rp) {
+    if (slots > 0)
+      HIP_TRY(hipMemcpyAsync(b + at, q.base + S * W * q.row, (size_t)slots * q.row, hipMemcpyDefault, s));
+    at += (size_t)W * q.row;
   }
   if (tail > 0 && c->P.c4)
-    HIP_TRY(hipMemcpyAsync(b + 2 * ring, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4,
+    HIP_TRY(hipMemcpyAsync(b + at, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4,
                            hipMemcpyDefault, s));
   *len_out = L;
   return kOk;
@@ -1101,13 +1135,17 @@ hsa_status hsa_state_restore(hsa_ctx* c, int32_t s_, const void* buf, int64_t ck
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t W = c->P.n_win, slots = std::min(ckpt_len, W), tail = ckpt_len % kBlk;
   const char* b = static_cast<const char*>(buf);
-  const size_t ring = (size_t)W * kRow * 2, S = (size_t)s_;
-  if (slots > 0) {
-    HIP_TRY(hipMemcpyAsync(c->P.swa_k + S * W * kRow, b, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
-    HIP_TRY(hipMemcpyAsync(c->P.swa_v + S * W * kRow, b + ring, (size_t)slots * kRow * 2, hipMemcpyDefault, s));
+  const size_t S = (size_t)s_;
+  RingPart rp[2];
+  ring_parts(c->P, rp);
+  size_t at = 0;
+  for (const RingPart& q : rp) {
+    if (slots > 0)
+      HIP_TRY(hipMemcpyAsync(q.base + S * W * q.row, b + at, (size_t)slots * q.row, hipMemcpyDefault, s));
+    at += (size_t)W * q.row;
   }
   if (tail > 0 && c->P.c4)
-    HIP_TRY(hipMemcpyAsync(c->P.idx_tail + S * kBlk * kIRow, b + 2 * ring, (size_t)tail * kIRow * 4,
+    HIP_TRY(hipMemcpyAsync(c->P.idx_tail + S * kBlk * kIRow, b + at, (size_t)tail * kIRow * 4,
                            hipMemcpyDefault, s));
   return recompute_open(c, &s_, 1, s);   // eager C4: the open block's entries
 }
@@ -1124,7 +1162,8 @@ hsa_status hsa_state_restore_batch(hsa_ctx* c, int32_t n, const int32_t* states,
   std::sort(seen.begin(), seen.end());
   if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return fail(kInvalid, "a state appears twice");
   const int64_t W = c->P.n_win;
-  const size_t ring = (size_t)W * kRow * 2;
+  RingPart rp[2];
+  ring_parts(c->P, rp);
   std::vector<CopySeg> segs;
   int64_t total = 0;
   auto add = [&](const char* src, void* dst, size_t bytes) {
@@ -1155,9 +1194,12 @@ hsa_status hsa_state_restore_batch(hsa_ctx* c, int32_t n, const int32_t* states,
     if (!b) return fail(kInvalid, "checkpoint buffer is not device or pinned host memory");
     const int64_t slots = std::min<int64_t>(ckpt_lens[i], W), tail = ckpt_lens[i] % kBlk;
     const size_t S = (size_t)s_;
-    add(b, c->P.swa_k + S * W * kRow, (size_t)slots * kRow * 2);
-    add(b + ring, c->P.swa_v + S * W * kRow, (size_t)slots * kRow * 2);
-    if (tail > 0 && c->P.c4) add(b + 2 * ring, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4);
+    size_t at = 0;
+    for (const RingPart& q : rp) {
+      add(b + at, q.base + S * W * q.row, (size_t)slots * q.row);
+      at += (size_t)W * q.row;
+    }
+    if (tail > 0 && c->P.c4) add(b + at, c->P.idx_tail + S * kBlk * kIRow, (size_t)tail * kIRow * 4);
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (!segs.empty()) {
@@ -1324,6 +1366,7 @@ hsa_status hsa_export_block(hsa_ctx* c, int32_t b, void* csa_k, void* csa_v, voi
   if (c->P.mx4 && idx_k) return fail(kInvalid, "MXFP4 indexer keys: export them with hsa_export_idx_mxfp4");
   if (!c->P.c4 && (csa_k || csa_v || idx_k)) return fail(kInvalid, "this layer keeps no C4 entries or indexer keys");
   if (!c->P.hca && (hca_k || hca_v)) return fail(kInvalid, "this layer keeps no HCA entries");
+  if (c->P.kv8 && (hca_k || hca_v)) return fail(kInvalid, "HCA entries are FP8: use hsa_export_hca_fp8");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t B = (size_t)b;
   if (csa_k) HIP_TRY(hipMemcpyAsync(csa_k, c->P.csa_k + B * kC4 * kRow, kC4 * kRow * 2, hipMemcpyDeviceToHost, s));
@@ -1400,6 +1443,7 @@ hsa_status hsa_export_state(hsa_ctx* c, int32_t s_, void* swa_k, void* swa_v, fl
   if (idx_tail && !c->P.c4) return fail(kInvalid, "this layer keeps no indexer tail");
   int st = set_device(c);
   if (st) return st;
+  if (c->P.kv8 && (swa_k || swa_v)) return fail(kInvalid, "the ring is FP8: use hsa_export_state_fp8");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t W = (size_t)c->P.n_win, S = (size_t)s_;
   if (swa_k) HIP_TRY(hipMemcpyAsync(swa_k, c->P.swa_k + S * W * kRow, W * kRow * 2, hipMemcpyDeviceToHost, s));
@@ -1407,6 +1451,51 @@ hsa_status hsa_export_state(hsa_ctx* c, int32_t s_, void* swa_k, void* swa_v, fl
   if (idx_tail)
     HIP_TRY(hipMemcpyAsync(idx_tail, c->P.idx_tail + S * kBlk * kIRow, kBlk * kIRow * 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
+  return kOk;
+}
+
+namespace {
+// n rows of FP8 scales as stored (head h at 4 (h % 4) + h / 4, K then V) to head order.
+void scales_to_heads(const float* in, int64_t n, float* out) {
+  for (int64_t r = 0; r < n; ++r)
+    for (int h = 0; h < kH; ++h) {
+      const int hp = 4 * (h % 4) + h / 4;
+      out[r * kC4Scales + h] = in[r * kC4Scales + hp];
+      out[r * kC4Scales + kH + h] = in[r * kC4Scales + kH + hp];
+    }
+}
+}  // namespace
+
+hsa_status hsa_export_state_fp8(hsa_ctx* c, int32_t s_, uint8_t* codes, float* scales, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->P.kv8) return fail(kInvalid, "the ring is bf16");
+  if (!c->ctl.valid_state(s_)) return fail(kInvalid, "state not allocated");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t W = (size_t)c->P.n_win, g0 = (size_t)s_ * W;
+  if (codes) HIP_TRY(hipMemcpyAsync(codes, c->P.swq + g0 * kC4Bytes, W * kC4Bytes, hipMemcpyDeviceToHost, s));
+  std::vector<float> sc(W * kC4Scales);
+  if (scales)
+    HIP_TRY(hipMemcpyAsync(sc.data(), c->P.sws + g0 * kC4Scales, sc.size() * 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (scales) scales_to_heads(sc.data(), (int64_t)W, scales);
+  return kOk;
+}
+
+hsa_status hsa_export_hca_fp8(hsa_ctx* c, int32_t b, uint8_t* codes, float* scales, void* stream) {
+  if (!c) return fail(kInvalid, "NULL context");
+  if (!c->P.kv8) return fail(kInvalid, "HCA entries are bf16");
+  if (!c->P.hca) return fail(kInvalid, "this layer keeps no HCA entries");
+  if (!c->ctl.valid_block(b) || c->ctl.refcount(b) == 0) return fail(kInvalid, "block not in use");
+  int st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (codes) HIP_TRY(hipMemcpyAsync(codes, c->P.hcq + (size_t)b * kC4Bytes, kC4Bytes, hipMemcpyDeviceToHost, s));
+  float sc[kC4Scales];
+  if (scales) HIP_TRY(hipMemcpyAsync(sc, c->P.hcs + (size_t)b * kC4Scales, sizeof(sc), hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (scales) scales_to_heads(sc, 1, scales);
   return kOk;
 }
 

@@ -22,10 +22,13 @@
 namespace hsa {
 
 // Where token t of the block being sealed lives: in the state (ring slot, indexer
-// tail slot) if its position precedes len_old, else in the packed input.
+// tail slot) if its position precedes len_old, else in the packed input. With FP8
+// KV the ring slots hold codes and scales (ring_q, ring_s: the state's first slot).
 struct TokSrc {
   const uint16_t* ring_k;
   const uint16_t* ring_v;
+  const uint8_t* ring_q;
+  const float* ring_s;
   const float* tail_i;
   const uint16_t* in_k;
   const uint16_t* in_v;
@@ -46,7 +49,42 @@ struct TokSrc {
     const int64_t p = pos0 + t;
     return p < len_old ? tail_i + (p % kBlk) * kIRow : in_i + (p - len_old) * kIRow;
   }
+  __device__ __forceinline__ const uint16_t* in_krow(int t) const { return in_k + (pos0 + t - len_old) * kRow; }
+  __device__ __forceinline__ const uint16_t* in_vrow(int t) const { return in_v + (pos0 + t - len_old) * kRow; }
+  __device__ __forceinline__ int64_t slot(int t) const { return (pos0 + t) % n_win; }
 };
+
+// This lane's 8 values (at off = 8 tid: head tid / 16) of token t's K and V, as the
+// State stores them. bf16 KV: the bf16 values, scales 1. FP8 KV (KV8): the E4M3
+// code values as exact bf16 pairs and the head's K and V scales (value = code *
+// scale); a token still in the input is quantised here exactly as the ring write
+// stores it (same lanes, same per-head maximum), so both give the same bits.
+template <bool KV8>
+__device__ __forceinline__ void load_tok(const TokSrc& src, int t, int off, uint4& kw, uint4& vw, float& sk,
+                                         float& sv) {
+  if constexpr (!KV8) {
+    kw = *reinterpret_cast<const uint4*>(src.k(t) + off);
+    vw = *reinterpret_cast<const uint4*>(src.v(t) + off);
+    sk = sv = 1.f;
+  } else {
+    const int h = threadIdx.x >> 4;
+    if (src.resident(t)) {   // workgroup-uniform
+      const int64_t g = src.slot(t);
+      const uint8_t* q = src.ring_q + g * kC4Bytes;
+      kw = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(q + off));
+      vw = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(q + kRow + off));
+      const float* sc = src.ring_s + g * kC4Scales;
+      sk = sc[4 * (h & 3) + (h >> 2)];
+      sv = sc[kH + 4 * (h & 3) + (h >> 2)];
+    } else {
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>(src.in_krow(t) + off), f);
+      kw = e4m3x8_to_bf16(quantize8_e4m3(f, sk));
+      unpack8(*reinterpret_cast<const uint4*>(src.in_vrow(t) + off), f);
+      vw = e4m3x8_to_bf16(quantize8_e4m3(f, sv));
+    }
+  }
+}
 
 constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
 
@@ -56,9 +94,12 @@ constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
 // scale (lanes 16h .. 16h+15 hold head h, so the scale's max runs over one DPP row).
 // The seal and the eager entries of an open block both store through it, so an
 // entry is the same bits before and after its block seals.
-template <bool FP8>
+// With FP8 KV (KV8) the tokens' values are code values and sk / sv their per-token
+// K and V scales, folded into the pooling weights.
+template <bool FP8, bool KV8 = false>
 __device__ __forceinline__ void c4_pool_store(const Pools& P, int64_t row, const uint4* kw, const uint4* vw,
-                                              const float* gc) {
+                                              const float* gc, const float* sk = nullptr,
+                                              const float* sv = nullptr) {
   const int tid = threadIdx.x;
   const int h = tid >> 4;
   const int off = tid * 8;
@@ -78,10 +119,12 @@ __device__ __forceinline__ void c4_pool_store(const Pools& P, int64_t row, const
     float kf[8], vf[8];
     unpack8(kw[u], kf);
     unpack8(vw[u], vf);
+    const float ek = KV8 ? e[u] * sk[u] : e[u];
+    const float ev = KV8 ? e[u] * sv[u] : e[u];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      ck[i] = fmaf(e[u], kf[i], ck[i]);
-      cv[i] = fmaf(e[u], vf[i], cv[i]);
+      ck[i] = fmaf(ek, kf[i], ck[i]);
+      cv[i] = fmaf(ev, vf[i], cv[i]);
     }
   }
 #pragma unroll
@@ -90,17 +133,9 @@ __device__ __forceinline__ void c4_pool_store(const Pools& P, int64_t row, const
     cv[i] *= inv;
   }
   if (FP8) {
-    float sk, sv;
-    const uint2 qk = quantize8_e4m3(ck, sk);
-    const uint2 qv = quantize8_e4m3(cv, sv);
-    uint8_t* q = P.c4q + row * kC4Bytes;
-    *reinterpret_cast<uint2*>(q + off) = qk;
-    *reinterpret_cast<uint2*>(q + kRow + off) = qv;
-    if ((tid & 15) == 0) {
-      const int hp = 4 * (h & 3) + (h >> 2);   // the order attention lanes read
-      P.c4s[row * kC4Scales + hp] = sk;
-      P.c4s[row * kC4Scales + kH + hp] = sv;
-    }
+    (void)h;
+    store_row_fp8(ck, P.c4q + row * kC4Bytes, P.c4s + row * kC4Scales);
+    store_row_fp8(cv, P.c4q + row * kC4Bytes + kRow, P.c4s + row * kC4Scales + kH);
   } else {
     uint4 ok, ov;
     ok.x = pack_bf2(ck[0], ck[1]); ok.y = pack_bf2(ck[2], ck[3]);
@@ -151,7 +186,7 @@ __device__ __forceinline__ void open_entry(const Pools& P, int32_t state, int32_
 // for this lane's 8 dims. Both seal paths build the HCA entry from the same eight
 // partials merged in the same order, so bulk and one-token appends give
 // bit-identical blocks.
-template <bool FP8, bool C4>
+template <bool FP8, bool C4, bool KV8 = false>
 __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int32_t id, int t0,
                                           float& m, float& l, float* acck, float* accv) {
   const int tid = threadIdx.x;
@@ -175,11 +210,9 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
   for (int g = 0; g < kSubTok / 4; ++g) {
     const int tb = t0 + 4 * g;
     uint4 kw[4], vw[4];
+    float sk[4], sv[4];   // FP8 KV: the tokens' per-head scales (1 with bf16 KV)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      kw[u] = *reinterpret_cast<const uint4*>(src.k(tb + u) + off);
-      vw[u] = *reinterpret_cast<const uint4*>(src.v(tb + u) + off);
-    }
+    for (int u = 0; u < 4; ++u) load_tok<KV8>(src, tb + u, off, kw[u], vw[u], sk[u], sv[u]);
     // indexer keys of the 4 tokens: 4 x 64 float4, one per lane (stored as MXFP4
     // when P.mx4, a wave per key); layers without C4 entries keep none
     if constexpr (C4) {
@@ -207,6 +240,10 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
       }
       gc[u] = row_sum16(a);
       gh[u] = row_sum16(b);
+      if constexpr (KV8) {
+        gc[u] *= sk[u];
+        gh[u] *= sk[u];
+      }
     }
     // HCA running softmax over the block's tokens
     {
@@ -226,17 +263,19 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
         float kf[8], vf[8];
         unpack8(kw[u], kf);
         unpack8(vw[u], vf);
+        const float ek = KV8 ? e[u] * sk[u] : e[u];
+        const float ev = KV8 ? e[u] * sv[u] : e[u];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          acck[i] = fmaf(e[u], kf[i], acck[i]);
-          accv[i] = fmaf(e[u], vf[i], accv[i]);
+          acck[i] = fmaf(ek, kf[i], acck[i]);
+          accv[i] = fmaf(ev, vf[i], accv[i]);
         }
       }
       m = mx;
     }
     // C4 entry (tokens tb .. tb+3) after the HCA update, so the packed tokens are
     // dead while an FP8 entry is quantised
-    if constexpr (C4) c4_pool_store<FP8>(P, (int64_t)id * kC4 + (tb >> 2), kw, vw, gc);
+    if constexpr (C4) c4_pool_store<FP8, KV8>(P, (int64_t)id * kC4 + (tb >> 2), kw, vw, gc, sk, sv);
   }
 }
 
@@ -259,6 +298,17 @@ __device__ __forceinline__ void store_hca(const Pools& P, int32_t id, float l, c
                                           const float* accv) {
   const int off = threadIdx.x * 8;
   const float inv = 1.f / l;
+  if (P.kv8) {   // FP8 KV: per-head E4M3 codes and scales
+    float k8[8], v8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      k8[i] = acck[i] * inv;
+      v8[i] = accv[i] * inv;
+    }
+    store_row_fp8(k8, P.hcq + (int64_t)id * kC4Bytes, P.hcs + (int64_t)id * kC4Scales);
+    store_row_fp8(v8, P.hcq + (int64_t)id * kC4Bytes + kRow, P.hcs + (int64_t)id * kC4Scales + kH);
+    return;
+  }
   uint4 ok, ov;
   ok.x = pack_bf2(acck[0] * inv, acck[1] * inv); ok.y = pack_bf2(acck[2] * inv, acck[3] * inv);
   ok.z = pack_bf2(acck[4] * inv, acck[5] * inv); ok.w = pack_bf2(acck[6] * inv, acck[7] * inv);
@@ -271,15 +321,33 @@ __device__ __forceinline__ void store_hca(const Pools& P, int32_t id, float l, c
 // Decode-time append of request i's one new token (position p = r.len - 1): ring
 // slot p mod n_win, indexer-tail slot p mod 128, and the device table entry of a
 // block the token seals (r.aux = its id, else -1). 256 threads.
+// Write one token's K and V rows (bf16 input rows krow, vrow) into ring slot g =
+// state * n_win + p % n_win, as bf16 or (FP8 KV) as per-head codes and scales.
+// 256 threads, each 8 values of each row.
+__device__ __forceinline__ void write_ring_token(const Pools& P, int64_t g, const uint16_t* krow,
+                                                 const uint16_t* vrow) {
+  const int tid = threadIdx.x;
+  const uint4 kw = reinterpret_cast<const uint4*>(krow)[tid];
+  const uint4 vw = reinterpret_cast<const uint4*>(vrow)[tid];
+  if (P.kv8) {
+    float f[8];
+    unpack8(kw, f);
+    store_row_fp8(f, P.swq + g * kC4Bytes, P.sws + g * kC4Scales);
+    unpack8(vw, f);
+    store_row_fp8(f, P.swq + g * kC4Bytes + kRow, P.sws + g * kC4Scales + kH);
+    return;
+  }
+  reinterpret_cast<uint4*>(P.swa_k + g * kRow)[tid] = kw;
+  reinterpret_cast<uint4*>(P.swa_v + g * kRow)[tid] = vw;
+}
+
 template <bool C4>
 __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i,
                                              const uint16_t* kin, const uint16_t* vin,
                                              const float* iin) {
   const int tid = threadIdx.x;
   const int64_t p = r.len - 1;
-  const int64_t ring = ((int64_t)r.state * P.n_win + (p % P.n_win)) * kRow;
-  reinterpret_cast<uint4*>(P.swa_k + ring)[tid] = reinterpret_cast<const uint4*>(kin + (int64_t)i * kRow)[tid];
-  reinterpret_cast<uint4*>(P.swa_v + ring)[tid] = reinterpret_cast<const uint4*>(vin + (int64_t)i * kRow)[tid];
+  write_ring_token(P, (int64_t)r.state * P.n_win + (p % P.n_win), kin + (int64_t)i * kRow, vin + (int64_t)i * kRow);
   if (C4 && tid < kIRow / 4) {   // the indexer tail (layers with C4 entries)
     const int64_t ti = ((int64_t)r.state * kBlk + (p % kBlk)) * kIRow;
     reinterpret_cast<float4*>(P.idx_tail + ti)[tid] =
@@ -292,14 +360,22 @@ __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i
 // 4 C4 entries, 16 indexer keys and one HCA partial to part[item * 8 + sub]. The
 // newest token (position r.len - 1) is read from input row i, so this may run in
 // the same launch as append_token. 256 threads.
-template <bool FP8, bool C4>
+// The state's ring as a token source of the seal (bf16 rows, or FP8 codes and scales).
+__device__ __forceinline__ void ring_src(const Pools& P, int32_t state, TokSrc& src) {
+  const int64_t g0 = (int64_t)state * P.n_win;
+  src.ring_k = P.kv8 ? nullptr : P.swa_k + g0 * kRow;
+  src.ring_v = P.kv8 ? nullptr : P.swa_v + g0 * kRow;
+  src.ring_q = P.kv8 ? P.swq + g0 * kC4Bytes : nullptr;
+  src.ring_s = P.kv8 ? P.sws + g0 * kC4Scales : nullptr;
+}
+
+template <bool FP8, bool C4, bool KV8 = false>
 __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i, int item, int sub,
                                             const uint16_t* kin, const uint16_t* vin,
                                             const float* iin, float* part) {
   const int tid = threadIdx.x;
   TokSrc src;
-  src.ring_k = P.swa_k + (int64_t)r.state * P.n_win * kRow;
-  src.ring_v = P.swa_v + (int64_t)r.state * P.n_win * kRow;
+  ring_src(P, r.state, src);
   src.tail_i = P.idx_tail + (int64_t)r.state * kBlk * kIRow;
   src.in_k = kin + (int64_t)i * kRow;
   src.in_v = vin + (int64_t)i * kRow;
@@ -308,7 +384,7 @@ __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i,
   src.pos0 = (int64_t)(r.nb - 1) * kBlk;
   src.n_win = P.n_win;
   float m, l, acck[8], accv[8];
-  seal_part<FP8, C4>(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
+  seal_part<FP8, C4, KV8>(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
   float* mine = part + (int64_t)(item * kSealSplit + sub) * kPartFloats;
   const int h = tid >> 4;
   if ((tid & 15) == 0) {

@@ -161,14 +161,15 @@ __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B,
 // FP8 entries: the seal's quantisation needs more registers than 4 workgroups per
 // CU leave, so that instance runs 3 per CU; the bf16 instance keeps 4.
 // (C4 false: a layer without C4 entries, whose seal keeps only the HCA partial)
-template <bool FP8, bool C4>
-__global__ __launch_bounds__(256, FP8 ? 3 : 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
+// (KV8: FP8 KV, whose seal reads codes and scales from the ring)
+template <bool FP8, bool C4, bool KV8>
+__global__ __launch_bounds__(256, FP8 || KV8 ? 3 : 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
   int bid = blockIdx.x;
   // -- seal eighths (first, so the longest single workgroups start early)
   if (bid < kSealSplit * B.n_seal) {
     const int item = bid / kSealSplit;
     const int ri = B.seal_req[item];
-    seal_eighth<FP8, C4>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
+    seal_eighth<FP8, C4, KV8>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
     return;
   }
   bid -= kSealSplit * B.n_seal;
@@ -210,8 +211,7 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
   const int swa = R.len < P.n_win ? R.len : P.n_win;
   int x0, x1;
   chunk_range(keys_a(P, R), nch, w, x0, x1);
-  const uint16_t* ring_k = P.swa_k + (int64_t)R.state * P.n_win * kRow;
-  const uint16_t* ring_v = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  const int64_t g0 = (int64_t)R.state * P.n_win;   // the state's first ring slot
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
   const int64_t p0 = (int64_t)R.len - swa;   // oldest SWA position; the ring holds all (S1 wrote the newest)
   auto key_a = [&](int x) {
@@ -219,23 +219,25 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
     a.k = a.v = nullptr;
     if (x < swa) {
       if (S.s2_append && p0 + x == R.len - 1) {   // being appended in this launch: from the input
-        a.k = S.kin + (int64_t)r * kRow;
+        a.k = S.kin + (int64_t)r * kRow;          // (bf16 KV only: FP8 KV appends in S1)
         a.v = S.vin + (int64_t)r * kRow;
         return a;
       }
-      const int64_t slot = (p0 + x) % P.n_win;
-      a.k = ring_k + slot * kRow;
-      a.v = ring_v + slot * kRow;
+      const C4Addr c = ring_addr(P, g0 + (p0 + x) % P.n_win);
+      a.k = c.k;
+      a.v = c.v;
       return a;
     }
     const int32_t id = tab[x - swa];
     if (id < 0 || id >= P.max_blocks) return a;
-    a.k = P.hca_k + (int64_t)id * kRow;
-    a.v = P.hca_v + (int64_t)id * kRow;
+    const C4Addr c = hca_addr(P, id);
+    a.k = c.k;
+    a.v = c.v;
     return a;
   };
+  const C4Addr dm = dummy_rows(P, R.state);
   float M, L, A8[8];
-  attend_keys<WAVES>(key_a, x0, x1, S.q + (int64_t)r * kRow, ring_k, ring_v, sh, M, L, A8);
+  attend_keys<WAVES>(key_a, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8, 0x7fffffff, P.kv8 != 0);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
 }
 
@@ -278,23 +280,23 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   sel_preload<NT>(N, S.scores + (int64_t)r * S.ld, tab, N / kC4, pre);
   __builtin_amdgcn_sched_barrier(0);   // the row's loads go out ahead of the key prefetch
 
-  const uint16_t* ring_k = P.swa_k + (int64_t)R.state * P.n_win * kRow;
-  const uint16_t* ring_v = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  const int64_t g0 = (int64_t)R.state * P.n_win;   // the state's first ring slot
   const int swa = R.len < P.n_win ? R.len : P.n_win;
   const int64_t p0 = (int64_t)R.len - swa;
   auto key_a = [&](int x) {
     KeyAddr a;
     a.k = a.v = nullptr;
     if (x < swa) {
-      const int64_t slot = (p0 + x) % P.n_win;
-      a.k = ring_k + slot * kRow;
-      a.v = ring_v + slot * kRow;
+      const C4Addr c = ring_addr(P, g0 + (p0 + x) % P.n_win);
+      a.k = c.k;
+      a.v = c.v;
       return a;
     }
     const int32_t id = load_global(tab + (x - swa));
     if (id < 0 || id >= P.max_blocks) return a;   // never taken
-    a.k = P.hca_k + (int64_t)id * kRow;
-    a.v = P.hca_v + (int64_t)id * kRow;
+    const C4Addr c = hca_addr(P, id);
+    a.k = c.k;
+    a.v = c.v;
     return a;
   };
   const int64_t max_row = (int64_t)P.c4_ids * kC4;   // blocks and (eager) open blocks
@@ -317,10 +319,11 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
                    SelWin{b0, b1, w == 0}, nc);
     __syncthreads();   // rows in LDS complete; the selection's LDS is free for attention
   };
+  const C4Addr dm = dummy_rows(P, R.state);
   float M, L, A8[8];
   attend_two<WAVES, kMixedRing>(key_a, a0, a1, key_b, b0, b1, stage, select,
-                                         S.q + (int64_t)r * kRow, ring_k, ring_v, sh.attn, M, L, A8,
-                                         P.fp8 != 0);
+                                         S.q + (int64_t)r * kRow, dm.k, dm.v, sh.attn, M, L, A8,
+                                         P.fp8 != 0, P.kv8 != 0);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
@@ -387,8 +390,9 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
     KeyAddr a;
     a.k = a.v = nullptr;
     if (x < sn) {
-      a.k = P.hca_k + (int64_t)R.aux * kRow;
-      a.v = P.hca_v + (int64_t)R.aux * kRow;
+      const C4Addr c = hca_addr(P, R.aux);
+      a.k = c.k;
+      a.v = c.v;
       return a;
     }
     const int64_t row = rows[x - sn];   // C4 row of a selected entry, from S2
@@ -398,11 +402,10 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
     a.v = c.v;
     return a;
   };
-  const uint16_t* dk = P.swa_k + (int64_t)R.state * P.n_win * kRow;   // valid row (L >= 1)
-  const uint16_t* dv = P.swa_v + (int64_t)R.state * P.n_win * kRow;
+  const C4Addr dm = dummy_rows(P, R.state);   // valid rows (L >= 1)
   float M, L, A8[8];
-  attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dk, dv, sh, M, L, A8,
-                           P.fp8 ? sn : 0x7fffffff);
+  attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8, sn, P.kv8 != 0,
+                           P.fp8 != 0);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
@@ -412,15 +415,16 @@ __global__ __launch_bounds__(256) void k_step4(Pools P, ReqBatch B, StepArgs S) 
   const int fb = S.first_b[r], cb = S.first_b[r + 1] - fb;
   const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
   const Req R = B.r[r];
-  ExtraKey xk{nullptr, nullptr, nullptr};
+  ExtraKey xk{nullptr, nullptr, nullptr, false};
   if (S.a_only && (blockIdx.x & 3) == 0)   // no C4 entries: the top-k row is padding
     for (int i = threadIdx.x; i < S.k; i += 256) {
       S.topk[(int64_t)r * S.k + i] = -1;
       if (S.score_out) S.score_out[(int64_t)r * S.k + i] = -INFINITY;
     }
-  if ((S.fused || S.a_only) && R.aux >= 0 && P.hca)   // the HCA entry of the block sealed now, merged in S2
-    xk = ExtraKey{P.hca_k + (int64_t)R.aux * kRow, P.hca_v + (int64_t)R.aux * kRow,
-                  S.q + (int64_t)r * kRow};
+  if ((S.fused || S.a_only) && R.aux >= 0 && P.hca) {   // the HCA entry of the block sealed now, merged in S2
+    const C4Addr c = hca_addr(P, R.aux);
+    xk = ExtraKey{c.k, c.v, S.q + (int64_t)r * kRow, P.kv8 != 0};
+  }
   merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
                  h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow, xk);
 }
@@ -432,9 +436,14 @@ hipError_t launch_step1(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
   const int grid = kSealSplit * B.n_seal + B.n + B.n_open + S.n_score;
   if (grid == 0) return hipSuccess;
   const dim3 g(grid), t(kAttnWaves * 64);
-  if (!P.c4) return launch_k(k_step1<false, false>, g, t, st, ev, P, B, S);
-  if (P.fp8) return launch_k(k_step1<true, true>, g, t, st, ev, P, B, S);
-  return launch_k(k_step1<false, true>, g, t, st, ev, P, B, S);
+  if (P.kv8) {
+    if (!P.c4) return launch_k(k_step1<false, false, true>, g, t, st, ev, P, B, S);
+    if (P.fp8) return launch_k(k_step1<true, true, true>, g, t, st, ev, P, B, S);
+    return launch_k(k_step1<false, true, true>, g, t, st, ev, P, B, S);
+  }
+  if (!P.c4) return launch_k(k_step1<false, false, false>, g, t, st, ev, P, B, S);
+  if (P.fp8) return launch_k(k_step1<true, true, false>, g, t, st, ev, P, B, S);
+  return launch_k(k_step1<false, true, false>, g, t, st, ev, P, B, S);
 }
 
 hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,

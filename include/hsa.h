@@ -92,7 +92,19 @@ typedef struct hsa_config {
                                    layer HSA_LAYER_MIXED                            */
   int32_t c4_mode;              /* HSA_C4_SEALED or HSA_C4_EAGER                    */
   uint32_t create_flags;        /* 0 or HSA_CREATE_POISON                           */
+  int32_t kv_format;            /* storage of SWA ring tokens and HCA entries: HSA_KV_BF16
+                                   or HSA_KV_FP8 ([Ch12] §1 accounts them in FP8)     */
+  int32_t reserved;             /* 0                                                */
 } hsa_config;
+
+/* SWA ring and HCA entry storage. BF16: K and V rows of 16 x 128 bf16. FP8: each
+ * token's K and V (as it enters the State: append, replay, fork, restore) and each
+ * HCA entry (at its seal) are stored per head as E4M3 codes and a float32 scale, by
+ * the HSA_ENTRY_FP8 rule; the State keeps no other copy of a token, so the seal pools
+ * the stored values of a block's tokens and attention reads them. Indexer keys are
+ * not affected. Not with HSA_C4_EAGER. */
+#define HSA_KV_BF16 0
+#define HSA_KV_FP8 1
 
 /* Create flag: fill every pool and every scratch buffer with 0xFF bytes when it is
  * allocated (bf16, fp32 and E4M3 NaN, E8M0 NaN scales, table entries -1), so that a
@@ -260,8 +272,9 @@ hsa_status hsa_state_write(hsa_ctx* ctx, int32_t n_req, const int32_t* states,
                            const int64_t* cu_tokens, const int64_t* pos0, const void* k,
                            const void* v, const float* idx, void* stream);
 
-/* Bytes of one State checkpoint: SWA ring K and V (n_win x 4 KiB each), then the
- * indexer tail (128 x 1 KiB). */
+/* Bytes of one State checkpoint: SWA ring K and V (n_win x 4 KiB each; with FP8 KV
+ * the ring's codes, n_win x 4 KiB, and scales, n_win x 128 B), then the indexer tail
+ * (128 x 1 KiB). */
 hsa_status hsa_checkpoint_bytes(hsa_ctx* ctx, int64_t* bytes);
 
 /* Copy a state's SWA ring and indexer tail into `buf` (device or pinned host memory,
@@ -360,8 +373,9 @@ hsa_status hsa_block_table_get(hsa_ctx* ctx, int32_t state, int32_t* ids, int64_
 hsa_status hsa_block_refcount(hsa_ctx* ctx, int32_t block, int32_t* rc);
 /* Copy one block to host buffers (any may be NULL): csa_k, csa_v bf16
  * [32][16][128] (must be NULL with FP8 entries: see hsa_export_c4_fp8); hca_k,
- * hca_v bf16 [16][128]; idx_k fp32 [128][4][64] (must be NULL with MXFP4 indexer
- * keys: see hsa_export_idx_mxfp4). */
+ * hca_v bf16 [16][128] (must be NULL with FP8 KV: see hsa_export_hca_fp8); idx_k
+ * fp32 [128][4][64] (must be NULL with MXFP4 indexer keys: see
+ * hsa_export_idx_mxfp4). */
 hsa_status hsa_export_block(hsa_ctx* ctx, int32_t block, void* csa_k, void* csa_v,
                             void* hca_k, void* hca_v, float* idx_k, void* stream);
 /* FP8 entries only: copy one block's C4 entries to host buffers (any may be NULL):
@@ -391,10 +405,21 @@ hsa_status hsa_mxfp4_quantize_rows(const float* x, int64_t n_rows, uint8_t* code
                                    void* stream);
 
 /* Copy one State block to host buffers (any may be NULL): swa_k, swa_v bf16
- * [n_win][16][128] in ring-slot order (token p sits in slot p mod n_win);
- * idx_tail fp32 [128][4][64] (token p in slot p mod 128). */
+ * [n_win][16][128] in ring-slot order (token p sits in slot p mod n_win; must be
+ * NULL with FP8 KV: see hsa_export_state_fp8); idx_tail fp32 [128][4][64] (token p in
+ * slot p mod 128). */
 hsa_status hsa_export_state(hsa_ctx* ctx, int32_t state, void* swa_k, void* swa_v,
                             float* idx_tail, void* stream);
+/* FP8 KV only: copy one State's ring to host buffers (either may be NULL): codes u8
+ * [n_win][K, V][16][128] E4M3 in ring-slot order, scales fp32 [n_win][K, V][16] per
+ * head. HSA_ERR_INVALID with bf16 KV. */
+hsa_status hsa_export_state_fp8(hsa_ctx* ctx, int32_t state, uint8_t* codes, float* scales,
+                                void* stream);
+/* FP8 KV only: copy one block's HCA entry to host buffers (either may be NULL): codes
+ * u8 [K, V][16][128], scales fp32 [K, V][16]. HSA_ERR_INVALID with bf16 KV or in a
+ * layer without HCA entries. */
+hsa_status hsa_export_hca_fp8(hsa_ctx* ctx, int32_t block, uint8_t* codes, float* scales,
+                              void* stream);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around each
  * launch of the kernels in `mask` (bit i = kernel id i below); 0 disables.

@@ -13,8 +13,8 @@ Checks, between the two contexts:
   and every sealed block's entries and indexer keys.
 A kernel that read a slot never written would put NaN into its results. One whose
 result depended on timing (a race between workgroups) would differ between the
-two runs. The measured storage is covered, and so are the low-bit formats and
-eager C4.
+two runs. The measured storage is covered, and so are the low-bit formats (FP8
+ring, HCA and C4 entries with MXFP4 indexer keys) and eager C4.
 """
 
 import numpy as np
@@ -44,7 +44,7 @@ def bf16_nan(bits):
     return (np.asarray(bits).view(np.uint16) & 0x7FFF) > 0x7F80
 
 
-def run_once(entries, index, c4_mode, steps=8):
+def run_once(entries, index, c4_mode, kv="bf16", steps=8):
     """One poisoned context through the b32 prefill and `steps` decode steps;
     returns the per-step results and every written pool slot, as host arrays."""
     import torch
@@ -55,7 +55,7 @@ def run_once(entries, index, c4_mode, steps=8):
     Wc, Wh = synth.gate_weights(wl.seed)
     nb = int(((L0 + steps) // 128).sum()) + B
     cache = Cache(wl.n_win, B, nb, Wc, Wh, entry_format=entries, index_format=index, c4_mode=c4_mode,
-                  poison=True)
+                  poison=True, kv_format=kv)
     try:
         st = [cache.state_alloc() for _ in range(B)]
         cu = np.concatenate([[0], np.cumsum(L0)])
@@ -82,8 +82,14 @@ def run_once(entries, index, c4_mode, steps=8):
             L = info["len"]
             ex = cache.export_state(s)
             ring = np.arange(L - info["swa_len"], L) % wl.n_win
-            pools[("ring_k", s)] = ex["swa_k"][ring]
-            pools[("ring_v", s)] = ex["swa_v"][ring]
+            if kv == "fp8":
+                pools[("ring_k", s)] = ex["swa_k_codes"][ring]
+                pools[("ring_v", s)] = ex["swa_v_codes"][ring]
+                pools[("ring_ks", s)] = ex["swa_k_scale"][ring]
+                pools[("ring_vs", s)] = ex["swa_v_scale"][ring]
+            else:
+                pools[("ring_k", s)] = ex["swa_k"][ring]
+                pools[("ring_v", s)] = ex["swa_v"][ring]
             pools[("tail", s)] = ex["idx_tail"][np.arange(L - info["hca_tail"], L) % 128]
             pools[("table", s)] = np.array(cache.block_table(s))
             for lb, b in enumerate(cache.block_table(s)):
@@ -94,11 +100,12 @@ def run_once(entries, index, c4_mode, steps=8):
         cache.close()
 
 
-@pytest.mark.parametrize("entries,index,c4_mode", [("bf16", "f32", "sealed"), ("fp8", "mxfp4", "sealed"),
-                                                   ("bf16", "f32", "eager")])
-def test_two_poisoned_runs_agree_byte_for_byte(entries, index, c4_mode):
-    r1, p1 = run_once(entries, index, c4_mode)
-    r2, p2 = run_once(entries, index, c4_mode)
+@pytest.mark.parametrize("entries,index,c4_mode,kv", [("bf16", "f32", "sealed", "bf16"),
+                                                      ("fp8", "mxfp4", "sealed", "fp8"),
+                                                      ("bf16", "f32", "eager", "bf16")])
+def test_two_poisoned_runs_agree_byte_for_byte(entries, index, c4_mode, kv):
+    r1, p1 = run_once(entries, index, c4_mode, kv)
+    r2, p2 = run_once(entries, index, c4_mode, kv)
     for t, ((i1, s1, o1), (i2, s2, o2)) in enumerate(zip(r1, r2)):
         assert not np.isnan(o1).any() and not np.isnan(s1).any(), t
         assert np.array_equal(i1, i2), t
@@ -113,7 +120,8 @@ def test_two_poisoned_runs_agree_byte_for_byte(entries, index, c4_mode):
             assert not bf16_nan(a).any(), key
         elif a.dtype == np.float32:                   # indexer keys, FP8 scales
             assert not np.isnan(a).any(), key
-        elif name in ("csa_k_codes", "csa_v_codes"):  # E4M3 NaN codes
+        elif name in ("csa_k_codes", "csa_v_codes", "hca_k_codes", "hca_v_codes",
+                      "ring_k", "ring_v") and a.dtype == np.uint8:   # E4M3 NaN codes
             assert not ((a & 0x7F) == 0x7F).any(), key
         elif name == "idx_scales":                    # E8M0 NaN
             assert not (a == 0xFF).any(), key

@@ -48,7 +48,9 @@ def _check_layer(cache, o, states, t):
             g = cache.export_block(b)
             r = o.block(b)
             c4 = t in ("csa", "mixed")
-            assert (("csa_k" in g) or ("csa_k_codes" in g)) == c4 and ("hca_k" in g) == (t in ("hca", "mixed"))
+            kv8 = cache.kv_format == "fp8"
+            assert (("csa_k" in g) or ("csa_k_codes" in g)) == c4
+            assert (("hca_k" in g) or ("hca_k_codes" in g)) == (t in ("hca", "mixed"))
             if c4 and fp8:
                 for n in ("k", "v"):
                     val = e4m3_decode(g[f"csa_{n}_codes"]) * g[f"csa_{n}_scale"][..., None].astype(np.float64)
@@ -60,7 +62,11 @@ def _check_layer(cache, o, states, t):
                 assert np.array_equal(g["idx_codes"], r.idx_codes) and np.array_equal(g["idx_scales"], r.idx_scales)
             elif c4:
                 assert np.array_equal(g["idx"], r.idx)
-            if t in ("hca", "mixed"):
+            if t in ("hca", "mixed") and kv8:   # codes decided from float32 vs float64 pools
+                for n in ("k", "v"):
+                    assert np.mean(g[f"hca_{n}_codes"] == getattr(r, f"hca_{n}_codes")) > 0.99, (t, n)
+                    assert np.allclose(g[f"hca_{n}_scale"], getattr(r, f"hca_{n}_scale"), rtol=1e-6, atol=0)
+            elif t in ("hca", "mixed"):
                 for n in ("hca_k", "hca_v"):
                     assert rel_l2(bf16_to_f64(g[n]), getattr(r, n)) <= TOL, (t, n)
         ex = cache.export_state(s)
@@ -69,18 +75,25 @@ def _check_layer(cache, o, states, t):
         L, W = st.L, cache.n_win
         for i, (k, v) in enumerate(st.swa):
             p = L - len(st.swa) + i
+            if cache.kv_format == "fp8":   # ring slots: the oracle's codes and scales exactly
+                kc, ks, vc, vs = st.swa_q[i]
+                assert np.array_equal(ex["swa_k_codes"][p % W], kc) and np.array_equal(ex["swa_v_codes"][p % W], vc)
+                assert np.array_equal(ex["swa_k_scale"][p % W], ks) and np.array_equal(ex["swa_v_scale"][p % W], vs)
+                continue
             assert np.array_equal(bf16_to_f64(ex["swa_k"][p % W]), k) and np.array_equal(bf16_to_f64(ex["swa_v"][p % W]), v)
         if t in ("csa", "mixed"):
             for i, (_, _, ki) in enumerate(st.tail):
                 assert np.array_equal(ex["idx_tail"][(L - len(st.tail) + i) % 128], ki)
 
 
-MODES = [("1", "bf16", "f32", "sealed"), ("0", "bf16", "f32", "sealed"), ("1", "fp8", "f32", "sealed"),
-         ("0", "bf16", "mxfp4", "sealed"), ("1", "bf16", "f32", "eager"), ("0", "bf16", "f32", "eager")]
+MODES = [("1", "bf16", "f32", "sealed", "bf16"), ("0", "bf16", "f32", "sealed", "bf16"),
+         ("1", "fp8", "f32", "sealed", "bf16"), ("0", "bf16", "mxfp4", "sealed", "bf16"),
+         ("1", "bf16", "f32", "eager", "bf16"), ("0", "bf16", "f32", "eager", "bf16"),
+         ("1", "bf16", "f32", "sealed", "fp8"), ("0", "fp8", "mxfp4", "sealed", "fp8")]
 
 
-@pytest.mark.parametrize("fused,entries,index,c4_mode", MODES)
-def test_layers_match_per_layer_oracles(monkeypatch, fused, entries, index, c4_mode):
+@pytest.mark.parametrize("fused,entries,index,c4_mode,kv", MODES)
+def test_layers_match_per_layer_oracles(monkeypatch, fused, entries, index, c4_mode, kv):
     import torch
     import heterogeneous_sparse_attention_amd as hsa
     monkeypatch.setenv("HSA_STEP_FUSED", fused)
@@ -92,7 +105,7 @@ def test_layers_match_per_layer_oracles(monkeypatch, fused, entries, index, c4_m
     # an HCA layer's step then runs its seal launch and the others skip it
     L0 = np.array([1, 127, 128, 254, 766, 1100])
     nbk = int((L0 + 140).sum() // 128 + B)
-    kw = dict(entry_format=entries, index_format=index, c4_mode=c4_mode)
+    kw = dict(entry_format=entries, index_format=index, c4_mode=c4_mode, kv_format=kv)
     cache = hsa.Cache(128, B, nbk, Wc, Wh, layer_types=TYPES, **kw)
     orc = [Oracle(128, g[0], g[1], B, nbk, layer_type=t, **kw) for g, t in zip(gates, TYPES)]
     st = [cache.state_alloc() for _ in range(B)]
