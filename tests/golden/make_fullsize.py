@@ -1,5 +1,7 @@
-"""Expected decode outputs for sampled requests of the two largest workloads,
-computed by the oracle alone (oracle.decode_reference) from the seeded inputs.
+"""Expected decode outputs of the two largest workloads, computed by the oracle
+alone (oracle.decode_reference) from the seeded inputs: every request of the long
+workload at every decode step, and every request of the prefix workload at four
+steps (the first, two inside and the last).
 
     python tests/golden/make_fullsize.py [--procs 8] [--only prefix|long]
 
@@ -29,36 +31,18 @@ import synth  # noqa: E402
 from oracle import decode_reference  # noqa: E402
 from synth.workloads import RequestTokens, make  # noqa: E402
 
-# (workload index, file, sampled requests, sampled decode steps)
+# (workload index, file, requests (None: all), decode steps)
 SAMPLES = {
-    "prefix": (3, "prefix_decode.npz", None, (0, 31)),
-    "long": (5, "long_decode.npz", (0, 3), (0, 7, 8, 15)),
+    "prefix": (3, "prefix_decode.npz", None, (0, 10, 21, 31)),
+    "long": (5, "long_decode.npz", None, tuple(range(16))),
 }
-
-
-def prefix_requests(wl) -> list:
-    """Four requests of different groups: the shortest and longest prefill, one
-    that forks inside the shared prefix and one that forks at its end."""
-    L0 = wl.prefill
-    short = int(np.argmin(L0))
-    long_ = int(np.argmax(L0))
-    picks = [short, long_]
-    for b in range(wl.batch):
-        if len(picks) == 4:
-            break
-        if b in picks or wl.group(b) in {wl.group(p) for p in picks}:
-            continue
-        inside = L0[b] < wl.prefix_len
-        if inside != (L0[picks[-1]] < wl.prefix_len) or len(picks) == 3:
-            picks.append(b)
-    return sorted(picks)
 
 
 def run(name: str, procs: int) -> None:
     index, fname, reqs, steps = SAMPLES[name]
     wl = make(index)
     if reqs is None:
-        reqs = prefix_requests(wl)
+        reqs = list(range(wl.batch))
     Wc, Wh = synth.gate_weights(wl.seed)
     rows = {"req": [], "step": [], "L": [], "idx": [], "out": []}
     with mp.get_context("fork").Pool(procs) as pool:

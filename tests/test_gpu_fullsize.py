@@ -3,15 +3,18 @@ times (one hsa_decode_step per step over the whole batch, default launch shapes)
 
 - b32 (32 requests, L0 up to 8192, 64 steps): every step of every request against
   the oracle driven token by token.
-- prefix (64 requests of 16K-64K tokens sharing 8 prefixes by fork, n_win 4096,
-  k 1024, 32 steps), long (4 requests of 2**20 tokens, k 2048, 16 steps across a
-  block boundary) and bulk (8 x 131072 tokens in one append): integer state and
-  refcounts exactly; selected scores exactly against the oracle's scores of those
-  entries; the selection against the oracle's scores of sampled blocks; sampled
-  block entries against the oracle's compressor; and, for sampled requests and
-  steps, the full top-k row and the attention output against
-  tests/golden/*_decode.npz, which tests/golden/make_fullsize.py writes with the
-  oracle alone.
+- long (4 requests of 2**20 tokens, k 2048, 16 steps across a block boundary) and
+  prefix (64 requests of 16K-64K tokens sharing 8 prefixes by fork, n_win 4096,
+  k 1024, 32 steps): every request's full top-k row and attention output against
+  tests/golden/*_decode.npz (every step of the long workload; steps 0, 10, 21 and
+  31 of the prefix workload), which tests/golden/make_fullsize.py writes with the
+  oracle alone. Also: integer state and refcounts exactly, the selected scores
+  exactly against the oracle's scores of those entries, the selection against the
+  oracle's scores of sampled blocks, the rings and tails, and at least 64 sealed
+  blocks per request against the oracle's compressor. The sampled blocks always
+  include the first and the last, the block sealed during the decode steps, and
+  the first and last shared-prefix blocks.
+- bulk (8 x 131072 tokens in one append): state, tables, sampled blocks, rings.
 """
 
 import os
@@ -83,23 +86,63 @@ def check_selection(src, idx, val, nb, k, q_idx, sample_blocks):
                 assert j > tie_max, (j, tie_max)
 
 
-def check_block(cache, block_id, src, lb, gates):
-    """A sealed block's device entries against the oracle's compressor of its tokens."""
+def expected_block(index, b, lb, gates):
+    """The oracle's entries of sealed block lb of request b of a workload: bf16-rounded
+    C4 and HCA entries (float32) and the block's indexer keys."""
     Wc, Wh = gates
-    g = cache.export_block(block_id)
-    K, V, KI = src(np.arange(BLOCK * lb, BLOCK * (lb + 1)))
+    K, V, KI = RequestTokens(index, b)(np.arange(BLOCK * lb, BLOCK * (lb + 1)))
     K = K.astype(np.float64)
     V = V.astype(np.float64)
-    ck = np.empty((C4_PER_BLOCK, 16, 128))
+    ck = np.empty((C4_PER_BLOCK, 16, 128), np.float32)
     cv = np.empty_like(ck)
     for j in range(C4_PER_BLOCK):
         ck[j], cv[j] = gated_pool(K[M_CSA * j:M_CSA * (j + 1)], V[M_CSA * j:M_CSA * (j + 1)], Wc)
     hk, hv = gated_pool(K, V, Wh)
-    for name, ref in (("csa_k", ck), ("csa_v", cv), ("hca_k", hk), ("hca_v", hv)):
+    return {"csa_k": ck, "csa_v": cv, "hca_k": hk.astype(np.float32), "hca_v": hv.astype(np.float32),
+            "idx": KI}
+
+
+def _expected_block_job(job):
+    return expected_block(*job)
+
+
+def compare_block(g, ref, where):
+    for name in ("csa_k", "csa_v", "hca_k", "hca_v"):
         val = bf16_to_f64(g[name])
-        assert rel_l2(val, ref) <= TOL, (name, lb, rel_l2(val, ref))
-        assert np.mean(val == ref) > 0.97, (name, lb)
-    assert np.array_equal(g["idx"], KI)
+        r = ref[name].astype(np.float64)
+        assert rel_l2(val, r) <= TOL, (name, where, rel_l2(val, r))
+        assert np.mean(val == r) > 0.97, (name, where)
+    assert np.array_equal(g["idx"], ref["idx"]), where
+
+
+def check_block(cache, block_id, src, lb, gates):
+    """A sealed block's device entries against the oracle's compressor of its tokens."""
+    compare_block(cache.export_block(block_id), expected_block(src.index, src.b, lb, gates), (src.b, lb))
+
+
+def check_blocks(cache, items, index, gates, workers=None):
+    """Check many sealed blocks: items = [(physical id, request, logical block)], each
+    physical id once. The oracle's entries come from worker processes (spawned: they
+    never touch the GPU), the device's from hsa_export_block."""
+    import multiprocessing as mp
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    jobs = [(index, b, lb, gates) for _, b, lb in items]
+    with mp.get_context("spawn").Pool(workers) as pool:
+        for (bid, b, lb), ref in zip(items, pool.imap(_expected_block_job, jobs, chunksize=4)):
+            compare_block(cache.export_block(bid), ref, (b, lb))
+    return len(items)
+
+
+def sample_blocks(rng, nb, must, n=64):
+    """At least n distinct logical blocks of [0, nb) (all of them if fewer), always
+    including `must`."""
+    picks = {x for x in must if 0 <= x < nb}
+    extra = rng.permutation(nb)
+    i = 0
+    while len(picks) < min(n, nb):
+        picks.add(int(extra[i]))
+        i += 1
+    return sorted(picks)
 
 
 def check_ring(cache, state, src, L, n_win):
@@ -158,23 +201,25 @@ def check_golden_rows(gold, b, t, idx, out):
 
 # ------------------------------------------------------------------ b32
 
-B32_MODES = [("bf16", "f32", "sealed", 64), ("fp8", "mxfp4", "sealed", 16), ("bf16", "f32", "eager", 16)]
+B32_MODES = [("bf16", "f32", "sealed", 64, "bf16"), ("fp8", "mxfp4", "sealed", 16, "fp8"),
+             ("bf16", "f32", "eager", 16, "bf16")]
 
 
-@pytest.mark.parametrize("entries,index,c4_mode,steps", B32_MODES)
-def test_b32_every_step_against_oracle(entries, index, c4_mode, steps):
+@pytest.mark.parametrize("entries,index,c4_mode,steps,kv", B32_MODES)
+def test_b32_every_step_against_oracle(entries, index, c4_mode, steps, kv):
     """Every step of every request; besides the measured storage, the pages' own
-    (FP8 entries, MXFP4 indexer keys) and eager C4 for 16 steps each."""
+    (FP8 SWA ring, HCA and C4 entries, MXFP4 indexer keys) and eager C4 for 16
+    steps each."""
     import bench
     wl = make(2)
     B, k = wl.batch, wl.topk
     L0 = wl.prefill.astype(np.int64)
-    cache, inst = bench.setup_decode(wl, steps, 1, entries, index, None, c4_mode)
+    cache, inst = bench.setup_decode(wl, steps, 1, entries, index, None, c4_mode, kv)
     states = inst[0]
-    say(f"b32 ({entries}, {index}, {c4_mode}): prefilled {int(L0.sum())} tokens on the GPU")
+    say(f"b32 ({entries}, {index}, {c4_mode}, kv {kv}): prefilled {int(L0.sum())} tokens on the GPU")
     Wc, Wh = synth.gate_weights(wl.seed)
     o = Oracle(wl.n_win, Wc, Wh, B, int(((L0 + steps) // BLOCK).sum()) + B, entry_format=entries,
-               index_format=index, c4_mode=c4_mode)
+               index_format=index, c4_mode=c4_mode, kv_format=kv)
     srcs = [RequestTokens(2, b) for b in range(B)]
     ost = []
     for b in range(B):
@@ -231,15 +276,18 @@ def test_long_context_full_size():
         say(f"long: step {t} ok")
 
     run_steps(cache, states, wl, L0, steps, on_step)
-    assert checked[0] == len(gold["req"])
+    assert checked[0] == len(gold["req"]) == B * steps
     gates = synth.gate_weights(wl.seed)
+    items = []
     for b in range(B):
         table = cache.block_table(states[b])
         nb = len(table)
-        for lb in sorted({0, 1, nb // 2, nb - 2, nb - 1, *rng.integers(0, nb, 3).tolist()}):
-            check_block(cache, table[lb], srcs[b], lb, gates)
+        # the first, second, middle and last blocks and the block sealed by step 8
+        must = {0, 1, nb // 2, nb - 2, nb - 1, int(L0[b]) // BLOCK}
+        items += [(table[lb], b, lb) for lb in sample_blocks(rng, nb, must)]
         check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win)
-    say("long: sampled blocks and rings ok")
+    n = check_blocks(cache, items, 5, gates)
+    say(f"long: {n} sampled blocks (at least 64 per request) and every ring ok")
     cache.close()
 
 
@@ -307,7 +355,7 @@ def test_prefix_sharing_full_size():
             assert cache.refcount(ids.pop()) == len(users)
 
     gold = load_golden("prefix_decode.npz")
-    sampled = sorted(set(gold["req"].tolist()))
+    gold_steps = set(gold["step"].tolist())
     srcs = {b: RequestTokens(3, b) for b in range(B)}
     rng = np.random.default_rng(wl.seed + 7)
     checked = [0]
@@ -316,7 +364,7 @@ def test_prefix_sharing_full_size():
         for b in range(B):
             L = int(L0[b]) + t + 1
             check_info(cache, states[b], L)
-            if b in sampled or t == steps - 1:
+            if t in gold_steps or t == steps - 1:
                 nb = L // BLOCK
                 _, qi = srcs[b].query(L - 1)
                 sample = sorted({0, nb - 1, *rng.integers(0, nb, 3).tolist()})
@@ -326,16 +374,24 @@ def test_prefix_sharing_full_size():
             say(f"prefix: step {t} ok")
 
     run_steps(cache, states, wl, L0, steps, on_step)
-    assert checked[0] == len(gold["req"])
+    assert checked[0] == len(gold["req"]) == B * len(gold_steps)
     gates = (Wc, Wh)
-    for b in sampled:
+    items, seen = [], set()
+    for b in range(B):
         table = cache.block_table(states[b])
         nb = len(table)
-        last_shared = fork[b] // BLOCK - 1
-        for lb in sorted({0, last_shared, nb - 1}):
-            check_block(cache, table[lb], srcs[b], lb, gates)
-        check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win)
-    say("prefix: sampled blocks and rings ok")
+        shared = fork[b] // BLOCK            # blocks [0, shared) are the group's prefix
+        # the first and last blocks, the first and last shared-prefix blocks, the
+        # first block of its own, and the block sealed during the decode steps
+        must = {0, nb - 1, shared - 1, shared, int(L0[b]) // BLOCK}
+        for lb in sample_blocks(rng, nb, must):
+            if table[lb] not in seen:        # a shared block is checked once
+                seen.add(table[lb])
+                items.append((table[lb], b, lb))
+        if b < wl.n_groups:                  # one ring per group
+            check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win)
+    n = check_blocks(cache, items, 3, gates)
+    say(f"prefix: {n} distinct sampled blocks (at least 64 per request) and rings ok")
     cache.close()
 
 
