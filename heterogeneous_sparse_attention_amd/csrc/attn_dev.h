@@ -257,8 +257,9 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
 }
 
 // Attention of one workgroup over two key lists of one request, A = [a0, a1) and
-// B = [b0, b1): each wave streams a contiguous share of each, its A keys first, in
-// one online softmax. The addresses of the B keys are known only after mid(),
+// B = [b0, b1), in one online softmax. The workgroup's keys are the list A then B;
+// wave w takes positions w, w + WAVES, w + 2 WAVES, ... of it, so no wave has more
+// than one key above the average, and every wave's A keys come first. The addresses of the B keys are known only after mid(),
 // work that every wave of the workgroup runs once (it may hold barriers and must
 // issue no global load). The first RING - 1 keys of each wave are A keys where
 // it has them, and their loads are issued before mid(), so they arrive while mid()
@@ -275,13 +276,11 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int pa = (a1 - a0 + WAVES - 1) / WAVES;
-  const int wa0 = a0 + wave * pa;
-  const int na = max(0, min(wa0 + pa, a1) - wa0);
-  const int pb = (b1 - b0 + WAVES - 1) / WAVES;
-  const int wb0 = b0 + wave * pb;
-  const int nbk = max(0, min(wb0 + pb, b1) - wb0);
-  const int n = na + nbk;   // the wave's keys: j < na is A key wa0 + j, else B key wb0 + j - na
+  const int nA = a1 - a0, nt = nA + (b1 - b0);
+  // the wave's keys: j < n at list position wave + WAVES j; the first na are A keys
+  const int n = wave < nt ? (nt - wave + WAVES - 1) / WAVES : 0;
+  const int na = wave < nA ? (nA - wave + WAVES - 1) / WAVES : 0;
+  auto pos = [&](int j) { return wave + WAVES * j; };
 
   uint4 qw[4];
 #pragma unroll
@@ -294,14 +293,14 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
   }
-  auto key_j = [&](int j) { return j < na ? key_a(wa0 + j) : key_b(wb0 + j - na); };
+  auto key_j = [&](int j) { return j < na ? key_a(a0 + pos(j)) : key_b(b0 + pos(j) - nA); };
 
   // group 0: A addresses, then the prefetch of the first RING - 1 keys (every load
   // issued, dummy rows where a slot has no A key)
   const int n0 = min(64, n);
   KeyAddr a;
   a.k = a.v = nullptr;
-  if (lane < n0 && lane < na) a = key_a(wa0 + lane);
+  if (lane < n0 && lane < na) a = key_a(a0 + pos(lane));
   bool okl = a.k != nullptr;
   uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
   uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
@@ -311,7 +310,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane, fp8_a);
   mid();
   if (lane < n0 && lane >= na) {
-    a = key_b(wb0 + lane - na);
+    a = key_b(b0 + pos(lane) - nA);
     okl = a.k != nullptr;
     kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
     vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);

@@ -224,6 +224,8 @@ struct StepArgs {
   int32_t s2_append;     // S1 is not launched: S2 appends the tokens (and part A reads the
                          // newest from the input)
   SelPlan sel;           // top-k workgroups of the four-launch form (long rows are sliced)
+  int32_t a_split[kMaxReq];       // request i's part-A keys [0, a_split[i]) are taken by part-A
+                                  // workgroups, the rest by the three-launch form's mixed ones
   int32_t first_a[kMaxReq + 1];   // request i's part-A partials: [first_a[i], first_a[i+1])
   int32_t first_b[kMaxReq + 1];   // part-B partials: n_a + [first_b[i], first_b[i+1])
   int32_t first_s[kMaxReq + 1];   // request i's first scoring workgroup

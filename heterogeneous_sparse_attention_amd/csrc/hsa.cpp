@@ -72,6 +72,11 @@ struct hsa_ctx {
                               // (one per CU at the step kernels' register use)
   int32_t select_slice = 0;   // top-k: longer score rows are selected in two rounds (0: by k)
   int32_t step_fused = 1;     // decode step in three launches when every row fits the LDS cache
+  // three-launch form: part-A keys a mixed workgroup takes (the rest go to part-A
+  // workgroups in the same launch; negative: all), and the selection's cost in keys
+  // of one workgroup for the balance
+  int32_t mixed_a = 8;
+  int32_t sel_lat = 16;
   int32_t mx_unit = 0;        // MXFP4 keys: blocks per scoring workgroup (0: by batch size)
   // layers: the pools of each (P is the current layer's); an append made at layer 0
   // and not yet repeated on every layer is kept in `seq` for the later layers
@@ -99,6 +104,8 @@ struct hsa_ctx {
     if (const char* e = std::getenv("HSA_ATTEND_WGS")) attend_wgs = std::max(16, std::atoi(e));
     if (const char* e = std::getenv("HSA_STEP_SLOTS")) step_slots = std::max(16, std::min(1 << 16, std::atoi(e)));
     if (const char* e = std::getenv("HSA_STEP_FUSED")) step_fused = std::atoi(e) != 0;
+    if (const char* e = std::getenv("HSA_MIXED_A")) mixed_a = std::atoi(e);
+    if (const char* e = std::getenv("HSA_SEL_LAT")) sel_lat = std::max(0, std::atoi(e));
     if (const char* e = std::getenv("HSA_MX_UNIT")) mx_unit = std::max(1, std::min(kMxUnitMax, std::atoi(e)));
     if (const char* e = std::getenv("HSA_SELECT_SLICE"))   // a multiple of 32, at least 32
       select_slice = std::max(32, std::min(1 << 24, std::atoi(e)) / 32 * 32);
@@ -486,9 +493,32 @@ void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32
   std::vector<int64_t> nab(n);
   for (int i = 0; i < n; ++i) nab[i] = na[i] + nb[i];
   AttnPart pa{&na, 0, 0, {}}, pb{fused ? &nab : &nb, 0, fused ? 1 : 0, {}};
-  if (fused) {
+  for (int i = 0; i < n; ++i) S.a_split[i] = (int32_t)na[i];
+  if (fused && c->mixed_a >= 0) {
+    // Every mixed workgroup (selection, then part B) runs the selection before its
+    // part-B keys are known; it takes mixed_a part-A keys, whose loads are in flight
+    // meanwhile. Part-A workgroups take the other part-A keys and stream them while
+    // the mixed ones select. The balance counts a selection as sel_lat keys.
+    std::vector<int64_t> ka = na, kb = nb;
+    AttnPart pm{&kb, c->sel_lat, 1, {}}, px{&ka, 0, 0, {}};
+    for (int it = 0; it < 2; ++it) {
+      balance_wgs({&pm, &px}, c->step_slots - B.n_seal);
+      for (int i = 0; i < n; ++i) {
+        const int64_t am = px.wgs[i] == 0 ? na[i] : std::min<int64_t>(na[i], (int64_t)c->mixed_a * pm.wgs[i]);
+        ka[i] = na[i] - am;
+        kb[i] = nb[i] + am;
+      }
+    }
+    for (int i = 0; i < n; ++i) {
+      if (ka[i] == 0) px.wgs[i] = 0;
+      S.a_split[i] = (int32_t)ka[i];
+    }
+    pa.wgs = px.wgs;
+    pb.wgs = pm.wgs;
+  } else if (fused) {
     balance_wgs({&pb}, c->step_slots - B.n_seal);
     pa.wgs.assign(n, 0);
+    for (int i = 0; i < n; ++i) S.a_split[i] = 0;
   } else if (a_only) {
     balance_wgs({&pa}, c->step_slots - B.n_seal - (S.s2_append ? n : 0));
     pb.wgs.assign(n, 0);

@@ -200,7 +200,8 @@ __global__ __launch_bounds__(256, FP8 || KV8 ? 3 : 4) void k_step1(Pools P, ReqB
 
 
 // Attention part A (SWA tokens + HCA of blocks sealed before this step) of chunk
-// `bid`: it needs no top-k, so it runs beside the selection.
+// `bid`, over the request's part-A keys [0, a_split): it needs no top-k, so it runs
+// beside the selection.
 template <int WAVES>
 __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const StepArgs& S, int bid,
                                        AttnSharedT<WAVES>& sh) {
@@ -210,7 +211,7 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
   const Req R = B.r[r];
   const int swa = R.len < P.n_win ? R.len : P.n_win;
   int x0, x1;
-  chunk_range(keys_a(P, R), nch, w, x0, x1);
+  chunk_range(S.a_split[r], nch, w, x0, x1);
   const int64_t g0 = (int64_t)R.state * P.n_win;   // the state's first ring slot
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
   const int64_t p0 = (int64_t)R.len - swa;   // oldest SWA position; the ring holds all (S1 wrote the newest)
@@ -273,7 +274,10 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   const int nc = c4_cands(P.c4, P.eager, R);     // candidates
   const int kk = min(S.k, nc);
   int a0, a1, b0, b1;
-  chunk_range(keys_a(P, R), nch, w, a0, a1);
+  const int as = S.a_split[r];   // part-A keys [as, keys_a) are the mixed workgroups'
+  chunk_range(keys_a(P, R) - as, nch, w, a0, a1);
+  a0 += as;
+  a1 += as;
   chunk_range(kk, nch, w, b0, b1);
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
   SelPre<NT> pre;
