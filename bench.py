@@ -68,10 +68,13 @@ def seal_bytes(entries: str, index: str = "f32", kv: str = "bf16") -> int:
 KERNEL_SYMBOL = {"append": "k_decode_append", "score": "k_score", "select": "k_select",
                  "attend": "k_attend", "merge": "k_merge", "seal": "k_seal_merge",
                  "write": "k_bulk_write", "step1": "k_step1", "step2": "k_step2",
-                 "step2b": "k_step2b", "step3": "k_step3", "step4": "k_step4"}
+                 "step2b": "k_step2b", "step3": "k_step3", "step4": "k_step4",
+                 "bulk_seal": "k_bulk_seal"}
 STEP_SOURCES = ["step.hip", "attn_dev.h", "score_dev.h", "seal_dev.h", "device.h"]
 KERNEL_SOURCES = {"step1": STEP_SOURCES, "step2": STEP_SOURCES, "step2b": STEP_SOURCES,
-                  "step3": STEP_SOURCES, "step4": STEP_SOURCES}
+                  "step3": STEP_SOURCES, "step4": STEP_SOURCES,
+                  "bulk_seal": ["append_seal.hip", "seal_dev.h", "device.h"],
+                  "write": ["append_seal.hip", "seal_dev.h", "device.h"]}
 STEP_KERNELS = ("step1", "step2", "step2b", "step3", "step4")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -173,6 +176,35 @@ def layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer, kv="b
     }
     out["step"] = sum(out.values())
     return out
+
+
+def counted_traffic(kernel: str, workload: str, args):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.json (scaled
+    rocprofv3 FETCH_SIZE + WRITE_SIZE), or None when the counters were taken on other
+    sources, formats or launch settings."""
+    try:
+        tr = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = tr.get("kernels", {}).get(workload, {}).get(KERNEL_SYMBOL[kernel])
+    if not ent or ent.get("src_sha") != src_hash(kernel):
+        return None
+    fmt = (getattr(args, "entries", "bf16"), getattr(args, "index", "f32"), getattr(args, "kv", "bf16"))
+    if (ent.get("entries", "bf16"), ent.get("index", "f32"), ent.get("kv", "bf16")) != fmt:
+        return None
+    if ent.get("env", "") != launch_env():
+        return None
+    return ent.get("traffic_bytes_per_launch")
+
+
+# the library's launch-shape settings read from the environment (tuning hooks)
+LAUNCH_KNOBS = ("HSA_ATTEND_WGS", "HSA_STEP_SLOTS", "HSA_STEP_FUSED", "HSA_MX_UNIT", "HSA_SELECT_SLICE",
+                "HSA_MIXED_A", "HSA_SEL_LAT")
+
+
+def launch_env() -> str:
+    """The launch settings set in the environment, as one string."""
+    return " ".join(f"{k}={os.environ[k]}" for k in LAUNCH_KNOBS if k in os.environ)
 
 
 def src_hash(kernel: str) -> str:
@@ -428,15 +460,7 @@ def run_decode(args) -> dict:
     achieved = (bytes_2[dominant] / dom_n) / (dom_ms / dom_n * 1e-3) / 1e9 if dom_n else None
     step_gbs = bytes_1["step"] / (ms_total * 1e-3) / 1e9
 
-    traffic = None
-    try:
-        tr = json.load(open(TRAFFIC_FILE))
-        ent = tr.get(KERNEL_SYMBOL[dominant])
-        if (ent and ent.get("src_sha") == src_hash(dominant) and ent.get("workload") == wl.name
-                and ent.get("entries", "bf16") == args.entries and ent.get("index", "f32") == args.index):
-            traffic = ent.get("traffic_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    traffic = counted_traffic(dominant, wl.name, args) if not layers else None
 
     fp8 = args.entries == "fp8"
     mx4 = args.index == "mxfp4"
@@ -562,7 +586,8 @@ def run_bulk(args) -> dict:
                      "achieved": seal_b / (seal_ms * 1e-3) / 1e9 if seal_ms else None,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": seal_b / (seal_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if seal_ms else None,
-                     "traffic": None, "avg_launch_us": seal_ms * 1e3 if seal_ms else None,
+                     "traffic": counted_traffic("bulk_seal", wl.name, args),
+                     "avg_launch_us": seal_ms * 1e3 if seal_ms else None,
                      "algorithmic_bytes_per_launch": seal_b,
                      "measured": "HIP event pair attached to the k_bulk_seal dispatch of one call"},
         "kernels_us_per_call": {"seal": kt["seal"][0] * 1e3, "write": kt["write"][0] * 1e3},
@@ -810,10 +835,20 @@ def summarize_counters(args):
                 and is_copy(r.get("Kernel_Name", "")) and "copy_counter" in os.path.basename(r["_file"])]
         return sum(vals) / len(vals) if vals else None
     cf, cw = per_copy("FETCH_SIZE"), per_copy("WRITE_SIZE")
-    out = {"copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes}
-    sf = copy_bytes / (cf * 1024) if cf else None
-    sw = copy_bytes / (cw * 1024) if cw else None
-    out["fetch_scale"], out["write_scale"] = sf, sw
+    try:
+        out = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        out = {}
+    if "kernels" not in out:   # an older single-workload file
+        out = {}
+    cal = out.get("calibration", {})
+    if cf and cw:   # this set of runs has its own calibration
+        cal = {"copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": copy_bytes,
+               "fetch_scale": copy_bytes / (cf * 1024), "write_scale": copy_bytes / (cw * 1024)}
+    out["calibration"] = cal
+    sf, sw = cal.get("fetch_scale"), cal.get("write_scale")
+    wl_out = out.setdefault("kernels", {})
+    wl_out[args.counters_workload] = {}
     for name, sym in KERNEL_SYMBOL.items():
         # the symbol, possibly with template arguments (k_step1<false>(...))
         hit = lambda n, s=sym: (s + "(") in n or (s + "<") in n
@@ -822,10 +857,10 @@ def summarize_counters(args):
         if not nf:
             continue
         ent = {"fetch_kib": f, "write_kib": w, "dispatches": nf, "src_sha": src_hash(name),
-               "workload": args.counters_workload}
+               "entries": "bf16", "index": "f32", "kv": "bf16", "env": launch_env()}
         if sf and sw and f is not None and w is not None:
             ent["traffic_bytes_per_launch"] = f * 1024 * sf + w * 1024 * sw
-        out[sym] = ent
+        wl_out[args.counters_workload][sym] = ent
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))

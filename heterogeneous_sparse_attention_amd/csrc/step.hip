@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256, FP8 || KV8 ? 3 : 4) void k_step1(Pools P, ReqB
 // Attention part A (SWA tokens + HCA of blocks sealed before this step) of chunk
 // `bid`, over the request's part-A keys [0, a_split): it needs no top-k, so it runs
 // beside the selection.
-template <int WAVES>
+template <int WAVES, int RING = ring_depth<WAVES>()>
 __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const StepArgs& S, int bid,
                                        AttnSharedT<WAVES>& sh) {
   const int r = owner_of(S.first_a, B.n, bid);
@@ -238,9 +238,17 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
   };
   const C4Addr dm = dummy_rows(P, R.state);
   float M, L, A8[8];
-  attend_keys<WAVES>(key_a, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8, 0x7fffffff, P.kv8 != 0);
+  attend_keys<WAVES, RING>(key_a, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8, 0x7fffffff,
+                           P.kv8 != 0);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
 }
+
+// Ring of the three-launch form's part-A workgroups, which stream while the mixed
+// workgroups select.
+#ifndef HSA_SPLIT_A_RING
+#define HSA_SPLIT_A_RING 4
+#endif
+constexpr int kSplitARing = HSA_SPLIT_A_RING;
 
 constexpr int kStep2Threads = 512;   // 8 waves: 256 VGPRs per wave for the attention role
 constexpr int kStep2Waves = kStep2Threads / 64;
@@ -363,7 +371,10 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
     return;
   }
   bid -= B.n_seal;
-  part_a<kStep2Waves>(P, B, S, bid, sh.attn);
+  if (S.fused)
+    part_a<kStep2Waves, kSplitARing>(P, B, S, bid, sh.attn);
+  else
+    part_a<kStep2Waves>(P, B, S, bid, sh.attn);
 }
 
 // Round 2 of the top-k of rows sliced in k_step2 (launched only when some are).
