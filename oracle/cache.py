@@ -326,27 +326,47 @@ def attention(q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray) -> np.ndarray:
 def block_range_summary(args):
     """HCA entries and C4 scores of the sealed blocks b0 .. b1-1 of one request.
 
-    args = (seq, gate_hca, q_idx_list, b0, b1); seq(pos) returns the request's
-    (K [n][H][D], V [n][H][D], kI [n][4][64]) at token positions pos. Block b holds
-    tokens 128b .. 128b+127 ([Q&A] §2.2): its HCA entry pools all 128 (reading R1)
-    and its 32 C4 scores follow reading R4, once per indexer query.
+    args = (seq, gate_hca, q_idx_list, b0, b1[, kv_format]); seq(pos) returns the
+    request's (K [n][H][D], V [n][H][D], kI [n][4][64]) at token positions pos, as
+    the State stores them. Block b holds tokens 128b .. 128b+127 ([Q&A] §2.2): its
+    HCA entry pools all 128 (reading R1), stored as bf16 or (kv_format "fp8",
+    reading R20) as per-head E4M3, and its 32 C4 scores follow reading R4, once per
+    indexer query.
     Returns (hca_k [n][H][D], hca_v, scores [len(q_idx_list)][32 n]).
     """
-    seq, gate_hca, qis, b0, b1 = args
+    seq, gate_hca, qis, b0, b1 = args[:5]
+    kv_format = args[5] if len(args) > 5 else "bf16"
     n = b1 - b0
     K, V, KI = seq(np.arange(BLOCK * b0, BLOCK * b1, dtype=np.int64))
-    hk = np.empty((n, N_HEADS, HEAD_DIM), np.float32)
+    hk = np.empty((n, N_HEADS, HEAD_DIM), np.float64)
     hv = np.empty_like(hk)
     sc = np.empty((len(qis), C4_PER_BLOCK * n), np.float64)
     for i in range(n):
         g = slice(BLOCK * i, BLOCK * (i + 1))
-        hk[i], hv[i] = gated_pool(K[g], V[g], gate_hca)
+        if kv_format == "fp8":                        # reading R20: the pooled entry's storage
+            Kh, Vh = gated_pool(K[g], V[g], gate_hca, rounded=False)
+            hk[i], hv[i] = quantize_e4m3_rows(Kh)[2], quantize_e4m3_rows(Vh)[2]
+        else:
+            hk[i], hv[i] = gated_pool(K[g], V[g], gate_hca)
         for c, qi in enumerate(qis):
             sc[c, C4_PER_BLOCK * i:C4_PER_BLOCK * (i + 1)] = c4_scores(KI[g], qi)
     return hk, hv, sc
 
 
-def decode_reference(seq, n_win: int, gate_csa, gate_hca, cases, pmap=map, chunk: int = 32):
+class StoredTokens:
+    """A token source whose K and V are what FP8 KV storage holds (reading R20): each
+    token's per-head E4M3 codes times their scale, as float64. Picklable."""
+
+    def __init__(self, seq):
+        self.seq = seq
+
+    def __call__(self, pos):
+        K, V, KI = self.seq(pos)
+        return quantize_e4m3_rows(K)[2], quantize_e4m3_rows(V)[2], KI
+
+
+def decode_reference(seq, n_win: int, gate_csa, gate_hca, cases, pmap=map, chunk: int = 32,
+                     kv_format: str = "bf16"):
     """Decode outputs of one request at several lengths, without holding its cache.
 
     The same arithmetic as driving Oracle token by token, streamed block by block
@@ -358,17 +378,23 @@ def decode_reference(seq, n_win: int, gate_csa, gate_hca, cases, pmap=map, chunk
     selected C4 entries in ascending ordinal order ([Q&A] §4; R5, R6, R12).
     seq(pos) gives the request's tokens (see block_range_summary); pmap maps
     block_range_summary over block ranges (a process pool's map works).
+    With kv_format "fp8" (reading R20) every token is taken as the State stores it
+    (StoredTokens): the SWA, the tokens the C4 entries pool and the HCA entries.
     Returns [(idx int32 [k], scores float64 [k], out float64 [H][D])] per case.
     """
+    if kv_format not in ("bf16", "fp8"):
+        raise OracleError("invalid", f"kv_format {kv_format!r}")
+    if kv_format == "fp8":
+        seq = StoredTokens(seq)
     W_csa = np.asarray(gate_csa, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
     W_hca = np.asarray(gate_hca, dtype=np.float64).reshape(N_HEADS, HEAD_DIM)
     qis = [np.asarray(c[2], dtype=np.float64) for c in cases]
     nb_max = max(int(c[0]) // BLOCK for c in cases)
-    ranges = [(seq, W_hca, qis, b, min(b + chunk, nb_max)) for b in range(0, nb_max, chunk)]
-    hk = np.empty((nb_max, N_HEADS, HEAD_DIM), np.float32)
+    ranges = [(seq, W_hca, qis, b, min(b + chunk, nb_max), kv_format) for b in range(0, nb_max, chunk)]
+    hk = np.empty((nb_max, N_HEADS, HEAD_DIM), np.float64)
     hv = np.empty_like(hk)
     sc = np.empty((len(cases), C4_PER_BLOCK * nb_max), np.float64)
-    for (_, _, _, b0, b1), (k_, v_, s_) in zip(ranges, pmap(block_range_summary, ranges)):
+    for (_, _, _, b0, b1, _), (k_, v_, s_) in zip(ranges, pmap(block_range_summary, ranges)):
         hk[b0:b1], hv[b0:b1], sc[:, C4_PER_BLOCK * b0:C4_PER_BLOCK * b1] = k_, v_, s_
     res = []
     for c, (L, q, _, k) in enumerate(cases):

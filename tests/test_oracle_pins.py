@@ -439,18 +439,21 @@ def test_errors_leave_state_unchanged():
 
 # ------------------------------------------------------------------ streamed reference
 
-@pytest.mark.parametrize("n_win,k", [(128, 20), (256, 4096)])
-def test_streamed_reference_matches_token_by_token(n_win, k):
+@pytest.mark.parametrize("n_win,k,kv", [(128, 20, "bf16"), (256, 4096, "bf16"), (128, 20, "fp8"),
+                                        (256, 4096, "fp8")])
+def test_streamed_reference_matches_token_by_token(n_win, k, kv):
     """decode_reference (one request streamed block by block, used for the large
     workloads) computes what the cache driven token by token computes: same top-k
-    rows, same selected scores, and the same attention output up to summation order."""
+    rows, same selected scores, and the same attention output up to summation order.
+    Also with FP8 KV storage (reading R20), where the window, the pooled tokens and
+    the HCA entries are the stored values."""
     from oracle import decode_reference
     from synth.workloads import RequestTokens, make
 
     src = RequestTokens(2, 5)
     wl = make(2)
     Wc, Wh = synth.gate_weights(wl.seed)
-    o = Oracle(n_win, Wc, Wh, 2, 64)
+    o = Oracle(n_win, Wc, Wh, 2, 64, kv_format=kv)
     s = o.state_alloc()
     L_cases = [5, 127, 128, 300, 640, 777]
     cases, expect = [], []
@@ -463,7 +466,10 @@ def test_streamed_reference_matches_token_by_token(n_win, k):
         idx, val = o.topk(s, qi, k)
         expect.append((idx, val, o.attend(s, q, idx, k)))
         cases.append((Lc, q, qi, k))
-    got = decode_reference(src, n_win, Wc, Wh, cases, chunk=2)
+    got = decode_reference(src, n_win, Wc, Wh, cases, chunk=2, kv_format=kv)
+    if kv == "fp8":   # the storage changes the output: the two formats must differ
+        ref = decode_reference(src, n_win, Wc, Wh, cases[-1:], chunk=2)
+        assert not np.allclose(ref[0][2], got[-1][2], rtol=1e-6, atol=0)
     for (i0, v0, o0), (i1, v1, o1) in zip(expect, got):
         np.testing.assert_array_equal(i0, i1)
         np.testing.assert_array_equal(v0, v1)
