@@ -334,6 +334,40 @@ def decode_inputs(wl, L0: np.ndarray, n_steps: int, seed=None):
     return {n_: x.view(n_steps, B, *x.shape[1:]) for n_, x in t.items()}
 
 
+def measured_roof(gib: int = 1, reps: int = 5) -> dict:
+    """The HBM bandwidth two plain runtime kernels reach on this GPU, beside the
+    vendor's 8 TB/s: a device-to-device copy of `gib` GiB (read + write counted) and
+    a sum over `gib` GiB (a read). Median of `reps` runs each, fresh buffers larger
+    than the 256 MB last-level cache."""
+    import torch
+    n = (gib << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def median_ms(fn):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+    b.copy_(a)                                   # warm up both kernels
+    a.sum()
+    copy_ms = median_ms(lambda: b.copy_(a))
+    read_ms = median_ms(lambda: a.sum())
+    nbytes = n * 4
+    out = {"copy_gbps": 2 * nbytes / (copy_ms * 1e-3) / 1e9, "read_gbps": nbytes / (read_ms * 1e-3) / 1e9,
+           "what": f"torch copy_ of {gib} GiB (read + write) and torch sum over {gib} GiB (read), "
+                   f"median of {reps} each"}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def gpu_lead(cycles: int = 500_000):
     """Keep the GPU busy for about 0.2 ms (a spin kernel) so that the host queues the
     first timed steps before the start event fires: the timed region then holds the
@@ -504,6 +538,7 @@ def run_decode(args) -> dict:
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": (achieved / PEAK_HBM_GBS) if achieved else None,
                      "traffic": traffic,
+                     "traffic_gbps": (traffic / (dom_ms / dom_n * 1e-3) / 1e9) if (traffic and dom_n) else None,
                      "avg_launch_us": (dom_ms / dom_n * 1e3) if dom_n else None,
                      "algorithmic_bytes_per_launch": (bytes_2[dominant] / dom_n) if dom_n else None,
                      "measured": f"HIP event pair attached to each {KERNEL_SYMBOL[dominant]} "
@@ -923,6 +958,7 @@ def main():
     if not args.no_cpu_baseline and args.workload == 2 and args.entries == "bf16" \
             and args.index == "f32" and not args.layers and args.c4_mode == "sealed" and args.kv == "bf16":
         res["cpu_baseline"] = cpu_baseline(args)
+    res["measured_roof"] = measured_roof()
     print(json.dumps(res), flush=True)
 
 
