@@ -487,9 +487,10 @@ void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32
   S.s2_append = a_only && B.n_seal == 0 && !c->P.kv8 ? 1 : 0;
   S.n_score = (int32_t)n_score;
   if (!fused && !a_only) plan_select_host(c, B, k, S.sel);
-  // workgroups: three-launch form, each S2 workgroup takes a share of both parts
-  // of one request (at least one per request: it writes the top-k padding);
-  // four-launch form, part A shares S2 with the selections, part B has S3
+  // workgroups: three-launch form, S2 holds mixed workgroups (at least one per
+  // request: the first writes the top-k padding), each with a share of part B and
+  // of part A, and part-A workgroups beside them; four-launch form, part A shares
+  // S2 with the selections, part B has S3
   std::vector<int64_t> nab(n);
   for (int i = 0; i < n; ++i) nab[i] = na[i] + nb[i];
   AttnPart pa{&na, 0, 0, {}}, pb{fused ? &nab : &nb, 0, fused ? 1 : 0, {}};
