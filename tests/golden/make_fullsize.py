@@ -1,11 +1,13 @@
 """Expected decode outputs of the two largest workloads, computed by the oracle
 alone (oracle.decode_reference) from the seeded inputs: every request of the long
-workload at every decode step, and every request of the prefix workload at four
-steps (the first, two inside and the last).
+workload at every decode step, every request of the prefix workload at four
+steps (the first, two inside and the last), and every request of the prefix
+workload with FP8 KV storage (reading R20) at the first and the last step.
 
-    python tests/golden/make_fullsize.py [--procs 8] [--only prefix|long]
+    python tests/golden/make_fullsize.py [--procs 8] [--only prefix|long|prefix_fp8kv]
 
-writes tests/golden/prefix_decode.npz and tests/golden/long_decode.npz:
+writes tests/golden/prefix_decode.npz, tests/golden/long_decode.npz and
+tests/golden/prefix_decode_fp8kv.npz:
   req [n], step [n], L [n]   request, decode step (0-based), length after the append
   idx [n][k] int32           top-k ordinals (ascending, -1 padded)
   out [n][16][128] float32   attention output (computed in float64)
@@ -31,15 +33,16 @@ import synth  # noqa: E402
 from oracle import decode_reference  # noqa: E402
 from synth.workloads import RequestTokens, make  # noqa: E402
 
-# (workload index, file, requests (None: all), decode steps)
+# (workload index, file, requests (None: all), decode steps, KV storage)
 SAMPLES = {
-    "prefix": (3, "prefix_decode.npz", None, (0, 10, 21, 31)),
-    "long": (5, "long_decode.npz", None, tuple(range(16))),
+    "prefix": (3, "prefix_decode.npz", None, (0, 10, 21, 31), "bf16"),
+    "long": (5, "long_decode.npz", None, tuple(range(16)), "bf16"),
+    "prefix_fp8kv": (3, "prefix_decode_fp8kv.npz", None, (0, 31), "fp8"),
 }
 
 
 def run(name: str, procs: int) -> None:
-    index, fname, reqs, steps = SAMPLES[name]
+    index, fname, reqs, steps, kv = SAMPLES[name]
     wl = make(index)
     if reqs is None:
         reqs = list(range(wl.batch))
@@ -54,7 +57,7 @@ def run(name: str, procs: int) -> None:
                 p = int(wl.prefill[b]) + t          # position of the step's new token
                 q, qi = src.query(p)
                 cases.append((p + 1, q, qi, wl.topk))
-            res = decode_reference(src, wl.n_win, Wc, Wh, cases, pmap=pool.map, chunk=16)
+            res = decode_reference(src, wl.n_win, Wc, Wh, cases, pmap=pool.map, chunk=16, kv_format=kv)
             for t, (L, *_), (idx, _, out) in zip(steps, cases, res):
                 rows["req"].append(b)
                 rows["step"].append(t)

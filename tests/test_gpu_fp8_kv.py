@@ -19,8 +19,9 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import Oracle, e4m3_decode
-from tests.gpu_util import bf16_to_f64, dev_queries, dev_tokens, host_queries, host_tokens, rel_l2
+from oracle import Oracle
+from tests.gpu_util import (bf16_to_f64, check_fp8, dev_queries, dev_tokens, host_queries, host_tokens,
+                            pool_magnitude, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,30 +61,6 @@ def check_ring(cache, o, sg, so):
         assert np.array_equal(ex["idx_tail"][p % 128], ki)
 
 
-GRID = e4m3_decode(np.arange(0x7F))
-
-
-def check_fp8(codes, scale, ref_codes, ref_scale, x, what):
-    """FP8 storage of an entry pooled on the GPU in float32 and by the oracle in
-    float64 (x: the oracle's unquantised entry [..][128]). The scales agree to 1e-6.
-    A code is an integer decided from the pooled value, and the two poolings differ
-    in their last bits, so a code may differ from the oracle's only where the
-    oracle's scaled value x / s lies within 1e-4 (relative) of the midpoint between
-    the two codes' values. There either rounding is correct."""
-    assert np.allclose(scale, ref_scale, rtol=1e-6, atol=0), what
-    diff = codes != ref_codes
-    assert np.mean(diff) < 0.005, (what, np.mean(diff))
-    if not diff.any():
-        return
-    y = (x / ref_scale[..., None].astype(np.float64))[diff]
-    a, b = e4m3_decode(codes[diff]), e4m3_decode(ref_codes[diff])
-    assert np.all((codes[diff] & 0x80) == (ref_codes[diff] & 0x80)), what   # same sign
-    steps = np.abs(np.searchsorted(GRID, np.abs(a)) - np.searchsorted(GRID, np.abs(b)))
-    assert np.all(steps == 1), (what, "codes more than one step apart")
-    mid = (a + b) / 2
-    assert np.all(np.abs(y - mid) <= 1e-4 * np.maximum(np.abs(y), 2.0 ** -9)), (what, y, a, b)
-
-
 def check_block(cache, o, bg, bo, entries, toks):
     """A sealed block against the oracle; toks: its 128 raw tokens (K, V), from
     which the oracle's unquantised entries are recomputed for the code check."""
@@ -94,14 +71,17 @@ def check_block(cache, o, bg, bo, entries, toks):
     Kq = quantize_e4m3_rows(toks[0])[2]
     Vq = quantize_e4m3_rows(toks[1])[2]
     hk, hv = gated_pool(Kq, Vq, o.W_hca, rounded=False)
-    for n, x in (("k", hk), ("v", hv)):
+    mags = pool_magnitude(Kq, Vq, o.W_hca)
+    for i, (n, x) in enumerate((("k", hk), ("v", hv))):
         check_fp8(g[f"hca_{n}_codes"], g[f"hca_{n}_scale"], getattr(r, f"hca_{n}_codes"),
-                  getattr(r, f"hca_{n}_scale"), x, ("hca", n, bo))
+                  getattr(r, f"hca_{n}_scale"), x, ("hca", n, bo), mags[i])
     if entries == "fp8":
         c4 = [gated_pool(Kq[4 * j:4 * j + 4], Vq[4 * j:4 * j + 4], o.W_csa, rounded=False) for j in range(32)]
+        c4m = [pool_magnitude(Kq[4 * j:4 * j + 4], Vq[4 * j:4 * j + 4], o.W_csa) for j in range(32)]
         for i, n in enumerate(("k", "v")):
             check_fp8(g[f"csa_{n}_codes"], g[f"csa_{n}_scale"], getattr(r, f"csa_{n}_codes"),
-                      getattr(r, f"csa_{n}_scale"), np.stack([e[i] for e in c4]), ("c4", n, bo))
+                      getattr(r, f"csa_{n}_scale"), np.stack([e[i] for e in c4]), ("c4", n, bo),
+                      np.stack([m[i] for m in c4m]))
     else:
         for n in ("k", "v"):
             val = bf16_to_f64(g[f"csa_{n}"])

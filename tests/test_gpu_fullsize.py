@@ -14,6 +14,11 @@ times (one hsa_decode_step per step over the whole batch, default launch shapes)
   blocks per request against the oracle's compressor. The sampled blocks always
   include the first and the last, the block sealed during the decode steps, and
   the first and last shared-prefix blocks.
+- prefix again with FP8 KV storage (reading R20: every ring token and HCA entry
+  as per-head E4M3 codes and scales; the SWA alone is 2 GiB of codes per step):
+  every request's top-k row and output at steps 0 and 31 against
+  tests/golden/prefix_decode_fp8kv.npz, ring codes and scales bit for bit, and the
+  sampled blocks' HCA codes by the FP8 rule of tests/gpu_util.py (check_fp8).
 - bulk (8 x 131072 tokens in one append): state, tables, sampled blocks, rings.
 """
 
@@ -25,7 +30,7 @@ import pytest
 import synth
 from oracle import BLOCK, C4_PER_BLOCK, M_CSA, Oracle, gated_pool, token_scores
 from synth.workloads import RequestTokens, make
-from tests.gpu_util import bf16_to_f64, dev_rows, rel_l2
+from tests.gpu_util import bf16_to_f64, check_fp8, dev_rows, pool_magnitude, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -86,20 +91,34 @@ def check_selection(src, idx, val, nb, k, q_idx, sample_blocks):
                 assert j > tie_max, (j, tie_max)
 
 
-def expected_block(index, b, lb, gates):
+def expected_block(index, b, lb, gates, kv="bf16"):
     """The oracle's entries of sealed block lb of request b of a workload: bf16-rounded
-    C4 and HCA entries (float32) and the block's indexer keys."""
+    C4 and HCA entries (float32) and the block's indexer keys. With FP8 KV (reading
+    R20) the tokens are their stored values, and the HCA entry is given as the
+    unquantised pooled value (hca_k_x, hca_v_x) with its E4M3 codes and scales."""
+    from oracle import quantize_e4m3_rows
     Wc, Wh = gates
     K, V, KI = RequestTokens(index, b)(np.arange(BLOCK * lb, BLOCK * (lb + 1)))
-    K = K.astype(np.float64)
-    V = V.astype(np.float64)
+    if kv == "fp8":
+        K, V = quantize_e4m3_rows(K)[2], quantize_e4m3_rows(V)[2]
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
     ck = np.empty((C4_PER_BLOCK, 16, 128), np.float32)
     cv = np.empty_like(ck)
     for j in range(C4_PER_BLOCK):
         ck[j], cv[j] = gated_pool(K[M_CSA * j:M_CSA * (j + 1)], V[M_CSA * j:M_CSA * (j + 1)], Wc)
+    ref = {"csa_k": ck, "csa_v": cv, "idx": KI}
+    if kv == "fp8":
+        hk, hv = gated_pool(K, V, Wh, rounded=False)
+        mags = pool_magnitude(K, V, Wh)
+        for n, x, m in (("k", hk, mags[0]), ("v", hv, mags[1])):
+            codes, scale, _ = quantize_e4m3_rows(x)
+            ref[f"hca_{n}_x"], ref[f"hca_{n}_codes"], ref[f"hca_{n}_scale"] = x, codes, scale
+            ref[f"hca_{n}_mag"] = m
+        return ref
     hk, hv = gated_pool(K, V, Wh)
-    return {"csa_k": ck, "csa_v": cv, "hca_k": hk.astype(np.float32), "hca_v": hv.astype(np.float32),
-            "idx": KI}
+    ref["hca_k"], ref["hca_v"] = hk.astype(np.float32), hv.astype(np.float32)
+    return ref
 
 
 def _expected_block_job(job):
@@ -107,7 +126,11 @@ def _expected_block_job(job):
 
 
 def compare_block(g, ref, where):
-    for name in ("csa_k", "csa_v", "hca_k", "hca_v"):
+    if "hca_k_x" in ref:   # FP8 KV: the HCA codes by the FP8 rule
+        for n in ("k", "v"):
+            check_fp8(g[f"hca_{n}_codes"], g[f"hca_{n}_scale"], ref[f"hca_{n}_codes"], ref[f"hca_{n}_scale"],
+                      ref[f"hca_{n}_x"], ("hca", n, where), ref[f"hca_{n}_mag"])
+    for name in ("csa_k", "csa_v") if "hca_k_x" in ref else ("csa_k", "csa_v", "hca_k", "hca_v"):
         val = bf16_to_f64(g[name])
         r = ref[name].astype(np.float64)
         assert rel_l2(val, r) <= TOL, (name, where, rel_l2(val, r))
@@ -120,13 +143,13 @@ def check_block(cache, block_id, src, lb, gates):
     compare_block(cache.export_block(block_id), expected_block(src.index, src.b, lb, gates), (src.b, lb))
 
 
-def check_blocks(cache, items, index, gates, workers=None):
+def check_blocks(cache, items, index, gates, workers=None, kv="bf16"):
     """Check many sealed blocks: items = [(physical id, request, logical block)], each
     physical id once. The oracle's entries come from worker processes (spawned: they
     never touch the GPU), the device's from hsa_export_block."""
     import multiprocessing as mp
     workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
-    jobs = [(index, b, lb, gates) for _, b, lb in items]
+    jobs = [(index, b, lb, gates, kv) for _, b, lb in items]
     with mp.get_context("spawn").Pool(workers) as pool:
         for (bid, b, lb), ref in zip(items, pool.imap(_expected_block_job, jobs, chunksize=4)):
             compare_block(cache.export_block(bid), ref, (b, lb))
@@ -145,12 +168,19 @@ def sample_blocks(rng, nb, must, n=64):
     return sorted(picks)
 
 
-def check_ring(cache, state, src, L, n_win):
+def check_ring(cache, state, src, L, n_win, kv="bf16"):
     ex = cache.export_state(state)
     p = np.arange(max(0, L - n_win), L)
     K, V, KI = src(p)
-    assert np.array_equal(bf16_to_f64(ex["swa_k"][p % n_win]), K)
-    assert np.array_equal(bf16_to_f64(ex["swa_v"][p % n_win]), V)
+    if kv == "fp8":   # reading R20: each token's per-head codes and scales, bit for bit
+        from oracle import quantize_e4m3_rows
+        for n, x in (("k", K), ("v", V)):
+            codes, scale, _ = quantize_e4m3_rows(x)
+            assert np.array_equal(ex[f"swa_{n}_codes"][p % n_win], codes)
+            assert np.array_equal(ex[f"swa_{n}_scale"][p % n_win], scale)
+    else:
+        assert np.array_equal(bf16_to_f64(ex["swa_k"][p % n_win]), K)
+        assert np.array_equal(bf16_to_f64(ex["swa_v"][p % n_win]), V)
     t = np.arange(L - L % BLOCK, L)
     assert np.array_equal(ex["idx_tail"][t % BLOCK], KI[len(p) - len(t):])
 
@@ -293,7 +323,8 @@ def test_long_context_full_size():
 
 # ------------------------------------------------------------------ prefix
 
-def test_prefix_sharing_full_size():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefix_sharing_full_size(kv):
     import torch
 
     from heterogeneous_sparse_attention_amd import Cache
@@ -303,7 +334,7 @@ def test_prefix_sharing_full_size():
     Wc, Wh = synth.gate_weights(wl.seed)
     max_len = wl.max_len()
     cache = Cache(wl.n_win, B + wl.n_groups, wl.max_blocks_total() + 64, Wc, Wh,
-                  max_blocks_per_state=max_len // BLOCK + 2)
+                  max_blocks_per_state=max_len // BLOCK + 2, kv_format=kv)
     states = [None] * B
     fork = {b: wl.fork_len(b) for b in range(B)}
 
@@ -340,7 +371,7 @@ def test_prefix_sharing_full_size():
         cache.state_free(parent)
     append(states, list(range(B)), [fork[b] for b in range(B)], [int(L0[b]) for b in range(B)])
     torch.cuda.synchronize()
-    say("prefix: forks and prefills done")
+    say(f"prefix (kv {kv}): forks and prefills done")
 
     # shared blocks: one physical copy per group, refcount = number of sharers
     for g in range(wl.n_groups):
@@ -354,7 +385,7 @@ def test_prefix_sharing_full_size():
             assert len(ids) == 1, (g, lb, ids)
             assert cache.refcount(ids.pop()) == len(users)
 
-    gold = load_golden("prefix_decode.npz")
+    gold = load_golden("prefix_decode.npz" if kv == "bf16" else "prefix_decode_fp8kv.npz")
     gold_steps = set(gold["step"].tolist())
     srcs = {b: RequestTokens(3, b) for b in range(B)}
     rng = np.random.default_rng(wl.seed + 7)
@@ -371,7 +402,7 @@ def test_prefix_sharing_full_size():
                 check_selection(srcs[b], topk[b], sc[b], nb, k, qi, sample)
             checked[0] += check_golden_rows(gold, b, t, topk[b], out[b])
         if t % 8 == 7:
-            say(f"prefix: step {t} ok")
+            say(f"prefix (kv {kv}): step {t} ok")
 
     run_steps(cache, states, wl, L0, steps, on_step)
     assert checked[0] == len(gold["req"]) == B * len(gold_steps)
@@ -389,9 +420,9 @@ def test_prefix_sharing_full_size():
                 seen.add(table[lb])
                 items.append((table[lb], b, lb))
         if b < wl.n_groups:                  # one ring per group
-            check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win)
-    n = check_blocks(cache, items, 3, gates)
-    say(f"prefix: {n} distinct sampled blocks (at least 64 per request) and rings ok")
+            check_ring(cache, states[b], srcs[b], int(L0[b]) + steps, wl.n_win, kv)
+    n = check_blocks(cache, items, 3, gates, kv=kv)
+    say(f"prefix (kv {kv}): {n} distinct sampled blocks (at least 64 per request) and rings ok")
     cache.close()
 
 
