@@ -335,11 +335,12 @@ def decode_inputs(wl, L0: np.ndarray, n_steps: int, seed=None):
 
 
 def measured_roof(gib: int = 1, reps: int = 5) -> dict:
-    """The HBM bandwidth two plain runtime kernels reach on this GPU, beside the
-    vendor's 8 TB/s: a device-to-device copy of `gib` GiB (read + write counted) and
-    a sum over `gib` GiB (a read). Median of `reps` runs each, fresh buffers larger
-    than the 256 MB last-level cache."""
+    """The HBM bandwidth plain kernels reach on this GPU, beside the vendor's 8 TB/s:
+    the harness's streaming read of `gib` GiB (synth/libhsa_synth.so), the runtime's
+    device copy of `gib` GiB (read + write counted) and torch's sum over `gib` GiB.
+    Median of `reps` runs each, on buffers larger than the 256 MB last-level cache."""
     import torch
+    from synth.device import roof_read
     n = (gib << 30) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -355,15 +356,21 @@ def measured_roof(gib: int = 1, reps: int = 5) -> dict:
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
-    b.copy_(a)                                   # warm up both kernels
+    blocks = 2048
+    fold = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    b.copy_(a)                                   # warm up the kernels
     a.sum()
+    roof_read(a, fold, blocks)
+    stream_ms = median_ms(lambda: (roof_read(a, fold, blocks), roof_read(b, fold, blocks)))
     copy_ms = median_ms(lambda: b.copy_(a))
     read_ms = median_ms(lambda: a.sum())
     nbytes = n * 4
-    out = {"copy_gbps": 2 * nbytes / (copy_ms * 1e-3) / 1e9, "read_gbps": nbytes / (read_ms * 1e-3) / 1e9,
-           "what": f"torch copy_ of {gib} GiB (read + write) and torch sum over {gib} GiB (read), "
-                   f"median of {reps} each"}
-    del a, b
+    out = {"stream_read_gbps": 2 * nbytes / (stream_ms * 1e-3) / 1e9,
+           "copy_gbps": 2 * nbytes / (copy_ms * 1e-3) / 1e9, "sum_gbps": nbytes / (read_ms * 1e-3) / 1e9,
+           "what": f"streaming read (a contiguous chunk per workgroup, 16-byte non-temporal loads, 8 in "
+                   f"flight per thread, {blocks} x 256 threads) of two {gib} GiB buffers in turn; torch copy_ of {gib} GiB (read + write); "
+                   f"torch sum over {gib} GiB; median of {reps} each"}
+    del a, b, fold
     torch.cuda.empty_cache()
     return out
 

@@ -1,6 +1,6 @@
 /*
- * hsa_synth.h - seeded synthetic inputs on the GPU (test and benchmark harness;
- * not part of the cache). The same counter generator as the Python module
+ * hsa_synth.h - seeded synthetic inputs on the GPU, and the benchmark's read roof
+ * (test and benchmark harness; not part of the cache). The same counter generator as the Python module
  * `synth`, so either side can regenerate any token at random access:
  *
  *   ctr = stream << 56 | key << 32 | (i >> 1)
@@ -28,6 +28,13 @@ extern "C" {
 int32_t hsa_synth_rows(uint64_t seed, uint32_t stream_id, const uint32_t* keys, uint32_t key,
                        const int64_t* pos, int64_t pos0, int64_t n_rows, int32_t row_len,
                        int32_t as_bf16, void* out, void* stream);
+
+/* Benchmark roof: read `bytes` (a multiple of 16) at device pointer buf with a
+ * streaming read kernel of `blocks` workgroups of 256 threads, each reading one
+ * contiguous chunk and folding it (out: device, `blocks` uint32, written only for a
+ * marker fold value). Enqueued on `stream`. Returns 0, -1 on a bad argument, -5 on
+ * a HIP error. */
+int32_t hsa_roof_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks, void* stream);
 
 #ifdef __cplusplus
 }

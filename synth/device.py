@@ -1,4 +1,5 @@
-"""GPU side of the synthetic-input generator (binding of synth/libhsa_synth.so).
+"""GPU side of the synthetic-input generator (binding of synth/libhsa_synth.so), and
+the benchmark's streaming-read roof.
 
 Produces on the device exactly what `synth.tokens_bf16` / `synth.tokens_f32`
 produce on the host."""
@@ -24,8 +25,23 @@ def load():
         lib.hsa_synth_rows.argtypes = [ctypes.c_uint64, ctypes.c_uint32, P, ctypes.c_uint32, P,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                        P, P]
+        lib.hsa_roof_read.restype = ctypes.c_int32
+        lib.hsa_roof_read.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, P]
         _lib = lib
     return _lib
+
+
+def roof_read(buf, out, blocks: int):
+    """Enqueue the streaming read of the whole contiguous device tensor buf on the
+    current stream; out: a device tensor of at least `blocks` int32 (the folds)."""
+    import torch
+    lib = load()
+    assert buf.is_cuda and buf.is_contiguous() and out.is_cuda and out.numel() >= blocks
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    r = lib.hsa_roof_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                          ctypes.c_void_p(out.data_ptr()), blocks, st)
+    if r != 0:
+        raise RuntimeError(f"hsa_roof_read failed ({r})")
 
 
 def fill_rows(out, seed: int, stream_id: int, *, key: int = 0, keys=None, pos0: int = 0, pos=None):

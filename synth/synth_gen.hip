@@ -1,5 +1,6 @@
-// synth_gen.hip - the counter generator of the Python module `synth`, on the GPU.
-// Harness only: fills benchmark / test inputs; holds no arithmetic of the cache.
+// synth_gen.hip - the counter generator of the Python module `synth`, on the GPU, and
+// the benchmark's streaming-read roof. Harness only: fills benchmark / test inputs and
+// measures the GPU; holds no arithmetic of the cache.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,7 +49,41 @@ __global__ void k_synth(uint64_t seed, uint32_t stream_id, const uint32_t* keys,
   }
 }
 
+// Streaming read of n16 16-byte words (bandwidth roof of the benchmark): workgroup b
+// reads the contiguous chunk [b chunk, (b + 1) chunk) with 8 non-temporal loads in
+// flight per thread (a chunk per workgroup keeps DRAM pages open: it measured 7.0
+// TB/s where a grid-stride walk read 5.9). The words are folded by XOR so the
+// loads cannot be dropped; a workgroup writes its fold only if it is a marker value.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_read_roof(const u32x4* __restrict__ in, int64_t n16, int64_t chunk,
+                                                   uint32_t* __restrict__ out) {
+  constexpr int U = 8;
+  const int64_t b0 = (int64_t)blockIdx.x * chunk;
+  const int64_t b1 = b0 + chunk < n16 ? b0 + chunk : n16;
+  uint32_t acc = 0u;
+  for (int64_t base = b0 + threadIdx.x; base < b1; base += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256;
+      v[u] = i < b1 ? __builtin_nontemporal_load(in + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;
+}
+
 }  // namespace
+
+extern "C" int32_t hsa_roof_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks, void* stream) {
+  if (!buf || !out || bytes <= 0 || (bytes & 15) || blocks <= 0) return -1;
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(k_read_roof, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(buf), n16, (n16 + blocks - 1) / blocks, out);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int32_t hsa_synth_rows(uint64_t seed, uint32_t stream_id, const uint32_t* keys,
                                   uint32_t key, const int64_t* pos, int64_t pos0, int64_t n_rows,
