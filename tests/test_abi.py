@@ -25,7 +25,7 @@ def test_headers_declare_the_boundary(root):
               "hsa_compress_flush", "hsa_block_table_share", "hsa_indexer_topk",
               "hsa_decode_attend", "hsa_decode_step"):
         assert n in names
-    assert declared(root, "hsa_synth.h") == ["hsa_synth_rows"]
+    assert declared(root, "hsa_synth.h") == ["hsa_roof_read", "hsa_synth_rows"]
 
 
 def test_libhsa_exports_every_declared_symbol(root):
