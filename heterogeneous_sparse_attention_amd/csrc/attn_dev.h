@@ -494,6 +494,114 @@ __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, con
   *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(ox, oy);
 }
 
+// Sum and max over each half of a wave (lanes 0-31, 32-63); every lane gets its half's.
+__device__ __forceinline__ float half_sum(float v) {
+  v = row_sum16(v);
+  return v + __shfl_xor(v, 16);
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = row_max16(v);
+  return fmaxf(v, __shfl_xor(v, 16));
+}
+
+// merge_partials for all 16 heads of a request by one 512-thread workgroup, so that
+// the whole merge costs one memory round trip (up to 32 partials): head h is taken
+// by threads 32h .. 32h + 31, lane j of them writes dims 4j .. 4j + 3 and holds the
+// max and sum of partial j. Same extra key as merge_partials.
+template <class PartFn>
+__device__ __forceinline__ void merge_partials_wg(PartFn part_of, int n, const float* part_acc,
+                                                  const float* part_ml, float* out_row, ExtraKey xk) {
+  const int h = threadIdx.x >> 5;
+  const int j = threadIdx.x & 31;
+  const int src0 = threadIdx.x & 32;   // the wave lane that holds the half's partial 0
+  const int o = h * kD + 4 * j;
+  float xs = kNoMax;
+  float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (xk.k) {
+    const uint2 qw = *reinterpret_cast<const uint2*>(xk.q + o);
+    float kx[4];
+    if (xk.fp8) {   // four codes of K and of V, and the head's scales
+      const uint8_t* codes = reinterpret_cast<const uint8_t*>(xk.k);
+      const float* sc = reinterpret_cast<const float*>(xk.v);
+      const int hp = 4 * (h & 3) + (h >> 2);
+      const int kc = (int)*reinterpret_cast<const uint32_t*>(codes + o);
+      const int vc = (int)*reinterpret_cast<const uint32_t*>(codes + kRow + o);
+      const float ks = sc[hp], vs = sc[kH + hp];
+      const f32x2_v k01 = __builtin_amdgcn_cvt_pk_f32_fp8(kc, false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8(kc, true);
+      const f32x2_v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(vc, false), v23 = __builtin_amdgcn_cvt_pk_f32_fp8(vc, true);
+      kx[0] = k01.x * ks;
+      kx[1] = k01.y * ks;
+      kx[2] = k23.x * ks;
+      kx[3] = k23.y * ks;
+      xv = make_float4(v01.x * vs, v01.y * vs, v23.x * vs, v23.y * vs);
+    } else {
+      const uint2 kw = *reinterpret_cast<const uint2*>(xk.k + o);
+      const uint2 vw = *reinterpret_cast<const uint2*>(xk.v + o);
+      kx[0] = bf_lo(kw.x);
+      kx[1] = bf_hi(kw.x);
+      kx[2] = bf_lo(kw.y);
+      kx[3] = bf_hi(kw.y);
+      xv = make_float4(bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y));
+    }
+    const float d = fmaf(bf_lo(qw.x), kx[0], bf_hi(qw.x) * kx[1]) + fmaf(bf_lo(qw.y), kx[2], bf_hi(qw.y) * kx[3]);
+    xs = half_sum(d) * kQScale;
+  }
+  float4 acc;
+  auto add = [&](float w, const float4& a) {
+    acc.x = fmaf(w, a.x, acc.x);
+    acc.y = fmaf(w, a.y, acc.y);
+    acc.z = fmaf(w, a.z, acc.z);
+    acc.w = fmaf(w, a.w, acc.w);
+  };
+  if (n <= 32) {   // rows, maxima and sums in one round trip
+    float4 a[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      if (c < n) a[c] = *reinterpret_cast<const float4*>(part_acc + part_of(c) * kRow + o);
+    float mm = kNoMax, ll = 0.f;
+    if (j < n) {
+      const int64_t p = part_of(j);
+      mm = part_ml[p * 2 * kH + h];
+      ll = part_ml[p * 2 * kH + kH + h];
+    }
+    const float M = fmaxf(half_max(mm), xs);
+    float w = j < n ? exp2f(mm - M) : 0.f;
+    const float xw = xk.k ? exp2f(xs - M) : 0.f;
+    const float invL = 1.f / (half_sum(w * ll) + xw);
+    w *= invL;
+    const float xwn = xw * invL;
+    acc = make_float4(xwn * xv.x, xwn * xv.y, xwn * xv.z, xwn * xv.w);
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      if (c < n) add(__shfl(w, src0 + c), a[c]);
+  } else {   // maxima, then sums, then the rows 32 partials at a time
+    float M = kNoMax;
+    for (int c = j; c < n; c += 32) M = fmaxf(M, part_ml[part_of(c) * 2 * kH + h]);
+    M = fmaxf(half_max(M), xs);
+    float L = 0.f;
+    for (int c = j; c < n; c += 32) {
+      const int64_t p = part_of(c);
+      L += exp2f(part_ml[p * 2 * kH + h] - M) * part_ml[p * 2 * kH + kH + h];
+    }
+    const float xw = xk.k ? exp2f(xs - M) : 0.f;
+    const float invL = 1.f / (half_sum(L) + xw);
+    const float xwn = xw * invL;
+    acc = make_float4(xwn * xv.x, xwn * xv.y, xwn * xv.z, xwn * xv.w);
+    for (int g = 0; g < n; g += 32) {
+      float4 a[32];
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (g + c < n) a[c] = *reinterpret_cast<const float4*>(part_acc + part_of(g + c) * kRow + o);
+      const int cl = g + j;
+      const float w = cl < n ? exp2f(part_ml[part_of(cl) * 2 * kH + h] - M) * invL : 0.f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (g + c < n) add(__shfl(w, src0 + c), a[c]);
+    }
+  }
+  *reinterpret_cast<float4*>(out_row + o) = acc;
+}
+
 // Log-sum-exp merge of n partials of one request into one partial (unnormalised)
 // at index dst, by one wave per head h; lane l holds dims 2l, 2l+1.
 template <class PartFn>
