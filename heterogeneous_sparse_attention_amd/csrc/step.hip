@@ -27,6 +27,8 @@
 // S2b) beside part A; S3 attends part B through the physical C4 rows S2 wrote.
 //
 // Key order differs from hsa_decode_attend only in the order of the softmax sum.
+#include <algorithm>
+
 #include "attn_dev.h"
 #include "device.h"
 #include "kernels.h"
@@ -425,9 +427,10 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
 }
 
 // S4: the log-sum-exp merge of each request's partials, one 512-thread workgroup per
-// request, so that every head of the request costs one memory round trip
-// (merge_partials_wg; four workgroups of one head per wave measured 0.2 us slower per
-// b32 step). The HCA entry of a block sealed in this step joins as one more key.
+// request, so that every head of the request costs one memory round trip when it has
+// at most 32 partials (merge_partials_wg; four workgroups of one head per wave
+// measured 0.2 us slower per b32 step). The HCA entry of a block sealed in this step
+// joins as one more key.
 __global__ __launch_bounds__(512) void k_step4(Pools P, ReqBatch B, StepArgs S) {
   const int r = blockIdx.x;
   const int fa = S.first_a[r], ca = S.first_a[r + 1] - fa;
@@ -445,6 +448,29 @@ __global__ __launch_bounds__(512) void k_step4(Pools P, ReqBatch B, StepArgs S) 
   }
   merge_partials_wg([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
                     S.part_acc, S.part_ml, S.out + (int64_t)r * kRow, xk);
+}
+
+// S4 when some request has more than 32 partials (few long requests over the whole
+// GPU): four workgroups per request, one head per wave, so that the partials' rows
+// are loaded by 16 waves per request instead of one workgroup's passes.
+__global__ __launch_bounds__(256) void k_step4_heads(Pools P, ReqBatch B, StepArgs S) {
+  const int r = blockIdx.x >> 2;
+  const int fa = S.first_a[r], ca = S.first_a[r + 1] - fa;
+  const int fb = S.first_b[r], cb = S.first_b[r + 1] - fb;
+  const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
+  const Req R = B.r[r];
+  ExtraKey xk{nullptr, nullptr, nullptr, false};
+  if (S.a_only && (blockIdx.x & 3) == 0)   // no C4 entries: the top-k row is padding
+    for (int i = threadIdx.x; i < S.k; i += 256) {
+      S.topk[(int64_t)r * S.k + i] = -1;
+      if (S.score_out) S.score_out[(int64_t)r * S.k + i] = -INFINITY;
+    }
+  if ((S.fused || S.a_only) && R.aux >= 0 && P.hca) {   // the HCA entry of the block sealed now, merged in S2
+    const C4Addr c = hca_addr(P, R.aux);
+    xk = ExtraKey{c.k, c.v, S.q + (int64_t)r * kRow, P.kv8 != 0};
+  }
+  merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
+                 h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow, xk);
 }
 
 }  // namespace
@@ -486,6 +512,10 @@ hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
 hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
   if (B.n == 0) return hipSuccess;
+  int parts = 0;   // the most partials of one request
+  for (int i = 0; i < B.n; ++i)
+    parts = std::max(parts, S.first_a[i + 1] - S.first_a[i] + S.first_b[i + 1] - S.first_b[i]);
+  if (parts > 32) return launch_k(k_step4_heads, dim3(4 * B.n), dim3(256), st, ev, P, B, S);
   return launch_k(k_step4, dim3(B.n), dim3(512), st, ev, P, B, S);
 }
 
