@@ -259,9 +259,9 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
 // Attention of one workgroup over two key lists of one request, A = [a0, a1) and
 // B = [b0, b1), in one online softmax. The workgroup's keys are the list A then B;
 // wave w takes positions w, w + WAVES, w + 2 WAVES, ... of it, so no wave has more
-// than one key above the average, and every wave's A keys come first. The addresses of the B keys are known only after mid(),
-// work that every wave of the workgroup runs once (it may hold barriers and must
-// issue no global load). The first RING - 1 keys of each wave are A keys where
+// than one key above the average, and every wave's A keys come first. The
+// addresses of the B keys are known only after mid(), work that every wave of the
+// workgroup runs once (it may hold barriers and must issue no global load). The first RING - 1 keys of each wave are A keys where
 // it has them, and their loads are issued before mid(), so they arrive while mid()
 // runs; pre() runs just before those loads are issued (work that should wait for
 // earlier loads first). key_a / key_b return the rows of a key or nullptrs for a

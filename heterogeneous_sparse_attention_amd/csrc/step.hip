@@ -18,10 +18,12 @@
 //   S4  log-sum-exp merge of every request's attention partials.
 //
 // Three-launch form (every score row fits the selection's LDS cache, top-k in
-// ordinal order): each S2 attention workgroup takes a share of both parts of one
-// request, loads the request's score row, starts loading its first part-A keys,
-// runs the top-k itself from LDS and then streams its keys; S4 also takes the
-// HCA entry of the block sealed now as one more key.
+// ordinal order): each mixed S2 workgroup takes a share of part B of one request
+// and the part-A keys its waves can prefetch (the last of the request's part-A
+// list); it loads the request's score row, starts loading those part-A keys, runs
+// the top-k itself from LDS and then streams its keys. Part-A workgroups in the
+// same launch stream the rest of the part-A keys meanwhile. S4 also takes the HCA
+// entry of the block sealed now as one more key.
 // Four-launch form (long rows, or sorted top-k output): S2 runs the selections
 // (one workgroup per row, or per slice of a long row with a second round in
 // S2b) beside part A; S3 attends part B through the physical C4 rows S2 wrote.
@@ -263,10 +265,11 @@ struct Step2Shared {
   int32_t rows[kCacheN];   // three-launch part B: physical C4 rows of the workgroup's share
 };
 
-// Three-launch form, workgroup `bid` of request r (w of nch): it attends its share
-// of both of the request's key lists, part A (SWA tokens and HCA entries of earlier
-// blocks, share chunk w of nch) and part B (the selected C4 entries, same share of
-// the selection), in one online softmax. It first loads the request's scores (at
+// Three-launch form, mixed workgroup `bid` of request r (w of nch): it attends its
+// share of both of the request's key lists, part A (SWA tokens and HCA entries of
+// earlier blocks: share chunk w of nch of the keys [a_split, keys_a), the rest being
+// the part-A workgroups') and part B (the selected C4 entries, same share of the
+// selection), in one online softmax. It first loads the request's scores (at
 // most kCacheN, into registers) and issues its first part-A key loads, then runs the
 // top-k itself from LDS while those loads are in flight: it keeps in LDS the
 // physical C4 rows of its share [b0, b1) of the selection and writes the same share
