@@ -21,9 +21,10 @@ Bars, against the fp64 oracle fed the same values:
   selection (inside the tie band several selections are correct).
 - the integer state: bit-exact.
 Both step forms are covered: the three-launch form (the default for these rows),
-and the four-launch form (forced by HSA_STEP_FUSED=0, and by sorted rows). So are
-the standalone hsa_indexer_topk and hsa_decode_attend (after the three-launch
-steps).
+and the four-launch form (forced by HSA_STEP_FUSED=0, and by sorted rows), once
+more with rows of more than 1024 scores cut into slices (HSA_SELECT_SLICE=1024:
+the two-round top-k of long rows). So are the standalone hsa_indexer_topk and
+hsa_decode_attend (after the three-launch steps, and with sliced rows).
 """
 
 import numpy as np
@@ -112,11 +113,14 @@ def to_dev(bits_or_f32, bf16):
     return t.cuda()
 
 
-def build(monkeypatch, fused):
-    """The GPU cache and the oracle, both prefilled with the same tokens."""
+def build(monkeypatch, fused, slice_=0):
+    """The GPU cache and the oracle, both prefilled with the same tokens. slice_ > 0
+    cuts longer score rows into slices of that many scores (two-round top-k)."""
     from heterogeneous_sparse_attention_amd import Cache
     if not fused:
         monkeypatch.setenv("HSA_STEP_FUSED", "0")
+    if slice_:
+        monkeypatch.setenv("HSA_SELECT_SLICE", str(slice_))
     L0 = lengths()
     Wc, Wh = synth.gate_weights(SEED)
     nb = int(((L0 + 16) // BLOCK).sum()) + N_REQ
@@ -153,11 +157,16 @@ def check_row(o, s, idx, val, qi, k, sorted=False):
     return len(set(sel.tolist()) ^ set(ref_idx[:kk].tolist()))
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["three_launch", "four_launch"])
-def test_general_inputs_decode_steps(monkeypatch, fused):
+@pytest.mark.parametrize("fused,slice_", [(True, 0), (False, 0), (False, 1024)],
+                         ids=["three_launch", "four_launch", "four_launch_sliced"])
+def test_general_inputs_decode_steps(monkeypatch, fused, slice_):
+    """Decode steps on general inputs in each step form; with slice_, the rows of more
+    than 1024 scores take the two-round top-k (per-slice candidates, then the row),
+    so the tie band is met inside the slices too."""
     import torch
-    cache, o, st, srcs, L0 = build(monkeypatch, fused)
-    say(f"general inputs ({'three' if fused else 'four'}-launch form): prefilled {int(L0.sum())} tokens")
+    cache, o, st, srcs, L0 = build(monkeypatch, fused, slice_)
+    say(f"general inputs ({'three' if fused else 'four'}-launch form{', sliced rows' if slice_ else ''}): "
+        f"prefilled {int(L0.sum())} tokens")
     try:
         L = L0.copy()
         topk = torch.empty((N_REQ, K), dtype=torch.int32, device="cuda")
@@ -187,7 +196,7 @@ def test_general_inputs_decode_steps(monkeypatch, fused):
             assert cache.block_table(st[b]) == o.table(st[b])
         say(f"general inputs: {steps + 2} steps x {N_REQ} requests, worst rel L2 {worst:.2e}, "
             f"{int(swaps)} entries swapped inside the tie band")
-        if fused:
+        if fused or slice_:
             standalone_calls(cache, o, st)
     finally:
         cache.close()
@@ -217,9 +226,10 @@ def test_near_tie_cluster(monkeypatch):
     reorders entries near it. Every indexer key of a request is one base vector plus
     a relative perturbation of 1e-7, so the request's C4 scores agree to about 1e-6.
     The oracle ranks them by the perturbations; the GPU's float32 sums differ from
-    the float64 ones by about as much. Both step forms, and sorted rows. The rows are
-    accepted within the tie band, and attention matches the oracle's over the GPU's
-    selection. At least one entry must differ from the oracle's selection, so that
+    the float64 ones by about as much. Both step forms (the four-launch one also with
+    rows cut into slices of 1024 scores, the two-round top-k), and sorted rows. The
+    rows are accepted within the tie band, and attention matches the oracle's over
+    the GPU's selection. At least one entry must differ from the oracle's selection, so that
     the band is really used."""
     import torch
     from heterogeneous_sparse_attention_amd import Cache
@@ -228,9 +238,11 @@ def test_near_tie_cluster(monkeypatch):
     L0 = np.array([8192, 8200, 6000, 4100, 8191, 300])
     Wc, Wh = synth.gate_weights(SEED)
     swaps = 0
-    for fused in (True, False):
+    for fused, slice_ in ((True, 0), (False, 0), (False, 1024)):
         if not fused:
             monkeypatch.setenv("HSA_STEP_FUSED", "0")
+        if slice_:
+            monkeypatch.setenv("HSA_SELECT_SLICE", str(slice_))
         nb = int(((L0 + 8) // BLOCK).sum()) + n_req
         cache = Cache(N_WIN, n_req, nb, Wc, Wh)
         o = Oracle(N_WIN, Wc, Wh, n_req, nb)
@@ -267,7 +279,7 @@ def test_near_tie_cluster(monkeypatch):
                     o.append([st[b]], [(bf16_vals(Kn[b:b + 1]), bf16_vals(Vn[b:b + 1]), KIn[b:b + 1])])
                     swaps += check_row(o, st[b], g_idx[b], g_val[b], QIn[b], k, sorted=sorted_)
                     r = rel_l2(g_out[b], o.attend(st[b], bf16_vals(Qn[b]), g_idx[b], k))
-                    assert r <= TOL, (fused, t, b, r)
+                    assert r <= TOL, (fused, slice_, t, b, r)
                 L += 1
             # the standalone top-k on the same cluster
             QI = rng.standard_normal((n_req, 4, 64)).astype(np.float32)
