@@ -31,11 +31,11 @@ def _gpu():
 SEED = 0x4E4F41
 
 
-def _pair(n_win, max_states, max_blocks):
+def _pair(n_win, max_states, max_blocks, **fmt):
     from heterogeneous_sparse_attention_amd import Cache
     Wc, Wh = synth.gate_weights(SEED)
-    return (Cache(n_win, max_states, max_blocks, Wc, Wh),
-            Cache(n_win, max_states, max_blocks, Wc, Wh))
+    return (Cache(n_win, max_states, max_blocks, Wc, Wh, **fmt),
+            Cache(n_win, max_states, max_blocks, Wc, Wh, **fmt))
 
 
 def _prefill(caches, L0):
@@ -91,7 +91,8 @@ def _same_pools(caches, st):
         L, W = info["len"], a.n_win
         ring = np.arange(L - info["swa_len"], L) % W        # slots holding the window
         tail = np.arange(L - info["hca_tail"], L) % 128     # slots holding the open block
-        for name, slots in (("swa_k", ring), ("swa_v", ring), ("idx_tail", tail)):
+        for name in ea:   # ring rows (bf16, or FP8 codes and scales) and the indexer tail
+            slots = tail if name == "idx_tail" else ring
             assert np.array_equal(ea[name][slots], eb[name][slots]), (s, name)
     for blk in sorted({x for s in st for x in a.block_table(s)}):
         ea, eb = a.export_block(blk), b.export_block(blk)
@@ -99,10 +100,15 @@ def _same_pools(caches, st):
             assert np.array_equal(ea[name], eb[name]), (blk, name)
 
 
-def test_noalloc_step_equals_decode_step_two_calls():
+FORMATS = [{}, {"entry_format": "fp8", "index_format": "mxfp4", "kv_format": "fp8"}]
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["bf16", "fp8_mxfp4_fp8kv"])
+def test_noalloc_step_equals_decode_step_two_calls(fmt):
     """Call 1: 12 requests (seals, a request with no block, rows long enough for the
-    four-launch form); call 2: 5 of them with a smaller k. Both step forms."""
-    caches = _pair(128, 16, 600)
+    four-launch form); call 2: 5 of them with a smaller k. Both step forms; the
+    measured storage and the low-bit one (FP8 entries and KV, MXFP4 keys)."""
+    caches = _pair(128, 16, 600, **fmt)
     try:
         L0 = np.array([127, 1, 255, 130, 17000, 383, 4096, 5, 128, 900, 2047, 3000])
         st = _prefill(caches, L0)
