@@ -56,7 +56,9 @@ __device__ __forceinline__ KeyAddr key_addr(const Pools& P, const Req& R, int x,
 // One workgroup per chunk of a request's keys; it writes an unnormalised partial,
 // or the output itself when the request is a single chunk. k_merge combines the
 // partials in the next launch: a kernel boundary costs far less on this GPU than a
-// device-scope fence in every workgroup.
+// device-scope fence in every workgroup. KV8: FP8 SWA ring and HCA entries; F8: FP8
+// C4 entries.
+template <bool KV8, bool F8>
 __global__ __launch_bounds__(kAttnWaves * 64) void k_attend(Pools P, ReqBatch B, int32_t chunk,
                                                            const uint16_t* q, const int32_t* topk,
                                                            int32_t k, float* part_acc,
@@ -72,9 +74,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attend(Pools P, ReqBatch B,
   const C4Addr dm = dummy_rows(P, R.state);   // valid rows (L >= 1)
   float M, L, A8[8];
   // keys below the C4 entries (SWA tokens, HCA entries) follow the KV format
-  attend_keys([&](int x) { return key_addr(P, R, x, sel); }, w * chunk, min(nk, (w + 1) * chunk),
-              q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8,
-              (R.len < P.n_win ? R.len : P.n_win) + (P.hca ? R.nb : 0), P.kv8 != 0, P.fp8 != 0);
+  attend_keys<kAttnWaves, ring_depth<kAttnWaves>(), KV8, F8>(
+      [&](int x) { return key_addr(P, R, x, sel); }, w * chunk, min(nk, (w + 1) * chunk), q + (int64_t)r * kRow,
+      dm.k, dm.v, sh, M, L, A8, (R.len < P.n_win ? R.len : P.n_win) + (P.hca ? R.nb : 0));
   if (nch == 1)
     store_output(out + (int64_t)r * kRow, L, A8);
   else
@@ -102,8 +104,13 @@ hipError_t launch_attend(const Pools& P, const ReqBatch& B, int64_t total_chunks
                          float* part_ml, float* out, hipStream_t st,
                  const LaunchEv& ev) {
   if (total_chunks == 0) return hipSuccess;
-  return launch_k(k_attend, dim3((unsigned)total_chunks), dim3(kAttnWaves * 64), st, ev, P, B,
-                     chunk, static_cast<const uint16_t*>(q), topk, k, part_acc, part_ml, out);
+  const dim3 g((unsigned)total_chunks), t(kAttnWaves * 64);
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  if (P.kv8)
+    return P.fp8 ? launch_k(k_attend<true, true>, g, t, st, ev, P, B, chunk, q16, topk, k, part_acc, part_ml, out)
+                 : launch_k(k_attend<true, false>, g, t, st, ev, P, B, chunk, q16, topk, k, part_acc, part_ml, out);
+  return P.fp8 ? launch_k(k_attend<false, true>, g, t, st, ev, P, B, chunk, q16, topk, k, part_acc, part_ml, out)
+               : launch_k(k_attend<false, false>, g, t, st, ev, P, B, chunk, q16, topk, k, part_acc, part_ml, out);
 }
 
 hipError_t launch_merge(const Pools& P, const ReqBatch& B, int32_t chunk, int32_t k,

@@ -70,34 +70,33 @@ struct KeyRegs {
   uint4 v[4];
 };
 
-// Issue the loads of key j (lane j's addresses) of the current 64-key group. For a
-// bf16 key kp/vp are its K and V rows; for an FP8 C4 key kp is its code row (K
-// codes, then V codes) and vp its scale row (K scales, then V scales, head h at
-// 4 (h % 4) + h / 4, so lane l's heads l/16 + 4c are 4 consecutive floats).
-__device__ __forceinline__ void load_key(KeyRegs& R, uint64_t kp, uint64_t vp, int j, int lane,
-                                         bool fp8) {
-  if (!fp8) {
-    const uint16_t* pk = lane_ptr(kp, j);
-    const uint16_t* pv = lane_ptr(vp, j);
+// Issue the loads of one key. bf16 key: pk / pv are its K and V rows. FP8 key: pk
+// is its code row (K codes, then V codes) and pv its scale row (K scales, then V
+// scales, head h at 4 (h % 4) + h / 4, so lane l's heads l/16 + 4c are 4 consecutive
+// floats). The format is a template parameter, so every path of a loop issues the
+// same number of loads and the compiler's wait counts stay exact.
+template <bool F8>
+__device__ __forceinline__ void load_key(KeyRegs& R, const uint16_t* pk, const uint16_t* pv, int lane) {
+  if constexpr (!F8) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       R.k[c] = load_stream(reinterpret_cast<const uint4*>(pk + c * 512) + lane);
       R.v[c] = load_stream(reinterpret_cast<const uint4*>(pv + c * 512) + lane);
     }
-    return;
-  }
-  const uint8_t* pq = reinterpret_cast<const uint8_t*>(lane_ptr(kp, j));
-  const float* ps = reinterpret_cast<const float*>(lane_ptr(vp, j)) + 4 * (lane >> 4);
-  const float4 sk = load_global(reinterpret_cast<const float4*>(ps));
-  const float4 sv = load_global(reinterpret_cast<const float4*>(ps + kH));
-  const float skc[4] = {sk.x, sk.y, sk.z, sk.w};
-  const float svc[4] = {sv.x, sv.y, sv.z, sv.w};
+  } else {
+    const uint8_t* pq = reinterpret_cast<const uint8_t*>(pk);
+    const float* ps = reinterpret_cast<const float*>(pv) + 4 * (lane >> 4);
+    const float4 sk = load_global(reinterpret_cast<const float4*>(ps));
+    const float4 sv = load_global(reinterpret_cast<const float4*>(ps + kH));
+    const float skc[4] = {sk.x, sk.y, sk.z, sk.w};
+    const float svc[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint2 a = load_stream(reinterpret_cast<const uint2*>(pq + c * 512) + lane);
-    const uint2 b = load_stream(reinterpret_cast<const uint2*>(pq + kRow + c * 512) + lane);
-    R.k[c] = make_uint4(a.x, a.y, __float_as_uint(skc[c]), 0u);
-    R.v[c] = make_uint4(b.x, b.y, __float_as_uint(svc[c]), 0u);
+    for (int c = 0; c < 4; ++c) {
+      const uint2 a = load_stream(reinterpret_cast<const uint2*>(pq + c * 512) + lane);
+      const uint2 b = load_stream(reinterpret_cast<const uint2*>(pq + kRow + c * 512) + lane);
+      R.k[c] = make_uint4(a.x, a.y, __float_as_uint(skc[c]), 0u);
+      R.v[c] = make_uint4(b.x, b.y, __float_as_uint(svc[c]), 0u);
+    }
   }
 }
 
@@ -132,10 +131,11 @@ __device__ __forceinline__ void compute_key_fp8(const KeyRegs& R, bool ok, const
   }
 }
 
-// Online softmax update of this lane's 4 heads with one key (bf16, or FP8 when fp8).
+// Online softmax update of this lane's 4 heads with one key (bf16, or FP8 when F8).
+template <bool F8>
 __device__ __forceinline__ void compute_key(const KeyRegs& R, bool ok, const uint4* qw, float* m,
-                                            float* l, float (*acc)[8], bool fp8 = false) {
-  if (fp8) {
+                                            float* l, float (*acc)[8]) {
+  if constexpr (F8) {
     compute_key_fp8(R, ok, qw, m, l, acc);
     return;
   }
@@ -155,6 +155,67 @@ __device__ __forceinline__ void compute_key(const KeyRegs& R, bool ok, const uin
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[c][i] = fmaf(p, vf[i], acc[c][i] * sc);
     m[c] = mx;
+  }
+}
+
+// The loads of keys [x0, x0 + RING - 1) of the current 64-key group into the ring
+// (lane x of kp / vp holds key x's rows; dummy rows from x1 on).
+template <int RING, bool F8>
+__device__ __forceinline__ void ring_fill(KeyRegs (&ring)[RING], int x0, int x1, uint64_t kp, uint64_t vp,
+                                          const uint16_t* dummy_k, const uint16_t* dummy_v, int lane) {
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) {
+    const int x = x0 + u;
+    const bool live = x < x1;
+    const int j = live ? x : 0;
+    load_key<F8>(ring[u], live ? lane_ptr(kp, j) : dummy_k, live ? lane_ptr(vp, j) : dummy_v, lane);
+  }
+}
+
+// Keys [x0, x1) of the current 64-key group through the ring: on entry slot u holds
+// key x0 + u (RING - 1 of them in flight); each step issues the loads of the key
+// RING - 1 ahead, a dummy row from x1 on, and consumes one. Issuing on every path
+// keeps the number of loads behind each key the same, so the wait for a key leaves
+// the next RING - 1 keys in flight.
+template <int RING, bool F8>
+__device__ __forceinline__ void ring_run(KeyRegs (&ring)[RING], int x0, int x1, uint64_t kp, uint64_t vp,
+                                         const uint16_t* dummy_k, const uint16_t* dummy_v, uint64_t okmask,
+                                         const uint4* qw, float* m, float* l, float (*acc)[8], int lane) {
+  for (int i = x0; i < x1; i += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const int x = i + u;
+      if (x >= x1) break;
+      const int xn = x + RING - 1;
+      const bool live = xn < x1;
+      const int j = live ? xn : 0;
+      load_key<F8>(ring[(u + RING - 1) % RING], live ? lane_ptr(kp, j) : dummy_k,
+                   live ? lane_ptr(vp, j) : dummy_v, lane);
+      compute_key<F8>(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+    }
+  }
+}
+
+// Keys [x0, x1) of the current group, those below `split` in format F8LO and the
+// others in F8HI: one ring run per format (a format change drains the ring).
+template <int RING, bool F8LO, bool F8HI>
+__device__ __forceinline__ void ring_runs(KeyRegs (&ring)[RING], int x0, int x1, int split, uint64_t kp,
+                                          uint64_t vp, const uint16_t* dummy_k, const uint16_t* dummy_v,
+                                          uint64_t okmask, const uint4* qw, float* m, float* l,
+                                          float (*acc)[8], int lane) {
+  if constexpr (F8LO == F8HI) {
+    ring_fill<RING, F8LO>(ring, x0, x1, kp, vp, dummy_k, dummy_v, lane);
+    ring_run<RING, F8LO>(ring, x0, x1, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
+  } else {
+    const int s = min(max(split, x0), x1);
+    if (x0 < s) {
+      ring_fill<RING, F8LO>(ring, x0, s, kp, vp, dummy_k, dummy_v, lane);
+      ring_run<RING, F8LO>(ring, x0, s, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
+    }
+    if (s < x1) {
+      ring_fill<RING, F8HI>(ring, s, x1, kp, vp, dummy_k, dummy_v, lane);
+      ring_run<RING, F8HI>(ring, s, x1, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
+    }
   }
 }
 
@@ -198,16 +259,15 @@ __device__ __forceinline__ void merge_waves(const float* m, const float* l, cons
 // Attention of one workgroup of WAVES waves over keys [x0, x1) of one request:
 // wave w streams a contiguous share. key_of(x) gives the K and V rows of key x (for
 // an FP8 key: its code and scale rows) or nullptrs for a skipped slot; keys x <
-// fp8_split are FP8 when fp8_lo, the others when fp8_hi. dummy_k / dummy_v are
-// valid rows (at least 4 KiB) read in place of skipped keys. On return threads
-// t < 256 hold head t/16, dims (t%16)*8 .. +8 of the unnormalised result: running
-// max M (log2 units), sum L, accumulator A8.
-template <int WAVES = kAttnWaves, int RING = ring_depth<WAVES>(), class KeyFn>
+// split are FP8 when F8LO, the others when F8HI. dummy_k / dummy_v are valid rows
+// (at least 4 KiB) read in place of skipped keys. On return threads t < 256 hold
+// head t/16, dims (t%16)*8 .. +8 of the unnormalised result: running max M (log2
+// units), sum L, accumulator A8.
+template <int WAVES, int RING, bool F8LO, bool F8HI, class KeyFn>
 __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const uint16_t* qrow,
                                             const uint16_t* dummy_k, const uint16_t* dummy_v,
                                             AttnSharedT<WAVES>& sh, float& M, float& L, float* A8,
-                                            int fp8_split = 0x7fffffff, bool fp8_lo = false,
-                                            bool fp8_hi = true) {
+                                            int split = 0x7fffffff) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -226,6 +286,7 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
   }
+  KeyRegs ring[RING];
   for (int g = w0; g < w1; g += 64) {
     KeyAddr a;
     a.k = a.v = nullptr;
@@ -234,45 +295,29 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
     const uint64_t okmask = __ballot(okl);
     const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
     const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
-    const int n = min(64, w1 - g);
-    const int f8 = fp8_split - g;   // keys x < f8 of this group follow fp8_lo, the others fp8_hi
-    auto is8 = [&](int x) { return x < f8 ? fp8_lo : fp8_hi; };
-    // ring of RING keys: RING - 1 keys stay in flight while one is consumed
-    KeyRegs ring[RING];
-#pragma unroll
-    for (int u = 0; u < RING - 1; ++u)
-      if (u < n) load_key(ring[u], kp, vp, u, lane, is8(u));
-    for (int i = 0; i < n; i += RING) {
-#pragma unroll
-      for (int u = 0; u < RING; ++u) {
-        const int x = i + u;
-        if (x >= n) break;
-        if (x + RING - 1 < n)
-          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane, is8(x + RING - 1));
-        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, is8(x));
-      }
-    }
+    ring_runs<RING, F8LO, F8HI>(ring, 0, min(64, w1 - g), split - g, kp, vp, dummy_k, dummy_v, okmask, qw, m,
+                                l, acc, lane);
   }
   merge_waves<WAVES>(m, l, acc, sh, M, L, A8);
 }
 
 // Attention of one workgroup over two key lists of one request, A = [a0, a1) and
-// B = [b0, b1), in one online softmax. The workgroup's keys are the list A then B;
-// wave w takes positions w, w + WAVES, w + 2 WAVES, ... of it, so no wave has more
-// than one key above the average, and every wave's A keys come first. The
-// addresses of the B keys are known only after mid(), work that every wave of the
-// workgroup runs once (it may hold barriers and must issue no global load). The first RING - 1 keys of each wave are A keys where
-// it has them, and their loads are issued before mid(), so they arrive while mid()
-// runs; pre() runs just before those loads are issued (work that should wait for
-// earlier loads first). key_a / key_b return the rows of a key or nullptrs for a
-// skipped slot (with fp8_a / fp8_b, key_a / key_b give the code and scale rows of FP8 keys);
-// dummy_k / dummy_v are valid rows (at least 4 KiB) read in their place. Result as
-// attend_keys.
-template <int WAVES, int RING, class KeyA, class KeyB, class Pre, class Mid>
+// B = [b0, b1), in one online softmax; A keys are in format F8A, B keys in F8B. The
+// workgroup's keys are the list A then B; wave w takes positions w, w + WAVES,
+// w + 2 WAVES, ... of it, so no wave has more than one key above the average, and
+// every wave's A keys come first. The addresses of the B keys are known only after
+// mid(), work that every wave of the workgroup runs once (it may hold barriers and
+// must issue no global load). The loads of each wave's first RING - 1 keys (its A
+// keys among them, dummy rows for the others) are issued before mid(), so they
+// arrive while mid() runs; pre() runs just before (work that should wait for earlier
+// loads first). key_a / key_b return the rows of a key (an FP8 key: its code and
+// scale rows) or nullptrs for a skipped slot; dummy_k / dummy_v are valid rows (at
+// least 4 KiB) read in their place. Result as attend_keys.
+template <int WAVES, int RING, bool F8A, bool F8B, class KeyA, class KeyB, class Pre, class Mid>
 __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_b, int b0, int b1, Pre pre, Mid mid,
                                            const uint16_t* qrow, const uint16_t* dummy_k,
                                            const uint16_t* dummy_v, AttnSharedT<WAVES>& sh, float& M,
-                                           float& L, float* A8, bool fp8_b = false, bool fp8_a = false) {
+                                           float& L, float* A8) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -295,19 +340,19 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   }
   auto key_j = [&](int j) { return j < na ? key_a(a0 + pos(j)) : key_b(b0 + pos(j) - nA); };
 
-  // group 0: A addresses, then the prefetch of the first RING - 1 keys (every load
-  // issued, dummy rows where a slot has no A key)
+  // group 0: A addresses, then the prefetch of keys [0, RING - 1) (dummy rows past
+  // the wave's A keys)
   const int n0 = min(64, n);
+  const int na0 = min(na, n0);
   KeyAddr a;
   a.k = a.v = nullptr;
-  if (lane < n0 && lane < na) a = key_a(a0 + pos(lane));
+  if (lane < na0) a = key_a(a0 + pos(lane));
   bool okl = a.k != nullptr;
   uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
   uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
   KeyRegs ring[RING];
   pre();
-#pragma unroll
-  for (int u = 0; u < RING - 1; ++u) load_key(ring[u], kp, vp, u, lane, fp8_a);
+  ring_fill<RING, F8A>(ring, 0, na0, kp, vp, dummy_k, dummy_v, lane);
   mid();
   if (lane < n0 && lane >= na) {
     a = key_b(b0 + pos(lane) - nA);
@@ -316,33 +361,28 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
     vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
   }
   uint64_t okmask = __ballot(okl);
+  if constexpr (F8A == F8B) {
+    // the prefetched slots that held dummies take their B keys
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u)
-    if (u >= na && u < n0) load_key(ring[u], kp, vp, u, lane, fp8_b);   // slots that held dummies
-  for (int g = 0; g < n; g += 64) {
+    for (int u = 0; u < RING - 1; ++u)
+      if (u >= na0 && u < n0) load_key<F8B>(ring[u], lane_ptr(kp, u), lane_ptr(vp, u), lane);
+    ring_run<RING, F8A>(ring, 0, n0, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
+  } else {
+    if (na0 > 0) ring_run<RING, F8A>(ring, 0, na0, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
+    if (na0 < n0) {
+      ring_fill<RING, F8B>(ring, na0, n0, kp, vp, dummy_k, dummy_v, lane);
+      ring_run<RING, F8B>(ring, na0, n0, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
+    }
+  }
+  for (int g = 64; g < n; g += 64) {
     const int ng = min(64, n - g);
-    if (g > 0) {
-      a.k = a.v = nullptr;
-      if (lane < ng) a = key_j(g + lane);
-      okl = a.k != nullptr;
-      okmask = __ballot(okl);
-      kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
-      vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
-#pragma unroll
-      for (int u = 0; u < RING - 1; ++u)
-        if (u < ng) load_key(ring[u], kp, vp, u, lane, g + u >= na ? fp8_b : fp8_a);
-    }
-    for (int i = 0; i < ng; i += RING) {
-#pragma unroll
-      for (int u = 0; u < RING; ++u) {
-        const int x = i + u;
-        if (x >= ng) break;
-        if (x + RING - 1 < ng)
-          load_key(ring[(u + RING - 1) % RING], kp, vp, x + RING - 1, lane,
-                   g + x + RING - 1 >= na ? fp8_b : fp8_a);
-        compute_key(ring[u], (okmask >> x) & 1ull, qw, m, l, acc, g + x >= na ? fp8_b : fp8_a);
-      }
-    }
+    a.k = a.v = nullptr;
+    if (lane < ng) a = key_j(g + lane);
+    okl = a.k != nullptr;
+    okmask = __ballot(okl);
+    kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
+    vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
+    ring_runs<RING, F8A, F8B>(ring, 0, ng, na - g, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
   }
   merge_waves<WAVES>(m, l, acc, sh, M, L, A8);
 }

@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, FP8 || KV8 ? 3 : 4) void k_step1(Pools P, ReqB
 // Attention part A (SWA tokens + HCA of blocks sealed before this step) of chunk
 // `bid`, over the request's part-A keys [0, a_split): it needs no top-k, so it runs
 // beside the selection.
-template <int WAVES, int RING = ring_depth<WAVES>()>
+template <int WAVES, bool KV8, int RING = ring_depth<WAVES>()>
 __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const StepArgs& S, int bid,
                                        AttnSharedT<WAVES>& sh) {
   const int r = owner_of(S.first_a, B.n, bid);
@@ -242,8 +242,7 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
   };
   const C4Addr dm = dummy_rows(P, R.state);
   float M, L, A8[8];
-  attend_keys<WAVES, RING>(key_a, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8, 0x7fffffff,
-                           P.kv8 != 0);
+  attend_keys<WAVES, RING, KV8, KV8>(key_a, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, bid, M, L, A8);
 }
 
@@ -275,7 +274,7 @@ struct Step2Shared {
 // physical C4 rows of its share [b0, b1) of the selection and writes the same share
 // of the top-k output (workgroup 0 also the padding). Every workgroup of a request
 // selects from the same scores, so the shares agree.
-template <int WAVES>
+template <int WAVES, bool KV8, bool F8>
 __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, const StepArgs& S, int bid,
                                            Step2Shared& sh) {
   constexpr int NT = WAVES * 64;
@@ -338,18 +337,19 @@ __device__ __forceinline__ void part_mixed(const Pools& P, const ReqBatch& B, co
   };
   const C4Addr dm = dummy_rows(P, R.state);
   float M, L, A8[8];
-  attend_two<WAVES, kMixedRing>(key_a, a0, a1, key_b, b0, b1, stage, select,
-                                         S.q + (int64_t)r * kRow, dm.k, dm.v, sh.attn, M, L, A8,
-                                         P.fp8 != 0, P.kv8 != 0);
+  attend_two<WAVES, kMixedRing, KV8, F8>(key_a, a0, a1, key_b, b0, b1, stage, select,
+                                          S.q + (int64_t)r * kRow, dm.k, dm.v, sh.attn, M, L, A8);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
+// KV8: FP8 SWA ring and HCA entries; F8: FP8 C4 entries (the attention's key formats)
+template <bool KV8, bool F8>
 __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, StepArgs S) {
   __shared__ Step2Shared sh;
   int bid = blockIdx.x;
   if (S.fused) {
     if (bid < S.n_b) {
-      part_mixed<kStep2Waves>(P, B, S, bid, sh);
+      part_mixed<kStep2Waves, KV8, F8>(P, B, S, bid, sh);
       return;
     }
     bid -= S.n_b;
@@ -377,9 +377,9 @@ __global__ __launch_bounds__(kStep2Threads) void k_step2(Pools P, ReqBatch B, St
   }
   bid -= B.n_seal;
   if (S.fused)
-    part_a<kStep2Waves, kSplitARing>(P, B, S, bid, sh.attn);
+    part_a<kStep2Waves, KV8, kSplitARing>(P, B, S, bid, sh.attn);
   else
-    part_a<kStep2Waves>(P, B, S, bid, sh.attn);
+    part_a<kStep2Waves, KV8>(P, B, S, bid, sh.attn);
 }
 
 // Round 2 of the top-k of rows sliced in k_step2 (launched only when some are).
@@ -394,6 +394,7 @@ __global__ __launch_bounds__(kSelThreads) void k_step2b(Pools P, ReqBatch B, Ste
 #endif
 constexpr int kStep3Waves = HSA_STEP3_WAVES;
 
+template <bool KV8, bool F8>
 __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B, StepArgs S) {
   __shared__ AttnSharedT<kStep3Waves> sh;
   const int bid = blockIdx.x;
@@ -424,8 +425,9 @@ __global__ __launch_bounds__(kStep3Waves * 64) void k_step3(Pools P, ReqBatch B,
   };
   const C4Addr dm = dummy_rows(P, R.state);   // valid rows (L >= 1)
   float M, L, A8[8];
-  attend_keys<kStep3Waves>(key_b, x0, x1, S.q + (int64_t)r * kRow, dm.k, dm.v, sh, M, L, A8, sn, P.kv8 != 0,
-                           P.fp8 != 0);
+  // the HCA entry of the block sealed now (key 0 when sn) is in the KV format
+  attend_keys<kStep3Waves, ring_depth<kStep3Waves>(), KV8, F8>(key_b, x0, x1, S.q + (int64_t)r * kRow, dm.k,
+                                                               dm.v, sh, M, L, A8, sn);
   if (threadIdx.x < 256) store_partial(S.part_acc, S.part_ml, (int64_t)S.n_a + bid, M, L, A8);
 }
 
@@ -497,7 +499,11 @@ hipError_t launch_step2(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
                  const LaunchEv& ev) {
   const int grid = (S.fused ? S.n_b : S.sel.n_wgs) + B.n_seal + S.n_a + (S.s2_append ? B.n : 0);
   if (grid == 0) return hipSuccess;
-  return launch_k(k_step2, dim3(grid), dim3(kStep2Threads), st, ev, P, B, S);
+  const dim3 g(grid), t(kStep2Threads);
+  if (P.kv8) return P.fp8 ? launch_k(k_step2<true, true>, g, t, st, ev, P, B, S)
+                          : launch_k(k_step2<true, false>, g, t, st, ev, P, B, S);
+  return P.fp8 ? launch_k(k_step2<false, true>, g, t, st, ev, P, B, S)
+               : launch_k(k_step2<false, false>, g, t, st, ev, P, B, S);
 }
 
 hipError_t launch_step2b(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
@@ -509,7 +515,11 @@ hipError_t launch_step2b(const Pools& P, const ReqBatch& B, const StepArgs& S, h
 hipError_t launch_step3(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
                  const LaunchEv& ev) {
   if (S.n_b == 0 || S.fused) return hipSuccess;
-  return launch_k(k_step3, dim3(S.n_b), dim3(kStep3Waves * 64), st, ev, P, B, S);
+  const dim3 g(S.n_b), t(kStep3Waves * 64);
+  if (P.kv8) return P.fp8 ? launch_k(k_step3<true, true>, g, t, st, ev, P, B, S)
+                          : launch_k(k_step3<true, false>, g, t, st, ev, P, B, S);
+  return P.fp8 ? launch_k(k_step3<false, true>, g, t, st, ev, P, B, S)
+               : launch_k(k_step3<false, false>, g, t, st, ev, P, B, S);
 }
 
 hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hipStream_t st,
