@@ -247,9 +247,10 @@ __device__ __forceinline__ void part_a(const Pools& P, const ReqBatch& B, const 
 }
 
 // Ring of the three-launch form's part-A workgroups, which stream while the mixed
-// workgroups select.
+// workgroups select: 3 keys (2 in flight per wave) measured faster than 2, 4 or 5 on
+// the b32 workload.
 #ifndef HSA_SPLIT_A_RING
-#define HSA_SPLIT_A_RING 4
+#define HSA_SPLIT_A_RING 3
 #endif
 constexpr int kSplitARing = HSA_SPLIT_A_RING;
 
