@@ -423,13 +423,13 @@ struct ExtraKey {
 // together with them, so up to 32 partials cost one memory round trip. With
 // xk.k set, the softmax also takes that key (score q.k / sqrt(128), weight on v),
 // as one more partial of max s, sum 1 and accumulator v.
-template <class PartFn>
-__device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, const float* part_acc,
-                                               const float* part_ml, float* out_row,
-                                               ExtraKey xk = ExtraKey{nullptr, nullptr, nullptr, false}) {
-  const int lane = threadIdx.x & 63;
-  const float* accb = part_acc + h * kD + 2 * lane;
-  float xs = kNoMax, xvx = 0.f, xvy = 0.f;
+// The extra key of a merge for head h, lane l (dims 2l, 2l+1): its score xs (log2
+// units, the same in every lane of the wave) and its V values; xs = kNoMax and zeros
+// without one.
+__device__ __forceinline__ void extra_key_lane(const ExtraKey& xk, int h, int lane, float& xs, float& xvx,
+                                               float& xvy) {
+  xs = kNoMax;
+  xvx = xvy = 0.f;
   if (xk.k) {
     const int o = h * kD + 2 * lane;
     const uint32_t qw = *reinterpret_cast<const uint32_t*>(xk.q + o);
@@ -455,6 +455,16 @@ __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, con
     }
     xs = wave_sum(fmaf(bf_lo(qw), k0, bf_hi(qw) * k1)) * kQScale;
   }
+}
+
+template <class PartFn>
+__device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, const float* part_acc,
+                                               const float* part_ml, float* out_row,
+                                               ExtraKey xk = ExtraKey{nullptr, nullptr, nullptr, false}) {
+  const int lane = threadIdx.x & 63;
+  const float* accb = part_acc + h * kD + 2 * lane;
+  float xs, xvx, xvy;
+  extra_key_lane(xk, h, lane, xs, xvx, xvy);
   float ox = 0.f, oy = 0.f;
   if (n <= 64) {
     float2 a[32];
@@ -532,6 +542,84 @@ __device__ __forceinline__ void merge_partials(PartFn part_of, int n, int h, con
     }
   }
   *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(ox, oy);
+}
+
+// merge_partials for one head h of a request by a workgroup of WAVES waves, for
+// requests with many partials: wave w takes partials w, w + WAVES, w + 2 WAVES, ...,
+// 32 at a time (their max, sum and row loaded together, one memory round trip),
+// keeping a running max, sum and unnormalised row; wave 0 combines the waves' states
+// from LDS and writes dims 2l, 2l+1 in lane l. Same extra key as merge_partials.
+template <int WAVES>
+struct MergeShared {
+  float m[WAVES];
+  float s[WAVES];
+  float o[WAVES][kD];
+};
+
+template <int WAVES, class PartFn>
+__device__ __forceinline__ void merge_partials_split(PartFn part_of, int n, int h, const float* part_acc,
+                                                     const float* part_ml, float* out_row, ExtraKey xk,
+                                                     MergeShared<WAVES>& sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const float* accb = part_acc + h * kD + 2 * lane;
+  const int nw = wave < n ? (n - wave + WAVES - 1) / WAVES : 0;   // partials wave + WAVES c, c < nw
+  float M = kNoMax, S = 0.f, ox = 0.f, oy = 0.f;
+  for (int g = 0; g < nw; g += 32) {
+    float2 a[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      if (g + c < nw) a[c] = *reinterpret_cast<const float2*>(accb + part_of(wave + WAVES * (g + c)) * kRow);
+    const int cl = g + (lane & 31);
+    const bool mine = lane < 32 && cl < nw;
+    float mm = kNoMax, ll = 0.f;
+    if (mine) {
+      const int64_t p = part_of(wave + WAVES * cl);
+      mm = part_ml[p * 2 * kH + h];
+      ll = part_ml[p * 2 * kH + kH + h];
+    }
+    float Mg = fmaxf(mm, __shfl_xor(mm, 32));
+    Mg = fmaxf(Mg, __shfl_xor(Mg, 16));
+    const float Mn = fmaxf(M, row_max16(Mg));
+    const float sc = exp2f(M - Mn);
+    const float w = mine ? exp2f(mm - Mn) : 0.f;
+    S = fmaf(S, sc, wave_sum(w * ll));
+    ox *= sc;
+    oy *= sc;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      if (g + c < nw) {
+        const float wc = __shfl(w, c);
+        ox = fmaf(wc, a[c].x, ox);
+        oy = fmaf(wc, a[c].y, oy);
+      }
+    }
+    M = Mn;
+  }
+  sh.o[wave][2 * lane] = ox;
+  sh.o[wave][2 * lane + 1] = oy;
+  if (lane == 0) {
+    sh.m[wave] = M;
+    sh.s[wave] = S;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float xs, xvx, xvy;
+  extra_key_lane(xk, h, lane, xs, xvx, xvy);
+  float Mx = xs;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) Mx = fmaxf(Mx, sh.m[v]);
+  const float xw = xk.k ? exp2f(xs - Mx) : 0.f;
+  float L = xw, rx = xw * xvx, ry = xw * xvy;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    const float e = exp2f(sh.m[v] - Mx);
+    L = fmaf(e, sh.s[v], L);
+    rx = fmaf(e, sh.o[v][2 * lane], rx);
+    ry = fmaf(e, sh.o[v][2 * lane + 1], ry);
+  }
+  const float inv = 1.f / L;
+  *reinterpret_cast<float2*>(out_row + h * kD + 2 * lane) = make_float2(rx * inv, ry * inv);
 }
 
 // Sum and max over each half of a wave (lanes 0-31, 32-63); every lane gets its half's.

@@ -457,17 +457,18 @@ __global__ __launch_bounds__(512) void k_step4(Pools P, ReqBatch B, StepArgs S) 
 }
 
 // S4 when some request has more than 32 partials (few long requests over the whole
-// GPU): four workgroups per request, one head per wave, so that the partials' rows
-// are loaded by 16 waves per request instead of one workgroup's passes.
-__global__ __launch_bounds__(256) void k_step4_heads(Pools P, ReqBatch B, StepArgs S) {
-  const int r = blockIdx.x >> 2;
+// GPU): one 8-wave workgroup per (request, head), each wave merging every eighth
+// partial (32 in one memory round trip), the waves' states combined in LDS.
+__global__ __launch_bounds__(512) void k_step4_heads(Pools P, ReqBatch B, StepArgs S) {
+  __shared__ MergeShared<8> sh;
+  const int r = blockIdx.x >> 4;
+  const int h = blockIdx.x & (kH - 1);
   const int fa = S.first_a[r], ca = S.first_a[r + 1] - fa;
   const int fb = S.first_b[r], cb = S.first_b[r + 1] - fb;
-  const int h = 4 * (blockIdx.x & 3) + (threadIdx.x >> 6);
   const Req R = B.r[r];
   ExtraKey xk{nullptr, nullptr, nullptr, false};
-  if (S.a_only && (blockIdx.x & 3) == 0)   // no C4 entries: the top-k row is padding
-    for (int i = threadIdx.x; i < S.k; i += 256) {
+  if (S.a_only && h == 0)   // no C4 entries: the top-k row is padding
+    for (int i = threadIdx.x; i < S.k; i += 512) {
       S.topk[(int64_t)r * S.k + i] = -1;
       if (S.score_out) S.score_out[(int64_t)r * S.k + i] = -INFINITY;
     }
@@ -475,8 +476,8 @@ __global__ __launch_bounds__(256) void k_step4_heads(Pools P, ReqBatch B, StepAr
     const C4Addr c = hca_addr(P, R.aux);
     xk = ExtraKey{c.k, c.v, S.q + (int64_t)r * kRow, P.kv8 != 0};
   }
-  merge_partials([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
-                 h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow, xk);
+  merge_partials_split<8>([&](int j) { return (int64_t)(j < ca ? fa + j : S.n_a + fb + (j - ca)); }, ca + cb,
+                          h, S.part_acc, S.part_ml, S.out + (int64_t)r * kRow, xk, sh);
 }
 
 }  // namespace
@@ -529,7 +530,7 @@ hipError_t launch_step4(const Pools& P, const ReqBatch& B, const StepArgs& S, hi
   int parts = 0;   // the most partials of one request
   for (int i = 0; i < B.n; ++i)
     parts = std::max(parts, S.first_a[i + 1] - S.first_a[i] + S.first_b[i + 1] - S.first_b[i]);
-  if (parts > 32) return launch_k(k_step4_heads, dim3(4 * B.n), dim3(256), st, ev, P, B, S);
+  if (parts > 32) return launch_k(k_step4_heads, dim3(kH * B.n), dim3(512), st, ev, P, B, S);
   return launch_k(k_step4, dim3(B.n), dim3(512), st, ev, P, B, S);
 }
 
