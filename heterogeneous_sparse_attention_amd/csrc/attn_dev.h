@@ -53,9 +53,10 @@ __device__ __forceinline__ const uint16_t* lane_ptr(uint64_t p, int i) {
 
 // Keys in the load ring of a wave: RING - 1 keys stay in flight while one is
 // consumed. 5 keys fit the 512 VGPRs of a wave that has a SIMD to itself (4-wave
-// workgroups); 8-wave workgroups (two waves per SIMD, 256 VGPRs each) take 4.
+// workgroups); 8-wave workgroups (two waves per SIMD, 256 VGPRs each) take 3, as 4
+// would spill.
 template <int WAVES>
-constexpr int ring_depth() { return WAVES > 4 ? 4 : 5; }
+constexpr int ring_depth() { return WAVES > 4 ? 3 : 5; }
 
 // Ring of the three-launch decode step's attention (8 waves, one workgroup per CU):
 // one key in flight per wave while another is consumed. On the b32 workload this
@@ -158,40 +159,61 @@ __device__ __forceinline__ void compute_key(const KeyRegs& R, bool ok, const uin
   }
 }
 
-// The loads of keys [x0, x0 + RING - 1) of the current 64-key group into the ring
-// (lane x of kp / vp holds key x's rows; dummy rows from x1 on).
+// The loads of keys [x0, min(x0 + RING - 1, x1)) of the current 64-key group into
+// ring slots 0, 1, ... (lane x of kp / vp holds key x's rows).
 template <int RING, bool F8>
 __device__ __forceinline__ void ring_fill(KeyRegs (&ring)[RING], int x0, int x1, uint64_t kp, uint64_t vp,
-                                          const uint16_t* dummy_k, const uint16_t* dummy_v, int lane) {
+                                          int lane) {
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u) {
-    const int x = x0 + u;
-    const bool live = x < x1;
-    const int j = live ? x : 0;
-    load_key<F8>(ring[u], live ? lane_ptr(kp, j) : dummy_k, live ? lane_ptr(vp, j) : dummy_v, lane);
-  }
+  for (int u = 0; u < RING - 1; ++u)
+    if (x0 + u < x1) load_key<F8>(ring[u], lane_ptr(kp, x0 + u), lane_ptr(vp, x0 + u), lane);
 }
 
 // Keys [x0, x1) of the current 64-key group through the ring: on entry slot u holds
 // key x0 + u (RING - 1 of them in flight); each step issues the loads of the key
-// RING - 1 ahead, a dummy row from x1 on, and consumes one. Issuing on every path
-// keeps the number of loads behind each key the same, so the wait for a key leaves
-// the next RING - 1 keys in flight.
+// RING - 1 ahead and consumes one. A load issued on some paths only would make the
+// compiler's wait for a key also wait for the loads behind it, so the steps issue
+// one load each on every path: a 2-key ring loads a dummy row (dummy_k / dummy_v,
+// valid rows of at least 4 KiB) past x1, one key's cost per run; deeper rings run
+// unconditional passes while keys remain for every step of a pass, and only their
+// last one or two passes load conditionally (a dummy per slot would cost more than
+// the short waits it saves on runs of a few keys).
 template <int RING, bool F8>
 __device__ __forceinline__ void ring_run(KeyRegs (&ring)[RING], int x0, int x1, uint64_t kp, uint64_t vp,
                                          const uint16_t* dummy_k, const uint16_t* dummy_v, uint64_t okmask,
                                          const uint4* qw, float* m, float* l, float (*acc)[8], int lane) {
-  for (int i = x0; i < x1; i += RING) {
+  int i = x0;
+  if constexpr (RING == 2) {
+    for (; i < x1; i += 2) {
 #pragma unroll
-    for (int u = 0; u < RING; ++u) {
-      const int x = i + u;
-      if (x >= x1) break;
-      const int xn = x + RING - 1;
-      const bool live = xn < x1;
-      const int j = live ? xn : 0;
-      load_key<F8>(ring[(u + RING - 1) % RING], live ? lane_ptr(kp, j) : dummy_k,
-                   live ? lane_ptr(vp, j) : dummy_v, lane);
-      compute_key<F8>(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+      for (int u = 0; u < 2; ++u) {
+        const int x = i + u;
+        if (x >= x1) break;
+        const bool live = x + 1 < x1;
+        const int j = live ? x + 1 : 0;
+        load_key<F8>(ring[(u + 1) % 2], live ? lane_ptr(kp, j) : dummy_k, live ? lane_ptr(vp, j) : dummy_v, lane);
+        compute_key<F8>(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+      }
+    }
+  } else {
+    for (; i + 2 * RING - 2 < x1; i += RING) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        const int x = i + u;
+        load_key<F8>(ring[(u + RING - 1) % RING], lane_ptr(kp, x + RING - 1), lane_ptr(vp, x + RING - 1), lane);
+        compute_key<F8>(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+      }
+    }
+    for (; i < x1; i += RING) {
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
+        const int x = i + u;
+        if (x >= x1) break;
+        if (x + RING - 1 < x1)
+          load_key<F8>(ring[(u + RING - 1) % RING], lane_ptr(kp, x + RING - 1), lane_ptr(vp, x + RING - 1),
+                       lane);
+        compute_key<F8>(ring[u], (okmask >> x) & 1ull, qw, m, l, acc);
+      }
     }
   }
 }
@@ -201,19 +223,19 @@ __device__ __forceinline__ void ring_run(KeyRegs (&ring)[RING], int x0, int x1, 
 template <int RING, bool F8LO, bool F8HI>
 __device__ __forceinline__ void ring_runs(KeyRegs (&ring)[RING], int x0, int x1, int split, uint64_t kp,
                                           uint64_t vp, const uint16_t* dummy_k, const uint16_t* dummy_v,
-                                          uint64_t okmask, const uint4* qw, float* m, float* l,
-                                          float (*acc)[8], int lane) {
+                                          uint64_t okmask, const uint4* qw, float* m, float* l, float (*acc)[8],
+                                          int lane) {
   if constexpr (F8LO == F8HI) {
-    ring_fill<RING, F8LO>(ring, x0, x1, kp, vp, dummy_k, dummy_v, lane);
+    ring_fill<RING, F8LO>(ring, x0, x1, kp, vp, lane);
     ring_run<RING, F8LO>(ring, x0, x1, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
   } else {
     const int s = min(max(split, x0), x1);
     if (x0 < s) {
-      ring_fill<RING, F8LO>(ring, x0, s, kp, vp, dummy_k, dummy_v, lane);
+      ring_fill<RING, F8LO>(ring, x0, s, kp, vp, lane);
       ring_run<RING, F8LO>(ring, x0, s, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
     }
     if (s < x1) {
-      ring_fill<RING, F8HI>(ring, s, x1, kp, vp, dummy_k, dummy_v, lane);
+      ring_fill<RING, F8HI>(ring, s, x1, kp, vp, lane);
       ring_run<RING, F8HI>(ring, s, x1, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
     }
   }
@@ -295,8 +317,8 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
     const uint64_t okmask = __ballot(okl);
     const uint64_t kp = reinterpret_cast<uint64_t>(okl ? a.k : dummy_k);
     const uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
-    ring_runs<RING, F8LO, F8HI>(ring, 0, min(64, w1 - g), split - g, kp, vp, dummy_k, dummy_v, okmask, qw, m,
-                                l, acc, lane);
+    ring_runs<RING, F8LO, F8HI>(ring, 0, min(64, w1 - g), split - g, kp, vp, dummy_k, dummy_v, okmask, qw, m, l,
+                                acc, lane);
   }
   merge_waves<WAVES>(m, l, acc, sh, M, L, A8);
 }
@@ -307,10 +329,9 @@ __device__ __forceinline__ void attend_keys(KeyFn key_of, int x0, int x1, const 
 // w + 2 WAVES, ... of it, so no wave has more than one key above the average, and
 // every wave's A keys come first. The addresses of the B keys are known only after
 // mid(), work that every wave of the workgroup runs once (it may hold barriers and
-// must issue no global load). The loads of each wave's first RING - 1 keys (its A
-// keys among them, dummy rows for the others) are issued before mid(), so they
-// arrive while mid() runs; pre() runs just before (work that should wait for earlier
-// loads first). key_a / key_b return the rows of a key (an FP8 key: its code and
+// must issue no global load). The loads of the A keys among each wave's first
+// RING - 1 keys are issued before mid(), so they arrive while mid() runs; pre() runs
+// just before (work that should wait for earlier loads first). key_a / key_b return the rows of a key (an FP8 key: its code and
 // scale rows) or nullptrs for a skipped slot; dummy_k / dummy_v are valid rows (at
 // least 4 KiB) read in their place. Result as attend_keys.
 template <int WAVES, int RING, bool F8A, bool F8B, class KeyA, class KeyB, class Pre, class Mid>
@@ -340,8 +361,8 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   }
   auto key_j = [&](int j) { return j < na ? key_a(a0 + pos(j)) : key_b(b0 + pos(j) - nA); };
 
-  // group 0: A addresses, then the prefetch of keys [0, RING - 1) (dummy rows past
-  // the wave's A keys)
+  // group 0: A addresses, then the prefetch of the wave's A keys among keys
+  // [0, RING - 1)
   const int n0 = min(64, n);
   const int na0 = min(na, n0);
   KeyAddr a;
@@ -352,7 +373,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   uint64_t vp = reinterpret_cast<uint64_t>(okl ? a.v : dummy_v);
   KeyRegs ring[RING];
   pre();
-  ring_fill<RING, F8A>(ring, 0, na0, kp, vp, dummy_k, dummy_v, lane);
+  ring_fill<RING, F8A>(ring, 0, na0, kp, vp, lane);
   mid();
   if (lane < n0 && lane >= na) {
     a = key_b(b0 + pos(lane) - nA);
@@ -362,7 +383,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   }
   uint64_t okmask = __ballot(okl);
   if constexpr (F8A == F8B) {
-    // the prefetched slots that held dummies take their B keys
+    // the ring's first slots past the A keys take their B keys
 #pragma unroll
     for (int u = 0; u < RING - 1; ++u)
       if (u >= na0 && u < n0) load_key<F8B>(ring[u], lane_ptr(kp, u), lane_ptr(vp, u), lane);
@@ -370,7 +391,7 @@ __device__ __forceinline__ void attend_two(KeyA key_a, int a0, int a1, KeyB key_
   } else {
     if (na0 > 0) ring_run<RING, F8A>(ring, 0, na0, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
     if (na0 < n0) {
-      ring_fill<RING, F8B>(ring, na0, n0, kp, vp, dummy_k, dummy_v, lane);
+      ring_fill<RING, F8B>(ring, na0, n0, kp, vp, lane);
       ring_run<RING, F8B>(ring, na0, n0, kp, vp, dummy_k, dummy_v, okmask, qw, m, l, acc, lane);
     }
   }
