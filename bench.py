@@ -178,6 +178,18 @@ def layer_step_bytes(L_after, nb, n_win, k, sealed, entries, index, layer, kv="b
     return out
 
 
+def storage_formats(args):
+    """(C4 entry, indexer key, KV) storage formats of a run."""
+    return (getattr(args, "entries", "bf16"), getattr(args, "index", "f32"), getattr(args, "kv", "bf16"))
+
+
+def traffic_key(workload: str, args) -> str:
+    """traffic.json key of a workload's counters: the workload name, with the storage
+    formats appended when they are not the default ones (b32:fp8-mxfp4-fp8)."""
+    fmt = storage_formats(args)
+    return workload if fmt == ("bf16", "f32", "bf16") else workload + ":" + "-".join(fmt)
+
+
 def counted_traffic(kernel: str, workload: str, args):
     """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.json (scaled
     rocprofv3 FETCH_SIZE + WRITE_SIZE), or None when the counters were taken on other
@@ -186,11 +198,10 @@ def counted_traffic(kernel: str, workload: str, args):
         tr = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    ent = tr.get("kernels", {}).get(workload, {}).get(KERNEL_SYMBOL[kernel])
+    ent = tr.get("kernels", {}).get(traffic_key(workload, args), {}).get(KERNEL_SYMBOL[kernel])
     if not ent or ent.get("src_sha") != src_hash(kernel):
         return None
-    fmt = (getattr(args, "entries", "bf16"), getattr(args, "index", "f32"), getattr(args, "kv", "bf16"))
-    if (ent.get("entries", "bf16"), ent.get("index", "f32"), ent.get("kv", "bf16")) != fmt:
+    if (ent.get("entries", "bf16"), ent.get("index", "f32"), ent.get("kv", "bf16")) != storage_formats(args):
         return None
     if ent.get("env", "") != launch_env():
         return None
@@ -890,7 +901,9 @@ def summarize_counters(args):
     out["calibration"] = cal
     sf, sw = cal.get("fetch_scale"), cal.get("write_scale")
     wl_out = out.setdefault("kernels", {})
-    wl_out[args.counters_workload] = {}
+    key = traffic_key(args.counters_workload, args)   # the counter runs' formats: --entries/--index/--kv
+    entries, index, kv = storage_formats(args)
+    wl_out[key] = {}
     for name, sym in KERNEL_SYMBOL.items():
         # the symbol, possibly with template arguments (k_step1<false>(...))
         hit = lambda n, s=sym: (s + "(") in n or (s + "<") in n
@@ -899,10 +912,10 @@ def summarize_counters(args):
         if not nf:
             continue
         ent = {"fetch_kib": f, "write_kib": w, "dispatches": nf, "src_sha": src_hash(name),
-               "entries": "bf16", "index": "f32", "kv": "bf16", "env": launch_env()}
+               "entries": entries, "index": index, "kv": kv, "env": launch_env()}
         if sf and sw and f is not None and w is not None:
             ent["traffic_bytes_per_launch"] = f * 1024 * sf + w * 1024 * sw
-        wl_out[args.counters_workload][sym] = ent
+        wl_out[key][sym] = ent
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))
