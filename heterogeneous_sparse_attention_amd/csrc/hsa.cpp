@@ -922,16 +922,17 @@ hsa_status hsa_create(const hsa_config* cfg, int device, hsa_ctx** out) {
 
 hsa_status hsa_destroy(hsa_ctx* c) {
   if (!c) return kOk;
-  hipSetDevice(c->device);
-  hipDeviceSynchronize();
-  for (void* p : c->allocs) hipFree(p);
-  if (c->plan_host) hipHostFree(c->plan_host);
-  if (c->plan_ev) hipEventDestroy(c->plan_ev);
+  // teardown releases what it can: an error here leaves nothing to undo
+  (void)hipSetDevice(c->device);
+  (void)hipDeviceSynchronize();
+  for (void* p : c->allocs) (void)hipFree(p);
+  if (c->plan_host) (void)hipHostFree(c->plan_host);
+  if (c->plan_ev) (void)hipEventDestroy(c->plan_ev);
   for (auto& r : c->recs) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
-  for (hipEvent_t e : c->ev_free) hipEventDestroy(e);
+  for (hipEvent_t e : c->ev_free) (void)hipEventDestroy(e);
   delete c;
   return kOk;
 }

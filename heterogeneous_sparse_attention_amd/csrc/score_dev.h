@@ -210,48 +210,6 @@ __device__ __forceinline__ void for_each_key(int N, const float* S, F f) {
   }
 }
 
-// Round 1 of the top-k (see SelPlan), workgroup `bid`: the whole selection of an
-// unsliced row, or one slice.
-template <int NT>
-__device__ __forceinline__ void select_round1(int bid, int n_req, const Req* reqs, const SelPlan& SP,
-                                              int32_t k, int32_t sorted, const float* scores,
-                                              int64_t ld, int32_t* topk, float* score_out,
-                                              SelShared& sh, const int32_t* table, int64_t stride,
-                                              int32_t* rows) {
-  const int r = owner_of(SP.first, n_req, bid);
-  const int g = bid - SP.first[r];
-  const int G = SP.first[r + 1] - SP.first[r];
-  const Req R = reqs[r];
-  const int N = c4_rowlen(1, SP.eager, R);
-  const float* S = scores + (int64_t)r * ld;
-  if (G == 1) {
-    select_run<NT>(N, k, sorted, S, topk + (int64_t)r * k, score_out ? score_out + (int64_t)r * k : nullptr,
-                   sh, table ? table + (int64_t)R.state * stride : nullptr,
-                   rows ? rows + (int64_t)r * k : nullptr, N / kC4, 0, nullptr, c4_cands(1, SP.eager, R));
-    return;
-  }
-  const int base = g * SP.slice;
-  const int64_t c0 = ((int64_t)r * SP.gmax + g) * SP.k1;
-  select_run<NT>(min(SP.slice, N - base), SP.k1, 0, S + base, SP.cand_ord + c0, SP.cand_score + c0, sh,
-                 nullptr, nullptr, 0, base);
-}
-
-// Round 2 for request `r` (no-op for an unsliced row).
-template <int NT>
-__device__ __forceinline__ void select_round2(int r, const Req* reqs, const SelPlan& SP, int32_t k,
-                                              int32_t sorted, int32_t* topk, float* score_out,
-                                              SelShared& sh, const int32_t* table, int64_t stride,
-                                              int32_t* rows) {
-  const int G = SP.first[r + 1] - SP.first[r];
-  if (G == 1) return;
-  const Req R = reqs[r];
-  const int64_t c0 = (int64_t)r * SP.gmax * SP.k1;
-  select_run<NT>(G * SP.k1, k, sorted, SP.cand_score + c0, topk + (int64_t)r * k,
-                 score_out ? score_out + (int64_t)r * k : nullptr, sh,
-                 table ? table + (int64_t)R.state * stride : nullptr, rows ? rows + (int64_t)r * k : nullptr,
-                 c4_rowlen(1, SP.eager, R) / kC4, 0, SP.cand_ord + c0, c4_cands(1, SP.eager, R));
-}
-
 // Exclusive prefix sum over the wave's lanes, and the wave total in `total`.
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
   const int lane = threadIdx.x & 63;
@@ -513,6 +471,49 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
     io[i] = -1;
     if (so) so[i] = -INFINITY;
   }
+}
+
+
+// Round 1 of the top-k (see SelPlan), workgroup `bid`: the whole selection of an
+// unsliced row, or one slice.
+template <int NT>
+__device__ __forceinline__ void select_round1(int bid, int n_req, const Req* reqs, const SelPlan& SP,
+                                              int32_t k, int32_t sorted, const float* scores,
+                                              int64_t ld, int32_t* topk, float* score_out,
+                                              SelShared& sh, const int32_t* table, int64_t stride,
+                                              int32_t* rows) {
+  const int r = owner_of(SP.first, n_req, bid);
+  const int g = bid - SP.first[r];
+  const int G = SP.first[r + 1] - SP.first[r];
+  const Req R = reqs[r];
+  const int N = c4_rowlen(1, SP.eager, R);
+  const float* S = scores + (int64_t)r * ld;
+  if (G == 1) {
+    select_run<NT>(N, k, sorted, S, topk + (int64_t)r * k, score_out ? score_out + (int64_t)r * k : nullptr,
+                   sh, table ? table + (int64_t)R.state * stride : nullptr,
+                   rows ? rows + (int64_t)r * k : nullptr, N / kC4, 0, nullptr, c4_cands(1, SP.eager, R));
+    return;
+  }
+  const int base = g * SP.slice;
+  const int64_t c0 = ((int64_t)r * SP.gmax + g) * SP.k1;
+  select_run<NT>(min(SP.slice, N - base), SP.k1, 0, S + base, SP.cand_ord + c0, SP.cand_score + c0, sh,
+                 nullptr, nullptr, 0, base);
+}
+
+// Round 2 for request `r` (no-op for an unsliced row).
+template <int NT>
+__device__ __forceinline__ void select_round2(int r, const Req* reqs, const SelPlan& SP, int32_t k,
+                                              int32_t sorted, int32_t* topk, float* score_out,
+                                              SelShared& sh, const int32_t* table, int64_t stride,
+                                              int32_t* rows) {
+  const int G = SP.first[r + 1] - SP.first[r];
+  if (G == 1) return;
+  const Req R = reqs[r];
+  const int64_t c0 = (int64_t)r * SP.gmax * SP.k1;
+  select_run<NT>(G * SP.k1, k, sorted, SP.cand_score + c0, topk + (int64_t)r * k,
+                 score_out ? score_out + (int64_t)r * k : nullptr, sh,
+                 table ? table + (int64_t)R.state * stride : nullptr, rows ? rows + (int64_t)r * k : nullptr,
+                 c4_rowlen(1, SP.eager, R) / kC4, 0, SP.cand_ord + c0, c4_cands(1, SP.eager, R));
 }
 
 
