@@ -103,10 +103,14 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
 }
 
 
+// MXFP4 sealed blocks whose loads a scoring workgroup issues together (the most
+// that keeps the 4-workgroup instances of k_step1 free of spills).
+constexpr int kMxPass = 3;
+
 // Indexer scores of scoring unit `unit` with MXFP4 keys: sealed blocks
-// [u G, u G + G) of one request (G = S.mx_unit), two blocks' loads in flight at a
-// time; a block sealed in this step (the request's last) is scored from the fp32
-// tail and the input, quantised as the seal stores it.
+// [u G, u G + G) of one request (G = S.mx_unit), kMxPass blocks' loads in flight
+// at a time; a block sealed in this step (the request's last) is scored from the
+// fp32 tail and the input, quantised as the seal stores it.
 __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B, const StepArgs& S,
                                               int unit) {
   const int r = owner_of(S.first_s, B.n, unit);
@@ -120,29 +124,37 @@ __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B,
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int b = lane & 7;
-  float q[32];
-  mx_load_q(qrow, b, q);
 #pragma unroll 1
-  for (int p = 0; lb0 + p < lbs; p += 2) {
-    uint4 w[2][4];
-    int e[2][4];
-    bool ok[2];
+  for (int p = 0; lb0 + p < lbs; p += kMxPass) {
+    uint4 w[kMxPass][4];
+    int e[kMxPass][4];
+    bool ok[kMxPass];
+    // Every load is unconditional: a slot past the stored blocks reads the pass's
+    // last stored block again, an invalid id (never written) block 0. A load inside
+    // a branch makes the compiler wait for every load in flight where the branch
+    // joins, which would serialise the pass into one round trip per load.
+    int32_t ids[kMxPass];   // all of the pass's ids first: one round trip, not one per block
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kMxPass; ++j) ids[j] = tab[min(lb0 + p + j, lbs - 1)];
+#pragma unroll
+    for (int j = 0; j < kMxPass; ++j) {
       const int lb = lb0 + p + j;
-      const int32_t id = lb < lbs ? tab[lb] : -1;
-      ok[j] = id >= 0 && id < P.max_blocks;   // false past the stored blocks (bad ids never occur)
-      const int64_t kr = (int64_t)(ok[j] ? id : 0) * kBlk;
+      const int32_t id = ids[j];
+      const bool valid = id >= 0 && id < P.max_blocks;
+      ok[j] = lb < lbs && valid;
+      const int64_t kr = (int64_t)(valid ? id : 0) * kBlk;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t t = kr + (wave * 4 + g) * 8 + (lane >> 3);
-        w[j][g] = ok[j] ? load_stream(reinterpret_cast<const uint4*>(P.idx_q + t * kIRowQ) + b)
-                        : make_uint4(0u, 0u, 0u, 0u);
-        e[j][g] = ok[j] ? (int)P.idx_e[t * kIRowE + b] : 127;
+        w[j][g] = load_stream(reinterpret_cast<const uint4*>(P.idx_q + t * kIRowQ) + b);
+        e[j][g] = (int)P.idx_e[t * kIRowE + b];
       }
     }
+    // the query after the keys (read again each pass), so its round trip overlaps theirs
+    float q[32];
+    mx_load_q(qrow, b, q);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kMxPass; ++j) {
       const int lb = lb0 + p + j;
       if (lb >= lbs) continue;
       float* o = out + kC4 * (p + j);
@@ -193,12 +205,14 @@ __global__ __launch_bounds__(256, FP8 || KV8 ? 3 : 4) void k_step1(Pools P, ReqB
   }
   bid -= B.n_open;
   // -- indexer scores, one workgroup per unit (a 1/kScoreSplit block of fp32 keys,
-  //    or S.mx_unit blocks of MXFP4 keys)
-  if (bid < S.n_score) {
-    if (P.mx4)
-      score_unit_mx(P, B, S, bid);
-    else
-      score_unit(P, B, S, bid);
+  //    or S.mx_unit blocks of MXFP4 keys); a layer without C4 entries scores nothing
+  if constexpr (C4) {
+    if (bid < S.n_score) {
+      if (P.mx4)
+        score_unit_mx(P, B, S, bid);
+      else
+        score_unit(P, B, S, bid);
+    }
   }
 }
 
