@@ -61,8 +61,7 @@ __global__ __launch_bounds__(256) void k_bulk_seal(Pools P, const SealDesc* seal
   src.in_v = vin ? vin + row0 * kRow : nullptr;
   src.in_i = iin ? iin + row0 * kIRow : nullptr;
   src.len_old = d.len_old;
-  src.pos0 = d.pos0;
-  src.n_win = P.n_win;
+  src.at_block(d.pos0, P.n_win);
   float M = -INFINITY, L = 0.f, K8[8] = {}, V8[8] = {};
   for (int sub = 0; sub < kSealSplit; ++sub) {
     float m, l, acck[8], accv[8];

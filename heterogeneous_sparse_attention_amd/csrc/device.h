@@ -49,6 +49,8 @@ constexpr int kMxBlk = 32;              // MXFP4 indexer keys: values per shared
 constexpr int kIRowQ = kIRow / 2;       // MXFP4 indexer key: 128 bytes of E2M1 codes
 constexpr int kIRowE = kIRow / kMxBlk;  // MXFP4 indexer key: 8 E8M0 scale bytes
 constexpr int kMxUnitMax = 8;           // MXFP4 keys: at most 8 sealed blocks (136 KiB) per scoring workgroup
+constexpr int kMxPass = 3;              // MXFP4 keys: sealed blocks whose loads a scoring pass issues together
+                                        // (the most that keeps the 4-workgroup k_step1 instances free of spills)
 
 // Decode-step scoring workgroups of a request with nb sealed blocks: kScoreSplit per
 // block of fp32 keys (64 KiB each, mx_unit 0), or one per mx_unit blocks of MXFP4

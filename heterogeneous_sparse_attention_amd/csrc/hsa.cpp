@@ -453,15 +453,11 @@ void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32
   for (int i = 0; i < n; ++i)
     fused = fused && h_rowlen(c->P, plan.reqs[b0 + i].len_new, plan.reqs[b0 + i].nb_new) <= kCacheN;
   std::vector<int64_t> na(n), nb(n);
-  int64_t maxnb = 0, n_score = 0, all_nb = 0;
-  for (int i = 0; i < n; ++i) all_nb += plan.reqs[b0 + i].nb_new;
-  // MXFP4 keys: as many blocks per scoring workgroup as leave about two workgroups
-  // per attention slot (more blocks per workgroup hide latency; fewer spread a
-  // small batch over the chip)
-  const int mx_unit = !c->P.mx4 ? 0
-                      : c->mx_unit ? c->mx_unit
-                                   : (int)std::max<int64_t>(1, std::min<int64_t>(kMxUnitMax,
-                                                                (all_nb + 2 * c->step_slots - 1) / (2 * c->step_slots)));
+  int64_t maxnb = 0, n_score = 0;
+  // MXFP4 keys: one scoring pass per workgroup (kMxPass blocks, whose loads a
+  // workgroup issues together); units of two passes or of a partial pass measured
+  // slower on both small and large batches
+  const int mx_unit = !c->P.mx4 ? 0 : c->mx_unit ? c->mx_unit : kMxPass;
   for (int i = 0; i < n; ++i) {
     const AppendReq& r = plan.reqs[b0 + i];
     const int32_t id = new_id[b0 + i];

@@ -34,24 +34,31 @@ struct TokSrc {
   const uint16_t* in_v;
   const float* in_i;
   int64_t pos0, len_old;
-  int32_t n_win;
+  int32_t slot0;   // ring slot of position pos0
 
+  // pos0 is a block start and n_win a multiple of 128, so slot0 is a multiple of 128
+  // and token t's ring slot slot0 + t (tail slot t) needs no division: a 64-bit
+  // modulo per token would put each token's loads in a block of its own
+  __device__ __forceinline__ void at_block(int64_t p0, int32_t n_win) {
+    pos0 = p0;
+    slot0 = (int32_t)(p0 % n_win);
+  }
   __device__ __forceinline__ bool resident(int t) const { return pos0 + t < len_old; }
   __device__ __forceinline__ const uint16_t* k(int t) const {
     const int64_t p = pos0 + t;
-    return p < len_old ? ring_k + (p % n_win) * kRow : in_k + (p - len_old) * kRow;
+    return p < len_old ? ring_k + (int64_t)(slot0 + t) * kRow : in_k + (p - len_old) * kRow;
   }
   __device__ __forceinline__ const uint16_t* v(int t) const {
     const int64_t p = pos0 + t;
-    return p < len_old ? ring_v + (p % n_win) * kRow : in_v + (p - len_old) * kRow;
+    return p < len_old ? ring_v + (int64_t)(slot0 + t) * kRow : in_v + (p - len_old) * kRow;
   }
   __device__ __forceinline__ const float* i(int t) const {
     const int64_t p = pos0 + t;
-    return p < len_old ? tail_i + (p % kBlk) * kIRow : in_i + (p - len_old) * kIRow;
+    return p < len_old ? tail_i + (int64_t)t * kIRow : in_i + (p - len_old) * kIRow;
   }
   __device__ __forceinline__ const uint16_t* in_krow(int t) const { return in_k + (pos0 + t - len_old) * kRow; }
   __device__ __forceinline__ const uint16_t* in_vrow(int t) const { return in_v + (pos0 + t - len_old) * kRow; }
-  __device__ __forceinline__ int64_t slot(int t) const { return (pos0 + t) % n_win; }
+  __device__ __forceinline__ int64_t slot(int t) const { return slot0 + t; }
 };
 
 // This lane's 8 values (at off = 8 tid: head tid / 16) of token t's K and V, as the
@@ -59,6 +66,26 @@ struct TokSrc {
 // code values as exact bf16 pairs and the head's K and V scales (value = code *
 // scale); a token still in the input is quantised here exactly as the ring write
 // stores it (same lanes, same per-head maximum), so both give the same bits.
+__device__ __forceinline__ void load_ring_tok(const TokSrc& src, int t, int off, uint4& kw, uint4& vw,
+                                              float& sk, float& sv) {
+  const int h = threadIdx.x >> 4;
+  const int64_t g = src.slot(t);
+  const uint8_t* q = src.ring_q + g * kC4Bytes;
+  kw = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(q + off));
+  vw = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(q + kRow + off));
+  const float* sc = src.ring_s + g * kC4Scales;
+  sk = sc[4 * (h & 3) + (h >> 2)];
+  sv = sc[kH + 4 * (h & 3) + (h >> 2)];
+}
+__device__ __forceinline__ void load_input_tok(const TokSrc& src, int t, int off, uint4& kw, uint4& vw,
+                                               float& sk, float& sv) {
+  float f[8];
+  unpack8(*reinterpret_cast<const uint4*>(src.in_krow(t) + off), f);
+  kw = e4m3x8_to_bf16(quantize8_e4m3(f, sk));
+  unpack8(*reinterpret_cast<const uint4*>(src.in_vrow(t) + off), f);
+  vw = e4m3x8_to_bf16(quantize8_e4m3(f, sv));
+}
+
 template <bool KV8>
 __device__ __forceinline__ void load_tok(const TokSrc& src, int t, int off, uint4& kw, uint4& vw, float& sk,
                                          float& sv) {
@@ -67,21 +94,34 @@ __device__ __forceinline__ void load_tok(const TokSrc& src, int t, int off, uint
     vw = *reinterpret_cast<const uint4*>(src.v(t) + off);
     sk = sv = 1.f;
   } else {
-    const int h = threadIdx.x >> 4;
-    if (src.resident(t)) {   // workgroup-uniform
-      const int64_t g = src.slot(t);
-      const uint8_t* q = src.ring_q + g * kC4Bytes;
-      kw = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(q + off));
-      vw = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(q + kRow + off));
-      const float* sc = src.ring_s + g * kC4Scales;
-      sk = sc[4 * (h & 3) + (h >> 2)];
-      sv = sc[kH + 4 * (h & 3) + (h >> 2)];
+    if (src.resident(t))   // workgroup-uniform
+      load_ring_tok(src, t, off, kw, vw, sk, sv);
+    else
+      load_input_tok(src, t, off, kw, vw, sk, sv);
+  }
+}
+
+// The 4 tokens tb .. tb + 3 of a group. With FP8 KV, one uniform branch per group
+// (positions increase with t: the whole group in the ring, the whole group in the
+// input, or, once per block at most, split between them), so that the group's loads
+// are issued together: a load inside a per-token branch makes the compiler wait for
+// every load in flight where the branch joins.
+template <bool KV8>
+__device__ __forceinline__ void load_group(const TokSrc& src, int tb, int off, uint4* kw, uint4* vw, float* sk,
+                                           float* sv) {
+  if constexpr (!KV8) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_tok<false>(src, tb + u, off, kw[u], vw[u], sk[u], sv[u]);
+  } else {
+    if (src.resident(tb + 3)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_ring_tok(src, tb + u, off, kw[u], vw[u], sk[u], sv[u]);
+    } else if (!src.resident(tb)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_input_tok(src, tb + u, off, kw[u], vw[u], sk[u], sv[u]);
     } else {
-      float f[8];
-      unpack8(*reinterpret_cast<const uint4*>(src.in_krow(t) + off), f);
-      kw = e4m3x8_to_bf16(quantize8_e4m3(f, sk));
-      unpack8(*reinterpret_cast<const uint4*>(src.in_vrow(t) + off), f);
-      vw = e4m3x8_to_bf16(quantize8_e4m3(f, sv));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_tok<true>(src, tb + u, off, kw[u], vw[u], sk[u], sv[u]);
     }
   }
 }
@@ -211,8 +251,7 @@ __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int
     const int tb = t0 + 4 * g;
     uint4 kw[4], vw[4];
     float sk[4], sv[4];   // FP8 KV: the tokens' per-head scales (1 with bf16 KV)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) load_tok<KV8>(src, tb + u, off, kw[u], vw[u], sk[u], sv[u]);
+    load_group<KV8>(src, tb, off, kw, vw, sk, sv);
     // indexer keys of the 4 tokens: 4 x 64 float4, one per lane (stored as MXFP4
     // when P.mx4, a wave per key); layers without C4 entries keep none
     if constexpr (C4) {
@@ -381,8 +420,7 @@ __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i,
   src.in_v = vin + (int64_t)i * kRow;
   src.in_i = iin + (int64_t)i * kIRow;
   src.len_old = r.len - 1;
-  src.pos0 = (int64_t)(r.nb - 1) * kBlk;
-  src.n_win = P.n_win;
+  src.at_block((int64_t)(r.nb - 1) * kBlk, P.n_win);
   float m, l, acck[8], accv[8];
   seal_part<FP8, C4, KV8>(P, src, r.aux, sub * kSubTok, m, l, acck, accv);
   float* mine = part + (int64_t)(item * kSealSplit + sub) * kPartFloats;

@@ -103,10 +103,6 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
 }
 
 
-// MXFP4 sealed blocks whose loads a scoring workgroup issues together (the most
-// that keeps the 4-workgroup instances of k_step1 free of spills).
-constexpr int kMxPass = 3;
-
 // Indexer scores of scoring unit `unit` with MXFP4 keys: sealed blocks
 // [u G, u G + G) of one request (G = S.mx_unit), kMxPass blocks' loads in flight
 // at a time; a block sealed in this step (the request's last) is scored from the
