@@ -52,11 +52,16 @@ constexpr int kMxUnitMax = 8;           // MXFP4 keys: at most 8 sealed blocks (
 constexpr int kMxPass = 3;              // MXFP4 keys: sealed blocks whose loads a scoring pass issues together
                                         // (the most that keeps the 4-workgroup k_step1 instances free of spills)
 
+// MXFP4 keys: scoring workgroups of a block sealed within the step, whose keys are
+// quantised from the fp32 tail as they are scored (32 tokens each)
+constexpr int kMxRawSplit = 4;
+
 // Decode-step scoring workgroups of a request with nb sealed blocks: kScoreSplit per
-// block of fp32 keys (64 KiB each, mx_unit 0), or one per mx_unit blocks of MXFP4
-// keys (17 KiB each).
-__host__ __device__ inline int64_t score_units(int64_t nb, int mx_unit) {
-  return mx_unit > 0 ? (nb + mx_unit - 1) / mx_unit : (int64_t)kScoreSplit * nb;
+// block of fp32 keys (64 KiB each, mx_unit 0), or one per mx_unit stored blocks of
+// MXFP4 keys (17 KiB each) plus kMxRawSplit for a block sealed in the step.
+__host__ __device__ inline int64_t score_units(int64_t nb, int mx_unit, bool sealed_now) {
+  const int64_t s = sealed_now ? 1 : 0;
+  return mx_unit > 0 ? (nb - s + mx_unit - 1) / mx_unit + s * kMxRawSplit : (int64_t)kScoreSplit * nb;
 }
 
 struct Pools {

@@ -469,7 +469,7 @@ void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32
     maxnb = std::max<int64_t>(maxnb, h_rowlen(c->P, r.len_new, r.nb_new) / kC4);
     // eager C4: the open block is scored too, and a completed group gets its entry
     const bool open = h_open(c->P, r.len_new, r.nb_new) > 0;
-    if (c4) n_score += score_units(r.nb_new, mx_unit) + (open ? kScoreSplit : 0);
+    if (c4) n_score += score_units(r.nb_new, mx_unit, id >= 0) + (open ? kScoreSplit : 0);
     if (c->P.eager && r.len_new % 4 == 0 && r.len_new % kBlk != 0) B.open_req[B.n_open++] = (int8_t)i;
   }
   S.ld = std::max<int64_t>(kC4 * maxnb, 1);
@@ -530,7 +530,8 @@ void plan_step_batch(hsa_ctx* c, const AppendPlan& plan, const std::vector<int32
     S.first_s[i] = (int32_t)ts;
     ta += pa.wgs[i];
     tb += pb.wgs[i];
-    ts += c4 ? score_units(B.r[i].nb, mx_unit) + (h_open(c->P, B.r[i].len, B.r[i].nb) > 0 ? kScoreSplit : 0)
+    ts += c4 ? score_units(B.r[i].nb, mx_unit, B.r[i].aux >= 0) +
+                   (h_open(c->P, B.r[i].len, B.r[i].nb) > 0 ? kScoreSplit : 0)
              : 0;
   }
   S.first_a[n] = (int32_t)ta;

@@ -103,18 +103,31 @@ __device__ __forceinline__ void score_unit(const Pools& P, const ReqBatch& B, co
 }
 
 
-// Indexer scores of scoring unit `unit` with MXFP4 keys: sealed blocks
-// [u G, u G + G) of one request (G = S.mx_unit), kMxPass blocks' loads in flight
-// at a time; a block sealed in this step (the request's last) is scored from the
-// fp32 tail and the input, quantised as the seal stores it.
+// Indexer scores of scoring unit `unit` with MXFP4 keys: stored blocks
+// [u G, u G + G) of one request (G = S.mx_unit), kMxPass blocks' loads in flight at
+// a time. A block sealed in this step (the request's last) has kMxRawSplit units of
+// its own after them, each scoring 32 of its tokens from the fp32 tail and the input,
+// quantised as the seal stores them.
 __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B, const StepArgs& S,
                                               int unit) {
   const int r = owner_of(S.first_s, B.n, unit);
   const Req R = B.r[r];
-  const int lb0 = (unit - S.first_s[r]) * S.mx_unit;
-  const int lb1 = min(lb0 + S.mx_unit, R.nb);
-  const int lbs = (R.aux >= 0 && lb1 == R.nb) ? lb1 - 1 : lb1;   // stored blocks: [lb0, lbs)
+  const int nst = R.aux >= 0 ? R.nb - 1 : R.nb;   // stored blocks
+  const int u = unit - S.first_s[r];
+  const int nsu = (nst + S.mx_unit - 1) / S.mx_unit;
   const float* qrow = S.qi + (int64_t)r * kIRow;
+  if (u >= nsu) {
+    constexpr int kTok = kBlk / kMxRawSplit;
+    const int t0 = (u - nsu) * kTok;
+    const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
+    const float* inrow = S.iin + (int64_t)r * kIRow;
+    score_block_mx_raw<kTok / 32>(
+        [&](int t) { return t0 + t == kBlk - 1 ? inrow : tail + (int64_t)(t0 + t) * kIRow; }, qrow,
+        S.scores + (int64_t)r * S.ld + (int64_t)kC4 * nst + t0 / 4);
+    return;
+  }
+  const int lb0 = u * S.mx_unit;
+  const int lbs = min(lb0 + S.mx_unit, nst);   // stored blocks [lb0, lbs) of this unit
   float* out = S.scores + (int64_t)r * S.ld + (int64_t)kC4 * lb0;
   const int32_t* tab = P.table + (int64_t)R.state * P.table_stride;
   const int lane = threadIdx.x & 63;
@@ -161,12 +174,6 @@ __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B,
 #pragma unroll
       for (int g = 0; g < 4; ++g) mx_write_pair(mx_dot(w[j][g], e[j][g] - 127, q), o + 2 * (wave * 4 + g));
     }
-  }
-  if (lbs < lb1) {
-    const float* tail = P.idx_tail + (int64_t)R.state * kBlk * kIRow;
-    const float* inrow = S.iin + (int64_t)r * kIRow;
-    score_block_mx_raw<kBlk / 32>([&](int t) { return t == kBlk - 1 ? inrow : tail + t * kIRow; }, qrow,
-                                  out + kC4 * (lbs - lb0));
   }
 }
 
