@@ -17,8 +17,8 @@ namespace {
 // Decode append (one token per request) with the seal fused in.
 // Workgroups [0, n): write request i's token into ring slot p mod n_win and
 // indexer-tail slot p mod 128 (p = len - 1), and record a new block id in the
-// device block table. Workgroups [n, n + 8 * n_seal): seal one eighth of a
-// sealing request's block (4 C4 entries, 16 indexer keys, one HCA partial).
+// device block table. Workgroups [n, n + kSealSplit * n_seal): seal one piece of
+// a sealing request's block (2 C4 entries, 8 indexer keys, one HCA partial).
 // No slot written by the first group is read by the second: the new token's
 // ring slot differs from the 127 older ones (n_win >= 128), and its tail slot is
 // 127, which the seal reads from the input instead.
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_decode_append(Pools P, ReqBatch B, cons
   const int item = (bid - B.n) / kSealSplit;
   const int sub = (bid - B.n) % kSealSplit;
   const int ri = B.seal_req[item];
-  seal_eighth<FP8, C4, KV8>(P, B.r[ri], ri, item, sub, kin, vin, iin, part);
+  seal_piece<FP8, C4, KV8>(P, B.r[ri], ri, item, sub, kin, vin, iin, part);
 }
 
 // One workgroup per block sealed by k_decode_append (next launch, so the partials
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_seal_merge(Pools P, ReqBatch B, const f
   seal_merge(P, B.r[B.seal_req[blockIdx.x]].aux, part, blockIdx.x);
 }
 
-// Bulk seal: one workgroup per block, its eight 16-token partials merged in
+// Bulk seal: one workgroup per block, its sixteen 8-token partials merged in
 // registers in order. Templates: FP8 C4 entries; the layer keeps C4 entries (C4)
 // and HCA entries (HCA); KV8 FP8 KV.
 template <bool FP8, bool C4, bool HCA, bool KV8>

@@ -34,7 +34,7 @@ constexpr int kIRow = kHi * kDi;   // 256 fp32 per indexer row
 constexpr int kBlk = 128;          // tokens per block = lcm(4, 128)
 constexpr int kC4 = 32;            // C4 entries per block
 constexpr int kMaxReq = 64;        // requests per launch descriptor
-constexpr int kSealSplit = 8;      // workgroups per decode-time seal (16 tokens each)
+constexpr int kSealSplit = 16;     // workgroups per decode-time seal (8 tokens each)
 #ifndef HSA_SCORE_SPLIT
 #define HSA_SCORE_SPLIT 2
 #endif

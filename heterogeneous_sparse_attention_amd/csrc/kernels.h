@@ -39,7 +39,7 @@ inline hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipS
 hipError_t launch_decode_append(const Pools& P, const ReqBatch& B, const void* kin, const void* vin,
                                 const float* iin, float* part, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
-// Fold the eight HCA partials of each block sealed by launch_decode_append.
+// Fold the kSealSplit HCA partials of each block sealed by launch_decode_append.
 hipError_t launch_seal_merge(const Pools& P, const ReqBatch& B, const float* part, hipStream_t st,
                  const LaunchEv& ev = LaunchEv{});
 hipError_t launch_bulk_seal(const Pools& P, const SealDesc* seals, int64_t n_seals, const void* kin,

@@ -9,7 +9,7 @@
 // head h, g_t = <W[h], K_t[h]>, alpha = softmax over the group's tokens, entry =
 // sum_t alpha_t (K_t[h], V_t[h]), stored as bf16 (round to nearest even). C4 entry
 // j of a block pools tokens 4j..4j+3 with W_csa; the HCA entry pools all 128 with
-// W_hca, as eight 16-token softmax partials folded in order.
+// W_hca, as sixteen 8-token softmax partials folded in order.
 //
 // Thread layout (256 lanes): lane t owns head t/16 and dims (t%16)*8 .. +8 of every
 // token, i.e. 16 contiguous bytes of each 4 KiB K or V row, so a token is one
@@ -126,7 +126,7 @@ __device__ __forceinline__ void load_group(const TokSrc& src, int tb, int off, u
   }
 }
 
-constexpr int kSubTok = kBlk / kSealSplit;   // 16 tokens per seal partial
+constexpr int kSubTok = kBlk / kSealSplit;   // 8 tokens per seal partial
 
 // C4 entry of 4 tokens: this lane's 8 dims of each (packed bf16) and their CSA gate
 // logits gc (<W_csa[h], K_t[h]>); softmax over the 4 gates, the weighted sums of K
@@ -219,13 +219,13 @@ __device__ __forceinline__ void open_entry(const Pools& P, int32_t state, int32_
   if (tid == 0) P.table[(int64_t)state * P.table_stride + nb] = P.max_blocks + state;
 }
 
-// Seal tokens [t0, t0 + 16) of one block (C4 entries bf16, or FP8 when FP8, which
-// the caller sets from P.fp8; C4 false for layers without C4 entries, set from
-// P.c4): writes their 4 C4 entries and 16
-// indexer keys, and returns the HCA softmax partial (m, l, acc) of these tokens
-// for this lane's 8 dims. Both seal paths build the HCA entry from the same eight
-// partials merged in the same order, so bulk and one-token appends give
-// bit-identical blocks.
+// Seal tokens [t0, t0 + kSubTok) of one block (C4 entries bf16, or FP8 when FP8,
+// which the caller sets from P.fp8; C4 false for layers without C4 entries, set
+// from P.c4): writes their kSubTok / 4 C4 entries and kSubTok indexer keys, and
+// returns the HCA softmax partial (m, l, acc) of these tokens for this lane's 8
+// dims. Both seal paths build the HCA entry from the same kSealSplit partials
+// merged in the same order, so bulk and one-token appends give bit-identical
+// blocks.
 template <bool FP8, bool C4, bool KV8 = false>
 __device__ __forceinline__ void seal_part(const Pools& P, const TokSrc& src, int32_t id, int t0,
                                           float& m, float& l, float* acck, float* accv) {
@@ -395,10 +395,6 @@ __device__ __forceinline__ void append_token(const Pools& P, const Req& r, int i
   if (tid == 0 && r.aux >= 0) P.table[(int64_t)r.state * P.table_stride + (r.nb - 1)] = r.aux;
 }
 
-// One eighth (16 tokens) of the decode-time seal of request i's block r.aux: its
-// 4 C4 entries, 16 indexer keys and one HCA partial to part[item * 8 + sub]. The
-// newest token (position r.len - 1) is read from input row i, so this may run in
-// the same launch as append_token. 256 threads.
 // The state's ring as a token source of the seal (bf16 rows, or FP8 codes and scales).
 __device__ __forceinline__ void ring_src(const Pools& P, int32_t state, TokSrc& src) {
   const int64_t g0 = (int64_t)state * P.n_win;
@@ -408,10 +404,14 @@ __device__ __forceinline__ void ring_src(const Pools& P, int32_t state, TokSrc& 
   src.ring_s = P.kv8 ? P.sws + g0 * kC4Scales : nullptr;
 }
 
+// One piece (kSubTok = 8 tokens) of the decode-time seal of request i's block r.aux:
+// its 2 C4 entries, 8 indexer keys and one HCA partial to part[item * kSealSplit +
+// sub]. The newest token (position r.len - 1) is read from input row i, so this
+// may run in the same launch as append_token. 256 threads.
 template <bool FP8, bool C4, bool KV8 = false>
-__device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i, int item, int sub,
-                                            const uint16_t* kin, const uint16_t* vin,
-                                            const float* iin, float* part) {
+__device__ __forceinline__ void seal_piece(const Pools& P, const Req& r, int i, int item, int sub,
+                                           const uint16_t* kin, const uint16_t* vin,
+                                           const float* iin, float* part) {
   const int tid = threadIdx.x;
   TokSrc src;
   ring_src(P, r.state, src);
@@ -437,7 +437,7 @@ __device__ __forceinline__ void seal_eighth(const Pools& P, const Req& r, int i,
   pv[1] = make_float4(accv[4], accv[5], accv[6], accv[7]);
 }
 
-// Fold the eight HCA partials of seal `item` in order (the arithmetic of the bulk
+// Fold the kSealSplit HCA partials of seal `item` in order (the arithmetic of the bulk
 // seal) and store block id's HCA entry. Threads 0..255 take part (of 256 or more).
 __device__ __forceinline__ void seal_merge(const Pools& P, int32_t id, const float* part, int item) {
   const int tid = threadIdx.x;

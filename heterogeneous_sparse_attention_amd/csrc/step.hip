@@ -7,7 +7,7 @@
 // step, for every request of the batch:
 //
 //   S1  append the token (ring + indexer tail), seal a full block (C4 entries,
-//       indexer keys, eight HCA partials) and indexer scores of every sealed
+//       indexer keys, sixteen HCA partials) and indexer scores of every sealed
 //       block. Nothing read in S1 is written in S1: the new token is read from
 //       the input wherever it is needed (last indexer key of a block sealed now,
 //       last token of the seal).
@@ -184,11 +184,11 @@ __device__ __forceinline__ void score_unit_mx(const Pools& P, const ReqBatch& B,
 template <bool FP8, bool C4, bool KV8>
 __global__ __launch_bounds__(256, FP8 || KV8 ? 3 : 4) void k_step1(Pools P, ReqBatch B, StepArgs S) {
   int bid = blockIdx.x;
-  // -- seal eighths (first, so the longest single workgroups start early)
+  // -- seal pieces (first, so the longest single workgroups start early)
   if (bid < kSealSplit * B.n_seal) {
     const int item = bid / kSealSplit;
     const int ri = B.seal_req[item];
-    seal_eighth<FP8, C4, KV8>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
+    seal_piece<FP8, C4, KV8>(P, B.r[ri], ri, item, bid % kSealSplit, S.kin, S.vin, S.iin, S.seal_part);
     return;
   }
   bid -= kSealSplit * B.n_seal;
