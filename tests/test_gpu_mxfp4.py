@@ -96,10 +96,15 @@ def _check_keys(cache, o, bg, bo):
     assert np.array_equal(g["idx_codes"], r.idx_codes), bo
 
 
-@pytest.mark.parametrize("fused,entries", [("1", "bf16"), ("0", "bf16"), ("1", "fp8")])
-def test_mxfp4_cache_matches_oracle(monkeypatch, fused, entries):
+# mx_unit: MXFP4 blocks per scoring workgroup ("" = the default, one 3-block pass);
+# 1 pads every pass with two repeated reads, 8 runs passes of 3, 3 and 2 blocks
+@pytest.mark.parametrize("fused,entries,mx_unit", [("1", "bf16", ""), ("0", "bf16", ""), ("1", "fp8", ""),
+                                                   ("1", "bf16", "1"), ("0", "bf16", "8")])
+def test_mxfp4_cache_matches_oracle(monkeypatch, fused, entries, mx_unit):
     import torch
     monkeypatch.setenv("HSA_STEP_FUSED", fused)
+    if mx_unit:
+        monkeypatch.setenv("HSA_MX_UNIT", mx_unit)
     seed = 0x4F4
     rng = np.random.default_rng(seed)
     B = 9
