@@ -192,11 +192,11 @@ __device__ __forceinline__ void for_each_key(int N, const float* S, F f) {
   const float4* S4 = reinterpret_cast<const float4*>(S);
   for (int b = 0; b < n4; b += NT * kSelBatch) {
     float4 v[kSelBatch];
+    // unconditional loads (an index past the row re-reads its last float4): a load
+    // inside a branch makes the compiler wait for every earlier one where the branch
+    // joins, which would serialise the batch
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) {
-      const int j = b + u * NT + (int)threadIdx.x;
-      if (j < n4) v[u] = S4[j];
-    }
+    for (int u = 0; u < kSelBatch; ++u) v[u] = S4[min(b + u * NT + (int)threadIdx.x, n4 - 1)];
 #pragma unroll
     for (int u = 0; u < kSelBatch; ++u) {
       const int j = b + u * NT + (int)threadIdx.x;
@@ -345,14 +345,22 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
       const int per = ((n4 + NW - 1) / NW + 63) & ~63;
       const int j0 = wv * per, j1 = min(n4, j0 + per);
       const float4* S4 = reinterpret_cast<const float4*>(S);
+      // kSelBatch float4s of the wave's range per lane are loaded before any is used
+      // (unconditionally: an index past the range re-reads its last float4)
       int gt_w = 0, eq_w = 0;
-      for (int j = j0 + lane; j < j1; j += 64) {
-        const float4 v = S4[j];
-        const uint32_t e[4] = {okey(v.x), okey(v.y), okey(v.z), okey(v.w)};
+      for (int jb = j0; jb < j1; jb += 64 * kSelBatch) {
+        float4 v[kSelBatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          gt_w += above(e[q]);
-          eq_w += at_tau(e[q]);
+        for (int u = 0; u < kSelBatch; ++u) v[u] = S4[min(jb + 64 * u + lane, j1 - 1)];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) {
+          if (jb + 64 * u + lane >= j1) continue;
+          const uint32_t e[4] = {okey(v[u].x), okey(v[u].y), okey(v[u].z), okey(v[u].w)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gt_w += above(e[q]);
+            eq_w += at_tau(e[q]);
+          }
         }
       }
       int tot;
@@ -370,33 +378,40 @@ __device__ __forceinline__ void select_run(int N, int32_t k, int32_t sorted, con
         base_gt += sh.cnt[0][0][w];
         base_eq += sh.cnt[0][1][w];
       }
-      for (int jb = j0; jb < j1; jb += 64) {
-        const int j = jb + lane;
-        uint32_t e[4] = {0u, 0u, 0u, 0u};
-        int g = 0, q_eq = 0;
-        if (j < j1) {
-          const float4 v = S4[j];
-          e[0] = okey(v.x); e[1] = okey(v.y); e[2] = okey(v.z); e[3] = okey(v.w);
+      for (int jb0 = j0; jb0 < j1; jb0 += 64 * kSelBatch) {
+        float4 v[kSelBatch];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            g += above(e[q]);
-            q_eq += at_tau(e[q]);
-          }
-        }
-        int g_tot, e_tot;
-        int gb = base_gt + wave_excl_scan(g, g_tot);
-        int eb = base_eq + wave_excl_scan(q_eq, e_tot);
-        if (j < j1) {
+        for (int u = 0; u < kSelBatch; ++u) v[u] = S4[min(jb0 + 64 * u + lane, j1 - 1)];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bool gt = above(e[q]), eq = at_tau(e[q]);
-            if (gt || (eq && eb < rem)) take(4 * j + q, e[q], gb + min(eb, rem));
-            gb += gt;
-            eb += eq;
+        for (int u = 0; u < kSelBatch; ++u) {
+          const int jb = jb0 + 64 * u;
+          if (jb >= j1) break;   // wave-uniform
+          const int j = jb + lane;
+          uint32_t e[4] = {0u, 0u, 0u, 0u};
+          int g = 0, q_eq = 0;
+          if (j < j1) {
+            e[0] = okey(v[u].x); e[1] = okey(v[u].y); e[2] = okey(v[u].z); e[3] = okey(v[u].w);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              g += above(e[q]);
+              q_eq += at_tau(e[q]);
+            }
           }
+          int g_tot, e_tot;
+          int gb = base_gt + wave_excl_scan(g, g_tot);
+          int eb = base_eq + wave_excl_scan(q_eq, e_tot);
+          if (j < j1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bool gt = above(e[q]), eq = at_tau(e[q]);
+              if (gt || (eq && eb < rem)) take(4 * j + q, e[q], gb + min(eb, rem));
+              gb += gt;
+              eb += eq;
+            }
+          }
+          base_gt += g_tot;
+          base_eq += e_tot;
         }
-        base_gt += g_tot;
-        base_eq += e_tot;
       }
     }
     int base_gt = 0, base_eq = 0, parity = 0;
