@@ -666,35 +666,40 @@ __device__ __forceinline__ void merge_partials_wg(PartFn part_of, int n, const f
   const int o = h * kD + 4 * j;
   float xs = kNoMax;
   float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (xk.k) {
-    const uint2 qw = *reinterpret_cast<const uint2*>(xk.q + o);
-    float kx[4];
-    if (xk.fp8) {   // four codes of K and of V, and the head's scales
-      const uint8_t* codes = reinterpret_cast<const uint8_t*>(xk.k);
-      const float* sc = reinterpret_cast<const float*>(xk.v);
-      const int hp = 4 * (h & 3) + (h >> 2);
-      const int kc = (int)*reinterpret_cast<const uint32_t*>(codes + o);
-      const int vc = (int)*reinterpret_cast<const uint32_t*>(codes + kRow + o);
-      const float ks = sc[hp], vs = sc[kH + hp];
-      const f32x2_v k01 = __builtin_amdgcn_cvt_pk_f32_fp8(kc, false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8(kc, true);
-      const f32x2_v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(vc, false), v23 = __builtin_amdgcn_cvt_pk_f32_fp8(vc, true);
-      kx[0] = k01.x * ks;
-      kx[1] = k01.y * ks;
-      kx[2] = k23.x * ks;
-      kx[3] = k23.y * ks;
-      xv = make_float4(v01.x * vs, v01.y * vs, v23.x * vs, v23.y * vs);
-    } else {
-      const uint2 kw = *reinterpret_cast<const uint2*>(xk.k + o);
-      const uint2 vw = *reinterpret_cast<const uint2*>(xk.v + o);
-      kx[0] = bf_lo(kw.x);
-      kx[1] = bf_hi(kw.x);
-      kx[2] = bf_lo(kw.y);
-      kx[3] = bf_hi(kw.y);
-      xv = make_float4(bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y));
+  // the extra key's score and V values; its loads sit in a branch, where the compiler
+  // waits for every load in flight, so it runs after the partials' loads are issued
+  auto extra_key = [&]() {
+    if (xk.k) {
+      const uint2 qw = *reinterpret_cast<const uint2*>(xk.q + o);
+      float kx[4];
+      if (xk.fp8) {   // four codes of K and of V, and the head's scales
+        const uint8_t* codes = reinterpret_cast<const uint8_t*>(xk.k);
+        const float* sc = reinterpret_cast<const float*>(xk.v);
+        const int hp = 4 * (h & 3) + (h >> 2);
+        const int kc = (int)*reinterpret_cast<const uint32_t*>(codes + o);
+        const int vc = (int)*reinterpret_cast<const uint32_t*>(codes + kRow + o);
+        const float ks = sc[hp], vs = sc[kH + hp];
+        const f32x2_v k01 = __builtin_amdgcn_cvt_pk_f32_fp8(kc, false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8(kc, true);
+        const f32x2_v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(vc, false), v23 = __builtin_amdgcn_cvt_pk_f32_fp8(vc, true);
+        kx[0] = k01.x * ks;
+        kx[1] = k01.y * ks;
+        kx[2] = k23.x * ks;
+        kx[3] = k23.y * ks;
+        xv = make_float4(v01.x * vs, v01.y * vs, v23.x * vs, v23.y * vs);
+      } else {
+        const uint2 kw = *reinterpret_cast<const uint2*>(xk.k + o);
+        const uint2 vw = *reinterpret_cast<const uint2*>(xk.v + o);
+        kx[0] = bf_lo(kw.x);
+        kx[1] = bf_hi(kw.x);
+        kx[2] = bf_lo(kw.y);
+        kx[3] = bf_hi(kw.y);
+        xv = make_float4(bf_lo(vw.x), bf_hi(vw.x), bf_lo(vw.y), bf_hi(vw.y));
+      }
+      const float d = fmaf(bf_lo(qw.x), kx[0], bf_hi(qw.x) * kx[1]) + fmaf(bf_lo(qw.y), kx[2], bf_hi(qw.y) * kx[3]);
+      xs = half_sum(d) * kQScale;
     }
-    const float d = fmaf(bf_lo(qw.x), kx[0], bf_hi(qw.x) * kx[1]) + fmaf(bf_lo(qw.y), kx[2], bf_hi(qw.y) * kx[3]);
-    xs = half_sum(d) * kQScale;
-  }
+  };
+  if (n > 32) extra_key();   // the merge in passes below: the key first, as its loads wait anyway
   float4 acc;
   auto add = [&](float w, const float4& a) {
     acc.x = fmaf(w, a.x, acc.x);
@@ -713,6 +718,7 @@ __device__ __forceinline__ void merge_partials_wg(PartFn part_of, int n, const f
       mm = part_ml[p * 2 * kH + h];
       ll = part_ml[p * 2 * kH + kH + h];
     }
+    extra_key();
     const float M = fmaxf(half_max(mm), xs);
     float w = j < n ? exp2f(mm - M) : 0.f;
     const float xw = xk.k ? exp2f(xs - M) : 0.f;
